@@ -1,0 +1,412 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each check is a function of an oracle implementation, so that the last test can plant
+plausible mistakes in a copy of the oracle (on the CPU) and show that some pin fails.
+"""
+import itertools
+import types
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import csahca as O
+from synthgen.codecs import f32_to_bf16_bits, f32_to_e4m3fn_bits
+from tests.conftest import read_golden
+
+
+def _impl(**over):
+    ns = types.SimpleNamespace(pool=O.pool, index_scores=O.index_scores, topk=O.topk,
+                               attend=O.attend, visible=O.visible, csa_rows=O.csa_rows,
+                               hca_rows=O.hca_rows, entry_counts=O.entry_counts,
+                               window_positions=O.window_positions)
+    for k, v in over.items():
+        setattr(ns, k, v)
+    return ns
+
+
+# ---------------------------------------------------------------------------------------
+# checks (each raises AssertionError when the implementation disagrees with its pin)
+# ---------------------------------------------------------------------------------------
+def check_budget_counts(o):
+    g = read_golden("budget_counts.txt")
+    stored, attended, hca = o.entry_counts(g["n"], 4, 128, 1024, 128)
+    assert stored == g["csa_stored"]
+    assert attended == g["csa_attended"]
+    assert hca == g["hca_stored"] == g["hca_attended"]
+
+
+def check_worked_example(o):
+    g = read_golden("worked_example.txt")
+    for n in (2000, 32000, 1000000):
+        _, att, _ = o.entry_counts(n, 4, 128, 1024, 128)
+        assert att == g[f"n_{n}_attended"]
+        pct = 100.0 * att / n
+        want = g[f"n_{n}_percent"]
+        # the page rounds to the shown digits
+        digits = len(str(want).split(".")[1]) if "." in str(want) else 0
+        assert round(pct, digits) == pytest.approx(want)
+
+
+def check_pool_counts(o):
+    g = read_golden("pool_counts.txt")
+    X = np.zeros((g["tokens"], 2))
+    assert o.pool(X, X, 4).shape[0] == g["entries_m4"]
+    assert o.pool(X, X, 128).shape[0] == g["entries_m128"]
+    _, _, hca = o.entry_counts(1_000_000, 4, 128, 1024, 128)
+    assert abs((hca - 128) - g["hca_entries_1m_approx"]) < 50
+
+
+def _budget_toy_inputs():
+    # Draw order of the page's toy: keys (16 x 6), then 4 position logits, then the query.
+    st = np.random.RandomState(0)
+    keys = st.randn(16, 6)
+    logits = st.randn(4)
+    q = st.randn(6)
+    return keys, logits, q
+
+
+def check_budget_toy(o):
+    """Position-only softmax gate (Z[j] = logit of position j), then the indexer with one
+    head of weight 1 -- its ReLU keeps the two positive winners -- then top-2."""
+    g = read_golden("budget_counts.txt")
+    keys, logits, q = _budget_toy_inputs()
+    Z = np.repeat(np.tile(logits, 4)[:, None], 6, axis=1)
+    C = o.pool(keys, Z, 4)
+    assert C.shape[0] == g["toy_entries"]
+    s = o.index_scores(q[None, :], np.ones(1), C, C.shape[0])
+    assert sorted(o.topk(s, 2).tolist()) == sorted(g["toy_top2"])
+
+
+def _recall_toy_inputs():
+    rng = np.random.default_rng(0)
+    keys = rng.normal(0, 1, (64, 8))
+    query = keys[37] + rng.normal(0, 0.3, 8)
+    return keys, query
+
+
+def check_pooling_recall(o):
+    """Mean pooling (constant gate logits) and a single-head indexer of weight 1."""
+    g = read_golden("pooling_recall.txt")
+    keys, query = _recall_toy_inputs()
+    for m in (1, 4, 16):
+        C = o.pool(keys, np.zeros_like(keys), m)
+        s = o.index_scores(query[None, :], np.ones(1), C, C.shape[0])
+        srt = np.sort(s)
+        assert int(np.argmax(s)) == g[f"best_entry_m{m}"]
+        assert round(srt[-1] - srt[-2], 2) == pytest.approx(g[f"lead_m{m}"])
+    C = o.pool(keys, np.zeros_like(keys), 4)
+    s = o.index_scores(query[None, :], np.ones(1), C, C.shape[0])
+    assert sorted(x for x in o.topk(s, 3).tolist() if x >= 0) == sorted(g["top3_m4"])
+    # window of 8 raw tokens + 3 selected entries
+    assert len(o.window_positions(63, 8)) + 3 == g["entries_attended"]
+
+
+def check_pool_closed_forms(o):
+    rng = np.random.default_rng(7)
+    n, c = 24, 5
+    X = rng.normal(size=(n, c))
+    Z = rng.normal(size=(n, c)) * 3
+    # identical tokens inside each block -> that token, for any gate
+    Xi = np.repeat(X[::4], 4, axis=0)
+    np.testing.assert_allclose(o.pool(Xi, Z, 4), X[::4], rtol=0, atol=1e-14)
+    # gate constant over a block (per channel) -> arithmetic mean of the block
+    Zc = np.repeat(rng.normal(size=(n // 4, c)), 4, axis=0)
+    np.testing.assert_allclose(o.pool(X, Zc, 4), X.reshape(6, 4, c).mean(1), atol=1e-14)
+    # shifting the logits of a block-channel by a constant changes nothing
+    Zs = Z + np.repeat(rng.normal(size=(n // 4, c)) * 10, 4, axis=0)
+    np.testing.assert_allclose(o.pool(X, Zs, 4), o.pool(X, Z, 4), atol=1e-12)
+    # m = 1 is the identity
+    np.testing.assert_allclose(o.pool(X, Z, 1), X, atol=0)
+    # m = 2 in closed form: weight of the first token is the logistic of z0 - z1, per channel
+    a = 1.0 / (1.0 + np.exp(-(Z[0::2] - Z[1::2])))
+    np.testing.assert_allclose(o.pool(X, Z, 2), a * X[0::2] + (1 - a) * X[1::2], atol=1e-13)
+    # a positional bias alone (Z = 0) is the page's position gate: token j of every block
+    # gets exp(P_j) / sum exp(P)
+    P = rng.normal(size=(3, c))
+    Xp = X[:21]
+    wts = np.exp(P) / np.exp(P).sum(0)
+    want = (Xp[:21].reshape(7, 3, c) * wts[None]).sum(1)
+    np.testing.assert_allclose(o.pool(Xp, np.zeros_like(Xp), 3, P), want, atol=1e-13)
+    # ragged tail: 26 tokens with m = 4 -> 6 entries, the last 2 tokens dropped
+    assert o.pool(np.vstack([X, X[:2]]), np.vstack([Z, Z[:2]]), 4).shape == (6, c)
+
+
+def check_indexer_closed_forms(o):
+    rng = np.random.default_rng(3)
+    n_ih, c_I, N = 4, 6, 9
+    # indexer queries along the first n_ih axes: q_h . k_s is coordinate h of k_s
+    qI = np.eye(n_ih, c_I)
+    KI = rng.normal(size=(N, c_I))
+    w = rng.random(n_ih)
+    got = o.index_scores(qI, w, KI, N)
+    for s in range(N):
+        want = sum(w[h] * max(0.0, KI[s, h]) for h in range(n_ih))
+        assert got[s] == pytest.approx(want, abs=1e-14)
+    # all weights zero -> all scores zero
+    assert np.all(o.index_scores(qI, np.zeros(n_ih), KI, N) == 0)
+    # positive scaling of the weights scales the scores and keeps the selection
+    s1 = o.index_scores(rng.normal(size=(n_ih, c_I)), w, KI, N)
+    qq = rng.normal(size=(n_ih, c_I))
+    s1 = o.index_scores(qq, w, KI, N)
+    s2 = o.index_scores(qq, 2.5 * w, KI, N)
+    np.testing.assert_allclose(s2, 2.5 * s1, atol=1e-13)
+    assert np.array_equal(o.topk(s1, 3), o.topk(s2, 3))
+    # only the first V entries are scored
+    assert o.index_scores(qq, w, KI, 5).shape == (5,)
+
+
+def _brute_topk(scores, k):
+    """The unique set of min(k, V) indices each of which beats every index outside it
+    (higher score, or equal score and lower index)."""
+    V = len(scores)
+    keff = min(k, V)
+
+    def beats(i, j):
+        return scores[i] > scores[j] or (scores[i] == scores[j] and i < j)
+
+    found = []
+    for S in itertools.combinations(range(V), keff):
+        rest = [j for j in range(V) if j not in S]
+        if all(beats(i, j) for i in S for j in rest):
+            found.append(S)
+    assert len(found) == 1
+    return sorted(found[0])
+
+
+def check_topk_brute(o):
+    rng = np.random.default_rng(11)
+    for trial in range(60):
+        V = int(rng.integers(1, 11))
+        k = int(rng.integers(1, 13))
+        if trial % 3 == 0:
+            s = rng.integers(0, 3, V).astype(np.float64)       # heavy ties
+        else:
+            s = rng.normal(size=V)
+        got = o.topk(s, k)
+        keff = min(k, V)
+        assert got.shape == (k,)
+        assert np.all(got[keff:] == -1)
+        assert got[:keff].tolist() == _brute_topk(s, k)
+    # all-equal scores, including -0.0 mixed with +0.0: lowest indices win
+    s = np.array([0.0, -0.0, 0.0, -0.0, 0.0, -0.0])
+    assert o.topk(s, 3).tolist() == [0, 1, 2]
+    # k >= V: everything, then padding
+    assert o.topk(np.array([3.0, 1.0]), 4).tolist() == [0, 1, -1, -1]
+
+
+def check_attend_textbook(o):
+    rng = np.random.default_rng(5)
+    n_h, c, R = 3, 8, 11
+    Q = rng.normal(size=(n_h, c))
+    rows = rng.normal(size=(R, c))
+    scale = 1 / np.sqrt(c)
+    Ot, _ = o.attend(Q, rows, scale)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(Q)[None], torch.from_numpy(rows)[None], torch.from_numpy(rows)[None],
+        scale=scale)[0].numpy()
+    np.testing.assert_allclose(Ot, ref, atol=1e-12)
+    # log-sum-exp against the library routine
+    from scipy.special import logsumexp
+    _, lse = o.attend(Q, rows, scale)
+    np.testing.assert_allclose(lse, logsumexp(scale * Q @ rows.T, axis=1), atol=1e-12)
+    # permuting the rows changes nothing
+    perm = rng.permutation(R)
+    np.testing.assert_allclose(o.attend(Q, rows[perm], scale)[0], Ot, atol=1e-12)
+    # two halves merged by their log-sum-exp give the joint softmax
+    Oa, la = o.attend(Q, rows[:4], scale)
+    Ob, lb = o.attend(Q, rows[4:], scale)
+    M = np.maximum(la, lb)
+    wa, wb = np.exp(la - M), np.exp(lb - M)
+    merged = (wa[:, None] * Oa + wb[:, None] * Ob) / (wa + wb)[:, None]
+    np.testing.assert_allclose(merged, Ot, atol=1e-12)
+    # a single row is returned exactly
+    np.testing.assert_array_equal(o.attend(Q, rows[:1], scale)[0], np.repeat(rows[:1], n_h, 0))
+
+
+def check_rows_and_visibility(o):
+    rng = np.random.default_rng(9)
+    c, m, W = 4, 4, 8
+    n = 64
+    X = rng.normal(size=(n, c))
+    Z = rng.normal(size=(n, c))
+    C = o.pool(X, Z, m)
+    # visibility: a block becomes usable when its last token is reached
+    assert [o.visible(p, 4, 16) for p in (0, 2, 3, 4, 7, 63, 1000)] == [0, 0, 1, 1, 2, 16, 16]
+    # window includes the query token; clipped at the sequence start
+    assert o.window_positions(0, 8).tolist() == [0]
+    assert o.window_positions(20, 8).tolist() == list(range(13, 21))
+    assert o.window_positions(5, 0).tolist() == []
+    # k >= visible: CSA over every usable entry equals HCA over the same cache
+    p = 37
+    V = o.visible(p, m, C.shape[0])
+    idx = np.full(20, -1)
+    idx[:V] = np.arange(V)
+    Q = rng.normal(size=(2, c))
+    a = o.attend(Q, o.csa_rows(C, idx, X, 0, p, W), 0.5)[0]
+    b = o.attend(Q, o.hca_rows(C, m, X, 0, p, W), 0.5)[0]
+    np.testing.assert_allclose(a, b, atol=1e-14)
+    # p = 0: nothing compressed is visible, the window is token 0 alone -> output = X[0]
+    idx0 = np.full(4, -1)
+    np.testing.assert_array_equal(o.attend(Q, o.csa_rows(C, idx0, X, 0, 0, W), 0.5)[0],
+                                  np.repeat(X[:1], 2, 0))
+    # window source with an offset start position
+    r1 = o.hca_rows(C, m, X, 0, 50, W)
+    r2 = o.hca_rows(C, m, X[30:], 30, 50, W)
+    np.testing.assert_array_equal(r1, r2)
+    assert r1.shape[0] == o.visible(50, m, C.shape[0]) + W
+
+
+ALL_CHECKS = [check_budget_counts, check_worked_example, check_pool_counts, check_budget_toy,
+              check_pooling_recall, check_pool_closed_forms, check_indexer_closed_forms,
+              check_topk_brute, check_attend_textbook, check_rows_and_visibility]
+
+
+@pytest.mark.parametrize("check", ALL_CHECKS, ids=lambda f: f.__name__)
+def test_oracle_pin(check):
+    check(_impl())
+
+
+# ---------------------------------------------------------------------------------------
+# storage decoding pins
+# ---------------------------------------------------------------------------------------
+def test_e4m3fn_known_codes():
+    t = oracle.E4M3FN_TABLE
+    assert t[0x38] == 1.0
+    assert t[0x7E] == 448.0 and t[0xFE] == -448.0
+    assert t[0x01] == 2.0 ** -9           # smallest subnormal
+    assert t[0x08] == 2.0 ** -6           # smallest normal
+    assert t[0x07] == 7 * 2.0 ** -9       # largest subnormal
+    assert t[0x40] == 2.0 and t[0x3C] == 1.5
+    assert np.isnan(t[0x7F]) and np.isnan(t[0xFF])
+    assert t[0x80] == 0.0 and np.signbit(t[0x80])
+    finite = t[~np.isnan(t)]
+    assert len(finite) == 254 and len(np.unique(finite)) == 253   # +0 and -0 compare equal
+
+
+def test_e4m3fn_roundtrip_and_rounding():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    vals = oracle.decode_e4m3fn(codes)
+    assert np.array_equal(f32_to_e4m3fn_bits(vals.astype(np.float32)), codes)
+    # ties go to the even mantissa; beyond 448 saturates
+    enc = lambda x: int(f32_to_e4m3fn_bits(np.array([x], np.float32))[0])
+    assert enc(1.0625) == 0x38            # halfway 1.0 / 1.125 -> 1.0 (even)
+    assert enc(1.1875) == 0x3A            # halfway 1.125 / 1.25 -> 1.25 (even)
+    assert enc(470.0) == 0x7E and enc(1e6) == 0x7E and enc(-1e6) == 0xFE
+    assert enc(2.0 ** -10) == 0x00        # halfway 0 / 2^-9 -> 0
+    assert enc(3 * 2.0 ** -10) == 0x02    # halfway 2^-9 / 2^-8 -> 2^-8 (even)
+    # every encoded value is the nearest representable one
+    rng = np.random.default_rng(0)
+    x = rng.normal(size=4000).astype(np.float32) * 30
+    dec = oracle.decode_e4m3fn(f32_to_e4m3fn_bits(x))
+    finite = np.unique(oracle.E4M3FN_TABLE[~np.isnan(oracle.E4M3FN_TABLE)])
+    nearest = finite[np.abs(x[:, None].astype(np.float64) - finite[None, :]).argmin(1)]
+    assert np.all(np.abs(dec - x) <= np.abs(nearest - x) + 0)
+
+
+def test_bf16_roundtrip_and_rounding():
+    rng = np.random.default_rng(1)
+    x = rng.normal(size=10000).astype(np.float32)
+    d = oracle.decode_bf16(f32_to_bf16_bits(x))
+    assert np.all(np.abs(d - x) <= np.abs(x) * 2.0 ** -8)
+    # against torch's conversion (round to nearest even)
+    tb = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(d, tb)
+    assert oracle.decode_bf16(f32_to_bf16_bits(np.array([1 + 2 ** -8], np.float32)))[0] == 1.0
+    assert oracle.decode_bf16(f32_to_bf16_bits(np.array([1 + 3 * 2 ** -8], np.float32)))[0] \
+        == 1 + 2 ** -6
+
+
+# ---------------------------------------------------------------------------------------
+# the pins catch plausible mistakes (mistakes planted in copies of the oracle, on the CPU)
+# ---------------------------------------------------------------------------------------
+_ORIG_POOL, _ORIG_ATTEND = O.pool, O.attend
+
+
+def _pool_wrong_axis(X, Z, m, P=None):
+    X = np.asarray(X, float)
+    Z = np.asarray(Z, float)
+    n, c = X.shape
+    N = n // m
+    zb = Z[:N * m].reshape(N, m, c)
+    e = np.exp(zb - zb.max(axis=2, keepdims=True))
+    S = e / e.sum(axis=2, keepdims=True)                 # softmax over channels
+    return (S * X[:N * m].reshape(N, m, c)).sum(1)
+
+
+def _pool_ceil(X, Z, m, P=None):
+    X = np.asarray(X, float)
+    pad = (-X.shape[0]) % m
+    Xp = np.vstack([X, np.zeros((pad, X.shape[1]))])
+    Zp = np.vstack([np.asarray(Z, float), np.zeros((pad, X.shape[1]))])
+    return _ORIG_POOL(Xp, Zp, m, P)                      # emits the partial tail block
+
+
+def _scores_no_relu(qI, w, KI, V):
+    return (np.asarray(KI, float)[:V] @ np.asarray(qI, float).T) @ np.asarray(w, float)
+
+
+def _topk_high_index_wins(scores, k):
+    s = np.asarray(scores, float)
+    V = len(s)
+    keff = min(k, V)
+    order = np.lexsort((-np.arange(V), -s))
+    out = np.full(k, -1)
+    out[:keff] = np.sort(order[:keff])
+    return out
+
+
+def _attend_no_scale(Q, rows, scale):
+    return _ORIG_ATTEND(Q, rows, 1.0)
+
+
+def _attend_transposed(Q, rows, scale):
+    Q = np.asarray(Q, float)
+    rows = np.asarray(rows, float)
+    s = (Q @ rows.T) * scale
+    e = np.exp(s - s.max(0, keepdims=True))
+    p = e / e.sum(0, keepdims=True)                      # normalised over heads
+    return p @ rows, np.zeros(Q.shape[0])
+
+
+def _visible_off_by_one(p, m, N):
+    return int(min(N, int(p) // m))
+
+
+def _window_excl(p, W):
+    return np.arange(max(0, int(p) - W), int(p), dtype=np.int64)
+
+
+def _counts_ceil(n, m, m_hca, k, W):
+    nc = -(-n // m)
+    return nc + W, min(nc, k) + W, -(-n // m_hca) + W
+
+
+MUTANTS = {
+    "pool_softmax_over_channels": dict(pool=_pool_wrong_axis),
+    "pool_emits_tail": dict(pool=_pool_ceil),
+    "indexer_without_relu": dict(index_scores=_scores_no_relu),
+    "topk_higher_index_wins": dict(topk=_topk_high_index_wins),
+    "attend_without_scale": dict(attend=_attend_no_scale),
+    "attend_softmax_over_heads": dict(attend=_attend_transposed),
+    "visibility_off_by_one": dict(visible=_visible_off_by_one),
+    "window_excludes_query": dict(window_positions=_window_excl),
+    "counts_round_up": dict(entry_counts=_counts_ceil),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, monkeypatch):
+    over = MUTANTS[name]
+    # row builders call the module-level helpers, so patch those too
+    for k, v in over.items():
+        monkeypatch.setattr(O, k, v)
+    o = _impl(**over)
+    failed = 0
+    for chk in ALL_CHECKS:
+        try:
+            chk(o)
+        except (AssertionError, ValueError, IndexError):
+            failed += 1
+    assert failed >= 1, f"no pin detects the planted mistake {name}"

@@ -1,0 +1,157 @@
+"""Python binding of libcsahca.so, the gfx950 CSA / HCA compressed-attention library.
+
+Argument marshalling only: every entry point forwards to the C function of the same name
+(declared in include/csahca.h) and raises CsaHcaError on a non-zero status.  Pointer
+arguments accept a torch tensor (its data_ptr is passed), a plain integer address or
+None.  ``stream`` defaults to torch's current HIP stream.  There is no fallback: if the
+shared library is missing or cannot be loaded, every call raises.
+"""
+import ctypes
+import os
+
+F32, BF16, FP8_E4M3FN = 0, 1, 2
+OK, EINVAL, ENOTSUP, EWORKSPACE, ELAUNCH = 0, -1, -2, -3, -4
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsahca.so")
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_LL = ctypes.c_longlong
+_F = ctypes.c_float
+_SZ = ctypes.c_size_t
+
+_SIGNATURES = {
+    "csa_compress": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _LL, _LL, _P]),
+    "hca_compress": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _LL, _LL, _P]),
+    "lightning_index_topk_workspace_size": (_SZ, [_I, _I, _I, _I, _I]),
+    "lightning_index_topk": (_I, [_P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P,
+                                  _P, _SZ, _P]),
+    "lightning_index_score": (_I, [_P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _SZ,
+                                   _P]),
+    "lightning_index_select": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _SZ, _P]),
+    "csa_attend_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
+    "csa_attend": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P,
+                        _P, _SZ, _P]),
+    "hca_attend_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
+    "hca_attend": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P,
+                        _SZ, _P]),
+    "csahca_last_error": (ctypes.c_char_p, []),
+    "csahca_version": (_I, []),
+}
+
+_lib = None
+
+
+class CsaHcaError(RuntimeError):
+    def __init__(self, name, status, msg):
+        super().__init__(f"{name} returned {status}: {msg}")
+        self.status = status
+
+
+def load(path=LIB_PATH):
+    """Load (once) and return the ctypes handle of the shared library."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise OSError(f"libcsahca.so not built ({path}); run __graft_entry__.build()")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(s):
+    if s is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+def _check(name, status):
+    if status != OK:
+        raise CsaHcaError(name, status, load().csahca_last_error().decode())
+    return status
+
+
+def version():
+    return load().csahca_version()
+
+
+def last_error():
+    return load().csahca_last_error().decode()
+
+
+def csa_compress(kv, gate, pos_bias, out, B, n, c, m, dtype, in_bstride, out_bstride,
+                 stream=None):
+    return _check("csa_compress", load().csa_compress(
+        _ptr(kv), _ptr(gate), _ptr(pos_bias), _ptr(out), B, n, c, m, dtype, in_bstride,
+        out_bstride, _stream(stream)))
+
+
+def hca_compress(kv, gate, pos_bias, out, B, n, c, m, dtype, in_bstride, out_bstride,
+                 stream=None):
+    return _check("hca_compress", load().hca_compress(
+        _ptr(kv), _ptr(gate), _ptr(pos_bias), _ptr(out), B, n, c, m, dtype, in_bstride,
+        out_bstride, _stream(stream)))
+
+
+def lightning_index_topk_workspace_size(B, Tq, n_ih, N_c, k):
+    return load().lightning_index_topk_workspace_size(B, Tq, n_ih, N_c, k)
+
+
+def lightning_index_topk(q_idx, w_idx, k_idx, idx_dtype, q_pos, m, B, Tq, n_ih, c_I, N_c, k,
+                         topk_idx, topk_score, all_scores, workspace, ws_bytes, stream=None):
+    return _check("lightning_index_topk", load().lightning_index_topk(
+        _ptr(q_idx), _ptr(w_idx), _ptr(k_idx), idx_dtype, _ptr(q_pos), m, B, Tq, n_ih, c_I, N_c,
+        k, _ptr(topk_idx), _ptr(topk_score), _ptr(all_scores), _ptr(workspace), ws_bytes,
+        _stream(stream)))
+
+
+def lightning_index_score(q_idx, w_idx, k_idx, idx_dtype, q_pos, m, B, Tq, n_ih, c_I, N_c, k,
+                          scores, workspace, ws_bytes, stream=None):
+    return _check("lightning_index_score", load().lightning_index_score(
+        _ptr(q_idx), _ptr(w_idx), _ptr(k_idx), idx_dtype, _ptr(q_pos), m, B, Tq, n_ih, c_I, N_c,
+        k, _ptr(scores), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def lightning_index_select(scores, q_pos, m, B, Tq, N_c, k, topk_idx, topk_score, workspace,
+                           ws_bytes, stream=None):
+    return _check("lightning_index_select", load().lightning_index_select(
+        _ptr(scores), _ptr(q_pos), m, B, Tq, N_c, k, _ptr(topk_idx), _ptr(topk_score),
+        _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def csa_attend_workspace_size(B, Tq, n_h, c, k, W):
+    return load().csa_attend_workspace_size(B, Tq, n_h, c, k, W)
+
+
+def csa_attend(q, ckv, topk_idx, win_kv, win_pos, q_pos, B, Tq, n_h, c, N_c, k, L, W, scale,
+               dtype, out, lse, workspace, ws_bytes, stream=None):
+    return _check("csa_attend", load().csa_attend(
+        _ptr(q), _ptr(ckv), _ptr(topk_idx), _ptr(win_kv), _ptr(win_pos), _ptr(q_pos), B, Tq,
+        n_h, c, N_c, k, L, W, float(scale), dtype, _ptr(out), _ptr(lse), _ptr(workspace),
+        ws_bytes, _stream(stream)))
+
+
+def hca_attend_workspace_size(B, Tq, n_h, c, N_h, W):
+    return load().hca_attend_workspace_size(B, Tq, n_h, c, N_h, W)
+
+
+def hca_attend(q, ckv, win_kv, win_pos, q_pos, m, B, Tq, n_h, c, N_h, L, W, scale, dtype, out,
+               lse, workspace, ws_bytes, stream=None):
+    return _check("hca_attend", load().hca_attend(
+        _ptr(q), _ptr(ckv), _ptr(win_kv), _ptr(win_pos), _ptr(q_pos), m, B, Tq, n_h, c, N_h, L, W,
+        float(scale), dtype, _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)))

@@ -1,0 +1,104 @@
+// Shared device helpers for the gfx950 compressed-attention kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "csahca.h"
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define CSAHCA_DEV __device__ __forceinline__
+
+// ---------------------------------------------------------------------------------------
+// host-side status handling
+// ---------------------------------------------------------------------------------------
+namespace csahca {
+
+void set_error(const char* fmt, ...);
+void clear_error();
+
+inline int fail(int code, const char* msg) {
+  set_error("%s", msg);
+  return code;
+}
+
+inline int launch_status(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    set_error("%s: launch failed: %s", what, hipGetErrorString(e));
+    return CSAHCA_ELAUNCH;
+  }
+  clear_error();
+  return CSAHCA_OK;
+}
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace csahca
+
+// ---------------------------------------------------------------------------------------
+// number formats
+// ---------------------------------------------------------------------------------------
+CSAHCA_DEV float bf16_to_f32(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
+
+// round to nearest even; inputs are finite
+CSAHCA_DEV uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+CSAHCA_DEV uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// Order-preserving map of a float score to an unsigned key (larger score -> larger key);
+// -0.0 is folded onto +0.0 so that the two compare equal.
+CSAHCA_DEV uint32_t score_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+CSAHCA_DEV float key_score(uint32_t k) {
+  uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+  return __uint_as_float(u);
+}
+
+// 64-bit selection key: score first, then the LOWER index wins among equal scores.
+// Every visible entry maps to a distinct nonzero key; 0 marks "no entry".
+CSAHCA_DEV uint64_t entry_key(float score, uint32_t idx) {
+  return ((uint64_t)score_key(score) << 32) | (uint64_t)(0xFFFFFFFFu - idx);
+}
+
+CSAHCA_DEV uint32_t key_index(uint64_t key) { return 0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFu); }
+
+// ---------------------------------------------------------------------------------------
+// wave-level helpers (wave64)
+// ---------------------------------------------------------------------------------------
+CSAHCA_DEV float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
+
+CSAHCA_DEV uint64_t shfl_xor_u64(uint64_t v, int m) {
+  uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  lo = __shfl_xor(lo, m, 64);
+  hi = __shfl_xor(hi, m, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+CSAHCA_DEV uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// ceil-div for host and device
+template <typename T>
+__host__ __device__ inline T cdiv(T a, T b) {
+  return (a + b - 1) / b;
+}

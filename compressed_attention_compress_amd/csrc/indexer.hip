@@ -1,0 +1,586 @@
+// Kernel 2: lightning-indexer scores and exact top-k selection.
+//
+// Source: "DeepSeek-V4 Hybrid Attention: CSA, HCA, mHC, MoE", section V.2: the score of
+// compressed block s for query t is sum_h w_{t,h} * ReLU(q_{t,h} . K_s) over the indexer
+// heads, and the selector keeps the k best blocks; "DeepSeek-V4: Anatomy of an
+// Open-Source Frontier Model" (lesson 6.7): the indexer runs in low precision and can
+// pick no more entries than exist.
+//
+// Scoring (index_score_fp8): the q_I . K_I contraction runs on MFMA
+// (v_mfma_f32_16x16x32_fp8_fp8; A = 16 indexer heads x 32 dims, B = 32 dims x 16 keys).
+// Each lane streams 32 contiguous bytes of one key row straight from HBM into the B
+// operand (no LDS); the dimension order inside the contraction is permuted identically
+// for A and B, which leaves the dot products unchanged.  ReLU, the head weights and the
+// cross-head sum are applied to the MFMA accumulators in registers.  Every score is
+// written once (fp32) and every group of 16 consecutive keys also writes its maximum
+// 64-bit selection key.
+//
+// Selection (select_topk): one workgroup per query.  Selection keys are
+// (order-preserving score bits << 32) | (~index), so all keys are distinct and "larger
+// key" means "better, lower index on ties".  Let T1 be the K-th largest group maximum.
+// At least K keys are >= T1 (one per selected group), so the K-th largest key overall is
+// >= T1 and every top-K key lies in one of exactly K selected groups.  The exact top-K is
+// then taken from those K*16 candidates.  Both K-th-largest searches are MSB-first radix
+// selects over LDS that skip the bits all remaining candidates share.  The candidates are
+// kept in index order, so the output comes out ascending without a sort.
+#include "common.hpp"
+
+namespace {
+
+constexpr int GROUP = 16;           // keys per group maximum
+constexpr int SEL_THREADS = 1024;
+constexpr int SEL_MAX_KEYS = 16384; // LDS capacity of the selector (128 KiB of keys)
+constexpr int MAX_NC = GROUP * SEL_MAX_KEYS;
+constexpr int MAX_K = SEL_MAX_KEYS / GROUP;
+
+CSAHCA_DEV int visible_entries(const int* q_pos, int b, int t, int m, int N_c) {
+  const long long p = (long long)q_pos[b] + t;
+  long long v = (p + 1) / m;
+  if (p + 1 <= 0) v = 0;
+  return (int)(v < N_c ? v : N_c);
+}
+
+// ---------------------------------------------------------------------------------------
+// scoring, FP8 E4M3FN keys on MFMA
+// ---------------------------------------------------------------------------------------
+template <int C_I>
+struct KeySlice {  // the C_I/4 contiguous bytes one lane holds: KS 8-byte MFMA operands
+  static constexpr int KS = C_I / 32;
+  long v[KS];
+  CSAHCA_DEV void load(const uint8_t* p) {
+    if constexpr (KS == 4) {
+      const u32x4 a = *reinterpret_cast<const u32x4*>(p);
+      const u32x4 b = *reinterpret_cast<const u32x4*>(p + 16);
+      v[0] = (long)(((uint64_t)a[1] << 32) | a[0]);
+      v[1] = (long)(((uint64_t)a[3] << 32) | a[2]);
+      v[2] = (long)(((uint64_t)b[1] << 32) | b[0]);
+      v[3] = (long)(((uint64_t)b[3] << 32) | b[2]);
+    } else if constexpr (KS == 2) {
+      const u32x4 a = *reinterpret_cast<const u32x4*>(p);
+      v[0] = (long)(((uint64_t)a[1] << 32) | a[0]);
+      v[1] = (long)(((uint64_t)a[3] << 32) | a[2]);
+    } else {
+      const u32x2 a = *reinterpret_cast<const u32x2*>(p);
+      v[0] = (long)(((uint64_t)a[1] << 32) | a[0]);
+    }
+  }
+  CSAHCA_DEV void zero() {
+#pragma unroll
+    for (int i = 0; i < KS; ++i) v[i] = 0;
+  }
+};
+
+// QPW queries per workgroup of 4 waves.  QPW = 1: the four waves split the key blocks of
+// one query (decode).  QPW = 4: each wave scores its own query over the same key blocks
+// (prefill; the repeated key reads hit in cache).
+template <int C_I, int HB, int QPW, int U>
+__global__ __launch_bounds__(256) void index_score_fp8(
+    const uint8_t* __restrict__ qI, const float* __restrict__ w, const uint8_t* __restrict__ KI,
+    const int* __restrict__ q_pos, int m, int Tq, int N_c, int CH, int nq, int NG,
+    float* __restrict__ scores, uint64_t* __restrict__ gkeys) {
+  constexpr int KS = C_I / 32;
+  constexpr int NIH = HB * 16;
+  constexpr int WPQ = 4 / QPW;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int q = blockIdx.y * QPW + wave / WPQ;
+  const int sub = wave % WPQ;
+  if (q >= nq) return;  // this kernel has no barriers: a finished wave may leave
+  const int b = q / Tq, t = q - b * Tq;
+  const int V = visible_entries(q_pos, b, t, m, N_c);
+  const int e_begin = blockIdx.x * CH;
+  const int e_end = min(e_begin + CH, V);
+  if (e_begin >= e_end) return;
+
+  const int row = lane & 15, g = lane >> 4;
+  // A operand: indexer query of head (16*hb + row), dims [g*C_I/4, (g+1)*C_I/4)
+  KeySlice<C_I> a[HB];
+  const uint8_t* qp = qI + (size_t)q * NIH * C_I;
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) a[hb].load(qp + (hb * 16 + row) * C_I + g * (C_I / 4));
+  // head weights of the accumulator rows this lane holds: heads 16*hb + 4*g + i
+  float wr[HB][4];
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wr[hb][i] = w[(size_t)q * NIH + hb * 16 + 4 * g + i];
+
+  const uint8_t* kb = KI + (size_t)b * N_c * C_I;
+  float* srow = scores + (size_t)q * N_c;
+  uint64_t* grow = gkeys + (size_t)q * NG;
+  const int nblk = cdiv(e_end - e_begin, GROUP);
+
+  for (int blk0 = sub; blk0 < nblk; blk0 += WPQ * U) {
+    KeySlice<C_I> kf[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int e = e_begin + (blk0 + u * WPQ) * GROUP + row;
+      if (blk0 + u * WPQ < nblk && e < e_end)
+        kf[u].load(kb + (size_t)e * C_I + g * (C_I / 4));
+      else
+        kf[u].zero();
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int blk = blk0 + u * WPQ;
+      if (blk >= nblk) break;  // wave-uniform
+      f32x4 acc[HB];
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) acc[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb)
+          acc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a[hb].v[ks], kf[u].v[ks],
+                                                                acc[hb], 0, 0, 0);
+      // lane holds key (row) for heads 16*hb + 4*g + i
+      float part = 0.f;
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) part = fmaf(wr[hb][i], fmaxf(acc[hb][i], 0.f), part);
+      part += shfl_xor_f(part, 16);
+      part += shfl_xor_f(part, 32);
+      const int e0 = e_begin + blk * GROUP;
+      const int e = e0 + row;
+      const bool valid = e < e_end;
+      if (g == 0 && valid) srow[e] = part;
+      uint64_t key = valid ? entry_key(part, (uint32_t)e) : 0ull;
+      key = umax64(key, shfl_xor_u64(key, 1));
+      key = umax64(key, shfl_xor_u64(key, 2));
+      key = umax64(key, shfl_xor_u64(key, 4));
+      key = umax64(key, shfl_xor_u64(key, 8));
+      if (lane == 0) grow[e0 / GROUP] = key;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// scoring, float32 keys (small heads; plain FMA)
+// ---------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void index_score_f32(
+    const float* __restrict__ qI, const float* __restrict__ w, const float* __restrict__ KI,
+    const int* __restrict__ q_pos, int m, int Tq, int N_c, int n_ih, int c_I, int NG,
+    float* __restrict__ scores, uint64_t* __restrict__ gkeys) {
+  extern __shared__ float smem_f[];
+  float* qs = smem_f;               // [n_ih * c_I]
+  float* ws = smem_f + n_ih * c_I;  // [n_ih]
+  const int q = blockIdx.y;
+  const int b = q / Tq, t = q - b * Tq;
+  for (int i = threadIdx.x; i < n_ih * c_I; i += blockDim.x) qs[i] = qI[(size_t)q * n_ih * c_I + i];
+  for (int i = threadIdx.x; i < n_ih; i += blockDim.x) ws[i] = w[(size_t)q * n_ih + i];
+  __syncthreads();
+  const int V = visible_entries(q_pos, b, t, m, N_c);
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;  // blockDim is a multiple of 16
+  const bool valid = e < V;
+  float s = 0.f;
+  if (valid) {
+    const float* kr = KI + ((size_t)b * N_c + e) * c_I;
+    for (int h = 0; h < n_ih; ++h) {
+      float d = 0.f;
+      for (int j = 0; j < c_I; ++j) d = fmaf(qs[h * c_I + j], kr[j], d);
+      s = fmaf(ws[h], fmaxf(d, 0.f), s);
+    }
+    scores[(size_t)q * N_c + e] = s;
+  }
+  uint64_t key = valid ? entry_key(s, (uint32_t)e) : 0ull;
+  key = umax64(key, shfl_xor_u64(key, 1));
+  key = umax64(key, shfl_xor_u64(key, 2));
+  key = umax64(key, shfl_xor_u64(key, 4));
+  key = umax64(key, shfl_xor_u64(key, 8));
+  if ((threadIdx.x & 15) == 0 && e < V) gkeys[(size_t)q * NG + e / GROUP] = key;
+}
+
+// ---------------------------------------------------------------------------------------
+// selection
+// ---------------------------------------------------------------------------------------
+struct SelScratch {
+  uint32_t hist[256];
+  uint64_t red_and[SEL_THREADS / 64];
+  uint64_t red_or[SEL_THREADS / 64];
+  uint32_t scan[SEL_THREADS / 64];
+  uint32_t found_digit;
+  uint32_t found_kth;
+  uint32_t total;
+};
+
+// exclusive prefix sum of v over the workgroup, in thread order; also returns the total
+CSAHCA_DEV uint32_t block_exclusive_scan(uint32_t v, SelScratch& sc, uint32_t& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) sc.scan[wave] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t run = 0;
+    for (int i = 0; i < SEL_THREADS / 64; ++i) {
+      const uint32_t tmp = sc.scan[i];
+      sc.scan[i] = run;
+      run += tmp;
+    }
+    sc.total = run;
+  }
+  __syncthreads();
+  total = sc.total;
+  const uint32_t res = sc.scan[wave] + x - v;
+  __syncthreads();
+  return res;
+}
+
+// K-th largest (1-based) of n distinct keys in LDS.
+CSAHCA_DEV uint64_t radix_select_kth(const uint64_t* keys, int n, int kth, SelScratch& sc) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint64_t prefix = 0, mask = 0;
+  for (;;) {
+    uint64_t a = ~0ull, o = 0ull;
+    for (int i = threadIdx.x; i < n; i += SEL_THREADS) {
+      const uint64_t k = keys[i];
+      if ((k & mask) == prefix) {
+        a &= k;
+        o |= k;
+      }
+    }
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      a &= shfl_xor_u64(a, d);
+      o |= shfl_xor_u64(o, d);
+    }
+    if (lane == 0) {
+      sc.red_and[wave] = a;
+      sc.red_or[wave] = o;
+    }
+    __syncthreads();
+    a = ~0ull;
+    o = 0ull;
+#pragma unroll
+    for (int i = 0; i < SEL_THREADS / 64; ++i) {
+      a &= sc.red_and[i];
+      o |= sc.red_or[i];
+    }
+    const uint64_t diff = a ^ o;
+    if (diff == 0ull) {
+      __syncthreads();
+      return a;  // one key left
+    }
+    const int hb = 63 - __builtin_clzll(diff);
+    const int sh = hb >= 7 ? hb - 7 : 0;
+    for (int i = threadIdx.x; i < 256; i += SEL_THREADS) sc.hist[i] = 0;
+    __syncthreads();
+    for (int i = threadIdx.x; i < n; i += SEL_THREADS) {
+      const uint64_t k = keys[i];
+      if ((k & mask) == prefix) atomicAdd(&sc.hist[(uint32_t)(k >> sh) & 255u], 1u);
+    }
+    __syncthreads();
+    if (wave == 0) {
+      // lane owns bins 4*lane .. 4*lane+3; count the keys in higher bins
+      uint32_t h[4];
+      uint32_t local = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        h[j] = sc.hist[4 * lane + j];
+        local += h[j];
+      }
+      uint32_t suf = local;  // inclusive suffix sum over lanes >= this one
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t y = __shfl_down(suf, d, 64);
+        if (lane + d < 64) suf += y;
+      }
+      uint32_t above = suf - local;
+#pragma unroll
+      for (int j = 3; j >= 0; --j) {
+        if (above < (uint32_t)kth && (uint32_t)kth <= above + h[j]) {
+          sc.found_digit = 4 * lane + j;
+          sc.found_kth = kth - above;
+        }
+        above += h[j];
+      }
+    }
+    __syncthreads();
+    const uint32_t dsel = sc.found_digit;
+    kth = (int)sc.found_kth;
+    const uint64_t hi_mask = hb == 63 ? 0ull : (~0ull << (hb + 1));
+    prefix = (a & hi_mask) | ((uint64_t)dsel << sh);
+    mask = ~0ull << sh;
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(SEL_THREADS) void select_topk(
+    const float* __restrict__ scores, const uint64_t* __restrict__ gkeys,
+    const int* __restrict__ q_pos, int m, int Tq, int N_c, int NG, int k,
+    int* __restrict__ topk_idx, float* __restrict__ topk_score) {
+  extern __shared__ uint64_t sel_keys[];  // [SEL cap]
+  __shared__ SelScratch sc;
+  __shared__ int glist[MAX_K];
+  const int q = blockIdx.x;
+  const int b = q / Tq, t = q - b * Tq;
+  const int V = visible_entries(q_pos, b, t, m, N_c);
+  const int keff = min(k, V);
+  const float* srow = scores + (size_t)q * N_c;
+  int* orow = topk_idx + (size_t)q * k;
+  float* osc = topk_score ? topk_score + (size_t)q * k : nullptr;
+
+  if (keff == V) {  // everything usable is selected
+    for (int i = threadIdx.x; i < k; i += SEL_THREADS) {
+      orow[i] = i < V ? i : -1;
+      if (osc) osc[i] = i < V ? srow[i] : -INFINITY;
+    }
+    return;
+  }
+  const int ng = cdiv(V, GROUP);
+  const uint64_t* grow = gkeys + (size_t)q * NG;
+  for (int i = threadIdx.x; i < ng; i += SEL_THREADS) sel_keys[i] = grow[i];
+  __syncthreads();
+  // With fewer groups than K every group is a candidate (T1 = 0 keeps every usable key).
+  const uint64_t T1 = keff < ng ? radix_select_kth(sel_keys, ng, keff, sc) : 0ull;
+
+  // exactly min(K, ng) groups have a maximum >= T1; list them in index order
+  uint32_t ngl;
+  {
+    const int per = cdiv(ng, SEL_THREADS);
+    const int lo = min(ng, (int)threadIdx.x * per), hi = min(ng, lo + per);
+    uint32_t cnt = 0;
+    for (int i = lo; i < hi; ++i) cnt += sel_keys[i] >= T1;
+    uint32_t off = block_exclusive_scan(cnt, sc, ngl);
+    for (int i = lo; i < hi; ++i)
+      if (sel_keys[i] >= T1) glist[off++] = i;
+    __syncthreads();
+  }
+  // candidates: the keys >= T1 inside the selected groups, in index order
+  constexpr int CPT = SEL_MAX_KEYS / SEL_THREADS;  // candidates per thread (<= 16)
+  uint32_t n2;
+  {
+    const int nc = (int)ngl * GROUP;
+    const int per = cdiv(nc, SEL_THREADS);
+    const int lo = min(nc, (int)threadIdx.x * per), hi = min(nc, lo + per);
+    uint64_t mine[CPT];
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      mine[j] = 0ull;
+      const int i = lo + j;
+      if (i < hi) {
+        const int e = glist[i / GROUP] * GROUP + (i % GROUP);
+        if (e < V) {
+          const uint64_t key = entry_key(srow[e], (uint32_t)e);
+          if (key >= T1) {
+            mine[j] = key;
+            ++cnt;
+          }
+        }
+      }
+    }
+    uint32_t off = block_exclusive_scan(cnt, sc, n2);
+#pragma unroll
+    for (int j = 0; j < CPT; ++j)
+      if (mine[j] != 0ull) sel_keys[off++] = mine[j];
+    __syncthreads();
+  }
+  const uint64_t T2 = radix_select_kth(sel_keys, (int)n2, keff, sc);
+  {
+    const int per = cdiv((int)n2, SEL_THREADS);
+    const int lo = min((int)n2, (int)threadIdx.x * per), hi = min((int)n2, lo + per);
+    uint32_t cnt = 0;
+    for (int i = lo; i < hi; ++i) cnt += sel_keys[i] >= T2;
+    uint32_t total;
+    uint32_t off = block_exclusive_scan(cnt, sc, total);
+    for (int i = lo; i < hi; ++i) {
+      const uint64_t key = sel_keys[i];
+      if (key >= T2) {
+        orow[off] = (int)key_index(key);
+        if (osc) osc[off] = key_score((uint32_t)(key >> 32));
+        ++off;
+      }
+    }
+  }
+  for (int i = keff + threadIdx.x; i < k; i += SEL_THREADS) {
+    orow[i] = -1;
+    if (osc) osc[i] = -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------------------
+struct WsLayout {
+  size_t gkeys_off, gkeys_bytes, scores_off, scores_bytes, total;
+};
+
+WsLayout ws_layout(long long nq, int N_c) {
+  WsLayout L;
+  const long long NG = cdiv<long long>(N_c, GROUP);
+  L.gkeys_off = 0;
+  L.gkeys_bytes = csahca::align_up((size_t)(nq * NG * 8), 256);
+  L.scores_off = L.gkeys_bytes;
+  L.scores_bytes = csahca::align_up((size_t)(nq * (long long)N_c * 4), 256);
+  L.total = L.scores_off + L.scores_bytes;
+  return L;
+}
+
+int check_common(const void* q_idx, const float* w_idx, const void* k_idx, int idx_dtype,
+                 const int* q_pos, int m, int B, int Tq, int n_ih, int c_I, int N_c, int k) {
+  using namespace csahca;
+  if (!q_idx || !w_idx || !k_idx || !q_pos)
+    return fail(CSAHCA_EINVAL, "indexer: q_idx, w_idx, k_idx and q_pos must be non-NULL");
+  if (B < 1 || Tq < 1 || n_ih < 1 || c_I < 1 || N_c < 1 || m < 1 || k < 1)
+    return fail(CSAHCA_EINVAL, "indexer: B, Tq, n_ih, c_I, N_c, m and k must be >= 1");
+  if (N_c > MAX_NC) return fail(CSAHCA_ENOTSUP, "indexer: N_c above 262144 is not built");
+  if (k > MAX_K) return fail(CSAHCA_ENOTSUP, "indexer: k above 1024 is not built");
+  if ((long long)B * Tq > 0x7FFFFFFFLL / 2) return fail(CSAHCA_ENOTSUP, "indexer: too many queries");
+  if (idx_dtype == CSAHCA_FP8_E4M3FN) {
+    if (n_ih % 16 != 0 || n_ih > 128)
+      return fail(CSAHCA_ENOTSUP, "indexer: FP8 keys need n_ih % 16 == 0 and n_ih <= 128");
+    if (c_I != 32 && c_I != 64 && c_I != 128)
+      return fail(CSAHCA_ENOTSUP, "indexer: FP8 keys need c_I in {32, 64, 128}");
+  } else if (idx_dtype == CSAHCA_F32) {
+    if (n_ih * c_I > 4096)
+      return fail(CSAHCA_ENOTSUP, "indexer: float32 keys need n_ih * c_I <= 4096");
+  } else {
+    return fail(CSAHCA_ENOTSUP, "indexer: idx_dtype must be CSAHCA_FP8_E4M3FN or CSAHCA_F32");
+  }
+  if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(w_idx))
+    return fail(CSAHCA_EINVAL, "indexer: q_idx, w_idx and k_idx must be 16-byte aligned");
+  return CSAHCA_OK;
+}
+
+template <int C_I, int HB>
+void launch_fp8(const void* q_idx, const float* w_idx, const void* k_idx, const int* q_pos,
+                int m, int Tq, int N_c, int nq, int NG, float* scores, uint64_t* gkeys,
+                hipStream_t st) {
+  const bool decode = Tq == 1;
+  const int QPW = decode ? 1 : 4;
+  const int qgroups = cdiv(nq, QPW);
+  int chunks = cdiv(2048, qgroups);
+  chunks = max(1, min(chunks, cdiv(N_c, 256)));
+  const int CH = cdiv(cdiv(N_c, chunks), 64) * 64;
+  chunks = cdiv(N_c, CH);
+  dim3 grid((unsigned)chunks, (unsigned)qgroups);
+  if (decode)
+    hipLaunchKernelGGL((index_score_fp8<C_I, HB, 1, 8>), grid, dim3(256), 0, st,
+                       (const uint8_t*)q_idx, w_idx, (const uint8_t*)k_idx, q_pos, m, Tq, N_c,
+                       CH, nq, NG, scores, gkeys);
+  else
+    hipLaunchKernelGGL((index_score_fp8<C_I, HB, 4, 4>), grid, dim3(256), 0, st,
+                       (const uint8_t*)q_idx, w_idx, (const uint8_t*)k_idx, q_pos, m, Tq, N_c,
+                       CH, nq, NG, scores, gkeys);
+}
+
+template <int C_I>
+bool launch_fp8_heads(int n_ih, const void* q_idx, const float* w_idx, const void* k_idx,
+                      const int* q_pos, int m, int Tq, int N_c, int nq, int NG, float* scores,
+                      uint64_t* gkeys, hipStream_t st) {
+  switch (n_ih / 16) {
+    case 1: launch_fp8<C_I, 1>(q_idx, w_idx, k_idx, q_pos, m, Tq, N_c, nq, NG, scores, gkeys, st); return true;
+    case 2: launch_fp8<C_I, 2>(q_idx, w_idx, k_idx, q_pos, m, Tq, N_c, nq, NG, scores, gkeys, st); return true;
+    case 4: launch_fp8<C_I, 4>(q_idx, w_idx, k_idx, q_pos, m, Tq, N_c, nq, NG, scores, gkeys, st); return true;
+    case 8: launch_fp8<C_I, 8>(q_idx, w_idx, k_idx, q_pos, m, Tq, N_c, nq, NG, scores, gkeys, st); return true;
+    default: return false;
+  }
+}
+
+int score_impl(const void* q_idx, const float* w_idx, const void* k_idx, int idx_dtype,
+               const int* q_pos, int m, int B, int Tq, int n_ih, int c_I, int N_c,
+               float* scores, uint64_t* gkeys, hipStream_t st) {
+  using namespace csahca;
+  const int nq = B * Tq;
+  const int NG = cdiv(N_c, GROUP);
+  if (idx_dtype == CSAHCA_FP8_E4M3FN) {
+    bool ok = false;
+    if (c_I == 128) ok = launch_fp8_heads<128>(n_ih, q_idx, w_idx, k_idx, q_pos, m, Tq, N_c, nq, NG, scores, gkeys, st);
+    else if (c_I == 64) ok = launch_fp8_heads<64>(n_ih, q_idx, w_idx, k_idx, q_pos, m, Tq, N_c, nq, NG, scores, gkeys, st);
+    else ok = launch_fp8_heads<32>(n_ih, q_idx, w_idx, k_idx, q_pos, m, Tq, N_c, nq, NG, scores, gkeys, st);
+    if (!ok) return fail(CSAHCA_ENOTSUP, "indexer: FP8 keys need n_ih in {16, 32, 64, 128}");
+  } else {
+    const size_t lds = (size_t)(n_ih * c_I + n_ih) * sizeof(float);
+    dim3 grid((unsigned)cdiv(N_c, 256), (unsigned)nq);
+    hipLaunchKernelGGL(index_score_f32, grid, dim3(256), lds, st, (const float*)q_idx, w_idx,
+                       (const float*)k_idx, q_pos, m, Tq, N_c, n_ih, c_I, NG, scores, gkeys);
+  }
+  return launch_status("lightning_index_score");
+}
+
+int select_impl(const float* scores, const uint64_t* gkeys, const int* q_pos, int m, int B,
+                int Tq, int N_c, int k, int* topk_idx, float* topk_score, hipStream_t st) {
+  using namespace csahca;
+  const int nq = B * Tq;
+  const int NG = cdiv(N_c, GROUP);
+  const int cap = max(NG, min(k, N_c) * GROUP);
+  const size_t lds = (size_t)min(cap, SEL_MAX_KEYS) * sizeof(uint64_t);
+  static bool attr_set = false;
+  if (!attr_set) {
+    if (hipFuncSetAttribute((const void*)select_topk, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            SEL_MAX_KEYS * (int)sizeof(uint64_t)) != hipSuccess)
+      return fail(CSAHCA_ELAUNCH, "lightning_index_select: cannot raise the LDS limit");
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(select_topk, dim3((unsigned)nq), dim3(SEL_THREADS), lds, st, scores,
+                     gkeys, q_pos, m, Tq, N_c, NG, k, topk_idx, topk_score);
+  return launch_status("lightning_index_select");
+}
+
+}  // namespace
+
+extern "C" size_t lightning_index_topk_workspace_size(int B, int Tq, int n_ih, int N_c, int k) {
+  (void)n_ih;
+  (void)k;
+  if (B < 1 || Tq < 1 || N_c < 1) return 0;
+  return ws_layout((long long)B * Tq, N_c).total;
+}
+
+extern "C" int lightning_index_score(const void* q_idx, const float* w_idx, const void* k_idx,
+                                     int idx_dtype, const int* q_pos, int m, int B, int Tq,
+                                     int n_ih, int c_I, int N_c, int k, float* scores,
+                                     void* workspace, size_t ws_bytes, void* stream) {
+  using namespace csahca;
+  int st = check_common(q_idx, w_idx, k_idx, idx_dtype, q_pos, m, B, Tq, n_ih, c_I, N_c, k);
+  if (st != CSAHCA_OK) return st;
+  if (!scores) return fail(CSAHCA_EINVAL, "lightning_index_score: scores must be non-NULL");
+  const WsLayout L = ws_layout((long long)B * Tq, N_c);
+  if (!workspace || ws_bytes < L.total)
+    return fail(CSAHCA_EWORKSPACE, "lightning_index_score: workspace missing or too small");
+  return score_impl(q_idx, w_idx, k_idx, idx_dtype, q_pos, m, B, Tq, n_ih, c_I, N_c, scores,
+                    (uint64_t*)((char*)workspace + L.gkeys_off), (hipStream_t)stream);
+}
+
+extern "C" int lightning_index_select(const float* scores, const int* q_pos, int m, int B,
+                                      int Tq, int N_c, int k, int* topk_idx, float* topk_score,
+                                      void* workspace, size_t ws_bytes, void* stream) {
+  using namespace csahca;
+  if (!scores || !q_pos || !topk_idx)
+    return fail(CSAHCA_EINVAL, "lightning_index_select: scores, q_pos and topk_idx must be non-NULL");
+  if (B < 1 || Tq < 1 || N_c < 1 || m < 1 || k < 1)
+    return fail(CSAHCA_EINVAL, "lightning_index_select: B, Tq, N_c, m and k must be >= 1");
+  if (N_c > MAX_NC || k > MAX_K)
+    return fail(CSAHCA_ENOTSUP, "lightning_index_select: N_c <= 262144 and k <= 1024 are built");
+  const WsLayout L = ws_layout((long long)B * Tq, N_c);
+  if (!workspace || ws_bytes < L.total)
+    return fail(CSAHCA_EWORKSPACE, "lightning_index_select: workspace missing or too small");
+  return select_impl(scores, (const uint64_t*)((char*)workspace + L.gkeys_off), q_pos, m, B, Tq,
+                     N_c, k, topk_idx, topk_score, (hipStream_t)stream);
+}
+
+extern "C" int lightning_index_topk(const void* q_idx, const float* w_idx, const void* k_idx,
+                                    int idx_dtype, const int* q_pos, int m, int B, int Tq,
+                                    int n_ih, int c_I, int N_c, int k, int* topk_idx,
+                                    float* topk_score, float* all_scores, void* workspace,
+                                    size_t ws_bytes, void* stream) {
+  using namespace csahca;
+  int st = check_common(q_idx, w_idx, k_idx, idx_dtype, q_pos, m, B, Tq, n_ih, c_I, N_c, k);
+  if (st != CSAHCA_OK) return st;
+  if (!topk_idx) return fail(CSAHCA_EINVAL, "lightning_index_topk: topk_idx must be non-NULL");
+  const WsLayout L = ws_layout((long long)B * Tq, N_c);
+  if (!workspace || ws_bytes < L.total)
+    return fail(CSAHCA_EWORKSPACE, "lightning_index_topk: workspace missing or too small");
+  if (all_scores && !aligned16(all_scores))
+    return fail(CSAHCA_EINVAL, "lightning_index_topk: all_scores must be 16-byte aligned");
+  float* scores = all_scores ? all_scores : (float*)((char*)workspace + L.scores_off);
+  uint64_t* gkeys = (uint64_t*)((char*)workspace + L.gkeys_off);
+  hipStream_t s = (hipStream_t)stream;
+  st = score_impl(q_idx, w_idx, k_idx, idx_dtype, q_pos, m, B, Tq, n_ih, c_I, N_c, scores, gkeys, s);
+  if (st != CSAHCA_OK) return st;
+  return select_impl(scores, gkeys, q_pos, m, B, Tq, N_c, k, topk_idx, topk_score, s);
+}

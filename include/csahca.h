@@ -1,0 +1,189 @@
+/*
+ * csahca.h -- C ABI of the MI355X (gfx950) compressed-attention library (libcsahca.so).
+ *
+ * DeepSeek-V4 compressed attention as the pages describe it:
+ *   CSA  (Compressed Sparse Attention): pool every m raw KV tokens into one entry with
+ *        softmax-gated weights, score every usable entry with the lightning indexer, keep
+ *        the top-k, and run multi-query attention over them plus a sliding window of raw
+ *        tokens.
+ *   HCA  (Heavily Compressed Attention): pool every m' tokens and attend to every usable
+ *        entry plus the same window.
+ * Sources, cited by page and section:
+ *   "DeepSeek-V4 Hybrid Attention: CSA, HCA, mHC, MoE" (trishampatil.com): section IV,
+ *     V.1 (compression), V.2 (lightning indexer, equation I_{t,s}), V.3 (core attention),
+ *     VI (HCA, equation o_{t,i}).
+ *   "DeepSeek-V4: Anatomy of an Open-Source Frontier Model" (modernaiengineering.com
+ *     lesson 6.7): "Hybrid attention with CSA and HCA", "One query in a CSA layer, step by
+ *     step", "Worked example, step by step".
+ *   "DeepSeek-V4 Architecture From Kernels ... C-Kernel-Engine" (shivasnotes.com):
+ *     section 6 (CSA attention reference contract: index input, explicit scale), section 9
+ *     (heterogeneous KV cache: compressed entries, tails, window, indexer cache).
+ *
+ * Conventions for every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller, row-major and
+ *     contiguous in the shapes given, 16-byte aligned.  The library never allocates,
+ *     frees or synchronises; every kernel is enqueued on `stream` (a hipStream_t, NULL =
+ *     the default stream) in call order.
+ *   - Scratch memory is a caller-owned device `workspace` of at least the size that the
+ *     matching *_workspace_size() returns for the same shape arguments.
+ *   - Every argument is validated on the host before anything is enqueued.  On error the
+ *     call returns a negative status, enqueues nothing and records a message readable
+ *     with csahca_last_error().  Values stored in device memory (positions, indices) are
+ *     not inspected on the host; their documented ranges are the caller's contract, and
+ *     the kernels never read outside the buffers whatever those values are.
+ *   - Positions: q_pos[b] (device int32) is the absolute position of query token 0 of
+ *     sequence b; query token t sits at p = q_pos[b] + t.  Compressed entry s of a cache
+ *     with block size m covers raw positions m*s .. m*s+m-1 and is usable by p iff
+ *     m*(s+1)-1 <= p (the block is complete) and s < the cache length.
+ *   - The sliding window of the query at p is raw positions max(0, p-W+1) .. p (the query's
+ *     own token included).  Window rows come from win_kv [B, L, c], whose row 0 is raw
+ *     position win_pos[b]; positions outside win_pos[b] .. win_pos[b]+L-1 are skipped.
+ *   - Scores, softmax and accumulation are float32 on the GPU.  bfloat16 results are
+ *     rounded to nearest even.
+ */
+#ifndef CSAHCA_H
+#define CSAHCA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element types */
+#define CSAHCA_F32 0
+#define CSAHCA_BF16 1
+#define CSAHCA_FP8_E4M3FN 2 /* OCP FP8: 4 exponent bits (bias 7), 3 mantissa bits, no inf */
+
+/* status codes */
+#define CSAHCA_OK 0
+#define CSAHCA_EINVAL (-1)     /* a pointer, size or value is invalid                  */
+#define CSAHCA_ENOTSUP (-2)    /* valid, but outside the shapes / types built here      */
+#define CSAHCA_EWORKSPACE (-3) /* workspace missing or smaller than *_workspace_size() */
+#define CSAHCA_ELAUNCH (-4)    /* the HIP runtime refused a launch                      */
+
+/*
+ * csa_compress / hca_compress -- softmax-gated block pooling.
+ * Source: trishampatil.com section V.1 (equation C_i^comp) and VI (non-overlapping m'
+ * blocks); shivasnotes.com section 6 ("blockwise softmax plus weighted reduction").
+ *
+ *   out[b, i, ch] = sum_{j<m} S[b,i,j,ch] * kv[b, m*i+j, ch],
+ *   S[b,i,.,ch]   = softmax_j( gate[b, m*i+j, ch] + pos_bias[j, ch] )
+ * for i < n / m (floor: a trailing partial block is not emitted).  The softmax runs over
+ * the m tokens of the block separately for every channel.
+ *
+ *   kv, gate   [B, n, c] of `dtype` (CSAHCA_F32 or CSAHCA_BF16); sequence b starts at
+ *              kv + b * in_bstride elements (same stride for gate); in_bstride >= n*c.
+ *   pos_bias   [m, c] float32, or NULL for zero bias.
+ *   out        [B, n/m, c] of `dtype`; sequence b starts at out + b * out_bstride
+ *              elements, out_bstride >= (n/m)*c.  A cache append is one call on the last
+ *              m tokens with `out` pointing at the new entry.
+ *   Limits: B >= 1, n >= 0, c >= 8 and c % 8 == 0, 1 <= m <= 4096.  With n < m nothing is
+ *   read or written (the pointers may then be NULL).
+ * The two names run the same kernel; they exist so that each branch's call reads as the
+ * pages name it (m = 4 for CSA, m' = 128 for HCA in the V4 settings).
+ */
+int csa_compress(const void* kv, const void* gate, const float* pos_bias, void* out, int B,
+                 int n, int c, int m, int dtype, long long in_bstride, long long out_bstride,
+                 void* stream);
+int hca_compress(const void* kv, const void* gate, const float* pos_bias, void* out, int B,
+                 int n, int c, int m, int dtype, long long in_bstride, long long out_bstride,
+                 void* stream);
+
+/*
+ * lightning_index_topk -- lightning-indexer scores and exact top-k selection.
+ * Source: trishampatil.com section V.2, equation I_{t,s} and the Top-k selector;
+ * modernaiengineering.com "Worked example" (top-k cannot pick more entries than exist).
+ *
+ *   I[b,t,s] = sum_h w_idx[b,t,h] * max(0, sum_d q_idx[b,t,h,d] * k_idx[b,s,d])
+ * for every usable entry s (V = min(N_c, (p+1)/m) of them).  The selection keeps
+ * K = min(k, V) entries with the highest scores; equal scores go to the lower index and
+ * -0.0 counts as +0.0.  topk_idx[b,t,:] lists them in ascending index order, followed by
+ * k-K entries of -1.
+ *
+ *   q_idx      [B, Tq, n_ih, c_I] of idx_dtype (CSAHCA_FP8_E4M3FN or CSAHCA_F32).
+ *   w_idx      [B, Tq, n_ih] float32.
+ *   k_idx      [B, N_c, c_I] of idx_dtype (the compressed indexer-key cache).
+ *   q_pos      [B] int32 device; m = CSA block size of the cache.
+ *   topk_idx   [B, Tq, k] int32 (out).
+ *   topk_score [B, Tq, k] float32 (out, nullable): the selected scores, -inf on padding.
+ *   all_scores [B, Tq, N_c] float32 (out, nullable): every score; entries s >= V are
+ *              left unwritten.
+ *   Limits: FP8 keys need n_ih in {16, 32, 64, 128} and c_I in {32, 64, 128}; F32 keys
+ *   need n_ih * c_I <= 4096.  1 <= k <= 1024, N_c <= 262144.
+ */
+size_t lightning_index_topk_workspace_size(int B, int Tq, int n_ih, int N_c, int k);
+int lightning_index_topk(const void* q_idx, const float* w_idx, const void* k_idx,
+                         int idx_dtype, const int* q_pos, int m, int B, int Tq, int n_ih,
+                         int c_I, int N_c, int k, int* topk_idx, float* topk_score,
+                         float* all_scores, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * The two halves of lightning_index_topk, for callers that time or check them apart.
+ * lightning_index_score writes every usable score to `scores` [B, Tq, N_c] and the
+ * per-16-entry group maxima to the workspace; lightning_index_select must then be given
+ * the same scores, workspace and shape arguments.  Running both equals one
+ * lightning_index_topk call.  Same limits and workspace size.
+ */
+int lightning_index_score(const void* q_idx, const float* w_idx, const void* k_idx,
+                          int idx_dtype, const int* q_pos, int m, int B, int Tq, int n_ih,
+                          int c_I, int N_c, int k, float* scores, void* workspace,
+                          size_t ws_bytes, void* stream);
+int lightning_index_select(const float* scores, const int* q_pos, int m, int B, int Tq,
+                           int N_c, int k, int* topk_idx, float* topk_score, void* workspace,
+                           size_t ws_bytes, void* stream);
+
+/*
+ * csa_attend -- multi-query attention over the selected compressed entries plus the
+ * sliding window, one joint softmax.
+ * Source: trishampatil.com section V.3 (core attention in MQA form over the selected
+ * blocks; one K = V row shared by all heads) and section I (softmax(QK^T/sqrt(c))V);
+ * modernaiengineering.com "One query in a CSA layer", steps 3-5 (selected entries plus the
+ * last 128 raw tokens, attended together).
+ *
+ *   rows(b,t) = { ckv[b, s] : s in topk_idx[b,t,:], s != -1 } followed by the window rows
+ *   out[b,t,h] = sum_r softmax_r(scale * q[b,t,h] . row_r) * row_r
+ *   lse[b,t,h] = log sum_r exp(scale * q[b,t,h] . row_r)   (natural log)
+ *
+ *   q       [B, Tq, n_h, c] of dtype; ckv [B, N_c, c]; topk_idx [B, Tq, k] int32 with
+ *           entries in [0, N_c) or -1 (other values are treated as -1).
+ *   win_kv  [B, L, c]; win_pos [B] int32 device; q_pos [B] int32 device.
+ *   out     [B, Tq, n_h, c] of dtype; lse [B, Tq, n_h] float32 or NULL.
+ *   dtype   CSAHCA_BF16: c == 512, n_h % 16 == 0, n_h <= 128.
+ *           CSAHCA_F32:  c <= 256, c % 4 == 0, n_h * (k + W) <= 12288.
+ *   A query with no row at all (not possible when W >= 1) gets out = 0, lse = -inf.
+ */
+size_t csa_attend_workspace_size(int B, int Tq, int n_h, int c, int k, int W);
+int csa_attend(const void* q, const void* ckv, const int* topk_idx, const void* win_kv,
+               const int* win_pos, const int* q_pos, int B, int Tq, int n_h, int c, int N_c,
+               int k, int L, int W, float scale, int dtype, void* out, float* lse,
+               void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * hca_attend -- multi-query attention over every usable compressed entry plus the window.
+ * Source: trishampatil.com section VI, equation o_{t,i} (query q_{t,i}, key = value =
+ * C^comp, dense over all compressed entries, MQA); modernaiengineering.com "Hybrid
+ * attention with CSA and HCA" (128-token uncompressed window in both layer types).
+ *
+ *   rows(b,t) = { ckv[b, s] : s < min(N_h, (p+1)/m) } followed by the window rows.
+ * Arguments as csa_attend, with m the HCA block size (m') and N_h the cache length.
+ *   dtype   CSAHCA_BF16: c == 512, n_h % 16 == 0, n_h <= 128.
+ *           CSAHCA_F32:  c <= 256, c % 4 == 0, n_h * (N_h + W) <= 12288.
+ */
+size_t hca_attend_workspace_size(int B, int Tq, int n_h, int c, int N_h, int W);
+int hca_attend(const void* q, const void* ckv, const void* win_kv, const int* win_pos,
+               const int* q_pos, int m, int B, int Tq, int n_h, int c, int N_h, int L, int W,
+               float scale, int dtype, void* out, float* lse, void* workspace,
+               size_t ws_bytes, void* stream);
+
+/* Message for the last non-OK status returned on the calling thread ("" if none). */
+const char* csahca_last_error(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int csahca_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSAHCA_H */

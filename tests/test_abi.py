@@ -1,0 +1,120 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects invalid arguments on
+the host before any HIP call (so these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import compressed_attention_compress_amd as lib
+from compressed_attention_compress_amd import EINVAL, ENOTSUP, EWORKSPACE
+from tests.conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "csahca.h")
+FAKE = 1 << 20  # an aligned, never-dereferenced address: validation fails before any use
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\s*\*?\s*([a-z_]+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for want in ("csa_compress", "hca_compress", "lightning_index_topk", "csa_attend",
+                 "hca_attend", "lightning_index_topk_workspace_size",
+                 "csa_attend_workspace_size", "hca_attend_workspace_size", "csahca_last_error"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    h = ctypes.CDLL(lib.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(h, name), name
+    # the binding wraps the same set
+    assert set(declared_functions()) <= set(lib._SIGNATURES)
+    assert lib.version() >= 10000
+
+
+def _status(fn, *args):
+    return getattr(lib.load(), fn)(*args)
+
+
+def test_pool_validation():
+    L = lib.load()
+    assert L.csa_compress(None, None, None, None, 1, 8, 8, 4, 1, 64, 16, None) == EINVAL
+    assert "non-NULL" in lib.last_error()
+    assert L.hca_compress(FAKE, FAKE, None, FAKE, 1, 8, 12, 4, 1, 96, 24, None) == EINVAL  # c % 8
+    assert L.csa_compress(FAKE, FAKE, None, FAKE, 1, 8, 8, 4, 2, 64, 16, None) == ENOTSUP  # fp8
+    assert L.csa_compress(FAKE, FAKE, None, FAKE, 1, 8, 8, 4, 1, 32, 16, None) == EINVAL   # stride
+    assert L.csa_compress(FAKE + 4, FAKE, None, FAKE, 1, 8, 8, 4, 1, 64, 16, None) == EINVAL
+    assert L.csa_compress(FAKE, FAKE, None, FAKE, 1, 8, 8, 0, 1, 64, 16, None) == EINVAL   # m
+    # fewer tokens than one block: nothing to do, pointers may be NULL
+    assert L.csa_compress(None, None, None, None, 1, 3, 8, 4, 1, 24, 0, None) == 0
+
+
+def test_indexer_validation():
+    L = lib.load()
+    B, Tq, n_ih, c_I, N_c, k = 2, 1, 64, 128, 1000, 64
+    ws = L.lightning_index_topk_workspace_size(B, Tq, n_ih, N_c, k)
+    NG = -(-N_c // 16)
+    assert ws == (-(-(B * NG * 8) // 256) * 256) + (-(-(B * N_c * 4) // 256) * 256)
+    args = [FAKE, FAKE, FAKE, 2, FAKE, 4, B, Tq, n_ih, c_I, N_c, k, FAKE, None, None]
+    assert L.lightning_index_topk(*args, FAKE, ws - 1, None) == EWORKSPACE
+    assert L.lightning_index_topk(*args, None, ws, None) == EWORKSPACE
+    bad = list(args)
+    bad[8] = 48 + 8  # n_ih not a multiple of 16
+    assert L.lightning_index_topk(*bad, FAKE, ws, None) == ENOTSUP
+    bad = list(args)
+    bad[9] = 96  # c_I
+    assert L.lightning_index_topk(*bad, FAKE, ws, None) == ENOTSUP
+    bad = list(args)
+    bad[11] = 2048  # k
+    assert L.lightning_index_topk(*bad, FAKE, ws, None) == ENOTSUP
+    bad = list(args)
+    bad[10] = 262144 + 16  # N_c
+    assert L.lightning_index_topk(*bad, FAKE, ws, None) == ENOTSUP
+    bad = list(args)
+    bad[0] = None
+    assert L.lightning_index_topk(*bad, FAKE, ws, None) == EINVAL
+    bad = list(args)
+    bad[3] = 1  # bf16 indexer keys are not a supported type
+    assert L.lightning_index_topk(*bad, FAKE, ws, None) == ENOTSUP
+    assert L.lightning_index_select(None, FAKE, 4, B, Tq, N_c, k, FAKE, None, FAKE, ws, None) == EINVAL
+    assert L.lightning_index_score(*args[:12], None, FAKE, ws, None) == EINVAL
+
+
+def test_attend_validation():
+    L = lib.load()
+    B, Tq, n_h, c, k, W = 2, 1, 64, 512, 512, 128
+    ws = L.csa_attend_workspace_size(B, Tq, n_h, c, k, W)
+    assert ws > 0  # decode with few queries splits the rows
+    base = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, B, Tq, n_h, c, 4096, k, 4096, W]
+    assert L.csa_attend(*base, 0.04, 1, FAKE, None, FAKE, ws - 1, None) == EWORKSPACE
+    assert L.csa_attend(*base, -1.0, 1, FAKE, None, FAKE, ws, None) == EINVAL
+    bad = list(base)
+    bad[9] = 256
+    assert L.csa_attend(*bad, 0.04, 1, FAKE, None, FAKE, ws, None) == ENOTSUP  # bf16 needs 512
+    bad = list(base)
+    bad[8] = 72
+    assert L.csa_attend(*bad, 0.04, 1, FAKE, None, FAKE, ws, None) == ENOTSUP  # n_h % 16
+    bad = list(base)
+    bad[2] = None
+    assert L.csa_attend(*bad, 0.04, 1, FAKE, None, FAKE, ws, None) == EINVAL
+    assert L.csa_attend(*base, 0.04, 2, FAKE, None, FAKE, ws, None) == ENOTSUP  # fp8 attention
+    wh = L.hca_attend_workspace_size(B, Tq, n_h, c, 1024, W)
+    hb = [FAKE, FAKE, FAKE, FAKE, FAKE, 128, B, Tq, n_h, c, 1024, 4096, W]
+    assert L.hca_attend(*hb, 0.04, 1, FAKE, None, FAKE, wh - 1, None) == EWORKSPACE
+    hbad = list(hb)
+    hbad[5] = 0
+    assert L.hca_attend(*hbad, 0.04, 1, FAKE, None, FAKE, wh, None) == EINVAL
+    # float32 path limits
+    assert L.hca_attend(FAKE, FAKE, FAKE, FAKE, FAKE, 128, B, Tq, 8, 512, 1024, 4096, W, 0.1, 0,
+                        FAKE, None, FAKE, wh, None) == ENOTSUP
+
+
+def test_binding_raises_with_message():
+    with pytest.raises(lib.CsaHcaError) as e:
+        lib.csa_compress(None, None, None, None, 1, 8, 8, 4, 1, 64, 16, stream=0)
+    assert e.value.status == EINVAL and "non-NULL" in str(e.value)

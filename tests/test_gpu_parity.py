@@ -1,0 +1,208 @@
+"""GPU parity: every stage of the HIP path against the CPU oracle on identical input bytes.
+
+Stages are compared on the bytes the GPU consumed (staged comparison): attention uses
+the GPU-written compressed cache and the GPU's top-k list, the top-k check uses the
+GPU's own fp32 scores.  Tolerances:
+  pooling    fp32: max |d| <= 1e-5; bf16: |d| <= one bf16 ulp of the fp64 value
+             + 2^-16 * sum_j S_j |x_j| (fp32 rounding of the weighted sum)
+  indexer    |d| <= 1e-3 * max(|ref|, RMS of the query's scores)
+  top-k      bit-exact index lists (ascending, -1 padded) given the GPU scores
+  attention  fp32: max |d| <= 1e-5; bf16: max |d| <= 2e-2 * RMS of the call's output, or
+             for a query with few rows the bf16 rounding bound 2^-7 (|O| + sum_r p_r |v_r|)
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synthgen.configs import BF16, CONFIGS, F32, FP8
+from synthgen.host import make_problem
+from tests import gpu_harness as H
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    H.require_gpu()
+
+
+def bf16_ulp(x):
+    ax = np.maximum(np.abs(x), 2.0 ** -126)
+    return 2.0 ** (np.floor(np.log2(ax)) - 7)
+
+
+def check_pool(Xc, Zc, dtype, m, gpu_out, P=None):
+    B = Xc.shape[0]
+    got = oracle.decode(H.to_host_codes(gpu_out, dtype), dtype)
+    for b in range(B):
+        ref = oracle.pool(oracle.decode(Xc[b], dtype), oracle.decode(Zc[b], dtype), m, P)
+        if dtype == F32:
+            assert np.max(np.abs(got[b] - ref), initial=0.0) <= 1e-5
+        else:
+            # one bf16 ulp of the exact value, plus the fp32 rounding of the weighted sum
+            # (its condition: sum_j S_j |x_j|), which matters only under cancellation
+            cond = oracle.pool(np.abs(oracle.decode(Xc[b], dtype)), oracle.decode(Zc[b], dtype), m, P)
+            bad = np.abs(got[b] - ref) > bf16_ulp(ref) + 2.0 ** -16 * cond
+            assert not bad.any(), f"seq {b}: {bad.sum()} pooled values outside tolerance"
+
+
+def check_index(prob, q_pos, k, idx, sc, alls):
+    cfg = prob["cfg"]
+    qI = oracle.decode(prob["qI"], cfg.idx_dtype)
+    KI = oracle.decode(prob["KI"], cfg.idx_dtype)
+    w = prob["w"]
+    idx = idx.cpu().numpy()
+    sc = sc.cpu().numpy()
+    alls = alls.cpu().numpy()
+    B, Tq = qI.shape[:2]
+    N_c = KI.shape[1]
+    for b in range(B):
+        for t in range(Tq):
+            p = int(q_pos[b]) + t
+            V = oracle.visible(p, cfg.m, N_c)
+            ref = oracle.index_scores(qI[b, t], w[b, t], KI[b], V)
+            g = alls[b, t, :V].astype(np.float64)
+            if V:
+                rms = math.sqrt(float(np.mean(ref * ref)))
+                tol = 1e-3 * np.maximum(np.abs(ref), rms)
+                assert np.all(np.abs(g - ref) <= tol), f"scores b={b} t={t}"
+            want = oracle.topk(g, k)
+            assert np.array_equal(idx[b, t], want), f"top-k b={b} t={t}"
+            keff = min(k, V)
+            assert np.array_equal(sc[b, t, :keff], alls[b, t, want[:keff]])
+            assert np.all(np.isneginf(sc[b, t, keff:]))
+
+
+def check_attend(Qc, dtype, rows_fn, gpu_out, gpu_lse, scale):
+    """rows_fn(b, t) -> fp64 row set for that query (from the GPU-consumed bytes)."""
+    Q = oracle.decode(Qc, dtype)
+    B, Tq = Q.shape[:2]
+    got = oracle.decode(H.to_host_codes(gpu_out, dtype), dtype)
+    lse = gpu_lse.cpu().numpy().astype(np.float64)
+    ref = np.zeros_like(got)
+    ref_abs = np.zeros_like(got)
+    ref_lse = np.zeros(lse.shape)
+    for b in range(B):
+        for t in range(Tq):
+            rows = rows_fn(b, t)
+            ref[b, t], ref_lse[b, t] = oracle.attend(Q[b, t], rows, scale)
+            if dtype != F32 and rows.shape[0]:
+                # the same softmax weights applied to |rows|: scale of the bf16 rounding of P
+                wts = np.exp(scale * Q[b, t] @ rows.T - ref_lse[b, t][:, None])
+                ref_abs[b, t] = wts @ np.abs(rows)
+    err = np.abs(got - ref)
+    if dtype == F32:
+        assert err.max() <= 1e-5, f"attention max |d| = {err.max()}"
+        assert np.max(np.abs(lse - ref_lse)) <= 1e-5
+    else:
+        rms = math.sqrt(float(np.mean(ref * ref)))
+        # 2e-2 x output RMS; for queries with only a few rows (the first tokens of a
+        # sequence) the bf16 rounding of P and O bounds the error by 2^-8 (|O| + sum p|v|)
+        tol = np.maximum(2e-2 * rms, 2.0 ** -7 * (np.abs(ref) + ref_abs))
+        assert np.all(err <= tol), f"attention max |d| = {err.max()}, RMS = {rms}"
+        assert np.max(np.abs(lse - ref_lse)) <= 1e-3
+    return float(err.max())
+
+
+# ---------------------------------------------------------------------------------------
+# cases
+# ---------------------------------------------------------------------------------------
+def small_cases():
+    c1 = CONFIGS[1]
+    c2 = CONFIGS[2]
+    c3 = CONFIGS[3]
+    c4 = CONFIGS[4]
+    c5 = CONFIGS[5]
+    return {
+        "cfg1_tiny_fp32": c1,
+        "hca_h64_ragged": c2.scaled(B=2, n=128 * 21 + 50, seed=21),
+        "hca_h128": c5.scaled(kind="hca_decode", B=1, n=128 * 40 + 3, seed=22, plants=0),
+        "csa_h64_k512": c3.scaled(B=2, n=4 * 900 + 2, seed=23),
+        "csa_h128_k1024": c5.scaled(kind="csa_decode", B=1, n=4 * 2600 + 1, seed=24),
+        "csa_k_ge_visible": c3.scaled(B=2, n=4 * 100, seed=25, plants=4),
+        "prefill_small": c4.scaled(n=4096, Tq=200, seed=26),
+        "prefill_from_zero": c4.scaled(n=0, Tq=40, seed=27, k=8),
+        "pair_h128": c5.scaled(B=2, n=4 * 3000, seed=28, plants=16),
+    }
+
+
+CASES = small_cases()
+
+
+def run_chain(cfg, split_index=False, W=None):
+    """Run every stage on the GPU and check each against the oracle; return outputs."""
+    prob = make_problem(cfg)
+    W = cfg.W if W is None else W
+    B, c, dt = cfg.B, cfg.c, cfg.dtype
+    n_total = prob["n_total"]
+    Tq = prob["Tq"]
+    q_pos_h = prob["q_pos"]
+    q_pos = H.to_dev(q_pos_h)
+    scale = 1.0 / math.sqrt(c)
+    results = {}
+    for layer in ("csa", "hca"):
+        if f"X_{layer}" not in prob:
+            continue
+        m = cfg.m if layer == "csa" else cfg.m_hca
+        Xh, Zh = prob[f"X_{layer}"], prob[f"Z_{layer}"]
+        X, Z = H.to_dev(Xh), H.to_dev(Zh)
+        fn = H.lib.csa_compress if layer == "csa" else H.lib.hca_compress
+        C = H.run_pool(X, Z, m, dt, fn=fn)
+        check_pool(Xh, Zh, dt, m, C)
+        Ch = oracle.decode(H.to_host_codes(C, dt), dt)
+        Xd = oracle.decode(Xh, dt)
+        win_pos = H.to_dev(np.zeros(B, np.int32))
+        Q = H.to_dev(prob[f"Q_{layer}"])
+        if layer == "csa":
+            if C.shape[1] == 0:
+                continue
+            qI, w, KI = H.to_dev(prob["qI"]), H.to_dev(prob["w"]), H.to_dev(prob["KI"])
+            idx, sc, alls = H.run_index(qI, w, KI, q_pos, m, cfg.k, cfg.idx_dtype, split=split_index)
+            check_index(prob, q_pos_h, cfg.k, idx, sc, alls)
+            idx_h = idx.cpu().numpy()
+            out, lse = H.run_csa_attend(Q, C, idx, X, win_pos, q_pos, W, dt)
+            rows = lambda b, t: oracle.csa_rows(Ch[b], idx_h[b, t], Xd[b], 0, int(q_pos_h[b]) + t, W)
+            results["csa_idx"] = idx_h
+            if "plant_positions" in prob:
+                rec = np.mean([np.isin(prob["plant_positions"][b], idx_h[b, 0]).mean() for b in range(B)])
+                results["planted_recall"] = rec
+        else:
+            if C.shape[1] == 0:
+                continue
+            out, lse = H.run_hca_attend(Q, C, X, win_pos, q_pos, m, W, dt)
+            rows = lambda b, t: oracle.hca_rows(Ch[b], m, Xd[b], 0, int(q_pos_h[b]) + t, W)
+        check_attend(prob[f"Q_{layer}"], dt, rows, out, lse, scale)
+        results[f"{layer}_out"] = out.cpu().numpy()
+        results[f"{layer}_lse"] = lse.cpu().numpy()
+        results[f"{layer}_C"] = C.cpu().numpy()
+    return results
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_chain_parity(name):
+    print(f"[case {name}]", flush=True)
+    res = run_chain(CASES[name])
+    if "planted_recall" in res:
+        print(f"planted recall {res['planted_recall']:.3f}")
+
+
+def test_split_index_equals_fused():
+    a = run_chain(CASES["csa_h64_k512"])
+    b = run_chain(CASES["csa_h64_k512"], split_index=True)
+    assert np.array_equal(a["csa_idx"], b["csa_idx"])
+
+
+def test_window_zero():
+    run_chain(CASES["hca_h64_ragged"], W=0)
+    run_chain(CASES["csa_h64_k512"], W=0)
+
+
+def test_deterministic():
+    a = run_chain(CASES["pair_h128"])
+    b = run_chain(CASES["pair_h128"])
+    for key in a:
+        if isinstance(a[key], np.ndarray):
+            assert np.array_equal(a[key], b[key]), key

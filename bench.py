@@ -1,0 +1,405 @@
+#!/usr/bin/env python3
+"""Throughput of the CSA + HCA hot path on one MI355X.
+
+A step is one pass of the whole path for one batch: the decode token at position n-1
+completes a CSA block (m = 4) and an HCA block (m' = 128), which are pooled into the
+caches; the lightning indexer scores every compressed entry and keeps the top-k; CSA
+attention runs over the selected entries plus the 128-token window and HCA attention over
+every HCA entry plus the window.  The default workload is the Pro-shaped 1M-token decode
+(batch 4, 262144 CSA entries, top-1024, 8192 HCA entries, 128 heads of dim 512).
+``--config 2|3`` time the 128K HCA / CSA decode layers and ``--config 4`` the 8192-token
+prefill chunk.
+
+Inputs are generated on the GPU from a fixed seed, the caches are built with the library's
+own pooling (untimed), and the timed steps rotate over ``--replicas`` copies of every tensor a
+step reads, so that each step reads HBM rather than the 256 MB last-level cache.  Steps are
+replayed from HIP graphs (one per replica).  The indexer scoring kernel, the dominant kernel,
+is also timed alone with HIP events around a graph of back-to-back launches.
+
+Prints one JSON line.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode query-tokens/s and achieved HBM GB/s, CSA+HCA at 128K/1M context"
+HBM_PEAK_GBS = 8000.0
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--config", type=int, default=5)
+    ap.add_argument("--replicas", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    return ap.parse_args()
+
+
+class Workload:
+    """All device state of one workload: inputs, caches, replicas, outputs, workspaces."""
+
+    def __init__(self, cfg, replicas):
+        import torch
+
+        import compressed_attention_compress_amd as lib
+        from synthgen.device import make_problem_device
+
+        self.lib = lib
+        self.cfg = cfg
+        self.R = replicas
+        dev = "cuda"
+        prob = make_problem_device(cfg, dev)
+        self.prob = prob
+        self.n = prob["n_total"]
+        self.Tq = prob["Tq"]
+        self.kind = cfg.kind
+        self.layers = [l for l in ("csa", "hca") if f"X_{l}" in prob]
+        B, c, n, dt = cfg.B, cfg.c, self.n, cfg.dtype
+        self.q_pos = prob["q_pos"]
+        self.win_pos = torch.zeros(B, dtype=torch.int32, device=dev)
+        self.scale = 1.0 / math.sqrt(c)
+        # the pooled caches as a prefill would leave them (untimed): every complete block
+        # before the step's own new blocks
+        self.n_old = n - (self.Tq if self.kind == "prefill" else 1)
+        base = {}
+        for l in self.layers:
+            m = cfg.m if l == "csa" else cfg.m_hca
+            C = torch.zeros((B, n // m, c), dtype=torch.int16, device=dev)
+            lib.csa_compress(prob[f"X_{l}"], prob[f"Z_{l}"], None, C, B, self.n_old, c, m, dt,
+                             n * c, (n // m) * c)
+            base[f"C_{l}"] = C
+            base[f"Q_{l}"] = prob[f"Q_{l}"]
+        if "csa" in self.layers:
+            for key in ("qI", "w", "KI"):
+                base[key] = prob[key]
+        torch.cuda.synchronize()
+        # replicas of everything a step reads (distinct memory, same values)
+        self.rep = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(replicas - 1)]
+        self.N_c = n // cfg.m
+        self.N_h = n // cfg.m_hca
+        nq = B * self.Tq
+        self.out = {l: torch.empty((B, self.Tq, cfg.n_h, c), dtype=torch.int16, device=dev)
+                    for l in self.layers}
+        if "csa" in self.layers:
+            self.idx = torch.empty((B, self.Tq, cfg.k), dtype=torch.int32, device=dev)
+            self.iws_b = lib.lightning_index_topk_workspace_size(B, self.Tq, cfg.n_ih, self.N_c, cfg.k)
+            self.iws = torch.empty(self.iws_b, dtype=torch.uint8, device=dev)
+            self.scores = torch.empty((nq * self.N_c,), dtype=torch.float32, device=dev)
+            self.cws_b = lib.csa_attend_workspace_size(B, self.Tq, cfg.n_h, c, cfg.k, cfg.W)
+            self.cws = torch.empty(max(self.cws_b, 256), dtype=torch.uint8, device=dev)
+        if "hca" in self.layers:
+            self.hws_b = lib.hca_attend_workspace_size(B, self.Tq, cfg.n_h, c, self.N_h, cfg.W)
+            self.hws = torch.empty(max(self.hws_b, 256), dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+
+    # -- the step -------------------------------------------------------------------------
+    def pool_new_blocks(self, r):
+        """Pool the blocks completed by the step's tokens into replica r's caches."""
+        cfg, lib, prob = self.cfg, self.lib, self.prob
+        B, c, n = cfg.B, cfg.c, self.n
+        for l in self.layers:
+            m = cfg.m if l == "csa" else cfg.m_hca
+            first_blk = self.n_old // m          # first block not yet in the cache
+            n_new = n // m - first_blk
+            if n_new <= 0:
+                continue
+            X, Z, C = prob[f"X_{l}"], prob[f"Z_{l}"], self.rep[r][f"C_{l}"]
+            tok0 = first_blk * m
+            lib.csa_compress(X[:, tok0:], Z[:, tok0:], None, C[:, first_blk:], B, n_new * m, c, m,
+                             cfg.dtype, n * c, (n // m) * c)
+
+    def index(self, r, split=True):
+        cfg, lib, rp = self.cfg, self.lib, self.rep[r]
+        B = cfg.B
+        if split:
+            self.index_score(r)
+            lib.lightning_index_select(self.scores, self.q_pos, cfg.m, B, self.Tq, self.N_c, cfg.k,
+                                       self.idx, None, self.iws, self.iws_b)
+        else:
+            lib.lightning_index_topk(rp["qI"], rp["w"], rp["KI"], cfg.idx_dtype, self.q_pos, cfg.m,
+                                     B, self.Tq, cfg.n_ih, cfg.c_I, self.N_c, cfg.k, self.idx, None,
+                                     self.scores, self.iws, self.iws_b)
+
+    def index_score(self, r):
+        cfg, rp = self.cfg, self.rep[r]
+        self.lib.lightning_index_score(rp["qI"], rp["w"], rp["KI"], cfg.idx_dtype, self.q_pos, cfg.m,
+                                       cfg.B, self.Tq, cfg.n_ih, cfg.c_I, self.N_c, cfg.k,
+                                       self.scores, self.iws, self.iws_b)
+
+    def attend(self, r):
+        cfg, lib, rp, prob = self.cfg, self.lib, self.rep[r], self.prob
+        B, c, n = cfg.B, cfg.c, self.n
+        if "csa" in self.layers:
+            lib.csa_attend(rp["Q_csa"], rp["C_csa"], self.idx, prob["X_csa"], self.win_pos,
+                           self.q_pos, B, self.Tq, cfg.n_h, c, self.N_c, cfg.k, n, cfg.W,
+                           self.scale, cfg.dtype, self.out["csa"], None, self.cws, self.cws_b)
+        if "hca" in self.layers:
+            lib.hca_attend(rp["Q_hca"], rp["C_hca"], prob["X_hca"], self.win_pos, self.q_pos,
+                           cfg.m_hca, B, self.Tq, cfg.n_h, c, self.N_h, n, cfg.W, self.scale,
+                           cfg.dtype, self.out["hca"], None, self.hws, self.hws_b)
+
+    def step(self, r):
+        self.pool_new_blocks(r)
+        if "csa" in self.layers:
+            self.index(r)
+        self.attend(r)
+
+    # -- accounting -----------------------------------------------------------------------
+    def algorithmic_bytes(self):
+        """Bytes the step must move at minimum: every input read once, every output written
+        once (compressed caches: only the rows the step reads)."""
+        cfg = self.cfg
+        B, c, W, Tq, n = cfg.B, cfg.c, cfg.W, self.Tq, self.n
+        e = 2  # bf16
+        total = 0
+        detail = {}
+        for l in self.layers:
+            m = cfg.m if l == "csa" else cfg.m_hca
+            n_new_blocks = n // m - self.n_old // m
+            pool = B * n_new_blocks * (2 * m * c * e + c * e)
+            total += pool
+            detail[f"pool_{l}"] = pool
+        qpos = [n - Tq + t for t in range(Tq)]
+        if "csa" in self.layers:
+            V = [min(self.N_c, (p + 1) // cfg.m) for p in qpos]
+            ki = B * max(V) * cfg.c_I  # keys are shared by a sequence's queries
+            idx = B * Tq * (cfg.n_ih * cfg.c_I + cfg.n_ih * 4 + cfg.k * 4)
+            detail["index"] = ki + idx
+            total += ki + idx
+            rows = sum(min(cfg.k, v) + min(W, p + 1) for v, p in zip(V, qpos))
+            att = B * rows * c * e + 2 * B * Tq * cfg.n_h * c * e + B * Tq * cfg.k * 4
+            if Tq > 1:  # rows shared between prefill queries are still read per query (gather)
+                pass
+            detail["csa_attend"] = att
+            total += att
+        if "hca" in self.layers:
+            Vh = [min(self.N_h, (p + 1) // cfg.m_hca) for p in qpos]
+            if Tq == 1:
+                rows = B * (Vh[0] + min(W, qpos[0] + 1))
+            else:  # one pass over the shared entries and the chunk's raw rows
+                rows = B * (max(Vh) + Tq + W - 1)
+            att = rows * c * e + 2 * B * Tq * cfg.n_h * c * e
+            detail["hca_attend"] = att
+            total += att
+        return total, detail
+
+    def index_score_bytes(self):
+        cfg = self.cfg
+        qpos = [self.n - self.Tq + t for t in range(self.Tq)]
+        V = max(min(self.N_c, (p + 1) // cfg.m) for p in qpos)
+        return cfg.B * V * cfg.c_I + cfg.B * self.Tq * cfg.n_ih * (cfg.c_I + 4)
+
+    def flops(self):
+        cfg = self.cfg
+        qpos = [self.n - self.Tq + t for t in range(self.Tq)]
+        f8 = bf = 0
+        for p in qpos:
+            if "csa" in self.layers:
+                V = min(self.N_c, (p + 1) // cfg.m)
+                f8 += 2 * V * cfg.n_ih * cfg.c_I
+                bf += 4 * cfg.n_h * cfg.c * (min(cfg.k, V) + min(cfg.W, p + 1))
+            if "hca" in self.layers:
+                Vh = min(self.N_h, (p + 1) // cfg.m_hca)
+                bf += 4 * cfg.n_h * cfg.c * (Vh + min(cfg.W, p + 1))
+        return cfg.B * f8, cfg.B * bf
+
+
+def read_traffic(kernel_name):
+    """HBM traffic of the dominant kernel from committed counter runs, if the kernel source
+    is unchanged since they were taken (else None)."""
+    try:
+        import hashlib
+        with open(PROFILE_TRAFFIC) as f:
+            rec = json.load(f)
+        src = os.path.join(ROOT, "compressed_attention_compress_amd", "csrc", "indexer.hip")
+        h = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        ent = rec.get(kernel_name)
+        if ent and ent.get("source_sha256") == h:
+            return ent["bytes_per_launch"]
+    except (OSError, ValueError, KeyError):
+        pass
+    return None
+
+
+def cpu_baseline(wl, seconds):
+    """The oracle, as it stands, on a bounded sample of the same workload: complete steps
+    for whole sequences, repeated until about `seconds` of CPU time is spent."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from synthgen.configs import BF16
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = len(os.sched_getaffinity(0))
+    cfg, prob = wl.cfg, wl.prob
+    if wl.Tq != 1:
+        return None
+    n, c, W = wl.n, cfg.c, cfg.W
+    p = n - 1
+
+    def codes(t):
+        a = t.detach().cpu().numpy()
+        return a.view(np.uint16) if a.dtype == np.int16 else a
+
+    # inputs of each sequence, decoded once (input preparation, not timed)
+    seqs = []
+    for b in range(cfg.B):
+        d = {}
+        for l in wl.layers:
+            m = cfg.m if l == "csa" else cfg.m_hca
+            C = oracle.decode(codes(wl.rep[0][f"C_{l}"][b]), BF16)
+            lo = (n // m - 1) * m
+            d[f"blk_{l}"] = (oracle.decode(codes(prob[f"X_{l}"][b, lo:n]), BF16),
+                             oracle.decode(codes(prob[f"Z_{l}"][b, lo:n]), BF16))
+            d[f"win_{l}"] = oracle.decode(codes(prob[f"X_{l}"][b, n - W:n]), BF16)
+            d[f"C_{l}"] = C
+            d[f"Q_{l}"] = oracle.decode(codes(prob[f"Q_{l}"][b, 0]), BF16)
+        if "csa" in wl.layers:
+            d["qI"] = oracle.decode(codes(prob["qI"][b, 0]), cfg.idx_dtype)
+            d["w"] = prob["w"][b, 0].cpu().numpy()
+            d["KI"] = oracle.decode(codes(prob["KI"][b]), cfg.idx_dtype)
+        seqs.append(d)
+
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        for d in seqs:
+            for l in wl.layers:
+                m = cfg.m if l == "csa" else cfg.m_hca
+                newC = oracle.pool(*d[f"blk_{l}"], m)
+                C = d[f"C_{l}"]
+                C[-1] = newC[0]
+                if l == "csa":
+                    V = oracle.visible(p, m, C.shape[0])
+                    s = oracle.index_scores(d["qI"], d["w"], d["KI"], V)
+                    sel = oracle.topk(s, cfg.k)
+                    rows = oracle.csa_rows(C, sel, d["win_csa"], n - W, p, W)
+                else:
+                    rows = oracle.hca_rows(C, m, d["win_hca"], n - W, p, W)
+                oracle.attend(d[f"Q_{l}"], rows, wl.scale)
+            done += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or done >= 64:
+            break
+    return {"value": done / el, "unit": "query-tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} complete decode steps of single sequences of this workload "
+                      f"({cfg.B} distinct sequences cycled), {el:.1f} s, NumPy fp64"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path has no multi-GPU mode)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from synthgen.configs import CONFIGS
+
+    cfg = CONFIGS[args.config]
+    decode = cfg.kind != "prefill"
+    steps = args.steps if args.steps is not None else (500 if decode else 20)
+    warmup = args.warmup if args.warmup is not None else (50 if decode else 3)
+    R = args.replicas if args.replicas is not None else (6 if decode else 1)
+    torch.cuda.set_device(0)
+    wl = Workload(cfg, R)
+
+    # warm up eagerly (also sets the library's one-time kernel attributes)
+    for i in range(warmup):
+        wl.step(i % R)
+    torch.cuda.synchronize()
+
+    graphs = []
+    side = torch.cuda.Stream()
+    for r in range(R):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            wl.step(r)
+        graphs.append(g)
+    for r in range(R):
+        graphs[r].replay()
+    torch.cuda.synchronize()
+
+    t0 = time.perf_counter()
+    for i in range(steps):
+        graphs[i % R].replay()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    sec = (t1 - t0) / steps
+    qtok = cfg.B * wl.Tq / sec
+    abytes, detail = wl.algorithmic_bytes()
+    f8, bf = wl.flops()
+
+    roofline = None
+    if "csa" in wl.layers:
+        gs = torch.cuda.CUDAGraph()
+        reps = max(R, 8)
+        with torch.cuda.graph(gs, stream=side):
+            for i in range(reps):
+                wl.index_score(i % R)
+        gs.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        rounds = 10 if decode else 1
+        with torch.cuda.stream(side):
+            e0.record(side)
+            for _ in range(rounds):
+                gs.replay()
+            e1.record(side)
+        torch.cuda.synchronize()
+        dur = e0.elapsed_time(e1) / 1e3 / (rounds * reps)
+        kb = wl.index_score_bytes()
+        ach = kb / dur / 1e9
+        roofline = {"kernel": "index_score_fp8", "bound": "hbm", "achieved": round(ach, 1),
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                    "traffic": read_traffic("index_score_fp8" + ("" if decode else "_prefill")),
+                    "avg_launch_us": round(dur * 1e6, 2), "bytes_per_launch": kb}
+
+    cpu = None
+    if not args.no_cpu_baseline and decode:
+        cpu = cpu_baseline(wl, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": round(qtok, 1),
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(sec * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16+fp8e4m3",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": cfg.B, "context": wl.n, "query_tokens": wl.Tq,
+                   "c": cfg.c, "n_h": cfg.n_h, "m": cfg.m, "m_hca": cfg.m_hca, "k": cfg.k,
+                   "n_ih": cfg.n_ih, "c_I": cfg.c_I, "window": cfg.W, "replicas": R,
+                   "timing": "hip graph per step, rotating replicas"},
+        "hbm_gbs": round(abytes / sec / 1e9, 1),
+        "hbm_frac": round(abytes / sec / 1e9 / HBM_PEAK_GBS, 4),
+        "algorithmic_bytes_per_step": abytes,
+        "tflops": {"fp8": round(f8 / sec / 1e12, 2), "bf16": round(bf / sec / 1e12, 2)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

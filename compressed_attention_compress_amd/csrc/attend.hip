@@ -14,16 +14,16 @@
 // which gives exactly the joint softmax.
 //
 // bf16 path (c = 512), per 32-slot tile:
-//   * the 32 rows are read once from HBM (each wave issues one 1 KiB row per load; rows
-//     of the next tile are in flight in registers while the current tile is computed)
-//     and staged in LDS with a 16-byte row pad;
+//   * the 32 rows are read once from HBM straight into LDS (global_load_lds_dwordx4: each
+//     wave instruction moves one 1 KiB row; rows keep a 16-byte pad), through a ring of
+//     tiles so that the next tile is in flight while one is computed;
 //   * every wave owns 16 (query, head) pairs.  S^T = E . Q^T on MFMA
 //     (v_mfma_f32_16x16x32_bf16, A = 16 rows x 32 dims from LDS, B = Q from registers);
 //     the accumulator layout puts one head per lane column, so the online-softmax
 //     statistics of a head live in the lanes that also hold its output;
 //   * O^T += E^T . P^T on MFMA: P stays in registers in exactly the layout the S
-//     accumulator produced it; E^T comes from LDS as 32-bit words holding two adjacent
-//     columns, which feed an "even column" and an "odd column" MFMA each.
+//     accumulator produced it; E^T comes from the same LDS tile through the gfx950
+//     transpose read (ds_read_b64_tr_b16), two reads per MFMA.
 // float32 path: plain FMA over LDS-resident scores (small heads only).
 #include "common.hpp"
 
@@ -33,7 +33,6 @@ constexpr int C = 512;            // head dim of the bf16 path
 constexpr int TILE = 32;          // slots per LDS tile
 constexpr int ROWB = C * 2 + 16;  // LDS row stride in bytes
 constexpr int KS = C / 32;        // MFMA K-steps of S (16 x 32 dims)
-constexpr int CPAIRS = C / 32;    // 32-column blocks of O
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
@@ -54,8 +53,11 @@ struct AttnArgs {
   int n_slots;    // n_slots_c + W + Tg - 1
   int Tg;         // consecutive query tokens per workgroup (HCA prefill shares rows)
   int HPW;        // heads per workgroup
+  int n_hg;       // head groups = n_h / HPW
   int nqg;        // query groups per sequence
   int n_splits, RS;
+  int n_work;     // B * nqg * n_splits * n_hg
+  int per_xcd;    // gridDim.x / 8
   float scale_log2;
 };
 
@@ -65,16 +67,73 @@ CSAHCA_DEV int vis_count(long long p, int m, int N) {
   return (int)(v < N ? v : N);
 }
 
-template <int NW>
-__global__ __launch_bounds__(NW * 64) void attend_bf16(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t tile[TILE * ROWB];
-  __shared__ int row_ok[TILE];
-  constexpr int NT = NW * 64;
-  constexpr int LOADS = TILE / NW;  // rows each wave loads per tile
+// Wait until at most N of this wave's vector-memory operations are outstanding, then
+// join the workgroup barrier.  Written as one asm statement with a memory clobber so the
+// compiler neither adds a full vmcnt(0) drain nor moves LDS reads across the barrier.
+template <int N>
+CSAHCA_DEV void wait_vmcnt_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// Every LDS read of this wave has completed; then join the workgroup barrier.
+CSAHCA_DEV void lds_reads_done_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// LDS ring depth: two tiles (one in flight while one is computed).  A deeper ring gains no
+// bandwidth here and costs registers; two 4-wave workgroups share a CU.
+constexpr int stages_for(int) { return 2; }
+
+size_t attend_lds_bytes(int NW, int RS, bool csa) {
+  const int ns = stages_for(NW);
+  return (size_t)ns * TILE * ROWB + (size_t)ns * NW * sizeof(uint32_t) +
+         (csa ? (size_t)RS * sizeof(int) : 0);
+}
+
+// bits [lo, hi) of a 32-bit mask, the bounds relative to `base` and clipped to [0, 32)
+CSAHCA_DEV uint32_t range_bits(int lo, int hi, int base) {
+  lo = min(max(lo - base, 0), 32);
+  hi = min(max(hi - base, 0), 32);
+  if (hi <= lo) return 0u;
+  const uint32_t up = hi == 32 ? 0xFFFFFFFFu : ((1u << hi) - 1u);
+  return up & ~((1u << lo) - 1u);
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// One workgroup: queries t0 .. t0+Tg-1 of one sequence, HPW heads, slots
+// [split*RS, (split+1)*RS).  Rows arrive by global_load_lds straight into an LDS ring of
+// NS tiles; each wave issues its share of every tile (one 1 KiB row per instruction) and
+// waits with an explicit vmcnt for the oldest tile only, so NS-1 tiles stay in flight
+// without holding registers.  Skipped slots load a valid dummy row; a wave-uniform 32-bit
+// mask per tile gives every skipped slot a zero weight.  The running maximum only moves
+// when a score exceeds it by more than 2^8 (weights stay <= 256), so the output
+// accumulators are rarely rescaled.  LDS operands are read in small groups, one group
+// ahead of the MFMAs that use them, which bounds the registers in use so that two
+// workgroups share a CU.
+template <int NW, int NS, bool CSA>
+__global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attend_bf16(AttnArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  constexpr int LPW = TILE / NW;  // rows each wave loads per tile
+  constexpr float LAZY = 8.f;     // log2 headroom before the running maximum moves
+  uint8_t* tiles = smem;
+  uint32_t* tmask = reinterpret_cast<uint32_t*>(smem + NS * TILE * ROWB);  // [NS][NW]
+  int* sidx = reinterpret_cast<int*>(tmask + NS * NW);                     // [RS]
+
+  // XCD-aware order: consecutive work items (the head groups of one row range first) run
+  // on the same XCD, so the rows they share are read from HBM once into that XCD's L2.
+  const int Lb = blockIdx.x;
+  const int wid = (Lb & 7) * a.per_xcd + (Lb >> 3);
+  if (wid >= a.n_work) return;  // grid padding, before any barrier
+  const int hg = wid % a.n_hg;
+  const int rest = wid / a.n_hg;
+  const int split = rest % a.n_splits;
+  const int qg = rest / a.n_splits;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int row16 = lane & 15, g = lane >> 4;
-  const int split = blockIdx.x, hg = blockIdx.y, qg = blockIdx.z;
   const int b = qg / a.nqg;
   const int t0 = (qg - b * a.nqg) * a.Tg;
   const int wpq = a.HPW / 16;
@@ -86,189 +145,223 @@ __global__ __launch_bounds__(NW * 64) void attend_bf16(AttnArgs a) {
   const long long pfirst = qpos0 + t0, plast = qpos0 + tlast;
   const long long p = qpos0 + (active ? tq : tlast);
   const long long wp = a.win_pos[b];
-  const int Vw = a.is_csa ? 0 : vis_count(p, a.m, a.Nc);
-  const int Vu = a.is_csa ? 0 : vis_count(plast, a.m, a.Nc);
   const int slot_lo = split * a.RS;
   const int slot_hi = min(a.n_slots, slot_lo + a.RS);
   const long long qrow = (long long)b * a.Tq + (active ? tq : tlast);
+  const uint16_t* ckv_b = a.ckv + (size_t)b * a.Nc * C;
+  const uint16_t* win_b = a.win + (size_t)b * a.L * C;
+  const int nsc = a.n_slots_c;
 
-  // source row of a slot for the union of this workgroup's queries (nullptr: skipped)
-  auto slot_src = [&](int j) -> const uint16_t* {
-    if (j >= slot_hi) return nullptr;
-    if (j < a.n_slots_c) {
-      if (a.is_csa) {
-        const int e = a.topk[((long long)b * a.Tq + t0) * a.k + j];
-        if (e < 0 || e >= a.Nc) return nullptr;
-        return a.ckv + ((long long)b * a.Nc + e) * C;
-      }
-      if (j >= Vu) return nullptr;
-      return a.ckv + ((long long)b * a.Nc + j) * C;
+  // window slot j >= nsc holds raw position wpos0 + (j - nsc), i.e. source row
+  // wrow0 + (j - nsc).  Usable raw positions: >= 0, inside the source rows, and in the
+  // query's own window (p-W, p]; for loading, the union over the workgroup's queries.
+  const long long wpos0 = pfirst - a.W + 1;
+  const long long wrow0 = wpos0 - wp;
+  auto win_slots = [&](long long lo_pos, long long hi_pos, int& lo, int& hi) {
+    lo_pos = max(lo_pos, max(0LL, wp));
+    hi_pos = min(hi_pos, wp + a.L - 1);
+    if (hi_pos < lo_pos) {
+      lo = hi = nsc;
+      return;
     }
-    const long long pos = pfirst - a.W + 1 + (j - a.n_slots_c);
-    if (pos < 0 || pos > plast) return nullptr;
-    const long long r = pos - wp;
-    if (r < 0 || r >= a.L) return nullptr;
-    return a.win + ((long long)b * a.L + r) * C;
+    lo = nsc + (int)(lo_pos - wpos0);
+    hi = nsc + (int)(hi_pos - wpos0) + 1;
   };
-  // is slot j (usable by the workgroup) usable by this wave's query?
-  auto slot_mine = [&](int j) -> bool {
-    if (j < a.n_slots_c) return a.is_csa || j < Vw;
-    const long long pos = pfirst - a.W + 1 + (j - a.n_slots_c);
-    return pos <= p && pos > p - a.W;
-  };
+  int wu_lo, wu_hi, wq_lo, wq_hi;
+  win_slots(wpos0, plast, wu_lo, wu_hi);
+  win_slots(p - a.W + 1, p, wq_lo, wq_hi);
+  const int Vu = CSA ? 0 : vis_count(plast, a.m, a.Nc);
+  const int Vw = CSA ? 0 : vis_count(p, a.m, a.Nc);
 
+  // CSA: this split's selected entry indices, staged in LDS
+  if (CSA) {
+    const int* tk = a.topk + ((long long)b * a.Tq + t0) * a.k;
+    const int hi = min(slot_hi, nsc);
+    for (int j = slot_lo + (int)threadIdx.x; j < hi; j += NW * 64) sidx[j - slot_lo] = tk[j];
+  }
   bf16x8 qf[KS];
-  if (active) {
+  {
     const uint16_t* qp = a.q + (qrow * a.n_h + h0 + row16) * C + g * (C / 4);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       qf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qp + ks * 8));
-  } else {
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
   }
-
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x4 oacc[CPAIRS][2];
-#pragma unroll
-  for (int cp = 0; cp < CPAIRS; ++cp) {
-    oacc[cp][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-    oacc[cp][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  u32x4 pre[LOADS];
-  int pre_ok[LOADS];
-  auto fetch = [&](int it) {
-    const int base = slot_lo + it * TILE;
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int r = wave + i * NW;  // wave-uniform row of the tile
-      const uint16_t* src = slot_src(base + r);
-      pre_ok[i] = src != nullptr;
-      pre[i] = src ? *reinterpret_cast<const u32x4*>(src + lane * 8) : u32x4{0, 0, 0, 0};
-    }
-  };
+  __syncthreads();  // sidx visible; also drains the loads above before the ring starts
 
   const int ntile = slot_hi > slot_lo ? cdiv(slot_hi - slot_lo, TILE) : 0;
-  if (ntile > 0) fetch(0);
-  for (int it = 0; it < ntile; ++it) {
-    __syncthreads();  // the previous tile is no longer read
+  auto issue = [&](int tt) {
+    const int stage = tt % NS;
+    uint8_t* st = tiles + stage * (TILE * ROWB);
+    const int base = slot_lo + tt * TILE;
+    uint32_t okbits = 0;
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
+    for (int i = 0; i < LPW; ++i) {
       const int r = wave + i * NW;
-      *reinterpret_cast<u32x4*>(tile + r * ROWB + lane * 16) = pre[i];
-      if (lane == 0) row_ok[r] = pre_ok[i];
+      const int j = base + r;
+      const uint16_t* src = ckv_b;  // dummy: any valid row
+      bool ok = false;
+      if (j < slot_hi) {
+        if (j < nsc) {
+          if (CSA) {
+            const int e = __builtin_amdgcn_readfirstlane(sidx[j - slot_lo]);
+            ok = (unsigned)e < (unsigned)a.Nc;
+            if (ok) src = ckv_b + (size_t)e * C;
+          } else if (j < Vu) {
+            ok = true;
+            src = ckv_b + (size_t)j * C;
+          }
+        } else if (j >= wu_lo && j < wu_hi) {
+          ok = true;
+          src = win_b + (size_t)(wrow0 + (j - nsc)) * C;
+        }
+      }
+      okbits |= ok ? (1u << r) : 0u;
+      __builtin_amdgcn_global_load_lds(src + lane * 8,
+                                       (__attribute__((address_space(3))) void*)(st + r * ROWB),
+                                       16, 0, 0);
     }
-    __syncthreads();
-    if (it + 1 < ntile) fetch(it + 1);
-    if (!active) continue;
+    if (lane == 0) tmask[stage * NW + wave] = okbits;
+  };
 
-    const int base = slot_lo + it * TILE;
-    // ---- S^T = E Q^T for 2 blocks of 16 slots ----
-    f32x4 s[2];
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 oacc[C / 16];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      s[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const uint8_t* rp = tile + (rb * 16 + row16) * ROWB + g * (C / 4) * 2;
+  for (int cb = 0; cb < C / 16; ++cb) oacc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // LDS byte offsets of this lane's operands inside a tile
+  const int s_off = row16 * ROWB + g * (C / 4) * 2;               // S: A = row, 8 dims
+  const int t_off = (4 * g + (row16 >> 2)) * ROWB + (row16 & 3) * 8;  // PV: transpose reads
+
+  for (int tt = 0; tt < NS - 1 && tt < ntile; ++tt) issue(tt);
+  for (int it = 0; it < ntile; ++it) {
+    // this wave's rows of tile `it` have landed, then every other wave's
+    if (it + NS - 1 < ntile) {
+      issue(it + NS - 1);
+      // (the counter holds at most 63; a smaller bound only waits longer)
+      wait_vmcnt_barrier<((NS - 1) * LPW < 63 ? (NS - 1) * LPW : 63)>();
+    } else {
+      wait_vmcnt_barrier<0>();
+    }
+    if (active) {
+      const int stage = it % NS;
+      const uint8_t* tile = tiles + stage * (TILE * ROWB);
+      const int base = slot_lo + it * TILE;
+      // slots of this tile usable by this wave's query (wave-uniform)
+      uint32_t loaded = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) loaded |= tmask[stage * NW + w];
+      loaded = __builtin_amdgcn_readfirstlane(loaded);
+      uint32_t vmask = range_bits(wq_lo, min(wq_hi, slot_hi), base);
+      if (CSA)
+        vmask |= range_bits(slot_lo, min(nsc, slot_hi), base);
+      else
+        vmask |= range_bits(0, min(min(Vw, nsc), slot_hi), base);
+      vmask &= loaded;
+
+      // ---- S^T = E Q^T for 2 blocks of 16 slots; reads run one K-step ahead ----
+      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s2 = s0;
+      const uint8_t* sp = tile + s_off;
+      u32x4 ra0 = *reinterpret_cast<const u32x4*>(sp);
+      u32x4 ra1 = *reinterpret_cast<const u32x4*>(sp + 16 * ROWB);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 ef = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(rp + ks * 16));
-        s[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ef, qf[ks], s[rb], 0, 0, 0);
+        u32x4 rb0, rb1;
+        if (ks + 1 < KS) {
+          rb0 = *reinterpret_cast<const u32x4*>(sp + (ks + 1) * 16);
+          rb1 = *reinterpret_cast<const u32x4*>(sp + 16 * ROWB + (ks + 1) * 16);
+        }
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ra0), qf[ks], s0, 0, 0, 0);
+        s2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ra1), qf[ks], s2, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        ra0 = rb0;
+        ra1 = rb1;
       }
-    }
-    // lane: head h0 + row16, slots base + rb*16 + 4g + i
-    float sv[8];
-    float mloc = -INFINITY;
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+      // lane: head h0 + row16, slots base + rb*16 + 4g + i
+      float sv[8];
+      float mloc = -INFINITY;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = rb * 16 + 4 * g + i;
-        const int j = base + r;
-        const bool ok = j < slot_hi && row_ok[r] && slot_mine(j);
-        const float x = ok ? s[rb][i] * a.scale_log2 : -INFINITY;
-        sv[rb * 4 + i] = x;
-        mloc = fmaxf(mloc, x);
+        const bool ok0 = (vmask >> (4 * g + i)) & 1u;
+        const bool ok1 = (vmask >> (16 + 4 * g + i)) & 1u;
+        sv[i] = ok0 ? s0[i] * a.scale_log2 : -INFINITY;
+        sv[4 + i] = ok1 ? s2[i] * a.scale_log2 : -INFINITY;
+        mloc = fmaxf(mloc, fmaxf(sv[i], sv[4 + i]));
       }
-    mloc = fmaxf(mloc, shfl_xor_f(mloc, 16));
-    mloc = fmaxf(mloc, shfl_xor_f(mloc, 32));
-    const float m_new = fmaxf(m_run, mloc);
-    float alpha = 1.f;
-    float pe[8];
-    float psum = 0.f;
-    if (m_new == -INFINITY) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pe[e] = 0.f;
-    } else {
-      alpha = exp2f(m_run - m_new);
+      mloc = fmaxf(mloc, shfl_xor_f(mloc, 16));
+      mloc = fmaxf(mloc, shfl_xor_f(mloc, 32));
+      // lazy running maximum: move it only when exceeded by more than LAZY
+      const bool bump = mloc > m_run + LAZY;
+      const float m_new = bump ? mloc : m_run;
+      const float alpha = bump ? exp2f(m_run - m_new) : 1.f;
+      float pe[8];
+      float psum = 0.f;
+      const bool none = m_new == -INFINITY;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        pe[e] = exp2f(sv[e] - m_new);
+        pe[e] = none ? 0.f : exp2f(sv[e] - m_new);  // skipped slots: exp2(-inf) = 0
         psum += pe[e];
       }
-    }
-    psum += shfl_xor_f(psum, 16);
-    psum += shfl_xor_f(psum, 32);
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    if (__any(alpha != 1.f)) {
+      psum += shfl_xor_f(psum, 16);
+      psum += shfl_xor_f(psum, 32);
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+      if (__any(bump)) {
 #pragma unroll
-      for (int cp = 0; cp < CPAIRS; ++cp)
-#pragma unroll
-        for (int par = 0; par < 2; ++par) oacc[cp][par] *= alpha;
-    }
-    // P^T as the B operand: k-slot e <-> slot (e < 4 ? 4g+e : 16+4g+e-4)
-    const u32x4 pw = {pack_bf16x2(pe[0], pe[1]), pack_bf16x2(pe[2], pe[3]),
-                      pack_bf16x2(pe[4], pe[5]), pack_bf16x2(pe[6], pe[7])};
-    const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
-    // ---- O^T += E^T P^T ----
-#pragma unroll
-    for (int cp = 0; cp < CPAIRS; ++cp) {
-      const uint8_t* cpb = tile + (32 * cp + 2 * row16) * 2;
-      uint32_t wv[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int r = e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4);
-        wv[e] = *reinterpret_cast<const uint32_t*>(cpb + r * ROWB);
+        for (int cb = 0; cb < C / 16; ++cb) oacc[cb] *= alpha;
       }
-      u32x4 ev, od;
+      // P^T as the B operand: k-slot e <-> slot (e < 4 ? 4g+e : 16+4g+e-4)
+      const u32x4 pw = {pack_bf16x2(pe[0], pe[1]), pack_bf16x2(pe[2], pe[3]),
+                        pack_bf16x2(pe[4], pe[5]), pack_bf16x2(pe[6], pe[7])};
+      const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
+      // ---- O^T += E^T P^T: E^T through LDS transpose reads, two column blocks ahead ----
+      // ds_read_b64_tr_b16: in each 16-lane group, lane i receives column i%4 of the four
+      // 4-element rows addressed by lanes i/4, i/4+4, i/4+8, i/4+12.  Lane j addresses row
+      // (4g + j/4) at column 16*cb + 4*(j%4), so lane i gets column 16*cb + i of rows
+      // 4g .. 4g+3 (and 16+4g .. 16+4g+3 with the second read): exactly its A operand.
+      const uint8_t* tp = tile + t_off;
+      auto tr_pair = [&](int cb) -> u32x4 {
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tp + cb * 32));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tp + 16 * ROWB + cb * 32));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        return u32x4{l2[0], l2[1], h2[0], h2[1]};
+      };
+      u32x4 ta0 = tr_pair(0), ta1 = tr_pair(1);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        ev[e] = (wv[2 * e] & 0xFFFFu) | (wv[2 * e + 1] << 16);
-        od[e] = (wv[2 * e] >> 16) | (wv[2 * e + 1] & 0xFFFF0000u);
+      for (int cb0 = 0; cb0 < C / 16; cb0 += 2) {
+        u32x4 tb0, tb1;
+        if (cb0 + 2 < C / 16) {
+          tb0 = tr_pair(cb0 + 2);
+          tb1 = tr_pair(cb0 + 3);
+        }
+        oacc[cb0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ta0), pf, oacc[cb0], 0, 0, 0);
+        oacc[cb0 + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ta1), pf, oacc[cb0 + 1], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        ta0 = tb0;
+        ta1 = tb1;
       }
-      oacc[cp][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ev), pf,
-                                                            oacc[cp][0], 0, 0, 0);
-      oacc[cp][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, od), pf,
-                                                            oacc[cp][1], 0, 0, 0);
     }
+    lds_reads_done_barrier();  // the stage is free for the next issue
   }
   if (!active) return;
 
-  // lane: head h0 + row16; oacc[cp][par][i] is column 32*cp + 8*g + 2*i + par
+  // lane: head h0 + row16; oacc[cb][i] is column 16*cb + 4*g + i
   const int h = h0 + row16;
   if (a.n_splits == 1) {
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-    uint16_t* op = a.out + (qrow * a.n_h + h) * C + 8 * g;
+    uint16_t* op = a.out + (qrow * a.n_h + h) * C + 4 * g;
 #pragma unroll
-    for (int cp = 0; cp < CPAIRS; ++cp) {
-      u32x4 o;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(oacc[cp][0][i] * inv, oacc[cp][1][i] * inv);
-      *reinterpret_cast<u32x4*>(op + 32 * cp) = o;
+    for (int cb = 0; cb < C / 16; ++cb) {
+      const u32x2 o = {pack_bf16x2(oacc[cb][0] * inv, oacc[cb][1] * inv),
+                       pack_bf16x2(oacc[cb][2] * inv, oacc[cb][3] * inv)};
+      *reinterpret_cast<u32x2*>(op + 16 * cb) = o;
     }
     if (a.lse && g == 0)
       a.lse[qrow * a.n_h + h] = l_run > 0.f ? (m_run + __log2f(l_run)) * LN2 : -INFINITY;
   } else {
     const long long pr = (qrow * a.n_splits + split) * a.n_h + h;
-    float* op = a.opart + pr * C + 8 * g;
+    float* op = a.opart + pr * C + 4 * g;
 #pragma unroll
-    for (int cp = 0; cp < CPAIRS; ++cp) {
-      const f32x4 lo = {oacc[cp][0][0], oacc[cp][1][0], oacc[cp][0][1], oacc[cp][1][1]};
-      const f32x4 hi = {oacc[cp][0][2], oacc[cp][1][2], oacc[cp][0][3], oacc[cp][1][3]};
-      *reinterpret_cast<f32x4*>(op + 32 * cp) = lo;
-      *reinterpret_cast<f32x4*>(op + 32 * cp + 4) = hi;
-    }
+    for (int cb = 0; cb < C / 16; ++cb) *reinterpret_cast<f32x4*>(op + 16 * cb) = oacc[cb];
     if (g == 0) {
       a.mlpart[pr * 2 + 0] = m_run;
       a.mlpart[pr * 2 + 1] = l_run;
@@ -276,7 +369,8 @@ __global__ __launch_bounds__(NW * 64) void attend_bf16(AttnArgs a) {
   }
 }
 
-// merge the splits of every (query, head) by their log-sum-exp; one wave per pair
+// Merge the splits of every (query, head) by their log-sum-exp.  64 threads per pair,
+// 8 columns each; the split loop keeps 4 partial rows in flight.
 __global__ __launch_bounds__(256) void attend_combine(const float* __restrict__ opart,
                                                       const float* __restrict__ mlpart,
                                                       uint16_t* __restrict__ out,
@@ -287,14 +381,37 @@ __global__ __launch_bounds__(256) void attend_combine(const float* __restrict__ 
   if (pair >= nqh) return;
   const long long qrow = pair / n_h;
   const int h = (int)(pair - qrow * n_h);
+  const long long pr0 = qrow * n_splits * n_h + h;  // partial row of split s: pr0 + s*n_h
   float M = -INFINITY;
-  for (int s = 0; s < n_splits; ++s)
-    M = fmaxf(M, mlpart[((qrow * n_splits + s) * n_h + h) * 2]);
+  for (int s = 0; s < n_splits; ++s) M = fmaxf(M, mlpart[(pr0 + (long long)s * n_h) * 2]);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float Ls = 0.f;
   if (M != -INFINITY) {
-    for (int s = 0; s < n_splits; ++s) {
-      const long long pr = (qrow * n_splits + s) * n_h + h;
+    int s = 0;
+    for (; s + 4 <= n_splits; s += 4) {
+      f32x4 x0[4], x1[4];
+      float ms[4], ls[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const long long pr = pr0 + (long long)(s + u) * n_h;
+        ms[u] = mlpart[pr * 2];
+        ls[u] = mlpart[pr * 2 + 1];
+        x0[u] = *reinterpret_cast<const f32x4*>(opart + pr * C + lane * 8);
+        x1[u] = *reinterpret_cast<const f32x4*>(opart + pr * C + lane * 8 + 4);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float wgt = ms[u] == -INFINITY ? 0.f : exp2f(ms[u] - M);
+        Ls = fmaf(wgt, ls[u], Ls);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[i] = fmaf(wgt, x0[u][i], acc[i]);
+          acc[4 + i] = fmaf(wgt, x1[u][i], acc[4 + i]);
+        }
+      }
+    }
+    for (; s < n_splits; ++s) {
+      const long long pr = pr0 + (long long)s * n_h;
       const float ms = mlpart[pr * 2], ls = mlpart[pr * 2 + 1];
       const float wgt = ms == -INFINITY ? 0.f : exp2f(ms - M);
       Ls = fmaf(wgt, ls, Ls);
@@ -414,32 +531,68 @@ __global__ __launch_bounds__(256) void attend_f32(AttnF32Args a) {
 // host side
 // ---------------------------------------------------------------------------------------
 struct Plan {
-  int Tg, HPW, NW, n_slots, n_splits, RS, nqg;
-  size_t opart_bytes, ml_bytes, ws;
+  int Tg, HPW, NW, n_hg, n_slots, n_splits, RS, nqg, n_work, per_xcd;
+  size_t opart_bytes, ml_bytes, ws, lds;
 };
 
+// Launch shape.  A workgroup holds up to 64 heads (4 waves; 8 waves when two prefill
+// queries share the rows).  The rows of a query are split over workgroups until about
+// 256 workgroups exist, but never below 128 rows per split: each split writes an fp32
+// partial of HPW x 512 floats, so shorter splits would move more partial bytes than rows.
 Plan make_plan(int B, int Tq, int n_h, int n_slots_c, int W, bool csa) {
   Plan P;
   P.Tg = 1;
   if (!csa && Tq > 1 && n_h <= 64) P.Tg = 128 / n_h < Tq ? 128 / n_h : Tq;
   if (P.Tg > 8) P.Tg = 8;
-  P.HPW = n_h * P.Tg <= 128 ? n_h : 128 / P.Tg;
+  P.HPW = n_h < 64 ? n_h : 64;
+  if (P.HPW * P.Tg > 128) P.HPW = 128 / P.Tg;
   P.NW = P.Tg * P.HPW / 16;
+  P.n_hg = n_h / P.HPW;
   P.n_slots = n_slots_c + W + P.Tg - 1;
   P.nqg = cdiv(Tq, P.Tg);
-  const long long base = (long long)(n_h / P.HPW) * B * P.nqg;
+  const long long base = (long long)P.n_hg * B * P.nqg;
   const int ntile = cdiv(P.n_slots, TILE);
-  long long want = cdiv<long long>(512, base);
-  int maxs = ntile / 2 > 1 ? ntile / 2 : 1;  // at least 2 tiles per split
+  const int min_tiles = 4;
+  long long want = cdiv<long long>(256, base);
+  const int maxs = ntile / min_tiles > 1 ? ntile / min_tiles : 1;
   int ns = (int)(want < maxs ? want : maxs);
   if (ns < 1) ns = 1;
   P.RS = cdiv(ntile, ns) * TILE;
   P.n_splits = cdiv(P.n_slots, P.RS);
+  P.n_work = (int)(base * P.n_splits);
+  P.per_xcd = cdiv(P.n_work, 8);
   const long long nqh = (long long)B * Tq * n_h;
   P.opart_bytes = P.n_splits > 1 ? csahca::align_up((size_t)(nqh * P.n_splits * C * 4), 256) : 0;
   P.ml_bytes = P.n_splits > 1 ? csahca::align_up((size_t)(nqh * P.n_splits * 2 * 4), 256) : 0;
   P.ws = P.opart_bytes + P.ml_bytes;
+  P.lds = attend_lds_bytes(P.NW, P.RS, csa);
   return P;
+}
+
+template <int NW, bool CSA>
+int launch_attend(const Plan& P, const AttnArgs& A, hipStream_t st) {
+  constexpr int NS = stages_for(NW);
+  static bool attr_set = false;
+  if (!attr_set) {
+    if (hipFuncSetAttribute((const void*)attend_bf16<NW, NS, CSA>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 1024) != hipSuccess)
+      return csahca::fail(CSAHCA_ELAUNCH, "attend: cannot raise the LDS limit");
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((attend_bf16<NW, NS, CSA>), dim3((unsigned)(P.per_xcd * 8)), dim3(NW * 64),
+                     P.lds, st, A);
+  return CSAHCA_OK;
+}
+
+template <bool CSA>
+int launch_attend_nw(const Plan& P, const AttnArgs& A, hipStream_t st) {
+  switch (P.NW) {
+    case 1: return launch_attend<1, CSA>(P, A, st);
+    case 2: return launch_attend<2, CSA>(P, A, st);
+    case 4: return launch_attend<4, CSA>(P, A, st);
+    case 8: return launch_attend<8, CSA>(P, A, st);
+    default: return csahca::fail(CSAHCA_ENOTSUP, "attend: unsupported wave count");
+  }
 }
 
 int check_attend(const char* name, const void* q, const void* ckv, const void* win_kv,
@@ -548,16 +701,15 @@ int attend_impl(const char* name, bool csa, const void* q, const void* ckv, cons
   A.n_splits = P.n_splits;
   A.RS = P.RS;
   A.scale_log2 = scale * LOG2E;
-  dim3 grid((unsigned)P.n_splits, (unsigned)(n_h / P.HPW), (unsigned)(B * P.nqg));
-  switch (P.NW) {
-    case 1: hipLaunchKernelGGL(attend_bf16<1>, grid, dim3(64), 0, st, A); break;
-    case 2: hipLaunchKernelGGL(attend_bf16<2>, grid, dim3(128), 0, st, A); break;
-    case 4: hipLaunchKernelGGL(attend_bf16<4>, grid, dim3(256), 0, st, A); break;
-    case 8: hipLaunchKernelGGL(attend_bf16<8>, grid, dim3(512), 0, st, A); break;
-    default:
-      set_error("%s: unsupported wave count %d", name, P.NW);
-      return CSAHCA_ENOTSUP;
+  A.n_hg = P.n_hg;
+  A.n_work = P.n_work;
+  A.per_xcd = P.per_xcd;
+  if (P.lds > 160 * 1024 - 1024) {
+    set_error("%s: a split needs too much LDS", name);
+    return CSAHCA_ENOTSUP;
   }
+  const int lrc = csa ? launch_attend_nw<true>(P, A, st) : launch_attend_nw<false>(P, A, st);
+  if (lrc != CSAHCA_OK) return lrc;
   int rc = launch_status(name);
   if (rc != CSAHCA_OK || P.n_splits == 1) return rc;
   const long long nqh = (long long)B * Tq * n_h;

@@ -21,17 +21,20 @@
 // At least K keys are >= T1 (one per selected group), so the K-th largest key overall is
 // >= T1 and every top-K key lies in one of exactly K selected groups.  The exact top-K is
 // then taken from those K*16 candidates.  Both K-th-largest searches are MSB-first radix
-// selects over LDS that skip the bits all remaining candidates share.  The candidates are
-// kept in index order, so the output comes out ascending without a sort.
+// selects over register-resident keys (an LDS histogram per 11-bit digit) that skip the
+// bits all remaining candidates share.  The candidates are kept in index order, so the
+// output comes out ascending without a sort.
 #include "common.hpp"
 
 namespace {
 
 constexpr int GROUP = 16;           // keys per group maximum
 constexpr int SEL_THREADS = 1024;
-constexpr int SEL_MAX_KEYS = 16384; // LDS capacity of the selector (128 KiB of keys)
+constexpr int KPT = 16;                              // selection keys per thread (registers)
+constexpr int SEL_MAX_KEYS = SEL_THREADS * KPT;      // 16384 group maxima per query
 constexpr int MAX_NC = GROUP * SEL_MAX_KEYS;
-constexpr int MAX_K = SEL_MAX_KEYS / GROUP;
+constexpr int MAX_K = SEL_THREADS;                   // one candidate group per thread
+static_assert(KPT == GROUP, "a thread scans exactly one candidate group");
 
 CSAHCA_DEV int visible_entries(const int* q_pos, int b, int t, int m, int N_c) {
   const long long p = (long long)q_pos[b] + t;
@@ -193,8 +196,10 @@ __global__ __launch_bounds__(256) void index_score_f32(
 // ---------------------------------------------------------------------------------------
 // selection
 // ---------------------------------------------------------------------------------------
+constexpr int NBIN = 2048;  // radix digit of 11 bits
+
 struct SelScratch {
-  uint32_t hist[256];
+  uint32_t hist[NBIN];
   uint64_t red_and[SEL_THREADS / 64];
   uint64_t red_or[SEL_THREADS / 64];
   uint32_t scan[SEL_THREADS / 64];
@@ -230,15 +235,18 @@ CSAHCA_DEV uint32_t block_exclusive_scan(uint32_t v, SelScratch& sc, uint32_t& t
   return res;
 }
 
-// K-th largest (1-based) of n distinct keys in LDS.
-CSAHCA_DEV uint64_t radix_select_kth(const uint64_t* keys, int n, int kth, SelScratch& sc) {
+// K-th largest (1-based) of the distinct nonzero keys the workgroup holds in registers
+// (KPT per thread; 0 = empty).  MSB-first radix select with 11-bit digits that starts
+// each round at the highest bit on which the remaining candidates still differ.
+CSAHCA_DEV uint64_t radix_select_kth(const uint64_t (&kr)[KPT], int kth, SelScratch& sc) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint64_t prefix = 0, mask = 0;
   for (;;) {
     uint64_t a = ~0ull, o = 0ull;
-    for (int i = threadIdx.x; i < n; i += SEL_THREADS) {
-      const uint64_t k = keys[i];
-      if ((k & mask) == prefix) {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const uint64_t k = kr[j];
+      if (k != 0ull && (k & mask) == prefix) {
         a &= k;
         o |= k;
       }
@@ -252,6 +260,7 @@ CSAHCA_DEV uint64_t radix_select_kth(const uint64_t* keys, int n, int kth, SelSc
       sc.red_and[wave] = a;
       sc.red_or[wave] = o;
     }
+    for (int i = threadIdx.x; i < NBIN; i += SEL_THREADS) sc.hist[i] = 0;
     __syncthreads();
     a = ~0ull;
     o = 0ull;
@@ -266,38 +275,26 @@ CSAHCA_DEV uint64_t radix_select_kth(const uint64_t* keys, int n, int kth, SelSc
       return a;  // one key left
     }
     const int hb = 63 - __builtin_clzll(diff);
-    const int sh = hb >= 7 ? hb - 7 : 0;
-    for (int i = threadIdx.x; i < 256; i += SEL_THREADS) sc.hist[i] = 0;
-    __syncthreads();
-    for (int i = threadIdx.x; i < n; i += SEL_THREADS) {
-      const uint64_t k = keys[i];
-      if ((k & mask) == prefix) atomicAdd(&sc.hist[(uint32_t)(k >> sh) & 255u], 1u);
+    const int sh = hb >= 10 ? hb - 10 : 0;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const uint64_t k = kr[j];
+      if (k != 0ull && (k & mask) == prefix)
+        atomicAdd(&sc.hist[(uint32_t)(k >> sh) & (NBIN - 1)], 1u);
     }
     __syncthreads();
-    if (wave == 0) {
-      // lane owns bins 4*lane .. 4*lane+3; count the keys in higher bins
-      uint32_t h[4];
-      uint32_t local = 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        h[j] = sc.hist[4 * lane + j];
-        local += h[j];
-      }
-      uint32_t suf = local;  // inclusive suffix sum over lanes >= this one
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const uint32_t y = __shfl_down(suf, d, 64);
-        if (lane + d < 64) suf += y;
-      }
-      uint32_t above = suf - local;
-#pragma unroll
-      for (int j = 3; j >= 0; --j) {
-        if (above < (uint32_t)kth && (uint32_t)kth <= above + h[j]) {
-          sc.found_digit = 4 * lane + j;
-          sc.found_kth = kth - above;
-        }
-        above += h[j];
-      }
+    // thread t owns bins NBIN-1-2t and NBIN-2-2t; thread order = descending digit
+    const uint32_t h0 = sc.hist[NBIN - 1 - 2 * threadIdx.x];
+    const uint32_t h1 = sc.hist[NBIN - 2 - 2 * threadIdx.x];
+    uint32_t tot;
+    const uint32_t above = block_exclusive_scan(h0 + h1, sc, tot);
+    const uint32_t kk = (uint32_t)kth;
+    if (above < kk && kk <= above + h0) {
+      sc.found_digit = NBIN - 1 - 2 * threadIdx.x;
+      sc.found_kth = kk - above;
+    } else if (above + h0 < kk && kk <= above + h0 + h1) {
+      sc.found_digit = NBIN - 2 - 2 * threadIdx.x;
+      sc.found_kth = kk - above - h0;
     }
     __syncthreads();
     const uint32_t dsel = sc.found_digit;
@@ -305,7 +302,6 @@ CSAHCA_DEV uint64_t radix_select_kth(const uint64_t* keys, int n, int kth, SelSc
     const uint64_t hi_mask = hb == 63 ? 0ull : (~0ull << (hb + 1));
     prefix = (a & hi_mask) | ((uint64_t)dsel << sh);
     mask = ~0ull << sh;
-    __syncthreads();
   }
 }
 
@@ -313,7 +309,6 @@ __global__ __launch_bounds__(SEL_THREADS) void select_topk(
     const float* __restrict__ scores, const uint64_t* __restrict__ gkeys,
     const int* __restrict__ q_pos, int m, int Tq, int N_c, int NG, int k,
     int* __restrict__ topk_idx, float* __restrict__ topk_score) {
-  extern __shared__ uint64_t sel_keys[];  // [SEL cap]
   __shared__ SelScratch sc;
   __shared__ int glist[MAX_K];
   const int q = blockIdx.x;
@@ -331,66 +326,55 @@ __global__ __launch_bounds__(SEL_THREADS) void select_topk(
     }
     return;
   }
+  // group maxima: thread t holds groups t*KPT .. t*KPT+KPT-1
   const int ng = cdiv(V, GROUP);
   const uint64_t* grow = gkeys + (size_t)q * NG;
-  for (int i = threadIdx.x; i < ng; i += SEL_THREADS) sel_keys[i] = grow[i];
-  __syncthreads();
+  uint64_t kr[KPT];
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const int gi = (int)threadIdx.x * KPT + j;
+    kr[j] = gi < ng ? grow[gi] : 0ull;
+  }
   // With fewer groups than K every group is a candidate (T1 = 0 keeps every usable key).
-  const uint64_t T1 = keff < ng ? radix_select_kth(sel_keys, ng, keff, sc) : 0ull;
+  const uint64_t T1 = keff < ng ? radix_select_kth(kr, keff, sc) : 0ull;
 
   // exactly min(K, ng) groups have a maximum >= T1; list them in index order
   uint32_t ngl;
   {
-    const int per = cdiv(ng, SEL_THREADS);
-    const int lo = min(ng, (int)threadIdx.x * per), hi = min(ng, lo + per);
-    uint32_t cnt = 0;
-    for (int i = lo; i < hi; ++i) cnt += sel_keys[i] >= T1;
-    uint32_t off = block_exclusive_scan(cnt, sc, ngl);
-    for (int i = lo; i < hi; ++i)
-      if (sel_keys[i] >= T1) glist[off++] = i;
-    __syncthreads();
-  }
-  // candidates: the keys >= T1 inside the selected groups, in index order
-  constexpr int CPT = SEL_MAX_KEYS / SEL_THREADS;  // candidates per thread (<= 16)
-  uint32_t n2;
-  {
-    const int nc = (int)ngl * GROUP;
-    const int per = cdiv(nc, SEL_THREADS);
-    const int lo = min(nc, (int)threadIdx.x * per), hi = min(nc, lo + per);
-    uint64_t mine[CPT];
     uint32_t cnt = 0;
 #pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-      mine[j] = 0ull;
-      const int i = lo + j;
-      if (i < hi) {
-        const int e = glist[i / GROUP] * GROUP + (i % GROUP);
-        if (e < V) {
-          const uint64_t key = entry_key(srow[e], (uint32_t)e);
-          if (key >= T1) {
-            mine[j] = key;
-            ++cnt;
-          }
-        }
+    for (int j = 0; j < KPT; ++j) cnt += (kr[j] != 0ull && kr[j] >= T1);
+    uint32_t off = block_exclusive_scan(cnt, sc, ngl);
+#pragma unroll
+    for (int j = 0; j < KPT; ++j)
+      if (kr[j] != 0ull && kr[j] >= T1) glist[off++] = (int)threadIdx.x * KPT + j;
+    __syncthreads();
+  }
+  // candidates: thread t scans the 16 keys of listed group t, keeping those >= T1
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) kr[j] = 0ull;
+  if (threadIdx.x < ngl) {
+    const int e0 = glist[threadIdx.x] * GROUP;
+#pragma unroll
+    for (int j = 0; j < GROUP; ++j) {
+      const int e = e0 + j;
+      if (e < V) {
+        const uint64_t key = entry_key(srow[e], (uint32_t)e);
+        kr[j] = key >= T1 ? key : 0ull;
       }
     }
-    uint32_t off = block_exclusive_scan(cnt, sc, n2);
-#pragma unroll
-    for (int j = 0; j < CPT; ++j)
-      if (mine[j] != 0ull) sel_keys[off++] = mine[j];
-    __syncthreads();
   }
-  const uint64_t T2 = radix_select_kth(sel_keys, (int)n2, keff, sc);
+  const uint64_t T2 = radix_select_kth(kr, keff, sc);
   {
-    const int per = cdiv((int)n2, SEL_THREADS);
-    const int lo = min((int)n2, (int)threadIdx.x * per), hi = min((int)n2, lo + per);
     uint32_t cnt = 0;
-    for (int i = lo; i < hi; ++i) cnt += sel_keys[i] >= T2;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) cnt += (kr[j] != 0ull && kr[j] >= T2);
     uint32_t total;
     uint32_t off = block_exclusive_scan(cnt, sc, total);
-    for (int i = lo; i < hi; ++i) {
-      const uint64_t key = sel_keys[i];
-      if (key >= T2) {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const uint64_t key = kr[j];
+      if (key != 0ull && key >= T2) {
         orow[off] = (int)key_index(key);
         if (osc) osc[off] = key_score((uint32_t)(key >> 32));
         ++off;
@@ -508,16 +492,7 @@ int select_impl(const float* scores, const uint64_t* gkeys, const int* q_pos, in
   using namespace csahca;
   const int nq = B * Tq;
   const int NG = cdiv(N_c, GROUP);
-  const int cap = max(NG, min(k, N_c) * GROUP);
-  const size_t lds = (size_t)min(cap, SEL_MAX_KEYS) * sizeof(uint64_t);
-  static bool attr_set = false;
-  if (!attr_set) {
-    if (hipFuncSetAttribute((const void*)select_topk, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            SEL_MAX_KEYS * (int)sizeof(uint64_t)) != hipSuccess)
-      return fail(CSAHCA_ELAUNCH, "lightning_index_select: cannot raise the LDS limit");
-    attr_set = true;
-  }
-  hipLaunchKernelGGL(select_topk, dim3((unsigned)nq), dim3(SEL_THREADS), lds, st, scores,
+  hipLaunchKernelGGL(select_topk, dim3((unsigned)nq), dim3(SEL_THREADS), 0, st, scores,
                      gkeys, q_pos, m, Tq, N_c, NG, k, topk_idx, topk_score);
   return launch_status("lightning_index_select");
 }

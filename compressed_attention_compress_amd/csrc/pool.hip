@@ -121,6 +121,94 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ X,
   Vec8<T>::store(out + (long long)b * out_bs + (long long)i * c + (long long)cv * VEC, res);
 }
 
+// Few blocks (a cache append at decode): one workgroup per (sequence, block).  Its
+// threads split the block's m tokens into S contiguous sub-ranges per 8-channel slice,
+// each with its own running softmax; the S partial states are merged in LDS in a fixed
+// order, so the result does not depend on timing.
+template <typename T>
+__global__ __launch_bounds__(1024) void pool_block_kernel(const T* __restrict__ X,
+                                                         const T* __restrict__ Z,
+                                                         const float* __restrict__ P,
+                                                         T* __restrict__ out, int N, int c,
+                                                         int m, int S, long long in_bs,
+                                                         long long out_bs) {
+  extern __shared__ float part[];  // [S][CV][3][VEC]
+  const int CV = c / VEC;
+  const int cv = threadIdx.x % CV, s = threadIdx.x / CV;
+  const int b = blockIdx.x / N, i = blockIdx.x % N;
+  const int span = cdiv(m, S);
+  const int j_lo = min(m, s * span), j_hi = min(m, j_lo + span);
+  const long long base = (long long)b * in_bs + (long long)i * m * c + (long long)cv * VEC;
+  float mx[VEC], sum[VEC], acc[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) {
+    mx[e] = -INFINITY;
+    sum[e] = 0.f;
+    acc[e] = 0.f;
+  }
+  for (int j0 = j_lo; j0 < j_hi; j0 += UNROLL) {
+    const int cnt = min(UNROLL, j_hi - j0);
+    Vec8<T> xv[UNROLL], zv[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      if (u < cnt) {
+        xv[u].load(X + base + (long long)(j0 + u) * c);
+        zv[u].load(Z + base + (long long)(j0 + u) * c);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      float z[UNROLL];
+      float cm = mx[e];
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+        if (u < cnt) {
+          z[u] = zv[u].get(e);
+          if (P) z[u] += P[(j0 + u) * c + cv * VEC + e];
+          cm = fmaxf(cm, z[u]);
+        }
+      }
+      const float alpha = __expf(mx[e] - cm);
+      float sm = sum[e] * alpha, a = acc[e] * alpha;
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+        if (u < cnt) {
+          const float p = __expf(z[u] - cm);
+          sm += p;
+          a = fmaf(p, xv[u].get(e), a);
+        }
+      }
+      mx[e] = cm;
+      sum[e] = sm;
+      acc[e] = a;
+    }
+  }
+  float* mine = part + ((size_t)s * CV + cv) * 3 * VEC;
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) {
+    mine[e] = mx[e];
+    mine[VEC + e] = sum[e];
+    mine[2 * VEC + e] = acc[e];
+  }
+  __syncthreads();
+  if (s != 0) return;
+  float res[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) {
+    float M = -INFINITY;
+    for (int r = 0; r < S; ++r) M = fmaxf(M, part[((size_t)r * CV + cv) * 3 * VEC + e]);
+    float sm = 0.f, a = 0.f;
+    for (int r = 0; r < S; ++r) {
+      const float* pr = part + ((size_t)r * CV + cv) * 3 * VEC;
+      const float w = __expf(pr[e] - M);  // empty sub-range: exp(-inf) = 0
+      sm = fmaf(pr[VEC + e], w, sm);
+      a = fmaf(pr[2 * VEC + e], w, a);
+    }
+    res[e] = a / sm;
+  }
+  Vec8<T>::store(out + (long long)b * out_bs + (long long)i * c + (long long)cv * VEC, res);
+}
+
 int pool_entry(const char* name, const void* kv, const void* gate, const float* pos_bias,
                void* out, int B, int n, int c, int m, int dtype, long long in_bs,
                long long out_bs, void* stream) {
@@ -142,10 +230,29 @@ int pool_entry(const char* name, const void* kv, const void* gate, const float* 
   if (!aligned16(kv) || !aligned16(gate) || !aligned16(out))
     return fail(CSAHCA_EINVAL, "pool: kv, gate and out must be 16-byte aligned");
   const long long total = (long long)B * N * (c / 8);
+  hipStream_t st = (hipStream_t)stream;
+  // few blocks of many tokens: split each block's tokens over more threads
+  int S = min(m / 8, 1024 / (c / 8));
+  if (S > 8) S = 8;
+  if (total < 32768 && S >= 2) {
+    const size_t lds = (size_t)S * (c / 8) * 3 * VEC * sizeof(float);
+    if (lds <= 65536) {
+      const unsigned grid = (unsigned)(B * N);
+      const unsigned threads = (unsigned)(S * (c / 8));
+      if (dtype == CSAHCA_BF16)
+        hipLaunchKernelGGL(pool_block_kernel<uint16_t>, dim3(grid), dim3(threads), lds, st,
+                           (const uint16_t*)kv, (const uint16_t*)gate, pos_bias, (uint16_t*)out,
+                           (int)N, c, m, S, in_bs, out_bs);
+      else
+        hipLaunchKernelGGL(pool_block_kernel<float>, dim3(grid), dim3(threads), lds, st,
+                           (const float*)kv, (const float*)gate, pos_bias, (float*)out, (int)N, c,
+                           m, S, in_bs, out_bs);
+      return launch_status(name);
+    }
+  }
   const int threads = 256;
   const long long blocks = cdiv<long long>(total, threads);
   if (blocks > 0x7FFFFFFFLL) return fail(CSAHCA_ENOTSUP, "pool: problem too large for one launch");
-  hipStream_t st = (hipStream_t)stream;
   if (dtype == CSAHCA_BF16) {
     hipLaunchKernelGGL(pool_kernel<uint16_t>, dim3((unsigned)blocks), dim3(threads), 0, st,
                        (const uint16_t*)kv, (const uint16_t*)gate, pos_bias, (uint16_t*)out,

@@ -11,6 +11,10 @@ LIB = os.path.join(HERE, "libcsahca.so")
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # device code only: inputs carry no NaNs (saves the NaN-quieting of every fmaxf), and
+    # MFMA results stay in ordinary VGPRs (no copies out of accumulation registers)
+    "-Xarch_device", "-fno-honor-nans",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wno-unused-command-line-argument",
 ]
 

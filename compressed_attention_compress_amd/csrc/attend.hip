@@ -80,13 +80,11 @@ CSAHCA_DEV void lds_reads_done_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// LDS ring depth: two tiles (one in flight while one is computed).  A deeper ring gains no
-// bandwidth here and costs registers; two 4-wave workgroups share a CU.
-constexpr int stages_for(int) { return 2; }
-
-size_t attend_lds_bytes(int NW, int RS, bool csa) {
-  const int ns = stages_for(NW);
-  return (size_t)ns * TILE * ROWB + (size_t)ns * NW * sizeof(uint32_t) +
+// LDS ring depth NS: 2 tiles when many workgroups run (two 4-wave workgroups share a CU
+// and hide each other's latency: prefill), 4 tiles when few queries are split over
+// workgroups (one workgroup per CU keeps three tiles in flight: decode).
+size_t attend_lds_bytes(int NS, int NW, int RS, bool csa) {
+  return (size_t)NS * TILE * ROWB + (size_t)NS * NW * sizeof(uint32_t) +
          (csa ? (size_t)RS * sizeof(int) : 0);
 }
 
@@ -113,7 +111,7 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 // ahead of the MFMAs that use them, which bounds the registers in use so that two
 // workgroups share a CU.
 template <int NW, int NS, bool CSA>
-__global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attend_bf16(AttnArgs a) {
+__global__ __launch_bounds__(NW * 64, (NW == 4 && NS == 2) ? 2 : 1) void attend_bf16(AttnArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   constexpr int LPW = TILE / NW;  // rows each wave loads per tile
   constexpr float LAZY = 8.f;     // log2 headroom before the running maximum moves
@@ -287,8 +285,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attend_bf16(AttnArgs
         sv[4 + i] = ok1 ? s2[i] * a.scale_log2 : -INFINITY;
         mloc = fmaxf(mloc, fmaxf(sv[i], sv[4 + i]));
       }
-      mloc = fmaxf(mloc, shfl_xor_f(mloc, 16));
-      mloc = fmaxf(mloc, shfl_xor_f(mloc, 32));
+      mloc = max_over_row_groups(mloc);
       // lazy running maximum: move it only when exceeded by more than LAZY
       const bool bump = mloc > m_run + LAZY;
       const float m_new = bump ? mloc : m_run;
@@ -301,8 +298,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attend_bf16(AttnArgs
         pe[e] = none ? 0.f : exp2f(sv[e] - m_new);  // skipped slots: exp2(-inf) = 0
         psum += pe[e];
       }
-      psum += shfl_xor_f(psum, 16);
-      psum += shfl_xor_f(psum, 32);
+      psum = sum_over_row_groups(psum);
       l_run = l_run * alpha + psum;
       m_run = m_new;
       if (__any(bump)) {
@@ -369,38 +365,46 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attend_bf16(AttnArgs
   }
 }
 
-// Merge the splits of every (query, head) by their log-sum-exp.  64 threads per pair,
-// 8 columns each; the split loop keeps 4 partial rows in flight.
+// Merge the splits of every (query, head) by their log-sum-exp.  One workgroup per pair:
+// wave w takes the splits w, w+4, ..., eight partial rows in flight per lane (8 columns
+// each); the four wave sums are then added in a fixed order.
 __global__ __launch_bounds__(256) void attend_combine(const float* __restrict__ opart,
                                                       const float* __restrict__ mlpart,
                                                       uint16_t* __restrict__ out,
-                                                      float* __restrict__ lse, long long nqh,
-                                                      int n_h, int n_splits) {
-  const long long pair = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (pair >= nqh) return;
+                                                      float* __restrict__ lse, int n_h,
+                                                      int n_splits) {
+  __shared__ float red[4][C + 4];
+  const long long pair = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const long long qrow = pair / n_h;
   const int h = (int)(pair - qrow * n_h);
   const long long pr0 = qrow * n_splits * n_h + h;  // partial row of split s: pr0 + s*n_h
   float M = -INFINITY;
-  for (int s = 0; s < n_splits; ++s) M = fmaxf(M, mlpart[(pr0 + (long long)s * n_h) * 2]);
+  for (int s = lane; s < n_splits; s += 64) M = fmaxf(M, mlpart[(pr0 + (long long)s * n_h) * 2]);
+  for (int d = 1; d < 64; d <<= 1) M = fmaxf(M, shfl_xor_f(M, d));
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float Ls = 0.f;
   if (M != -INFINITY) {
-    int s = 0;
-    for (; s + 4 <= n_splits; s += 4) {
-      f32x4 x0[4], x1[4];
-      float ms[4], ls[4];
+    for (int s0 = wave; s0 < n_splits; s0 += 32) {
+      f32x4 x0[8], x1[8];
+      float ms[8], ls[8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const long long pr = pr0 + (long long)(s + u) * n_h;
-        ms[u] = mlpart[pr * 2];
-        ls[u] = mlpart[pr * 2 + 1];
-        x0[u] = *reinterpret_cast<const f32x4*>(opart + pr * C + lane * 8);
-        x1[u] = *reinterpret_cast<const f32x4*>(opart + pr * C + lane * 8 + 4);
+      for (int u = 0; u < 8; ++u) {
+        const int s = s0 + 4 * u;
+        if (s < n_splits) {
+          const long long pr = pr0 + (long long)s * n_h;
+          ms[u] = mlpart[pr * 2];
+          ls[u] = mlpart[pr * 2 + 1];
+          x0[u] = *reinterpret_cast<const f32x4*>(opart + pr * C + lane * 8);
+          x1[u] = *reinterpret_cast<const f32x4*>(opart + pr * C + lane * 8 + 4);
+        } else {
+          ms[u] = -INFINITY;
+          ls[u] = 0.f;
+          x0[u] = x1[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < 8; ++u) {
         const float wgt = ms[u] == -INFINITY ? 0.f : exp2f(ms[u] - M);
         Ls = fmaf(wgt, ls[u], Ls);
 #pragma unroll
@@ -410,26 +414,25 @@ __global__ __launch_bounds__(256) void attend_combine(const float* __restrict__ 
         }
       }
     }
-    for (; s < n_splits; ++s) {
-      const long long pr = pr0 + (long long)s * n_h;
-      const float ms = mlpart[pr * 2], ls = mlpart[pr * 2 + 1];
-      const float wgt = ms == -INFINITY ? 0.f : exp2f(ms - M);
-      Ls = fmaf(wgt, ls, Ls);
-      const f32x4 x0 = *reinterpret_cast<const f32x4*>(opart + pr * C + lane * 8);
-      const f32x4 x1 = *reinterpret_cast<const f32x4*>(opart + pr * C + lane * 8 + 4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[i] = fmaf(wgt, x0[i], acc[i]);
-        acc[4 + i] = fmaf(wgt, x1[i], acc[4 + i]);
-      }
-    }
   }
-  const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) red[wave][lane * 8 + i] = acc[i];
+  if (lane == 0) red[wave][C] = Ls;
+  __syncthreads();
+  if (wave != 0) return;
+  float o8[8];
+  const float Lt = ((red[0][C] + red[1][C]) + red[2][C]) + red[3][C];
+  const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int c = lane * 8 + i;
+    o8[i] = (((red[0][c] + red[1][c]) + red[2][c]) + red[3][c]) * inv;
+  }
   u32x4 o;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i] * inv, acc[2 * i + 1] * inv);
+  for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(o8[2 * i], o8[2 * i + 1]);
   *reinterpret_cast<u32x4*>(out + (qrow * n_h + h) * C + lane * 8) = o;
-  if (lse && lane == 0) lse[qrow * n_h + h] = Ls > 0.f ? (M + __log2f(Ls)) * LN2 : -INFINITY;
+  if (lse && lane == 0) lse[qrow * n_h + h] = Lt > 0.f ? (M + __log2f(Lt)) * LN2 : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -531,14 +534,14 @@ __global__ __launch_bounds__(256) void attend_f32(AttnF32Args a) {
 // host side
 // ---------------------------------------------------------------------------------------
 struct Plan {
-  int Tg, HPW, NW, n_hg, n_slots, n_splits, RS, nqg, n_work, per_xcd;
+  int Tg, HPW, NW, NS, n_hg, n_slots, n_splits, RS, nqg, n_work, per_xcd;
   size_t opart_bytes, ml_bytes, ws, lds;
 };
 
 // Launch shape.  A workgroup holds up to 64 heads (4 waves; 8 waves when two prefill
-// queries share the rows).  The rows of a query are split over workgroups until about
-// 256 workgroups exist, but never below 128 rows per split: each split writes an fp32
-// partial of HPW x 512 floats, so shorter splits would move more partial bytes than rows.
+// queries share the rows).  When the queries alone give fewer than 256 workgroups their
+// rows are split over more (one per CU, each keeping three tiles in flight), but never
+// below 96 rows per split: each split writes an fp32 partial of HPW x 512 floats.
 Plan make_plan(int B, int Tq, int n_h, int n_slots_c, int W, bool csa) {
   Plan P;
   P.Tg = 1;
@@ -551,9 +554,10 @@ Plan make_plan(int B, int Tq, int n_h, int n_slots_c, int W, bool csa) {
   P.n_slots = n_slots_c + W + P.Tg - 1;
   P.nqg = cdiv(Tq, P.Tg);
   const long long base = (long long)P.n_hg * B * P.nqg;
+  P.NS = (P.NW == 4 && base < 256) ? 4 : 2;
   const int ntile = cdiv(P.n_slots, TILE);
-  const int min_tiles = 4;
-  long long want = cdiv<long long>(256, base);
+  const int min_tiles = 3;
+  const long long want = cdiv<long long>(256, base);
   const int maxs = ntile / min_tiles > 1 ? ntile / min_tiles : 1;
   int ns = (int)(want < maxs ? want : maxs);
   if (ns < 1) ns = 1;
@@ -565,13 +569,12 @@ Plan make_plan(int B, int Tq, int n_h, int n_slots_c, int W, bool csa) {
   P.opart_bytes = P.n_splits > 1 ? csahca::align_up((size_t)(nqh * P.n_splits * C * 4), 256) : 0;
   P.ml_bytes = P.n_splits > 1 ? csahca::align_up((size_t)(nqh * P.n_splits * 2 * 4), 256) : 0;
   P.ws = P.opart_bytes + P.ml_bytes;
-  P.lds = attend_lds_bytes(P.NW, P.RS, csa);
+  P.lds = attend_lds_bytes(P.NS, P.NW, P.RS, csa);
   return P;
 }
 
-template <int NW, bool CSA>
+template <int NW, int NS, bool CSA>
 int launch_attend(const Plan& P, const AttnArgs& A, hipStream_t st) {
-  constexpr int NS = stages_for(NW);
   static bool attr_set = false;
   if (!attr_set) {
     if (hipFuncSetAttribute((const void*)attend_bf16<NW, NS, CSA>,
@@ -587,10 +590,10 @@ int launch_attend(const Plan& P, const AttnArgs& A, hipStream_t st) {
 template <bool CSA>
 int launch_attend_nw(const Plan& P, const AttnArgs& A, hipStream_t st) {
   switch (P.NW) {
-    case 1: return launch_attend<1, CSA>(P, A, st);
-    case 2: return launch_attend<2, CSA>(P, A, st);
-    case 4: return launch_attend<4, CSA>(P, A, st);
-    case 8: return launch_attend<8, CSA>(P, A, st);
+    case 1: return launch_attend<1, 2, CSA>(P, A, st);
+    case 2: return launch_attend<2, 2, CSA>(P, A, st);
+    case 4: return P.NS == 4 ? launch_attend<4, 4, CSA>(P, A, st) : launch_attend<4, 2, CSA>(P, A, st);
+    case 8: return launch_attend<8, 2, CSA>(P, A, st);
     default: return csahca::fail(CSAHCA_ENOTSUP, "attend: unsupported wave count");
   }
 }
@@ -713,8 +716,8 @@ int attend_impl(const char* name, bool csa, const void* q, const void* ckv, cons
   int rc = launch_status(name);
   if (rc != CSAHCA_OK || P.n_splits == 1) return rc;
   const long long nqh = (long long)B * Tq * n_h;
-  hipLaunchKernelGGL(attend_combine, dim3((unsigned)cdiv<long long>(nqh, 4)), dim3(256), 0, st,
-                     A.opart, A.mlpart, A.out, lse, nqh, n_h, P.n_splits);
+  hipLaunchKernelGGL(attend_combine, dim3((unsigned)nqh), dim3(256), 0, st, A.opart, A.mlpart,
+                     A.out, lse, n_h, P.n_splits);
   return launch_status(name);
 }
 

@@ -97,6 +97,66 @@ CSAHCA_DEV uint64_t shfl_xor_u64(uint64_t v, int m) {
 
 CSAHCA_DEV uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 
+// x[l] + x[l ^ 16] + x[l ^ 32] + x[l ^ 48] in every lane (gfx950 permlane swaps, no LDS);
+// the additions happen in the same order in all four lanes, so they agree bit for bit.
+CSAHCA_DEV float sum_over_row_groups(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// max over lanes l, l^16, l^32, l^48
+CSAHCA_DEV float max_over_row_groups(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// max over the 16 lanes of each row (DPP: xor 1, xor 2, rotate 4, rotate 8)
+CSAHCA_DEV float row16_max(float x) {
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false)));
+  return x;
+}
+
+// inclusive prefix sum over the 64 lanes of a wave (DPP: shifts inside each row of 16,
+// then row broadcasts; lanes without a source add 0)
+CSAHCA_DEV uint32_t wave_incl_scan(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, true);  // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, true);  // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, true);  // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, true);  // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false); // row_bcast:15
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false); // row_bcast:31
+  return v;
+}
+
+// bitwise AND / OR over the 64 lanes of a wave, result in every lane
+CSAHCA_DEV uint32_t wave_and(uint32_t x) {
+  x &= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false);
+  x &= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false);
+  x &= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x124, 0xF, 0xF, false);
+  x &= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x128, 0xF, 0xF, false);
+  const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = a[0] & a[1];
+  const auto b = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return b[0] & b[1];
+}
+CSAHCA_DEV uint32_t wave_or(uint32_t x) {
+  x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false);
+  x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false);
+  x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x124, 0xF, 0xF, false);
+  x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x128, 0xF, 0xF, false);
+  const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = a[0] | a[1];
+  const auto b = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return b[0] | b[1];
+}
+
 // ceil-div for host and device
 template <typename T>
 __host__ __device__ inline T cdiv(T a, T b) {

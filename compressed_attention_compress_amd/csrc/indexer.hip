@@ -6,11 +6,12 @@
 // Open-Source Frontier Model" (lesson 6.7): the indexer runs in low precision and can
 // pick no more entries than exist.
 //
-// Scoring (index_score_fp8): the q_I . K_I contraction runs on MFMA
-// (v_mfma_f32_16x16x32_fp8_fp8; A = 16 indexer heads x 32 dims, B = 32 dims x 16 keys).
-// Each lane streams 32 contiguous bytes of one key row straight from HBM into the B
-// operand (no LDS); the dimension order inside the contraction is permuted identically
-// for A and B, which leaves the dot products unchanged.  ReLU, the head weights and the
+// Scoring (index_score_fp8): the q_I . K_I contraction runs on MFMA (for c_I = 128 one
+// v_mfma_scale_f32_16x16x128_f8f6f4 with unit block scales per 16 heads x 16 keys; for
+// c_I = 32/64 v_mfma_f32_16x16x32_fp8_fp8).  Each lane streams C_I/4 contiguous bytes of
+// one key row straight from HBM into the B operand (no LDS); A takes the same bytes of
+// the indexer query row, so whatever order the instruction assigns to the contraction
+// dimension, it is the same for both operands and the dot products are exact.  ReLU, the head weights and the
 // cross-head sum are applied to the MFMA accumulators in registers.  Every score is
 // written once (fp32) and every group of 16 consecutive keys also writes its maximum
 // 64-bit selection key.
@@ -27,6 +28,13 @@
 #include "common.hpp"
 
 namespace {
+
+#ifndef CSAHCA_SCORE_WGS
+#define CSAHCA_SCORE_WGS 512  // scoring workgroups to aim for (about two per CU)
+#endif
+#ifndef CSAHCA_SCORE_CONTIG
+#define CSAHCA_SCORE_CONTIG 0  // 1: each wave scores a contiguous quarter of its chunk
+#endif
 
 constexpr int GROUP = 16;           // keys per group maximum
 constexpr int SEL_THREADS = 1024;
@@ -46,19 +54,32 @@ CSAHCA_DEV int visible_entries(const int* q_pos, int b, int t, int m, int N_c) {
 // ---------------------------------------------------------------------------------------
 // scoring, FP8 E4M3FN keys on MFMA
 // ---------------------------------------------------------------------------------------
+// QPW queries per workgroup of 4 waves.  QPW = 1: the four waves split the key blocks of
+// one query (decode).  QPW = 4: each wave scores its own query over the same key blocks
+// (prefill; the repeated key reads hit in cache).  A wave walks its blocks with PF blocks
+// of keys in flight in registers: block k is scored while blocks k+1 .. k+PF-1 load.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
 template <int C_I>
-struct KeySlice {  // the C_I/4 contiguous bytes one lane holds: KS 8-byte MFMA operands
+struct KeyOperand;  // the C_I/4 contiguous key bytes one lane contributes per 16-key block
+
+template <>
+struct KeyOperand<128> {  // one v_mfma_scale_f32_16x16x128_f8f6f4 per head block
+  i32x8 v;
+  CSAHCA_DEV void load(const uint8_t* p) { v = *reinterpret_cast<const i32x8*>(p); }
+  CSAHCA_DEV void zero() { v = i32x8{0, 0, 0, 0, 0, 0, 0, 0}; }
+  CSAHCA_DEV static f32x4 mma(const KeyOperand& a, const KeyOperand& b, f32x4 c) {
+    // operand formats 0 = FP8 E4M3; block scales 127 = 2^0 (E8M0), i.e. no scaling
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a.v, b.v, c, 0, 0, 0, 127, 0, 127);
+  }
+};
+
+template <int C_I>
+struct KeyOperand {  // C_I in {32, 64}: v_mfma_f32_16x16x32_fp8_fp8, C_I/32 K-steps
   static constexpr int KS = C_I / 32;
   long v[KS];
   CSAHCA_DEV void load(const uint8_t* p) {
-    if constexpr (KS == 4) {
-      const u32x4 a = *reinterpret_cast<const u32x4*>(p);
-      const u32x4 b = *reinterpret_cast<const u32x4*>(p + 16);
-      v[0] = (long)(((uint64_t)a[1] << 32) | a[0]);
-      v[1] = (long)(((uint64_t)a[3] << 32) | a[2]);
-      v[2] = (long)(((uint64_t)b[1] << 32) | b[0]);
-      v[3] = (long)(((uint64_t)b[3] << 32) | b[2]);
-    } else if constexpr (KS == 2) {
+    if constexpr (KS == 2) {
       const u32x4 a = *reinterpret_cast<const u32x4*>(p);
       v[0] = (long)(((uint64_t)a[1] << 32) | a[0]);
       v[1] = (long)(((uint64_t)a[3] << 32) | a[2]);
@@ -71,20 +92,23 @@ struct KeySlice {  // the C_I/4 contiguous bytes one lane holds: KS 8-byte MFMA 
 #pragma unroll
     for (int i = 0; i < KS; ++i) v[i] = 0;
   }
+  CSAHCA_DEV static f32x4 mma(const KeyOperand& a, const KeyOperand& b, f32x4 c) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      c = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a.v[ks], b.v[ks], c, 0, 0, 0);
+    return c;
+  }
 };
 
-// QPW queries per workgroup of 4 waves.  QPW = 1: the four waves split the key blocks of
-// one query (decode).  QPW = 4: each wave scores its own query over the same key blocks
-// (prefill; the repeated key reads hit in cache).
-template <int C_I, int HB, int QPW, int U>
+template <int C_I, int HB, int QPW, int PF>
 __global__ __launch_bounds__(256) void index_score_fp8(
     const uint8_t* __restrict__ qI, const float* __restrict__ w, const uint8_t* __restrict__ KI,
     const int* __restrict__ q_pos, int m, int Tq, int N_c, int CH, int nq, int NG,
     float* __restrict__ scores, uint64_t* __restrict__ gkeys) {
-  constexpr int KS = C_I / 32;
   constexpr int NIH = HB * 16;
   constexpr int WPQ = 4 / QPW;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   const int q = blockIdx.y * QPW + wave / WPQ;
   const int sub = wave % WPQ;
   if (q >= nq) return;  // this kernel has no barriers: a finished wave may leave
@@ -95,8 +119,9 @@ __global__ __launch_bounds__(256) void index_score_fp8(
   if (e_begin >= e_end) return;
 
   const int row = lane & 15, g = lane >> 4;
-  // A operand: indexer query of head (16*hb + row), dims [g*C_I/4, (g+1)*C_I/4)
-  KeySlice<C_I> a[HB];
+  // A operand: indexer query of head (16*hb + row), dims [g*C_I/4, (g+1)*C_I/4); the same
+  // dims of a key row form the B operand, so the dot products are those of the full rows
+  KeyOperand<C_I> a[HB];
   const uint8_t* qp = qI + (size_t)q * NIH * C_I;
 #pragma unroll
   for (int hb = 0; hb < HB; ++hb) a[hb].load(qp + (hb * 16 + row) * C_I + g * (C_I / 4));
@@ -107,53 +132,69 @@ __global__ __launch_bounds__(256) void index_score_fp8(
 #pragma unroll
     for (int i = 0; i < 4; ++i) wr[hb][i] = w[(size_t)q * NIH + hb * 16 + 4 * g + i];
 
-  const uint8_t* kb = KI + (size_t)b * N_c * C_I;
+  const uint8_t* kb = KI + (size_t)b * N_c * C_I + g * (C_I / 4);
   float* srow = scores + (size_t)q * N_c;
   uint64_t* grow = gkeys + (size_t)q * NG;
   const int nblk = cdiv(e_end - e_begin, GROUP);
+#if CSAHCA_SCORE_CONTIG
+  // block k of this wave is sub*per + k
+  const int per = cdiv(nblk, WPQ);
+  const int nmine = max(0, min(per, nblk - sub * per));
+  auto blk_of = [&](int k) { return sub * per + k; };
+#else
+  const int nmine = nblk > sub ? cdiv(nblk - sub, WPQ) : 0;  // blocks sub, sub+WPQ, ...
+  auto blk_of = [&](int k) { return sub + k * WPQ; };
+#endif
 
-  for (int blk0 = sub; blk0 < nblk; blk0 += WPQ * U) {
-    KeySlice<C_I> kf[U];
+  // blocks past the end load a valid row instead (their scores are never used)
+  auto load_block = [&](KeyOperand<C_I>& dst, int k) {
+    const int e = min(e_begin + blk_of(min(k, nmine - 1)) * GROUP + row, e_end - 1);
+    dst.load(kb + (size_t)e * C_I);
+  };
+  // two register buffers of PF blocks: while one is scored the other is in flight, so
+  // every load has a full iteration of scoring to arrive
+  KeyOperand<C_I> kf0[PF], kf1[PF];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int e = e_begin + (blk0 + u * WPQ) * GROUP + row;
-      if (blk0 + u * WPQ < nblk && e < e_end)
-        kf[u].load(kb + (size_t)e * C_I + g * (C_I / 4));
-      else
-        kf[u].zero();
-    }
+  for (int u = 0; u < PF; ++u) {
+    load_block(kf0[u], u);
+    load_block(kf1[u], PF + u);
+  }
+  auto score_blocks = [&](KeyOperand<C_I>(&kf)[PF], int k0) {
+    f32x4 acc[PF][HB];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int blk = blk0 + u * WPQ;
-      if (blk >= nblk) break;  // wave-uniform
-      f32x4 acc[HB];
+    for (int u = 0; u < PF; ++u)
 #pragma unroll
-      for (int hb = 0; hb < HB; ++hb) acc[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int hb = 0; hb < HB; ++hb) acc[u][hb] = KeyOperand<C_I>::mma(a[hb], kf[u], f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
+    for (int u = 0; u < PF; ++u) load_block(kf[u], k0 + 2 * PF + u);  // refill: two rounds ahead
 #pragma unroll
-        for (int hb = 0; hb < HB; ++hb)
-          acc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a[hb].v[ks], kf[u].v[ks],
-                                                                acc[hb], 0, 0, 0);
-      // lane holds key (row) for heads 16*hb + 4*g + i
-      float part = 0.f;
+    for (int u = 0; u < PF; ++u) {
+      const int k = k0 + u;
+      // lane holds key (row) for heads 16*hb + 4*g + i; sum over heads as a balanced tree
+      float t[4 * HB];
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) part = fmaf(wr[hb][i], fmaxf(acc[hb][i], 0.f), part);
-      part += shfl_xor_f(part, 16);
-      part += shfl_xor_f(part, 32);
-      const int e0 = e_begin + blk * GROUP;
+        for (int i = 0; i < 4; ++i) t[4 * hb + i] = wr[hb][i] * fmaxf(acc[u][hb][i], 0.f);
+#pragma unroll
+      for (int wdt = 2 * HB; wdt >= 1; wdt /= 2)
+#pragma unroll
+        for (int v = 0; v < wdt; ++v) t[v] += t[v + wdt];
+      const float score = sum_over_row_groups(t[0]);  // same value in lanes row, row+16, ...
+      const int e0 = e_begin + blk_of(k) * GROUP;
       const int e = e0 + row;
-      const bool valid = e < e_end;
-      if (g == 0 && valid) srow[e] = part;
-      uint64_t key = valid ? entry_key(part, (uint32_t)e) : 0ull;
-      key = umax64(key, shfl_xor_u64(key, 1));
-      key = umax64(key, shfl_xor_u64(key, 2));
-      key = umax64(key, shfl_xor_u64(key, 4));
-      key = umax64(key, shfl_xor_u64(key, 8));
-      if (lane == 0) grow[e0 / GROUP] = key;
+      const bool valid = k < nmine && e < e_end;
+      if (g == 0 && valid) srow[e] = score;
+      // group maximum: the best score of the 16 keys, lowest index among equal scores
+      const float sv = valid ? score : -INFINITY;
+      const float best = row16_max(sv);
+      const uint64_t hit = __ballot(valid && sv == best) & 0xFFFFull;
+      if (lane == 0 && hit != 0ull) grow[e0 / GROUP] = entry_key(best, (uint32_t)(e0 + __builtin_ctzll(hit)));
     }
+  };
+  for (int k0 = 0; k0 < nmine; k0 += 2 * PF) {
+    score_blocks(kf0, k0);
+    if (k0 + PF < nmine) score_blocks(kf1, k0 + PF);
   }
 }
 
@@ -197,111 +238,124 @@ __global__ __launch_bounds__(256) void index_score_f32(
 // selection
 // ---------------------------------------------------------------------------------------
 constexpr int NBIN = 2048;  // radix digit of 11 bits
+constexpr int NWAVE = SEL_THREADS / 64;
 
 struct SelScratch {
-  uint32_t hist[NBIN];
-  uint64_t red_and[SEL_THREADS / 64];
-  uint64_t red_or[SEL_THREADS / 64];
-  uint32_t scan[SEL_THREADS / 64];
+  uint32_t hist[2][NBIN];
+  uint64_t red_and[NWAVE];
+  uint64_t red_or[NWAVE];
+  uint32_t scan[NWAVE];
+  uint32_t total;
   uint32_t found_digit;
   uint32_t found_kth;
-  uint32_t total;
+  uint32_t found_count;
+  uint64_t result;
 };
 
 // exclusive prefix sum of v over the workgroup, in thread order; also returns the total
 CSAHCA_DEV uint32_t block_exclusive_scan(uint32_t v, SelScratch& sc, uint32_t& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t x = v;
+  const uint32_t incl = wave_incl_scan(v);
+  if (lane == 63) sc.scan[wave] = incl;
+  __syncthreads();
+  uint32_t before = 0, all = 0;
 #pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t y = __shfl_up(x, d, 64);
-    if (lane >= d) x += y;
+  for (int i = 0; i < NWAVE; ++i) {
+    const uint32_t x = sc.scan[i];
+    before += i < wave ? x : 0u;
+    all += x;
   }
-  if (lane == 63) sc.scan[wave] = x;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t run = 0;
-    for (int i = 0; i < SEL_THREADS / 64; ++i) {
-      const uint32_t tmp = sc.scan[i];
-      sc.scan[i] = run;
-      run += tmp;
-    }
-    sc.total = run;
-  }
-  __syncthreads();
-  total = sc.total;
-  const uint32_t res = sc.scan[wave] + x - v;
-  __syncthreads();
-  return res;
+  total = all;
+  __syncthreads();  // sc.scan may be reused right after
+  return before + incl - v;
 }
 
 // K-th largest (1-based) of the distinct nonzero keys the workgroup holds in registers
-// (KPT per thread; 0 = empty).  MSB-first radix select with 11-bit digits that starts
-// each round at the highest bit on which the remaining candidates still differ.
+// (KPT per thread; 0 = empty).  One AND/OR reduction finds the highest bit on which the
+// keys differ; from there MSB-first radix passes of 11 bits narrow the candidates.  A
+// pass builds an LDS histogram of the digit, then every wave scans 128 digits (two per
+// lane, in descending order) and the lane whose range holds the K-th key reports the
+// digit.  The search stops as soon as that digit holds a single candidate.
 CSAHCA_DEV uint64_t radix_select_kth(const uint64_t (&kr)[KPT], int kth, SelScratch& sc) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint64_t prefix = 0, mask = 0;
-  for (;;) {
-    uint64_t a = ~0ull, o = 0ull;
+  uint32_t alo = ~0u, ahi = ~0u, olo = 0u, ohi = 0u;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    if (kr[j] != 0ull) {
+      alo &= (uint32_t)kr[j];
+      ahi &= (uint32_t)(kr[j] >> 32);
+      olo |= (uint32_t)kr[j];
+      ohi |= (uint32_t)(kr[j] >> 32);
+    }
+  }
+  alo = wave_and(alo);
+  ahi = wave_and(ahi);
+  olo = wave_or(olo);
+  ohi = wave_or(ohi);
+  if (lane == 0) {
+    sc.red_and[wave] = ((uint64_t)ahi << 32) | alo;
+    sc.red_or[wave] = ((uint64_t)ohi << 32) | olo;
+  }
+  for (int i = threadIdx.x; i < 2 * NBIN; i += SEL_THREADS) (&sc.hist[0][0])[i] = 0u;
+  __syncthreads();
+  uint64_t a = ~0ull, o = 0ull;
+#pragma unroll
+  for (int i = 0; i < NWAVE; ++i) {
+    a &= sc.red_and[i];
+    o |= sc.red_or[i];
+  }
+  const uint64_t diff = a ^ o;
+  if (diff == 0ull) return a;  // a single key
+  const int hb = 63 - __builtin_clzll(diff);
+  // bits above hb are common to every key
+  uint64_t mask = hb == 63 ? 0ull : (~0ull << (hb + 1));
+  uint64_t prefix = a & mask;
+  int buf = 0;
+  for (int sh = hb >= 10 ? hb - 10 : 0;; sh = sh >= 11 ? sh - 11 : 0) {
+    uint32_t* h = sc.hist[buf];
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
       const uint64_t k = kr[j];
-      if (k != 0ull && (k & mask) == prefix) {
-        a &= k;
-        o |= k;
-      }
+      if (k != 0ull && (k & mask) == prefix) atomicAdd(&h[(uint32_t)(k >> sh) & (NBIN - 1)], 1u);
     }
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      a &= shfl_xor_u64(a, d);
-      o |= shfl_xor_u64(o, d);
-    }
-    if (lane == 0) {
-      sc.red_and[wave] = a;
-      sc.red_or[wave] = o;
-    }
-    for (int i = threadIdx.x; i < NBIN; i += SEL_THREADS) sc.hist[i] = 0;
+    for (int i = threadIdx.x; i < NBIN; i += SEL_THREADS) sc.hist[buf ^ 1][i] = 0u;
     __syncthreads();
-    a = ~0ull;
-    o = 0ull;
-#pragma unroll
-    for (int i = 0; i < SEL_THREADS / 64; ++i) {
-      a &= sc.red_and[i];
-      o |= sc.red_or[i];
-    }
-    const uint64_t diff = a ^ o;
-    if (diff == 0ull) {
-      __syncthreads();
-      return a;  // one key left
-    }
-    const int hb = 63 - __builtin_clzll(diff);
-    const int sh = hb >= 10 ? hb - 10 : 0;
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const uint64_t k = kr[j];
-      if (k != 0ull && (k & mask) == prefix)
-        atomicAdd(&sc.hist[(uint32_t)(k >> sh) & (NBIN - 1)], 1u);
-    }
+    // this lane's two digits, descending with the thread index
+    const int d_hi = NBIN - 1 - 2 * (int)threadIdx.x;
+    const uint32_t c_hi = h[d_hi], c_lo = h[d_hi - 1];
+    const uint32_t incl = wave_incl_scan(c_hi + c_lo);
+    if (lane == 63) sc.scan[wave] = incl;
     __syncthreads();
-    // thread t owns bins NBIN-1-2t and NBIN-2-2t; thread order = descending digit
-    const uint32_t h0 = sc.hist[NBIN - 1 - 2 * threadIdx.x];
-    const uint32_t h1 = sc.hist[NBIN - 2 - 2 * threadIdx.x];
-    uint32_t tot;
-    const uint32_t above = block_exclusive_scan(h0 + h1, sc, tot);
+    uint32_t above = incl - (c_hi + c_lo);
+#pragma unroll
+    for (int i = 0; i < NWAVE; ++i) above += i < wave ? sc.scan[i] : 0u;
     const uint32_t kk = (uint32_t)kth;
-    if (above < kk && kk <= above + h0) {
-      sc.found_digit = NBIN - 1 - 2 * threadIdx.x;
+    if (above < kk && kk <= above + c_hi) {
+      sc.found_digit = d_hi;
       sc.found_kth = kk - above;
-    } else if (above + h0 < kk && kk <= above + h0 + h1) {
-      sc.found_digit = NBIN - 2 - 2 * threadIdx.x;
-      sc.found_kth = kk - above - h0;
+      sc.found_count = c_hi;
+    } else if (above + c_hi < kk && kk <= above + c_hi + c_lo) {
+      sc.found_digit = d_hi - 1;
+      sc.found_kth = kk - above - c_hi;
+      sc.found_count = c_lo;
     }
     __syncthreads();
-    const uint32_t dsel = sc.found_digit;
+    const uint64_t dsel = sc.found_digit;
     kth = (int)sc.found_kth;
-    const uint64_t hi_mask = hb == 63 ? 0ull : (~0ull << (hb + 1));
-    prefix = (a & hi_mask) | ((uint64_t)dsel << sh);
-    mask = ~0ull << sh;
+    const uint32_t count = sc.found_count;
+    prefix = (prefix & ~((uint64_t)(NBIN - 1) << sh)) | (dsel << sh);
+    mask |= (uint64_t)(NBIN - 1) << sh;
+    if (sh == 0) return prefix;  // every bit decided
+    if (count == 1) {            // the K-th key is the only candidate left
+#pragma unroll
+      for (int j = 0; j < KPT; ++j)
+        if (kr[j] != 0ull && (kr[j] & mask) == prefix) sc.result = kr[j];
+      __syncthreads();
+      const uint64_t r = sc.result;
+      __syncthreads();
+      return r;
+    }
+    buf ^= 1;
   }
 }
 
@@ -438,13 +492,14 @@ void launch_fp8(const void* q_idx, const float* w_idx, const void* k_idx, const 
   const bool decode = Tq == 1;
   const int QPW = decode ? 1 : 4;
   const int qgroups = cdiv(nq, QPW);
-  int chunks = cdiv(2048, qgroups);
+  // about two workgroups per CU, each streaming a long chunk of keys
+  int chunks = cdiv(CSAHCA_SCORE_WGS, qgroups);
   chunks = max(1, min(chunks, cdiv(N_c, 256)));
   const int CH = cdiv(cdiv(N_c, chunks), 64) * 64;
   chunks = cdiv(N_c, CH);
   dim3 grid((unsigned)chunks, (unsigned)qgroups);
   if (decode)
-    hipLaunchKernelGGL((index_score_fp8<C_I, HB, 1, 8>), grid, dim3(256), 0, st,
+    hipLaunchKernelGGL((index_score_fp8<C_I, HB, 1, 4>), grid, dim3(256), 0, st,
                        (const uint8_t*)q_idx, w_idx, (const uint8_t*)k_idx, q_pos, m, Tq, N_c,
                        CH, nq, NG, scores, gkeys);
   else

@@ -15,7 +15,6 @@
 namespace {
 
 constexpr int VEC = 8;      // channels per thread
-constexpr int UNROLL = 8;   // tokens whose loads are issued together
 
 template <typename T>
 struct Vec8;
@@ -50,7 +49,74 @@ struct Vec8<float> {
   }
 };
 
-template <typename T>
+// Online softmax-weighted sum over tokens [j_lo, j_hi) of one 8-channel slice.  Full
+// chunks of UB tokens issue all their loads first and reduce the chunk as balanced trees
+// (max, sum of weights, sum of weighted values), so the dependent chain per chunk is
+// log2(UB) deep instead of UB; a partial last chunk takes the guarded path.
+template <typename T, int UB, bool HAS_P>
+CSAHCA_DEV void pool_run(const T* __restrict__ xp, const T* __restrict__ zp,
+                         const float* __restrict__ pp, int c, int j_lo, int j_hi,
+                         float (&mx)[VEC], float (&sum)[VEC], float (&acc)[VEC]) {
+  int j0 = j_lo;
+  for (; j0 + UB <= j_hi; j0 += UB) {
+    Vec8<T> xv[UB], zv[UB];
+#pragma unroll
+    for (int u = 0; u < UB; ++u) {
+      xv[u].load(xp + (long long)(j0 + u) * c);
+      zv[u].load(zp + (long long)(j0 + u) * c);
+    }
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      float z[UB], t[UB];
+#pragma unroll
+      for (int u = 0; u < UB; ++u) {
+        z[u] = zv[u].get(e);
+        if (HAS_P) z[u] += pp[(j0 + u) * c + e];
+        t[u] = z[u];
+      }
+#pragma unroll
+      for (int w = UB / 2; w >= 1; w /= 2)
+#pragma unroll
+        for (int u = 0; u < w; ++u) t[u] = fmaxf(t[u], t[u + w]);
+      const float cm = fmaxf(mx[e], t[0]);
+      const float alpha = __expf(mx[e] - cm);  // exp(-inf) = 0 on the first chunk
+      float pw[UB], px[UB];
+#pragma unroll
+      for (int u = 0; u < UB; ++u) {
+        pw[u] = __expf(z[u] - cm);
+        px[u] = pw[u] * xv[u].get(e);
+      }
+#pragma unroll
+      for (int w = UB / 2; w >= 1; w /= 2)
+#pragma unroll
+        for (int u = 0; u < w; ++u) {
+          pw[u] += pw[u + w];
+          px[u] += px[u + w];
+        }
+      mx[e] = cm;
+      sum[e] = fmaf(sum[e], alpha, pw[0]);
+      acc[e] = fmaf(acc[e], alpha, px[0]);
+    }
+  }
+  for (; j0 < j_hi; ++j0) {  // tail: one token at a time
+    Vec8<T> xv, zv;
+    xv.load(xp + (long long)j0 * c);
+    zv.load(zp + (long long)j0 * c);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      float z = zv.get(e);
+      if (HAS_P) z += pp[j0 * c + e];
+      const float cm = fmaxf(mx[e], z);
+      const float alpha = __expf(mx[e] - cm);
+      const float p = __expf(z - cm);
+      mx[e] = cm;
+      sum[e] = fmaf(sum[e], alpha, p);
+      acc[e] = fmaf(acc[e], alpha, p * xv.get(e));
+    }
+  }
+}
+
+template <typename T, int UB, bool HAS_P>
 __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ X,
                                                    const T* __restrict__ Z,
                                                    const float* __restrict__ P,
@@ -64,11 +130,7 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ X,
   const long long rest = item / CV;
   const int i = (int)(rest % N);
   const int b = (int)(rest / N);
-
   const long long base = (long long)b * in_bs + (long long)i * m * c + (long long)cv * VEC;
-  const T* xp = X + base;
-  const T* zp = Z + base;
-
   float mx[VEC], sum[VEC], acc[VEC];
 #pragma unroll
   for (int e = 0; e < VEC; ++e) {
@@ -76,45 +138,7 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ X,
     sum[e] = 0.f;
     acc[e] = 0.f;
   }
-
-  for (int j0 = 0; j0 < m; j0 += UNROLL) {
-    const int cnt = min(UNROLL, m - j0);
-    Vec8<T> xv[UNROLL], zv[UNROLL];
-#pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      if (u < cnt) {
-        xv[u].load(xp + (long long)(j0 + u) * c);
-        zv[u].load(zp + (long long)(j0 + u) * c);
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      float z[UNROLL];
-      float cm = mx[e];
-#pragma unroll
-      for (int u = 0; u < UNROLL; ++u) {
-        if (u < cnt) {
-          z[u] = zv[u].get(e);
-          if (P) z[u] += P[(j0 + u) * c + cv * VEC + e];
-          cm = fmaxf(cm, z[u]);
-        }
-      }
-      // cm is finite: at least one finite logit has been seen
-      const float alpha = __expf(mx[e] - cm);  // exp(-inf) = 0 on the first chunk
-      float s = sum[e] * alpha, a = acc[e] * alpha;
-#pragma unroll
-      for (int u = 0; u < UNROLL; ++u) {
-        if (u < cnt) {
-          const float p = __expf(z[u] - cm);
-          s += p;
-          a = fmaf(p, xv[u].get(e), a);
-        }
-      }
-      mx[e] = cm;
-      sum[e] = s;
-      acc[e] = a;
-    }
-  }
+  pool_run<T, UB, HAS_P>(X + base, Z + base, HAS_P ? P + cv * VEC : nullptr, c, 0, m, mx, sum, acc);
   float res[VEC];
 #pragma unroll
   for (int e = 0; e < VEC; ++e) res[e] = acc[e] / sum[e];
@@ -125,13 +149,13 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ X,
 // threads split the block's m tokens into S contiguous sub-ranges per 8-channel slice,
 // each with its own running softmax; the S partial states are merged in LDS in a fixed
 // order, so the result does not depend on timing.
-template <typename T>
-__global__ __launch_bounds__(1024) void pool_block_kernel(const T* __restrict__ X,
-                                                         const T* __restrict__ Z,
-                                                         const float* __restrict__ P,
-                                                         T* __restrict__ out, int N, int c,
-                                                         int m, int S, long long in_bs,
-                                                         long long out_bs) {
+template <typename T, int UB, bool HAS_P>
+__global__ __launch_bounds__(512) void pool_block_kernel(const T* __restrict__ X,
+                                                        const T* __restrict__ Z,
+                                                        const float* __restrict__ P,
+                                                        T* __restrict__ out, int N, int c,
+                                                        int m, int S, long long in_bs,
+                                                        long long out_bs) {
   extern __shared__ float part[];  // [S][CV][3][VEC]
   const int CV = c / VEC;
   const int cv = threadIdx.x % CV, s = threadIdx.x / CV;
@@ -146,43 +170,7 @@ __global__ __launch_bounds__(1024) void pool_block_kernel(const T* __restrict__ 
     sum[e] = 0.f;
     acc[e] = 0.f;
   }
-  for (int j0 = j_lo; j0 < j_hi; j0 += UNROLL) {
-    const int cnt = min(UNROLL, j_hi - j0);
-    Vec8<T> xv[UNROLL], zv[UNROLL];
-#pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      if (u < cnt) {
-        xv[u].load(X + base + (long long)(j0 + u) * c);
-        zv[u].load(Z + base + (long long)(j0 + u) * c);
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      float z[UNROLL];
-      float cm = mx[e];
-#pragma unroll
-      for (int u = 0; u < UNROLL; ++u) {
-        if (u < cnt) {
-          z[u] = zv[u].get(e);
-          if (P) z[u] += P[(j0 + u) * c + cv * VEC + e];
-          cm = fmaxf(cm, z[u]);
-        }
-      }
-      const float alpha = __expf(mx[e] - cm);
-      float sm = sum[e] * alpha, a = acc[e] * alpha;
-#pragma unroll
-      for (int u = 0; u < UNROLL; ++u) {
-        if (u < cnt) {
-          const float p = __expf(z[u] - cm);
-          sm += p;
-          a = fmaf(p, xv[u].get(e), a);
-        }
-      }
-      mx[e] = cm;
-      sum[e] = sm;
-      acc[e] = a;
-    }
-  }
+  pool_run<T, UB, HAS_P>(X + base, Z + base, HAS_P ? P + cv * VEC : nullptr, c, j_lo, j_hi, mx, sum, acc);
   float* mine = part + ((size_t)s * CV + cv) * 3 * VEC;
 #pragma unroll
   for (int e = 0; e < VEC; ++e) {
@@ -209,6 +197,34 @@ __global__ __launch_bounds__(1024) void pool_block_kernel(const T* __restrict__ 
   Vec8<T>::store(out + (long long)b * out_bs + (long long)i * c + (long long)cv * VEC, res);
 }
 
+template <typename T, bool HAS_P>
+void launch_pool(const void* kv, const void* gate, const float* pos_bias, void* out, int B,
+                 long long N, int c, int m, long long in_bs, long long out_bs, hipStream_t st) {
+  const long long total = (long long)B * N * (c / 8);
+  // few blocks of many tokens: split each block's tokens over more threads
+  int S = min(m / 8, 512 / (c / 8));
+  if (S > 8) S = 8;
+  const size_t lds = (size_t)max(S, 1) * (c / 8) * 3 * VEC * sizeof(float);
+  if (total < 32768 && S >= 2 && lds <= 65536) {
+    const int span = cdiv(m, S);
+    const unsigned grid = (unsigned)(B * N), threads = (unsigned)(S * (c / 8));
+    if (span % 16 == 0 && sizeof(T) == 2)
+      hipLaunchKernelGGL((pool_block_kernel<T, 16, HAS_P>), dim3(grid), dim3(threads), lds, st,
+                         (const T*)kv, (const T*)gate, pos_bias, (T*)out, (int)N, c, m, S, in_bs, out_bs);
+    else
+      hipLaunchKernelGGL((pool_block_kernel<T, 8, HAS_P>), dim3(grid), dim3(threads), lds, st,
+                         (const T*)kv, (const T*)gate, pos_bias, (T*)out, (int)N, c, m, S, in_bs, out_bs);
+    return;
+  }
+  const unsigned blocks = (unsigned)cdiv<long long>(total, 256);
+  if (m % 8 == 0)
+    hipLaunchKernelGGL((pool_kernel<T, 8, HAS_P>), dim3(blocks), dim3(256), 0, st, (const T*)kv,
+                       (const T*)gate, pos_bias, (T*)out, (int)N, c, m, in_bs, out_bs, total);
+  else
+    hipLaunchKernelGGL((pool_kernel<T, 4, HAS_P>), dim3(blocks), dim3(256), 0, st, (const T*)kv,
+                       (const T*)gate, pos_bias, (T*)out, (int)N, c, m, in_bs, out_bs, total);
+}
+
 int pool_entry(const char* name, const void* kv, const void* gate, const float* pos_bias,
                void* out, int B, int n, int c, int m, int dtype, long long in_bs,
                long long out_bs, void* stream) {
@@ -230,37 +246,15 @@ int pool_entry(const char* name, const void* kv, const void* gate, const float* 
   if (!aligned16(kv) || !aligned16(gate) || !aligned16(out))
     return fail(CSAHCA_EINVAL, "pool: kv, gate and out must be 16-byte aligned");
   const long long total = (long long)B * N * (c / 8);
+  if (cdiv<long long>(total, 256) > 0x7FFFFFFFLL)
+    return fail(CSAHCA_ENOTSUP, "pool: problem too large for one launch");
   hipStream_t st = (hipStream_t)stream;
-  // few blocks of many tokens: split each block's tokens over more threads
-  int S = min(m / 8, 1024 / (c / 8));
-  if (S > 8) S = 8;
-  if (total < 32768 && S >= 2) {
-    const size_t lds = (size_t)S * (c / 8) * 3 * VEC * sizeof(float);
-    if (lds <= 65536) {
-      const unsigned grid = (unsigned)(B * N);
-      const unsigned threads = (unsigned)(S * (c / 8));
-      if (dtype == CSAHCA_BF16)
-        hipLaunchKernelGGL(pool_block_kernel<uint16_t>, dim3(grid), dim3(threads), lds, st,
-                           (const uint16_t*)kv, (const uint16_t*)gate, pos_bias, (uint16_t*)out,
-                           (int)N, c, m, S, in_bs, out_bs);
-      else
-        hipLaunchKernelGGL(pool_block_kernel<float>, dim3(grid), dim3(threads), lds, st,
-                           (const float*)kv, (const float*)gate, pos_bias, (float*)out, (int)N, c,
-                           m, S, in_bs, out_bs);
-      return launch_status(name);
-    }
-  }
-  const int threads = 256;
-  const long long blocks = cdiv<long long>(total, threads);
-  if (blocks > 0x7FFFFFFFLL) return fail(CSAHCA_ENOTSUP, "pool: problem too large for one launch");
   if (dtype == CSAHCA_BF16) {
-    hipLaunchKernelGGL(pool_kernel<uint16_t>, dim3((unsigned)blocks), dim3(threads), 0, st,
-                       (const uint16_t*)kv, (const uint16_t*)gate, pos_bias, (uint16_t*)out,
-                       (int)N, c, m, in_bs, out_bs, total);
+    if (pos_bias) launch_pool<uint16_t, true>(kv, gate, pos_bias, out, B, N, c, m, in_bs, out_bs, st);
+    else launch_pool<uint16_t, false>(kv, gate, pos_bias, out, B, N, c, m, in_bs, out_bs, st);
   } else {
-    hipLaunchKernelGGL(pool_kernel<float>, dim3((unsigned)blocks), dim3(threads), 0, st,
-                       (const float*)kv, (const float*)gate, pos_bias, (float*)out, (int)N, c,
-                       m, in_bs, out_bs, total);
+    if (pos_bias) launch_pool<float, true>(kv, gate, pos_bias, out, B, N, c, m, in_bs, out_bs, st);
+    else launch_pool<float, false>(kv, gate, pos_bias, out, B, N, c, m, in_bs, out_bs, st);
   }
   return launch_status(name);
 }

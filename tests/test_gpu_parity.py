@@ -206,3 +206,72 @@ def test_deterministic():
     for key in a:
         if isinstance(a[key], np.ndarray):
             assert np.array_equal(a[key], b[key]), key
+
+
+def test_pool_bias_and_paths():
+    """Positional bias, both pooling kernels (few blocks / many blocks), fp32 and bf16."""
+    rng = np.random.default_rng(5)
+    for dtype, m, B, n in ((BF16, 4, 2, 4 * 300 + 3), (BF16, 128, 2, 128 * 5 + 7),
+                           (BF16, 128, 2, 128 * 300), (F32, 4, 1, 4 * 64), (F32, 128, 1, 128 * 3 + 1),
+                           (BF16, 1, 1, 40), (BF16, 3, 1, 3 * 50 + 2)):
+        c = 512 if dtype == BF16 else 64
+        from synthgen.host import encode
+        Xh = encode(rng.standard_normal((B, n, c), dtype=np.float32) * 0.1, dtype)
+        Zh = encode(rng.standard_normal((B, n, c), dtype=np.float32), dtype)
+        P = rng.standard_normal((m, c)).astype(np.float32)
+        for bias in (None, P):
+            out = H.run_pool(H.to_dev(Xh), H.to_dev(Zh), m, dtype,
+                             P=None if bias is None else H.to_dev(bias))
+            check_pool(Xh, Zh, dtype, m, out, P=bias)
+
+
+def test_window_source_offset():
+    """A window source holding only the last W raw tokens (win_pos = n - W) gives the same
+    output as the whole raw sequence as source."""
+    cfg = CASES["pair_h128"]
+    prob = make_problem(cfg)
+    n, W, B = prob["n_total"], cfg.W, cfg.B
+    q_pos = H.to_dev(prob["q_pos"])
+    for layer in ("csa", "hca"):
+        X, Z = H.to_dev(prob[f"X_{layer}"]), H.to_dev(prob[f"Z_{layer}"])
+        m = cfg.m if layer == "csa" else cfg.m_hca
+        C = H.run_pool(X, Z, m, BF16)
+        Q = H.to_dev(prob[f"Q_{layer}"])
+        tail = X[:, n - W:].contiguous()
+        wp0 = H.to_dev(np.zeros(B, np.int32))
+        wp1 = H.to_dev(np.full(B, n - W, np.int32))
+        if layer == "csa":
+            idx, _, _ = H.run_index(H.to_dev(prob["qI"]), H.to_dev(prob["w"]), H.to_dev(prob["KI"]),
+                                    q_pos, m, cfg.k, cfg.idx_dtype)
+            a, la = H.run_csa_attend(Q, C, idx, X, wp0, q_pos, W, BF16)
+            b, lb = H.run_csa_attend(Q, C, idx, tail, wp1, q_pos, W, BF16)
+        else:
+            a, la = H.run_hca_attend(Q, C, X, wp0, q_pos, m, W, BF16)
+            b, lb = H.run_hca_attend(Q, C, tail, wp1, q_pos, m, W, BF16)
+        assert torch.equal(a, b) and torch.equal(la, lb), layer
+
+
+@pytest.mark.parametrize("n_h", [16, 32])
+def test_fewer_heads(n_h):
+    run_chain(CONFIGS[3].scaled(B=2, n=4 * 700 + 3, n_h=n_h, seed=40 + n_h))
+    run_chain(CONFIGS[2].scaled(B=2, n=128 * 9 + 5, n_h=n_h, seed=50 + n_h))
+
+
+def test_ties_resolve_to_lower_index():
+    """Identical indexer keys give identical scores everywhere: the selection must be the
+    lowest indices.  All-zero head weights give all-zero scores: same rule."""
+    cfg = CONFIGS[3].scaled(B=2, n=4 * 3000, seed=61, plants=0)
+    prob = make_problem(cfg)
+    KI = prob["KI"].copy()
+    KI[:] = KI[:, :1]                       # every key equals key 0
+    prob_w0 = dict(prob)
+    for name, ki, w in (("identical keys", KI, prob["w"]), ("zero weights", prob["KI"], np.zeros_like(prob["w"]))):
+        q_pos = H.to_dev(prob["q_pos"])
+        idx, sc, alls = H.run_index(H.to_dev(prob["qI"]), H.to_dev(w), H.to_dev(ki), q_pos, cfg.m, cfg.k,
+                                    cfg.idx_dtype)
+        got = idx.cpu().numpy()
+        for b in range(cfg.B):
+            assert np.array_equal(got[b, 0], np.arange(cfg.k)), name
+        # and the oracle's selection on the GPU scores agrees
+        p2 = dict(prob, KI=ki, w=w)
+        check_index(p2, prob["q_pos"], cfg.k, idx, sc, alls)

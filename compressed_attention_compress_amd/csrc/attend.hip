@@ -80,6 +80,19 @@ CSAHCA_DEV void lds_reads_done_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Wait until at most `inflight` tiles (LPW row loads each) of this wave are outstanding,
+// inflight in [0, MAXF]; vmcnt takes an immediate, so dispatch on the value.
+template <int MAXF, int LPW>
+CSAHCA_DEV void wait_tiles(int inflight) {
+  constexpr int c1 = LPW < 63 ? LPW : 63;
+  constexpr int c2 = 2 * LPW < 63 ? 2 * LPW : 63;
+  constexpr int c3 = 3 * LPW < 63 ? 3 * LPW : 63;
+  if (MAXF >= 3 && inflight >= 3) wait_vmcnt_barrier<c3>();
+  else if (MAXF >= 2 && inflight >= 2) wait_vmcnt_barrier<c2>();
+  else if (MAXF >= 1 && inflight >= 1) wait_vmcnt_barrier<c1>();
+  else wait_vmcnt_barrier<0>();
+}
+
 // LDS ring depth NS: 2 tiles when many workgroups run (two 4-wave workgroups share a CU
 // and hide each other's latency: prefill), 4 tiles when few queries are split over
 // workgroups (one workgroup per CU keeps three tiles in flight: decode).
@@ -87,6 +100,29 @@ size_t attend_lds_bytes(int NS, int NW, int RS, bool csa) {
   return (size_t)NS * TILE * ROWB + (size_t)NS * NW * sizeof(uint32_t) +
          (csa ? (size_t)RS * sizeof(int) : 0);
 }
+
+// Optional per-workgroup timestamps for latency studies (compiled out by default):
+// shader-clock stamps in slots 0..13, fixed-rate stamps in slots 14 and 15.
+#ifdef CSAHCA_TRACE_ENABLED
+__device__ unsigned long long csahca_trace[8192 * 16];
+#define CSAHCA_TRACE(slot)                                                              \
+  do {                                                                                  \
+    if (threadIdx.x == 0 && blockIdx.x < 8192)                                          \
+      csahca_trace[blockIdx.x * 16 + (slot)] = __builtin_amdgcn_s_memtime();            \
+  } while (0)
+#define CSAHCA_TRACE_RT(slot)                                                           \
+  do {                                                                                  \
+    if (threadIdx.x == 0 && blockIdx.x < 8192)                                          \
+      csahca_trace[blockIdx.x * 16 + (slot)] = __builtin_amdgcn_s_memrealtime();        \
+  } while (0)
+#else
+#define CSAHCA_TRACE(slot) \
+  do {                     \
+  } while (0)
+#define CSAHCA_TRACE_RT(slot) \
+  do {                        \
+  } while (0)
+#endif
 
 // bits [lo, hi) of a 32-bit mask, the bounds relative to `base` and clipped to [0, 32)
 CSAHCA_DEV uint32_t range_bits(int lo, int hi, int base) {
@@ -97,8 +133,22 @@ CSAHCA_DEV uint32_t range_bits(int lo, int hi, int base) {
   return up & ~((1u << lo) - 1u);
 }
 
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+// 32-bit LDS byte address of a pointer into dynamic shared memory
+CSAHCA_DEV uint32_t lds_addr(const uint8_t* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
+}
+
+// O^T += E^T P^T as asm text (pv_asm.inc, written by gen_pv_asm.py): the transpose reads
+// ds_read_b64_tr_b16 feed v_mfma_f32_16x16x32_bf16 with waits on LDS reads only.
+#include "pv_asm.inc"
+#define PV_ACC_OPERANDS                                                                   \
+  "+v"(oacc[0]), "+v"(oacc[1]), "+v"(oacc[2]), "+v"(oacc[3]), "+v"(oacc[4]), "+v"(oacc[5]), \
+      "+v"(oacc[6]), "+v"(oacc[7]), "+v"(oacc[8]), "+v"(oacc[9]), "+v"(oacc[10]),           \
+      "+v"(oacc[11]), "+v"(oacc[12]), "+v"(oacc[13]), "+v"(oacc[14]), "+v"(oacc[15]),       \
+      "+v"(oacc[16]), "+v"(oacc[17]), "+v"(oacc[18]), "+v"(oacc[19]), "+v"(oacc[20]),       \
+      "+v"(oacc[21]), "+v"(oacc[22]), "+v"(oacc[23]), "+v"(oacc[24]), "+v"(oacc[25]),       \
+      "+v"(oacc[26]), "+v"(oacc[27]), "+v"(oacc[28]), "+v"(oacc[29]), "+v"(oacc[30]),       \
+      "+v"(oacc[31])
 
 // One workgroup: queries t0 .. t0+Tg-1 of one sequence, HPW heads, slots
 // [split*RS, (split+1)*RS).  Rows arrive by global_load_lds straight into an LDS ring of
@@ -121,6 +171,8 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && NS == 2) ? 2 : 1) void attend_
 
   // XCD-aware order: consecutive work items (the head groups of one row range first) run
   // on the same XCD, so the rows they share are read from HBM once into that XCD's L2.
+  CSAHCA_TRACE(0);
+  CSAHCA_TRACE_RT(14);
   const int Lb = blockIdx.x;
   const int wid = (Lb & 7) * a.per_xcd + (Lb >> 3);
   if (wid >= a.n_work) return;  // grid padding, before any barrier
@@ -171,20 +223,14 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && NS == 2) ? 2 : 1) void attend_
   const int Vu = CSA ? 0 : vis_count(plast, a.m, a.Nc);
   const int Vw = CSA ? 0 : vis_count(p, a.m, a.Nc);
 
-  // CSA: this split's selected entry indices, staged in LDS
+  // CSA: this split's selected entry indices, staged in LDS (before any row is issued)
   if (CSA) {
     const int* tk = a.topk + ((long long)b * a.Tq + t0) * a.k;
     const int hi = min(slot_hi, nsc);
     for (int j = slot_lo + (int)threadIdx.x; j < hi; j += NW * 64) sidx[j - slot_lo] = tk[j];
+    __syncthreads();
   }
-  bf16x8 qf[KS];
-  {
-    const uint16_t* qp = a.q + (qrow * a.n_h + h0 + row16) * C + g * (C / 4);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      qf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qp + ks * 8));
-  }
-  __syncthreads();  // sidx visible; also drains the loads above before the ring starts
+  CSAHCA_TRACE(1);
 
   const int ntile = slot_hi > slot_lo ? cdiv(slot_hi - slot_lo, TILE) : 0;
   auto issue = [&](int tt) {
@@ -221,123 +267,173 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && NS == 2) ? 2 : 1) void attend_
     if (lane == 0) tmask[stage * NW + wave] = okbits;
   };
 
+  // Q fragments, then the first iteration's tiles, then the rest of the ring.  The
+  // compiler does not assume that row DMAs and register loads complete in order, so its
+  // wait for Q (forced here by the empty asm, once, rather than before the first MFMA of
+  // every iteration) drains every load issued so far: only the tiles needed first.
+  constexpr int TPI = NS >= 4 ? 2 : 1;  // tiles consumed per iteration
+  bf16x8 qf[KS];
+  {
+    const uint16_t* qp = a.q + (qrow * a.n_h + h0 + row16) * C + g * (C / 4);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qp + ks * 8));
+  }
+  for (int tt = 0; tt < TPI && tt < ntile; ++tt) issue(tt);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(qf[ks]));
+  for (int tt = TPI; tt < NS && tt < ntile; ++tt) issue(tt);
+
   float m_run = -INFINITY, l_run = 0.f;
   f32x4 oacc[C / 16];
 #pragma unroll
   for (int cb = 0; cb < C / 16; ++cb) oacc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // LDS byte offsets of this lane's operands inside a tile
-  const int s_off = row16 * ROWB + g * (C / 4) * 2;               // S: A = row, 8 dims
+  const int s_off = row16 * ROWB + g * (C / 4) * 2;                  // S: A = row, 8 dims
   const int t_off = (4 * g + (row16 >> 2)) * ROWB + (row16 & 3) * 8;  // PV: transpose reads
 
-  for (int tt = 0; tt < NS - 1 && tt < ntile; ++tt) issue(tt);
-  for (int it = 0; it < ntile; ++it) {
-    // this wave's rows of tile `it` have landed, then every other wave's
-    if (it + NS - 1 < ntile) {
-      issue(it + NS - 1);
-      // (the counter holds at most 63; a smaller bound only waits longer)
-      wait_vmcnt_barrier<((NS - 1) * LPW < 63 ? (NS - 1) * LPW : 63)>();
-    } else {
-      wait_vmcnt_barrier<0>();
-    }
-    if (active) {
-      const int stage = it % NS;
-      const uint8_t* tile = tiles + stage * (TILE * ROWB);
-      const int base = slot_lo + it * TILE;
-      // slots of this tile usable by this wave's query (wave-uniform)
-      uint32_t loaded = 0;
+  auto tile_mask = [&](int stage, int base) -> uint32_t {
+    uint32_t loaded = 0;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) loaded |= tmask[stage * NW + w];
-      loaded = __builtin_amdgcn_readfirstlane(loaded);
-      uint32_t vmask = range_bits(wq_lo, min(wq_hi, slot_hi), base);
-      if (CSA)
-        vmask |= range_bits(slot_lo, min(nsc, slot_hi), base);
-      else
-        vmask |= range_bits(0, min(min(Vw, nsc), slot_hi), base);
-      vmask &= loaded;
+    for (int w = 0; w < NW; ++w) loaded |= tmask[stage * NW + w];
+    loaded = __builtin_amdgcn_readfirstlane(loaded);
+    uint32_t vm = range_bits(wq_lo, min(wq_hi, slot_hi), base);
+    if (CSA)
+      vm |= range_bits(slot_lo, min(nsc, slot_hi), base);
+    else
+      vm |= range_bits(0, min(min(Vw, nsc), slot_hi), base);
+    return vm & loaded;
+  };
 
-      // ---- S^T = E Q^T for 2 blocks of 16 slots; reads run one K-step ahead ----
-      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s2 = s0;
-      const uint8_t* sp = tile + s_off;
-      u32x4 ra0 = *reinterpret_cast<const u32x4*>(sp);
-      u32x4 ra1 = *reinterpret_cast<const u32x4*>(sp + 16 * ROWB);
+  // Each iteration consumes TPI tiles: with a 4-tile ring two (64 slots: four independent
+  // S chains, one softmax update, 64 PV MFMAs) while the next two are in flight; with a
+  // 2-tile ring one, while the other is in flight.
+  static_assert(NS % TPI == 0, "the ring holds whole iterations");
+  for (int it = 0; it < ntile; it += TPI) {
+    // tiles it .. min(ntile, it+NS)-1 are issued; all but the first TPI may stay in flight
+    wait_tiles<NS - TPI, LPW>(min(ntile - it, NS) - TPI);
+    if (it < 3 * TPI) CSAHCA_TRACE(2 + 2 * (it / TPI) + (it ? 4 : 0));
+    const bool two = TPI == 2 && ntile - it >= 2;
+    if (active) {
+      const int stA = it % NS, stB = (it + 1) % NS;
+      const uint8_t* tA = tiles + stA * (TILE * ROWB);
+      const uint8_t* tB = two ? tiles + stB * (TILE * ROWB) : tA;
+      const int base = slot_lo + it * TILE;
+      const uint32_t vmA = tile_mask(stA, base);
+      const uint32_t vmB = two ? tile_mask(stB, base + TILE) : 0u;
+
+      // ---- S^T = E Q^T in 16-slot blocks, operands read one K-step ahead ----
+      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0, s2 = s0, s3 = s0;
+      const uint8_t* spA = tA + s_off;
+      const uint8_t* spB = tB + s_off;
+      u32x4 r0 = *reinterpret_cast<const u32x4*>(spA);
+      u32x4 r1 = *reinterpret_cast<const u32x4*>(spA + 16 * ROWB);
+      u32x4 r2, r3;
+      if (TPI == 2) {
+        r2 = *reinterpret_cast<const u32x4*>(spB);
+        r3 = *reinterpret_cast<const u32x4*>(spB + 16 * ROWB);
+      }
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        u32x4 rb0, rb1;
+        u32x4 n0, n1, n2, n3;
         if (ks + 1 < KS) {
-          rb0 = *reinterpret_cast<const u32x4*>(sp + (ks + 1) * 16);
-          rb1 = *reinterpret_cast<const u32x4*>(sp + 16 * ROWB + (ks + 1) * 16);
+          n0 = *reinterpret_cast<const u32x4*>(spA + (ks + 1) * 16);
+          n1 = *reinterpret_cast<const u32x4*>(spA + 16 * ROWB + (ks + 1) * 16);
+          if (TPI == 2) {
+            n2 = *reinterpret_cast<const u32x4*>(spB + (ks + 1) * 16);
+            n3 = *reinterpret_cast<const u32x4*>(spB + 16 * ROWB + (ks + 1) * 16);
+          }
         }
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ra0), qf[ks], s0, 0, 0, 0);
-        s2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ra1), qf[ks], s2, 0, 0, 0);
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, r0), qf[ks], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, r1), qf[ks], s1, 0, 0, 0);
+        if (TPI == 2) {
+          s2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, r2), qf[ks], s2, 0, 0, 0);
+          s3 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, r3), qf[ks], s3, 0, 0, 0);
+        }
         __builtin_amdgcn_sched_barrier(0);
-        ra0 = rb0;
-        ra1 = rb1;
+        r0 = n0;
+        r1 = n1;
+        if (TPI == 2) {
+          r2 = n2;
+          r3 = n3;
+        }
       }
-      // lane: head h0 + row16, slots base + rb*16 + 4g + i
-      float sv[8];
-      float mloc = -INFINITY;
+      // lane: head h0 + row16; sv[4*rb + i] is slot base + 16*rb + 4g + i (rb 2, 3: tile B)
+      constexpr int NSV = 8 * TPI;
+      float sv[NSV];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const bool ok0 = (vmask >> (4 * g + i)) & 1u;
-        const bool ok1 = (vmask >> (16 + 4 * g + i)) & 1u;
-        sv[i] = ok0 ? s0[i] * a.scale_log2 : -INFINITY;
-        sv[4 + i] = ok1 ? s2[i] * a.scale_log2 : -INFINITY;
-        mloc = fmaxf(mloc, fmaxf(sv[i], sv[4 + i]));
+        const int r = 4 * g + i;
+        sv[i] = ((vmA >> r) & 1u) ? s0[i] * a.scale_log2 : -INFINITY;
+        sv[4 + i] = ((vmA >> (16 + r)) & 1u) ? s1[i] * a.scale_log2 : -INFINITY;
+        if (TPI == 2) {
+          sv[(8 + i) % NSV] = ((vmB >> r) & 1u) ? s2[i] * a.scale_log2 : -INFINITY;
+          sv[(12 + i) % NSV] = ((vmB >> (16 + r)) & 1u) ? s3[i] * a.scale_log2 : -INFINITY;
+        }
       }
-      mloc = max_over_row_groups(mloc);
+      float mx[NSV / 2];
+#pragma unroll
+      for (int e = 0; e < NSV / 2; ++e) mx[e] = fmaxf(sv[e], sv[e + NSV / 2]);
+#pragma unroll
+      for (int w = NSV / 4; w >= 1; w >>= 1)
+#pragma unroll
+        for (int e = 0; e < w; ++e) mx[e] = fmaxf(mx[e], mx[e + w]);
+      const float mloc = max_over_row_groups(mx[0]);
       // lazy running maximum: move it only when exceeded by more than LAZY
       const bool bump = mloc > m_run + LAZY;
       const float m_new = bump ? mloc : m_run;
       const float alpha = bump ? exp2f(m_run - m_new) : 1.f;
-      float pe[8];
-      float psum = 0.f;
       const bool none = m_new == -INFINITY;
+      float pe[NSV];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pe[e] = none ? 0.f : exp2f(sv[e] - m_new);  // skipped slots: exp2(-inf) = 0
-        psum += pe[e];
-      }
-      psum = sum_over_row_groups(psum);
+      for (int e = 0; e < NSV; ++e) pe[e] = none ? 0.f : exp2f(sv[e] - m_new);  // skipped: 0
+      float ps[NSV / 2];
+#pragma unroll
+      for (int e = 0; e < NSV / 2; ++e) ps[e] = pe[e] + pe[e + NSV / 2];
+#pragma unroll
+      for (int w = NSV / 4; w >= 1; w >>= 1)
+#pragma unroll
+        for (int e = 0; e < w; ++e) ps[e] += ps[e + w];
+      const float psum = sum_over_row_groups(ps[0]);
       l_run = l_run * alpha + psum;
       m_run = m_new;
       if (__any(bump)) {
 #pragma unroll
         for (int cb = 0; cb < C / 16; ++cb) oacc[cb] *= alpha;
       }
-      // P^T as the B operand: k-slot e <-> slot (e < 4 ? 4g+e : 16+4g+e-4)
-      const u32x4 pw = {pack_bf16x2(pe[0], pe[1]), pack_bf16x2(pe[2], pe[3]),
-                        pack_bf16x2(pe[4], pe[5]), pack_bf16x2(pe[6], pe[7])};
-      const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
-      // ---- O^T += E^T P^T: E^T through LDS transpose reads, two column blocks ahead ----
+      // P^T as B operands: k-slot e <-> slot (e < 4 ? 4g+e : 16+4g+e-4) of its tile
+      const bf16x8 pfA = __builtin_bit_cast(bf16x8, u32x4{pack_bf16x2(pe[0], pe[1]), pack_bf16x2(pe[2], pe[3]),
+                                                          pack_bf16x2(pe[4], pe[5]), pack_bf16x2(pe[6], pe[7])});
+      bf16x8 pfB;
+      if (TPI == 2)
+        pfB = __builtin_bit_cast(bf16x8, u32x4{pack_bf16x2(pe[8 % NSV], pe[9 % NSV]),
+                                               pack_bf16x2(pe[10 % NSV], pe[11 % NSV]),
+                                               pack_bf16x2(pe[12 % NSV], pe[13 % NSV]),
+                                               pack_bf16x2(pe[14 % NSV], pe[15 % NSV])});
+      // ---- O^T += E^T P^T: E^T through LDS transpose reads, issued in asm ahead of use ----
       // ds_read_b64_tr_b16: in each 16-lane group, lane i receives column i%4 of the four
       // 4-element rows addressed by lanes i/4, i/4+4, i/4+8, i/4+12.  Lane j addresses row
       // (4g + j/4) at column 16*cb + 4*(j%4), so lane i gets column 16*cb + i of rows
       // 4g .. 4g+3 (and 16+4g .. 16+4g+3 with the second read): exactly its A operand.
-      const uint8_t* tp = tile + t_off;
-      auto tr_pair = [&](int cb) -> u32x4 {
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tp + cb * 32));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tp + 16 * ROWB + cb * 32));
-        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-        return u32x4{l2[0], l2[1], h2[0], h2[1]};
-      };
-      u32x4 ta0 = tr_pair(0), ta1 = tr_pair(1);
-#pragma unroll
-      for (int cb0 = 0; cb0 < C / 16; cb0 += 2) {
-        u32x4 tb0, tb1;
-        if (cb0 + 2 < C / 16) {
-          tb0 = tr_pair(cb0 + 2);
-          tb1 = tr_pair(cb0 + 3);
-        }
-        oacc[cb0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ta0), pf, oacc[cb0], 0, 0, 0);
-        oacc[cb0 + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ta1), pf, oacc[cb0 + 1], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        ta0 = tb0;
-        ta1 = tb1;
+      const uint32_t aA = lds_addr(tA + t_off), aB = lds_addr(tB + t_off);
+      if constexpr (TPI == 2) {
+        asm volatile(CSAHCA_PV_ASM_2TILE
+                     : PV_ACC_OPERANDS
+                     : "v"(pfA), "v"(pfB), "v"(aA), "v"(aB)
+                     : CSAHCA_PV_CLOBBERS, "memory");
+      } else {
+        asm volatile(CSAHCA_PV_ASM_1TILE
+                     : PV_ACC_OPERANDS
+                     : "v"(pfA), "v"(aA)
+                     : CSAHCA_PV_CLOBBERS, "memory");
       }
     }
-    lds_reads_done_barrier();  // the stage is free for the next issue
+    lds_reads_done_barrier();  // the consumed stages are free for the next issue
+    if (it < 3 * TPI) CSAHCA_TRACE(3 + 2 * (it / TPI) + (it ? 4 : 0));
+    for (int tt = it + NS; tt < it + NS + TPI && tt < ntile; ++tt) issue(tt);
   }
+  CSAHCA_TRACE(4);
   if (!active) return;
 
   // lane: head h0 + row16; oacc[cb][i] is column 16*cb + 4*g + i
@@ -363,6 +459,8 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && NS == 2) ? 2 : 1) void attend_
       a.mlpart[pr * 2 + 1] = l_run;
     }
   }
+  CSAHCA_TRACE(5);
+  CSAHCA_TRACE_RT(15);
 }
 
 // Merge the splits of every (query, head) by their log-sum-exp.  One workgroup per pair:

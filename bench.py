@@ -42,6 +42,12 @@ def parse():
     ap.add_argument("--replicas", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only copy 1 GiB device to device (torch), for scaling HBM counters")
+    ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="rocprofv3 --pmc output folders: write the traffic record and exit")
+    ap.add_argument("--traffic-out", default=PROFILE_TRAFFIC,
+                    help="where --traffic-from writes its record")
     return ap.parse_args()
 
 
@@ -221,7 +227,7 @@ def read_traffic(kernel_name):
         import hashlib
         with open(PROFILE_TRAFFIC) as f:
             rec = json.load(f)
-        src = os.path.join(ROOT, "compressed_attention_compress_amd", "csrc", "indexer.hip")
+        src = os.path.join(ROOT, "compressed_attention_compress_amd", "csrc", "index_score.hip")
         h = hashlib.sha256(open(src, "rb").read()).hexdigest()
         ent = rec.get(kernel_name)
         if ent and ent.get("source_sha256") == h:
@@ -229,6 +235,63 @@ def read_traffic(kernel_name):
     except (OSError, ValueError, KeyError):
         pass
     return None
+
+
+COPY_BYTES = 1 << 30
+COPY_KERNEL = "neg"  # name part of torch's elementwise negation kernel
+TRAFFIC_KERNELS = {"index_score_fp8": "index_score_fp8"}
+
+
+def _counter_means(folder, counter, name_part):
+    """Mean per dispatch of `counter` over the dispatches of kernels whose name contains
+    `name_part`, from a rocprofv3 --pmc csv output folder."""
+    import csv
+    import glob
+    vals = []
+    for f in glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for row in csv.DictReader(fh):
+                if row["Counter_Name"] == counter and name_part in row["Kernel_Name"]:
+                    vals.append(float(row["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"no {counter} samples for kernels named like {name_part!r} in {folder}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def write_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, out_path):
+    """HBM bytes per launch of the dominant kernel: FETCH_SIZE + WRITE_SIZE (KiB per
+    dispatch), each scaled by what the same counter reads for a plain 1 GiB device copy."""
+    import hashlib
+    cf, _ = _counter_means(copy_fetch_dir, "FETCH_SIZE", COPY_KERNEL)
+    cw, _ = _counter_means(copy_write_dir, "WRITE_SIZE", COPY_KERNEL)
+    f_scale = COPY_BYTES / (cf * 1024.0)   # true bytes per counted byte
+    w_scale = COPY_BYTES / (cw * 1024.0)
+    src = os.path.join(ROOT, "compressed_attention_compress_amd", "csrc", "index_score.hip")
+    rec = {"copy_calibration": {"bytes": COPY_BYTES, "fetch_kib": cf, "write_kib": cw,
+                                "fetch_scale": f_scale, "write_scale": w_scale}}
+    for key, name in TRAFFIC_KERNELS.items():
+        fk, nf = _counter_means(fetch_dir, "FETCH_SIZE", name)
+        wk, nw = _counter_means(write_dir, "WRITE_SIZE", name)
+        rec[key] = {"fetch_kib_per_dispatch": fk, "write_kib_per_dispatch": wk,
+                    "dispatches": [nf, nw],
+                    "bytes_per_launch": round(fk * 1024.0 * f_scale + wk * 1024.0 * w_scale),
+                    "source_sha256": hashlib.sha256(open(src, "rb").read()).hexdigest()}
+    with open(out_path, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
+def calibrate_copy():
+    import torch
+    # torch.neg: one elementwise kernel that reads 1 GiB and writes 1 GiB (the values are
+    # irrelevant, so the source is left uninitialised: no fill kernel to tell apart)
+    a = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.neg(a, out=b)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES}), flush=True)
 
 
 def cpu_baseline(wl, seconds):
@@ -293,7 +356,7 @@ def cpu_baseline(wl, seconds):
                 oracle.attend(d[f"Q_{l}"], rows, wl.scale)
             done += 1
         el = time.perf_counter() - t0
-        if el >= seconds or done >= 64:
+        if el >= seconds:
             break
     return {"value": done / el, "unit": "query-tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{done} complete decode steps of single sequences of this workload "
@@ -302,6 +365,9 @@ def cpu_baseline(wl, seconds):
 
 def main():
     args = parse()
+    if args.traffic_from:
+        write_traffic(*args.traffic_from, args.traffic_out)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the path has no multi-GPU mode)", file=sys.stderr)
@@ -310,6 +376,9 @@ def main():
 
     from synthgen.configs import CONFIGS
 
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     cfg = CONFIGS[args.config]
     decode = cfg.kind != "prefill"
     steps = args.steps if args.steps is not None else (500 if decode else 20)

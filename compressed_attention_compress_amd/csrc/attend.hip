@@ -101,29 +101,6 @@ size_t attend_lds_bytes(int NS, int NW, int RS, bool csa) {
          (csa ? (size_t)RS * sizeof(int) : 0);
 }
 
-// Optional per-workgroup timestamps for latency studies (compiled out by default):
-// shader-clock stamps in slots 0..13, fixed-rate stamps in slots 14 and 15.
-#ifdef CSAHCA_TRACE_ENABLED
-__device__ unsigned long long csahca_trace[8192 * 16];
-#define CSAHCA_TRACE(slot)                                                              \
-  do {                                                                                  \
-    if (threadIdx.x == 0 && blockIdx.x < 8192)                                          \
-      csahca_trace[blockIdx.x * 16 + (slot)] = __builtin_amdgcn_s_memtime();            \
-  } while (0)
-#define CSAHCA_TRACE_RT(slot)                                                           \
-  do {                                                                                  \
-    if (threadIdx.x == 0 && blockIdx.x < 8192)                                          \
-      csahca_trace[blockIdx.x * 16 + (slot)] = __builtin_amdgcn_s_memrealtime();        \
-  } while (0)
-#else
-#define CSAHCA_TRACE(slot) \
-  do {                     \
-  } while (0)
-#define CSAHCA_TRACE_RT(slot) \
-  do {                        \
-  } while (0)
-#endif
-
 // bits [lo, hi) of a 32-bit mask, the bounds relative to `base` and clipped to [0, 32)
 CSAHCA_DEV uint32_t range_bits(int lo, int hi, int base) {
   lo = min(max(lo - base, 0), 32);

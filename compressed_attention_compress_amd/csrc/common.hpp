@@ -157,6 +157,30 @@ CSAHCA_DEV uint32_t wave_or(uint32_t x) {
   return b[0] | b[1];
 }
 
+// Optional per-workgroup timestamps for latency studies (compiled out by default; a
+// study includes one kernel source with CSAHCA_TRACE_ENABLED defined):
+// shader-clock stamps in slots 0..13, fixed-rate stamps in slots 14 and 15.
+#ifdef CSAHCA_TRACE_ENABLED
+__device__ unsigned long long csahca_trace[8192 * 16];
+#define CSAHCA_TRACE(slot)                                                              \
+  do {                                                                                  \
+    if (threadIdx.x == 0 && blockIdx.x < 8192)                                          \
+      csahca_trace[blockIdx.x * 16 + (slot)] = __builtin_amdgcn_s_memtime();            \
+  } while (0)
+#define CSAHCA_TRACE_RT(slot)                                                           \
+  do {                                                                                  \
+    if (threadIdx.x == 0 && blockIdx.x < 8192)                                          \
+      csahca_trace[blockIdx.x * 16 + (slot)] = __builtin_amdgcn_s_memrealtime();        \
+  } while (0)
+#else
+#define CSAHCA_TRACE(slot) \
+  do {                     \
+  } while (0)
+#define CSAHCA_TRACE_RT(slot) \
+  do {                        \
+  } while (0)
+#endif
+
 // ceil-div for host and device
 template <typename T>
 __host__ __device__ inline T cdiv(T a, T b) {

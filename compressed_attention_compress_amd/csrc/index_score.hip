@@ -1,0 +1,320 @@
+// Kernel 2a: lightning-indexer scores.
+//
+// Source: "DeepSeek-V4 Hybrid Attention: CSA, HCA, mHC, MoE", section V.2: the score of
+// compressed block s for query t is sum_h w_{t,h} * ReLU(q_{t,h} . K_s) over the indexer
+// heads; "DeepSeek-V4: Anatomy of an Open-Source Frontier Model" (lesson 6.7): the
+// indexer runs in low precision.
+//
+// Scoring (index_score_fp8): the q_I . K_I contraction runs on MFMA (for c_I = 128 one
+// v_mfma_scale_f32_16x16x128_f8f6f4 with unit block scales per 16 heads x 16 keys; for
+// c_I = 32/64 v_mfma_f32_16x16x32_fp8_fp8).  Each lane streams C_I/4 contiguous bytes of
+// one key row straight from HBM into the B operand (no LDS); A takes the same bytes of
+// the indexer query row, so whatever order the instruction assigns to the contraction
+// dimension, it is the same for both operands and the dot products are exact.  ReLU, the
+// head weights and the cross-head sum are applied to the MFMA accumulators in registers.  Every score is
+// written once (fp32) and every group of 16 consecutive keys also writes its maximum
+// 64-bit selection key.
+#include "indexer.hpp"
+
+namespace {
+
+using namespace csahca;
+
+#ifndef CSAHCA_SCORE_WGS
+#define CSAHCA_SCORE_WGS 512  // scoring workgroups to aim for (about two per CU)
+#endif
+#ifndef CSAHCA_SCORE_CONTIG
+#define CSAHCA_SCORE_CONTIG 0  // 1: each wave scores a contiguous quarter of its chunk
+#endif
+
+// ---------------------------------------------------------------------------------------
+// scoring, FP8 E4M3FN keys on MFMA
+// ---------------------------------------------------------------------------------------
+// QPW queries per workgroup of 4 waves.  QPW = 1: the four waves split the key blocks of
+// one query (decode).  QPW = 4: each wave scores its own query over the same key blocks
+// (prefill; the repeated key reads hit in cache).  A wave walks its blocks with PF blocks
+// of keys in flight in registers: block k is scored while blocks k+1 .. k+PF-1 load.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+template <int C_I>
+struct KeyOperand;  // the C_I/4 contiguous key bytes one lane contributes per 16-key block
+
+template <>
+struct KeyOperand<128> {  // one v_mfma_scale_f32_16x16x128_f8f6f4 per head block
+  i32x8 v;
+  CSAHCA_DEV void load(const uint8_t* p) { v = *reinterpret_cast<const i32x8*>(p); }
+  CSAHCA_DEV void zero() { v = i32x8{0, 0, 0, 0, 0, 0, 0, 0}; }
+  CSAHCA_DEV static f32x4 mma(const KeyOperand& a, const KeyOperand& b, f32x4 c) {
+    // operand formats 0 = FP8 E4M3; block scales 127 = 2^0 (E8M0), i.e. no scaling
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a.v, b.v, c, 0, 0, 0, 127, 0, 127);
+  }
+};
+
+template <int C_I>
+struct KeyOperand {  // C_I in {32, 64}: v_mfma_f32_16x16x32_fp8_fp8, C_I/32 K-steps
+  static constexpr int KS = C_I / 32;
+  long v[KS];
+  CSAHCA_DEV void load(const uint8_t* p) {
+    if constexpr (KS == 2) {
+      const u32x4 a = *reinterpret_cast<const u32x4*>(p);
+      v[0] = (long)(((uint64_t)a[1] << 32) | a[0]);
+      v[1] = (long)(((uint64_t)a[3] << 32) | a[2]);
+    } else {
+      const u32x2 a = *reinterpret_cast<const u32x2*>(p);
+      v[0] = (long)(((uint64_t)a[1] << 32) | a[0]);
+    }
+  }
+  CSAHCA_DEV void zero() {
+#pragma unroll
+    for (int i = 0; i < KS; ++i) v[i] = 0;
+  }
+  CSAHCA_DEV static f32x4 mma(const KeyOperand& a, const KeyOperand& b, f32x4 c) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      c = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a.v[ks], b.v[ks], c, 0, 0, 0);
+    return c;
+  }
+};
+
+template <int C_I, int HB, int QPW, int PF>
+__global__ __launch_bounds__(256) void index_score_fp8(
+    const uint8_t* __restrict__ qI, const float* __restrict__ w, const uint8_t* __restrict__ KI,
+    const int* __restrict__ q_pos, int m, int Tq, int N_c, int CH, int nq, int NG,
+    float* __restrict__ scores, uint64_t* __restrict__ gkeys) {
+  constexpr int NIH = HB * 16;
+  constexpr int WPQ = 4 / QPW;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int q = blockIdx.y * QPW + wave / WPQ;
+  const int sub = wave % WPQ;
+  if (q >= nq) return;  // this kernel has no barriers: a finished wave may leave
+  const int b = q / Tq, t = q - b * Tq;
+  const int V = visible_entries(q_pos, b, t, m, N_c);
+  const int e_begin = blockIdx.x * CH;
+  const int e_end = min(e_begin + CH, V);
+  if (e_begin >= e_end) return;
+
+  const int row = lane & 15, g = lane >> 4;
+  // A operand: indexer query of head (16*hb + row), dims [g*C_I/4, (g+1)*C_I/4); the same
+  // dims of a key row form the B operand, so the dot products are those of the full rows
+  KeyOperand<C_I> a[HB];
+  const uint8_t* qp = qI + (size_t)q * NIH * C_I;
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) a[hb].load(qp + (hb * 16 + row) * C_I + g * (C_I / 4));
+  // head weights of the accumulator rows this lane holds: heads 16*hb + 4*g + i
+  float wr[HB][4];
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wr[hb][i] = w[(size_t)q * NIH + hb * 16 + 4 * g + i];
+
+  const uint8_t* kb = KI + (size_t)b * N_c * C_I + g * (C_I / 4);
+  float* srow = scores + (size_t)q * N_c;
+  uint64_t* grow = gkeys + (size_t)q * NG;
+  const int nblk = cdiv(e_end - e_begin, GROUP);
+#if CSAHCA_SCORE_CONTIG
+  // block k of this wave is sub*per + k
+  const int per = cdiv(nblk, WPQ);
+  const int nmine = max(0, min(per, nblk - sub * per));
+  auto blk_of = [&](int k) { return sub * per + k; };
+#else
+  const int nmine = nblk > sub ? cdiv(nblk - sub, WPQ) : 0;  // blocks sub, sub+WPQ, ...
+  auto blk_of = [&](int k) { return sub + k * WPQ; };
+#endif
+
+  // blocks past the end load a valid row instead (their scores are never used)
+  auto load_block = [&](KeyOperand<C_I>& dst, int k) {
+    const int e = min(e_begin + blk_of(min(k, nmine - 1)) * GROUP + row, e_end - 1);
+    dst.load(kb + (size_t)e * C_I);
+  };
+  // two register buffers of PF blocks: while one is scored the other is in flight, so
+  // every load has a full iteration of scoring to arrive
+  KeyOperand<C_I> kf0[PF], kf1[PF];
+#pragma unroll
+  for (int u = 0; u < PF; ++u) {
+    load_block(kf0[u], u);
+    load_block(kf1[u], PF + u);
+  }
+  auto score_blocks = [&](KeyOperand<C_I>(&kf)[PF], int k0) {
+    f32x4 acc[PF][HB];
+#pragma unroll
+    for (int u = 0; u < PF; ++u)
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) acc[u][hb] = KeyOperand<C_I>::mma(a[hb], kf[u], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+    for (int u = 0; u < PF; ++u) load_block(kf[u], k0 + 2 * PF + u);  // refill: two rounds ahead
+#pragma unroll
+    for (int u = 0; u < PF; ++u) {
+      const int k = k0 + u;
+      // lane holds key (row) for heads 16*hb + 4*g + i; sum over heads as a balanced tree
+      float t[4 * HB];
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) t[4 * hb + i] = wr[hb][i] * fmaxf(acc[u][hb][i], 0.f);
+#pragma unroll
+      for (int wdt = 2 * HB; wdt >= 1; wdt /= 2)
+#pragma unroll
+        for (int v = 0; v < wdt; ++v) t[v] += t[v + wdt];
+      const float score = sum_over_row_groups(t[0]);  // same value in lanes row, row+16, ...
+      const int e0 = e_begin + blk_of(k) * GROUP;
+      const int e = e0 + row;
+      const bool valid = k < nmine && e < e_end;
+      if (g == 0 && valid) srow[e] = score;
+      // group maximum: the best score of the 16 keys, lowest index among equal scores
+      const float sv = valid ? score : -INFINITY;
+      const float best = row16_max(sv);
+      const uint64_t hit = __ballot(valid && sv == best) & 0xFFFFull;
+      if (lane == 0 && hit != 0ull) grow[e0 / GROUP] = entry_key(best, (uint32_t)(e0 + __builtin_ctzll(hit)));
+    }
+  };
+  for (int k0 = 0; k0 < nmine; k0 += 2 * PF) {
+    score_blocks(kf0, k0);
+    if (k0 + PF < nmine) score_blocks(kf1, k0 + PF);
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// scoring, float32 keys (small heads; plain FMA)
+// ---------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void index_score_f32(
+    const float* __restrict__ qI, const float* __restrict__ w, const float* __restrict__ KI,
+    const int* __restrict__ q_pos, int m, int Tq, int N_c, int n_ih, int c_I, int NG,
+    float* __restrict__ scores, uint64_t* __restrict__ gkeys) {
+  extern __shared__ float smem_f[];
+  float* qs = smem_f;               // [n_ih * c_I]
+  float* ws = smem_f + n_ih * c_I;  // [n_ih]
+  const int q = blockIdx.y;
+  const int b = q / Tq, t = q - b * Tq;
+  for (int i = threadIdx.x; i < n_ih * c_I; i += blockDim.x) qs[i] = qI[(size_t)q * n_ih * c_I + i];
+  for (int i = threadIdx.x; i < n_ih; i += blockDim.x) ws[i] = w[(size_t)q * n_ih + i];
+  __syncthreads();
+  const int V = visible_entries(q_pos, b, t, m, N_c);
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;  // blockDim is a multiple of 16
+  const bool valid = e < V;
+  float s = 0.f;
+  if (valid) {
+    const float* kr = KI + ((size_t)b * N_c + e) * c_I;
+    for (int h = 0; h < n_ih; ++h) {
+      float d = 0.f;
+      for (int j = 0; j < c_I; ++j) d = fmaf(qs[h * c_I + j], kr[j], d);
+      s = fmaf(ws[h], fmaxf(d, 0.f), s);
+    }
+    scores[(size_t)q * N_c + e] = s;
+  }
+  uint64_t key = valid ? entry_key(s, (uint32_t)e) : 0ull;
+  key = umax64(key, shfl_xor_u64(key, 1));
+  key = umax64(key, shfl_xor_u64(key, 2));
+  key = umax64(key, shfl_xor_u64(key, 4));
+  key = umax64(key, shfl_xor_u64(key, 8));
+  if ((threadIdx.x & 15) == 0 && e < V) gkeys[(size_t)q * NG + e / GROUP] = key;
+}
+
+
+// ---------------------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------------------
+template <int C_I, int HB>
+void launch_fp8(const void* q_idx, const float* w_idx, const void* k_idx, const int* q_pos,
+                int m, int Tq, int N_c, int nq, int NG, float* scores, uint64_t* gkeys,
+                hipStream_t st) {
+  const bool decode = Tq == 1;
+  const int QPW = decode ? 1 : 4;
+  const int qgroups = cdiv(nq, QPW);
+  // about two workgroups per CU, each streaming a long chunk of keys
+  int chunks = cdiv(CSAHCA_SCORE_WGS, qgroups);
+  chunks = max(1, min(chunks, cdiv(N_c, 256)));
+  const int CH = cdiv(cdiv(N_c, chunks), 64) * 64;
+  chunks = cdiv(N_c, CH);
+  dim3 grid((unsigned)chunks, (unsigned)qgroups);
+  if (decode)
+    hipLaunchKernelGGL((index_score_fp8<C_I, HB, 1, 4>), grid, dim3(256), 0, st,
+                       (const uint8_t*)q_idx, w_idx, (const uint8_t*)k_idx, q_pos, m, Tq, N_c,
+                       CH, nq, NG, scores, gkeys);
+  else
+    hipLaunchKernelGGL((index_score_fp8<C_I, HB, 4, 4>), grid, dim3(256), 0, st,
+                       (const uint8_t*)q_idx, w_idx, (const uint8_t*)k_idx, q_pos, m, Tq, N_c,
+                       CH, nq, NG, scores, gkeys);
+}
+
+template <int C_I>
+bool launch_fp8_heads(int n_ih, const void* q_idx, const float* w_idx, const void* k_idx,
+                      const int* q_pos, int m, int Tq, int N_c, int nq, int NG, float* scores,
+                      uint64_t* gkeys, hipStream_t st) {
+  switch (n_ih / 16) {
+    case 1: launch_fp8<C_I, 1>(q_idx, w_idx, k_idx, q_pos, m, Tq, N_c, nq, NG, scores, gkeys, st); return true;
+    case 2: launch_fp8<C_I, 2>(q_idx, w_idx, k_idx, q_pos, m, Tq, N_c, nq, NG, scores, gkeys, st); return true;
+    case 4: launch_fp8<C_I, 4>(q_idx, w_idx, k_idx, q_pos, m, Tq, N_c, nq, NG, scores, gkeys, st); return true;
+    case 8: launch_fp8<C_I, 8>(q_idx, w_idx, k_idx, q_pos, m, Tq, N_c, nq, NG, scores, gkeys, st); return true;
+    default: return false;
+  }
+}
+
+}  // namespace
+
+namespace csahca {
+
+int index_check_common(const void* q_idx, const float* w_idx, const void* k_idx, int idx_dtype,
+                       const int* q_pos, int m, int B, int Tq, int n_ih, int c_I, int N_c, int k) {
+  using namespace csahca;
+  if (!q_idx || !w_idx || !k_idx || !q_pos)
+    return fail(CSAHCA_EINVAL, "indexer: q_idx, w_idx, k_idx and q_pos must be non-NULL");
+  if (B < 1 || Tq < 1 || n_ih < 1 || c_I < 1 || N_c < 1 || m < 1 || k < 1)
+    return fail(CSAHCA_EINVAL, "indexer: B, Tq, n_ih, c_I, N_c, m and k must be >= 1");
+  if (N_c > MAX_NC) return fail(CSAHCA_ENOTSUP, "indexer: N_c above 262144 is not built");
+  if (k > MAX_K) return fail(CSAHCA_ENOTSUP, "indexer: k above 1024 is not built");
+  if ((long long)B * Tq > 0x7FFFFFFFLL / 2) return fail(CSAHCA_ENOTSUP, "indexer: too many queries");
+  if (idx_dtype == CSAHCA_FP8_E4M3FN) {
+    if (n_ih % 16 != 0 || n_ih > 128)
+      return fail(CSAHCA_ENOTSUP, "indexer: FP8 keys need n_ih % 16 == 0 and n_ih <= 128");
+    if (c_I != 32 && c_I != 64 && c_I != 128)
+      return fail(CSAHCA_ENOTSUP, "indexer: FP8 keys need c_I in {32, 64, 128}");
+  } else if (idx_dtype == CSAHCA_F32) {
+    if (n_ih * c_I > 4096)
+      return fail(CSAHCA_ENOTSUP, "indexer: float32 keys need n_ih * c_I <= 4096");
+  } else {
+    return fail(CSAHCA_ENOTSUP, "indexer: idx_dtype must be CSAHCA_FP8_E4M3FN or CSAHCA_F32");
+  }
+  if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(w_idx))
+    return fail(CSAHCA_EINVAL, "indexer: q_idx, w_idx and k_idx must be 16-byte aligned");
+  return CSAHCA_OK;
+}
+
+
+int index_score_impl(const void* q_idx, const float* w_idx, const void* k_idx, int idx_dtype,
+                     const int* q_pos, int m, int B, int Tq, int n_ih, int c_I, int N_c,
+                     float* scores, uint64_t* gkeys, hipStream_t st) {
+  using namespace csahca;
+  const int nq = B * Tq;
+  const int NG = cdiv(N_c, GROUP);
+  if (idx_dtype == CSAHCA_FP8_E4M3FN) {
+    bool ok = false;
+    if (c_I == 128) ok = launch_fp8_heads<128>(n_ih, q_idx, w_idx, k_idx, q_pos, m, Tq, N_c, nq, NG, scores, gkeys, st);
+    else if (c_I == 64) ok = launch_fp8_heads<64>(n_ih, q_idx, w_idx, k_idx, q_pos, m, Tq, N_c, nq, NG, scores, gkeys, st);
+    else ok = launch_fp8_heads<32>(n_ih, q_idx, w_idx, k_idx, q_pos, m, Tq, N_c, nq, NG, scores, gkeys, st);
+    if (!ok) return fail(CSAHCA_ENOTSUP, "indexer: FP8 keys need n_ih in {16, 32, 64, 128}");
+  } else {
+    const size_t lds = (size_t)(n_ih * c_I + n_ih) * sizeof(float);
+    dim3 grid((unsigned)cdiv(N_c, 256), (unsigned)nq);
+    hipLaunchKernelGGL(index_score_f32, grid, dim3(256), lds, st, (const float*)q_idx, w_idx,
+                       (const float*)k_idx, q_pos, m, Tq, N_c, n_ih, c_I, NG, scores, gkeys);
+  }
+  return launch_status("lightning_index_score");
+}
+
+}  // namespace csahca
+
+extern "C" int lightning_index_score(const void* q_idx, const float* w_idx, const void* k_idx,
+                                     int idx_dtype, const int* q_pos, int m, int B, int Tq,
+                                     int n_ih, int c_I, int N_c, int k, float* scores,
+                                     void* workspace, size_t ws_bytes, void* stream) {
+  using namespace csahca;
+  int st = index_check_common(q_idx, w_idx, k_idx, idx_dtype, q_pos, m, B, Tq, n_ih, c_I, N_c, k);
+  if (st != CSAHCA_OK) return st;
+  if (!scores) return fail(CSAHCA_EINVAL, "lightning_index_score: scores must be non-NULL");
+  const WsLayout L = ws_layout((long long)B * Tq, N_c);
+  if (!workspace || ws_bytes < L.total)
+    return fail(CSAHCA_EWORKSPACE, "lightning_index_score: workspace missing or too small");
+  return index_score_impl(q_idx, w_idx, k_idx, idx_dtype, q_pos, m, B, Tq, n_ih, c_I, N_c, scores,
+                          (uint64_t*)((char*)workspace + L.gkeys_off), (hipStream_t)stream);
+}

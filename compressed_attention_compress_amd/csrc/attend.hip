@@ -45,8 +45,8 @@ struct AttnArgs {
   const int* q_pos;
   uint16_t* out;
   float* lse;
-  float* opart;   // [nq, n_splits, n_h, C] unnormalised partial outputs
-  float* mlpart;  // [nq, n_splits, n_h, 2] running max (log2 units) and sum
+  uint16_t* opart;  // [nq, n_splits, n_h, C] partial outputs O/l, scaled float16
+  float* mlpart;    // [nq, n_splits, n_h, 4] running max (log2 units), sum, scale, pad
   int B, Tq, n_h, Nc, k, L, W, m;
   int is_csa;
   int n_slots_c;  // compressed slots: k (CSA) or Nc (HCA)
@@ -61,10 +61,12 @@ struct AttnArgs {
   float scale_log2;
 };
 
+// entries visible to position p: min(N, (p+1)/m); positions are below 2^31 (32-bit
+// division: the 64-bit one is a long software sequence)
 CSAHCA_DEV int vis_count(long long p, int m, int N) {
-  long long v = (p + 1) / m;
-  if (p + 1 <= 0) v = 0;
-  return (int)(v < N ? v : N);
+  if (p + 1 <= 0) return 0;
+  const uint32_t v = (uint32_t)(p + 1) / (uint32_t)m;
+  return v < (uint32_t)N ? (int)v : N;
 }
 
 // Wait until at most N of this wave's vector-memory operations are outstanding, then
@@ -168,9 +170,9 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && NS == 2) ? 2 : 1) void attend_
   const int h0 = hg * a.HPW + (wave % wpq) * 16;
   const bool active = tq < a.Tq;
   const int tlast = min(t0 + a.Tg, a.Tq) - 1;
+  // positions first, while no DMA has been issued: uniform loads the compiler can make
+  // scalar (their wait is then independent of the vector loads issued below)
   const long long qpos0 = a.q_pos[b];
-  const long long pfirst = qpos0 + t0, plast = qpos0 + tlast;
-  const long long p = qpos0 + (active ? tq : tlast);
   const long long wp = a.win_pos[b];
   const int slot_lo = split * a.RS;
   const int slot_hi = min(a.n_slots, slot_lo + a.RS);
@@ -178,12 +180,109 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && NS == 2) ? 2 : 1) void attend_
   const uint16_t* ckv_b = a.ckv + (size_t)b * a.Nc * C;
   const uint16_t* win_b = a.win + (size_t)b * a.L * C;
   const int nsc = a.n_slots_c;
+  const int ntile = slot_hi > slot_lo ? cdiv(slot_hi - slot_lo, TILE) : 0;
+  constexpr int TPI = NS >= 4 ? 2 : 1;  // tiles consumed per iteration
 
+  // Position-dependent ranges, set once the positions have arrived (below):
   // window slot j >= nsc holds raw position wpos0 + (j - nsc), i.e. source row
   // wrow0 + (j - nsc).  Usable raw positions: >= 0, inside the source rows, and in the
   // query's own window (p-W, p]; for loading, the union over the workgroup's queries.
+  long long wrow0 = 0;
+  int wu_lo = nsc, wu_hi = nsc, wq_lo = nsc, wq_hi = nsc;
+  int Vu = 0, Vw = 0;  // HCA: entries visible to the last / to this wave's query
+
+  // DMA of tile tt into its ring stage: each wave issues rows wave, wave + NW, ...  of
+  // the tile, one 1 KiB row per instruction.  HCA with `spec`: compressed rows are
+  // loaded before the positions are known (every row below N_h is valid memory;
+  // visibility is applied by the score mask).  Tiles whose rows are all contiguous
+  // compressed rows (HCA) or all window rows, and CSA tiles of selected entries only, take
+  // short paths with no per-row branching; other tiles decide row by row.
+  uint32_t mybits = 0;  // this wave's rows of a tile
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) mybits |= 1u << (wave + i * NW);
+  auto dma_row = [&](const uint16_t* src, uint8_t* st, int r) {
+    __builtin_amdgcn_global_load_lds(src + lane * 8,
+                                     (__attribute__((address_space(3))) void*)(st + r * ROWB),
+                                     16, 0, 0);
+  };
+  auto issue = [&](int tt, bool spec) {
+    const int stage = tt % NS;
+    uint8_t* st = tiles + stage * (TILE * ROWB);
+    const int base = slot_lo + tt * TILE;
+    const int cend = min(slot_hi, nsc);  // end of this split's compressed slots
+    uint32_t okbits = 0;
+    if (!CSA && base + TILE <= cend && (spec || base + TILE <= Vu)) {
+      const uint16_t* src = ckv_b + (size_t)(base + wave) * C;
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) dma_row(src + (size_t)i * NW * C, st, wave + i * NW);
+      okbits = mybits;
+    } else if (base >= nsc && base >= wu_lo && base + TILE <= min(wu_hi, slot_hi)) {
+      const uint16_t* src = win_b + (size_t)(wrow0 + (base - nsc) + wave) * C;
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) dma_row(src + (size_t)i * NW * C, st, wave + i * NW);
+      okbits = mybits;
+    } else if (CSA && base + TILE <= cend) {
+      // lane i < LPW fetches the entry index of row wave + i*NW; rows read them by lane
+      const int ev = lane < LPW ? sidx[base - slot_lo + wave + lane * NW] : 0;
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) {
+        const int e = __builtin_amdgcn_readlane(ev, i);
+        const bool ok = (unsigned)e < (unsigned)a.Nc;
+        dma_row(ckv_b + (size_t)(ok ? e : 0) * C, st, wave + i * NW);
+        okbits |= ok ? (1u << (wave + i * NW)) : 0u;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) {
+        const int r = wave + i * NW;
+        const int j = base + r;
+        const uint16_t* src = ckv_b;  // dummy: any valid row
+        bool ok = false;
+        if (j < slot_hi) {
+          if (j < nsc) {
+            if (CSA) {
+              const int e = __builtin_amdgcn_readfirstlane(sidx[j - slot_lo]);
+              ok = (unsigned)e < (unsigned)a.Nc;
+              if (ok) src = ckv_b + (size_t)e * C;
+            } else if (spec || j < Vu) {
+              ok = true;
+              src = ckv_b + (size_t)j * C;
+            }
+          } else if (j >= wu_lo && j < wu_hi) {
+            ok = true;
+            src = win_b + (size_t)(wrow0 + (j - nsc)) * C;
+          }
+        }
+        okbits |= ok ? (1u << r) : 0u;
+        dma_row(src, st, r);
+      }
+    }
+    if (lane == 0) tmask[stage * NW + wave] = okbits;
+  };
+
+  // Start-up, ordered so that independent latencies overlap: the Q fragments, then (CSA)
+  // this split's entry indices or (HCA, when the first tiles hold only compressed rows)
+  // the first tiles themselves, while the positions arrive.
+  bf16x8 qf[KS];
+  {
+    const uint16_t* qp = a.q + (qrow * a.n_h + h0 + row16) * C + g * (C / 4);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qp + ks * 8));
+  }
+  if (CSA) {  // the split's selected entry indices, staged in LDS
+    const int* tk = a.topk + ((long long)b * a.Tq + t0) * a.k;
+    const int hi = min(slot_hi, nsc);
+    for (int j = slot_lo + (int)threadIdx.x; j < hi; j += NW * 64) sidx[j - slot_lo] = tk[j];
+  }
+  const bool spec = !CSA && slot_lo + TPI * TILE <= nsc;
+  if (spec)
+    for (int tt = 0; tt < TPI && tt < ntile; ++tt) issue(tt, true);
+
+  const long long pfirst = qpos0 + t0, plast = qpos0 + tlast;
+  const long long p = qpos0 + (active ? tq : tlast);
   const long long wpos0 = pfirst - a.W + 1;
-  const long long wrow0 = wpos0 - wp;
+  wrow0 = wpos0 - wp;
   auto win_slots = [&](long long lo_pos, long long hi_pos, int& lo, int& hi) {
     lo_pos = max(lo_pos, max(0LL, wp));
     hi_pos = min(hi_pos, wp + a.L - 1);
@@ -194,72 +293,23 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && NS == 2) ? 2 : 1) void attend_
     lo = nsc + (int)(lo_pos - wpos0);
     hi = nsc + (int)(hi_pos - wpos0) + 1;
   };
-  int wu_lo, wu_hi, wq_lo, wq_hi;
   win_slots(wpos0, plast, wu_lo, wu_hi);
   win_slots(p - a.W + 1, p, wq_lo, wq_hi);
-  const int Vu = CSA ? 0 : vis_count(plast, a.m, a.Nc);
-  const int Vw = CSA ? 0 : vis_count(p, a.m, a.Nc);
-
-  // CSA: this split's selected entry indices, staged in LDS (before any row is issued)
-  if (CSA) {
-    const int* tk = a.topk + ((long long)b * a.Tq + t0) * a.k;
-    const int hi = min(slot_hi, nsc);
-    for (int j = slot_lo + (int)threadIdx.x; j < hi; j += NW * 64) sidx[j - slot_lo] = tk[j];
-    __syncthreads();
+  if (!CSA) {
+    Vu = vis_count(plast, a.m, a.Nc);
+    Vw = vis_count(p, a.m, a.Nc);
   }
+  if (CSA) __syncthreads();  // sidx complete
   CSAHCA_TRACE(1);
 
-  const int ntile = slot_hi > slot_lo ? cdiv(slot_hi - slot_lo, TILE) : 0;
-  auto issue = [&](int tt) {
-    const int stage = tt % NS;
-    uint8_t* st = tiles + stage * (TILE * ROWB);
-    const int base = slot_lo + tt * TILE;
-    uint32_t okbits = 0;
-#pragma unroll
-    for (int i = 0; i < LPW; ++i) {
-      const int r = wave + i * NW;
-      const int j = base + r;
-      const uint16_t* src = ckv_b;  // dummy: any valid row
-      bool ok = false;
-      if (j < slot_hi) {
-        if (j < nsc) {
-          if (CSA) {
-            const int e = __builtin_amdgcn_readfirstlane(sidx[j - slot_lo]);
-            ok = (unsigned)e < (unsigned)a.Nc;
-            if (ok) src = ckv_b + (size_t)e * C;
-          } else if (j < Vu) {
-            ok = true;
-            src = ckv_b + (size_t)j * C;
-          }
-        } else if (j >= wu_lo && j < wu_hi) {
-          ok = true;
-          src = win_b + (size_t)(wrow0 + (j - nsc)) * C;
-        }
-      }
-      okbits |= ok ? (1u << r) : 0u;
-      __builtin_amdgcn_global_load_lds(src + lane * 8,
-                                       (__attribute__((address_space(3))) void*)(st + r * ROWB),
-                                       16, 0, 0);
-    }
-    if (lane == 0) tmask[stage * NW + wave] = okbits;
-  };
-
-  // Q fragments, then the first iteration's tiles, then the rest of the ring.  The
-  // compiler does not assume that row DMAs and register loads complete in order, so its
-  // wait for Q (forced here by the empty asm, once, rather than before the first MFMA of
-  // every iteration) drains every load issued so far: only the tiles needed first.
-  constexpr int TPI = NS >= 4 ? 2 : 1;  // tiles consumed per iteration
-  bf16x8 qf[KS];
-  {
-    const uint16_t* qp = a.q + (qrow * a.n_h + h0 + row16) * C + g * (C / 4);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      qf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qp + ks * 8));
-  }
-  for (int tt = 0; tt < TPI && tt < ntile; ++tt) issue(tt);
+  // The compiler does not assume that row DMAs and register loads complete in order, so
+  // its wait for Q (forced here by the empty asm, once, rather than before the first MFMA
+  // of every iteration) drains every load issued so far: only the tiles needed first.
+  if (!spec)
+    for (int tt = 0; tt < TPI && tt < ntile; ++tt) issue(tt, false);
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(qf[ks]));
-  for (int tt = TPI; tt < NS && tt < ntile; ++tt) issue(tt);
+  for (int tt = TPI; tt < NS && tt < ntile; ++tt) issue(tt, false);
 
   float m_run = -INFINITY, l_run = 0.f;
   f32x4 oacc[C / 16];
@@ -408,33 +458,64 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && NS == 2) ? 2 : 1) void attend_
     }
     lds_reads_done_barrier();  // the consumed stages are free for the next issue
     if (it < 3 * TPI) CSAHCA_TRACE(3 + 2 * (it / TPI) + (it ? 4 : 0));
-    for (int tt = it + NS; tt < it + NS + TPI && tt < ntile; ++tt) issue(tt);
+    for (int tt = it + NS; tt < it + NS + TPI && tt < ntile; ++tt) issue(tt, false);
   }
   CSAHCA_TRACE(4);
   if (!active) return;
 
-  // lane: head h0 + row16; oacc[cb][i] is column 16*cb + 4*g + i
+  // lane: head h0 + row16; oacc[cb][i] is column 16*cb + 4*g + i.  The wave's 16 output
+  // rows (heads h0 .. h0+15) are contiguous in both destinations.
   const int h = h0 + row16;
+  float f;              // multiplier from the accumulators to the stored 16-bit values
+  uint16_t* dst;        // the wave's first output row
+  bool as_f16;
   if (a.n_splits == 1) {
-    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-    uint16_t* op = a.out + (qrow * a.n_h + h) * C + 4 * g;
-#pragma unroll
-    for (int cb = 0; cb < C / 16; ++cb) {
-      const u32x2 o = {pack_bf16x2(oacc[cb][0] * inv, oacc[cb][1] * inv),
-                       pack_bf16x2(oacc[cb][2] * inv, oacc[cb][3] * inv)};
-      *reinterpret_cast<u32x2*>(op + 16 * cb) = o;
-    }
+    f = l_run > 0.f ? 1.f / l_run : 0.f;
+    dst = a.out + (qrow * a.n_h + h0) * C;
+    as_f16 = false;
     if (a.lse && g == 0)
       a.lse[qrow * a.n_h + h] = l_run > 0.f ? (m_run + __log2f(l_run)) * LN2 : -INFINITY;
   } else {
-    const long long pr = (qrow * a.n_splits + split) * a.n_h + h;
-    float* op = a.opart + pr * C + 4 * g;
+    // Partial output O / l in float16, scaled by a power of two 2^-e chosen per row so
+    // that its largest magnitude lies in [1, 2): no input range overflows, and every value
+    // keeps float16's 11-bit precision relative to the row's largest.  The record (m, l,
+    // 2^e) lets the merge weigh the row by l * 2^(m - M) * 2^e.
+    const long long pr0 = (qrow * a.n_splits + split) * a.n_h + h0;
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    float amax = 0.f;
 #pragma unroll
-    for (int cb = 0; cb < C / 16; ++cb) *reinterpret_cast<f32x4*>(op + 16 * cb) = oacc[cb];
+    for (int cb = 0; cb < C / 16; ++cb)
+      amax = fmaxf(amax, fmaxf(fmaxf(fabsf(oacc[cb][0]), fabsf(oacc[cb][1])),
+                               fmaxf(fabsf(oacc[cb][2]), fabsf(oacc[cb][3]))));
+    amax = max_over_row_groups(amax) * inv;  // the head's four lanes hold its 512 columns
+    const uint32_t ex = min(max((__float_as_uint(amax) >> 23) & 0xFFu, 1u), 253u);
+    f = inv * __uint_as_float((254u - ex) << 23);  // 1 / (l * 2^(ex - 127))
+    dst = a.opart + pr0 * C;
+    as_f16 = true;
     if (g == 0) {
-      a.mlpart[pr * 2 + 0] = m_run;
-      a.mlpart[pr * 2 + 1] = l_run;
+      *reinterpret_cast<f32x4*>(a.mlpart + (pr0 + row16) * 4) =
+          f32x4{m_run, l_run, __uint_as_float(ex << 23), 0.f};
     }
+  }
+  auto pack = [&](float x, float y) { return as_f16 ? pack_f16x2(x * f, y * f) : pack_bf16x2(x * f, y * f); };
+  constexpr int EROWB = C * 2 + 16;  // staging row stride in bytes
+  if (NW * 16 * EROWB <= NS * TILE * ROWB) {
+    // through LDS (the tiles are free: every wave passed the loop's last barrier and no
+    // row load is outstanding), so that each store writes one whole 1 KiB row
+    uint8_t* stg = tiles + wave * 16 * EROWB;
+#pragma unroll
+    for (int cb = 0; cb < C / 16; ++cb)
+      *reinterpret_cast<u32x2*>(stg + row16 * EROWB + (16 * cb + 4 * g) * 2) =
+          u32x2{pack(oacc[cb][0], oacc[cb][1]), pack(oacc[cb][2], oacc[cb][3])};
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      *reinterpret_cast<u32x4*>(dst + r * C + lane * 8) =
+          *reinterpret_cast<const u32x4*>(stg + r * EROWB + lane * 16);
+  } else {
+    uint16_t* op = dst + row16 * C + 4 * g;
+#pragma unroll
+    for (int cb = 0; cb < C / 16; ++cb)
+      *reinterpret_cast<u32x2*>(op + 16 * cb) = u32x2{pack(oacc[cb][0], oacc[cb][1]), pack(oacc[cb][2], oacc[cb][3])};
   }
   CSAHCA_TRACE(5);
   CSAHCA_TRACE_RT(15);
@@ -442,8 +523,10 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && NS == 2) ? 2 : 1) void attend_
 
 // Merge the splits of every (query, head) by their log-sum-exp.  One workgroup per pair:
 // wave w takes the splits w, w+4, ..., eight partial rows in flight per lane (8 columns
-// each); the four wave sums are then added in a fixed order.
-__global__ __launch_bounds__(256) void attend_combine(const float* __restrict__ opart,
+// each); the four wave sums are then added in a fixed order.  A split's partial row holds
+// its output normalised by its own sum l_s and scaled by 2^-e_s (float16); its weight in
+// the merge is l_s * 2^(m_s - M) * 2^e_s, M the largest running maximum.
+__global__ __launch_bounds__(256) void attend_combine(const uint16_t* __restrict__ opart,
                                                       const float* __restrict__ mlpart,
                                                       uint16_t* __restrict__ out,
                                                       float* __restrict__ lse, int n_h,
@@ -455,37 +538,35 @@ __global__ __launch_bounds__(256) void attend_combine(const float* __restrict__ 
   const int h = (int)(pair - qrow * n_h);
   const long long pr0 = qrow * n_splits * n_h + h;  // partial row of split s: pr0 + s*n_h
   float M = -INFINITY;
-  for (int s = lane; s < n_splits; s += 64) M = fmaxf(M, mlpart[(pr0 + (long long)s * n_h) * 2]);
+  for (int s = lane; s < n_splits; s += 64) M = fmaxf(M, mlpart[(pr0 + (long long)s * n_h) * 4]);
   for (int d = 1; d < 64; d <<= 1) M = fmaxf(M, shfl_xor_f(M, d));
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float Ls = 0.f;
   if (M != -INFINITY) {
     for (int s0 = wave; s0 < n_splits; s0 += 32) {
-      f32x4 x0[8], x1[8];
-      float ms[8], ls[8];
+      u32x4 x[8];
+      f32x4 ml[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int s = s0 + 4 * u;
         if (s < n_splits) {
           const long long pr = pr0 + (long long)s * n_h;
-          ms[u] = mlpart[pr * 2];
-          ls[u] = mlpart[pr * 2 + 1];
-          x0[u] = *reinterpret_cast<const f32x4*>(opart + pr * C + lane * 8);
-          x1[u] = *reinterpret_cast<const f32x4*>(opart + pr * C + lane * 8 + 4);
+          ml[u] = *reinterpret_cast<const f32x4*>(mlpart + pr * 4);
+          x[u] = *reinterpret_cast<const u32x4*>(opart + pr * C + lane * 8);
         } else {
-          ms[u] = -INFINITY;
-          ls[u] = 0.f;
-          x0[u] = x1[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+          ml[u] = f32x4{-INFINITY, 0.f, 0.f, 0.f};
+          x[u] = u32x4{0u, 0u, 0u, 0u};
         }
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const float wgt = ms[u] == -INFINITY ? 0.f : exp2f(ms[u] - M);
-        Ls = fmaf(wgt, ls[u], Ls);
+        const float w = ml[u][0] == -INFINITY ? 0.f : ml[u][1] * exp2f(ml[u][0] - M);
+        Ls += w;
+        const float wgt = w * ml[u][2];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          acc[i] = fmaf(wgt, x0[u][i], acc[i]);
-          acc[4 + i] = fmaf(wgt, x1[u][i], acc[4 + i]);
+          acc[2 * i] = fmaf(wgt, f16_lo(x[u][i]), acc[2 * i]);
+          acc[2 * i + 1] = fmaf(wgt, f16_hi(x[u][i]), acc[2 * i + 1]);
         }
       }
     }
@@ -616,7 +697,7 @@ struct Plan {
 // Launch shape.  A workgroup holds up to 64 heads (4 waves; 8 waves when two prefill
 // queries share the rows).  When the queries alone give fewer than 256 workgroups their
 // rows are split over more (one per CU, each keeping three tiles in flight), but never
-// below 96 rows per split: each split writes an fp32 partial of HPW x 512 floats.
+// below 96 rows per split: each split writes a partial of HPW x 512 float16 values.
 Plan make_plan(int B, int Tq, int n_h, int n_slots_c, int W, bool csa) {
   Plan P;
   P.Tg = 1;
@@ -641,8 +722,8 @@ Plan make_plan(int B, int Tq, int n_h, int n_slots_c, int W, bool csa) {
   P.n_work = (int)(base * P.n_splits);
   P.per_xcd = cdiv(P.n_work, 8);
   const long long nqh = (long long)B * Tq * n_h;
-  P.opart_bytes = P.n_splits > 1 ? csahca::align_up((size_t)(nqh * P.n_splits * C * 4), 256) : 0;
-  P.ml_bytes = P.n_splits > 1 ? csahca::align_up((size_t)(nqh * P.n_splits * 2 * 4), 256) : 0;
+  P.opart_bytes = P.n_splits > 1 ? csahca::align_up((size_t)(nqh * P.n_splits * C * 2), 256) : 0;
+  P.ml_bytes = P.n_splits > 1 ? csahca::align_up((size_t)(nqh * P.n_splits * 4 * 4), 256) : 0;
   P.ws = P.opart_bytes + P.ml_bytes;
   P.lds = attend_lds_bytes(P.NS, P.NW, P.RS, csa);
   return P;
@@ -691,7 +772,7 @@ int check_attend(const char* name, const void* q, const void* ckv, const void* w
   }
   if (dtype == CSAHCA_BF16) {
     if (c != C || n_h % 16 != 0 || n_h > 128) {
-      set_error("%s: bfloat16 needs c == 512, n_h % 16 == 0 and n_h <= 128", name);
+      set_error("%s: bfloat16 needs c == 512, n_h %% 16 == 0 and n_h <= 128", name);
       return CSAHCA_ENOTSUP;
     }
   } else if (dtype == CSAHCA_F32) {
@@ -760,7 +841,7 @@ int attend_impl(const char* name, bool csa, const void* q, const void* ckv, cons
   A.q_pos = q_pos;
   A.out = (uint16_t*)out;
   A.lse = lse;
-  A.opart = P.n_splits > 1 ? (float*)workspace : nullptr;
+  A.opart = P.n_splits > 1 ? (uint16_t*)workspace : nullptr;
   A.mlpart = P.n_splits > 1 ? (float*)((char*)workspace + P.opart_bytes) : nullptr;
   A.B = B;
   A.Tq = Tq;

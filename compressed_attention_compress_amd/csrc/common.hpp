@@ -62,6 +62,14 @@ CSAHCA_DEV uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
 }
 
+// float16, round to nearest even (the hardware conversion); two halves in one word
+CSAHCA_DEV uint32_t pack_f16x2(float lo, float hi) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
+}
+CSAHCA_DEV float f16_lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu)); }
+CSAHCA_DEV float f16_hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
+
 // Order-preserving map of a float score to an unsigned key (larger score -> larger key);
 // -0.0 is folded onto +0.0 so that the two compare equal.
 CSAHCA_DEV uint32_t score_key(float f) {

@@ -64,8 +64,9 @@ extern "C" {
 
 /*
  * csa_compress / hca_compress -- softmax-gated block pooling.
- * Source: trishampatil.com section V.1 (equation C_i^comp) and VI (non-overlapping m'
- * blocks); shivasnotes.com section 6 ("blockwise softmax plus weighted reduction").
+ * Source: "DeepSeek-V4 Hybrid Attention: CSA, HCA, mHC, MoE", section V.1 (equation
+ * C_i^comp) and VI (non-overlapping m' blocks); "DeepSeek-V4 Architecture From Kernels",
+ * section 6 (a softmax within each block followed by a weighted sum).
  *
  *   out[b, i, ch] = sum_{j<m} S[b,i,j,ch] * kv[b, m*i+j, ch],
  *   S[b,i,.,ch]   = softmax_j( gate[b, m*i+j, ch] + pos_bias[j, ch] )
@@ -92,8 +93,9 @@ int hca_compress(const void* kv, const void* gate, const float* pos_bias, void* 
 
 /*
  * lightning_index_topk -- lightning-indexer scores and exact top-k selection.
- * Source: trishampatil.com section V.2, equation I_{t,s} and the Top-k selector;
- * modernaiengineering.com "Worked example" (top-k cannot pick more entries than exist).
+ * Source: "DeepSeek-V4 Hybrid Attention: CSA, HCA, mHC, MoE", section V.2, equation
+ * I_{t,s} and the top-k selector; "DeepSeek-V4: Anatomy of an Open-Source Frontier
+ * Model", "Worked example" (top-k can pick no more entries than exist).
  *
  *   I[b,t,s] = sum_h w_idx[b,t,h] * max(0, sum_d q_idx[b,t,h,d] * k_idx[b,s,d])
  * for every usable entry s (V = min(N_c, (p+1)/m) of them).  The selection keeps
@@ -136,10 +138,11 @@ int lightning_index_select(const float* scores, const int* q_pos, int m, int B, 
 /*
  * csa_attend -- multi-query attention over the selected compressed entries plus the
  * sliding window, one joint softmax.
- * Source: trishampatil.com section V.3 (core attention in MQA form over the selected
- * blocks; one K = V row shared by all heads) and section I (softmax(QK^T/sqrt(c))V);
- * modernaiengineering.com "One query in a CSA layer", steps 3-5 (selected entries plus the
- * last 128 raw tokens, attended together).
+ * Source: "DeepSeek-V4 Hybrid Attention: CSA, HCA, mHC, MoE", section V.3 (core attention
+ * in MQA form over the selected blocks; one K = V row shared by all heads) and section I
+ * (softmax(QK^T/sqrt(c))V); "DeepSeek-V4: Anatomy of an Open-Source Frontier Model",
+ * "One query in a CSA layer", steps 3-5 (selected entries plus the last 128 raw tokens,
+ * attended together).
  *
  *   rows(b,t) = { ckv[b, s] : s in topk_idx[b,t,:], s != -1 } followed by the window rows
  *   out[b,t,h] = sum_r softmax_r(scale * q[b,t,h] . row_r) * row_r
@@ -161,9 +164,10 @@ int csa_attend(const void* q, const void* ckv, const int* topk_idx, const void* 
 
 /*
  * hca_attend -- multi-query attention over every usable compressed entry plus the window.
- * Source: trishampatil.com section VI, equation o_{t,i} (query q_{t,i}, key = value =
- * C^comp, dense over all compressed entries, MQA); modernaiengineering.com "Hybrid
- * attention with CSA and HCA" (128-token uncompressed window in both layer types).
+ * Source: "DeepSeek-V4 Hybrid Attention: CSA, HCA, mHC, MoE", section VI, equation
+ * o_{t,i} (query q_{t,i}, key = value = C^comp, dense over all compressed entries, MQA);
+ * "DeepSeek-V4: Anatomy of an Open-Source Frontier Model", "Hybrid attention with CSA and
+ * HCA" (128-token uncompressed window in both layer types).
  *
  *   rows(b,t) = { ckv[b, s] : s < min(N_h, (p+1)/m) } followed by the window rows.
  * Arguments as csa_attend, with m the HCA block size (m') and N_h the cache length.

@@ -126,10 +126,18 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ X,
   const long long item = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (item >= total) return;
   const int CV = c / VEC;
-  const int cv = (int)(item % CV);
-  const long long rest = item / CV;
-  const int i = (int)(rest % N);
-  const int b = (int)(rest / N);
+  int cv, i, b;
+  if (total <= 0x7FFFFFFFLL) {  // 32-bit index math (64-bit division is a long sequence)
+    const uint32_t it = (uint32_t)item, rest = it / (uint32_t)CV;
+    cv = (int)(it - rest * (uint32_t)CV);
+    b = (int)(rest / (uint32_t)N);
+    i = (int)(rest - (uint32_t)b * (uint32_t)N);
+  } else {
+    cv = (int)(item % CV);
+    const long long rest = item / CV;
+    i = (int)(rest % N);
+    b = (int)(rest / N);
+  }
   const long long base = (long long)b * in_bs + (long long)i * m * c + (long long)cv * VEC;
   float mx[VEC], sum[VEC], acc[VEC];
 #pragma unroll
@@ -145,21 +153,31 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ X,
   Vec8<T>::store(out + (long long)b * out_bs + (long long)i * c + (long long)cv * VEC, res);
 }
 
-// Few blocks (a cache append at decode): one workgroup per (sequence, block).  Its
-// threads split the block's m tokens into S contiguous sub-ranges per 8-channel slice,
-// each with its own running softmax; the S partial states are merged in LDS in a fixed
-// order, so the result does not depend on timing.
+// Few blocks (a cache append at decode): the workgroups of one (sequence, block) split
+// its channels into groups of CVG 8-channel slices, and a workgroup's threads split the
+// block's tokens into S contiguous sub-ranges per slice, each with its own running
+// softmax.  The S partial states of a channel are merged in LDS in a fixed order (the
+// result does not depend on timing), one thread per channel.
+template <typename T>
+CSAHCA_DEV void store_one(T* p, float v);
+template <>
+CSAHCA_DEV void store_one<uint16_t>(uint16_t* p, float v) { *p = f32_to_bf16(v); }
+template <>
+CSAHCA_DEV void store_one<float>(float* p, float v) { *p = v; }
+
 template <typename T, int UB, bool HAS_P>
-__global__ __launch_bounds__(512) void pool_block_kernel(const T* __restrict__ X,
+__global__ __launch_bounds__(256) void pool_block_kernel(const T* __restrict__ X,
                                                         const T* __restrict__ Z,
                                                         const float* __restrict__ P,
                                                         T* __restrict__ out, int N, int c,
-                                                        int m, int S, long long in_bs,
+                                                        int m, int S, int CVG, long long in_bs,
                                                         long long out_bs) {
-  extern __shared__ float part[];  // [S][CV][3][VEC]
-  const int CV = c / VEC;
-  const int cv = threadIdx.x % CV, s = threadIdx.x / CV;
-  const int b = blockIdx.x / N, i = blockIdx.x % N;
+  extern __shared__ float part[];  // [S][CVG][3][VEC]
+  const int CG = c / VEC / CVG;
+  const int cvl = threadIdx.x % CVG, s = threadIdx.x / CVG;
+  const int cg = blockIdx.x % CG, bi = blockIdx.x / CG;
+  const int b = bi / N, i = bi - b * N;
+  const int cv = cg * CVG + cvl;
   const int span = cdiv(m, S);
   const int j_lo = min(m, s * span), j_hi = min(m, j_lo + span);
   const long long base = (long long)b * in_bs + (long long)i * m * c + (long long)cv * VEC;
@@ -171,7 +189,7 @@ __global__ __launch_bounds__(512) void pool_block_kernel(const T* __restrict__ X
     acc[e] = 0.f;
   }
   pool_run<T, UB, HAS_P>(X + base, Z + base, HAS_P ? P + cv * VEC : nullptr, c, j_lo, j_hi, mx, sum, acc);
-  float* mine = part + ((size_t)s * CV + cv) * 3 * VEC;
+  float* mine = part + ((size_t)s * CVG + cvl) * 3 * VEC;
 #pragma unroll
   for (int e = 0; e < VEC; ++e) {
     mine[e] = mx[e];
@@ -179,41 +197,45 @@ __global__ __launch_bounds__(512) void pool_block_kernel(const T* __restrict__ X
     mine[2 * VEC + e] = acc[e];
   }
   __syncthreads();
-  if (s != 0) return;
-  float res[VEC];
-#pragma unroll
-  for (int e = 0; e < VEC; ++e) {
+  T* orow = out + (long long)b * out_bs + (long long)i * c + (long long)cg * CVG * VEC;
+  for (int t = threadIdx.x; t < CVG * VEC; t += blockDim.x) {
+    const int sl = t / VEC, e = t - sl * VEC;
     float M = -INFINITY;
-    for (int r = 0; r < S; ++r) M = fmaxf(M, part[((size_t)r * CV + cv) * 3 * VEC + e]);
-    float sm = 0.f, a = 0.f;
+    for (int r = 0; r < S; ++r) M = fmaxf(M, part[((size_t)r * CVG + sl) * 3 * VEC + e]);
+    float sm = 0.f, av = 0.f;
     for (int r = 0; r < S; ++r) {
-      const float* pr = part + ((size_t)r * CV + cv) * 3 * VEC;
+      const float* pr = part + ((size_t)r * CVG + sl) * 3 * VEC;
       const float w = __expf(pr[e] - M);  // empty sub-range: exp(-inf) = 0
       sm = fmaf(pr[VEC + e], w, sm);
-      a = fmaf(pr[2 * VEC + e], w, a);
+      av = fmaf(pr[2 * VEC + e], w, av);
     }
-    res[e] = a / sm;
+    store_one<T>(orow + t, av / sm);
   }
-  Vec8<T>::store(out + (long long)b * out_bs + (long long)i * c + (long long)cv * VEC, res);
 }
 
 template <typename T, bool HAS_P>
 void launch_pool(const void* kv, const void* gate, const float* pos_bias, void* out, int B,
                  long long N, int c, int m, long long in_bs, long long out_bs, hipStream_t st) {
   const long long total = (long long)B * N * (c / 8);
-  // few blocks of many tokens: split each block's tokens over more threads
-  int S = min(m / 8, 512 / (c / 8));
-  if (S > 8) S = 8;
-  const size_t lds = (size_t)max(S, 1) * (c / 8) * 3 * VEC * sizeof(float);
-  if (total < 32768 && S >= 2 && lds <= 65536) {
-    const int span = cdiv(m, S);
-    const unsigned grid = (unsigned)(B * N), threads = (unsigned)(S * (c / 8));
-    if (span % 16 == 0 && sizeof(T) == 2)
-      hipLaunchKernelGGL((pool_block_kernel<T, 16, HAS_P>), dim3(grid), dim3(threads), lds, st,
-                         (const T*)kv, (const T*)gate, pos_bias, (T*)out, (int)N, c, m, S, in_bs, out_bs);
-    else
+  const int CV = c / VEC;
+  if (total < 32768 && m >= 8) {
+    // few blocks of many tokens: 8-channel slices in groups of up to 8 per workgroup,
+    // tokens in sub-ranges of at least 4, at most 256 threads per workgroup
+    int CVG = 8;
+    while (CV % CVG != 0) CVG /= 2;
+    const int smax = 256 / CVG;
+    const int span = max(4, cdiv(m, smax));
+    const int S = cdiv(m, span);
+    const size_t lds = (size_t)S * CVG * 3 * VEC * sizeof(float);
+    const unsigned grid = (unsigned)(B * N * (CV / CVG)), threads = (unsigned)(S * CVG);
+    if (span % 8 == 0)
       hipLaunchKernelGGL((pool_block_kernel<T, 8, HAS_P>), dim3(grid), dim3(threads), lds, st,
-                         (const T*)kv, (const T*)gate, pos_bias, (T*)out, (int)N, c, m, S, in_bs, out_bs);
+                         (const T*)kv, (const T*)gate, pos_bias, (T*)out, (int)N, c, m, S, CVG,
+                         in_bs, out_bs);
+    else
+      hipLaunchKernelGGL((pool_block_kernel<T, 4, HAS_P>), dim3(grid), dim3(threads), lds, st,
+                         (const T*)kv, (const T*)gate, pos_bias, (T*)out, (int)N, c, m, S, CVG,
+                         in_bs, out_bs);
     return;
   }
   const unsigned blocks = (unsigned)cdiv<long long>(total, 256);

@@ -170,15 +170,16 @@ CSAHCA_DEV uint32_t wave_or(uint32_t x) {
 // shader-clock stamps in slots 0..13, fixed-rate stamps in slots 14 and 15.
 #ifdef CSAHCA_TRACE_ENABLED
 __device__ unsigned long long csahca_trace[8192 * 16];
+#define CSAHCA_TRACE_WG (blockIdx.x + blockIdx.y * gridDim.x)
 #define CSAHCA_TRACE(slot)                                                              \
   do {                                                                                  \
-    if (threadIdx.x == 0 && blockIdx.x < 8192)                                          \
-      csahca_trace[blockIdx.x * 16 + (slot)] = __builtin_amdgcn_s_memtime();            \
+    if (threadIdx.x == 0 && CSAHCA_TRACE_WG < 8192)                                     \
+      csahca_trace[CSAHCA_TRACE_WG * 16 + (slot)] = __builtin_amdgcn_s_memtime();       \
   } while (0)
 #define CSAHCA_TRACE_RT(slot)                                                           \
   do {                                                                                  \
-    if (threadIdx.x == 0 && blockIdx.x < 8192)                                          \
-      csahca_trace[blockIdx.x * 16 + (slot)] = __builtin_amdgcn_s_memrealtime();        \
+    if (threadIdx.x == 0 && CSAHCA_TRACE_WG < 8192)                                     \
+      csahca_trace[CSAHCA_TRACE_WG * 16 + (slot)] = __builtin_amdgcn_s_memrealtime();   \
   } while (0)
 #else
 #define CSAHCA_TRACE(slot) \
@@ -191,6 +192,6 @@ __device__ unsigned long long csahca_trace[8192 * 16];
 
 // ceil-div for host and device
 template <typename T>
-__host__ __device__ inline T cdiv(T a, T b) {
+__host__ __device__ constexpr T cdiv(T a, T b) {
   return (a + b - 1) / b;
 }

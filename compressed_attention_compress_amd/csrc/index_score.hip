@@ -23,9 +23,7 @@ using namespace csahca;
 #ifndef CSAHCA_SCORE_WGS
 #define CSAHCA_SCORE_WGS 512  // scoring workgroups to aim for (about two per CU)
 #endif
-#ifndef CSAHCA_SCORE_CONTIG
-#define CSAHCA_SCORE_CONTIG 0  // 1: each wave scores a contiguous quarter of its chunk
-#endif
+constexpr int SCORE_STAGE = 4096;  // keys per decode workgroup (LDS-staged scores)
 
 // ---------------------------------------------------------------------------------------
 // scoring, FP8 E4M3FN keys on MFMA
@@ -87,12 +85,12 @@ __global__ __launch_bounds__(256) void index_score_fp8(
   const int lane = threadIdx.x & 63;
   const int q = blockIdx.y * QPW + wave / WPQ;
   const int sub = wave % WPQ;
-  if (q >= nq) return;  // this kernel has no barriers: a finished wave may leave
+  if (q >= nq) return;  // QPW == 1: the four waves share q (the one barrier stays uniform)
   const int b = q / Tq, t = q - b * Tq;
-  const int V = visible_entries(q_pos, b, t, m, N_c);
   const int e_begin = blockIdx.x * CH;
-  const int e_end = min(e_begin + CH, V);
-  if (e_begin >= e_end) return;
+  // the chunk's keys are loaded before the visible count is known (every key below N_c is
+  // valid memory); scores past the visible count are never written
+  const int e_lim = min(e_begin + CH, N_c);
 
   const int row = lane & 15, g = lane >> 4;
   // A operand: indexer query of head (16*hb + row), dims [g*C_I/4, (g+1)*C_I/4); the same
@@ -111,20 +109,14 @@ __global__ __launch_bounds__(256) void index_score_fp8(
   const uint8_t* kb = KI + (size_t)b * N_c * C_I + g * (C_I / 4);
   float* srow = scores + (size_t)q * N_c;
   uint64_t* grow = gkeys + (size_t)q * NG;
-  const int nblk = cdiv(e_end - e_begin, GROUP);
-#if CSAHCA_SCORE_CONTIG
-  // block k of this wave is sub*per + k
-  const int per = cdiv(nblk, WPQ);
-  const int nmine = max(0, min(per, nblk - sub * per));
-  auto blk_of = [&](int k) { return sub * per + k; };
-#else
-  const int nmine = nblk > sub ? cdiv(nblk - sub, WPQ) : 0;  // blocks sub, sub+WPQ, ...
-  auto blk_of = [&](int k) { return sub + k * WPQ; };
-#endif
+  auto count_mine = [&](int nblk) { return nblk > sub ? cdiv(nblk - sub, WPQ) : 0; };
+  auto blk_of = [&](int k) { return sub + k * WPQ; };  // blocks sub, sub+WPQ, ...
+  int nmine = count_mine(cdiv(e_lim - e_begin, GROUP));
+  int e_last = e_lim - 1;
 
   // blocks past the end load a valid row instead (their scores are never used)
   auto load_block = [&](KeyOperand<C_I>& dst, int k) {
-    const int e = min(e_begin + blk_of(min(k, nmine - 1)) * GROUP + row, e_end - 1);
+    const int e = min(e_begin + blk_of(min(k, nmine - 1)) * GROUP + row, e_last);
     dst.load(kb + (size_t)e * C_I);
   };
   // two register buffers of PF blocks: while one is scored the other is in flight, so
@@ -135,12 +127,26 @@ __global__ __launch_bounds__(256) void index_score_fp8(
     load_block(kf0[u], u);
     load_block(kf1[u], PF + u);
   }
+  const int V = visible_entries(q_pos, b, t, m, N_c);
+  const int e_end = min(e_lim, V);
+  if (e_begin >= e_end) return;  // uniform over the workgroup when QPW == 1
+  nmine = count_mine(cdiv(e_end - e_begin, GROUP));
+  e_last = e_end - 1;
+  // QPW == 1 (decode): scores and group maxima are staged in LDS and written after the
+  // last key load.  Vector stores share the load counter and may complete out of order
+  // with loads, so a store inside the loop would make every later wait for a key block a
+  // wait for all of them.
+  __shared__ float s_sc[QPW == 1 ? SCORE_STAGE : 1];
+  __shared__ uint64_t s_gk[QPW == 1 ? SCORE_STAGE / GROUP : 1];
   auto score_blocks = [&](KeyOperand<C_I>(&kf)[PF], int k0) {
     f32x4 acc[PF][HB];
 #pragma unroll
     for (int u = 0; u < PF; ++u)
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb) acc[u][hb] = KeyOperand<C_I>::mma(a[hb], kf[u], f32x4{0.f, 0.f, 0.f, 0.f});
+    // the refill may not move above the MFMAs that read the buffer: then the loads can
+    // reuse its registers, and no load result is copied (waited for) at the loop edge
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < PF; ++u) load_block(kf[u], k0 + 2 * PF + u);  // refill: two rounds ahead
 #pragma unroll
@@ -160,18 +166,191 @@ __global__ __launch_bounds__(256) void index_score_fp8(
       const int e0 = e_begin + blk_of(k) * GROUP;
       const int e = e0 + row;
       const bool valid = k < nmine && e < e_end;
-      if (g == 0 && valid) srow[e] = score;
+      if (g == 0 && valid) {
+        if (QPW == 1) s_sc[e - e_begin] = score;
+        else srow[e] = score;
+      }
       // group maximum: the best score of the 16 keys, lowest index among equal scores
       const float sv = valid ? score : -INFINITY;
       const float best = row16_max(sv);
       const uint64_t hit = __ballot(valid && sv == best) & 0xFFFFull;
-      if (lane == 0 && hit != 0ull) grow[e0 / GROUP] = entry_key(best, (uint32_t)(e0 + __builtin_ctzll(hit)));
+      if (lane == 0 && hit != 0ull) {
+        const uint64_t key = entry_key(best, (uint32_t)(e0 + __builtin_ctzll(hit)));
+        if (QPW == 1) s_gk[(e0 - e_begin) / GROUP] = key;
+        else grow[e0 / GROUP] = key;
+      }
     }
   };
+  // both buffers every iteration (blocks past nmine are masked), so that each buffer is
+  // refilled in place and no load result has to be copied at the loop edge
   for (int k0 = 0; k0 < nmine; k0 += 2 * PF) {
     score_blocks(kf0, k0);
-    if (k0 + PF < nmine) score_blocks(kf1, k0 + PF);
+    score_blocks(kf1, k0 + PF);
   }
+  if (QPW == 1) {  // coalesced write-out of the staged chunk
+    __syncthreads();
+    const int n = e_end - e_begin;
+    for (int i = (int)threadIdx.x; i < n; i += 256) srow[e_begin + i] = s_sc[i];
+    for (int i = (int)threadIdx.x; i < cdiv(n, GROUP); i += 256) grow[e_begin / GROUP + i] = s_gk[i];
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// scoring at decode, c_I = 128: key blocks streamed by row DMA into per-wave LDS rings
+// ---------------------------------------------------------------------------------------
+// One query per workgroup of 4 waves; wave w scores key blocks w, w+4, ... of the
+// workgroup's chunk.  Each wave keeps RING - 1 blocks of 16 keys (2 KiB each) in flight
+// with global_load_lds (the data bypasses registers, so no register rotation can force
+// a drain) and waits for its own oldest block with an explicit vmcnt; the rings are
+// private to a wave, so there is no barrier until the final write-out.  Inside a block,
+// row r holds its 16-byte chunks in the order c ^ (r & 7): a lane reading 32 bytes of its
+// key row then hits eight distinct bank groups per eight lanes.
+constexpr int RING = 6;
+
+template <int MAXN>
+CSAHCA_DEV void wait_vm_le(int n) {  // s_waitcnt vmcnt(2 * min(n, MAXN)): n blocks may stay
+  if (MAXN >= 5 && n >= 5) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+  else if (MAXN >= 4 && n >= 4) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else if (MAXN >= 3 && n >= 3) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+  else if (MAXN >= 2 && n >= 2) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  else if (MAXN >= 1 && n >= 1) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+template <int HB>
+__global__ __launch_bounds__(256, 2) void index_score_dec128(
+    const uint8_t* __restrict__ qI, const float* __restrict__ w, const uint8_t* __restrict__ KI,
+    const int* __restrict__ q_pos, int m, int N_c, int CH, int NG, float* __restrict__ scores,
+    uint64_t* __restrict__ gkeys) {
+  constexpr int C_I = 128, NIH = HB * 16, BLKB = GROUP * C_I;
+  static_assert(RING - 1 <= 5, "wait_vm_le covers up to five blocks in flight");
+  __shared__ __attribute__((aligned(16))) uint8_t ring[4][RING][BLKB];
+  __shared__ __attribute__((aligned(16))) uint8_t s_q[NIH * C_I];
+  __shared__ float s_w[cdiv(NIH, 64) * 64];
+  __shared__ float s_sc[SCORE_STAGE];
+  __shared__ uint64_t s_gk[SCORE_STAGE / GROUP];
+  CSAHCA_TRACE(0);
+  CSAHCA_TRACE_RT(14);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int q = blockIdx.y;  // decode: one query token per sequence, b = q
+  const int e_begin = blockIdx.x * CH;
+  const int e_lim = min(e_begin + CH, N_c);
+  const int row = lane & 15, g = lane >> 4;
+  // read before any DMA is issued, so that it can be a scalar load with its own counter
+  const int V = visible_entries(q_pos, q, 0, m, N_c);
+
+  // blocks of this wave: wave + 4k, k < nmine; loads are clamped to the chunk's last key
+  // (the first blocks are issued before the visible count is applied)
+  int nmine = 0, e_last = e_lim - 1;
+  auto count_mine = [&](int nblk) { return nblk > wave ? cdiv(nblk - wave, 4) : 0; };
+  nmine = count_mine(cdiv(e_lim - e_begin, GROUP));
+  const uint8_t* kb = KI + (size_t)q * N_c * C_I;
+  // in each 1 KiB half of a block: lane l moves row l/8, chunk (l%8) ^ (l/8)
+  const int dma_row = lane >> 3, dma_chunk = (lane & 7) ^ (lane >> 3);
+  auto issue = [&](int k) {
+    const int e0 = e_begin + (wave + 4 * min(k, nmine - 1)) * GROUP;
+    uint8_t* dst = ring[wave][k % RING];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int e = min(e0 + 8 * h + dma_row, e_last);
+      __builtin_amdgcn_global_load_lds(kb + (size_t)e * C_I + dma_chunk * 16,
+                                       (__attribute__((address_space(3))) void*)(dst + h * 1024),
+                                       16, 0, 0);
+    }
+  };
+  // The query's indexer vectors and head weights come by DMA too, ahead of the key
+  // blocks: with only DMA in flight, one counted wait covers exactly them.  Wave w moves
+  // the 1 KiB pieces w, w+4, ... of q_I and the 64-weight pieces w, w+4, ... of w.
+  constexpr int QPIECES = NIH * C_I / 1024, WPIECES = cdiv(NIH, 64);
+  int nown = 0;
+  const uint8_t* qsrc = qI + (size_t)q * NIH * C_I;
+  for (int i = wave; i < QPIECES; i += 4, ++nown)
+    __builtin_amdgcn_global_load_lds(qsrc + i * 1024 + lane * 16,
+                                     (__attribute__((address_space(3))) void*)(s_q + i * 1024),
+                                     16, 0, 0);
+  for (int i = wave; i < WPIECES; i += 4, ++nown)
+    __builtin_amdgcn_global_load_lds(w + (size_t)q * NIH + min(i * 64 + lane, NIH - 1),
+                                     (__attribute__((address_space(3))) void*)(s_w + i * 64),
+                                     4, 0, 0);
+  const int nfill = min(RING - 1, nmine);
+  for (int k = 0; k < nfill; ++k) issue(k);
+  CSAHCA_TRACE(1);
+  wait_vm_le<RING - 1>(nfill);  // this wave's q_I / w pieces have landed
+  // ... and every other wave's (a bare barrier: __syncthreads would also drain the ring)
+  asm volatile("s_barrier" ::: "memory");
+  // A operand: indexer query of head (16*hb + row), dims [g*32, g*32 + 32); head weights
+  // of the accumulator rows this lane holds: heads 16*hb + 4*g + i
+  KeyOperand<C_I> a[HB];
+  float wr[HB][4];
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) {
+    const uint8_t* qr = s_q + (hb * 16 + row) * C_I + g * 32;
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(qr);
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(qr + 16);
+    a[hb].v = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wr[hb][i] = s_w[hb * 16 + 4 * g + i];
+  }
+
+  const int e_end = min(e_lim, V);
+  if (e_begin >= e_end) {  // uniform: nothing usable in this chunk
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no DMA may target LDS at exit
+    return;
+  }
+  const int nmine_lim = nmine;
+  nmine = count_mine(cdiv(e_end - e_begin, GROUP));
+  // reader offsets of this lane's 32 bytes (chunks 2g, 2g+1 of row `row`)
+  const int rd0 = (row * 8 + ((2 * g) ^ (row & 7))) * 16;
+  const int rd1 = (row * 8 + ((2 * g + 1) ^ (row & 7))) * 16;
+  for (int k = 0; k < nmine; ++k) {
+    // blocks k+1 .. min(nmine_lim, k+RING-1)-1 may stay in flight
+    wait_vm_le<RING - 2>(min(nmine_lim, k + RING - 1) - 1 - k);
+    const uint8_t* blk = ring[wave][k % RING];
+    KeyOperand<C_I> kf;
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(blk + rd0);
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(blk + rd1);
+    kf.v = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    f32x4 acc[HB];
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) acc[hb] = KeyOperand<C_I>::mma(a[hb], kf, f32x4{0.f, 0.f, 0.f, 0.f});
+    // slot (k-1) % RING was read in the previous iteration: refill it
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (k + RING - 1 < nmine_lim) issue(k + RING - 1);
+    // lane holds key (row) for heads 16*hb + 4*g + i; sum over heads as a balanced tree
+    float t[4 * HB];
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) t[4 * hb + i] = wr[hb][i] * fmaxf(acc[hb][i], 0.f);
+#pragma unroll
+    for (int wdt = 2 * HB; wdt >= 1; wdt /= 2)
+#pragma unroll
+      for (int v = 0; v < wdt; ++v) t[v] += t[v + wdt];
+    const float score = sum_over_row_groups(t[0]);  // same value in lanes row, row+16, ...
+    const int e0 = e_begin + (wave + 4 * k) * GROUP;
+    const bool valid = e0 + row < e_end;
+    if (g == 0 && valid) s_sc[e0 - e_begin + row] = score;
+    // group maximum: the best score of the 16 keys, lowest index among equal scores
+    const float sv = valid ? score : -INFINITY;
+    const float best = row16_max(sv);
+    const uint64_t hit = __ballot(valid && sv == best) & 0xFFFFull;
+    if (lane == 0 && hit != 0ull)
+      s_gk[(e0 - e_begin) / GROUP] = entry_key(best, (uint32_t)(e0 + __builtin_ctzll(hit)));
+    if (k == 0) CSAHCA_TRACE(2);
+  }
+  CSAHCA_TRACE(3);
+  // the loop waited for every block up to nmine - 1; blocks past it (issued before the
+  // visible count was known) are waited for here, before the workgroup barrier
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  const int n = e_end - e_begin;
+  float* srow = scores + (size_t)q * N_c;
+  uint64_t* grow = gkeys + (size_t)q * NG;
+  for (int i = (int)threadIdx.x; i < n; i += 256) srow[e_begin + i] = s_sc[i];
+  for (int i = (int)threadIdx.x; i < cdiv(n, GROUP); i += 256) grow[e_begin / GROUP + i] = s_gk[i];
+  CSAHCA_TRACE(4);
+  CSAHCA_TRACE_RT(15);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -221,13 +400,18 @@ void launch_fp8(const void* q_idx, const float* w_idx, const void* k_idx, const 
   const bool decode = Tq == 1;
   const int QPW = decode ? 1 : 4;
   const int qgroups = cdiv(nq, QPW);
-  // about two workgroups per CU, each streaming a long chunk of keys
+  // about two workgroups per CU, each streaming a long chunk of keys (decode: at most
+  // SCORE_STAGE keys, the LDS staging of its scores)
   int chunks = cdiv(CSAHCA_SCORE_WGS, qgroups);
   chunks = max(1, min(chunks, cdiv(N_c, 256)));
+  if (decode) chunks = max(chunks, cdiv(N_c, SCORE_STAGE));
   const int CH = cdiv(cdiv(N_c, chunks), 64) * 64;
   chunks = cdiv(N_c, CH);
   dim3 grid((unsigned)chunks, (unsigned)qgroups);
-  if (decode)
+  if (decode && C_I == 128)
+    hipLaunchKernelGGL((index_score_dec128<HB>), grid, dim3(256), 0, st, (const uint8_t*)q_idx,
+                       w_idx, (const uint8_t*)k_idx, q_pos, m, N_c, CH, NG, scores, gkeys);
+  else if (decode)
     hipLaunchKernelGGL((index_score_fp8<C_I, HB, 1, 4>), grid, dim3(256), 0, st,
                        (const uint8_t*)q_idx, w_idx, (const uint8_t*)k_idx, q_pos, m, Tq, N_c,
                        CH, nq, NG, scores, gkeys);

@@ -98,9 +98,18 @@ CSAHCA_DEV void wait_tiles(int inflight) {
 // LDS ring depth NS: 2 tiles when many workgroups run (two 4-wave workgroups share a CU
 // and hide each other's latency: prefill), 4 tiles when few queries are split over
 // workgroups (one workgroup per CU keeps three tiles in flight: decode).
-size_t attend_lds_bytes(int NS, int NW, int RS, bool csa) {
+// Column-split workgroups (CS) add an exchange area: P^T operands [TPI][NW][64 lanes]
+// (16 bytes each), the per-head factors alpha [NW][16], one flag per wave, and at the end
+// the running maxima and sums [NW][16] and partial row maxima [NW][NW * 16].
+constexpr size_t xch_bytes(int NW, int TPI) {
+  return (size_t)TPI * NW * 64 * 16 + (size_t)NW * 16 * 4 + 64 + 2 * (size_t)NW * 16 * 4 +
+         (size_t)NW * NW * 16 * 4;
+}
+
+size_t attend_lds_bytes(int NS, int NW, int RS, bool csa, bool cs) {
+  const int TPI = NS >= 4 ? 2 : 1;
   return (size_t)NS * TILE * ROWB + (size_t)NS * NW * sizeof(uint32_t) +
-         (csa ? (size_t)RS * sizeof(int) : 0);
+         (csa ? (size_t)RS * sizeof(int) : 0) + (cs ? xch_bytes(NW, TPI) : 0);
 }
 
 // bits [lo, hi) of a 32-bit mask, the bounds relative to `base` and clipped to [0, 32)
@@ -139,14 +148,24 @@ CSAHCA_DEV uint32_t lds_addr(const uint8_t* p) {
 // accumulators are rarely rescaled.  LDS operands are read in small groups, one group
 // ahead of the MFMAs that use them, which bounds the registers in use so that two
 // workgroups share a CU.
-template <int NW, int NS, bool CSA>
+// CS (column split, NW = 2 or 4, one query per workgroup, one tile per iteration): each
+// wave still computes the scores and softmax of its own 16 heads, but the P^T operands
+// and rescale factors go through LDS, and for O^T += E^T P^T wave w owns the output
+// columns [w*512/NW, (w+1)*512/NW) of all NW head blocks: every E^T fragment it reads
+// from LDS feeds NW MFMAs, so the transpose reads per tile drop by NW.
+template <int NW, int NS, bool CSA, bool CS>
 __global__ __launch_bounds__(NW * 64, (NW == 4 && NS == 2) ? 2 : 1) void attend_bf16(AttnArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   constexpr int LPW = TILE / NW;  // rows each wave loads per tile
   constexpr float LAZY = 8.f;     // log2 headroom before the running maximum moves
+  static_assert(!CS || NW == 2 || NW == 4, "column split: 2 or 4 waves");
+  static_assert(!CS || NS == 2, "column split: one tile per iteration");
   uint8_t* tiles = smem;
   uint32_t* tmask = reinterpret_cast<uint32_t*>(smem + NS * TILE * ROWB);  // [NS][NW]
   int* sidx = reinterpret_cast<int*>(tmask + NS * NW);                     // [RS]
+  // exchange area (CS): after sidx, 16-byte aligned
+  uint8_t* xch = smem + NS * TILE * ROWB + NS * NW * 4 + (CSA ? a.RS * 4 : 0);
+  xch = reinterpret_cast<uint8_t*>((reinterpret_cast<uintptr_t>(xch) + 15) & ~(uintptr_t)15);
 
   // XCD-aware order: consecutive work items (the head groups of one row range first) run
   // on the same XCD, so the rows they share are read from HBM once into that XCD's L2.
@@ -312,6 +331,9 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && NS == 2) ? 2 : 1) void attend_
   for (int tt = TPI; tt < NS && tt < ntile; ++tt) issue(tt, false);
 
   float m_run = -INFINITY, l_run = 0.f;
+  // O^T accumulators: without CS oacc[cb][i] is column 16*cb + 4*g + i of head
+  // h0 + row16; with CS oacc[cbl*NW + hb][i] is column 16*(wave*32/NW + cbl) + 4*g + i of
+  // head hg*HPW + 16*hb + row16
   f32x4 oacc[C / 16];
 #pragma unroll
   for (int cb = 0; cb < C / 16; ++cb) oacc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -386,6 +408,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && NS == 2) ? 2 : 1) void attend_
           r3 = n3;
         }
       }
+      if (it == TPI) CSAHCA_TRACE(12);
       // lane: head h0 + row16; sv[4*rb + i] is slot base + 16*rb + 4g + i (rb 2, 3: tile B)
       constexpr int NSV = 8 * TPI;
       float sv[NSV];
@@ -425,10 +448,6 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && NS == 2) ? 2 : 1) void attend_
       const float psum = sum_over_row_groups(ps[0]);
       l_run = l_run * alpha + psum;
       m_run = m_new;
-      if (__any(bump)) {
-#pragma unroll
-        for (int cb = 0; cb < C / 16; ++cb) oacc[cb] *= alpha;
-      }
       // P^T as B operands: k-slot e <-> slot (e < 4 ? 4g+e : 16+4g+e-4) of its tile
       const bf16x8 pfA = __builtin_bit_cast(bf16x8, u32x4{pack_bf16x2(pe[0], pe[1]), pack_bf16x2(pe[2], pe[3]),
                                                           pack_bf16x2(pe[4], pe[5]), pack_bf16x2(pe[6], pe[7])});
@@ -443,17 +462,61 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && NS == 2) ? 2 : 1) void attend_
       // 4-element rows addressed by lanes i/4, i/4+4, i/4+8, i/4+12.  Lane j addresses row
       // (4g + j/4) at column 16*cb + 4*(j%4), so lane i gets column 16*cb + i of rows
       // 4g .. 4g+3 (and 16+4g .. 16+4g+3 with the second read): exactly its A operand.
+      if (it == TPI) CSAHCA_TRACE(13);
       const uint32_t aA = lds_addr(tA + t_off), aB = lds_addr(tB + t_off);
-      if constexpr (TPI == 2) {
-        asm volatile(CSAHCA_PV_ASM_2TILE
-                     : PV_ACC_OPERANDS
-                     : "v"(pfA), "v"(pfB), "v"(aA), "v"(aB)
-                     : CSAHCA_PV_CLOBBERS, "memory");
+      if constexpr (!CS) {
+        if (__any(bump)) {
+#pragma unroll
+          for (int cb = 0; cb < C / 16; ++cb) oacc[cb] *= alpha;
+        }
+        if constexpr (TPI == 2) {
+          asm volatile(CSAHCA_PV_ASM_2TILE
+                       : PV_ACC_OPERANDS
+                       : "v"(pfA), "v"(pfB), "v"(aA), "v"(aB)
+                       : CSAHCA_PV_CLOBBERS, "memory");
+        } else {
+          asm volatile(CSAHCA_PV_ASM_1TILE
+                       : PV_ACC_OPERANDS
+                       : "v"(pfA), "v"(aA)
+                       : CSAHCA_PV_CLOBBERS, "memory");
+        }
       } else {
-        asm volatile(CSAHCA_PV_ASM_1TILE
-                     : PV_ACC_OPERANDS
-                     : "v"(pfA), "v"(aA)
-                     : CSAHCA_PV_CLOBBERS, "memory");
+        // exchange: this wave's P^T operands, rescale factors and rescale flag, then every
+        // wave's (the barrier also orders the previous iteration's reads before the writes)
+        u32x4* xp = reinterpret_cast<u32x4*>(xch);                   // [TPI][NW][64]
+        float* xa = reinterpret_cast<float*>(xch + TPI * NW * 1024);  // [NW][16]
+        uint32_t* xf = reinterpret_cast<uint32_t*>(xa + NW * 16);     // [NW]
+        xp[wave * 64 + lane] = __builtin_bit_cast(u32x4, pfA);
+        if (TPI == 2) xp[(NW + wave) * 64 + lane] = __builtin_bit_cast(u32x4, pfB);
+        if (g == 0) xa[wave * 16 + row16] = alpha;
+        const uint32_t any_bump = __any(bump) ? 1u : 0u;
+        if (lane == 0) xf[wave] = any_bump;
+        lds_reads_done_barrier();
+        u32x4 px[NW][TPI];
+#pragma unroll
+        for (int hb = 0; hb < NW; ++hb) {
+#pragma unroll
+          for (int tt = 0; tt < TPI; ++tt) px[hb][tt] = xp[(tt * NW + hb) * 64 + lane];
+          if (__builtin_amdgcn_readfirstlane(xf[hb])) {
+            const float al = xa[hb * 16 + row16];
+#pragma unroll
+            for (int cbl = 0; cbl < C / 16 / NW; ++cbl) oacc[cbl * NW + hb] *= al;
+          }
+        }
+        if (it == TPI) CSAHCA_TRACE(6);
+        const uint32_t cofs = (uint32_t)wave * (C / 16 / NW) * 32;  // the wave's first column block
+        const uint32_t cA = aA + cofs;
+        if constexpr (NW == 4) {
+          asm volatile(CSAHCA_PVC_ASM_4W_1T
+                       : PV_ACC_OPERANDS
+                       : "v"(px[0][0]), "v"(px[1 % NW][0]), "v"(px[2 % NW][0]), "v"(px[3 % NW][0]), "v"(cA)
+                       : CSAHCA_PV_CLOBBERS, "memory");
+        } else {
+          asm volatile(CSAHCA_PVC_ASM_2W_1T
+                       : PV_ACC_OPERANDS
+                       : "v"(px[0][0]), "v"(px[1 % NW][0]), "v"(cA)
+                       : CSAHCA_PV_CLOBBERS, "memory");
+        }
       }
     }
     lds_reads_done_barrier();  // the consumed stages are free for the next issue
@@ -461,6 +524,71 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && NS == 2) ? 2 : 1) void attend_
     for (int tt = it + NS; tt < it + NS + TPI && tt < ntile; ++tt) issue(tt, false);
   }
   CSAHCA_TRACE(4);
+  if constexpr (CS) {  // one query per workgroup: every wave is active
+    constexpr int CPW = C / 16 / NW;   // column blocks per wave
+    constexpr int EROWB = C * 2 + 16;  // staging row stride in bytes
+    float* xm = reinterpret_cast<float*>(xch + TPI * NW * 1024 + NW * 16 * 4 + 64);  // [NW][16]
+    float* xl = xm + NW * 16;                                                       // [NW][16]
+    float* xam = xl + NW * 16;  // [NW][NW*16]: |O| maxima over a wave's columns, per head
+    if (g == 0) {
+      xm[wave * 16 + row16] = m_run;
+      xl[wave * 16 + row16] = l_run;
+    }
+#pragma unroll
+    for (int hb = 0; hb < NW; ++hb) {
+      float pam = 0.f;
+#pragma unroll
+      for (int cbl = 0; cbl < CPW; ++cbl) {
+        const f32x4 o = oacc[cbl * NW + hb];
+        pam = fmaxf(pam, fmaxf(fmaxf(fabsf(o[0]), fabsf(o[1])), fmaxf(fabsf(o[2]), fabsf(o[3]))));
+      }
+      pam = max_over_row_groups(pam);
+      if (g == 0) xam[wave * NW * 16 + hb * 16 + row16] = pam;
+    }
+    lds_reads_done_barrier();
+    // every head block's values of this wave's columns, as 16-bit rows [head][column]
+#pragma unroll
+    for (int hb = 0; hb < NW; ++hb) {
+      const float lh = xl[hb * 16 + row16], mh = xm[hb * 16 + row16];
+      const float inv = lh > 0.f ? 1.f / lh : 0.f;
+      float f = inv;
+      const bool as_f16 = a.n_splits > 1;
+      if (as_f16) {  // partial O / l scaled by 2^-e per row (see the merge)
+        float amax = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) amax = fmaxf(amax, xam[w * NW * 16 + hb * 16 + row16]);
+        amax *= inv;
+        const uint32_t ex = min(max((__float_as_uint(amax) >> 23) & 0xFFu, 1u), 253u);
+        f = inv * __uint_as_float((254u - ex) << 23);
+        if (hb == wave && g == 0) {
+          const long long pr = (qrow * a.n_splits + split) * a.n_h + h0 + row16;
+          *reinterpret_cast<f32x4*>(a.mlpart + pr * 4) = f32x4{mh, lh, __uint_as_float(ex << 23), 0.f};
+        }
+      } else if (hb == wave && a.lse && g == 0) {
+        a.lse[qrow * a.n_h + h0 + row16] = lh > 0.f ? (mh + __log2f(lh)) * LN2 : -INFINITY;
+      }
+      uint8_t* srow = tiles + (hb * 16 + row16) * EROWB;
+#pragma unroll
+      for (int cbl = 0; cbl < CPW; ++cbl) {
+        const f32x4 o = oacc[cbl * NW + hb];
+        const int cb = wave * CPW + cbl;
+        *reinterpret_cast<u32x2*>(srow + (16 * cb + 4 * g) * 2) =
+            as_f16 ? u32x2{pack_f16x2(o[0] * f, o[1] * f), pack_f16x2(o[2] * f, o[3] * f)}
+                   : u32x2{pack_bf16x2(o[0] * f, o[1] * f), pack_bf16x2(o[2] * f, o[3] * f)};
+      }
+    }
+    lds_reads_done_barrier();
+    // this wave's own head block: 16 whole rows, one 1 KiB store each
+    uint16_t* dst = a.n_splits == 1 ? a.out + (qrow * a.n_h + h0) * C
+                                    : a.opart + ((qrow * a.n_splits + split) * a.n_h + h0) * C;
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr)
+      *reinterpret_cast<u32x4*>(dst + rr * C + lane * 8) =
+          *reinterpret_cast<const u32x4*>(tiles + (wave * 16 + rr) * EROWB + lane * 16);
+    CSAHCA_TRACE(5);
+    CSAHCA_TRACE_RT(15);
+    return;
+  }
   if (!active) return;
 
   // lane: head h0 + row16; oacc[cb][i] is column 16*cb + 4*g + i.  The wave's 16 output
@@ -691,6 +819,7 @@ __global__ __launch_bounds__(256) void attend_f32(AttnF32Args a) {
 // ---------------------------------------------------------------------------------------
 struct Plan {
   int Tg, HPW, NW, NS, n_hg, n_slots, n_splits, RS, nqg, n_work, per_xcd;
+  bool CS;  // column-split PV (one query per workgroup, 2 or 4 waves)
   size_t opart_bytes, ml_bytes, ws, lds;
 };
 
@@ -725,31 +854,37 @@ Plan make_plan(int B, int Tq, int n_h, int n_slots_c, int W, bool csa) {
   P.opart_bytes = P.n_splits > 1 ? csahca::align_up((size_t)(nqh * P.n_splits * C * 2), 256) : 0;
   P.ml_bytes = P.n_splits > 1 ? csahca::align_up((size_t)(nqh * P.n_splits * 4 * 4), 256) : 0;
   P.ws = P.opart_bytes + P.ml_bytes;
-  P.lds = attend_lds_bytes(P.NS, P.NW, P.RS, csa);
+  // column split only with the 2-tile ring (many workgroups, one tile per iteration):
+  // with two tiles per iteration the exchange costs what the fewer transpose reads save
+  P.CS = P.Tg == 1 && (P.NW == 2 || P.NW == 4) && P.NS == 2;
+  P.lds = attend_lds_bytes(P.NS, P.NW, P.RS, csa, P.CS);
   return P;
 }
 
-template <int NW, int NS, bool CSA>
+template <int NW, int NS, bool CSA, bool CS>
 int launch_attend(const Plan& P, const AttnArgs& A, hipStream_t st) {
   static bool attr_set = false;
   if (!attr_set) {
-    if (hipFuncSetAttribute((const void*)attend_bf16<NW, NS, CSA>,
+    if (hipFuncSetAttribute((const void*)attend_bf16<NW, NS, CSA, CS>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 1024) != hipSuccess)
       return csahca::fail(CSAHCA_ELAUNCH, "attend: cannot raise the LDS limit");
     attr_set = true;
   }
-  hipLaunchKernelGGL((attend_bf16<NW, NS, CSA>), dim3((unsigned)(P.per_xcd * 8)), dim3(NW * 64),
-                     P.lds, st, A);
+  hipLaunchKernelGGL((attend_bf16<NW, NS, CSA, CS>), dim3((unsigned)(P.per_xcd * 8)),
+                     dim3(NW * 64), P.lds, st, A);
   return CSAHCA_OK;
 }
 
 template <bool CSA>
 int launch_attend_nw(const Plan& P, const AttnArgs& A, hipStream_t st) {
   switch (P.NW) {
-    case 1: return launch_attend<1, 2, CSA>(P, A, st);
-    case 2: return launch_attend<2, 2, CSA>(P, A, st);
-    case 4: return P.NS == 4 ? launch_attend<4, 4, CSA>(P, A, st) : launch_attend<4, 2, CSA>(P, A, st);
-    case 8: return launch_attend<8, 2, CSA>(P, A, st);
+    case 1: return launch_attend<1, 2, CSA, false>(P, A, st);
+    case 2:
+      return P.CS ? launch_attend<2, 2, CSA, true>(P, A, st) : launch_attend<2, 2, CSA, false>(P, A, st);
+    case 4:
+      if (P.CS) return launch_attend<4, 2, CSA, true>(P, A, st);
+      return P.NS == 4 ? launch_attend<4, 4, CSA, false>(P, A, st) : launch_attend<4, 2, CSA, false>(P, A, st);
+    case 8: return launch_attend<8, 2, CSA, false>(P, A, st);
     default: return csahca::fail(CSAHCA_ENOTSUP, "attend: unsupported wave count");
   }
 }

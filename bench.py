@@ -239,7 +239,7 @@ def read_traffic(kernel_name):
 
 COPY_BYTES = 1 << 30
 COPY_KERNEL = "neg"  # name part of torch's elementwise negation kernel
-TRAFFIC_KERNELS = {"index_score_fp8": "index_score_fp8"}
+TRAFFIC_KERNELS = {"index_score_dec128": "index_score_dec128"}  # decode scoring kernel
 
 
 def _counter_means(folder, counter, name_part):
@@ -434,9 +434,10 @@ def main():
         dur = e0.elapsed_time(e1) / 1e3 / (rounds * reps)
         kb = wl.index_score_bytes()
         ach = kb / dur / 1e9
-        roofline = {"kernel": "index_score_fp8", "bound": "hbm", "achieved": round(ach, 1),
+        kname = "index_score_dec128" if decode and cfg.c_I == 128 else "index_score_fp8"
+        roofline = {"kernel": kname, "bound": "hbm", "achieved": round(ach, 1),
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
-                    "traffic": read_traffic("index_score_fp8" + ("" if decode else "_prefill")),
+                    "traffic": read_traffic(kname) if decode else None,
                     "avg_launch_us": round(dur * 1e6, 2), "bytes_per_launch": kb}
 
     cpu = None

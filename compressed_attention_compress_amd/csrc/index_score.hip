@@ -354,6 +354,145 @@ __global__ __launch_bounds__(256, 2) void index_score_dec128(
 }
 
 // ---------------------------------------------------------------------------------------
+// scoring at prefill, c_I = 128: four queries per workgroup share key stages in LDS
+// ---------------------------------------------------------------------------------------
+// Wave w scores query 4*blockIdx.x + w (same sequence) over a range of PRE_KEYS keys.  Key
+// stages of PRE_STG keys (four 16-key blocks, 8 KiB) arrive by row DMA into a ring of
+// PRE_NSTG stages that all four waves read, so every key byte crosses the memory path once
+// per four queries; one barrier per stage hands a slot back for refill.  Per stage a wave
+// runs the 4 x HB MFMAs, reduces each lane's 4*HB accumulators over its heads, and then
+// one reduce-scatter over the four row groups (two permlane16 swaps, one permlane32 swap)
+// leaves every lane with the complete score of one key: lane l holds key 64*stage + l, so
+// a stage's 64 scores leave in one coalesced store.  The waits on the row DMA count only
+// the DMA issued after the awaited stage: as vector loads complete in order among
+// themselves, that bound holds whatever the order in which the stores complete.
+constexpr int PRE_STG = 64;
+constexpr int PRE_NSTG = 4;
+constexpr int PRE_KEYS = 8192;
+
+template <int HB>
+__global__ __launch_bounds__(256, HB >= 8 ? 2 : 4) void index_score_pre128(
+    const uint8_t* __restrict__ qI, const float* __restrict__ w, const uint8_t* __restrict__ KI,
+    const int* __restrict__ q_pos, int m, int Tq, int N_c, int NG, float* __restrict__ scores,
+    uint64_t* __restrict__ gkeys) {
+  constexpr int C_I = 128, NIH = HB * 16, STGB = PRE_STG * C_I, NBS = PRE_STG / GROUP;
+  static_assert(NBS == 4, "the reduce-scatter spreads four blocks over the four row groups");
+  static_assert(PRE_NSTG - 2 <= 5, "wait_vm_le covers up to five stages in flight");
+  __shared__ __attribute__((aligned(16))) uint8_t ring[PRE_NSTG][STGB];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int row = lane & 15, g = lane >> 4;
+  const int qgs = cdiv(Tq, 4);  // query groups per sequence
+  const int b = blockIdx.x / qgs;
+  const int t0 = (blockIdx.x - b * qgs) * 4;
+  const int tl = min(t0 + 3, Tq - 1);       // the workgroup's last query
+  const int t = min(t0 + wave, tl);         // waves past Tq repeat it and store nothing
+  const bool qact = t0 + wave < Tq;
+  const int q = b * Tq + t;
+  const int e_begin = blockIdx.y * PRE_KEYS;
+  // read before any DMA is issued, so that they can be scalar loads with their own counter
+  const int Vmax = visible_entries(q_pos, b, tl, m, N_c);
+  const int Vw = qact ? visible_entries(q_pos, b, t, m, N_c) : 0;
+  if (e_begin >= Vmax) return;  // uniform over the workgroup, before any barrier
+  const int nst = cdiv(min(e_begin + PRE_KEYS, Vmax) - e_begin, PRE_STG);
+
+  // A operand: indexer query of head (16*hb + row), dims [g*32, g*32 + 32); head weights
+  // of the accumulator rows this lane holds: heads 16*hb + 4*g + i
+  KeyOperand<C_I> a[HB];
+  f32x4 wr[HB];
+  const uint8_t* qp = qI + (size_t)q * NIH * C_I;
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) {
+    a[hb].load(qp + (hb * 16 + row) * C_I + g * 32);
+    wr[hb] = *reinterpret_cast<const f32x4*>(w + (size_t)q * NIH + hb * 16 + 4 * g);
+  }
+
+  // stage s: rows e_begin + 64*s + r; wave w moves the 1 KiB pieces w and w + 4 (rows
+  // 8p .. 8p+7); in a piece lane l moves row l/8, 16-byte chunk (l%8) ^ (l/8), so that a
+  // reader of 32 bytes of its row hits eight distinct bank groups per eight lanes
+  const uint8_t* kb = KI + (size_t)b * N_c * C_I;
+  const int dma_row = lane >> 3, dma_chunk = (lane & 7) ^ (lane >> 3);
+  auto issue = [&](int st) {
+    uint8_t* dst = ring[st % PRE_NSTG];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int p = wave + 4 * h;
+      const int e = min(e_begin + st * PRE_STG + 8 * p + dma_row, N_c - 1);
+      __builtin_amdgcn_global_load_lds(kb + (size_t)e * C_I + dma_chunk * 16,
+                                       (__attribute__((address_space(3))) void*)(dst + p * 1024),
+                                       16, 0, 0);
+    }
+  };
+  const int nfill = min(PRE_NSTG - 1, nst);
+  for (int st = 0; st < nfill; ++st) issue(st);
+  // the compiler does not order register loads and row DMAs: its wait for the query and
+  // weights (forced here, once) also covers the first stages, which are needed next anyway
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) asm volatile("" : "+v"(a[hb].v), "+v"(wr[hb]));
+
+  float* srow = scores + (size_t)q * N_c;
+  uint64_t* grow = gkeys + (size_t)q * NG;
+  // reader offsets of this lane's 32 bytes (chunks 2g, 2g+1 of row `row` of a block)
+  const int rd0 = (row * 8 + ((2 * g) ^ (row & 7))) * 16;
+  const int rd1 = (row * 8 + ((2 * g + 1) ^ (row & 7))) * 16;
+  for (int st = 0; st < nst; ++st) {
+    // stages st+1 .. min(nst, st+NSTG-1)-1 may stay in flight
+    wait_vm_le<PRE_NSTG - 2>(min(nst - 1, st + PRE_NSTG - 2) - st);
+    // every wave's part of stage st has landed, and every wave is done with stage st-1
+    asm volatile("s_barrier" ::: "memory");
+    if (st + PRE_NSTG - 1 < nst) issue(st + PRE_NSTG - 1);
+    const uint8_t* stg = ring[st % PRE_NSTG];
+    KeyOperand<C_I> kf[NBS];
+#pragma unroll
+    for (int u = 0; u < NBS; ++u) {
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(stg + u * (GROUP * C_I) + rd0);
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(stg + u * (GROUP * C_I) + rd1);
+      kf[u].v = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    }
+    f32x4 acc[NBS][HB];
+#pragma unroll
+    for (int u = 0; u < NBS; ++u)
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) acc[u][hb] = KeyOperand<C_I>::mma(a[hb], kf[u], f32x4{0.f, 0.f, 0.f, 0.f});
+    // this lane's heads (16*hb + 4*g + i) of key `row` of block u
+    float pu[NBS];
+#pragma unroll
+    for (int u = 0; u < NBS; ++u) {
+      float th[HB];
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) {
+        float x = wr[hb][0] * fmaxf(acc[u][hb][0], 0.f);
+#pragma unroll
+        for (int i = 1; i < 4; ++i) x = fmaf(wr[hb][i], fmaxf(acc[u][hb][i], 0.f), x);
+        th[hb] = x;
+      }
+#pragma unroll
+      for (int wdt = HB / 2; wdt >= 1; wdt /= 2)
+#pragma unroll
+        for (int v = 0; v < wdt; ++v) th[v] += th[v + wdt];
+      pu[u] = th[0];
+    }
+    // reduce-scatter over the row groups: afterwards row group r holds block r
+    const auto x01 = __builtin_amdgcn_permlane16_swap(__float_as_uint(pu[0]), __float_as_uint(pu[1]), false, false);
+    const auto x23 = __builtin_amdgcn_permlane16_swap(__float_as_uint(pu[2]), __float_as_uint(pu[3]), false, false);
+    const float s01 = __uint_as_float(x01[0]) + __uint_as_float(x01[1]);
+    const float s23 = __uint_as_float(x23[0]) + __uint_as_float(x23[1]);
+    const auto y = __builtin_amdgcn_permlane32_swap(__float_as_uint(s01), __float_as_uint(s23), false, false);
+    const float score = __uint_as_float(y[0]) + __uint_as_float(y[1]);
+    const int e = e_begin + st * PRE_STG + lane;
+    const bool valid = e < Vw;
+    if (valid) srow[e] = score;
+    // group maximum of each row group's 16 keys, lowest index among equal scores
+    const float sv = valid ? score : -INFINITY;
+    const float best = row16_max(sv);
+    const uint64_t hit = __ballot(valid && sv == best);
+    const uint32_t hr = (uint32_t)(hit >> (lane & 48)) & 0xFFFFu;
+    if (row == 0 && hr != 0u) grow[e / GROUP] = entry_key(best, (uint32_t)(e + __builtin_ctz(hr)));
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no DMA may target LDS at exit
+}
+
+// ---------------------------------------------------------------------------------------
 // scoring, float32 keys (small heads; plain FMA)
 // ---------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void index_score_f32(
@@ -415,6 +554,10 @@ void launch_fp8(const void* q_idx, const float* w_idx, const void* k_idx, const 
     hipLaunchKernelGGL((index_score_fp8<C_I, HB, 1, 4>), grid, dim3(256), 0, st,
                        (const uint8_t*)q_idx, w_idx, (const uint8_t*)k_idx, q_pos, m, Tq, N_c,
                        CH, nq, NG, scores, gkeys);
+  else if (C_I == 128)
+    hipLaunchKernelGGL((index_score_pre128<HB>),
+                       dim3((unsigned)(nq / Tq * cdiv(Tq, 4)), (unsigned)cdiv(N_c, PRE_KEYS)), dim3(256), 0, st,
+                       (const uint8_t*)q_idx, w_idx, (const uint8_t*)k_idx, q_pos, m, Tq, N_c, NG, scores, gkeys);
   else
     hipLaunchKernelGGL((index_score_fp8<C_I, HB, 4, 4>), grid, dim3(256), 0, st,
                        (const uint8_t*)q_idx, w_idx, (const uint8_t*)k_idx, q_pos, m, Tq, N_c,

@@ -409,17 +409,30 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && NS == 2) ? 2 : 1) void attend_
         }
       }
       if (it == TPI) CSAHCA_TRACE(12);
-      // lane: head h0 + row16; sv[4*rb + i] is slot base + 16*rb + 4g + i (rb 2, 3: tile B)
+      // lane: head h0 + row16; sv[4*rb + i] is slot base + 16*rb + 4g + i (rb 2, 3: tile B):
+      // the raw score q.k, -inf where the slot is masked (no masking when every slot of
+      // the iteration is usable, the common case)
       constexpr int NSV = 8 * TPI;
       float sv[NSV];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = 4 * g + i;
-        sv[i] = ((vmA >> r) & 1u) ? s0[i] * a.scale_log2 : -INFINITY;
-        sv[4 + i] = ((vmA >> (16 + r)) & 1u) ? s1[i] * a.scale_log2 : -INFINITY;
+        sv[i] = s0[i];
+        sv[4 + i] = s1[i];
         if (TPI == 2) {
-          sv[(8 + i) % NSV] = ((vmB >> r) & 1u) ? s2[i] * a.scale_log2 : -INFINITY;
-          sv[(12 + i) % NSV] = ((vmB >> (16 + r)) & 1u) ? s3[i] * a.scale_log2 : -INFINITY;
+          sv[(8 + i) % NSV] = s2[i];
+          sv[(12 + i) % NSV] = s3[i];
+        }
+      }
+      if ((vmA & (TPI == 2 ? vmB : ~0u)) != ~0u) {  // wave-uniform
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * g + i;
+          sv[i] = ((vmA >> r) & 1u) ? sv[i] : -INFINITY;
+          sv[4 + i] = ((vmA >> (16 + r)) & 1u) ? sv[4 + i] : -INFINITY;
+          if (TPI == 2) {
+            sv[(8 + i) % NSV] = ((vmB >> r) & 1u) ? sv[(8 + i) % NSV] : -INFINITY;
+            sv[(12 + i) % NSV] = ((vmB >> (16 + r)) & 1u) ? sv[(12 + i) % NSV] : -INFINITY;
+          }
         }
       }
       float mx[NSV / 2];
@@ -429,15 +442,18 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && NS == 2) ? 2 : 1) void attend_
       for (int w = NSV / 4; w >= 1; w >>= 1)
 #pragma unroll
         for (int e = 0; e < w; ++e) mx[e] = fmaxf(mx[e], mx[e + w]);
-      const float mloc = max_over_row_groups(mx[0]);
+      // in log2 units (the scale is positive, so the maximum commutes with it)
+      const float mloc = max_over_row_groups(mx[0]) * a.scale_log2;
       // lazy running maximum: move it only when exceeded by more than LAZY
       const bool bump = mloc > m_run + LAZY;
       const float m_new = bump ? mloc : m_run;
-      const float alpha = bump ? exp2f(m_run - m_new) : 1.f;
-      const bool none = m_new == -INFINITY;
+      // hardware exp2: results below 2^-126 flush to zero, negligible next to the running
+      // sum, which is at least 1 (it holds the term of the score that set the maximum)
+      const float alpha = bump ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;  // nothing usable yet: all -inf
       float pe[NSV];
 #pragma unroll
-      for (int e = 0; e < NSV; ++e) pe[e] = none ? 0.f : exp2f(sv[e] - m_new);  // skipped: 0
+      for (int e = 0; e < NSV; ++e) pe[e] = __builtin_amdgcn_exp2f(fmaf(sv[e], a.scale_log2, -m_use));
       float ps[NSV / 2];
 #pragma unroll
       for (int e = 0; e < NSV / 2; ++e) ps[e] = pe[e] + pe[e + NSV / 2];

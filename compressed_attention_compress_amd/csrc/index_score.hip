@@ -11,9 +11,9 @@
 // one key row straight from HBM into the B operand (no LDS); A takes the same bytes of
 // the indexer query row, so whatever order the instruction assigns to the contraction
 // dimension, it is the same for both operands and the dot products are exact.  ReLU, the
-// head weights and the cross-head sum are applied to the MFMA accumulators in registers.  Every score is
-// written once (fp32) and every group of 16 consecutive keys also writes its maximum
-// 64-bit selection key.
+// head weights and the cross-head sum are applied to the MFMA accumulators in registers.
+// Every score is written once (fp32) and every group of 16 consecutive keys also writes
+// the order-preserving 32-bit key of its maximum score.
 #include "indexer.hpp"
 
 namespace {
@@ -78,7 +78,7 @@ template <int C_I, int HB, int QPW, int PF>
 __global__ __launch_bounds__(256) void index_score_fp8(
     const uint8_t* __restrict__ qI, const float* __restrict__ w, const uint8_t* __restrict__ KI,
     const int* __restrict__ q_pos, int m, int Tq, int N_c, int CH, int nq, int NG,
-    float* __restrict__ scores, uint64_t* __restrict__ gkeys) {
+    float* __restrict__ scores, uint32_t* __restrict__ gkeys) {
   constexpr int NIH = HB * 16;
   constexpr int WPQ = 4 / QPW;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -108,7 +108,7 @@ __global__ __launch_bounds__(256) void index_score_fp8(
 
   const uint8_t* kb = KI + (size_t)b * N_c * C_I + g * (C_I / 4);
   float* srow = scores + (size_t)q * N_c;
-  uint64_t* grow = gkeys + (size_t)q * NG;
+  uint32_t* grow = gkeys + (size_t)q * NG;
   auto count_mine = [&](int nblk) { return nblk > sub ? cdiv(nblk - sub, WPQ) : 0; };
   auto blk_of = [&](int k) { return sub + k * WPQ; };  // blocks sub, sub+WPQ, ...
   int nmine = count_mine(cdiv(e_lim - e_begin, GROUP));
@@ -137,7 +137,7 @@ __global__ __launch_bounds__(256) void index_score_fp8(
   // with loads, so a store inside the loop would make every later wait for a key block a
   // wait for all of them.
   __shared__ float s_sc[QPW == 1 ? SCORE_STAGE : 1];
-  __shared__ uint64_t s_gk[QPW == 1 ? SCORE_STAGE / GROUP : 1];
+  __shared__ uint32_t s_gk[QPW == 1 ? SCORE_STAGE / GROUP : 1];
   auto score_blocks = [&](KeyOperand<C_I>(&kf)[PF], int k0) {
     f32x4 acc[PF][HB];
 #pragma unroll
@@ -170,14 +170,11 @@ __global__ __launch_bounds__(256) void index_score_fp8(
         if (QPW == 1) s_sc[e - e_begin] = score;
         else srow[e] = score;
       }
-      // group maximum: the best score of the 16 keys, lowest index among equal scores
-      const float sv = valid ? score : -INFINITY;
-      const float best = row16_max(sv);
-      const uint64_t hit = __ballot(valid && sv == best) & 0xFFFFull;
-      if (lane == 0 && hit != 0ull) {
-        const uint64_t key = entry_key(best, (uint32_t)(e0 + __builtin_ctzll(hit)));
-        if (QPW == 1) s_gk[(e0 - e_begin) / GROUP] = key;
-        else grow[e0 / GROUP] = key;
+      // group maximum over the group's usable keys (a prefix of its 16)
+      const float best = row16_max(valid ? score : -INFINITY);
+      if (lane == 0 && valid) {
+        if (QPW == 1) s_gk[(e0 - e_begin) / GROUP] = score_key(best);
+        else grow[e0 / GROUP] = score_key(best);
       }
     }
   };
@@ -221,14 +218,14 @@ template <int HB>
 __global__ __launch_bounds__(256, 2) void index_score_dec128(
     const uint8_t* __restrict__ qI, const float* __restrict__ w, const uint8_t* __restrict__ KI,
     const int* __restrict__ q_pos, int m, int N_c, int CH, int NG, float* __restrict__ scores,
-    uint64_t* __restrict__ gkeys) {
+    uint32_t* __restrict__ gkeys) {
   constexpr int C_I = 128, NIH = HB * 16, BLKB = GROUP * C_I;
   static_assert(RING - 1 <= 5, "wait_vm_le covers up to five blocks in flight");
   __shared__ __attribute__((aligned(16))) uint8_t ring[4][RING][BLKB];
   __shared__ __attribute__((aligned(16))) uint8_t s_q[NIH * C_I];
   __shared__ float s_w[cdiv(NIH, 64) * 64];
   __shared__ float s_sc[SCORE_STAGE];
-  __shared__ uint64_t s_gk[SCORE_STAGE / GROUP];
+  __shared__ uint32_t s_gk[SCORE_STAGE / GROUP];
   CSAHCA_TRACE(0);
   CSAHCA_TRACE_RT(14);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -331,12 +328,9 @@ __global__ __launch_bounds__(256, 2) void index_score_dec128(
     const int e0 = e_begin + (wave + 4 * k) * GROUP;
     const bool valid = e0 + row < e_end;
     if (g == 0 && valid) s_sc[e0 - e_begin + row] = score;
-    // group maximum: the best score of the 16 keys, lowest index among equal scores
-    const float sv = valid ? score : -INFINITY;
-    const float best = row16_max(sv);
-    const uint64_t hit = __ballot(valid && sv == best) & 0xFFFFull;
-    if (lane == 0 && hit != 0ull)
-      s_gk[(e0 - e_begin) / GROUP] = entry_key(best, (uint32_t)(e0 + __builtin_ctzll(hit)));
+    // group maximum over the group's usable keys (a prefix of its 16)
+    const float best = row16_max(valid ? score : -INFINITY);
+    if (lane == 0 && valid) s_gk[(e0 - e_begin) / GROUP] = score_key(best);
     if (k == 0) CSAHCA_TRACE(2);
   }
   CSAHCA_TRACE(3);
@@ -346,7 +340,7 @@ __global__ __launch_bounds__(256, 2) void index_score_dec128(
   __syncthreads();
   const int n = e_end - e_begin;
   float* srow = scores + (size_t)q * N_c;
-  uint64_t* grow = gkeys + (size_t)q * NG;
+  uint32_t* grow = gkeys + (size_t)q * NG;
   for (int i = (int)threadIdx.x; i < n; i += 256) srow[e_begin + i] = s_sc[i];
   for (int i = (int)threadIdx.x; i < cdiv(n, GROUP); i += 256) grow[e_begin / GROUP + i] = s_gk[i];
   CSAHCA_TRACE(4);
@@ -374,7 +368,7 @@ template <int HB>
 __global__ __launch_bounds__(256, HB >= 8 ? 2 : 4) void index_score_pre128(
     const uint8_t* __restrict__ qI, const float* __restrict__ w, const uint8_t* __restrict__ KI,
     const int* __restrict__ q_pos, int m, int Tq, int N_c, int NG, float* __restrict__ scores,
-    uint64_t* __restrict__ gkeys) {
+    uint32_t* __restrict__ gkeys) {
   constexpr int C_I = 128, NIH = HB * 16, STGB = PRE_STG * C_I, NBS = PRE_STG / GROUP;
   static_assert(NBS == 4, "the reduce-scatter spreads four blocks over the four row groups");
   static_assert(PRE_NSTG - 2 <= 5, "wait_vm_le covers up to five stages in flight");
@@ -431,7 +425,7 @@ __global__ __launch_bounds__(256, HB >= 8 ? 2 : 4) void index_score_pre128(
   for (int hb = 0; hb < HB; ++hb) asm volatile("" : "+v"(a[hb].v), "+v"(wr[hb]));
 
   float* srow = scores + (size_t)q * N_c;
-  uint64_t* grow = gkeys + (size_t)q * NG;
+  uint32_t* grow = gkeys + (size_t)q * NG;
   // reader offsets of this lane's 32 bytes (chunks 2g, 2g+1 of row `row` of a block)
   const int rd0 = (row * 8 + ((2 * g) ^ (row & 7))) * 16;
   const int rd1 = (row * 8 + ((2 * g + 1) ^ (row & 7))) * 16;
@@ -482,12 +476,9 @@ __global__ __launch_bounds__(256, HB >= 8 ? 2 : 4) void index_score_pre128(
     const int e = e_begin + st * PRE_STG + lane;
     const bool valid = e < Vw;
     if (valid) srow[e] = score;
-    // group maximum of each row group's 16 keys, lowest index among equal scores
-    const float sv = valid ? score : -INFINITY;
-    const float best = row16_max(sv);
-    const uint64_t hit = __ballot(valid && sv == best);
-    const uint32_t hr = (uint32_t)(hit >> (lane & 48)) & 0xFFFFu;
-    if (row == 0 && hr != 0u) grow[e / GROUP] = entry_key(best, (uint32_t)(e + __builtin_ctz(hr)));
+    // group maximum of each row group's usable keys (a prefix of its 16)
+    const float best = row16_max(valid ? score : -INFINITY);
+    if (row == 0 && valid) grow[e / GROUP] = score_key(best);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no DMA may target LDS at exit
 }
@@ -498,7 +489,7 @@ __global__ __launch_bounds__(256, HB >= 8 ? 2 : 4) void index_score_pre128(
 __global__ __launch_bounds__(256) void index_score_f32(
     const float* __restrict__ qI, const float* __restrict__ w, const float* __restrict__ KI,
     const int* __restrict__ q_pos, int m, int Tq, int N_c, int n_ih, int c_I, int NG,
-    float* __restrict__ scores, uint64_t* __restrict__ gkeys) {
+    float* __restrict__ scores, uint32_t* __restrict__ gkeys) {
   extern __shared__ float smem_f[];
   float* qs = smem_f;               // [n_ih * c_I]
   float* ws = smem_f + n_ih * c_I;  // [n_ih]
@@ -520,11 +511,9 @@ __global__ __launch_bounds__(256) void index_score_f32(
     }
     scores[(size_t)q * N_c + e] = s;
   }
-  uint64_t key = valid ? entry_key(s, (uint32_t)e) : 0ull;
-  key = umax64(key, shfl_xor_u64(key, 1));
-  key = umax64(key, shfl_xor_u64(key, 2));
-  key = umax64(key, shfl_xor_u64(key, 4));
-  key = umax64(key, shfl_xor_u64(key, 8));
+  uint32_t key = valid ? score_key(s) : 0u;
+#pragma unroll
+  for (int d = 1; d < 16; d <<= 1) key = max(key, (uint32_t)__shfl_xor((int)key, d, 64));
   if ((threadIdx.x & 15) == 0 && e < V) gkeys[(size_t)q * NG + e / GROUP] = key;
 }
 
@@ -534,7 +523,7 @@ __global__ __launch_bounds__(256) void index_score_f32(
 // ---------------------------------------------------------------------------------------
 template <int C_I, int HB>
 void launch_fp8(const void* q_idx, const float* w_idx, const void* k_idx, const int* q_pos,
-                int m, int Tq, int N_c, int nq, int NG, float* scores, uint64_t* gkeys,
+                int m, int Tq, int N_c, int nq, int NG, float* scores, uint32_t* gkeys,
                 hipStream_t st) {
   const bool decode = Tq == 1;
   const int QPW = decode ? 1 : 4;
@@ -567,7 +556,7 @@ void launch_fp8(const void* q_idx, const float* w_idx, const void* k_idx, const 
 template <int C_I>
 bool launch_fp8_heads(int n_ih, const void* q_idx, const float* w_idx, const void* k_idx,
                       const int* q_pos, int m, int Tq, int N_c, int nq, int NG, float* scores,
-                      uint64_t* gkeys, hipStream_t st) {
+                      uint32_t* gkeys, hipStream_t st) {
   switch (n_ih / 16) {
     case 1: launch_fp8<C_I, 1>(q_idx, w_idx, k_idx, q_pos, m, Tq, N_c, nq, NG, scores, gkeys, st); return true;
     case 2: launch_fp8<C_I, 2>(q_idx, w_idx, k_idx, q_pos, m, Tq, N_c, nq, NG, scores, gkeys, st); return true;
@@ -610,7 +599,7 @@ int index_check_common(const void* q_idx, const float* w_idx, const void* k_idx,
 
 int index_score_impl(const void* q_idx, const float* w_idx, const void* k_idx, int idx_dtype,
                      const int* q_pos, int m, int B, int Tq, int n_ih, int c_I, int N_c,
-                     float* scores, uint64_t* gkeys, hipStream_t st) {
+                     float* scores, uint32_t* gkeys, hipStream_t st) {
   using namespace csahca;
   const int nq = B * Tq;
   const int NG = cdiv(N_c, GROUP);
@@ -643,5 +632,5 @@ extern "C" int lightning_index_score(const void* q_idx, const float* w_idx, cons
   if (!workspace || ws_bytes < L.total)
     return fail(CSAHCA_EWORKSPACE, "lightning_index_score: workspace missing or too small");
   return index_score_impl(q_idx, w_idx, k_idx, idx_dtype, q_pos, m, B, Tq, n_ih, c_I, N_c, scores,
-                          (uint64_t*)((char*)workspace + L.gkeys_off), (hipStream_t)stream);
+                          (uint32_t*)((char*)workspace + L.gkeys_off), (hipStream_t)stream);
 }

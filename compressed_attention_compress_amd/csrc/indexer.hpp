@@ -24,7 +24,7 @@ CSAHCA_DEV int visible_entries(const int* q_pos, int b, int t, int m, int N_c) {
   return (int)(v < N_c ? v : N_c);
 }
 
-// Workspace: the 64-bit maximum selection key of every group of GROUP entries, then the
+// Workspace: the maximum score key (score_key) of every group of GROUP entries, then the
 // fp32 scores (used when the caller passes no all_scores buffer).
 struct WsLayout {
   size_t gkeys_off, gkeys_bytes, scores_off, scores_bytes, total;
@@ -34,7 +34,7 @@ inline WsLayout ws_layout(long long nq, int N_c) {
   WsLayout L;
   const long long NG = cdiv<long long>(N_c, GROUP);
   L.gkeys_off = 0;
-  L.gkeys_bytes = align_up((size_t)(nq * NG * 8), 256);
+  L.gkeys_bytes = align_up((size_t)(nq * NG * 4), 256);
   L.scores_off = L.gkeys_bytes;
   L.scores_bytes = align_up((size_t)(nq * (long long)N_c * 4), 256);
   L.total = L.scores_off + L.scores_bytes;
@@ -48,10 +48,10 @@ int index_check_common(const void* q_idx, const float* w_idx, const void* k_idx,
 // enqueue the scoring kernel: scores [B*Tq, N_c] and group maxima [B*Tq, ceil(N_c/16)]
 int index_score_impl(const void* q_idx, const float* w_idx, const void* k_idx, int idx_dtype,
                      const int* q_pos, int m, int B, int Tq, int n_ih, int c_I, int N_c,
-                     float* scores, uint64_t* gkeys, hipStream_t st);
+                     float* scores, uint32_t* gkeys, hipStream_t st);
 
 // enqueue the selection kernel over scores and group maxima written by index_score_impl
-int index_select_impl(const float* scores, const uint64_t* gkeys, const int* q_pos, int m,
+int index_select_impl(const float* scores, const uint32_t* gkeys, const int* q_pos, int m,
                       int B, int Tq, int N_c, int k, int* topk_idx, float* topk_score,
                       hipStream_t st);
 

@@ -6,12 +6,15 @@
 //
 // Selection: one workgroup per query.  Selection keys are
 // (order-preserving score bits << 32) | (~index), so all keys are distinct and "larger
-// key" means "better, lower index on ties".  Let T1 be the K-th largest group maximum.
-// At least K keys are >= T1 (one per selected group), so the K-th largest key overall is
-// >= T1 and every top-K key lies in one of exactly K selected groups.  The exact top-K is
-// then taken from those K*16 candidates.  Both K-th-largest searches are MSB-first radix
-// selects over register-resident keys (an LDS histogram per 11-bit digit) that skip the
-// bits all remaining candidates share.  The candidates are kept in index order, so the
+// key" means "better, lower index on ties".  A group of 16 entries is keyed by its maximum
+// score, then by the lower group index (groups are index ranges, so this orders equal
+// maxima as their best entries are ordered).  Let T1 be the K-th largest group key and s1
+// its score.  The K selected groups hold K entries whose keys beat every entry of an
+// unselected group, so every top-K entry lies in a selected group and scores at least s1.
+// The exact top-K is then taken from the entries of those K groups that score >= s1.
+// Both K-th-largest searches are MSB-first radix selects over register-resident keys (an
+// LDS histogram per 11-bit digit) that skip the bits all remaining candidates share and
+// rank the last few candidates directly.  The candidates are kept in index order, so the
 // output comes out ascending without a sort.
 #include "indexer.hpp"
 
@@ -22,7 +25,9 @@ using namespace csahca;
 // ---------------------------------------------------------------------------------------
 // selection
 // ---------------------------------------------------------------------------------------
-constexpr int NBIN = 2048;  // radix digit of 11 bits
+constexpr int DBITS = 11;                // radix digit
+constexpr int NBIN = 1 << DBITS;
+constexpr int BPT = NBIN / SEL_THREADS;  // digits each thread scans
 constexpr int NWAVE = SEL_THREADS / 64;
 
 struct SelScratch {
@@ -43,7 +48,9 @@ struct SelScratch {
 // keys differ; from there MSB-first radix passes of 11 bits narrow the candidates.  A
 // pass builds an LDS histogram of the digit, then every wave scans 128 digits (two per
 // lane, in descending order) and the lane whose range holds the K-th key reports the
-// digit.  The search stops as soon as that digit holds a single candidate.
+// digit.  The search stops as soon as that digit holds a single candidate.  (All 1024
+// threads run on one CU, so every phase costs its instruction count times 16 cycles:
+// a second pass is cheaper than gathering and ranking even a hundred keys.)
 CSAHCA_DEV uint64_t radix_select_kth(const uint64_t (&kr)[KPT], int kth, SelScratch& sc) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint32_t alo = ~0u, ahi = ~0u, olo = 0u, ohi = 0u;
@@ -85,7 +92,7 @@ CSAHCA_DEV uint64_t radix_select_kth(const uint64_t (&kr)[KPT], int kth, SelScra
   CSAHCA_TRACE(tslot);
   bool tfirst = true;
 #endif
-  for (int sh = hb >= 10 ? hb - 10 : 0;; sh = sh >= 11 ? sh - 11 : 0) {
+  for (int sh = hb >= DBITS - 1 ? hb - (DBITS - 1) : 0;; sh = sh >= DBITS ? sh - DBITS : 0) {
     uint32_t* h = sc.hist[buf];
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
@@ -98,24 +105,29 @@ CSAHCA_DEV uint64_t radix_select_kth(const uint64_t (&kr)[KPT], int kth, SelScra
     if (threadIdx.x == 0 && blockIdx.x < 8192 && tfirst)
       csahca_trace[blockIdx.x * 16 + tslot + 1] = __builtin_amdgcn_s_memtime();
 #endif
-    // this lane's two digits, descending with the thread index
-    const int d_hi = NBIN - 1 - 2 * (int)threadIdx.x;
-    const uint32_t c_hi = h[d_hi], c_lo = h[d_hi - 1];
-    const uint32_t incl = wave_incl_scan(c_hi + c_lo);
+    // this lane's BPT digits, descending with the thread index
+    const int d_hi = NBIN - 1 - BPT * (int)threadIdx.x;
+    uint32_t c[BPT], csum = 0;
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) {
+      c[i] = h[d_hi - i];
+      csum += c[i];
+    }
+    const uint32_t incl = wave_incl_scan(csum);
     if (lane == 63) sc.scan[wave] = incl;
     __syncthreads();
-    uint32_t above = incl - (c_hi + c_lo);
+    uint32_t above = incl - csum;
 #pragma unroll
     for (int i = 0; i < NWAVE; ++i) above += i < wave ? sc.scan[i] : 0u;
     const uint32_t kk = (uint32_t)kth;
-    if (above < kk && kk <= above + c_hi) {
-      sc.found_digit = d_hi;
-      sc.found_kth = kk - above;
-      sc.found_count = c_hi;
-    } else if (above + c_hi < kk && kk <= above + c_hi + c_lo) {
-      sc.found_digit = d_hi - 1;
-      sc.found_kth = kk - above - c_hi;
-      sc.found_count = c_lo;
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) {
+      if (above < kk && kk <= above + c[i]) {
+        sc.found_digit = d_hi - i;
+        sc.found_kth = kk - above;
+        sc.found_count = c[i];
+      }
+      above += c[i];
     }
     __syncthreads();
 #ifdef CSAHCA_TRACE_ENABLED
@@ -145,7 +157,7 @@ CSAHCA_DEV uint64_t radix_select_kth(const uint64_t (&kr)[KPT], int kth, SelScra
 }
 
 __global__ __launch_bounds__(SEL_THREADS) void select_topk(
-    const float* __restrict__ scores, const uint64_t* __restrict__ gkeys,
+    const float* __restrict__ scores, const uint32_t* __restrict__ gmax,
     const int* __restrict__ q_pos, int m, int Tq, int N_c, int NG, int k,
     int* __restrict__ topk_idx, float* __restrict__ topk_score) {
   __shared__ SelScratch sc;
@@ -157,13 +169,15 @@ __global__ __launch_bounds__(SEL_THREADS) void select_topk(
   const int q = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   // group maxima, coalesced: thread t holds groups j*SEL_THREADS + t (j < KPT); issued
-  // before the visible count is known, masked afterwards
-  const uint64_t* grow = gkeys + (size_t)q * NG;
+  // before the visible count is known, masked afterwards.  A group's key is its maximum
+  // score key, then the lower group index: as groups are index ranges, that orders equal
+  // maxima as their best entries are ordered.
+  const uint32_t* grow = gmax + (size_t)q * NG;
   uint64_t kr[KPT];
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     const int gi = j * SEL_THREADS + (int)threadIdx.x;
-    kr[j] = gi < NG ? grow[gi] : 0ull;
+    kr[j] = gi < NG ? ((uint64_t)grow[gi] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)gi) : 0ull;
   }
   const int b = q / Tq, t = q - b * Tq;
   const int V = visible_entries(q_pos, b, t, m, N_c);
@@ -185,6 +199,8 @@ __global__ __launch_bounds__(SEL_THREADS) void select_topk(
     if (j * SEL_THREADS + (int)threadIdx.x >= ng) kr[j] = 0ull;  // not (yet) complete groups
   // With fewer groups than K every group is a candidate (T1 = 0 keeps every usable key).
   const uint64_t T1 = keff < ng ? radix_select_kth(kr, keff, sc) : 0ull;
+  // entries scoring below the T1 group's maximum cannot be among the top K
+  const uint64_t T1s = T1 & 0xFFFFFFFF00000000ull;
   CSAHCA_TRACE(1);
 
   // exactly min(K, ng) groups have a maximum >= T1; list them in index order, which is
@@ -228,19 +244,20 @@ __global__ __launch_bounds__(SEL_THREADS) void select_topk(
   }
   CSAHCA_TRACE(2);
   // candidates, coalesced: 16 lanes read the 16 scores of one listed group; key j of lane
-  // (wave, lane) is element lane%16 of listed group wave*64 + j*4 + lane/16
+  // (wave, lane) is element lane%16 of listed group wave*64 + j*4 + lane/16.  Every load
+  // is issued (clamped to valid memory) before any is used, so they overlap.
+  int ce[KPT];
+  float cv[KPT];
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     const int gp = wave * 64 + j * 4 + (lane >> 4);
-    uint64_t key = 0ull;
-    if (gp < (int)ngl) {
-      const int e = glist[gp] * GROUP + (lane & 15);
-      if (e < V) {
-        key = entry_key(srow[e], (uint32_t)e);
-        key = key >= T1 ? key : 0ull;
-      }
-    }
-    kr[j] = key;
+    ce[j] = gp < (int)ngl ? glist[gp] * GROUP + (lane & 15) : V;
+    cv[j] = srow[min(ce[j], N_c - 1)];
+  }
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const uint64_t key = ce[j] < V ? entry_key(cv[j], (uint32_t)ce[j]) : 0ull;
+    kr[j] = key >= T1s ? key : 0ull;
   }
   const uint64_t T2 = radix_select_kth(kr, keff, sc);
   CSAHCA_TRACE(3);
@@ -281,13 +298,13 @@ __global__ __launch_bounds__(SEL_THREADS) void select_topk(
 
 namespace csahca {
 
-int index_select_impl(const float* scores, const uint64_t* gkeys, const int* q_pos, int m, int B,
+int index_select_impl(const float* scores, const uint32_t* gmax, const int* q_pos, int m, int B,
                       int Tq, int N_c, int k, int* topk_idx, float* topk_score, hipStream_t st) {
   using namespace csahca;
   const int nq = B * Tq;
   const int NG = cdiv(N_c, GROUP);
   hipLaunchKernelGGL(select_topk, dim3((unsigned)nq), dim3(SEL_THREADS), 0, st, scores,
-                     gkeys, q_pos, m, Tq, N_c, NG, k, topk_idx, topk_score);
+                     gmax, q_pos, m, Tq, N_c, NG, k, topk_idx, topk_score);
   return launch_status("lightning_index_select");
 }
 
@@ -313,7 +330,7 @@ extern "C" int lightning_index_select(const float* scores, const int* q_pos, int
   const WsLayout L = ws_layout((long long)B * Tq, N_c);
   if (!workspace || ws_bytes < L.total)
     return fail(CSAHCA_EWORKSPACE, "lightning_index_select: workspace missing or too small");
-  return index_select_impl(scores, (const uint64_t*)((char*)workspace + L.gkeys_off), q_pos, m, B, Tq,
+  return index_select_impl(scores, (const uint32_t*)((char*)workspace + L.gkeys_off), q_pos, m, B, Tq,
                      N_c, k, topk_idx, topk_score, (hipStream_t)stream);
 }
 
@@ -332,7 +349,7 @@ extern "C" int lightning_index_topk(const void* q_idx, const float* w_idx, const
   if (all_scores && !aligned16(all_scores))
     return fail(CSAHCA_EINVAL, "lightning_index_topk: all_scores must be 16-byte aligned");
   float* scores = all_scores ? all_scores : (float*)((char*)workspace + L.scores_off);
-  uint64_t* gkeys = (uint64_t*)((char*)workspace + L.gkeys_off);
+  uint32_t* gkeys = (uint32_t*)((char*)workspace + L.gkeys_off);
   hipStream_t s = (hipStream_t)stream;
   st = index_score_impl(q_idx, w_idx, k_idx, idx_dtype, q_pos, m, B, Tq, n_ih, c_I, N_c, scores, gkeys, s);
   if (st != CSAHCA_OK) return st;

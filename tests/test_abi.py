@@ -59,7 +59,8 @@ def test_indexer_validation():
     B, Tq, n_ih, c_I, N_c, k = 2, 1, 64, 128, 1000, 64
     ws = L.lightning_index_topk_workspace_size(B, Tq, n_ih, N_c, k)
     NG = -(-N_c // 16)
-    assert ws == (-(-(B * NG * 8) // 256) * 256) + (-(-(B * N_c * 4) // 256) * 256)
+    # one 32-bit maximum key per group of 16 entries, then the fp32 scores
+    assert ws == (-(-(B * NG * 4) // 256) * 256) + (-(-(B * N_c * 4) // 256) * 256)
     args = [FAKE, FAKE, FAKE, 2, FAKE, 4, B, Tq, n_ih, c_I, N_c, k, FAKE, None, None]
     assert L.lightning_index_topk(*args, FAKE, ws - 1, None) == EWORKSPACE
     assert L.lightning_index_topk(*args, None, ws, None) == EWORKSPACE

@@ -841,8 +841,8 @@ struct Plan {
 
 // Launch shape.  A workgroup holds up to 64 heads (4 waves; 8 waves when two prefill
 // queries share the rows).  When the queries alone give fewer than 256 workgroups their
-// rows are split over more (one per CU, each keeping three tiles in flight), but never
-// below 96 rows per split: each split writes a partial of HPW x 512 float16 values.
+// rows are split over more (one per CU, each keeping three tiles in flight), each split
+// holding whole iterations (64 rows with the 4-tile ring).
 Plan make_plan(int B, int Tq, int n_h, int n_slots_c, int W, bool csa) {
   Plan P;
   P.Tg = 1;
@@ -856,13 +856,13 @@ Plan make_plan(int B, int Tq, int n_h, int n_slots_c, int W, bool csa) {
   P.nqg = cdiv(Tq, P.Tg);
   const long long base = (long long)P.n_hg * B * P.nqg;
   P.NS = (P.NW == 4 && base < 256) ? 4 : 2;
-  const int ntile = cdiv(P.n_slots, TILE);
-  const int min_tiles = 3;
+  // splits hold whole iterations (TPI tiles), at least one each
+  const int tpi = P.NS >= 4 ? 2 : 1;
+  const int niter = cdiv(cdiv(P.n_slots, TILE), tpi);
   const long long want = cdiv<long long>(256, base);
-  const int maxs = ntile / min_tiles > 1 ? ntile / min_tiles : 1;
-  int ns = (int)(want < maxs ? want : maxs);
+  int ns = (int)(want < niter ? want : niter);
   if (ns < 1) ns = 1;
-  P.RS = cdiv(ntile, ns) * TILE;
+  P.RS = cdiv(niter, ns) * tpi * TILE;
   P.n_splits = cdiv(P.n_slots, P.RS);
   P.n_work = (int)(base * P.n_splits);
   P.per_xcd = cdiv(P.n_work, 8);

@@ -202,16 +202,25 @@ __global__ __launch_bounds__(256) void index_score_fp8(
 // private to a wave, so there is no barrier until the final write-out.  Inside a block,
 // row r holds its 16-byte chunks in the order c ^ (r & 7): a lane reading 32 bytes of its
 // key row then hits eight distinct bank groups per eight lanes.
-constexpr int RING = 6;
+#ifndef CSAHCA_SCORE_RING
+#define CSAHCA_SCORE_RING 6  // key blocks per wave ring (RING - 1 in flight)
+#endif
+constexpr int RING = CSAHCA_SCORE_RING;
 
+// s_waitcnt vmcnt(2 * min(n, MAXN)): n blocks (two row loads each) may stay in flight
+template <int N>
+CSAHCA_DEV void wait_vm_exact() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * N) : "memory");
+}
 template <int MAXN>
-CSAHCA_DEV void wait_vm_le(int n) {  // s_waitcnt vmcnt(2 * min(n, MAXN)): n blocks may stay
-  if (MAXN >= 5 && n >= 5) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
-  else if (MAXN >= 4 && n >= 4) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-  else if (MAXN >= 3 && n >= 3) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
-  else if (MAXN >= 2 && n >= 2) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-  else if (MAXN >= 1 && n >= 1) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+CSAHCA_DEV void wait_vm_le(int n) {
+  static_assert(MAXN >= 0 && 2 * MAXN <= 63, "vmcnt holds at most 63");
+  if constexpr (MAXN == 0) {
+    wait_vm_exact<0>();
+  } else {
+    if (n >= MAXN) wait_vm_exact<MAXN>();
+    else wait_vm_le<MAXN - 1>(n);
+  }
 }
 
 template <int HB>
@@ -220,7 +229,6 @@ __global__ __launch_bounds__(256, 2) void index_score_dec128(
     const int* __restrict__ q_pos, int m, int N_c, int CH, int NG, float* __restrict__ scores,
     uint32_t* __restrict__ gkeys) {
   constexpr int C_I = 128, NIH = HB * 16, BLKB = GROUP * C_I;
-  static_assert(RING - 1 <= 5, "wait_vm_le covers up to five blocks in flight");
   __shared__ __attribute__((aligned(16))) uint8_t ring[4][RING][BLKB];
   __shared__ __attribute__((aligned(16))) uint8_t s_q[NIH * C_I];
   __shared__ float s_w[cdiv(NIH, 64) * 64];
@@ -371,7 +379,6 @@ __global__ __launch_bounds__(256, HB >= 8 ? 2 : 4) void index_score_pre128(
     uint32_t* __restrict__ gkeys) {
   constexpr int C_I = 128, NIH = HB * 16, STGB = PRE_STG * C_I, NBS = PRE_STG / GROUP;
   static_assert(NBS == 4, "the reduce-scatter spreads four blocks over the four row groups");
-  static_assert(PRE_NSTG - 2 <= 5, "wait_vm_le covers up to five stages in flight");
   __shared__ __attribute__((aligned(16))) uint8_t ring[PRE_NSTG][STGB];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;

@@ -88,6 +88,7 @@ def check_attend_queries(wl, layer, queries):
     got = np.stack(gots)
     rms = math.sqrt(float(np.mean(ref * ref)))
     err = float(np.max(np.abs(got - ref)))
+    print(f"{layer}: max |d| = {err:.3g}, {err / (2e-2 * rms):.3f} of the tolerance", flush=True)
     assert err <= 2e-2 * rms, f"{layer}: max |d| {err} vs RMS {rms}"
 
 

@@ -103,6 +103,46 @@ def pool(X, Z, m, P=None):
     return out
 
 
+def pool_overlap(Xa, Za, Xb, Zb, m, P=None, prev=0):
+    """Compressed entries of one sequence, the overlapped two-stream CSA form.
+
+    [P2] V.1, equation C_i^comp: CSA projects two KV streams (a, b) with their own
+    compression scores; entry i is the channel-wise weighted sum of stream a over block i
+    and stream b over block i-1 (2m raw entries, so a block boundary is covered twice),
+    the weights being the softmax pooling weights over the scores plus a positional
+    bias.
+
+    Readings (the pages give the sum, not the normalisation): one joint softmax per
+    channel over the 2m logits [Za of block i + P[0:m]; Zb of block i-1 + P[m:2m]]; for
+    the first block of a sequence there is no block i-1 and the softmax runs over stream
+    a's m logits alone.  `prev` = 1 says that the arrays start one block before the first
+    entry to emit (a cache append reads blocks i-1 and i): entry e then pools stream a
+    block e+1 and stream b block e, and n//m - 1 entries are returned.
+
+    Xa, Za, Xb, Zb: float arrays [n, c] (decoded).  P: [2m, c] or None.
+    Returns [n // m - prev, c] fp64.
+    """
+    Xa, Za, Xb, Zb = (np.asarray(a, dtype=np.float64) for a in (Xa, Za, Xb, Zb))
+    n, c = Xa.shape
+    N = n // m
+    Pa = np.zeros((m, c)) if P is None else np.asarray(P, dtype=np.float64)[:m]
+    Pb = np.zeros((m, c)) if P is None else np.asarray(P, dtype=np.float64)[m:2 * m]
+    out = np.empty((max(N - prev, 0), c))
+    for e in range(N - prev):
+        i = e + prev                                 # block of stream a
+        logits = [Za[m * i:m * i + m] + Pa]
+        values = [Xa[m * i:m * i + m]]
+        if i >= 1:                                   # stream b over block i-1
+            logits.append(Zb[m * (i - 1):m * i] + Pb)
+            values.append(Xb[m * (i - 1):m * i])
+        z = np.concatenate(logits, axis=0)           # [m or 2m, c]
+        x = np.concatenate(values, axis=0)
+        w = np.exp(z - z.max(axis=0, keepdims=True))
+        S = w / w.sum(axis=0, keepdims=True)         # softmax over the tokens, per channel
+        out[e] = (S * x).sum(axis=0)
+    return out
+
+
 # ----------------------------------------------------------------------------------------
 # visibility and window
 # ----------------------------------------------------------------------------------------

@@ -17,7 +17,8 @@ from tests.conftest import read_golden
 
 
 def _impl(**over):
-    ns = types.SimpleNamespace(pool=O.pool, index_scores=O.index_scores, topk=O.topk,
+    ns = types.SimpleNamespace(pool=O.pool, pool_overlap=O.pool_overlap,
+                               index_scores=O.index_scores, topk=O.topk,
                                attend=O.attend, visible=O.visible, csa_rows=O.csa_rows,
                                hca_rows=O.hca_rows, entry_counts=O.entry_counts,
                                window_positions=O.window_positions)
@@ -131,6 +132,49 @@ def check_pool_closed_forms(o):
     np.testing.assert_allclose(o.pool(Xp, np.zeros_like(Xp), 3, P), want, atol=1e-13)
     # ragged tail: 26 tokens with m = 4 -> 6 entries, the last 2 tokens dropped
     assert o.pool(np.vstack([X, X[:2]]), np.vstack([Z, Z[:2]]), 4).shape == (6, c)
+
+
+def check_pool_overlap_closed_forms(o):
+    """Overlapped two-stream pooling ([P2] V.1): entry i pools stream a over block i and
+    stream b over block i-1 with one softmax over the 2m logits (m for the first block)."""
+    rng = np.random.default_rng(11)
+    m, c, N = 4, 3, 6
+    n = m * N
+    Xa, Xb = rng.normal(size=(n, c)), rng.normal(size=(n, c))
+    Za, Zb = rng.normal(size=(n, c)) * 2, rng.normal(size=(n, c)) * 2
+    # every one of an entry's 2m raw values equal to v_i -> v_i, for any gate
+    v = rng.normal(size=(N, c))
+    Xa_i = np.repeat(v, m, axis=0)
+    Xb_i = np.repeat(np.vstack([v[1:], v[-1:]]), m, axis=0)  # block i-1 of b carries v_i
+    np.testing.assert_allclose(o.pool_overlap(Xa_i, Za, Xb_i, Zb, m), v, rtol=0, atol=1e-14)
+    # equal logits -> the mean of the 2m values (of stream a's m values for entry 0)
+    Zc = np.zeros((n, c))
+    want = [Xa[:m].mean(0)] + [np.vstack([Xa[m * i:m * i + m], Xb[m * i - m:m * i]]).mean(0)
+                               for i in range(1, N)]
+    np.testing.assert_allclose(o.pool_overlap(Xa, Zc, Xb, Zc, m), np.array(want), atol=1e-14)
+    # stream b gated off -> the single-stream pool of stream a
+    off = np.full((n, c), -1e300)
+    np.testing.assert_allclose(o.pool_overlap(Xa, Za, Xb, off, m), o.pool(Xa, Za, m), atol=1e-14)
+    # stream a gated off -> entry i >= 1 is stream b's pool of block i-1
+    np.testing.assert_allclose(o.pool_overlap(Xa, off, Xb, Zb, m)[1:], o.pool(Xb, Zb, m)[:N - 1],
+                               atol=1e-14)
+    # m = 1: a two-token softmax, the weight of stream a is the logistic of za_i - zb_{i-1}
+    s = 1.0 / (1.0 + np.exp(-(Za[1:] - Zb[:-1])))
+    got = o.pool_overlap(Xa, Za, Xb, Zb, 1)
+    np.testing.assert_allclose(got[1:], s * Xa[1:] + (1 - s) * Xb[:-1], atol=1e-13)
+    np.testing.assert_allclose(got[0], Xa[0], atol=0)
+    # positional bias alone: rows 0..m-1 weigh stream a's positions, m..2m-1 stream b's
+    P = rng.normal(size=(2 * m, c))
+    wts = np.exp(P) / np.exp(P).sum(0)
+    i = 3
+    want = (wts[:m] * Xa[m * i:m * i + m]).sum(0) + (wts[m:] * Xb[m * i - m:m * i]).sum(0)
+    np.testing.assert_allclose(o.pool_overlap(Xa, Zc, Xb, Zc, m, P)[i], want, atol=1e-13)
+    # an append (prev = 1) over blocks i-1 and i emits entry i alone
+    sl = slice(m * (i - 1), m * (i + 1))
+    np.testing.assert_allclose(o.pool_overlap(Xa[sl], Za[sl], Xb[sl], Zb[sl], m, prev=1)[0],
+                               o.pool_overlap(Xa, Za, Xb, Zb, m)[i], atol=1e-14)
+    # ragged tail: whole blocks only
+    assert o.pool_overlap(Xa[:n - 1], Za[:n - 1], Xb[:n - 1], Zb[:n - 1], m).shape == (N - 1, c)
 
 
 def check_indexer_closed_forms(o):
@@ -259,7 +303,8 @@ def check_rows_and_visibility(o):
 
 
 ALL_CHECKS = [check_budget_counts, check_worked_example, check_pool_counts, check_budget_toy,
-              check_pooling_recall, check_pool_closed_forms, check_indexer_closed_forms,
+              check_pooling_recall, check_pool_closed_forms, check_pool_overlap_closed_forms,
+              check_indexer_closed_forms,
               check_topk_brute, check_attend_textbook, check_rows_and_visibility]
 
 
@@ -343,6 +388,33 @@ def _pool_ceil(X, Z, m, P=None):
     return _ORIG_POOL(Xp, Zp, m, P)                      # emits the partial tail block
 
 
+_ORIG_POOL_OVERLAP = O.pool_overlap
+
+
+def _overlap_same_block(Xa, Za, Xb, Zb, m, P=None, prev=0):
+    # stream b taken over block i instead of block i-1
+    Xb2 = np.vstack([np.asarray(Xb, float)[m:], np.zeros((m, np.shape(Xb)[1]))])
+    Zb2 = np.vstack([np.asarray(Zb, float)[m:], np.zeros((m, np.shape(Zb)[1]))])
+    return _ORIG_POOL_OVERLAP(Xa, Za, Xb2, Zb2, m, P, prev)
+
+
+def _overlap_two_softmaxes(Xa, Za, Xb, Zb, m, P=None, prev=0):
+    # each stream normalised on its own, then summed
+    a = O.pool(Xa, Za, m, None if P is None else np.asarray(P)[:m])
+    b = O.pool(Xb, Zb, m, None if P is None else np.asarray(P)[m:])
+    out = a.copy()
+    out[1:] += b[:-1]
+    return out[prev:]
+
+
+def _overlap_zero_block_before_first(Xa, Za, Xb, Zb, m, P=None, prev=0):
+    # the missing block -1 treated as zero values with zero logits
+    z = np.zeros((m, np.shape(Xa)[1]))
+    out = _ORIG_POOL_OVERLAP(np.vstack([z, Xa]), np.vstack([z, Za]), np.vstack([z, Xb]),
+                             np.vstack([z, Zb]), m, P, prev)
+    return out[1:]
+
+
 def _scores_no_relu(qI, w, KI, V):
     return (np.asarray(KI, float)[:V] @ np.asarray(qI, float).T) @ np.asarray(w, float)
 
@@ -386,6 +458,9 @@ def _counts_ceil(n, m, m_hca, k, W):
 MUTANTS = {
     "pool_softmax_over_channels": dict(pool=_pool_wrong_axis),
     "pool_emits_tail": dict(pool=_pool_ceil),
+    "overlap_stream_b_same_block": dict(pool_overlap=_overlap_same_block),
+    "overlap_two_softmaxes": dict(pool_overlap=_overlap_two_softmaxes),
+    "overlap_zero_block_before_first": dict(pool_overlap=_overlap_zero_block_before_first),
     "indexer_without_relu": dict(index_scores=_scores_no_relu),
     "topk_higher_index_wins": dict(topk=_topk_high_index_wins),
     "attend_without_scale": dict(attend=_attend_no_scale),

@@ -23,6 +23,7 @@ _SZ = ctypes.c_size_t
 _SIGNATURES = {
     "csa_compress": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _LL, _LL, _P]),
     "hca_compress": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _LL, _LL, _P]),
+    "csa_compress_overlap": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _LL, _LL, _P]),
     "lightning_index_topk_workspace_size": (_SZ, [_I, _I, _I, _I, _I]),
     "lightning_index_topk": (_I, [_P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P,
                                   _P, _SZ, _P]),
@@ -106,6 +107,13 @@ def hca_compress(kv, gate, pos_bias, out, B, n, c, m, dtype, in_bstride, out_bst
     return _check("hca_compress", load().hca_compress(
         _ptr(kv), _ptr(gate), _ptr(pos_bias), _ptr(out), B, n, c, m, dtype, in_bstride,
         out_bstride, _stream(stream)))
+
+
+def csa_compress_overlap(kv_a, gate_a, kv_b, gate_b, pos_bias, out, B, n, c, m, prev, dtype,
+                         in_bstride, out_bstride, stream=None):
+    return _check("csa_compress_overlap", load().csa_compress_overlap(
+        _ptr(kv_a), _ptr(gate_a), _ptr(kv_b), _ptr(gate_b), _ptr(pos_bias), _ptr(out), B, n, c,
+        m, prev, dtype, in_bstride, out_bstride, _stream(stream)))
 
 
 def lightning_index_topk_workspace_size(B, Tq, n_ih, N_c, k):

@@ -10,6 +10,10 @@
 // tokens with an online (running-max) softmax, so that X and Z are each read exactly
 // once.  Consecutive threads own consecutive 8-channel slices of the same token row, so
 // one wave reads a contiguous 64 x 16 B = 1 KiB row segment per token (bf16).
+//
+// Overlapped two-stream form (csa_compress_overlap, section V.1's equation with two KV
+// streams): entry i walks stream a over block i and then stream b over block i-1 with
+// the same running softmax, which is one joint softmax over the 2m logits.
 #include "common.hpp"
 
 namespace {
@@ -116,12 +120,14 @@ CSAHCA_DEV void pool_run(const T* __restrict__ xp, const T* __restrict__ zp,
   }
 }
 
-template <typename T, int UB, bool HAS_P>
+template <typename T, int UB, bool HAS_P, bool OV>
 __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ X,
                                                    const T* __restrict__ Z,
+                                                   const T* __restrict__ Xb,
+                                                   const T* __restrict__ Zb,
                                                    const float* __restrict__ P,
                                                    T* __restrict__ out, int N, int c, int m,
-                                                   long long in_bs, long long out_bs,
+                                                   int prev, long long in_bs, long long out_bs,
                                                    long long total) {
   const long long item = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (item >= total) return;
@@ -138,7 +144,8 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ X,
     i = (int)(rest % N);
     b = (int)(rest / N);
   }
-  const long long base = (long long)b * in_bs + (long long)i * m * c + (long long)cv * VEC;
+  const int blk = OV ? i + prev : i;  // block of X (stream a)
+  const long long base = (long long)b * in_bs + (long long)blk * m * c + (long long)cv * VEC;
   float mx[VEC], sum[VEC], acc[VEC];
 #pragma unroll
   for (int e = 0; e < VEC; ++e) {
@@ -147,6 +154,9 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ X,
     acc[e] = 0.f;
   }
   pool_run<T, UB, HAS_P>(X + base, Z + base, HAS_P ? P + cv * VEC : nullptr, c, 0, m, mx, sum, acc);
+  if (OV && blk >= 1)  // stream b over the previous block, bias rows m .. 2m-1
+    pool_run<T, UB, HAS_P>(Xb + base - (long long)m * c, Zb + base - (long long)m * c,
+                           HAS_P ? P + (long long)m * c + cv * VEC : nullptr, c, 0, m, mx, sum, acc);
   float res[VEC];
 #pragma unroll
   for (int e = 0; e < VEC; ++e) res[e] = acc[e] / sum[e];
@@ -165,22 +175,28 @@ CSAHCA_DEV void store_one<uint16_t>(uint16_t* p, float v) { *p = f32_to_bf16(v);
 template <>
 CSAHCA_DEV void store_one<float>(float* p, float v) { *p = v; }
 
-template <typename T, int UB, bool HAS_P>
+template <typename T, int UB, bool HAS_P, bool OV>
 __global__ __launch_bounds__(256) void pool_block_kernel(const T* __restrict__ X,
                                                         const T* __restrict__ Z,
+                                                        const T* __restrict__ Xb,
+                                                        const T* __restrict__ Zb,
                                                         const float* __restrict__ P,
                                                         T* __restrict__ out, int N, int c,
-                                                        int m, int S, int CVG, long long in_bs,
-                                                        long long out_bs) {
+                                                        int m, int prev, int S, int CVG,
+                                                        long long in_bs, long long out_bs) {
   extern __shared__ float part[];  // [S][CVG][3][VEC]
   const int CG = c / VEC / CVG;
   const int cvl = threadIdx.x % CVG, s = threadIdx.x / CVG;
   const int cg = blockIdx.x % CG, bi = blockIdx.x / CG;
   const int b = bi / N, i = bi - b * N;
   const int cv = cg * CVG + cvl;
-  const int span = cdiv(m, S);
-  const int j_lo = min(m, s * span), j_hi = min(m, j_lo + span);
-  const long long base = (long long)b * in_bs + (long long)i * m * c + (long long)cv * VEC;
+  const int blk = OV ? i + prev : i;
+  // the entry's tokens: stream a's m, then (overlapped, after the first block) stream b's
+  // m of the previous block; thread s takes the s-th sub-range of them
+  const int mt = (OV && blk >= 1) ? 2 * m : m;
+  const int span = cdiv(OV ? 2 * m : m, S);
+  const int j_lo = min(mt, s * span), j_hi = min(mt, j_lo + span);
+  const long long base = (long long)b * in_bs + (long long)blk * m * c + (long long)cv * VEC;
   float mx[VEC], sum[VEC], acc[VEC];
 #pragma unroll
   for (int e = 0; e < VEC; ++e) {
@@ -188,7 +204,12 @@ __global__ __launch_bounds__(256) void pool_block_kernel(const T* __restrict__ X
     sum[e] = 0.f;
     acc[e] = 0.f;
   }
-  pool_run<T, UB, HAS_P>(X + base, Z + base, HAS_P ? P + cv * VEC : nullptr, c, j_lo, j_hi, mx, sum, acc);
+  pool_run<T, UB, HAS_P>(X + base, Z + base, HAS_P ? P + cv * VEC : nullptr, c, j_lo, min(j_hi, m),
+                         mx, sum, acc);
+  if (OV && j_hi > m)
+    pool_run<T, UB, HAS_P>(Xb + base - (long long)m * c, Zb + base - (long long)m * c,
+                           HAS_P ? P + (long long)m * c + cv * VEC : nullptr, c, max(j_lo, m) - m,
+                           j_hi - m, mx, sum, acc);
   float* mine = part + ((size_t)s * CVG + cvl) * 3 * VEC;
 #pragma unroll
   for (int e = 0; e < VEC; ++e) {
@@ -213,71 +234,104 @@ __global__ __launch_bounds__(256) void pool_block_kernel(const T* __restrict__ X
   }
 }
 
-template <typename T, bool HAS_P>
-void launch_pool(const void* kv, const void* gate, const float* pos_bias, void* out, int B,
-                 long long N, int c, int m, long long in_bs, long long out_bs, hipStream_t st) {
+template <typename T, bool HAS_P, bool OV>
+void launch_pool(const void* kv, const void* gate, const void* kv_b, const void* gate_b,
+                 const float* pos_bias, void* out, int B, long long N, int c, int m, int prev,
+                 long long in_bs, long long out_bs, hipStream_t st) {
   const long long total = (long long)B * N * (c / 8);
   const int CV = c / VEC;
-  if (total < 32768 && m >= 8) {
+  const int mt = OV ? 2 * m : m;  // tokens an entry reads
+  const T *X = (const T*)kv, *Z = (const T*)gate, *Xb = (const T*)kv_b, *Zb = (const T*)gate_b;
+  if (total < 32768 && mt >= 8) {
     // few blocks of many tokens: 8-channel slices in groups of up to 8 per workgroup,
     // tokens in sub-ranges of at least 4, at most 256 threads per workgroup
     int CVG = 8;
     while (CV % CVG != 0) CVG /= 2;
     const int smax = 256 / CVG;
-    const int span = max(4, cdiv(m, smax));
-    const int S = cdiv(m, span);
+    const int span = max(4, cdiv(mt, smax));
+    const int S = cdiv(mt, span);
     const size_t lds = (size_t)S * CVG * 3 * VEC * sizeof(float);
     const unsigned grid = (unsigned)(B * N * (CV / CVG)), threads = (unsigned)(S * CVG);
-    if (span % 8 == 0)
-      hipLaunchKernelGGL((pool_block_kernel<T, 8, HAS_P>), dim3(grid), dim3(threads), lds, st,
-                         (const T*)kv, (const T*)gate, pos_bias, (T*)out, (int)N, c, m, S, CVG,
-                         in_bs, out_bs);
+    if (span % 8 == 0 && m % 8 == 0)
+      hipLaunchKernelGGL((pool_block_kernel<T, 8, HAS_P, OV>), dim3(grid), dim3(threads), lds, st,
+                         X, Z, Xb, Zb, pos_bias, (T*)out, (int)N, c, m, prev, S, CVG, in_bs, out_bs);
     else
-      hipLaunchKernelGGL((pool_block_kernel<T, 4, HAS_P>), dim3(grid), dim3(threads), lds, st,
-                         (const T*)kv, (const T*)gate, pos_bias, (T*)out, (int)N, c, m, S, CVG,
-                         in_bs, out_bs);
+      hipLaunchKernelGGL((pool_block_kernel<T, 4, HAS_P, OV>), dim3(grid), dim3(threads), lds, st,
+                         X, Z, Xb, Zb, pos_bias, (T*)out, (int)N, c, m, prev, S, CVG, in_bs, out_bs);
     return;
   }
   const unsigned blocks = (unsigned)cdiv<long long>(total, 256);
   if (m % 8 == 0)
-    hipLaunchKernelGGL((pool_kernel<T, 8, HAS_P>), dim3(blocks), dim3(256), 0, st, (const T*)kv,
-                       (const T*)gate, pos_bias, (T*)out, (int)N, c, m, in_bs, out_bs, total);
+    hipLaunchKernelGGL((pool_kernel<T, 8, HAS_P, OV>), dim3(blocks), dim3(256), 0, st, X, Z, Xb, Zb,
+                       pos_bias, (T*)out, (int)N, c, m, prev, in_bs, out_bs, total);
   else
-    hipLaunchKernelGGL((pool_kernel<T, 4, HAS_P>), dim3(blocks), dim3(256), 0, st, (const T*)kv,
-                       (const T*)gate, pos_bias, (T*)out, (int)N, c, m, in_bs, out_bs, total);
+    hipLaunchKernelGGL((pool_kernel<T, 4, HAS_P, OV>), dim3(blocks), dim3(256), 0, st, X, Z, Xb, Zb,
+                       pos_bias, (T*)out, (int)N, c, m, prev, in_bs, out_bs, total);
 }
 
-int pool_entry(const char* name, const void* kv, const void* gate, const float* pos_bias,
-               void* out, int B, int n, int c, int m, int dtype, long long in_bs,
-               long long out_bs, void* stream) {
+int pool_entry(const char* name, const void* kv, const void* gate, const void* kv_b,
+               const void* gate_b, bool ov, int prev, const float* pos_bias, void* out, int B,
+               int n, int c, int m, int dtype, long long in_bs, long long out_bs, void* stream) {
   using namespace csahca;
-  if (B < 1 || n < 0 || c < 8 || (c % 8) != 0 || m < 1 || m > 4096)
-    return fail(CSAHCA_EINVAL, "pool: need B >= 1, n >= 0, c >= 8 with c % 8 == 0, 1 <= m <= 4096");
-  if (dtype != CSAHCA_F32 && dtype != CSAHCA_BF16)
-    return fail(CSAHCA_ENOTSUP, "pool: dtype must be CSAHCA_F32 or CSAHCA_BF16");
-  const long long N = n / m;
-  if (N == 0) {  // no complete block: nothing to emit, nothing is read
+  if (B < 1 || n < 0 || c < 8 || (c % 8) != 0 || m < 1 || m > 4096) {
+    set_error("%s: need B >= 1, n >= 0, c >= 8 with c %% 8 == 0, 1 <= m <= 4096", name);
+    return CSAHCA_EINVAL;
+  }
+  if (prev != 0 && prev != 1) {
+    set_error("%s: prev must be 0 or 1", name);
+    return CSAHCA_EINVAL;
+  }
+  if (dtype != CSAHCA_F32 && dtype != CSAHCA_BF16) {
+    set_error("%s: dtype must be CSAHCA_F32 or CSAHCA_BF16", name);
+    return CSAHCA_ENOTSUP;
+  }
+  const long long N = n / m - prev;  // entries to emit
+  if (N <= 0) {  // no complete block to emit: nothing is read
     clear_error();
     return CSAHCA_OK;
   }
-  if (!kv || !gate || !out) return fail(CSAHCA_EINVAL, "pool: kv, gate and out must be non-NULL");
-  if (in_bs < (long long)n * c || out_bs < N * c)
-    return fail(CSAHCA_EINVAL, "pool: in_bstride must be >= n*c and out_bstride >= (n/m)*c");
-  if ((in_bs % 8) != 0 || (out_bs % 8) != 0)
-    return fail(CSAHCA_EINVAL, "pool: strides must be multiples of 8 elements");
-  if (!aligned16(kv) || !aligned16(gate) || !aligned16(out))
-    return fail(CSAHCA_EINVAL, "pool: kv, gate and out must be 16-byte aligned");
-  const long long total = (long long)B * N * (c / 8);
-  if (cdiv<long long>(total, 256) > 0x7FFFFFFFLL)
-    return fail(CSAHCA_ENOTSUP, "pool: problem too large for one launch");
-  hipStream_t st = (hipStream_t)stream;
-  if (dtype == CSAHCA_BF16) {
-    if (pos_bias) launch_pool<uint16_t, true>(kv, gate, pos_bias, out, B, N, c, m, in_bs, out_bs, st);
-    else launch_pool<uint16_t, false>(kv, gate, pos_bias, out, B, N, c, m, in_bs, out_bs, st);
-  } else {
-    if (pos_bias) launch_pool<float, true>(kv, gate, pos_bias, out, B, N, c, m, in_bs, out_bs, st);
-    else launch_pool<float, false>(kv, gate, pos_bias, out, B, N, c, m, in_bs, out_bs, st);
+  if (!kv || !gate || !out || (ov && (!kv_b || !gate_b))) {
+    set_error("%s: the KV, gate and out pointers must be non-NULL", name);
+    return CSAHCA_EINVAL;
   }
+  if (in_bs < (long long)n * c || out_bs < N * c) {
+    set_error("%s: in_bstride must be >= n*c and out_bstride >= entries*c", name);
+    return CSAHCA_EINVAL;
+  }
+  if ((in_bs % 8) != 0 || (out_bs % 8) != 0) {
+    set_error("%s: strides must be multiples of 8 elements", name);
+    return CSAHCA_EINVAL;
+  }
+  if (!aligned16(kv) || !aligned16(gate) || !aligned16(out) || (ov && (!aligned16(kv_b) || !aligned16(gate_b)))) {
+    set_error("%s: the KV, gate and out pointers must be 16-byte aligned", name);
+    return CSAHCA_EINVAL;
+  }
+  const long long total = (long long)B * N * (c / 8);
+  if (cdiv<long long>(total, 256) > 0x7FFFFFFFLL) {
+    set_error("%s: problem too large for one launch", name);
+    return CSAHCA_ENOTSUP;
+  }
+  hipStream_t st = (hipStream_t)stream;
+#define CSAHCA_POOL_LAUNCH(T, HP, O) \
+  launch_pool<T, HP, O>(kv, gate, kv_b, gate_b, pos_bias, out, B, N, c, m, prev, in_bs, out_bs, st)
+  if (dtype == CSAHCA_BF16) {
+    if (ov) {
+      if (pos_bias) CSAHCA_POOL_LAUNCH(uint16_t, true, true);
+      else CSAHCA_POOL_LAUNCH(uint16_t, false, true);
+    } else {
+      if (pos_bias) CSAHCA_POOL_LAUNCH(uint16_t, true, false);
+      else CSAHCA_POOL_LAUNCH(uint16_t, false, false);
+    }
+  } else {
+    if (ov) {
+      if (pos_bias) CSAHCA_POOL_LAUNCH(float, true, true);
+      else CSAHCA_POOL_LAUNCH(float, false, true);
+    } else {
+      if (pos_bias) CSAHCA_POOL_LAUNCH(float, true, false);
+      else CSAHCA_POOL_LAUNCH(float, false, false);
+    }
+  }
+#undef CSAHCA_POOL_LAUNCH
   return launch_status(name);
 }
 
@@ -286,13 +340,21 @@ int pool_entry(const char* name, const void* kv, const void* gate, const float* 
 extern "C" int csa_compress(const void* kv, const void* gate, const float* pos_bias, void* out,
                             int B, int n, int c, int m, int dtype, long long in_bstride,
                             long long out_bstride, void* stream) {
-  return pool_entry("csa_compress", kv, gate, pos_bias, out, B, n, c, m, dtype, in_bstride,
-                    out_bstride, stream);
+  return pool_entry("csa_compress", kv, gate, nullptr, nullptr, false, 0, pos_bias, out, B, n, c,
+                    m, dtype, in_bstride, out_bstride, stream);
 }
 
 extern "C" int hca_compress(const void* kv, const void* gate, const float* pos_bias, void* out,
                             int B, int n, int c, int m, int dtype, long long in_bstride,
                             long long out_bstride, void* stream) {
-  return pool_entry("hca_compress", kv, gate, pos_bias, out, B, n, c, m, dtype, in_bstride,
-                    out_bstride, stream);
+  return pool_entry("hca_compress", kv, gate, nullptr, nullptr, false, 0, pos_bias, out, B, n, c,
+                    m, dtype, in_bstride, out_bstride, stream);
+}
+
+extern "C" int csa_compress_overlap(const void* kv_a, const void* gate_a, const void* kv_b,
+                                    const void* gate_b, const float* pos_bias, void* out, int B,
+                                    int n, int c, int m, int prev, int dtype,
+                                    long long in_bstride, long long out_bstride, void* stream) {
+  return pool_entry("csa_compress_overlap", kv_a, gate_a, kv_b, gate_b, true, prev, pos_bias, out,
+                    B, n, c, m, dtype, in_bstride, out_bstride, stream);
 }

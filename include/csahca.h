@@ -92,6 +92,35 @@ int hca_compress(const void* kv, const void* gate, const float* pos_bias, void* 
                  void* stream);
 
 /*
+ * csa_compress_overlap -- the overlapped two-stream CSA compressor.
+ * Source: "DeepSeek-V4 Hybrid Attention: CSA, HCA, mHC, MoE", section V.1 (two KV
+ * streams a and b with their own compression scores; entry i combines stream a's block i
+ * with stream b's block i-1, equation C_i^comp).
+ *
+ *   out[b, e, ch] = sum_{j<m} S[j, ch] * kv_a[b, m*i+j, ch]
+ *                 + sum_{j<m} S[m+j, ch] * kv_b[b, m*(i-1)+j, ch],     i = e + prev,
+ *   S[., ch] = softmax over the 2m logits ( gate_a[b, m*i+j, ch] + pos_bias[j, ch] ;
+ *                                           gate_b[b, m*(i-1)+j, ch] + pos_bias[m+j, ch] )
+ * One joint softmax per channel (the pages give the sum; normalising the 2m weights
+ * together is the reading adopted).  Block i = 0 has no predecessor: its softmax runs
+ * over stream a's m logits alone.  With prev = 1 the arrays start one block before the
+ * first entry to emit (a cache append passes the last 2m tokens, blocks i-1 and i, and
+ * gets entry i); n/m - prev entries are written.
+ *
+ *   kv_a, gate_a, kv_b, gate_b  [B, n, c] of `dtype` (CSAHCA_F32 or CSAHCA_BF16), all
+ *              with the batch stride in_bstride (elements) >= n*c.
+ *   pos_bias   [2m, c] float32 (rows 0..m-1 stream a positions, m..2m-1 stream b), or
+ *              NULL for zero bias.
+ *   out        [B, n/m - prev, c] of `dtype`, batch stride out_bstride.
+ *   prev       0 or 1.
+ *   Limits and errors as csa_compress; nothing is read or written when n/m - prev <= 0.
+ */
+int csa_compress_overlap(const void* kv_a, const void* gate_a, const void* kv_b,
+                         const void* gate_b, const float* pos_bias, void* out, int B, int n,
+                         int c, int m, int prev, int dtype, long long in_bstride,
+                         long long out_bstride, void* stream);
+
+/*
  * lightning_index_topk -- lightning-indexer scores and exact top-k selection.
  * Source: "DeepSeek-V4 Hybrid Attention: CSA, HCA, mHC, MoE", section V.2, equation
  * I_{t,s} and the top-k selector; "DeepSeek-V4: Anatomy of an Open-Source Frontier

@@ -19,6 +19,7 @@ from .csahca import (  # noqa: F401
     hca_rows,
     index_scores,
     pool,
+    pool_overlap,
     topk,
     visible,
     window_positions,

@@ -49,6 +49,15 @@ def run_pool(X, Z, m, dtype, P=None, fn=lib.csa_compress):
     return out
 
 
+def run_pool_overlap(Xa, Za, Xb, Zb, m, prev, dtype, P=None):
+    """Overlapped two-stream pooling: device [B, n, c] x 4 -> device [B, n//m - prev, c]."""
+    B, n, c = Xa.shape
+    N = max(n // m - prev, 0)
+    out = empty((B, N, c), dtype)
+    lib.csa_compress_overlap(Xa, Za, Xb, Zb, P, out, B, n, c, m, prev, dtype, n * c, max(N, 1) * c)
+    return out
+
+
 def run_index(qI, w, KI, q_pos, m, k, idx_dtype, split=False):
     B, Tq, n_ih, c_I = qI.shape
     N_c = KI.shape[1]

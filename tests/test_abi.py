@@ -52,6 +52,14 @@ def test_pool_validation():
     assert L.csa_compress(FAKE, FAKE, None, FAKE, 1, 8, 8, 0, 1, 64, 16, None) == EINVAL   # m
     # fewer tokens than one block: nothing to do, pointers may be NULL
     assert L.csa_compress(None, None, None, None, 1, 3, 8, 4, 1, 24, 0, None) == 0
+    # overlapped form: prev is 0 or 1, stream b pointers are required, an append of one
+    # block with prev = 1 emits nothing
+    ov = L.csa_compress_overlap
+    assert ov(FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 8, 8, 4, 2, 1, 64, 16, None) == EINVAL
+    assert ov(FAKE, FAKE, None, FAKE, None, FAKE, 1, 8, 8, 4, 0, 1, 64, 16, None) == EINVAL
+    assert ov(FAKE, FAKE, FAKE + 4, FAKE, None, FAKE, 1, 8, 8, 4, 0, 1, 64, 16, None) == EINVAL
+    assert ov(FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 8, 8, 4, 0, 2, 64, 16, None) == ENOTSUP
+    assert ov(None, None, None, None, None, None, 1, 4, 8, 4, 1, 1, 32, 0, None) == 0
 
 
 def test_indexer_validation():

@@ -48,6 +48,9 @@ def parse():
                     help="rocprofv3 --pmc output folders: write the traffic record and exit")
     ap.add_argument("--traffic-out", default=PROFILE_TRAFFIC,
                     help="where --traffic-from writes its record")
+    ap.add_argument("--overlap-pool", action="store_true",
+                    help="time the overlapped two-stream CSA pooling (full context pass and a "
+                         "decode append) at the config's shape instead of the step")
     return ap.parse_args()
 
 
@@ -363,6 +366,105 @@ def cpu_baseline(wl, seconds):
                       f"({cfg.B} distinct sequences cycled), {el:.1f} s, NumPy fp64"}
 
 
+def overlap_pool(cfg, reps, cpu_seconds, no_cpu):
+    """csa_compress_overlap at the config's CSA shape: one pass over the whole context
+    (every entry; reads four [B, n, c] arrays, writes [B, n/m, c]) and a decode append
+    (the last two blocks, prev = 1, one entry per sequence)."""
+    import numpy as np
+    import torch
+
+    import compressed_attention_compress_amd as lib
+
+    B, n, c, m = cfg.B, cfg.n, cfg.c, cfg.m
+    dt = cfg.dtype
+    g = torch.Generator(device="cuda").manual_seed(1234)
+    tdt = torch.bfloat16 if dt == 1 else torch.float32
+    arrs = []
+    for k in range(4):  # X_a, Z_a, X_b, Z_b
+        a = torch.randn((B, n, c), generator=g, device="cuda", dtype=torch.float32)
+        if k % 2 == 0:
+            a.mul_(1.0 / math.sqrt(c))
+        arrs.append(a.to(tdt))
+        del a
+    N = n // m
+    out = torch.empty((B, N, c), dtype=tdt, device="cuda")
+    st = torch.cuda.current_stream()
+
+    def full():
+        lib.csa_compress_overlap(*arrs, None, out, B, n, c, m, 0, dt, n * c, N * c, stream=st)
+
+    full()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(reps):
+        full()
+    e1.record(st)
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) / 1e3 / reps
+    es = 2 if dt == 1 else 4
+    nbytes = 4 * B * n * c * es + B * N * c * es
+
+    # decode append: the last 2m tokens of every sequence, one entry each
+    tail = [a[:, n - 2 * m:] for a in arrs]
+    app_out = out[:, N - 1:N]
+
+    def append():
+        lib.csa_compress_overlap(*tail, None, app_out, B, 2 * m, c, m, 1, dt, n * c, N * c, stream=st)
+
+    side = torch.cuda.Stream()
+    append()
+    torch.cuda.synchronize()
+    ga = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(ga, stream=side):
+        for _ in range(20):
+            lib.csa_compress_overlap(*tail, None, app_out, B, 2 * m, c, m, 1, dt, n * c, N * c,
+                                     stream=side)
+    ga.replay()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        e0.record(side)
+        for _ in range(10):
+            ga.replay()
+        e1.record(side)
+    torch.cuda.synchronize()
+    app_us = e0.elapsed_time(e1) * 1e3 / 200
+
+    cpu = None
+    if not no_cpu:
+        import oracle
+        rng = np.random.default_rng(5)
+        ntok = 1 << 14  # tokens per oracle call (one sequence slice)
+        Xa, Za, Xb, Zb = (rng.standard_normal((ntok, c)) for _ in range(4))
+        t0 = time.perf_counter()
+        done = 0
+        while True:
+            oracle.pool_overlap(Xa, Za, Xb, Zb, m)
+            done += ntok
+            el = time.perf_counter() - t0
+            if el >= cpu_seconds:
+                break
+        cpu = {"value": round(done * (4 * c + c / m) * es / el / 1e9, 3), "unit": "GB/s",
+               "cores": torch.get_num_threads(), "kind": "oracle",
+               "sample": f"{done} tokens in {ntok}-token slices of one sequence, {el:.1f} s, "
+                         f"NumPy fp64 (bytes counted at the GPU's storage width)"}
+    gbs = nbytes / sec / 1e9
+    line = {
+        "metric": "overlapped two-stream CSA pooling, achieved HBM GB/s over the full context",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": reps, "warmup": 1,
+        "ms_per_pass": round(sec * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if dt == 1 else "f32", "data": "synthetic",
+        "config": {"workload": f"csa_overlap_pool_{cfg.name}", "batch": B, "context": n, "c": c,
+                   "m": m, "timing": "HIP events around back-to-back launches"},
+        "append_us": round(app_us, 2),
+        "roofline": {"kernel": "pool_kernel (overlapped)", "bound": "hbm", "achieved": round(gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None, "avg_launch_us": round(sec * 1e6, 2), "bytes_per_launch": nbytes},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.traffic_from:
@@ -380,6 +482,9 @@ def main():
         calibrate_copy()
         return
     cfg = CONFIGS[args.config]
+    if args.overlap_pool:
+        overlap_pool(cfg, args.steps or 10, min(args.cpu_seconds, 10.0), args.no_cpu_baseline)
+        return
     decode = cfg.kind != "prefill"
     steps = args.steps if args.steps is not None else (500 if decode else 20)
     warmup = args.warmup if args.warmup is not None else (50 if decode else 3)

@@ -108,9 +108,8 @@ def pool_overlap(Xa, Za, Xb, Zb, m, P=None, prev=0):
 
     [P2] V.1, equation C_i^comp: CSA projects two KV streams (a, b) with their own
     compression scores; entry i is the channel-wise weighted sum of stream a over block i
-    and stream b over block i-1 (2m raw entries, so a block boundary is covered twice),
-    the weights being the softmax pooling weights over the scores plus a positional
-    bias.
+    and stream b over block i-1, so consecutive entries share a block boundary; the
+    weights are the softmax pooling weights over the scores plus a positional bias.
 
     Readings (the pages give the sum, not the normalisation): one joint softmax per
     channel over the 2m logits [Za of block i + P[0:m]; Zb of block i-1 + P[m:2m]]; for
@@ -212,7 +211,7 @@ def topk(scores, k):
 # ----------------------------------------------------------------------------------------
 # (a4, a5) attention over a row set (MQA: one shared K = V row per entry)
 # ----------------------------------------------------------------------------------------
-def attend(Q, rows, scale):
+def attend(Q, rows, scale, sink=None):
     """O_h = sum_r softmax_r(scale * Q_h . row_r) row_r, and its log-sum-exp.
 
     [P2] I: softmax(QK^T / sqrt(c)) V; [P2] VI eq. o_{t,i}: key = value = compressed
@@ -220,16 +219,28 @@ def attend(Q, rows, scale):
     window rows enter one joint softmax ([P4] step 5: ordinary attention over the union),
     without removing rows that appear both raw and inside a compressed entry.
 
+    sink: optional [n_h] per-head learnable attention sink ([P2] IV names it for both
+    branches).  Reading: a logit in the same units as scale * q . k that enters the
+    softmax denominator only (a row of value zero), so
+    O_h = sum_r e^{z_r} row_r / (e^{sink_h} + sum_r e^{z_r}) and the lse includes it.
+
     Q: [n_h, c]; rows: [R, c].  Returns (O [n_h, c], lse [n_h]).
     """
     Q = np.asarray(Q, dtype=np.float64)
     rows = np.asarray(rows, dtype=np.float64)
+    n_h = Q.shape[0]
+    sk = None if sink is None else np.asarray(sink, dtype=np.float64).reshape(n_h, 1)
     if rows.shape[0] == 0:
-        return np.zeros_like(Q), np.full((Q.shape[0],), -np.inf)
+        lse = np.full((n_h,), -np.inf) if sk is None else sk[:, 0].copy()
+        return np.zeros_like(Q), lse
     s = (Q @ rows.T) * float(scale)        # [n_h, R]
     mx = s.max(axis=1, keepdims=True)
+    if sk is not None:
+        mx = np.maximum(mx, sk)
     e = np.exp(s - mx)
     l = e.sum(axis=1, keepdims=True)
+    if sk is not None:
+        l = l + np.exp(sk - mx)            # the sink's weight: denominator only
     O = (e @ rows) / l
     lse = (mx + np.log(l))[:, 0]
     return O, lse

@@ -269,6 +269,36 @@ def check_attend_textbook(o):
     np.testing.assert_array_equal(o.attend(Q, rows[:1], scale)[0], np.repeat(rows[:1], n_h, 0))
 
 
+def check_attend_sink(o):
+    """Per-head attention sink: a logit that joins the softmax denominator only."""
+    rng = np.random.default_rng(13)
+    n_h, c, R = 5, 8, 7
+    Q = rng.normal(size=(n_h, c))
+    rows = rng.normal(size=(R, c))
+    scale = 1.0 / np.sqrt(c)
+    O0, l0 = o.attend(Q, rows, scale)
+    # a sink at -inf changes nothing
+    O1, l1 = o.attend(Q, rows, scale, sink=np.full(n_h, -np.inf))
+    np.testing.assert_allclose(O1, O0, atol=1e-15)
+    np.testing.assert_allclose(l1, l0, atol=1e-15)
+    # a sink of 0 is an extra row of zeros (its score q . 0 = 0, its value 0)
+    O2, l2 = o.attend(Q, rows, scale, sink=np.zeros(n_h))
+    O3, l3 = o.attend(Q, np.vstack([rows, np.zeros((1, c))]), scale)
+    np.testing.assert_allclose(O2, O3, atol=1e-14)
+    np.testing.assert_allclose(l2, l3, atol=1e-14)
+    # the lse gains the sink: log(e^lse + e^sink)
+    sk = rng.normal(size=n_h) * 2
+    O4, l4 = o.attend(Q, rows, scale, sink=sk)
+    np.testing.assert_allclose(l4, np.logaddexp(l0, sk), atol=1e-13)
+    # the weights shrink by e^{lse} / (e^{lse} + e^{sink}), the logistic of lse - sink
+    np.testing.assert_allclose(O4, O0 * (1.0 / (1.0 + np.exp(sk - l0)))[:, None], atol=1e-13)
+    # one row v: O = v * logistic(scale * q . v - sink)
+    v = rows[:1]
+    z = (Q @ v.T)[:, 0] * scale
+    O5, _ = o.attend(Q, v, scale, sink=sk)
+    np.testing.assert_allclose(O5, (1.0 / (1.0 + np.exp(sk - z)))[:, None] * v, atol=1e-14)
+
+
 def check_rows_and_visibility(o):
     rng = np.random.default_rng(9)
     c, m, W = 4, 4, 8
@@ -305,7 +335,8 @@ def check_rows_and_visibility(o):
 ALL_CHECKS = [check_budget_counts, check_worked_example, check_pool_counts, check_budget_toy,
               check_pooling_recall, check_pool_closed_forms, check_pool_overlap_closed_forms,
               check_indexer_closed_forms,
-              check_topk_brute, check_attend_textbook, check_rows_and_visibility]
+              check_topk_brute, check_attend_textbook, check_attend_sink,
+              check_rows_and_visibility]
 
 
 @pytest.mark.parametrize("check", ALL_CHECKS, ids=lambda f: f.__name__)
@@ -429,17 +460,34 @@ def _topk_high_index_wins(scores, k):
     return out
 
 
-def _attend_no_scale(Q, rows, scale):
-    return _ORIG_ATTEND(Q, rows, 1.0)
+def _attend_no_scale(Q, rows, scale, sink=None):
+    return _ORIG_ATTEND(Q, rows, 1.0, sink)
 
 
-def _attend_transposed(Q, rows, scale):
+def _attend_transposed(Q, rows, scale, sink=None):
     Q = np.asarray(Q, float)
     rows = np.asarray(rows, float)
     s = (Q @ rows.T) * scale
     e = np.exp(s - s.max(0, keepdims=True))
     p = e / e.sum(0, keepdims=True)                      # normalised over heads
     return p @ rows, np.zeros(Q.shape[0])
+
+
+def _attend_sink_scaled(Q, rows, scale, sink=None):
+    # the sink multiplied by the attention scale like a dot product
+    return _ORIG_ATTEND(Q, rows, scale, None if sink is None else np.asarray(sink) * scale)
+
+
+def _attend_sink_in_numerator(Q, rows, scale, sink=None):
+    # the sink as a row of ones (it then adds to every output value)
+    if sink is None:
+        return _ORIG_ATTEND(Q, rows, scale)
+    Q = np.asarray(Q, float)
+    rows = np.asarray(rows, float)
+    s = np.hstack([(Q @ rows.T) * scale, np.asarray(sink, float)[:, None]])
+    e = np.exp(s - s.max(1, keepdims=True))
+    vals = np.vstack([rows, np.ones((1, rows.shape[1]))])
+    return (e @ vals) / e.sum(1, keepdims=True), np.log(e.sum(1)) + s.max(1)
 
 
 def _visible_off_by_one(p, m, N):
@@ -465,6 +513,8 @@ MUTANTS = {
     "topk_higher_index_wins": dict(topk=_topk_high_index_wins),
     "attend_without_scale": dict(attend=_attend_no_scale),
     "attend_softmax_over_heads": dict(attend=_attend_transposed),
+    "attend_sink_scaled": dict(attend=_attend_sink_scaled),
+    "attend_sink_in_numerator": dict(attend=_attend_sink_in_numerator),
     "visibility_off_by_one": dict(visible=_visible_off_by_one),
     "window_excludes_query": dict(window_positions=_window_excl),
     "counts_round_up": dict(entry_counts=_counts_ceil),

@@ -48,6 +48,9 @@ def parse():
                     help="rocprofv3 --pmc output folders: write the traffic record and exit")
     ap.add_argument("--traffic-out", default=PROFILE_TRAFFIC,
                     help="where --traffic-from writes its record")
+    ap.add_argument("--sink", action="store_true",
+                    help="run both attention calls with a per-head attention sink "
+                         "(csa_attend_sink / hca_attend_sink)")
     ap.add_argument("--overlap-pool", action="store_true",
                     help="time the overlapped two-stream CSA pooling (full context pass and a "
                          "decode append) at the config's shape instead of the step")
@@ -57,7 +60,7 @@ def parse():
 class Workload:
     """All device state of one workload: inputs, caches, replicas, outputs, workspaces."""
 
-    def __init__(self, cfg, replicas):
+    def __init__(self, cfg, replicas, sink=False):
         import torch
 
         import compressed_attention_compress_amd as lib
@@ -109,6 +112,10 @@ class Workload:
         if "hca" in self.layers:
             self.hws_b = lib.hca_attend_workspace_size(B, self.Tq, cfg.n_h, c, self.N_h, cfg.W)
             self.hws = torch.empty(max(self.hws_b, 256), dtype=torch.uint8, device=dev)
+        self.sink = None
+        if sink:  # seeded per-head logits, N(0, 2^2)
+            gs = torch.Generator(device=dev).manual_seed(99)
+            self.sink = torch.randn((cfg.n_h,), generator=gs, device=dev) * 2.0
         torch.cuda.synchronize()
 
     # -- the step -------------------------------------------------------------------------
@@ -148,14 +155,23 @@ class Workload:
     def attend(self, r):
         cfg, lib, rp, prob = self.cfg, self.lib, self.rep[r], self.prob
         B, c, n = cfg.B, cfg.c, self.n
+        sk = self.sink
         if "csa" in self.layers:
-            lib.csa_attend(rp["Q_csa"], rp["C_csa"], self.idx, prob["X_csa"], self.win_pos,
-                           self.q_pos, B, self.Tq, cfg.n_h, c, self.N_c, cfg.k, n, cfg.W,
-                           self.scale, cfg.dtype, self.out["csa"], None, self.cws, self.cws_b)
+            args = (rp["Q_csa"], rp["C_csa"], self.idx, prob["X_csa"], self.win_pos, self.q_pos, B,
+                    self.Tq, cfg.n_h, c, self.N_c, cfg.k, n, cfg.W, self.scale)
+            tail = (cfg.dtype, self.out["csa"], None, self.cws, self.cws_b)
+            if sk is None:
+                lib.csa_attend(*args, *tail)
+            else:
+                lib.csa_attend_sink(*args, sk, *tail)
         if "hca" in self.layers:
-            lib.hca_attend(rp["Q_hca"], rp["C_hca"], prob["X_hca"], self.win_pos, self.q_pos,
-                           cfg.m_hca, B, self.Tq, cfg.n_h, c, self.N_h, n, cfg.W, self.scale,
-                           cfg.dtype, self.out["hca"], None, self.hws, self.hws_b)
+            args = (rp["Q_hca"], rp["C_hca"], prob["X_hca"], self.win_pos, self.q_pos, cfg.m_hca, B,
+                    self.Tq, cfg.n_h, c, self.N_h, n, cfg.W, self.scale)
+            tail = (cfg.dtype, self.out["hca"], None, self.hws, self.hws_b)
+            if sk is None:
+                lib.hca_attend(*args, *tail)
+            else:
+                lib.hca_attend_sink(*args, sk, *tail)
 
     def step(self, r):
         self.pool_new_blocks(r)
@@ -490,7 +506,7 @@ def main():
     warmup = args.warmup if args.warmup is not None else (50 if decode else 3)
     R = args.replicas if args.replicas is not None else (6 if decode else 1)
     torch.cuda.set_device(0)
-    wl = Workload(cfg, R)
+    wl = Workload(cfg, R, sink=args.sink)
 
     # warm up eagerly (also sets the library's one-time kernel attributes)
     for i in range(warmup):
@@ -565,7 +581,8 @@ def main():
         "config": {"workload": cfg.name, "batch": cfg.B, "context": wl.n, "query_tokens": wl.Tq,
                    "c": cfg.c, "n_h": cfg.n_h, "m": cfg.m, "m_hca": cfg.m_hca, "k": cfg.k,
                    "n_ih": cfg.n_ih, "c_I": cfg.c_I, "window": cfg.W, "replicas": R,
-                   "timing": "hip graph per step, rotating replicas"},
+                   "timing": "hip graph per step, rotating replicas",
+                   **({"attention_sink": "per-head, N(0, 2^2)"} if args.sink else {})},
         "hbm_gbs": round(abytes / sec / 1e9, 1),
         "hbm_frac": round(abytes / sec / 1e9 / HBM_PEAK_GBS, 4),
         "algorithmic_bytes_per_step": abytes,

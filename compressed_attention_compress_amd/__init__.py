@@ -36,6 +36,10 @@ _SIGNATURES = {
     "hca_attend_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
     "hca_attend": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P,
                         _SZ, _P]),
+    "csa_attend_sink": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _I,
+                             _P, _P, _P, _SZ, _P]),
+    "hca_attend_sink": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _I, _P,
+                             _P, _P, _SZ, _P]),
     "csahca_last_error": (ctypes.c_char_p, []),
     "csahca_version": (_I, []),
 }
@@ -163,3 +167,19 @@ def hca_attend(q, ckv, win_kv, win_pos, q_pos, m, B, Tq, n_h, c, N_h, L, W, scal
     return _check("hca_attend", load().hca_attend(
         _ptr(q), _ptr(ckv), _ptr(win_kv), _ptr(win_pos), _ptr(q_pos), m, B, Tq, n_h, c, N_h, L, W,
         float(scale), dtype, _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def csa_attend_sink(q, ckv, topk_idx, win_kv, win_pos, q_pos, B, Tq, n_h, c, N_c, k, L, W, scale,
+                    sink, dtype, out, lse, workspace, ws_bytes, stream=None):
+    return _check("csa_attend_sink", load().csa_attend_sink(
+        _ptr(q), _ptr(ckv), _ptr(topk_idx), _ptr(win_kv), _ptr(win_pos), _ptr(q_pos), B, Tq,
+        n_h, c, N_c, k, L, W, float(scale), _ptr(sink), dtype, _ptr(out), _ptr(lse),
+        _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def hca_attend_sink(q, ckv, win_kv, win_pos, q_pos, m, B, Tq, n_h, c, N_h, L, W, scale, sink,
+                    dtype, out, lse, workspace, ws_bytes, stream=None):
+    return _check("hca_attend_sink", load().hca_attend_sink(
+        _ptr(q), _ptr(ckv), _ptr(win_kv), _ptr(win_pos), _ptr(q_pos), m, B, Tq, n_h, c, N_h, L, W,
+        float(scale), _ptr(sink), dtype, _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
+        _stream(stream)))

@@ -36,6 +36,21 @@ constexpr int KS = C / 32;        // MFMA K-steps of S (16 x 32 dims)
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
+// Per-head attention sink: a logit (natural-log units, the units of scale * q.k) that
+// joins the softmax denominator only.  Folds it into a head's maximum m (log2 units) and
+// sum l, and returns the factor that carries accumulators taken relative to the old
+// maximum over to the new one.
+CSAHCA_DEV float fold_sink(const float* sink, int h, float& m, float& l) {
+  if (!sink) return 1.f;
+  const float s2 = sink[h] * LOG2E;
+  if (s2 == -INFINITY) return 1.f;
+  const float M = fmaxf(m, s2);
+  const float r = m == -INFINITY ? 0.f : exp2f(m - M);
+  l = l * r + exp2f(s2 - M);
+  m = M;
+  return r;
+}
+
 struct AttnArgs {
   const uint16_t* q;
   const uint16_t* ckv;
@@ -47,6 +62,7 @@ struct AttnArgs {
   float* lse;
   uint16_t* opart;  // [nq, n_splits, n_h, C] partial outputs O/l, scaled float16
   float* mlpart;    // [nq, n_splits, n_h, 4] running max (log2 units), sum, scale, pad
+  const float* sink;  // [n_h] attention sink logits (natural-log units) or null
   int B, Tq, n_h, Nc, k, L, W, m;
   int is_csa;
   int n_slots_c;  // compressed slots: k (CSA) or Nc (HCA)
@@ -565,10 +581,12 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && NS == 2) ? 2 : 1) void attend_
     // every head block's values of this wave's columns, as 16-bit rows [head][column]
 #pragma unroll
     for (int hb = 0; hb < NW; ++hb) {
-      const float lh = xl[hb * 16 + row16], mh = xm[hb * 16 + row16];
-      const float inv = lh > 0.f ? 1.f / lh : 0.f;
-      float f = inv;
+      float lh = xl[hb * 16 + row16], mh = xm[hb * 16 + row16];
       const bool as_f16 = a.n_splits > 1;
+      // one split: the sink joins here (with splits, in the merge)
+      const float rs = as_f16 ? 1.f : fold_sink(a.sink, hg * a.HPW + 16 * hb + row16, mh, lh);
+      const float inv = lh > 0.f ? rs / lh : 0.f;
+      float f = inv;
       if (as_f16) {  // partial O / l scaled by 2^-e per row (see the merge)
         float amax = 0.f;
 #pragma unroll
@@ -614,11 +632,12 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && NS == 2) ? 2 : 1) void attend_
   uint16_t* dst;        // the wave's first output row
   bool as_f16;
   if (a.n_splits == 1) {
-    f = l_run > 0.f ? 1.f / l_run : 0.f;
+    float mm = m_run, ll = l_run;
+    const float rs = fold_sink(a.sink, h, mm, ll);
+    f = ll > 0.f ? rs / ll : 0.f;
     dst = a.out + (qrow * a.n_h + h0) * C;
     as_f16 = false;
-    if (a.lse && g == 0)
-      a.lse[qrow * a.n_h + h] = l_run > 0.f ? (m_run + __log2f(l_run)) * LN2 : -INFINITY;
+    if (a.lse && g == 0) a.lse[qrow * a.n_h + h] = ll > 0.f ? (mm + __log2f(ll)) * LN2 : -INFINITY;
   } else {
     // Partial output O / l in float16, scaled by a power of two 2^-e chosen per row so
     // that its largest magnitude lies in [1, 2): no input range overflows, and every value
@@ -673,7 +692,8 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && NS == 2) ? 2 : 1) void attend_
 __global__ __launch_bounds__(256) void attend_combine(const uint16_t* __restrict__ opart,
                                                       const float* __restrict__ mlpart,
                                                       uint16_t* __restrict__ out,
-                                                      float* __restrict__ lse, int n_h,
+                                                      float* __restrict__ lse,
+                                                      const float* __restrict__ sink, int n_h,
                                                       int n_splits) {
   __shared__ float red[4][C + 4];
   const long long pair = blockIdx.x;
@@ -721,8 +741,9 @@ __global__ __launch_bounds__(256) void attend_combine(const uint16_t* __restrict
   __syncthreads();
   if (wave != 0) return;
   float o8[8];
-  const float Lt = ((red[0][C] + red[1][C]) + red[2][C]) + red[3][C];
-  const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
+  float Lt = ((red[0][C] + red[1][C]) + red[2][C]) + red[3][C];
+  const float rs = fold_sink(sink, h, M, Lt);
+  const float inv = Lt > 0.f ? rs / Lt : 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int c = lane * 8 + i;
@@ -747,6 +768,7 @@ struct AttnF32Args {
   const int* q_pos;
   float* out;
   float* lse;
+  const float* sink;  // [n_h] or null
   int Tq, n_h, c, Nc, k, L, W, m, is_csa, n_slots_c, n_slots;
   float scale;
 };
@@ -808,6 +830,13 @@ __global__ __launch_bounds__(256) void attend_f32(AttnF32Args a) {
     }
     for (int d = 1; d < 64; d <<= 1) sum += shfl_xor_f(sum, d);
     if (lane == 0) {
+      if (a.sink && a.sink[h] != -INFINITY) {  // the sink joins the denominator only
+        const float M = fmaxf(mm, a.sink[h]);
+        const float r = mm == -INFINITY ? 0.f : expf(mm - M);
+        for (int j = 0; j < a.n_slots; ++j) S[h * a.n_slots + j] *= r;
+        sum = sum * r + expf(a.sink[h] - M);
+        mm = M;
+      }
       stat[h] = sum;
       mx[h] = mm;
     }
@@ -944,8 +973,8 @@ int check_attend(const char* name, const void* q, const void* ckv, const void* w
 
 int attend_impl(const char* name, bool csa, const void* q, const void* ckv, const int* topk,
                 const void* win_kv, const int* win_pos, const int* q_pos, int m, int B, int Tq,
-                int n_h, int c, int N, int k, int L, int W, float scale, int dtype, void* out,
-                float* lse, void* workspace, size_t ws_bytes, hipStream_t st) {
+                int n_h, int c, int N, int k, int L, int W, float scale, const float* sink,
+                int dtype, void* out, float* lse, void* workspace, size_t ws_bytes, hipStream_t st) {
   using namespace csahca;
   const int n_slots_c = csa ? k : N;
   if (dtype == CSAHCA_F32) {
@@ -958,6 +987,7 @@ int attend_impl(const char* name, bool csa, const void* q, const void* ckv, cons
     A.q_pos = q_pos;
     A.out = (float*)out;
     A.lse = lse;
+    A.sink = sink;
     A.Tq = Tq;
     A.n_h = n_h;
     A.c = c;
@@ -992,6 +1022,7 @@ int attend_impl(const char* name, bool csa, const void* q, const void* ckv, cons
   A.q_pos = q_pos;
   A.out = (uint16_t*)out;
   A.lse = lse;
+  A.sink = sink;
   A.opart = P.n_splits > 1 ? (uint16_t*)workspace : nullptr;
   A.mlpart = P.n_splits > 1 ? (float*)((char*)workspace + P.opart_bytes) : nullptr;
   A.B = B;
@@ -1024,7 +1055,7 @@ int attend_impl(const char* name, bool csa, const void* q, const void* ckv, cons
   if (rc != CSAHCA_OK || P.n_splits == 1) return rc;
   const long long nqh = (long long)B * Tq * n_h;
   hipLaunchKernelGGL(attend_combine, dim3((unsigned)nqh), dim3(256), 0, st, A.opart, A.mlpart,
-                     A.out, lse, n_h, P.n_splits);
+                     A.out, lse, sink, n_h, P.n_splits);
   return launch_status(name);
 }
 
@@ -1042,33 +1073,79 @@ extern "C" size_t hca_attend_workspace_size(int B, int Tq, int n_h, int c, int N
   return make_plan(B, Tq, n_h, N_h, W, false).ws;
 }
 
+namespace {
+
+int csa_entry(const char* name, const void* q, const void* ckv, const int* topk_idx,
+              const void* win_kv, const int* win_pos, const int* q_pos, int B, int Tq, int n_h,
+              int c, int N_c, int k, int L, int W, float scale, const float* sink, int dtype,
+              void* out, float* lse, void* workspace, size_t ws_bytes, void* stream) {
+  using namespace csahca;
+  int rc = check_attend(name, q, ckv, win_kv, win_pos, q_pos, B, Tq, n_h, c, N_c, L, W, dtype, out, k);
+  if (rc != CSAHCA_OK) return rc;
+  if (!topk_idx || k < 1) {
+    set_error("%s: topk_idx must be non-NULL and k >= 1", name);
+    return CSAHCA_EINVAL;
+  }
+  if (!(scale > 0.f) || scale != scale) {
+    set_error("%s: scale must be > 0", name);
+    return CSAHCA_EINVAL;
+  }
+  return attend_impl(name, true, q, ckv, topk_idx, win_kv, win_pos, q_pos, 1, B, Tq, n_h, c, N_c, k,
+                     L, W, scale, sink, dtype, out, lse, workspace, ws_bytes, (hipStream_t)stream);
+}
+
+int hca_entry(const char* name, const void* q, const void* ckv, const void* win_kv,
+              const int* win_pos, const int* q_pos, int m, int B, int Tq, int n_h, int c, int N_h,
+              int L, int W, float scale, const float* sink, int dtype, void* out, float* lse,
+              void* workspace, size_t ws_bytes, void* stream) {
+  using namespace csahca;
+  int rc = check_attend(name, q, ckv, win_kv, win_pos, q_pos, B, Tq, n_h, c, N_h, L, W, dtype, out, N_h);
+  if (rc != CSAHCA_OK) return rc;
+  if (m < 1) {
+    set_error("%s: m must be >= 1", name);
+    return CSAHCA_EINVAL;
+  }
+  if (!(scale > 0.f) || scale != scale) {
+    set_error("%s: scale must be > 0", name);
+    return CSAHCA_EINVAL;
+  }
+  return attend_impl(name, false, q, ckv, nullptr, win_kv, win_pos, q_pos, m, B, Tq, n_h, c, N_h, N_h,
+                     L, W, scale, sink, dtype, out, lse, workspace, ws_bytes, (hipStream_t)stream);
+}
+
+}  // namespace
+
 extern "C" int csa_attend(const void* q, const void* ckv, const int* topk_idx,
                           const void* win_kv, const int* win_pos, const int* q_pos, int B,
                           int Tq, int n_h, int c, int N_c, int k, int L, int W, float scale,
                           int dtype, void* out, float* lse, void* workspace, size_t ws_bytes,
                           void* stream) {
-  using namespace csahca;
-  int rc = check_attend("csa_attend", q, ckv, win_kv, win_pos, q_pos, B, Tq, n_h, c, N_c, L, W,
-                        dtype, out, k);
-  if (rc != CSAHCA_OK) return rc;
-  if (!topk_idx || k < 1) return fail(CSAHCA_EINVAL, "csa_attend: topk_idx must be non-NULL and k >= 1");
-  if (!(scale > 0.f) || scale != scale) return fail(CSAHCA_EINVAL, "csa_attend: scale must be > 0");
-  return attend_impl("csa_attend", true, q, ckv, topk_idx, win_kv, win_pos, q_pos, 1, B, Tq,
-                     n_h, c, N_c, k, L, W, scale, dtype, out, lse, workspace, ws_bytes,
-                     (hipStream_t)stream);
+  return csa_entry("csa_attend", q, ckv, topk_idx, win_kv, win_pos, q_pos, B, Tq, n_h, c, N_c, k, L,
+                   W, scale, nullptr, dtype, out, lse, workspace, ws_bytes, stream);
 }
 
 extern "C" int hca_attend(const void* q, const void* ckv, const void* win_kv, const int* win_pos,
                           const int* q_pos, int m, int B, int Tq, int n_h, int c, int N_h,
                           int L, int W, float scale, int dtype, void* out, float* lse,
                           void* workspace, size_t ws_bytes, void* stream) {
-  using namespace csahca;
-  int rc = check_attend("hca_attend", q, ckv, win_kv, win_pos, q_pos, B, Tq, n_h, c, N_h, L, W,
-                        dtype, out, N_h);
-  if (rc != CSAHCA_OK) return rc;
-  if (m < 1) return fail(CSAHCA_EINVAL, "hca_attend: m must be >= 1");
-  if (!(scale > 0.f) || scale != scale) return fail(CSAHCA_EINVAL, "hca_attend: scale must be > 0");
-  return attend_impl("hca_attend", false, q, ckv, nullptr, win_kv, win_pos, q_pos, m, B, Tq, n_h,
-                     c, N_h, N_h, L, W, scale, dtype, out, lse, workspace, ws_bytes,
-                     (hipStream_t)stream);
+  return hca_entry("hca_attend", q, ckv, win_kv, win_pos, q_pos, m, B, Tq, n_h, c, N_h, L, W, scale,
+                   nullptr, dtype, out, lse, workspace, ws_bytes, stream);
+}
+
+extern "C" int csa_attend_sink(const void* q, const void* ckv, const int* topk_idx,
+                               const void* win_kv, const int* win_pos, const int* q_pos, int B,
+                               int Tq, int n_h, int c, int N_c, int k, int L, int W, float scale,
+                               const float* sink, int dtype, void* out, float* lse,
+                               void* workspace, size_t ws_bytes, void* stream) {
+  return csa_entry("csa_attend_sink", q, ckv, topk_idx, win_kv, win_pos, q_pos, B, Tq, n_h, c, N_c,
+                   k, L, W, scale, sink, dtype, out, lse, workspace, ws_bytes, stream);
+}
+
+extern "C" int hca_attend_sink(const void* q, const void* ckv, const void* win_kv,
+                               const int* win_pos, const int* q_pos, int m, int B, int Tq,
+                               int n_h, int c, int N_h, int L, int W, float scale,
+                               const float* sink, int dtype, void* out, float* lse,
+                               void* workspace, size_t ws_bytes, void* stream) {
+  return hca_entry("hca_attend_sink", q, ckv, win_kv, win_pos, q_pos, m, B, Tq, n_h, c, N_h, L, W,
+                   scale, sink, dtype, out, lse, workspace, ws_bytes, stream);
 }

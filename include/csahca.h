@@ -209,6 +209,30 @@ int hca_attend(const void* q, const void* ckv, const void* win_kv, const int* wi
                float scale, int dtype, void* out, float* lse, void* workspace,
                size_t ws_bytes, void* stream);
 
+/*
+ * csa_attend_sink / hca_attend_sink -- csa_attend / hca_attend with a per-head attention
+ * sink.
+ * Source: "DeepSeek-V4 Hybrid Attention: CSA, HCA, mHC, MoE", section IV (a learnable
+ * attention sink per head, inside both branches).  Reading: the sink is a logit in the
+ * units of scale * q.row that joins the softmax denominator and adds no value:
+ *
+ *   out[b,t,h] = sum_r e^{z_r} row_r / (e^{sink[h]} + sum_r e^{z_r}),  z_r = scale*q.row_r
+ *   lse[b,t,h] = log(e^{sink[h]} + sum_r e^{z_r})
+ *
+ *   sink   [n_h] float32, device; NULL gives the plain call, an entry of -inf has no
+ *          effect.
+ * Every other argument, the limits and the errors are those of csa_attend / hca_attend
+ * (same workspace size).
+ */
+int csa_attend_sink(const void* q, const void* ckv, const int* topk_idx, const void* win_kv,
+                    const int* win_pos, const int* q_pos, int B, int Tq, int n_h, int c,
+                    int N_c, int k, int L, int W, float scale, const float* sink, int dtype,
+                    void* out, float* lse, void* workspace, size_t ws_bytes, void* stream);
+int hca_attend_sink(const void* q, const void* ckv, const void* win_kv, const int* win_pos,
+                    const int* q_pos, int m, int B, int Tq, int n_h, int c, int N_h, int L,
+                    int W, float scale, const float* sink, int dtype, void* out, float* lse,
+                    void* workspace, size_t ws_bytes, void* stream);
+
 /* Message for the last non-OK status returned on the calling thread ("" if none). */
 const char* csahca_last_error(void);
 

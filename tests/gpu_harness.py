@@ -76,7 +76,7 @@ def run_index(qI, w, KI, q_pos, m, k, idx_dtype, split=False):
     return idx, sc, alls
 
 
-def run_csa_attend(Q, C, topk, win, win_pos, q_pos, W, dtype, scale=None, lse=True):
+def run_csa_attend(Q, C, topk, win, win_pos, q_pos, W, dtype, scale=None, lse=True, sink=None):
     B, Tq, n_h, c = Q.shape
     N_c = C.shape[1]
     k = topk.shape[2]
@@ -86,12 +86,16 @@ def run_csa_attend(Q, C, topk, win, win_pos, q_pos, W, dtype, scale=None, lse=Tr
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=DEV)
     out = empty((B, Tq, n_h, c), dtype)
     l = torch.empty((B, Tq, n_h), dtype=torch.float32, device=DEV) if lse else None
-    lib.csa_attend(Q, C, topk, win, win_pos, q_pos, B, Tq, n_h, c, N_c, k, L, W, scale, dtype,
-                   out, l, ws, ws_bytes)
+    if sink is None:
+        lib.csa_attend(Q, C, topk, win, win_pos, q_pos, B, Tq, n_h, c, N_c, k, L, W, scale, dtype,
+                       out, l, ws, ws_bytes)
+    else:
+        lib.csa_attend_sink(Q, C, topk, win, win_pos, q_pos, B, Tq, n_h, c, N_c, k, L, W, scale, sink,
+                            dtype, out, l, ws, ws_bytes)
     return out, l
 
 
-def run_hca_attend(Q, C, win, win_pos, q_pos, m, W, dtype, scale=None, lse=True):
+def run_hca_attend(Q, C, win, win_pos, q_pos, m, W, dtype, scale=None, lse=True, sink=None):
     B, Tq, n_h, c = Q.shape
     N_h = C.shape[1]
     L = win.shape[1]
@@ -100,6 +104,10 @@ def run_hca_attend(Q, C, win, win_pos, q_pos, m, W, dtype, scale=None, lse=True)
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=DEV)
     out = empty((B, Tq, n_h, c), dtype)
     l = torch.empty((B, Tq, n_h), dtype=torch.float32, device=DEV) if lse else None
-    lib.hca_attend(Q, C, win, win_pos, q_pos, m, B, Tq, n_h, c, N_h, L, W, scale, dtype, out, l,
-                   ws, ws_bytes)
+    if sink is None:
+        lib.hca_attend(Q, C, win, win_pos, q_pos, m, B, Tq, n_h, c, N_h, L, W, scale, dtype, out, l,
+                       ws, ws_bytes)
+    else:
+        lib.hca_attend_sink(Q, C, win, win_pos, q_pos, m, B, Tq, n_h, c, N_h, L, W, scale, sink, dtype,
+                            out, l, ws, ws_bytes)
     return out, l

@@ -121,6 +121,12 @@ def test_attend_validation():
     # float32 path limits
     assert L.hca_attend(FAKE, FAKE, FAKE, FAKE, FAKE, 128, B, Tq, 8, 512, 1024, 4096, W, 0.1, 0,
                         FAKE, None, FAKE, wh, None) == ENOTSUP
+    # the sink variants check the same arguments (the sink itself may be NULL)
+    assert L.csa_attend_sink(*base, 0.04, FAKE, 1, FAKE, None, FAKE, ws - 1, None) == EWORKSPACE
+    assert L.csa_attend_sink(*base, -1.0, None, 1, FAKE, None, FAKE, ws, None) == EINVAL
+    assert "csa_attend_sink" in lib.last_error()
+    assert L.hca_attend_sink(*hbad, 0.04, FAKE, 1, FAKE, None, FAKE, wh, None) == EINVAL
+    assert L.hca_attend_sink(*hb, 0.04, FAKE, 2, FAKE, None, FAKE, wh, None) == ENOTSUP
 
 
 def test_binding_raises_with_message():

@@ -76,7 +76,7 @@ def check_index(prob, q_pos, k, idx, sc, alls):
             assert np.all(np.isneginf(sc[b, t, keff:]))
 
 
-def check_attend(Qc, dtype, rows_fn, gpu_out, gpu_lse, scale):
+def check_attend(Qc, dtype, rows_fn, gpu_out, gpu_lse, scale, sink=None):
     """rows_fn(b, t) -> fp64 row set for that query (from the GPU-consumed bytes)."""
     Q = oracle.decode(Qc, dtype)
     B, Tq = Q.shape[:2]
@@ -88,7 +88,7 @@ def check_attend(Qc, dtype, rows_fn, gpu_out, gpu_lse, scale):
     for b in range(B):
         for t in range(Tq):
             rows = rows_fn(b, t)
-            ref[b, t], ref_lse[b, t] = oracle.attend(Q[b, t], rows, scale)
+            ref[b, t], ref_lse[b, t] = oracle.attend(Q[b, t], rows, scale, sink)
             if dtype != F32 and rows.shape[0]:
                 # the same softmax weights applied to |rows|: scale of the bf16 rounding of P
                 wts = np.exp(scale * Q[b, t] @ rows.T - ref_lse[b, t][:, None])
@@ -132,8 +132,9 @@ def small_cases():
 CASES = small_cases()
 
 
-def run_chain(cfg, split_index=False, W=None):
-    """Run every stage on the GPU and check each against the oracle; return outputs."""
+def run_chain(cfg, split_index=False, W=None, sink=None):
+    """Run every stage on the GPU and check each against the oracle; return outputs.
+    sink: optional [n_h] float32 attention sink for both attention calls."""
     prob = make_problem(cfg)
     W = cfg.W if W is None else W
     B, c, dt = cfg.B, cfg.c, cfg.dtype
@@ -163,7 +164,8 @@ def run_chain(cfg, split_index=False, W=None):
             idx, sc, alls = H.run_index(qI, w, KI, q_pos, m, cfg.k, cfg.idx_dtype, split=split_index)
             check_index(prob, q_pos_h, cfg.k, idx, sc, alls)
             idx_h = idx.cpu().numpy()
-            out, lse = H.run_csa_attend(Q, C, idx, X, win_pos, q_pos, W, dt)
+            out, lse = H.run_csa_attend(Q, C, idx, X, win_pos, q_pos, W, dt,
+                                        sink=None if sink is None else H.to_dev(sink))
             rows = lambda b, t: oracle.csa_rows(Ch[b], idx_h[b, t], Xd[b], 0, int(q_pos_h[b]) + t, W)
             results["csa_idx"] = idx_h
             if "plant_positions" in prob:
@@ -172,9 +174,10 @@ def run_chain(cfg, split_index=False, W=None):
         else:
             if C.shape[1] == 0:
                 continue
-            out, lse = H.run_hca_attend(Q, C, X, win_pos, q_pos, m, W, dt)
+            out, lse = H.run_hca_attend(Q, C, X, win_pos, q_pos, m, W, dt,
+                                        sink=None if sink is None else H.to_dev(sink))
             rows = lambda b, t: oracle.hca_rows(Ch[b], m, Xd[b], 0, int(q_pos_h[b]) + t, W)
-        check_attend(prob[f"Q_{layer}"], dt, rows, out, lse, scale)
+        check_attend(prob[f"Q_{layer}"], dt, rows, out, lse, scale, sink)
         results[f"{layer}_out"] = out.cpu().numpy()
         results[f"{layer}_lse"] = lse.cpu().numpy()
         results[f"{layer}_C"] = C.cpu().numpy()
@@ -187,6 +190,28 @@ def test_chain_parity(name):
     res = run_chain(CASES[name])
     if "planted_recall" in res:
         print(f"planted recall {res['planted_recall']:.3f}")
+
+
+@pytest.mark.parametrize("name", ["cfg1_tiny_fp32", "hca_h64_ragged", "csa_h128_k1024",
+                                  "prefill_small", "prefill_from_zero", "pair_h128"])
+def test_attention_sink(name):
+    """csa_attend_sink / hca_attend_sink against the oracle's sink: per-head logits of
+    both signs, one dominating the rows and one at -inf (no effect)."""
+    print(f"[sink {name}]", flush=True)
+    cfg = CASES[name]
+    rng = np.random.default_rng(41)
+    sink = (rng.standard_normal(cfg.n_h) * 3).astype(np.float32)
+    sink[0] = 30.0
+    sink[-1] = -np.inf
+    run_chain(cfg, sink=sink)
+
+
+def test_sink_of_minus_inf_changes_no_bit():
+    cfg = CASES["pair_h128"]
+    a = run_chain(cfg)
+    b = run_chain(cfg, sink=np.full(cfg.n_h, -np.inf, dtype=np.float32))
+    for key in ("csa_out", "hca_out", "csa_lse", "hca_lse"):
+        assert np.array_equal(a[key], b[key]), key
 
 
 def test_split_index_equals_fused():

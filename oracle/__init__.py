@@ -9,12 +9,14 @@ Parity status: every function here is pinned by a CPU test against values printe
 the pages or against closed forms and brute force (see ``tests/test_oracle_pins.py``).
 """
 from .csahca import (  # noqa: F401
+    E2M1_TABLE,
     E4M3FN_TABLE,
     attend,
     csa_rows,
     decode,
     decode_bf16,
     decode_e4m3fn,
+    decode_mxfp4,
     entry_counts,
     hca_rows,
     index_scores,

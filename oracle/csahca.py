@@ -59,6 +59,35 @@ def decode_e4m3fn(u8):
     return v
 
 
+def _build_e2m1_table():
+    """Value of each OCP FP4 E2M1 code: bias 1, 1 mantissa bit, subnormal at E = 0."""
+    t = np.empty(16, dtype=np.float64)
+    for code in range(16):
+        sign = -1.0 if code & 0x8 else 1.0
+        e = (code >> 1) & 0x3
+        mant = code & 0x1
+        t[code] = sign * ((mant / 2.0) if e == 0 else (1.0 + mant / 2.0) * 2.0 ** (e - 1))
+    return t
+
+
+E2M1_TABLE = _build_e2m1_table()
+
+
+def decode_mxfp4(packed, scales):
+    """OCP MX FP4: packed [..., K/2] bytes (two E2M1 elements each, the first in the low
+    nibble) and scales [..., K/32] E8M0 bytes (2^(s - 127), one per 32 elements; 255 is
+    NaN).  Returns [..., K] fp64."""
+    p = np.asarray(packed, dtype=np.uint8)
+    sc = np.asarray(scales, dtype=np.uint8)
+    if np.any(sc == 255):
+        raise ValueError("E8M0 NaN scale in an input")
+    el = np.stack([p & 0xF, p >> 4], axis=-1).reshape(p.shape[:-1] + (p.shape[-1] * 2,))
+    v = E2M1_TABLE[el]
+    K = v.shape[-1]
+    mult = np.exp2(sc.astype(np.float64) - 127.0)
+    return (v.reshape(v.shape[:-1] + (K // 32, 32)) * mult[..., None]).reshape(v.shape)
+
+
 def decode(arr, dtype):
     if dtype == F32:
         return np.asarray(arr, dtype=np.float32).astype(np.float64)

@@ -381,6 +381,54 @@ def test_e4m3fn_roundtrip_and_rounding():
     assert np.all(np.abs(dec - x) <= np.abs(nearest - x) + 0)
 
 
+def test_e2m1_known_codes():
+    """OCP FP4 E2M1: bias 1, one mantissa bit; codes 0..7 are 0, 0.5, 1, 1.5, 2, 3, 4, 6
+    and bit 3 is the sign."""
+    mags = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    want = np.array(mags + [-v for v in mags])
+    np.testing.assert_array_equal(oracle.E2M1_TABLE, want)
+
+
+def test_mxfp4_packing_and_scales():
+    """Two elements per byte, the first in the low nibble; E8M0 scale s is 2^(s - 127)."""
+    packed = np.zeros((1, 16), dtype=np.uint8)
+    packed[0, 0] = 0x21                      # element 0 = code 1 (0.5), element 1 = code 2 (1.0)
+    packed[0, 15] = 0xF7                     # element 30 = 6, element 31 = -6
+    v = oracle.decode_mxfp4(packed, np.array([[127]], dtype=np.uint8))
+    assert v.shape == (1, 32)
+    assert (v[0, 0], v[0, 1], v[0, 30], v[0, 31]) == (0.5, 1.0, 6.0, -6.0)
+    assert np.all(v[0, 2:30] == 0)
+    np.testing.assert_array_equal(oracle.decode_mxfp4(packed, np.array([[128]], np.uint8)), 2 * v)
+    np.testing.assert_array_equal(oracle.decode_mxfp4(packed, np.array([[120]], np.uint8)), v / 128)
+    with pytest.raises(ValueError):
+        oracle.decode_mxfp4(packed, np.array([[255]], np.uint8))
+
+
+def test_mxfp4_roundtrip_and_rounding():
+    from synthgen.codecs import f32_to_mxfp4
+    rng = np.random.default_rng(9)
+    # representable blocks: decoding, encoding and decoding again gives the same values
+    p = rng.integers(0, 256, size=(50, 64), dtype=np.uint8)
+    sc = rng.integers(100, 150, size=(50, 4)).astype(np.uint8)
+    v = oracle.decode_mxfp4(p, sc)
+    p2, s2 = f32_to_mxfp4(v.astype(np.float32))
+    np.testing.assert_array_equal(oracle.decode_mxfp4(p2, s2), v)
+    # the block scale puts the largest magnitude in [4, 8): error within one 2^X step
+    x = rng.standard_normal((200, 128)) * np.exp2(rng.integers(-6, 6, size=(200, 1)))
+    p3, s3 = f32_to_mxfp4(x.astype(np.float32))
+    q = oracle.decode_mxfp4(p3, s3)
+    step = np.repeat(np.exp2(s3.astype(float) - 127.0), 32, axis=1)
+    assert np.all(np.abs(q - x.astype(np.float32)) <= 2.0 * step)
+    amax = np.abs(x.astype(np.float32)).reshape(200, 4, 32).max(-1)
+    assert np.all((amax / np.exp2(s3.astype(float) - 127.0) >= 4) & (amax / np.exp2(s3.astype(float) - 127.0) < 8))
+    # ties go to the even code: 1.25 -> 1.0, 1.75 -> 2.0, 5.0 -> 4.0 (block max 6 -> unit scale)
+    t = np.zeros((1, 32), np.float32)
+    t[0, :4] = [1.25, 1.75, 5.0, 6.0]
+    pt, st = f32_to_mxfp4(t)
+    assert st[0, 0] == 127
+    np.testing.assert_array_equal(oracle.decode_mxfp4(pt, st)[0, :4], [1.0, 2.0, 4.0, 6.0])
+
+
 def test_bf16_roundtrip_and_rounding():
     rng = np.random.default_rng(1)
     x = rng.normal(size=10000).astype(np.float32)

@@ -48,6 +48,8 @@ def parse():
                     help="rocprofv3 --pmc output folders: write the traffic record and exit")
     ap.add_argument("--traffic-out", default=PROFILE_TRAFFIC,
                     help="where --traffic-from writes its record")
+    ap.add_argument("--fp4-keys", action="store_true",
+                    help="indexer keys in MX FP4 (E2M1 + E8M0 per 32) instead of FP8")
     ap.add_argument("--sink", action="store_true",
                     help="run both attention calls with a per-head attention sink "
                          "(csa_attend_sink / hca_attend_sink)")
@@ -92,8 +94,12 @@ class Workload:
             base[f"C_{l}"] = C
             base[f"Q_{l}"] = prob[f"Q_{l}"]
         if "csa" in self.layers:
-            for key in ("qI", "w", "KI"):
+            for key in ("qI", "w"):
                 base[key] = prob[key]
+            if "KI_scales" in prob:  # MX FP4 keys: all packed rows, then all scales
+                base["KI"] = torch.cat([prob["KI"].reshape(-1), prob["KI_scales"].reshape(-1)])
+            else:
+                base["KI"] = prob["KI"]
         torch.cuda.synchronize()
         # replicas of everything a step reads (distinct memory, same values)
         self.rep = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(replicas - 1)]
@@ -197,7 +203,7 @@ class Workload:
         qpos = [n - Tq + t for t in range(Tq)]
         if "csa" in self.layers:
             V = [min(self.N_c, (p + 1) // cfg.m) for p in qpos]
-            ki = B * max(V) * cfg.c_I  # keys are shared by a sequence's queries
+            ki = B * max(V) * self.key_row_bytes()  # keys are shared by a sequence's queries
             idx = B * Tq * (cfg.n_ih * cfg.c_I + cfg.n_ih * 4 + cfg.k * 4)
             detail["index"] = ki + idx
             total += ki + idx
@@ -222,7 +228,12 @@ class Workload:
         cfg = self.cfg
         qpos = [self.n - self.Tq + t for t in range(self.Tq)]
         V = max(min(self.N_c, (p + 1) // cfg.m) for p in qpos)
-        return cfg.B * V * cfg.c_I + cfg.B * self.Tq * cfg.n_ih * (cfg.c_I + 4)
+        return cfg.B * V * self.key_row_bytes() + cfg.B * self.Tq * cfg.n_ih * (cfg.c_I + 4)
+
+    def key_row_bytes(self):
+        """Bytes of one indexer key: c_I codes, or for MX FP4 c_I/2 plus a scale per 32."""
+        c_I = self.cfg.c_I
+        return c_I // 2 + c_I // 32 if self.cfg.idx_dtype == 3 else c_I
 
     def flops(self):
         cfg = self.cfg
@@ -351,9 +362,13 @@ def cpu_baseline(wl, seconds):
             d[f"C_{l}"] = C
             d[f"Q_{l}"] = oracle.decode(codes(prob[f"Q_{l}"][b, 0]), BF16)
         if "csa" in wl.layers:
-            d["qI"] = oracle.decode(codes(prob["qI"][b, 0]), cfg.idx_dtype)
+            f4 = cfg.idx_dtype == 3
+            d["qI"] = oracle.decode(codes(prob["qI"][b, 0]), 2 if f4 else cfg.idx_dtype)
             d["w"] = prob["w"][b, 0].cpu().numpy()
-            d["KI"] = oracle.decode(codes(prob["KI"][b]), cfg.idx_dtype)
+            if f4:
+                d["KI"] = oracle.decode_mxfp4(codes(prob["KI"][b]), codes(prob["KI_scales"][b]))
+            else:
+                d["KI"] = oracle.decode(codes(prob["KI"][b]), cfg.idx_dtype)
         seqs.append(d)
 
     done = 0
@@ -498,6 +513,11 @@ def main():
         calibrate_copy()
         return
     cfg = CONFIGS[args.config]
+    if args.fp4_keys:
+        if cfg.idx_dtype != 2:
+            print("--fp4-keys needs a config with an FP8 indexer", file=sys.stderr)
+            sys.exit(2)
+        cfg = cfg.scaled(idx_dtype=3)
     if args.overlap_pool:
         overlap_pool(cfg, args.steps or 10, min(args.cpu_seconds, 10.0), args.no_cpu_baseline)
         return
@@ -556,6 +576,8 @@ def main():
         kb = wl.index_score_bytes()
         ach = kb / dur / 1e9
         kname = "index_score_dec128" if decode and cfg.c_I == 128 else "index_score_fp8"
+        if cfg.idx_dtype == 3:
+            kname += " (MX FP4 keys)"  # no counter record for this instance
         roofline = {"kernel": kname, "bound": "hbm", "achieved": round(ach, 1),
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
                     "traffic": read_traffic(kname) if decode else None,
@@ -582,7 +604,8 @@ def main():
                    "c": cfg.c, "n_h": cfg.n_h, "m": cfg.m, "m_hca": cfg.m_hca, "k": cfg.k,
                    "n_ih": cfg.n_ih, "c_I": cfg.c_I, "window": cfg.W, "replicas": R,
                    "timing": "hip graph per step, rotating replicas",
-                   **({"attention_sink": "per-head, N(0, 2^2)"} if args.sink else {})},
+                   **({"attention_sink": "per-head, N(0, 2^2)"} if args.sink else {}),
+                   **({"indexer_keys": "MX FP4 (E2M1, E8M0 per 32), FP8 queries"} if args.fp4_keys else {})},
         "hbm_gbs": round(abytes / sec / 1e9, 1),
         "hbm_frac": round(abytes / sec / 1e9 / HBM_PEAK_GBS, 4),
         "algorithmic_bytes_per_step": abytes,

@@ -48,6 +48,20 @@ struct KeyOperand<128> {  // one v_mfma_scale_f32_16x16x128_f8f6f4 per head bloc
   }
 };
 
+// MX FP4 keys (c_I = 128): the B operand is the lane's 32 E2M1 elements (16 bytes, the
+// low 4 registers; the instruction reads no more for FP4) and its 32-element block's E8M0
+// scale; the queries stay FP8 with unit scale.  With an FP8 A and an FP4 B operand the
+// instruction does not take K in the same order from both: when lane group g of B holds
+// key elements [32g, 32g+32) (one scale block, so one scale per lane), lane group g of A
+// supplies dimensions [16g, 16g+16) in its first 16 bytes and [64+16g, 80+16g) in its
+// last 16.  The queries are loaded in that order.
+// (Found with one-hot queries against random keys; the parity tests pin it.)
+CSAHCA_DEV f32x4 mma_fp8_fp4(const i32x8& a, const u32x4& b, uint32_t scale_b, f32x4 c) {
+  const i32x8 bv = i32x8{(int)b[0], (int)b[1], (int)b[2], (int)b[3], 0, 0, 0, 0};
+  // formats: A 0 = FP8 E4M3, B 4 = FP4 E2M1; A scale 127 = 2^0, B scale from the lane
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bv, c, 0, 4, 0, 127, 0, (int)scale_b);
+}
+
 template <int C_I>
 struct KeyOperand {  // C_I in {32, 64}: v_mfma_f32_16x16x32_fp8_fp8, C_I/32 K-steps
   static constexpr int KS = C_I / 32;
@@ -223,12 +237,16 @@ CSAHCA_DEV void wait_vm_le(int n) {
   }
 }
 
-template <int HB>
+template <int HB, bool F4>
 __global__ __launch_bounds__(256, 2) void index_score_dec128(
     const uint8_t* __restrict__ qI, const float* __restrict__ w, const uint8_t* __restrict__ KI,
+    const uint8_t* __restrict__ KS,
     const int* __restrict__ q_pos, int m, int N_c, int CH, int NG, float* __restrict__ scores,
     uint32_t* __restrict__ gkeys) {
-  constexpr int C_I = 128, NIH = HB * 16, BLKB = GROUP * C_I;
+  constexpr int C_I = 128, NIH = HB * 16;
+  // a block of 16 keys: FP8 rows of 128 bytes, or FP4 rows of 64 bytes followed by a
+  // 256-byte slot whose first 64 bytes are the 16 keys' four E8M0 scales each
+  constexpr int KRB = F4 ? C_I / 2 : C_I, BLKB = GROUP * KRB + (F4 ? 256 : 0);
   __shared__ __attribute__((aligned(16))) uint8_t ring[4][RING][BLKB];
   __shared__ __attribute__((aligned(16))) uint8_t s_q[NIH * C_I];
   __shared__ float s_w[cdiv(NIH, 64) * 64];
@@ -250,18 +268,32 @@ __global__ __launch_bounds__(256, 2) void index_score_dec128(
   int nmine = 0, e_last = e_lim - 1;
   auto count_mine = [&](int nblk) { return nblk > wave ? cdiv(nblk - wave, 4) : 0; };
   nmine = count_mine(cdiv(e_lim - e_begin, GROUP));
-  const uint8_t* kb = KI + (size_t)q * N_c * C_I;
-  // in each 1 KiB half of a block: lane l moves row l/8, chunk (l%8) ^ (l/8)
-  const int dma_row = lane >> 3, dma_chunk = (lane & 7) ^ (lane >> 3);
+  const uint8_t* kb = KI + (size_t)q * N_c * KRB;
+  const uint8_t* ksb = KS + (size_t)q * N_c * 4;  // FP4: four scale bytes per key
+  // FP8, in each 1 KiB half of a block: lane l moves row l/8, chunk (l%8) ^ (l/8).
+  // FP4: lane l moves row l/4, chunk l%4 (the 1 KiB is read back whole, conflict-free),
+  // and lanes 0..15 move the scale words of rows 0..15 (the others repeat row 15).
+  const int dma_row = F4 ? lane >> 2 : lane >> 3;
+  const int dma_chunk = F4 ? lane & 3 : (lane & 7) ^ (lane >> 3);
   auto issue = [&](int k) {
     const int e0 = e_begin + (wave + 4 * min(k, nmine - 1)) * GROUP;
     uint8_t* dst = ring[wave][k % RING];
+    if constexpr (F4) {
+      const int e = min(e0 + dma_row, e_last);
+      __builtin_amdgcn_global_load_lds(kb + (size_t)e * KRB + dma_chunk * 16,
+                                       (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+      const int es = min(e0 + min(lane, GROUP - 1), e_last);
+      __builtin_amdgcn_global_load_lds(ksb + (size_t)es * 4,
+                                       (__attribute__((address_space(3))) void*)(dst + GROUP * KRB),
+                                       4, 0, 0);
+    } else {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int e = min(e0 + 8 * h + dma_row, e_last);
-      __builtin_amdgcn_global_load_lds(kb + (size_t)e * C_I + dma_chunk * 16,
-                                       (__attribute__((address_space(3))) void*)(dst + h * 1024),
-                                       16, 0, 0);
+      for (int h = 0; h < 2; ++h) {
+        const int e = min(e0 + 8 * h + dma_row, e_last);
+        __builtin_amdgcn_global_load_lds(kb + (size_t)e * C_I + dma_chunk * 16,
+                                         (__attribute__((address_space(3))) void*)(dst + h * 1024),
+                                         16, 0, 0);
+      }
     }
   };
   // The query's indexer vectors and head weights come by DMA too, ahead of the key
@@ -290,9 +322,9 @@ __global__ __launch_bounds__(256, 2) void index_score_dec128(
   float wr[HB][4];
 #pragma unroll
   for (int hb = 0; hb < HB; ++hb) {
-    const uint8_t* qr = s_q + (hb * 16 + row) * C_I + g * 32;
-    const u32x4 lo = *reinterpret_cast<const u32x4*>(qr);
-    const u32x4 hi = *reinterpret_cast<const u32x4*>(qr + 16);
+    const uint8_t* qr = s_q + (hb * 16 + row) * C_I;
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(qr + (F4 ? 16 * g : 32 * g));
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(qr + (F4 ? 64 + 16 * g : 32 * g + 16));
     a[hb].v = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
 #pragma unroll
     for (int i = 0; i < 4; ++i) wr[hb][i] = s_w[hb * 16 + 4 * g + i];
@@ -305,20 +337,28 @@ __global__ __launch_bounds__(256, 2) void index_score_dec128(
   }
   const int nmine_lim = nmine;
   nmine = count_mine(cdiv(e_end - e_begin, GROUP));
-  // reader offsets of this lane's 32 bytes (chunks 2g, 2g+1 of row `row`)
-  const int rd0 = (row * 8 + ((2 * g) ^ (row & 7))) * 16;
-  const int rd1 = (row * 8 + ((2 * g + 1) ^ (row & 7))) * 16;
+  // reader offsets of this lane's 32 bytes (chunks 2g, 2g+1 of row `row`); FP4: its 16
+  // bytes (elements 32g .. 32g+31 of row `row`) and its block's scale byte
+  const int rd0 = F4 ? row * KRB + g * 16 : (row * 8 + ((2 * g) ^ (row & 7))) * 16;
+  const int rd1 = F4 ? GROUP * KRB + row * 4 + g : (row * 8 + ((2 * g + 1) ^ (row & 7))) * 16;
   for (int k = 0; k < nmine; ++k) {
     // blocks k+1 .. min(nmine_lim, k+RING-1)-1 may stay in flight
     wait_vm_le<RING - 2>(min(nmine_lim, k + RING - 1) - 1 - k);
     const uint8_t* blk = ring[wave][k % RING];
-    KeyOperand<C_I> kf;
-    const u32x4 lo = *reinterpret_cast<const u32x4*>(blk + rd0);
-    const u32x4 hi = *reinterpret_cast<const u32x4*>(blk + rd1);
-    kf.v = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
     f32x4 acc[HB];
+    if constexpr (F4) {
+      const u32x4 kv = *reinterpret_cast<const u32x4*>(blk + rd0);
+      const uint32_t ks = blk[rd1];
 #pragma unroll
-    for (int hb = 0; hb < HB; ++hb) acc[hb] = KeyOperand<C_I>::mma(a[hb], kf, f32x4{0.f, 0.f, 0.f, 0.f});
+      for (int hb = 0; hb < HB; ++hb) acc[hb] = mma_fp8_fp4(a[hb].v, kv, ks, f32x4{0.f, 0.f, 0.f, 0.f});
+    } else {
+      KeyOperand<C_I> kf;
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(blk + rd0);
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(blk + rd1);
+      kf.v = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) acc[hb] = KeyOperand<C_I>::mma(a[hb], kf, f32x4{0.f, 0.f, 0.f, 0.f});
+    }
     // slot (k-1) % RING was read in the previous iteration: refill it
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     if (k + RING - 1 < nmine_lim) issue(k + RING - 1);
@@ -372,12 +412,17 @@ constexpr int PRE_STG = 64;
 constexpr int PRE_NSTG = 4;
 constexpr int PRE_KEYS = 8192;
 
-template <int HB>
+template <int HB, bool F4>
 __global__ __launch_bounds__(256, HB >= 8 ? 2 : 4) void index_score_pre128(
     const uint8_t* __restrict__ qI, const float* __restrict__ w, const uint8_t* __restrict__ KI,
+    const uint8_t* __restrict__ KS,
     const int* __restrict__ q_pos, int m, int Tq, int N_c, int NG, float* __restrict__ scores,
     uint32_t* __restrict__ gkeys) {
-  constexpr int C_I = 128, NIH = HB * 16, STGB = PRE_STG * C_I, NBS = PRE_STG / GROUP;
+  // a stage: FP8 rows of 128 bytes, or FP4 rows of 64 bytes then one 256-byte slot per
+  // wave whose first 64 bytes hold the wave's 16 keys' four E8M0 scales each (a 4-byte
+  // row DMA writes all 64 lanes; the rest of the slot takes repeats)
+  constexpr int C_I = 128, NIH = HB * 16, NBS = PRE_STG / GROUP;
+  constexpr int KRB = F4 ? C_I / 2 : C_I, STGB = PRE_STG * KRB + (F4 ? 4 * 256 : 0);
   static_assert(NBS == 4, "the reduce-scatter spreads four blocks over the four row groups");
   __shared__ __attribute__((aligned(16))) uint8_t ring[PRE_NSTG][STGB];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -404,24 +449,46 @@ __global__ __launch_bounds__(256, HB >= 8 ? 2 : 4) void index_score_pre128(
   const uint8_t* qp = qI + (size_t)q * NIH * C_I;
 #pragma unroll
   for (int hb = 0; hb < HB; ++hb) {
-    a[hb].load(qp + (hb * 16 + row) * C_I + g * 32);
+    if constexpr (F4) {
+      const uint8_t* qr = qp + (hb * 16 + row) * C_I;
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(qr + 16 * g);
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(qr + 64 + 16 * g);
+      a[hb].v = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    } else {
+      a[hb].load(qp + (hb * 16 + row) * C_I + g * 32);
+    }
     wr[hb] = *reinterpret_cast<const f32x4*>(w + (size_t)q * NIH + hb * 16 + 4 * g);
   }
 
   // stage s: rows e_begin + 64*s + r; wave w moves the 1 KiB pieces w and w + 4 (rows
   // 8p .. 8p+7); in a piece lane l moves row l/8, 16-byte chunk (l%8) ^ (l/8), so that a
   // reader of 32 bytes of its row hits eight distinct bank groups per eight lanes
-  const uint8_t* kb = KI + (size_t)b * N_c * C_I;
-  const int dma_row = lane >> 3, dma_chunk = (lane & 7) ^ (lane >> 3);
+  const uint8_t* kb = KI + (size_t)b * N_c * KRB;
+  const uint8_t* ksb = KS + (size_t)b * N_c * 4;
+  // FP4: wave w moves the 1 KiB of rows 16w .. 16w+15 (lane l: row l/4, chunk l%4) and
+  // lanes 0..15 the scale words of the same rows
+  const int dma_row = F4 ? lane >> 2 : lane >> 3;
+  const int dma_chunk = F4 ? lane & 3 : (lane & 7) ^ (lane >> 3);
   auto issue = [&](int st) {
     uint8_t* dst = ring[st % PRE_NSTG];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int p = wave + 4 * h;
-      const int e = min(e_begin + st * PRE_STG + 8 * p + dma_row, N_c - 1);
-      __builtin_amdgcn_global_load_lds(kb + (size_t)e * C_I + dma_chunk * 16,
-                                       (__attribute__((address_space(3))) void*)(dst + p * 1024),
+    if constexpr (F4) {
+      const int e = min(e_begin + st * PRE_STG + 16 * wave + dma_row, N_c - 1);
+      __builtin_amdgcn_global_load_lds(kb + (size_t)e * KRB + dma_chunk * 16,
+                                       (__attribute__((address_space(3))) void*)(dst + wave * 1024),
                                        16, 0, 0);
+      const int es = min(e_begin + st * PRE_STG + 16 * wave + min(lane, GROUP - 1), N_c - 1);
+      __builtin_amdgcn_global_load_lds(
+          ksb + (size_t)es * 4,
+          (__attribute__((address_space(3))) void*)(dst + PRE_STG * KRB + wave * 256), 4, 0, 0);
+    } else {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int p = wave + 4 * h;
+        const int e = min(e_begin + st * PRE_STG + 8 * p + dma_row, N_c - 1);
+        __builtin_amdgcn_global_load_lds(kb + (size_t)e * C_I + dma_chunk * 16,
+                                         (__attribute__((address_space(3))) void*)(dst + p * 1024),
+                                         16, 0, 0);
+      }
     }
   };
   const int nfill = min(PRE_NSTG - 1, nst);
@@ -443,18 +510,32 @@ __global__ __launch_bounds__(256, HB >= 8 ? 2 : 4) void index_score_pre128(
     asm volatile("s_barrier" ::: "memory");
     if (st + PRE_NSTG - 1 < nst) issue(st + PRE_NSTG - 1);
     const uint8_t* stg = ring[st % PRE_NSTG];
-    KeyOperand<C_I> kf[NBS];
-#pragma unroll
-    for (int u = 0; u < NBS; ++u) {
-      const u32x4 lo = *reinterpret_cast<const u32x4*>(stg + u * (GROUP * C_I) + rd0);
-      const u32x4 hi = *reinterpret_cast<const u32x4*>(stg + u * (GROUP * C_I) + rd1);
-      kf[u].v = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-    }
     f32x4 acc[NBS][HB];
+    if constexpr (F4) {
+      u32x4 kv[NBS];
+      uint32_t ks[NBS];
 #pragma unroll
-    for (int u = 0; u < NBS; ++u)
+      for (int u = 0; u < NBS; ++u) {
+        kv[u] = *reinterpret_cast<const u32x4*>(stg + (u * GROUP + row) * KRB + g * 16);
+        ks[u] = stg[PRE_STG * KRB + u * 256 + row * 4 + g];
+      }
 #pragma unroll
-      for (int hb = 0; hb < HB; ++hb) acc[u][hb] = KeyOperand<C_I>::mma(a[hb], kf[u], f32x4{0.f, 0.f, 0.f, 0.f});
+      for (int u = 0; u < NBS; ++u)
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) acc[u][hb] = mma_fp8_fp4(a[hb].v, kv[u], ks[u], f32x4{0.f, 0.f, 0.f, 0.f});
+    } else {
+      KeyOperand<C_I> kf[NBS];
+#pragma unroll
+      for (int u = 0; u < NBS; ++u) {
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(stg + u * (GROUP * C_I) + rd0);
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(stg + u * (GROUP * C_I) + rd1);
+        kf[u].v = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      }
+#pragma unroll
+      for (int u = 0; u < NBS; ++u)
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) acc[u][hb] = KeyOperand<C_I>::mma(a[hb], kf[u], f32x4{0.f, 0.f, 0.f, 0.f});
+    }
     // this lane's heads (16*hb + 4*g + i) of key `row` of block u
     float pu[NBS];
 #pragma unroll
@@ -528,7 +609,7 @@ __global__ __launch_bounds__(256) void index_score_f32(
 // ---------------------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------------------
-template <int C_I, int HB>
+template <int C_I, int HB, bool F4>
 void launch_fp8(const void* q_idx, const float* w_idx, const void* k_idx, const int* q_pos,
                 int m, int Tq, int N_c, int nq, int NG, float* scores, uint32_t* gkeys,
                 hipStream_t st) {
@@ -543,32 +624,33 @@ void launch_fp8(const void* q_idx, const float* w_idx, const void* k_idx, const 
   const int CH = cdiv(cdiv(N_c, chunks), 64) * 64;
   chunks = cdiv(N_c, CH);
   dim3 grid((unsigned)chunks, (unsigned)qgroups);
+  const uint8_t* KI = (const uint8_t*)k_idx;
+  // MX FP4 keys: [B, N_c, 64] E2M1 rows, then [B, N_c, 4] E8M0 scales
+  const uint8_t* KS = F4 ? KI + (size_t)(nq / Tq) * N_c * (C_I / 2) : nullptr;
   if (decode && C_I == 128)
-    hipLaunchKernelGGL((index_score_dec128<HB>), grid, dim3(256), 0, st, (const uint8_t*)q_idx,
-                       w_idx, (const uint8_t*)k_idx, q_pos, m, N_c, CH, NG, scores, gkeys);
+    hipLaunchKernelGGL((index_score_dec128<HB, F4>), grid, dim3(256), 0, st, (const uint8_t*)q_idx,
+                       w_idx, KI, KS, q_pos, m, N_c, CH, NG, scores, gkeys);
+  else if (C_I == 128)
+    hipLaunchKernelGGL((index_score_pre128<HB, F4>),
+                       dim3((unsigned)(nq / Tq * cdiv(Tq, 4)), (unsigned)cdiv(N_c, PRE_KEYS)), dim3(256), 0, st,
+                       (const uint8_t*)q_idx, w_idx, KI, KS, q_pos, m, Tq, N_c, NG, scores, gkeys);
   else if (decode)
     hipLaunchKernelGGL((index_score_fp8<C_I, HB, 1, 4>), grid, dim3(256), 0, st,
-                       (const uint8_t*)q_idx, w_idx, (const uint8_t*)k_idx, q_pos, m, Tq, N_c,
-                       CH, nq, NG, scores, gkeys);
-  else if (C_I == 128)
-    hipLaunchKernelGGL((index_score_pre128<HB>),
-                       dim3((unsigned)(nq / Tq * cdiv(Tq, 4)), (unsigned)cdiv(N_c, PRE_KEYS)), dim3(256), 0, st,
-                       (const uint8_t*)q_idx, w_idx, (const uint8_t*)k_idx, q_pos, m, Tq, N_c, NG, scores, gkeys);
+                       (const uint8_t*)q_idx, w_idx, KI, q_pos, m, Tq, N_c, CH, nq, NG, scores, gkeys);
   else
     hipLaunchKernelGGL((index_score_fp8<C_I, HB, 4, 4>), grid, dim3(256), 0, st,
-                       (const uint8_t*)q_idx, w_idx, (const uint8_t*)k_idx, q_pos, m, Tq, N_c,
-                       CH, nq, NG, scores, gkeys);
+                       (const uint8_t*)q_idx, w_idx, KI, q_pos, m, Tq, N_c, CH, nq, NG, scores, gkeys);
 }
 
-template <int C_I>
+template <int C_I, bool F4>
 bool launch_fp8_heads(int n_ih, const void* q_idx, const float* w_idx, const void* k_idx,
                       const int* q_pos, int m, int Tq, int N_c, int nq, int NG, float* scores,
                       uint32_t* gkeys, hipStream_t st) {
   switch (n_ih / 16) {
-    case 1: launch_fp8<C_I, 1>(q_idx, w_idx, k_idx, q_pos, m, Tq, N_c, nq, NG, scores, gkeys, st); return true;
-    case 2: launch_fp8<C_I, 2>(q_idx, w_idx, k_idx, q_pos, m, Tq, N_c, nq, NG, scores, gkeys, st); return true;
-    case 4: launch_fp8<C_I, 4>(q_idx, w_idx, k_idx, q_pos, m, Tq, N_c, nq, NG, scores, gkeys, st); return true;
-    case 8: launch_fp8<C_I, 8>(q_idx, w_idx, k_idx, q_pos, m, Tq, N_c, nq, NG, scores, gkeys, st); return true;
+    case 1: launch_fp8<C_I, 1, F4>(q_idx, w_idx, k_idx, q_pos, m, Tq, N_c, nq, NG, scores, gkeys, st); return true;
+    case 2: launch_fp8<C_I, 2, F4>(q_idx, w_idx, k_idx, q_pos, m, Tq, N_c, nq, NG, scores, gkeys, st); return true;
+    case 4: launch_fp8<C_I, 4, F4>(q_idx, w_idx, k_idx, q_pos, m, Tq, N_c, nq, NG, scores, gkeys, st); return true;
+    case 8: launch_fp8<C_I, 8, F4>(q_idx, w_idx, k_idx, q_pos, m, Tq, N_c, nq, NG, scores, gkeys, st); return true;
     default: return false;
   }
 }
@@ -592,11 +674,14 @@ int index_check_common(const void* q_idx, const float* w_idx, const void* k_idx,
       return fail(CSAHCA_ENOTSUP, "indexer: FP8 keys need n_ih % 16 == 0 and n_ih <= 128");
     if (c_I != 32 && c_I != 64 && c_I != 128)
       return fail(CSAHCA_ENOTSUP, "indexer: FP8 keys need c_I in {32, 64, 128}");
+  } else if (idx_dtype == CSAHCA_MXFP4) {
+    if (n_ih % 16 != 0 || n_ih > 128 || c_I != 128)
+      return fail(CSAHCA_ENOTSUP, "indexer: MX FP4 keys need n_ih % 16 == 0, n_ih <= 128, c_I == 128");
   } else if (idx_dtype == CSAHCA_F32) {
     if (n_ih * c_I > 4096)
       return fail(CSAHCA_ENOTSUP, "indexer: float32 keys need n_ih * c_I <= 4096");
   } else {
-    return fail(CSAHCA_ENOTSUP, "indexer: idx_dtype must be CSAHCA_FP8_E4M3FN or CSAHCA_F32");
+    return fail(CSAHCA_ENOTSUP, "indexer: idx_dtype must be CSAHCA_FP8_E4M3FN, CSAHCA_MXFP4 or CSAHCA_F32");
   }
   if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(w_idx))
     return fail(CSAHCA_EINVAL, "indexer: q_idx, w_idx and k_idx must be 16-byte aligned");
@@ -612,10 +697,13 @@ int index_score_impl(const void* q_idx, const float* w_idx, const void* k_idx, i
   const int NG = cdiv(N_c, GROUP);
   if (idx_dtype == CSAHCA_FP8_E4M3FN) {
     bool ok = false;
-    if (c_I == 128) ok = launch_fp8_heads<128>(n_ih, q_idx, w_idx, k_idx, q_pos, m, Tq, N_c, nq, NG, scores, gkeys, st);
-    else if (c_I == 64) ok = launch_fp8_heads<64>(n_ih, q_idx, w_idx, k_idx, q_pos, m, Tq, N_c, nq, NG, scores, gkeys, st);
-    else ok = launch_fp8_heads<32>(n_ih, q_idx, w_idx, k_idx, q_pos, m, Tq, N_c, nq, NG, scores, gkeys, st);
+    if (c_I == 128) ok = launch_fp8_heads<128, false>(n_ih, q_idx, w_idx, k_idx, q_pos, m, Tq, N_c, nq, NG, scores, gkeys, st);
+    else if (c_I == 64) ok = launch_fp8_heads<64, false>(n_ih, q_idx, w_idx, k_idx, q_pos, m, Tq, N_c, nq, NG, scores, gkeys, st);
+    else ok = launch_fp8_heads<32, false>(n_ih, q_idx, w_idx, k_idx, q_pos, m, Tq, N_c, nq, NG, scores, gkeys, st);
     if (!ok) return fail(CSAHCA_ENOTSUP, "indexer: FP8 keys need n_ih in {16, 32, 64, 128}");
+  } else if (idx_dtype == CSAHCA_MXFP4) {
+    if (!launch_fp8_heads<128, true>(n_ih, q_idx, w_idx, k_idx, q_pos, m, Tq, N_c, nq, NG, scores, gkeys, st))
+      return fail(CSAHCA_ENOTSUP, "indexer: MX FP4 keys need n_ih in {16, 32, 64, 128}");
   } else {
     const size_t lds = (size_t)(n_ih * c_I + n_ih) * sizeof(float);
     dim3 grid((unsigned)cdiv(N_c, 256), (unsigned)nq);

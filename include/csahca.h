@@ -54,6 +54,11 @@ extern "C" {
 #define CSAHCA_F32 0
 #define CSAHCA_BF16 1
 #define CSAHCA_FP8_E4M3FN 2 /* OCP FP8: 4 exponent bits (bias 7), 3 mantissa bits, no inf */
+/* Indexer keys in OCP MX FP4 (E2M1 elements: 2 exponent bits, bias 1, 1 mantissa bit;
+ * two per byte, the first in the low nibble; one E8M0 scale byte 2^(s-127) per 32
+ * elements) with FP8 E4M3FN queries (unit scale).  Key layout: all rows
+ * [B, N_c, c_I/2] bytes, then all scales [B, N_c, c_I/32] bytes, in one buffer. */
+#define CSAHCA_MXFP4 3
 
 /* status codes */
 #define CSAHCA_OK 0
@@ -132,15 +137,19 @@ int csa_compress_overlap(const void* kv_a, const void* gate_a, const void* kv_b,
  * -0.0 counts as +0.0.  topk_idx[b,t,:] lists them in ascending index order, followed by
  * k-K entries of -1.
  *
- *   q_idx      [B, Tq, n_ih, c_I] of idx_dtype (CSAHCA_FP8_E4M3FN or CSAHCA_F32).
+ *   q_idx      [B, Tq, n_ih, c_I] of idx_dtype (CSAHCA_FP8_E4M3FN or CSAHCA_F32; FP8 for
+ *              CSAHCA_MXFP4).
  *   w_idx      [B, Tq, n_ih] float32.
- *   k_idx      [B, N_c, c_I] of idx_dtype (the compressed indexer-key cache).
+ *   k_idx      [B, N_c, c_I] of idx_dtype (the compressed indexer-key cache); for
+ *              CSAHCA_MXFP4 the packed rows and then the scales (see the define).
  *   q_pos      [B] int32 device; m = CSA block size of the cache.
  *   topk_idx   [B, Tq, k] int32 (out).
  *   topk_score [B, Tq, k] float32 (out, nullable): the selected scores, -inf on padding.
  *   all_scores [B, Tq, N_c] float32 (out, nullable): every score; entries s >= V are
  *              left unwritten.
- *   Limits: FP8 keys need n_ih in {16, 32, 64, 128} and c_I in {32, 64, 128}; F32 keys
+ *   Limits: FP8 keys need n_ih in {16, 32, 64, 128} and c_I in {32, 64, 128}; MX FP4
+ *   keys n_ih in {16, 32, 64, 128} and c_I = 128 (source: "DeepSeek-V4: Anatomy of an
+ *   Open-Source Frontier Model", the indexer's query-key path trained down to FP4); F32 keys
  *   need n_ih * c_I <= 4096.  1 <= k <= 1024, N_c <= 262144.
  */
 size_t lightning_index_topk_workspace_size(int B, int Tq, int n_ih, int N_c, int k);

@@ -8,7 +8,7 @@ a CSA layer, step by step").
 """
 from dataclasses import dataclass, replace
 
-F32, BF16, FP8 = 0, 1, 2
+F32, BF16, FP8, MXFP4 = 0, 1, 2, 3  # MXFP4: indexer keys only (queries stay FP8)
 
 
 @dataclass(frozen=True)

@@ -8,7 +8,7 @@ conversion happen here.
 """
 import torch
 
-from .configs import BF16, F32, FP8
+from .configs import BF16, F32, FP8, MXFP4
 from .host import layers_of
 
 
@@ -34,6 +34,30 @@ def _normal(gen, shape, std, dtype, device, chunk_rows=1 << 20):
             x.mul_(std)
         flat[r0:r1] = _store(x, dtype)
     return out
+
+
+def _mxfp4(x, chunk_rows=1 << 16):
+    """MX FP4 encoding of float32 rows [..., K] (K % 32 == 0), as ``synthgen.codecs`` defines
+    it: returns (packed uint8 [..., K/2], scales uint8 [..., K/32]).  Nearest value with
+    ties to even: below 2 the grid step is 0.5, below 4 it is 1, above it 2, and torch's
+    round() rounds halves to even, which is the even code on each of these grids."""
+    K = x.shape[-1]
+    flat = x.reshape(-1, K)
+    packed = torch.empty((flat.shape[0], K // 2), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((flat.shape[0], K // 32), dtype=torch.uint8, device=x.device)
+    for r0 in range(0, flat.shape[0], chunk_rows):
+        blk = flat[r0:r0 + chunk_rows].float().reshape(-1, K // 32, 32)
+        amax = blk.abs().amax(-1)
+        _, E = torch.frexp(torch.where(amax > 0, amax, torch.ones_like(amax)))
+        X = torch.where(amax > 0, E - 3, torch.full_like(E, -127)).clamp(-127, 127)
+        v = blk / torch.exp2(X.float())[..., None]
+        a = v.abs().clamp(max=6.0)
+        q = torch.where(a < 2, torch.round(a * 2) / 2, torch.where(a < 4, torch.round(a), torch.round(a / 2) * 2))
+        code = torch.where(q < 2, q * 2, torch.where(q < 4, q + 2, torch.where(q < 5, 6.0, 7.0))).to(torch.uint8)
+        nib = (code | (torch.signbit(v).to(torch.uint8) << 3)).reshape(blk.shape[0], K)
+        packed[r0:r0 + chunk_rows] = nib[:, 0::2] | (nib[:, 1::2] << 4)
+        scales[r0:r0 + chunk_rows] = (X + 127).to(torch.uint8)
+    return packed.reshape(x.shape[:-1] + (K // 2,)), scales.reshape(x.shape[:-1] + (K // 32,))
 
 
 def make_problem_device(cfg, device="cuda"):
@@ -62,7 +86,8 @@ def make_problem_device(cfg, device="cuda"):
         N_c = n_total // cfg.m
         qI = torch.randn((B, Tq, cfg.n_ih, cfg.c_I), generator=gen, device=device)
         w = torch.rand((B, Tq, cfg.n_ih), generator=gen, device=device)
-        KI = _normal(gen, (B, N_c, cfg.c_I), 1.0, cfg.idx_dtype, device)
+        f4 = cfg.idx_dtype == MXFP4  # keys drawn in fp32, encoded after planting
+        KI = _normal(gen, (B, N_c, cfg.c_I), 1.0, F32 if f4 else cfg.idx_dtype, device)
         if cfg.plants > 0:
             if Tq != 1:
                 raise ValueError("planted keys are defined for single-token decode only")
@@ -73,10 +98,15 @@ def make_problem_device(cfg, device="cuda"):
                 u = (w[b, 0, :, None] * qI[b, 0]).sum(0)
                 u = u * (cfg.c_I ** 0.5 / u.norm())
                 noise = torch.randn((pos.numel(), cfg.c_I), generator=gen, device=device)
-                KI[b, pos] = _store(u[None, :] + cfg.plant_noise * noise, cfg.idx_dtype)
+                KI[b, pos] = _store(u[None, :] + cfg.plant_noise * noise, F32 if f4 else cfg.idx_dtype)
                 plants.append(torch.sort(pos).values)
             out["plant_positions"] = plants
-        out["qI"] = _store(qI, cfg.idx_dtype)
         out["w"] = w.contiguous()
-        out["KI"] = KI
+        if f4:
+            out["qI"] = _store(qI, FP8)
+            out["KI"], out["KI_scales"] = _mxfp4(KI)
+            del KI
+        else:
+            out["qI"] = _store(qI, cfg.idx_dtype)
+            out["KI"] = KI
     return out

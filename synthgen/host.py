@@ -14,8 +14,8 @@ positions are drawn without replacement from the visible entries.
 """
 import numpy as np
 
-from .codecs import f32_to_bf16_bits, f32_to_e4m3fn_bits
-from .configs import BF16, F32, FP8
+from .codecs import f32_to_bf16_bits, f32_to_e4m3fn_bits, f32_to_mxfp4
+from .configs import BF16, F32, FP8, MXFP4
 
 _STREAMS = ["X_csa", "Z_csa", "X_hca", "Z_hca", "Q_csa", "Q_hca", "qI", "w", "KI",
             "plant_pos", "plant_noise"]
@@ -90,7 +90,11 @@ def make_problem(cfg):
                 noise = r["plant_noise"].standard_normal((len(pos), cfg.c_I), dtype=np.float32)
                 KI[b, pos] = u[None, :] + np.float32(cfg.plant_noise) * noise
                 out.setdefault("plant_positions", []).append(np.sort(pos))
-        out["qI"] = encode(qI, cfg.idx_dtype)
+        if cfg.idx_dtype == MXFP4:  # FP8 queries; keys as MX FP4 rows and their scales
+            out["qI"] = encode(qI, FP8)
+            out["KI"], out["KI_scales"] = f32_to_mxfp4(KI)
+        else:
+            out["qI"] = encode(qI, cfg.idx_dtype)
+            out["KI"] = encode(KI, cfg.idx_dtype)
         out["w"] = w
-        out["KI"] = encode(KI, cfg.idx_dtype)
     return out

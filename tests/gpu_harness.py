@@ -6,7 +6,7 @@ import numpy as np
 import torch
 
 import compressed_attention_compress_amd as lib
-from synthgen.configs import BF16, F32, FP8
+from synthgen.configs import BF16, F32, FP8, MXFP4
 
 DEV = "cuda"
 
@@ -58,9 +58,21 @@ def run_pool_overlap(Xa, Za, Xb, Zb, m, prev, dtype, P=None):
     return out
 
 
-def run_index(qI, w, KI, q_pos, m, k, idx_dtype, split=False):
+def key_buffer(prob):
+    """The indexer-key argument: the key codes, or for MX FP4 all packed rows followed by
+    all scales in one device buffer."""
+    KI = prob["KI"]
+    if "KI_scales" not in prob:
+        return KI if torch.is_tensor(KI) else to_dev(KI)
+    rows, sc = KI, prob["KI_scales"]
+    if not torch.is_tensor(rows):
+        rows, sc = to_dev(rows), to_dev(sc)
+    return torch.cat([rows.reshape(-1), sc.reshape(-1)])
+
+
+def run_index(qI, w, KI, q_pos, m, k, idx_dtype, split=False, N_c=None):
     B, Tq, n_ih, c_I = qI.shape
-    N_c = KI.shape[1]
+    N_c = KI.shape[1] if N_c is None else N_c
     ws_bytes = lib.lightning_index_topk_workspace_size(B, Tq, n_ih, N_c, k)
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=DEV)
     idx = torch.empty((B, Tq, k), dtype=torch.int32, device=DEV)

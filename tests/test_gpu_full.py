@@ -51,8 +51,12 @@ def check_index_queries(wl, queries):
     for b, t in queries:
         p = wl.n - wl.Tq + t
         V = oracle.visible(p, cfg.m, wl.N_c)
-        ref = oracle.index_scores(dec(prob["qI"][b, t], cfg.idx_dtype), prob["w"][b, t].cpu().numpy(),
-                                  dec(prob["KI"][b, :V], cfg.idx_dtype), V)
+        if cfg.idx_dtype == 3:  # MX FP4 keys, FP8 queries
+            qI = dec(prob["qI"][b, t], 2)
+            KI = oracle.decode_mxfp4(prob["KI"][b, :V].cpu().numpy(), prob["KI_scales"][b, :V].cpu().numpy())
+        else:
+            qI, KI = dec(prob["qI"][b, t], cfg.idx_dtype), dec(prob["KI"][b, :V], cfg.idx_dtype)
+        ref = oracle.index_scores(qI, prob["w"][b, t].cpu().numpy(), KI, V)
         g = scores[b, t, :V].cpu().numpy().astype(np.float64)
         rms = math.sqrt(float(np.mean(ref * ref)))
         assert np.all(np.abs(g - ref) <= 1e-3 * np.maximum(np.abs(ref), rms)), (b, t)
@@ -92,9 +96,11 @@ def check_attend_queries(wl, layer, queries):
     assert err <= 2e-2 * rms, f"{layer}: max |d| {err} vs RMS {rms}"
 
 
-def run_workload(ci):
+def run_workload(ci, fp4=False):
     import bench
     cfg = CONFIGS[ci]
+    if fp4:
+        cfg = cfg.scaled(idx_dtype=3)
     wl = bench.Workload(cfg, 1)
     wl.step(0)
     torch.cuda.synchronize()
@@ -128,6 +134,20 @@ def test_full_decode(ci):
         print(f"planted-key recall {rec:.3f}")
     for layer in wl.layers:
         check_attend_queries(wl, layer, queries)
+
+
+def test_full_decode_fp4_keys():
+    """The Pro 1M decode step with MX FP4 indexer keys: scores, top-k and CSA attention on
+    sampled queries, planted-key recall reported."""
+    print("[full-size decode config 5, MX FP4 keys]", flush=True)
+    wl = run_workload(5, fp4=True)
+    cfg = wl.cfg
+    queries = [(b, 0) for b in range(cfg.B)]
+    check_index_queries(wl, queries)
+    rec = np.mean([np.isin(wl.prob["plant_positions"][b].cpu().numpy(), wl.idx[b, 0].cpu().numpy()).mean()
+                   for b in range(cfg.B)])
+    print(f"planted-key recall {rec:.3f}")
+    check_attend_queries(wl, "csa", queries)
 
 
 def test_full_prefill():

@@ -17,7 +17,7 @@ import pytest
 import torch
 
 import oracle
-from synthgen.configs import BF16, CONFIGS, F32, FP8
+from synthgen.configs import BF16, CONFIGS, F32, FP8, MXFP4
 from synthgen.host import make_problem
 from tests import gpu_harness as H
 
@@ -49,10 +49,17 @@ def check_pool(Xc, Zc, dtype, m, gpu_out, P=None):
             assert not bad.any(), f"seq {b}: {bad.sum()} pooled values outside tolerance"
 
 
+def decode_keys(prob):
+    """Indexer queries and keys as fp64, from the bytes the GPU consumed."""
+    cfg = prob["cfg"]
+    if cfg.idx_dtype == MXFP4:
+        return oracle.decode(prob["qI"], FP8), oracle.decode_mxfp4(prob["KI"], prob["KI_scales"])
+    return oracle.decode(prob["qI"], cfg.idx_dtype), oracle.decode(prob["KI"], cfg.idx_dtype)
+
+
 def check_index(prob, q_pos, k, idx, sc, alls):
     cfg = prob["cfg"]
-    qI = oracle.decode(prob["qI"], cfg.idx_dtype)
-    KI = oracle.decode(prob["KI"], cfg.idx_dtype)
+    qI, KI = decode_keys(prob)
     w = prob["w"]
     idx = idx.cpu().numpy()
     sc = sc.cpu().numpy()
@@ -126,6 +133,10 @@ def small_cases():
         "prefill_small": c4.scaled(n=4096, Tq=200, seed=26),
         "prefill_from_zero": c4.scaled(n=0, Tq=40, seed=27, k=8),
         "pair_h128": c5.scaled(B=2, n=4 * 3000, seed=28, plants=16),
+        # MX FP4 indexer keys (FP8 queries)
+        "csa_fp4_h64_k512": c3.scaled(B=2, n=4 * 900 + 2, seed=29, idx_dtype=MXFP4),
+        "pair_fp4_h128": c5.scaled(B=2, n=4 * 3000 + 1, seed=30, plants=16, idx_dtype=MXFP4),
+        "prefill_fp4": c4.scaled(n=4096, Tq=200, seed=31, idx_dtype=MXFP4),
     }
 
 
@@ -160,8 +171,9 @@ def run_chain(cfg, split_index=False, W=None, sink=None):
         if layer == "csa":
             if C.shape[1] == 0:
                 continue
-            qI, w, KI = H.to_dev(prob["qI"]), H.to_dev(prob["w"]), H.to_dev(prob["KI"])
-            idx, sc, alls = H.run_index(qI, w, KI, q_pos, m, cfg.k, cfg.idx_dtype, split=split_index)
+            qI, w, KI = H.to_dev(prob["qI"]), H.to_dev(prob["w"]), H.key_buffer(prob)
+            idx, sc, alls = H.run_index(qI, w, KI, q_pos, m, cfg.k, cfg.idx_dtype, split=split_index,
+                                        N_c=prob["KI"].shape[1])
             check_index(prob, q_pos_h, cfg.k, idx, sc, alls)
             idx_h = idx.cpu().numpy()
             out, lse = H.run_csa_attend(Q, C, idx, X, win_pos, q_pos, W, dt,

@@ -421,6 +421,14 @@ def test_mxfp4_roundtrip_and_rounding():
     assert np.all(np.abs(q - x.astype(np.float32)) <= 2.0 * step)
     amax = np.abs(x.astype(np.float32)).reshape(200, 4, 32).max(-1)
     assert np.all((amax / np.exp2(s3.astype(float) - 127.0) >= 4) & (amax / np.exp2(s3.astype(float) - 127.0) < 8))
+    # the device generator's encoder (torch; run on the CPU here) writes the same bytes
+    from synthgen.device import _mxfp4
+    xt = x.astype(np.float32)
+    xt[0, :8] = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 7.9]
+    pa, sa = f32_to_mxfp4(xt)
+    pb, sb = _mxfp4(torch.from_numpy(xt))
+    np.testing.assert_array_equal(pa, pb.numpy())
+    np.testing.assert_array_equal(sa, sb.numpy())
     # ties go to the even code: 1.25 -> 1.0, 1.75 -> 2.0, 5.0 -> 4.0 (block max 6 -> unit scale)
     t = np.zeros((1, 32), np.float32)
     t[0, :4] = [1.25, 1.75, 5.0, 6.0]

@@ -8,6 +8,7 @@ seeded generators in ``synthgen``.
 Parity status: every function here is pinned by a CPU test against values printed on
 the pages or against closed forms and brute force (see ``tests/test_oracle_pins.py``).
 """
+from . import kvcache  # noqa: F401
 from .csahca import (  # noqa: F401
     E2M1_TABLE,
     E4M3FN_TABLE,

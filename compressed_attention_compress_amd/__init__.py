@@ -24,6 +24,10 @@ _SIGNATURES = {
     "csa_compress": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _LL, _LL, _P]),
     "hca_compress": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _LL, _LL, _P]),
     "csa_compress_overlap": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _LL, _LL, _P]),
+    "csahca_kv_ring_rows": (_I, [_I, _I]),
+    "csahca_kv_append": (_I, [_P, _P, _P, _P, _P, _P, _I, _LL, _I, _I, _I, _I, _I, _LL, _LL, _LL,
+                              _P]),
+    "csahca_kv_fork": (_I, [_P, _P, _P, _P, _P, _P, _I, _LL, _I, _I, _I, _I, _LL, _LL, _P]),
     "lightning_index_topk_workspace_size": (_SZ, [_I, _I, _I, _I, _I]),
     "lightning_index_topk": (_I, [_P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P,
                                   _P, _SZ, _P]),
@@ -118,6 +122,27 @@ def csa_compress_overlap(kv_a, gate_a, kv_b, gate_b, pos_bias, out, B, n, c, m, 
     return _check("csa_compress_overlap", load().csa_compress_overlap(
         _ptr(kv_a), _ptr(gate_a), _ptr(kv_b), _ptr(gate_b), _ptr(pos_bias), _ptr(out), B, n, c,
         m, prev, dtype, in_bstride, out_bstride, _stream(stream)))
+
+
+def csahca_kv_ring_rows(W, m):
+    return load().csahca_kv_ring_rows(W, m)
+
+
+def csahca_kv_append(kv_ring, gate_ring, entries, kv_new, gate_new, pos_bias, B, n_old, n_new,
+                     c, m, W, dtype, new_bstride, ring_bstride, ent_bstride, stream=None):
+    return _check("csahca_kv_append", load().csahca_kv_append(
+        _ptr(kv_ring), _ptr(gate_ring), _ptr(entries), _ptr(kv_new), _ptr(gate_new),
+        _ptr(pos_bias), B, n_old, n_new, c, m, W, dtype, new_bstride, ring_bstride, ent_bstride,
+        _stream(stream)))
+
+
+def csahca_kv_fork(dst_kv_ring, dst_gate_ring, dst_entries, src_kv_ring, src_gate_ring,
+                   src_entries, B, n_entries, c, m, W, dtype, ring_bstride, ent_bstride,
+                   stream=None):
+    return _check("csahca_kv_fork", load().csahca_kv_fork(
+        _ptr(dst_kv_ring), _ptr(dst_gate_ring), _ptr(dst_entries), _ptr(src_kv_ring),
+        _ptr(src_gate_ring), _ptr(src_entries), B, n_entries, c, m, W, dtype, ring_bstride,
+        ent_bstride, _stream(stream)))
 
 
 def lightning_index_topk_workspace_size(B, Tq, n_ih, N_c, k):

@@ -14,7 +14,7 @@
 // Overlapped two-stream form (csa_compress_overlap, section V.1's equation with two KV
 // streams): entry i walks stream a over block i and then stream b over block i-1 with
 // the same running softmax, which is one joint softmax over the 2m logits.
-#include "common.hpp"
+#include "pool.hpp"
 
 namespace {
 
@@ -269,6 +269,10 @@ void launch_pool(const void* kv, const void* gate, const void* kv_b, const void*
                        pos_bias, (T*)out, (int)N, c, m, prev, in_bs, out_bs, total);
 }
 
+}  // namespace
+
+namespace csahca {
+
 int pool_entry(const char* name, const void* kv, const void* gate, const void* kv_b,
                const void* gate_b, bool ov, int prev, const float* pos_bias, void* out, int B,
                int n, int c, int m, int dtype, long long in_bs, long long out_bs, void* stream) {
@@ -335,7 +339,9 @@ int pool_entry(const char* name, const void* kv, const void* gate, const void* k
   return launch_status(name);
 }
 
-}  // namespace
+}  // namespace csahca
+
+using csahca::pool_entry;
 
 extern "C" int csa_compress(const void* kv, const void* gate, const float* pos_bias, void* out,
                             int B, int n, int c, int m, int dtype, long long in_bstride,

@@ -242,6 +242,57 @@ int hca_attend_sink(const void* q, const void* ckv, const void* win_kv, const in
                     int W, float scale, const float* sink, int dtype, void* out, float* lse,
                     void* workspace, size_t ws_bytes, void* stream);
 
+/*
+ * csahca_kv_ring_rows / csahca_kv_append / csahca_kv_fork -- the cache lifecycle of one
+ * layer: raw tokens arrive, completed blocks become compressed entries, the recent window
+ * stays exact, a request can start from another's prefix.
+ * Source: "DeepSeek-V4 Architecture From Kernels ... C-Kernel-Engine", section 9
+ * (heterogeneous KV cache: per request the last W raw tokens, one compressed entry per m
+ * tokens and the tail of the incomplete block; an entry is made when its block completes;
+ * tails must stay consistent when a request reuses a cached prefix).
+ *
+ * Ring layout (the reading adopted): the raw values and gate logits of a sequence are kept
+ * in rings of R = csahca_kv_ring_rows(W, m) = m * ceil((W + m - 1) / m) rows, the smallest
+ * whole number of blocks holding the window and a tail.  Position p is stored twice, at
+ * rows p mod R and p mod R + R, so
+ *   - the last L <= R positions p0 .. p0+L-1 are the L contiguous rows from p0 mod R, and
+ *   - with ring_bstride == 2*R*c, csa_attend / hca_attend read the window straight from
+ *     the ring: win_kv = kv_ring, L = 2R, win_pos[b] = R * floor(max(0, n - R) / R) for a
+ *     sequence of n tokens, valid for queries at positions >= n - R + W - 1 (decode and
+ *     chunks of up to R - W + 1 tokens).
+ *
+ * csahca_kv_append: append n_new tokens to sequences that each hold n_old (the same for
+ * every sequence of the call).  Entries s with n_old/m <= s < (n_old+n_new)/m are written,
+ * each pooled as csa_compress does (the block that was a tail is pooled from the ring),
+ * then the last min(n_new, R) tokens enter the ring.
+ *   kv_ring, gate_ring  [B, 2R, c] of `dtype`, batch stride ring_bstride >= 2*R*c.
+ *   entries   [B, >= (n_old+n_new)/m, c] of `dtype`, batch stride ent_bstride; may be NULL
+ *             when no block completes.
+ *   kv_new, gate_new  [B, n_new, c] of `dtype`, batch stride new_bstride >= n_new*c.
+ *   pos_bias  [m, c] float32 or NULL (as csa_compress).
+ *   Strides are in elements and multiples of 8.  Limits: c % 8 == 0, 1 <= m <= 4096,
+ *   W >= 0, dtype CSAHCA_F32 or CSAHCA_BF16.  n_new == 0 does nothing.  Two appends to
+ *   the same sequences must be ordered (same stream).
+ *
+ * csahca_kv_fork: a new request sharing the source's prefix.  Copies the source rings
+ * (both halves, all B sequences) as they stand, i.e. the prefix is the source's current
+ * length P, and its first n_entries = P / m entries; the copy then takes appends with
+ * n_old = P.  Rings and entries use the batch strides of csahca_kv_append; dst and src
+ * must not overlap.
+ *
+ * Both return CSAHCA_OK or a negative status as every entry point;
+ * csahca_kv_ring_rows returns 0 for W < 0 or m < 1.
+ */
+int csahca_kv_ring_rows(int W, int m);
+int csahca_kv_append(void* kv_ring, void* gate_ring, void* entries, const void* kv_new,
+                     const void* gate_new, const float* pos_bias, int B, long long n_old,
+                     int n_new, int c, int m, int W, int dtype, long long new_bstride,
+                     long long ring_bstride, long long ent_bstride, void* stream);
+int csahca_kv_fork(void* dst_kv_ring, void* dst_gate_ring, void* dst_entries,
+                   const void* src_kv_ring, const void* src_gate_ring, const void* src_entries,
+                   int B, long long n_entries, int c, int m, int W, int dtype,
+                   long long ring_bstride, long long ent_bstride, void* stream);
+
 /* Message for the last non-OK status returned on the calling thread ("" if none). */
 const char* csahca_last_error(void);
 

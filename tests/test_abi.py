@@ -133,3 +133,45 @@ def test_binding_raises_with_message():
     with pytest.raises(lib.CsaHcaError) as e:
         lib.csa_compress(None, None, None, None, 1, 8, 8, 4, 1, 64, 16, stream=0)
     assert e.value.status == EINVAL and "non-NULL" in str(e.value)
+
+
+def test_kv_cache_validation():
+    """Ring size agrees with the simulator's rule; invalid appends and forks are refused on
+    the host."""
+    from oracle import kvcache
+    L = lib.load()
+    for W, m in ((128, 4), (128, 128), (0, 4), (5, 3), (128, 1), (1, 4096)):
+        assert L.csahca_kv_ring_rows(W, m) == kvcache.ring_rows(W, m)
+    assert L.csahca_kv_ring_rows(-1, 4) == 0 and L.csahca_kv_ring_rows(128, 0) == 0
+    R = kvcache.ring_rows(128, 4)
+    c = 512
+    ok = [FAKE, FAKE, FAKE, FAKE, FAKE, None, 2, 6, 10, c, 4, 128, 1, 10 * c, 2 * R * c, 4 * c, None]
+    ap = L.csahca_kv_append
+
+    def with_(i, v):
+        a = list(ok)
+        a[i] = v
+        return a
+    assert ap(*with_(12, 2)) == ENOTSUP                 # fp8 raw tokens
+    assert ap(*with_(9, 12)) == EINVAL                  # c % 8
+    assert ap(*with_(14, 2 * R * c - 8)) == EINVAL      # ring too small
+    assert ap(*with_(15, 3 * c)) == EINVAL              # entries stride below (6+10)/4 = 4
+    assert ap(*with_(13, 9 * c)) == EINVAL              # new tokens stride
+    assert ap(*with_(3, FAKE + 4)) == EINVAL            # alignment
+    assert ap(*with_(2, None)) == EINVAL                # blocks complete, no entries
+    assert "entries" in lib.last_error()
+    assert ap(*with_(8, 0)) == 0                        # nothing appended: nothing done
+    fk = L.csahca_kv_fork
+    fok = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 4, c, 4, 128, 1, 2 * R * c, 4 * c, None]
+    f = list(fok)
+    f[12] = 2 * R * c - 8
+    assert fk(*f) == EINVAL
+    f = list(fok)
+    f[2] = None
+    assert fk(*f) == EINVAL
+    f = list(fok)
+    f[11] = 2
+    assert fk(*f) == ENOTSUP
+    f = list(fok)
+    f[13] = 3 * c
+    assert fk(*f) == EINVAL

@@ -53,6 +53,9 @@ def parse():
     ap.add_argument("--sink", action="store_true",
                     help="run both attention calls with a per-head attention sink "
                          "(csa_attend_sink / hca_attend_sink)")
+    ap.add_argument("--kv-append", action="store_true",
+                    help="time the cache lifecycle at the config's shape (csahca_kv_append of a "
+                         "chunk and of one decode token, CSA and HCA caches) instead of the step")
     ap.add_argument("--overlap-pool", action="store_true",
                     help="time the overlapped two-stream CSA pooling (full context pass and a "
                          "decode append) at the config's shape instead of the step")
@@ -496,6 +499,118 @@ def overlap_pool(cfg, reps, cpu_seconds, no_cpu):
     print(json.dumps(line), flush=True)
 
 
+def kv_append(cfg, reps, cpu_seconds, no_cpu):
+    """csahca_kv_append at the config's shape, for the CSA (m) and the HCA (m') cache of a
+    layer pair.  Every sequence holds n - 1 tokens, so that both caches have a tail of
+    m - 1 tokens.  Chunk: the config's prefill chunk (8192 tokens for a decode config) is
+    appended to every sequence; bytes counted are the new tokens' values and gate logits
+    read once, the tail read back from the ring, the entries written and the last R tokens
+    written to the ring once (the ring's second copy is layout, not counted).  Decode: one
+    token per sequence, which completes a block of both caches; timed from a graph of 20."""
+    import numpy as np
+    import torch
+
+    import compressed_attention_compress_amd as lib
+
+    B, c, W, dt = cfg.B, cfg.c, cfg.W, cfg.dtype
+    n_old = cfg.n - 1
+    chunk = cfg.Tq if cfg.kind == "prefill" else 8192
+    es = 2 if dt == 1 else 4
+    tdt = torch.bfloat16 if dt == 1 else torch.float32
+    g = torch.Generator(device="cuda").manual_seed(4321)
+    X = (torch.randn((B, chunk, c), generator=g, device="cuda") / math.sqrt(c)).to(tdt)
+    Z = torch.randn((B, chunk, c), generator=g, device="cuda").to(tdt)
+    caches = []
+    for m in (cfg.m, cfg.m_hca):
+        R = lib.csahca_kv_ring_rows(W, m)
+        NE = (n_old + chunk) // m
+        caches.append(dict(m=m, R=R, NE=NE,
+                           rx=torch.zeros((B, 2 * R, c), dtype=tdt, device="cuda"),
+                           rz=torch.zeros((B, 2 * R, c), dtype=tdt, device="cuda"),
+                           ent=torch.zeros((B, NE, c), dtype=tdt, device="cuda")))
+    st = torch.cuda.current_stream()
+
+    def append(k, stream):
+        for cc in caches:
+            lib.csahca_kv_append(cc["rx"], cc["rz"], cc["ent"], X, Z, None, B, n_old, k, c, cc["m"],
+                                 W, dt, chunk * c, 2 * cc["R"] * c, cc["NE"] * c, stream=stream)
+
+    def chunk_bytes(k):
+        tot = 0
+        for cc in caches:
+            m, R = cc["m"], cc["R"]
+            t = n_old % m
+            made = (n_old + k) // m - n_old // m
+            tot += B * c * es * (2 * k + (2 * t if k >= m - t else 0) + made + 2 * min(k, R))
+        return tot
+
+    append(chunk, st)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(reps):
+        append(chunk, st)
+    e1.record(st)
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) / 1e3 / reps
+    nbytes = chunk_bytes(chunk)
+    gbs = nbytes / sec / 1e9
+
+    side = torch.cuda.Stream()
+    ga = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(ga, stream=side):
+        for _ in range(20):
+            append(1, side)
+    ga.replay()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        e0.record(side)
+        for _ in range(10):
+            ga.replay()
+        e1.record(side)
+    torch.cuda.synchronize()
+    dec_us = e0.elapsed_time(e1) * 1e3 / 200
+
+    cpu = None
+    if not no_cpu:
+        from oracle import kvcache as K
+        rng = np.random.default_rng(6)
+        ntok = 1024  # tokens per simulator append (one sequence)
+        Xc, Zc = rng.standard_normal((ntok, c)), rng.standard_normal((ntok, c))
+        el, done = 0.0, 0
+        while el < cpu_seconds:  # fresh simulators with an m' - 1 token tail each round
+            sims = [K.KVSim(c, cc["m"], W) for cc in caches]
+            for s in sims:
+                s.append(Xc[:cfg.m_hca - 1], Zc[:cfg.m_hca - 1])
+            t0 = time.perf_counter()
+            for s in sims:
+                s.append(Xc, Zc)
+            el += time.perf_counter() - t0
+            done += 1
+        per = sum(c * es * (2 * ntok + ntok // cc["m"] + 2 * min(ntok, cc["R"])) for cc in caches)
+        cpu = {"value": round(done * per / el / 1e9, 4), "unit": "GB/s",
+               "cores": torch.get_num_threads(), "kind": "oracle",
+               "sample": f"{done} appends of {ntok} tokens to the CSA and HCA simulators of one "
+                         f"sequence, {el:.1f} s, NumPy fp64 (bytes counted at the GPU's storage "
+                         f"width)"}
+    line = {
+        "metric": "KV-cache append (CSA + HCA caches), achieved HBM GB/s for a chunk",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": reps, "warmup": 1,
+        "ms_per_append": round(sec * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if dt == 1 else "f32", "data": "synthetic",
+        "config": {"workload": f"kv_append_{cfg.name}", "batch": B, "n_old": n_old, "chunk": chunk,
+                   "c": c, "m": [cfg.m, cfg.m_hca], "W": W,
+                   "timing": "HIP events around back-to-back calls"},
+        "decode_append_us": round(dec_us, 2),
+        "roofline": {"kernel": "csahca_kv_append (pool_kernel + ring_store)", "bound": "hbm",
+                     "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "avg_launch_us": round(sec * 1e6, 2), "bytes_per_launch": nbytes},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.traffic_from:
@@ -518,6 +633,9 @@ def main():
             print("--fp4-keys needs a config with an FP8 indexer", file=sys.stderr)
             sys.exit(2)
         cfg = cfg.scaled(idx_dtype=3)
+    if args.kv_append:
+        kv_append(cfg, args.steps or 20, min(args.cpu_seconds, 10.0), args.no_cpu_baseline)
+        return
     if args.overlap_pool:
         overlap_pool(cfg, args.steps or 10, min(args.cpu_seconds, 10.0), args.no_cpu_baseline)
         return

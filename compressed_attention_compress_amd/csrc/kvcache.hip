@@ -93,11 +93,19 @@ extern "C" int csahca_kv_append(void* kv_ring, void* gate_ring, void* entries, c
   const long long nbs = new_bstride * e, rbs = ring_bstride * e;
   const int t = (int)(n_old % m);
   const long long a0 = t ? n_old + (m - t) : n_old;  // first block start at or after n_old
+  const int keep = n_new < R ? n_new : R;  // the last tokens, kept for the window and tail
   int rc;
-  // 1. a block begun by earlier appends (its tail is in the ring) and completed now: the
-  //    missing tokens join the ring and the block is pooled from there
+  // With room for the old tail and all new tokens (decode, short chunks), the new tokens
+  // enter the ring first and a block begun earlier is pooled from there; otherwise the
+  // block's missing tokens enter first, then the last tokens once it is pooled.
+  const bool early = n_new + t <= R;
+  if (early && (rc = store_rows(kv_new, gate_new, kv_ring, gate_ring, B, 0, n_new, n_old, R, rb, nbs, rbs, st)))
+    return rc;
+  // 1. a block begun by earlier appends (its tail is in the ring) and completed now
   if (t && n_new >= m - t) {
-    if ((rc = store_rows(kv_new, gate_new, kv_ring, gate_ring, B, 0, m - t, n_old, R, rb, nbs, rbs, st))) return rc;
+    if (!early &&
+        (rc = store_rows(kv_new, gate_new, kv_ring, gate_ring, B, 0, m - t, n_old, R, rb, nbs, rbs, st)))
+      return rc;
     const long long blk = n_old / m;
     const long long row = (blk * m) % R;
     if ((rc = pool_entry(name, (const char*)kv_ring + row * rb, (const char*)gate_ring + row * rb, nullptr,
@@ -114,8 +122,11 @@ extern "C" int csahca_kv_append(void* kv_ring, void* gate_ring, void* entries, c
                          dtype, new_bstride, ent_bstride, stream)))
       return rc;
   }
-  // 3. the last tokens (up to R of them: the window and any new tail) join the ring
-  const int keep = n_new < R ? n_new : R;
+  // 3. the last tokens join the ring (after step 1 has read the rows they may replace)
+  if (early) {
+    clear_error();
+    return CSAHCA_OK;
+  }
   return store_rows(kv_new, gate_new, kv_ring, gate_ring, B, n_new - keep, keep, n_old, R, rb, nbs, rbs, st);
 }
 

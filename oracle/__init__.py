@@ -19,10 +19,14 @@ from .csahca import (  # noqa: F401
     decode_e4m3fn,
     decode_mxfp4,
     entry_counts,
+    entry_positions,
     hca_rows,
     index_scores,
+    norm_rope,
     pool,
     pool_overlap,
+    rmsnorm,
+    rope_tail,
     topk,
     visible,
     window_positions,

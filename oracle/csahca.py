@@ -172,6 +172,62 @@ def pool_overlap(Xa, Za, Xb, Zb, m, P=None, prev=0):
 
 
 # ----------------------------------------------------------------------------------------
+# RMSNorm and partial RoPE ([P2] section IV: both branches normalise the queries and the
+# compressed KV entries and rotate only the last 64 dimensions)
+# ----------------------------------------------------------------------------------------
+def rmsnorm(x, gamma=None, eps=1e-6):
+    """Root-mean-square normalisation over the last axis.
+
+    [P2] IV names RMSNorm on the queries and on the compressed KV entries without writing
+    it out.  Reading: the usual definition, y = x / sqrt(mean(x^2) + eps) * gamma, with a
+    per-channel gain gamma (1 when None) and eps given by the caller.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    ms = (x * x).mean(axis=-1, keepdims=True)
+    y = x / np.sqrt(ms + eps)
+    if gamma is not None:
+        y = y * np.asarray(gamma, dtype=np.float64)
+    return y
+
+
+def rope_tail(x, pos, d_rope=64, theta=10000.0):
+    """Rotary position embedding on the last d_rope dimensions of x.
+
+    [P1] "The Code: RoPE Helpers": the rotated dimensions are taken as consecutive pairs
+    (2i, 2i+1), each read as the complex number x[2i] + i x[2i+1] and multiplied by
+    e^{i pos f_i} with f_i = theta^(-2i / d_rope), i < d_rope / 2 (theta = 10000 there).
+    [P2] IV: only the last 64 dimensions carry RoPE; the others pass unchanged.
+
+    x: [..., c]; pos: broadcastable to x.shape[:-1] (the position of every row).
+    """
+    x = np.array(x, dtype=np.float64)
+    c = x.shape[-1]
+    if d_rope == 0:
+        return x
+    i = np.arange(d_rope // 2, dtype=np.float64)
+    f = theta ** (-2.0 * i / d_rope)                            # [d_rope/2]
+    ang = np.asarray(pos, dtype=np.float64)[..., None] * f       # [..., d_rope/2]
+    tail = x[..., c - d_rope:]
+    z = tail[..., 0::2] + 1j * tail[..., 1::2]
+    z = z * np.exp(1j * ang)
+    out = x.copy()
+    out[..., c - d_rope::2] = z.real
+    out[..., c - d_rope + 1::2] = z.imag
+    return out
+
+
+def norm_rope(x, pos, gamma=None, eps=1e-6, d_rope=64, theta=10000.0):
+    """RMSNorm, then RoPE on the last d_rope dimensions, row by row (x: [..., c])."""
+    return rope_tail(rmsnorm(x, gamma, eps), pos, d_rope, theta)
+
+
+def entry_positions(m, entry0, N):
+    """Position a compressed entry carries for RoPE.  The pages do not say; reading: the
+    first raw position of its block, m * s for entry s (entries entry0 .. entry0+N-1)."""
+    return m * (entry0 + np.arange(N))
+
+
+# ----------------------------------------------------------------------------------------
 # visibility and window
 # ----------------------------------------------------------------------------------------
 def visible(p, m, N):

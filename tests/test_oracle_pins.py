@@ -21,7 +21,8 @@ def _impl(**over):
                                index_scores=O.index_scores, topk=O.topk,
                                attend=O.attend, visible=O.visible, csa_rows=O.csa_rows,
                                hca_rows=O.hca_rows, entry_counts=O.entry_counts,
-                               window_positions=O.window_positions)
+                               window_positions=O.window_positions, rmsnorm=O.rmsnorm,
+                               rope_tail=O.rope_tail, norm_rope=O.norm_rope)
     for k, v in over.items():
         setattr(ns, k, v)
     return ns
@@ -332,11 +333,73 @@ def check_rows_and_visibility(o):
     assert r1.shape[0] == o.visible(50, m, C.shape[0]) + W
 
 
+def check_rmsnorm(o):
+    """RMSNorm: values worked by hand, and the invariants of the definition."""
+    # [3, 4]: mean square 12.5; with eps = 3.5 the divisor is sqrt(16) = 4
+    np.testing.assert_allclose(o.rmsnorm(np.array([3.0, 4.0]), eps=3.5), [0.75, 1.0], atol=1e-15)
+    # no centring: [1, 1, 1, 5] has mean square 7 (a LayerNorm would subtract the mean 2)
+    np.testing.assert_allclose(o.rmsnorm(np.array([1.0, 1, 1, 5]), eps=0.0),
+                               np.array([1.0, 1, 1, 5]) / np.sqrt(7.0), atol=1e-15)
+    rng = np.random.default_rng(21)
+    x = rng.normal(size=(6, 16)) * 3
+    y = o.rmsnorm(x, eps=0.0)
+    np.testing.assert_allclose(np.sqrt((y * y).mean(axis=-1)), 1.0, atol=1e-14)  # unit RMS
+    np.testing.assert_allclose(o.rmsnorm(2.5 * x, eps=0.0), y, atol=1e-14)      # scale-free
+    np.testing.assert_allclose(o.rmsnorm(-x, eps=0.0), -y, atol=1e-14)
+    g = rng.uniform(0.5, 2.0, size=16)
+    np.testing.assert_allclose(o.rmsnorm(x, g, eps=0.0), y * g, atol=1e-14)     # per-channel gain
+    # a constant row returns the gain (with the row's sign)
+    np.testing.assert_allclose(o.rmsnorm(np.full(16, -0.3), g, eps=0.0), -g, atol=1e-14)
+    assert np.all(o.rmsnorm(np.zeros(8), eps=1e-6) == 0.0)
+
+
+def check_rope(o):
+    """Partial RoPE: consecutive pairs of the last d dimensions rotate by pos * f_i,
+    f_i = theta^(-2i/d)."""
+    c, d = 12, 8
+    rng = np.random.default_rng(22)
+    x = rng.normal(size=(5, c))
+    np.testing.assert_allclose(o.rope_tail(x, np.zeros(5), d), x, atol=0)        # position 0
+    r = o.rope_tail(x, np.arange(5) * 7, d)
+    np.testing.assert_array_equal(r[:, :c - d], x[:, :c - d])                    # head untouched
+    # one-hot on the first rotated dimension: pair 0 has frequency 1 and rotates
+    # counter-clockwise into its partner, the next dimension
+    e = np.zeros((1, c))
+    e[0, c - d] = 1.0
+    for p in (1, 2, 5):
+        out = o.rope_tail(e, [p], d)[0]
+        np.testing.assert_allclose(out[c - d:c - d + 2], [np.cos(p), np.sin(p)], atol=1e-15)
+        np.testing.assert_allclose(np.delete(out, [c - d, c - d + 1]), 0.0, atol=0)
+    # pair i = 16 of 64 rotated dimensions: f = 10000^(-1/2) = 0.01, so position 100 turns it
+    # by exactly one radian
+    e = np.zeros((1, 64))
+    e[0, 32] = 1.0
+    np.testing.assert_allclose(o.rope_tail(e, [100], 64)[0, 32:34], [np.cos(1.0), np.sin(1.0)],
+                               atol=1e-14)
+    # theta = 1: every pair turns by the position itself
+    e = np.zeros((1, 8))
+    e[0, 6] = 1.0
+    np.testing.assert_allclose(o.rope_tail(e, [3], 8, theta=1.0)[0, 6:], [np.cos(3), np.sin(3)],
+                               atol=1e-15)
+    # pair norms are kept; rotations compose; scores depend on the offset only
+    pn = lambda a: np.hypot(a[..., c - d::2], a[..., c - d + 1::2])
+    np.testing.assert_allclose(pn(r), pn(x), atol=1e-14)
+    np.testing.assert_allclose(o.rope_tail(o.rope_tail(x, [3] * 5, d), [1000] * 5, d),
+                               o.rope_tail(x, [1003] * 5, d), atol=1e-12)
+    q, k = x[0], x[1]
+    s1 = o.rope_tail(q, 50, d) @ o.rope_tail(k, 20, d)
+    s2 = o.rope_tail(q, 1030, d) @ o.rope_tail(k, 1000, d)
+    assert abs(s1 - s2) < 1e-12
+    # norm then RoPE: with unit gain the order does not matter (RoPE keeps the RMS)
+    np.testing.assert_allclose(o.norm_rope(x, np.arange(5), None, 1e-6, d),
+                               o.rmsnorm(o.rope_tail(x, np.arange(5), d), None, 1e-6), atol=1e-14)
+
+
 ALL_CHECKS = [check_budget_counts, check_worked_example, check_pool_counts, check_budget_toy,
               check_pooling_recall, check_pool_closed_forms, check_pool_overlap_closed_forms,
               check_indexer_closed_forms,
               check_topk_brute, check_attend_textbook, check_attend_sink,
-              check_rows_and_visibility]
+              check_rows_and_visibility, check_rmsnorm, check_rope]
 
 
 @pytest.mark.parametrize("check", ALL_CHECKS, ids=lambda f: f.__name__)
@@ -559,7 +622,49 @@ def _counts_ceil(n, m, m_hca, k, W):
     return nc + W, min(nc, k) + W, -(-n // m_hca) + W
 
 
+def _rmsnorm_centred(x, gamma=None, eps=1e-6):
+    x = np.asarray(x, dtype=np.float64)
+    x = x - x.mean(axis=-1, keepdims=True)
+    y = x / np.sqrt((x * x).mean(axis=-1, keepdims=True) + eps)
+    return y if gamma is None else y * gamma
+
+
+def _rmsnorm_eps_outside(x, gamma=None, eps=1e-6):
+    x = np.asarray(x, dtype=np.float64)
+    y = x / (np.sqrt((x * x).mean(axis=-1, keepdims=True)) + eps)
+    return y if gamma is None else y * gamma
+
+
+def _rope_variant(half_split=False, sign=1.0, fexp=2.0, head=False):
+    def f(x, pos, d_rope=64, theta=10000.0):
+        x = np.array(x, dtype=np.float64)
+        c = x.shape[-1]
+        i = np.arange(d_rope // 2)
+        ang = sign * np.asarray(pos, dtype=np.float64)[..., None] * theta ** (-fexp * i / d_rope)
+        lo = 0 if head else c - d_rope
+        t = x[..., lo:lo + d_rope]
+        if half_split:
+            a, b = t[..., :d_rope // 2], t[..., d_rope // 2:]
+        else:
+            a, b = t[..., 0::2], t[..., 1::2]
+        ra = a * np.cos(ang) - b * np.sin(ang)
+        rb = a * np.sin(ang) + b * np.cos(ang)
+        out = x.copy()
+        if half_split:
+            out[..., lo:lo + d_rope // 2], out[..., lo + d_rope // 2:lo + d_rope] = ra, rb
+        else:
+            out[..., lo:lo + d_rope:2], out[..., lo + 1:lo + d_rope:2] = ra, rb
+        return out
+    return f
+
+
 MUTANTS = {
+    "rmsnorm_centred": dict(rmsnorm=_rmsnorm_centred),
+    "rmsnorm_eps_outside_sqrt": dict(rmsnorm=_rmsnorm_eps_outside),
+    "rope_half_split_pairs": dict(rope_tail=_rope_variant(half_split=True)),
+    "rope_clockwise": dict(rope_tail=_rope_variant(sign=-1.0)),
+    "rope_frequency_exponent": dict(rope_tail=_rope_variant(fexp=1.0)),
+    "rope_on_first_dims": dict(rope_tail=_rope_variant(head=True)),
     "pool_softmax_over_channels": dict(pool=_pool_wrong_axis),
     "pool_emits_tail": dict(pool=_pool_ceil),
     "overlap_stream_b_same_block": dict(pool_overlap=_overlap_same_block),

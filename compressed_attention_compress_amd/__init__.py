@@ -24,6 +24,11 @@ _SIGNATURES = {
     "csa_compress": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _LL, _LL, _P]),
     "hca_compress": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _LL, _LL, _P]),
     "csa_compress_overlap": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _LL, _LL, _P]),
+    "csahca_compress_norm_rope": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _LL, _I, _F, _F, _I,
+                                       _LL, _LL, _P]),
+    "csa_compress_overlap_norm_rope": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _LL,
+                                            _I, _F, _F, _I, _LL, _LL, _P]),
+    "csahca_norm_rope": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _F, _I, _I, _P]),
     "csahca_kv_ring_rows": (_I, [_I, _I]),
     "csahca_kv_append": (_I, [_P, _P, _P, _P, _P, _P, _I, _LL, _I, _I, _I, _I, _I, _LL, _LL, _LL,
                               _P]),
@@ -122,6 +127,29 @@ def csa_compress_overlap(kv_a, gate_a, kv_b, gate_b, pos_bias, out, B, n, c, m, 
     return _check("csa_compress_overlap", load().csa_compress_overlap(
         _ptr(kv_a), _ptr(gate_a), _ptr(kv_b), _ptr(gate_b), _ptr(pos_bias), _ptr(out), B, n, c,
         m, prev, dtype, in_bstride, out_bstride, _stream(stream)))
+
+
+def csahca_compress_norm_rope(kv, gate, pos_bias, gamma, out, B, n, c, m, entry0, d_rope, eps,
+                              theta, dtype, in_bstride, out_bstride, stream=None):
+    return _check("csahca_compress_norm_rope", load().csahca_compress_norm_rope(
+        _ptr(kv), _ptr(gate), _ptr(pos_bias), _ptr(gamma), _ptr(out), B, n, c, m, entry0, d_rope,
+        eps, theta, dtype, in_bstride, out_bstride, _stream(stream)))
+
+
+def csa_compress_overlap_norm_rope(kv_a, gate_a, kv_b, gate_b, pos_bias, gamma, out, B, n, c, m,
+                                   prev, entry0, d_rope, eps, theta, dtype, in_bstride,
+                                   out_bstride, stream=None):
+    return _check("csa_compress_overlap_norm_rope", load().csa_compress_overlap_norm_rope(
+        _ptr(kv_a), _ptr(gate_a), _ptr(kv_b), _ptr(gate_b), _ptr(pos_bias), _ptr(gamma), _ptr(out),
+        B, n, c, m, prev, entry0, d_rope, eps, theta, dtype, in_bstride, out_bstride,
+        _stream(stream)))
+
+
+def csahca_norm_rope(x, y, gamma, pos, B, T, H, c, pstride, d_rope, eps, theta, norm, dtype,
+                     stream=None):
+    return _check("csahca_norm_rope", load().csahca_norm_rope(
+        _ptr(x), _ptr(y), _ptr(gamma), _ptr(pos), B, T, H, c, pstride, d_rope, eps, theta, norm,
+        dtype, _stream(stream)))
 
 
 def csahca_kv_ring_rows(W, m):

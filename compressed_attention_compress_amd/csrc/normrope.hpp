@@ -1,0 +1,107 @@
+// RMSNorm and partial RoPE of rows held 8 channels per lane, shared by the pooling epilogue
+// and the row kernel.
+//
+// Sources: "DeepSeek-V4 Hybrid Attention: CSA, HCA, mHC, MoE", section IV (both branches
+// normalise the queries and the compressed KV entries and rotate only the last 64
+// dimensions); the MLA walk-through's "The Code: RoPE Helpers" (consecutive pairs read as
+// complex numbers, multiplied by e^{i pos f_i}, f_i = theta^(-2i/d)).  RMSNorm is the usual
+// y = x / sqrt(mean(x^2) + eps) * gamma.
+#pragma once
+
+#include "common.hpp"
+
+namespace csahca {
+
+constexpr int VEC = 8;  // channels per lane
+
+template <typename T>
+struct Vec8;
+
+template <>
+struct Vec8<uint16_t> {
+  u32x4 raw;
+  CSAHCA_DEV void load(const uint16_t* p) { raw = *reinterpret_cast<const u32x4*>(p); }
+  CSAHCA_DEV float get(int i) const {
+    uint32_t w = raw[i >> 1];
+    return (i & 1) ? __uint_as_float(w & 0xFFFF0000u) : __uint_as_float(w << 16);
+  }
+  static CSAHCA_DEV void store(uint16_t* p, const float* v) {
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
+    *reinterpret_cast<u32x4*>(p) = o;
+  }
+};
+
+template <>
+struct Vec8<float> {
+  f32x4 a, b;
+  CSAHCA_DEV void load(const float* p) {
+    a = *reinterpret_cast<const f32x4*>(p);
+    b = *reinterpret_cast<const f32x4*>(p + 4);
+  }
+  CSAHCA_DEV float get(int i) const { return i < 4 ? a[i] : b[i - 4]; }
+  static CSAHCA_DEV void store(float* p, const float* v) {
+    *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<f32x4*>(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
+  }
+};
+
+// What to apply to a row of c channels: RMSNorm (when `norm`) with gain `gamma` ([c] fp32,
+// NULL for unit gain), then RoPE on the last `d` channels (d % 8 == 0, 0 = none).
+struct NormRope {
+  const float* gamma;
+  float eps;
+  float theta;
+  int d;
+  int norm;
+};
+
+// Sum over the CV consecutive lanes that hold one row (CV a power of two, at most 64,
+// groups aligned to CV lanes).
+CSAHCA_DEV float row_sum(float v, int CV) {
+  for (int o = 1; o < CV; o <<= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Rotate the pair (a, b) = (x[2i], x[2i+1]) of the rotated block by pos * theta^(-2i/d).
+// The angle is formed in double: positions reach 2^20 and more, where a float angle would
+// be off by a sizeable fraction of a radian.
+CSAHCA_DEV void rope_rotate(float& a, float& b, long long pos, int i, int d, float theta) {
+  const double f = pow((double)theta, -2.0 * (double)i / (double)d);
+  double s, co;
+  sincos((double)pos * f, &s, &co);
+  const float cs = (float)co, sn = (float)s;
+  const float a2 = a * cs - b * sn;
+  const float b2 = a * sn + b * cs;
+  a = a2;
+  b = b2;
+}
+
+// Channels ch0 .. ch0+7 of a row whose c channels are spread over CV consecutive lanes.
+CSAHCA_DEV void norm_rope8(float (&v)[VEC], int ch0, int CV, int c, const NormRope& nr,
+                           long long pos) {
+  if (nr.norm) {
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) ss = fmaf(v[e], v[e], ss);
+    ss = row_sum(ss, CV);
+    const float inv = 1.0f / sqrtf(ss / (float)c + nr.eps);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) v[e] *= nr.gamma ? inv * nr.gamma[ch0 + e] : inv;
+  }
+  if (ch0 >= c - nr.d) {
+    const int i0 = (ch0 - (c - nr.d)) / 2;
+#pragma unroll
+    for (int q = 0; q < VEC / 2; ++q) rope_rotate(v[2 * q], v[2 * q + 1], pos, i0 + q, nr.d, nr.theta);
+  }
+}
+
+// Host-side check shared by the entry points that take a NormRope.
+inline bool norm_rope_args_ok(int c, int d, float eps, float theta) {
+  const int CV = c / VEC;
+  return c % VEC == 0 && CV >= 1 && CV <= 64 && (CV & (CV - 1)) == 0 && d >= 0 && d <= c &&
+         d % 8 == 0 && eps >= 0.f && eps < 1e30f && theta > 0.f && theta < 1e30f;
+}
+
+}  // namespace csahca

@@ -14,44 +14,14 @@
 // Overlapped two-stream form (csa_compress_overlap, section V.1's equation with two KV
 // streams): entry i walks stream a over block i and then stream b over block i-1 with
 // the same running softmax, which is one joint softmax over the 2m logits.
+#include "normrope.hpp"
 #include "pool.hpp"
 
 namespace {
 
-constexpr int VEC = 8;      // channels per thread
-
-template <typename T>
-struct Vec8;
-
-template <>
-struct Vec8<uint16_t> {
-  u32x4 raw;
-  CSAHCA_DEV void load(const uint16_t* p) { raw = *reinterpret_cast<const u32x4*>(p); }
-  CSAHCA_DEV float get(int i) const {
-    uint32_t w = raw[i >> 1];
-    return (i & 1) ? __uint_as_float(w & 0xFFFF0000u) : __uint_as_float(w << 16);
-  }
-  static CSAHCA_DEV void store(uint16_t* p, const float* v) {
-    u32x4 o;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
-    *reinterpret_cast<u32x4*>(p) = o;
-  }
-};
-
-template <>
-struct Vec8<float> {
-  f32x4 a, b;
-  CSAHCA_DEV void load(const float* p) {
-    a = *reinterpret_cast<const f32x4*>(p);
-    b = *reinterpret_cast<const f32x4*>(p + 4);
-  }
-  CSAHCA_DEV float get(int i) const { return i < 4 ? a[i] : b[i - 4]; }
-  static CSAHCA_DEV void store(float* p, const float* v) {
-    *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
-    *reinterpret_cast<f32x4*>(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
-  }
-};
+using csahca::NormRope;
+using csahca::Vec8;
+using csahca::VEC;
 
 // Online softmax-weighted sum over tokens [j_lo, j_hi) of one 8-channel slice.  Full
 // chunks of UB tokens issue all their loads first and reduce the chunk as balanced trees
@@ -120,7 +90,7 @@ CSAHCA_DEV void pool_run(const T* __restrict__ xp, const T* __restrict__ zp,
   }
 }
 
-template <typename T, int UB, bool HAS_P, bool OV>
+template <typename T, int UB, bool HAS_P, bool OV, bool NR>
 __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ X,
                                                    const T* __restrict__ Z,
                                                    const T* __restrict__ Xb,
@@ -128,7 +98,7 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ X,
                                                    const float* __restrict__ P,
                                                    T* __restrict__ out, int N, int c, int m,
                                                    int prev, long long in_bs, long long out_bs,
-                                                   long long total) {
+                                                   long long total, NormRope nr, long long entry0) {
   const long long item = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (item >= total) return;
   const int CV = c / VEC;
@@ -160,6 +130,8 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ X,
   float res[VEC];
 #pragma unroll
   for (int e = 0; e < VEC; ++e) res[e] = acc[e] / sum[e];
+  // the CV lanes of one entry are consecutive and aligned, so the row sum stays in them
+  if (NR) csahca::norm_rope8(res, cv * VEC, CV, c, nr, (long long)m * (entry0 + i));
   Vec8<T>::store(out + (long long)b * out_bs + (long long)i * c + (long long)cv * VEC, res);
 }
 
@@ -175,16 +147,17 @@ CSAHCA_DEV void store_one<uint16_t>(uint16_t* p, float v) { *p = f32_to_bf16(v);
 template <>
 CSAHCA_DEV void store_one<float>(float* p, float v) { *p = v; }
 
-template <typename T, int UB, bool HAS_P, bool OV>
-__global__ __launch_bounds__(256) void pool_block_kernel(const T* __restrict__ X,
+template <typename T, int UB, bool HAS_P, bool OV, bool NR>
+__global__ __launch_bounds__(NR ? 512 : 256) void pool_block_kernel(const T* __restrict__ X,
                                                         const T* __restrict__ Z,
                                                         const T* __restrict__ Xb,
                                                         const T* __restrict__ Zb,
                                                         const float* __restrict__ P,
                                                         T* __restrict__ out, int N, int c,
                                                         int m, int prev, int S, int CVG,
-                                                        long long in_bs, long long out_bs) {
-  extern __shared__ float part[];  // [S][CVG][3][VEC]
+                                                        long long in_bs, long long out_bs,
+                                                        NormRope nr, long long entry0) {
+  extern __shared__ float part[];  // [S][CVG][3][VEC], then (NR) [c] results + [16] sums
   const int CG = c / VEC / CVG;
   const int cvl = threadIdx.x % CVG, s = threadIdx.x / CVG;
   const int cg = blockIdx.x % CG, bi = blockIdx.x / CG;
@@ -219,6 +192,7 @@ __global__ __launch_bounds__(256) void pool_block_kernel(const T* __restrict__ X
   }
   __syncthreads();
   T* orow = out + (long long)b * out_bs + (long long)i * c + (long long)cg * CVG * VEC;
+  float* fin = part + (size_t)S * CVG * 3 * VEC;  // NR: the entry's c pooled values
   for (int t = threadIdx.x; t < CVG * VEC; t += blockDim.x) {
     const int sl = t / VEC, e = t - sl * VEC;
     float M = -INFINITY;
@@ -230,43 +204,115 @@ __global__ __launch_bounds__(256) void pool_block_kernel(const T* __restrict__ X
       sm = fmaf(pr[VEC + e], w, sm);
       av = fmaf(pr[2 * VEC + e], w, av);
     }
-    store_one<T>(orow + t, av / sm);
+    if (NR)
+      fin[t] = av / sm;
+    else
+      store_one<T>(orow + t, av / sm);
+  }
+  if (NR) {
+    // the workgroup holds the whole entry (CVG * VEC == c): RMS over the c values, then
+    // the gain and the rotation of the last d channels, pairs read from LDS
+    float* wsum = fin + c;
+    __syncthreads();
+    float inv = 1.f;
+    if (nr.norm) {
+      float ss = 0.f;
+      for (int t = threadIdx.x; t < c; t += blockDim.x) ss = fmaf(fin[t], fin[t], ss);
+      ss = csahca::row_sum(ss, 64);
+      if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = ss;
+      __syncthreads();
+      ss = 0.f;
+      for (int w = 0; w < (int)(blockDim.x + 63) / 64; ++w) ss += wsum[w];  // fixed order
+      inv = 1.0f / sqrtf(ss / (float)c + nr.eps);
+    }
+    const long long pos = (long long)m * (entry0 + i);
+    for (int t = threadIdx.x; t < c; t += blockDim.x) {
+      float v = fin[t] * (nr.gamma ? inv * nr.gamma[t] : inv);
+      if (t >= c - nr.d) {
+        const int u = t ^ 1;  // the pair's other channel
+        const float w = fin[u] * (nr.gamma ? inv * nr.gamma[u] : inv);
+        float a = (t & 1) ? w : v, bb = (t & 1) ? v : w;
+        csahca::rope_rotate(a, bb, pos, (t - (c - nr.d)) >> 1, nr.d, nr.theta);
+        v = (t & 1) ? bb : a;
+      }
+      store_one<T>(orow + t, v);
+    }
   }
 }
 
-template <typename T, bool HAS_P, bool OV>
+template <typename T, bool HAS_P, bool OV, bool NR>
 void launch_pool(const void* kv, const void* gate, const void* kv_b, const void* gate_b,
                  const float* pos_bias, void* out, int B, long long N, int c, int m, int prev,
-                 long long in_bs, long long out_bs, hipStream_t st) {
+                 long long in_bs, long long out_bs, const NormRope& nr, long long entry0,
+                 hipStream_t st) {
   const long long total = (long long)B * N * (c / 8);
   const int CV = c / VEC;
   const int mt = OV ? 2 * m : m;  // tokens an entry reads
   const T *X = (const T*)kv, *Z = (const T*)gate, *Xb = (const T*)kv_b, *Zb = (const T*)gate_b;
   if (total < 32768 && mt >= 8) {
     // few blocks of many tokens: 8-channel slices in groups of up to 8 per workgroup,
-    // tokens in sub-ranges of at least 4, at most 256 threads per workgroup
-    int CVG = 8;
-    while (CV % CVG != 0) CVG /= 2;
-    const int smax = 256 / CVG;
+    // tokens in sub-ranges of at least 4, at most 256 threads per workgroup.  With the
+    // norm the workgroup holds the whole entry (all CV slices, at most 512 threads, a
+    // whole number of waves).
+    int CVG = 8, smax, unit = 1;
+    if (NR) {
+      CVG = CV;
+      smax = 512 / CV;
+      unit = CV >= 64 ? 1 : 64 / CV;
+    } else {
+      while (CV % CVG != 0) CVG /= 2;
+      smax = 256 / CVG;
+    }
     const int span = max(4, cdiv(mt, smax));
-    const int S = cdiv(mt, span);
-    const size_t lds = (size_t)S * CVG * 3 * VEC * sizeof(float);
+    const int S = cdiv(cdiv(mt, span), unit) * unit;
+    const size_t lds = ((size_t)S * CVG * 3 * VEC + (NR ? (size_t)c + 16 : 0)) * sizeof(float);
     const unsigned grid = (unsigned)(B * N * (CV / CVG)), threads = (unsigned)(S * CVG);
     if (span % 8 == 0 && m % 8 == 0)
-      hipLaunchKernelGGL((pool_block_kernel<T, 8, HAS_P, OV>), dim3(grid), dim3(threads), lds, st,
-                         X, Z, Xb, Zb, pos_bias, (T*)out, (int)N, c, m, prev, S, CVG, in_bs, out_bs);
+      hipLaunchKernelGGL((pool_block_kernel<T, 8, HAS_P, OV, NR>), dim3(grid), dim3(threads), lds, st,
+                         X, Z, Xb, Zb, pos_bias, (T*)out, (int)N, c, m, prev, S, CVG, in_bs, out_bs,
+                         nr, entry0);
     else
-      hipLaunchKernelGGL((pool_block_kernel<T, 4, HAS_P, OV>), dim3(grid), dim3(threads), lds, st,
-                         X, Z, Xb, Zb, pos_bias, (T*)out, (int)N, c, m, prev, S, CVG, in_bs, out_bs);
+      hipLaunchKernelGGL((pool_block_kernel<T, 4, HAS_P, OV, NR>), dim3(grid), dim3(threads), lds, st,
+                         X, Z, Xb, Zb, pos_bias, (T*)out, (int)N, c, m, prev, S, CVG, in_bs, out_bs,
+                         nr, entry0);
     return;
   }
   const unsigned blocks = (unsigned)cdiv<long long>(total, 256);
   if (m % 8 == 0)
-    hipLaunchKernelGGL((pool_kernel<T, 8, HAS_P, OV>), dim3(blocks), dim3(256), 0, st, X, Z, Xb, Zb,
-                       pos_bias, (T*)out, (int)N, c, m, prev, in_bs, out_bs, total);
+    hipLaunchKernelGGL((pool_kernel<T, 8, HAS_P, OV, NR>), dim3(blocks), dim3(256), 0, st, X, Z, Xb,
+                       Zb, pos_bias, (T*)out, (int)N, c, m, prev, in_bs, out_bs, total, nr, entry0);
   else
-    hipLaunchKernelGGL((pool_kernel<T, 4, HAS_P, OV>), dim3(blocks), dim3(256), 0, st, X, Z, Xb, Zb,
-                       pos_bias, (T*)out, (int)N, c, m, prev, in_bs, out_bs, total);
+    hipLaunchKernelGGL((pool_kernel<T, 4, HAS_P, OV, NR>), dim3(blocks), dim3(256), 0, st, X, Z, Xb,
+                       Zb, pos_bias, (T*)out, (int)N, c, m, prev, in_bs, out_bs, total, nr, entry0);
+}
+
+struct PoolArgs {
+  const void *kv, *gate, *kv_b, *gate_b;
+  const float* pos_bias;
+  void* out;
+  int B;
+  long long N;
+  int c, m, prev;
+  long long in_bs, out_bs;
+  NormRope nr;
+  long long entry0;
+  hipStream_t st;
+};
+
+template <typename T, bool HP, bool OV, bool NR>
+void run_pool(const PoolArgs& a) {
+  launch_pool<T, HP, OV, NR>(a.kv, a.gate, a.kv_b, a.gate_b, a.pos_bias, a.out, a.B, a.N, a.c, a.m,
+                             a.prev, a.in_bs, a.out_bs, a.nr, a.entry0, a.st);
+}
+
+template <typename T>
+void pick_pool(const PoolArgs& a, bool hp, bool ov, bool nr) {
+  using F = void (*)(const PoolArgs&);
+  static const F tab[8] = {run_pool<T, false, false, false>, run_pool<T, false, false, true>,
+                           run_pool<T, false, true, false>,  run_pool<T, false, true, true>,
+                           run_pool<T, true, false, false>,  run_pool<T, true, false, true>,
+                           run_pool<T, true, true, false>,   run_pool<T, true, true, true>};
+  tab[(hp ? 4 : 0) + (ov ? 2 : 0) + (nr ? 1 : 0)](a);
 }
 
 }  // namespace
@@ -275,7 +321,8 @@ namespace csahca {
 
 int pool_entry(const char* name, const void* kv, const void* gate, const void* kv_b,
                const void* gate_b, bool ov, int prev, const float* pos_bias, void* out, int B,
-               int n, int c, int m, int dtype, long long in_bs, long long out_bs, void* stream) {
+               int n, int c, int m, int dtype, long long in_bs, long long out_bs, void* stream,
+               const NormRope* nr, long long entry0) {
   using namespace csahca;
   if (B < 1 || n < 0 || c < 8 || (c % 8) != 0 || m < 1 || m > 4096) {
     set_error("%s: need B >= 1, n >= 0, c >= 8 with c %% 8 == 0, 1 <= m <= 4096", name);
@@ -315,27 +362,17 @@ int pool_entry(const char* name, const void* kv, const void* gate, const void* k
     set_error("%s: problem too large for one launch", name);
     return CSAHCA_ENOTSUP;
   }
-  hipStream_t st = (hipStream_t)stream;
-#define CSAHCA_POOL_LAUNCH(T, HP, O) \
-  launch_pool<T, HP, O>(kv, gate, kv_b, gate_b, pos_bias, out, B, N, c, m, prev, in_bs, out_bs, st)
-  if (dtype == CSAHCA_BF16) {
-    if (ov) {
-      if (pos_bias) CSAHCA_POOL_LAUNCH(uint16_t, true, true);
-      else CSAHCA_POOL_LAUNCH(uint16_t, false, true);
-    } else {
-      if (pos_bias) CSAHCA_POOL_LAUNCH(uint16_t, true, false);
-      else CSAHCA_POOL_LAUNCH(uint16_t, false, false);
-    }
-  } else {
-    if (ov) {
-      if (pos_bias) CSAHCA_POOL_LAUNCH(float, true, true);
-      else CSAHCA_POOL_LAUNCH(float, false, true);
-    } else {
-      if (pos_bias) CSAHCA_POOL_LAUNCH(float, true, false);
-      else CSAHCA_POOL_LAUNCH(float, false, false);
-    }
+  if (nr && (!norm_rope_args_ok(c, nr->d, nr->eps, nr->theta) || entry0 < 0)) {
+    set_error("%s: the norm needs c / 8 a power of two <= 64, d_rope %% 8 == 0 and <= c, "
+              "eps >= 0, theta > 0 and entry0 >= 0", name);
+    return CSAHCA_EINVAL;
   }
-#undef CSAHCA_POOL_LAUNCH
+  PoolArgs a{kv, gate, kv_b, gate_b, pos_bias, out, B, N, c, m, prev, in_bs, out_bs,
+             nr ? *nr : NormRope{nullptr, 0.f, 1.f, 0, 0}, entry0, (hipStream_t)stream};
+  if (dtype == CSAHCA_BF16)
+    pick_pool<uint16_t>(a, pos_bias != nullptr, ov, nr != nullptr);
+  else
+    pick_pool<float>(a, pos_bias != nullptr, ov, nr != nullptr);
   return launch_status(name);
 }
 
@@ -347,14 +384,14 @@ extern "C" int csa_compress(const void* kv, const void* gate, const float* pos_b
                             int B, int n, int c, int m, int dtype, long long in_bstride,
                             long long out_bstride, void* stream) {
   return pool_entry("csa_compress", kv, gate, nullptr, nullptr, false, 0, pos_bias, out, B, n, c,
-                    m, dtype, in_bstride, out_bstride, stream);
+                    m, dtype, in_bstride, out_bstride, stream, nullptr, 0);
 }
 
 extern "C" int hca_compress(const void* kv, const void* gate, const float* pos_bias, void* out,
                             int B, int n, int c, int m, int dtype, long long in_bstride,
                             long long out_bstride, void* stream) {
   return pool_entry("hca_compress", kv, gate, nullptr, nullptr, false, 0, pos_bias, out, B, n, c,
-                    m, dtype, in_bstride, out_bstride, stream);
+                    m, dtype, in_bstride, out_bstride, stream, nullptr, 0);
 }
 
 extern "C" int csa_compress_overlap(const void* kv_a, const void* gate_a, const void* kv_b,
@@ -362,5 +399,28 @@ extern "C" int csa_compress_overlap(const void* kv_a, const void* gate_a, const 
                                     int n, int c, int m, int prev, int dtype,
                                     long long in_bstride, long long out_bstride, void* stream) {
   return pool_entry("csa_compress_overlap", kv_a, gate_a, kv_b, gate_b, true, prev, pos_bias, out,
-                    B, n, c, m, dtype, in_bstride, out_bstride, stream);
+                    B, n, c, m, dtype, in_bstride, out_bstride, stream, nullptr, 0);
+}
+
+extern "C" int csahca_compress_norm_rope(const void* kv, const void* gate, const float* pos_bias,
+                                         const float* gamma, void* out, int B, int n, int c,
+                                         int m, long long entry0, int d_rope, float eps,
+                                         float theta, int dtype, long long in_bstride,
+                                         long long out_bstride, void* stream) {
+  const NormRope nr{gamma, eps, theta, d_rope, 1};
+  return pool_entry("csahca_compress_norm_rope", kv, gate, nullptr, nullptr, false, 0, pos_bias,
+                    out, B, n, c, m, dtype, in_bstride, out_bstride, stream, &nr, entry0);
+}
+
+extern "C" int csa_compress_overlap_norm_rope(const void* kv_a, const void* gate_a,
+                                              const void* kv_b, const void* gate_b,
+                                              const float* pos_bias, const float* gamma,
+                                              void* out, int B, int n, int c, int m, int prev,
+                                              long long entry0, int d_rope, float eps,
+                                              float theta, int dtype, long long in_bstride,
+                                              long long out_bstride, void* stream) {
+  const NormRope nr{gamma, eps, theta, d_rope, 1};
+  return pool_entry("csa_compress_overlap_norm_rope", kv_a, gate_a, kv_b, gate_b, true, prev,
+                    pos_bias, out, B, n, c, m, dtype, in_bstride, out_bstride, stream, &nr,
+                    entry0);
 }

@@ -243,6 +243,51 @@ int hca_attend_sink(const void* q, const void* ckv, const void* win_kv, const in
                     void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * csahca_compress_norm_rope / csa_compress_overlap_norm_rope / csahca_norm_rope -- RMSNorm
+ * and partial RoPE, fused into pooling or on rows.
+ * Source: "DeepSeek-V4 Hybrid Attention: CSA, HCA, mHC, MoE", section IV (both branches
+ * apply RMSNorm to the queries and to the compressed KV entries, and RoPE to the last 64
+ * dimensions only); the MLA walk-through's "The Code: RoPE Helpers" (the rotated
+ * dimensions are consecutive pairs (2i, 2i+1), read as complex numbers and multiplied by
+ * e^{i pos f_i}, f_i = theta^(-2i/d); theta = 10000 there).
+ *
+ *   norm_rope(x, pos)[ch] = rope_d( x / sqrt(mean_ch(x^2) + eps) * gamma , pos )
+ * where rope_d rotates the last d channels as above and leaves the others unchanged.
+ * Readings (the pages name RMSNorm but do not write it): the usual definition with a
+ * per-channel gain and the caller's eps.  A compressed entry s carries position m * s,
+ * the first raw position of its block.  Angles are formed in double precision, rotation
+ * and normalisation in float32, the result rounded once to the row dtype.
+ *
+ * csahca_compress_norm_rope: csa_compress / hca_compress (same arguments and limits),
+ *   then every emitted entry is normalised and rotated; the first emitted entry is
+ *   entry `entry0` of the cache (0 for a whole pass, the entry's index for an append).
+ * csa_compress_overlap_norm_rope: csa_compress_overlap, then the same.
+ *   gamma   [c] float32 device, or NULL for unit gain.
+ *   d_rope  rotated channels at the end of the row, d_rope % 8 == 0 and <= c (64 in the
+ *           V4 settings, 0 for none).
+ *   eps >= 0, theta > 0.  c / 8 must be a power of two no larger than 64 (c <= 512).
+ *
+ * csahca_norm_rope: rows x [B, T, H, c] of `dtype` (contiguous) -> y (same shape; y == x
+ *   is allowed).  Row (b, t, h) has position pos[b] + t * pstride: queries pass q_pos and
+ *   pstride 1 (H = n_h), a window source its win_pos and 1 (H = 1), compressed entries
+ *   built elsewhere NULL and m.  pos: [B] int32 device, or NULL for 0.  norm = 0 applies
+ *   RoPE only.  Limits as above; T == 0 does nothing.
+ */
+int csahca_compress_norm_rope(const void* kv, const void* gate, const float* pos_bias,
+                              const float* gamma, void* out, int B, int n, int c, int m,
+                              long long entry0, int d_rope, float eps, float theta, int dtype,
+                              long long in_bstride, long long out_bstride, void* stream);
+int csa_compress_overlap_norm_rope(const void* kv_a, const void* gate_a, const void* kv_b,
+                                   const void* gate_b, const float* pos_bias,
+                                   const float* gamma, void* out, int B, int n, int c, int m,
+                                   int prev, long long entry0, int d_rope, float eps,
+                                   float theta, int dtype, long long in_bstride,
+                                   long long out_bstride, void* stream);
+int csahca_norm_rope(const void* x, void* y, const float* gamma, const int* pos, int B, int T,
+                     int H, int c, int pstride, int d_rope, float eps, float theta, int norm,
+                     int dtype, void* stream);
+
+/*
  * csahca_kv_ring_rows / csahca_kv_append / csahca_kv_fork -- the cache lifecycle of one
  * layer: raw tokens arrive, completed blocks become compressed entries, the recent window
  * stays exact, a request can start from another's prefix.

@@ -175,3 +175,39 @@ def test_kv_cache_validation():
     f = list(fok)
     f[13] = 3 * c
     assert fk(*f) == EINVAL
+
+
+def test_norm_rope_validation():
+    L = lib.load()
+    nr = L.csahca_norm_rope
+    ok = [FAKE, FAKE, None, None, 2, 3, 4, 512, 1, 64, 1e-6, 10000.0, 1, 1, None]
+
+    def with_(i, v, base=ok):
+        a = list(base)
+        a[i] = v
+        return a
+    assert nr(*with_(7, 96)) == EINVAL       # c / 8 = 12 is not a power of two
+    assert nr(*with_(7, 1024)) == EINVAL     # c / 8 > 64
+    assert nr(*with_(9, 60)) == EINVAL       # d_rope % 8
+    assert nr(*with_(9, 520)) == EINVAL      # d_rope > c
+    assert nr(*with_(10, -1.0)) == EINVAL    # eps
+    assert nr(*with_(11, 0.0)) == EINVAL     # theta
+    assert nr(*with_(12, 2)) == EINVAL       # norm flag
+    assert nr(*with_(13, 2)) == ENOTSUP      # fp8 rows
+    assert nr(*with_(1, FAKE + 8)) == EINVAL  # alignment
+    assert nr(*with_(0, None)) == EINVAL
+    assert nr(*with_(5, 0)) == 0             # no rows
+    cp = L.csahca_compress_norm_rope
+    cok = [FAKE, FAKE, None, None, FAKE, 1, 8, 512, 4, 0, 64, 1e-6, 10000.0, 1, 8 * 512, 2 * 512,
+           None]
+    assert cp(*with_(7, 96, cok)) == EINVAL
+    assert cp(*with_(10, 12, cok)) == EINVAL
+    assert cp(*with_(9, -1, cok)) == EINVAL  # entry0
+    assert "csahca_compress_norm_rope" in lib.last_error()
+    assert cp(*with_(13, 2, cok)) == ENOTSUP
+    ov = L.csa_compress_overlap_norm_rope
+    ook = [FAKE, FAKE, FAKE, FAKE, None, None, FAKE, 1, 8, 512, 4, 0, 0, 64, 1e-6, 10000.0, 1,
+           8 * 512, 2 * 512, None]
+    assert ov(*with_(12, -3, ook)) == EINVAL
+    assert ov(*with_(11, 2, ook)) == EINVAL  # prev
+    assert ov(*with_(2, None, ook)) == EINVAL

@@ -53,6 +53,9 @@ def parse():
     ap.add_argument("--sink", action="store_true",
                     help="run both attention calls with a per-head attention sink "
                          "(csa_attend_sink / hca_attend_sink)")
+    ap.add_argument("--norm-rope", action="store_true",
+                    help="run the step with RMSNorm + partial RoPE (64 dims): fused into the "
+                         "pooling of new blocks, and on the queries and window rows")
     ap.add_argument("--kv-append", action="store_true",
                     help="time the cache lifecycle at the config's shape (csahca_kv_append of a "
                          "chunk and of one decode token, CSA and HCA caches) instead of the step")
@@ -65,7 +68,9 @@ def parse():
 class Workload:
     """All device state of one workload: inputs, caches, replicas, outputs, workspaces."""
 
-    def __init__(self, cfg, replicas, sink=False):
+    NR_D, NR_EPS, NR_THETA = 64, 1e-6, 10000.0
+
+    def __init__(self, cfg, replicas, sink=False, norm_rope=False):
         import torch
 
         import compressed_attention_compress_amd as lib
@@ -88,12 +93,30 @@ class Workload:
         # the pooled caches as a prefill would leave them (untimed): every complete block
         # before the step's own new blocks
         self.n_old = n - (self.Tq if self.kind == "prefill" else 1)
+        self.nr = norm_rope
+        if norm_rope:  # seeded gains U(0.5, 1.5) for the KV rows and for the queries
+            gn = torch.Generator(device=dev).manual_seed(77)
+            self.g_kv = torch.rand((c,), generator=gn, device=dev) + 0.5
+            self.g_q = torch.rand((c,), generator=gn, device=dev) + 0.5
+            # normalised, rotated window rows (positions n - Tq - W + 1 .. n - 1) and queries
+            self.nr_wpos0 = max(0, n - self.Tq - cfg.W + 1)
+            self.nr_L = n - self.nr_wpos0
+            self.nr_win_pos = torch.full((B,), self.nr_wpos0, dtype=torch.int32, device=dev)
+            self.nr_win = {l: torch.empty((B, self.nr_L, c), dtype=torch.int16, device=dev)
+                           for l in self.layers}
+            self.nr_q = {l: torch.empty((B, self.Tq, cfg.n_h, c), dtype=torch.int16, device=dev)
+                         for l in self.layers}
         base = {}
         for l in self.layers:
             m = cfg.m if l == "csa" else cfg.m_hca
             C = torch.zeros((B, n // m, c), dtype=torch.int16, device=dev)
-            lib.csa_compress(prob[f"X_{l}"], prob[f"Z_{l}"], None, C, B, self.n_old, c, m, dt,
-                             n * c, (n // m) * c)
+            if norm_rope:
+                lib.csahca_compress_norm_rope(prob[f"X_{l}"], prob[f"Z_{l}"], None, self.g_kv, C, B,
+                                              self.n_old, c, m, 0, self.NR_D, self.NR_EPS,
+                                              self.NR_THETA, dt, n * c, (n // m) * c)
+            else:
+                lib.csa_compress(prob[f"X_{l}"], prob[f"Z_{l}"], None, C, B, self.n_old, c, m, dt,
+                                 n * c, (n // m) * c)
             base[f"C_{l}"] = C
             base[f"Q_{l}"] = prob[f"Q_{l}"]
         if "csa" in self.layers:
@@ -140,8 +163,14 @@ class Workload:
                 continue
             X, Z, C = prob[f"X_{l}"], prob[f"Z_{l}"], self.rep[r][f"C_{l}"]
             tok0 = first_blk * m
-            lib.csa_compress(X[:, tok0:], Z[:, tok0:], None, C[:, first_blk:], B, n_new * m, c, m,
-                             cfg.dtype, n * c, (n // m) * c)
+            if self.nr:
+                lib.csahca_compress_norm_rope(X[:, tok0:], Z[:, tok0:], None, self.g_kv,
+                                              C[:, first_blk:], B, n_new * m, c, m, first_blk,
+                                              self.NR_D, self.NR_EPS, self.NR_THETA, cfg.dtype,
+                                              n * c, (n // m) * c)
+            else:
+                lib.csa_compress(X[:, tok0:], Z[:, tok0:], None, C[:, first_blk:], B, n_new * m, c,
+                                 m, cfg.dtype, n * c, (n // m) * c)
 
     def index(self, r, split=True):
         cfg, lib, rp = self.cfg, self.lib, self.rep[r]
@@ -161,21 +190,37 @@ class Workload:
                                        cfg.B, self.Tq, cfg.n_ih, cfg.c_I, self.N_c, cfg.k,
                                        self.scores, self.iws, self.iws_b)
 
+    def norm_rope_rows(self, r, l):
+        """Queries and window rows of layer l through RMSNorm + partial RoPE; returns the
+        (queries, window source, win_pos, L) the attention call reads."""
+        cfg, lib, rp, prob = self.cfg, self.lib, self.rep[r], self.prob
+        B, c, n = cfg.B, cfg.c, self.n
+        if not self.nr:
+            return rp[f"Q_{l}"], prob[f"X_{l}"], self.win_pos, n
+        lib.csahca_norm_rope(rp[f"Q_{l}"], self.nr_q[l], self.g_q, self.q_pos, B, self.Tq, cfg.n_h, c,
+                             1, self.NR_D, self.NR_EPS, self.NR_THETA, 1, cfg.dtype)
+        lib.csahca_norm_rope(prob[f"X_{l}"][:, self.nr_wpos0:], self.nr_win[l], self.g_kv,
+                             self.nr_win_pos, B, self.nr_L, 1, c, 1, self.NR_D, self.NR_EPS,
+                             self.NR_THETA, 1, cfg.dtype, x_bstride=n * c, y_bstride=self.nr_L * c)
+        return self.nr_q[l], self.nr_win[l], self.nr_win_pos, self.nr_L
+
     def attend(self, r):
         cfg, lib, rp, prob = self.cfg, self.lib, self.rep[r], self.prob
         B, c, n = cfg.B, cfg.c, self.n
         sk = self.sink
         if "csa" in self.layers:
-            args = (rp["Q_csa"], rp["C_csa"], self.idx, prob["X_csa"], self.win_pos, self.q_pos, B,
-                    self.Tq, cfg.n_h, c, self.N_c, cfg.k, n, cfg.W, self.scale)
+            q, win, wpos, L = self.norm_rope_rows(r, "csa")
+            args = (q, rp["C_csa"], self.idx, win, wpos, self.q_pos, B,
+                    self.Tq, cfg.n_h, c, self.N_c, cfg.k, L, cfg.W, self.scale)
             tail = (cfg.dtype, self.out["csa"], None, self.cws, self.cws_b)
             if sk is None:
                 lib.csa_attend(*args, *tail)
             else:
                 lib.csa_attend_sink(*args, sk, *tail)
         if "hca" in self.layers:
-            args = (rp["Q_hca"], rp["C_hca"], prob["X_hca"], self.win_pos, self.q_pos, cfg.m_hca, B,
-                    self.Tq, cfg.n_h, c, self.N_h, n, cfg.W, self.scale)
+            q, win, wpos, L = self.norm_rope_rows(r, "hca")
+            args = (q, rp["C_hca"], win, wpos, self.q_pos, cfg.m_hca, B,
+                    self.Tq, cfg.n_h, c, self.N_h, L, cfg.W, self.scale)
             tail = (cfg.dtype, self.out["hca"], None, self.hws, self.hws_b)
             if sk is None:
                 lib.hca_attend(*args, *tail)
@@ -225,6 +270,10 @@ class Workload:
             att = rows * c * e + 2 * B * Tq * cfg.n_h * c * e
             detail["hca_attend"] = att
             total += att
+        if self.nr:  # queries and window rows read and written once more
+            nrb = len(self.layers) * 2 * B * (Tq * cfg.n_h + self.nr_L) * c * e
+            detail["norm_rope_rows"] = nrb
+            total += nrb
         return total, detail
 
     def index_score_bytes(self):
@@ -644,7 +693,7 @@ def main():
     warmup = args.warmup if args.warmup is not None else (50 if decode else 3)
     R = args.replicas if args.replicas is not None else (6 if decode else 1)
     torch.cuda.set_device(0)
-    wl = Workload(cfg, R, sink=args.sink)
+    wl = Workload(cfg, R, sink=args.sink, norm_rope=args.norm_rope)
 
     # warm up eagerly (also sets the library's one-time kernel attributes)
     for i in range(warmup):
@@ -723,7 +772,9 @@ def main():
                    "n_ih": cfg.n_ih, "c_I": cfg.c_I, "window": cfg.W, "replicas": R,
                    "timing": "hip graph per step, rotating replicas",
                    **({"attention_sink": "per-head, N(0, 2^2)"} if args.sink else {}),
-                   **({"indexer_keys": "MX FP4 (E2M1, E8M0 per 32), FP8 queries"} if args.fp4_keys else {})},
+                   **({"indexer_keys": "MX FP4 (E2M1, E8M0 per 32), FP8 queries"} if args.fp4_keys else {}),
+                   **({"norm_rope": "RMSNorm + RoPE on the last 64 dims: entries, queries, window"}
+                      if args.norm_rope else {})},
         "hbm_gbs": round(abytes / sec / 1e9, 1),
         "hbm_frac": round(abytes / sec / 1e9 / HBM_PEAK_GBS, 4),
         "algorithmic_bytes_per_step": abytes,

@@ -28,7 +28,8 @@ _SIGNATURES = {
                                        _LL, _LL, _P]),
     "csa_compress_overlap_norm_rope": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _LL,
                                             _I, _F, _F, _I, _LL, _LL, _P]),
-    "csahca_norm_rope": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _F, _I, _I, _P]),
+    "csahca_norm_rope": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _F, _I, _I, _LL, _LL,
+                              _P]),
     "csahca_kv_ring_rows": (_I, [_I, _I]),
     "csahca_kv_append": (_I, [_P, _P, _P, _P, _P, _P, _I, _LL, _I, _I, _I, _I, _I, _LL, _LL, _LL,
                               _P]),
@@ -146,10 +147,13 @@ def csa_compress_overlap_norm_rope(kv_a, gate_a, kv_b, gate_b, pos_bias, gamma, 
 
 
 def csahca_norm_rope(x, y, gamma, pos, B, T, H, c, pstride, d_rope, eps, theta, norm, dtype,
-                     stream=None):
+                     x_bstride=None, y_bstride=None, stream=None):
+    """Strides default to contiguous [B, T, H, c]."""
+    seq = T * H * c
     return _check("csahca_norm_rope", load().csahca_norm_rope(
         _ptr(x), _ptr(y), _ptr(gamma), _ptr(pos), B, T, H, c, pstride, d_rope, eps, theta, norm,
-        dtype, _stream(stream)))
+        dtype, seq if x_bstride is None else x_bstride, seq if y_bstride is None else y_bstride,
+        _stream(stream)))
 
 
 def csahca_kv_ring_rows(W, m):

@@ -19,30 +19,45 @@ using csahca::VEC;
 template <typename T>
 __global__ __launch_bounds__(256) void norm_rope_rows(const T* __restrict__ x, T* y, NormRope nr,
                                                       const int* __restrict__ pos, int T_, int H,
-                                                      int c, int pstride, long long rows) {
+                                                      int c, int pstride, long long rows,
+                                                      long long x_bs, long long y_bs) {
   const int CV = c / VEC;
   const long long item = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  const long long row = item / CV;
+  long long row;
+  int cv, t, b;
+  if (rows * CV <= 0x7FFFFFFFLL) {  // 32-bit index math (64-bit division is a long sequence)
+    const uint32_t it = (uint32_t)item, r32 = it / (uint32_t)CV, bt = r32 / (uint32_t)H;
+    row = r32;
+    cv = (int)(it - r32 * (uint32_t)CV);
+    b = (int)(bt / (uint32_t)T_);
+    t = (int)(bt - (uint32_t)b * (uint32_t)T_);
+  } else {
+    row = item / CV;
+    cv = (int)(item - row * CV);
+    const long long bt = row / H;
+    t = (int)(bt % T_);
+    b = (int)(bt / T_);
+  }
   if (row >= rows) return;  // whole rows leave together (CV divides 64)
-  const int cv = (int)(item - row * CV);
-  const long long bt = row / H;
-  const int t = (int)(bt % T_);
-  const int b = (int)(bt / T_);
-  const long long p = (pos ? (long long)pos[b] : 0LL) + (long long)t * pstride;
+  const long long in_seq = (row - (long long)b * T_ * H) * c + cv * VEC;  // (t, h) offset
   Vec8<T> v;
-  v.load(x + row * c + cv * VEC);
+  v.load(x + b * x_bs + in_seq);  // the row, its gains and its position load together
+  float g[VEC];
+  csahca::load_gain8(nr, cv * VEC, g);
+  const long long p = (pos ? (long long)pos[b] : 0LL) + (long long)t * pstride;
   float f[VEC];
 #pragma unroll
   for (int e = 0; e < VEC; ++e) f[e] = v.get(e);
-  csahca::norm_rope8(f, cv * VEC, CV, c, nr, p);
-  Vec8<T>::store(y + row * c + cv * VEC, f);
+  csahca::norm_rope8(f, g, cv * VEC, CV, c, nr, p);
+  Vec8<T>::store(y + b * y_bs + in_seq, f);
 }
 
 }  // namespace
 
 extern "C" int csahca_norm_rope(const void* x, void* y, const float* gamma, const int* pos, int B,
                                 int T, int H, int c, int pstride, int d_rope, float eps,
-                                float theta, int norm, int dtype, void* stream) {
+                                float theta, int norm, int dtype, long long x_bstride,
+                                long long y_bstride, void* stream) {
   using namespace csahca;
   if (B < 1 || T < 0 || H < 1 || (norm != 0 && norm != 1))
     return fail(CSAHCA_EINVAL, "csahca_norm_rope: need B >= 1, T >= 0, H >= 1 and norm 0 or 1");
@@ -56,7 +71,11 @@ extern "C" int csahca_norm_rope(const void* x, void* y, const float* gamma, cons
     return CSAHCA_OK;
   }
   if (!x || !y) return fail(CSAHCA_EINVAL, "csahca_norm_rope: x and y must be non-NULL");
-  if (!aligned16(x) || !aligned16(y)) return fail(CSAHCA_EINVAL, "csahca_norm_rope: x and y must be 16-byte aligned");
+  if (!aligned16(x) || !aligned16(y) || !aligned16(gamma))
+    return fail(CSAHCA_EINVAL, "csahca_norm_rope: x, y and gamma must be 16-byte aligned");
+  const long long seq = (long long)T * H * c;
+  if (x_bstride < seq || y_bstride < seq || x_bstride % 8 || y_bstride % 8)
+    return fail(CSAHCA_EINVAL, "csahca_norm_rope: batch strides must be >= T*H*c and multiples of 8");
   const long long rows = (long long)B * T * H;
   const long long threads = rows * (c / VEC);
   if (cdiv<long long>(threads, 256) > 0x7FFFFFFFLL) return fail(CSAHCA_ENOTSUP, "csahca_norm_rope: too many rows");
@@ -65,9 +84,9 @@ extern "C" int csahca_norm_rope(const void* x, void* y, const float* gamma, cons
   hipStream_t st = (hipStream_t)stream;
   if (dtype == CSAHCA_BF16)
     hipLaunchKernelGGL(norm_rope_rows<uint16_t>, grid, dim3(256), 0, st, (const uint16_t*)x, (uint16_t*)y, nr,
-                       pos, T, H, c, pstride, rows);
+                       pos, T, H, c, pstride, rows, x_bstride, y_bstride);
   else
     hipLaunchKernelGGL(norm_rope_rows<float>, grid, dim3(256), 0, st, (const float*)x, (float*)y, nr, pos, T,
-                       H, c, pstride, rows);
+                       H, c, pstride, rows, x_bstride, y_bstride);
   return launch_status("csahca_norm_rope");
 }

@@ -64,23 +64,58 @@ CSAHCA_DEV float row_sum(float v, int CV) {
   return v;
 }
 
-// Rotate the pair (a, b) = (x[2i], x[2i+1]) of the rotated block by pos * theta^(-2i/d).
-// The angle is formed in double: positions reach 2^20 and more, where a float angle would
-// be off by a sizeable fraction of a radian.
-CSAHCA_DEV void rope_rotate(float& a, float& b, long long pos, int i, int d, float theta) {
-  const double f = pow((double)theta, -2.0 * (double)i / (double)d);
-  double s, co;
-  sincos((double)pos * f, &s, &co);
-  const float cs = (float)co, sn = (float)s;
+// cos and sin of pos * f for a rotation frequency f given in double.  The angle is formed
+// and reduced modulo 2 pi in double (positions reach 2^20 and more, where a float angle
+// would be off by a sizeable fraction of a radian); the reduced angle, in [-pi, pi], goes
+// to the float sincos.
+CSAHCA_DEV void rope_cos_sin(long long pos, double f, float& cs, float& sn) {
+  const double a = (double)pos * f;
+  const double k = rint(a * 0.15915494309189535);        // 1 / (2 pi)
+  double r = fma(-k, 6.283185307179586, a);               // 2 pi, high part
+  r = fma(-k, 2.4492935982947064e-16, r);                 // 2 pi, low part
+  sincosf((float)r, &sn, &cs);
+}
+
+// Frequency of rotated pair i: theta^(-2i/d) = 2^(-2i log2(theta) / d), in double.
+CSAHCA_DEV double rope_freq(int i, int d, float theta) {
+  return exp2(-2.0 * (double)i * log2((double)theta) / (double)d);
+}
+
+// Rotate (a, b) = (x[2i], x[2i+1]) by the angle whose cos and sin are given.
+CSAHCA_DEV void rope_apply(float& a, float& b, float cs, float sn) {
   const float a2 = a * cs - b * sn;
   const float b2 = a * sn + b * cs;
   a = a2;
   b = b2;
 }
 
-// Channels ch0 .. ch0+7 of a row whose c channels are spread over CV consecutive lanes.
-CSAHCA_DEV void norm_rope8(float (&v)[VEC], int ch0, int CV, int c, const NormRope& nr,
-                           long long pos) {
+CSAHCA_DEV void rope_rotate(float& a, float& b, long long pos, int i, int d, float theta) {
+  float cs, sn;
+  rope_cos_sin(pos, rope_freq(i, d, theta), cs, sn);
+  rope_apply(a, b, cs, sn);
+}
+
+// Gains of channels ch0 .. ch0+7 (1 without a gain vector), loaded as two 16-byte vectors;
+// callers issue this early so that the load overlaps their own.
+CSAHCA_DEV void load_gain8(const NormRope& nr, int ch0, float (&g)[VEC]) {
+  if (nr.gamma) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(nr.gamma + ch0);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(nr.gamma + ch0 + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      g[e] = a[e];
+      g[4 + e] = b[e];
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) g[e] = 1.f;
+  }
+}
+
+// Channels ch0 .. ch0+7 of a row whose c channels are spread over CV consecutive lanes;
+// g holds their gains (load_gain8).
+CSAHCA_DEV void norm_rope8(float (&v)[VEC], const float (&g)[VEC], int ch0, int CV, int c,
+                           const NormRope& nr, long long pos) {
   if (nr.norm) {
     float ss = 0.f;
 #pragma unroll
@@ -88,12 +123,21 @@ CSAHCA_DEV void norm_rope8(float (&v)[VEC], int ch0, int CV, int c, const NormRo
     ss = row_sum(ss, CV);
     const float inv = 1.0f / sqrtf(ss / (float)c + nr.eps);
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) v[e] *= nr.gamma ? inv * nr.gamma[ch0 + e] : inv;
+    for (int e = 0; e < VEC; ++e) v[e] *= inv * g[e];
   }
   if (ch0 >= c - nr.d) {
+    // the lane's four pairs: f_{i0+q} = f_{i0} * step^q, step = theta^(-2/d)
     const int i0 = (ch0 - (c - nr.d)) / 2;
+    const double l2t = log2((double)nr.theta);
+    double f = exp2(-2.0 * (double)i0 * l2t / (double)nr.d);
+    const double step = exp2(-2.0 * l2t / (double)nr.d);
 #pragma unroll
-    for (int q = 0; q < VEC / 2; ++q) rope_rotate(v[2 * q], v[2 * q + 1], pos, i0 + q, nr.d, nr.theta);
+    for (int q = 0; q < VEC / 2; ++q) {
+      float cs, sn;
+      rope_cos_sin(pos, f, cs, sn);
+      rope_apply(v[2 * q], v[2 * q + 1], cs, sn);
+      f *= step;
+    }
   }
 }
 

@@ -116,6 +116,8 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ X,
   }
   const int blk = OV ? i + prev : i;  // block of X (stream a)
   const long long base = (long long)b * in_bs + (long long)blk * m * c + (long long)cv * VEC;
+  float g[VEC];  // NR: the channels' gains, loaded with the first tokens
+  if (NR) csahca::load_gain8(nr, cv * VEC, g);
   float mx[VEC], sum[VEC], acc[VEC];
 #pragma unroll
   for (int e = 0; e < VEC; ++e) {
@@ -131,7 +133,7 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ X,
 #pragma unroll
   for (int e = 0; e < VEC; ++e) res[e] = acc[e] / sum[e];
   // the CV lanes of one entry are consecutive and aligned, so the row sum stays in them
-  if (NR) csahca::norm_rope8(res, cv * VEC, CV, c, nr, (long long)m * (entry0 + i));
+  if (NR) csahca::norm_rope8(res, g, cv * VEC, CV, c, nr, (long long)m * (entry0 + i));
   Vec8<T>::store(out + (long long)b * out_bs + (long long)i * c + (long long)cv * VEC, res);
 }
 
@@ -227,10 +229,11 @@ __global__ __launch_bounds__(NR ? 512 : 256) void pool_block_kernel(const T* __r
     }
     const long long pos = (long long)m * (entry0 + i);
     for (int t = threadIdx.x; t < c; t += blockDim.x) {
-      float v = fin[t] * (nr.gamma ? inv * nr.gamma[t] : inv);
+      const int u = t ^ 1;  // the pair's other channel
+      const float gt = nr.gamma ? nr.gamma[t] : 1.f, gu = nr.gamma ? nr.gamma[u] : 1.f;
+      float v = fin[t] * (inv * gt);
       if (t >= c - nr.d) {
-        const int u = t ^ 1;  // the pair's other channel
-        const float w = fin[u] * (nr.gamma ? inv * nr.gamma[u] : inv);
+        const float w = fin[u] * (inv * gu);
         float a = (t & 1) ? w : v, bb = (t & 1) ? v : w;
         csahca::rope_rotate(a, bb, pos, (t - (c - nr.d)) >> 1, nr.d, nr.theta);
         v = (t & 1) ? bb : a;
@@ -362,9 +365,9 @@ int pool_entry(const char* name, const void* kv, const void* gate, const void* k
     set_error("%s: problem too large for one launch", name);
     return CSAHCA_ENOTSUP;
   }
-  if (nr && (!norm_rope_args_ok(c, nr->d, nr->eps, nr->theta) || entry0 < 0)) {
+  if (nr && (!norm_rope_args_ok(c, nr->d, nr->eps, nr->theta) || entry0 < 0 || !aligned16(nr->gamma))) {
     set_error("%s: the norm needs c / 8 a power of two <= 64, d_rope %% 8 == 0 and <= c, "
-              "eps >= 0, theta > 0 and entry0 >= 0", name);
+              "eps >= 0, theta > 0, entry0 >= 0 and gamma 16-byte aligned", name);
     return CSAHCA_EINVAL;
   }
   PoolArgs a{kv, gate, kv_b, gate_b, pos_bias, out, B, N, c, m, prev, in_bs, out_bs,

@@ -262,13 +262,14 @@ int hca_attend_sink(const void* q, const void* ckv, const void* win_kv, const in
  *   then every emitted entry is normalised and rotated; the first emitted entry is
  *   entry `entry0` of the cache (0 for a whole pass, the entry's index for an append).
  * csa_compress_overlap_norm_rope: csa_compress_overlap, then the same.
- *   gamma   [c] float32 device, or NULL for unit gain.
+ *   gamma   [c] float32 device (16-byte aligned), or NULL for unit gain.
  *   d_rope  rotated channels at the end of the row, d_rope % 8 == 0 and <= c (64 in the
  *           V4 settings, 0 for none).
  *   eps >= 0, theta > 0.  c / 8 must be a power of two no larger than 64 (c <= 512).
  *
- * csahca_norm_rope: rows x [B, T, H, c] of `dtype` (contiguous) -> y (same shape; y == x
- *   is allowed).  Row (b, t, h) has position pos[b] + t * pstride: queries pass q_pos and
+ * csahca_norm_rope: rows x [B, T, H, c] of `dtype` -> y (same shape; y == x is allowed).
+ *   Sequence b starts at x + b * x_bstride (y + b * y_bstride) elements; inside a
+ *   sequence the rows are contiguous.  Strides >= T*H*c and multiples of 8.  Row (b, t, h) has position pos[b] + t * pstride: queries pass q_pos and
  *   pstride 1 (H = n_h), a window source its win_pos and 1 (H = 1), compressed entries
  *   built elsewhere NULL and m.  pos: [B] int32 device, or NULL for 0.  norm = 0 applies
  *   RoPE only.  Limits as above; T == 0 does nothing.
@@ -285,7 +286,7 @@ int csa_compress_overlap_norm_rope(const void* kv_a, const void* gate_a, const v
                                    long long out_bstride, void* stream);
 int csahca_norm_rope(const void* x, void* y, const float* gamma, const int* pos, int B, int T,
                      int H, int c, int pstride, int d_rope, float eps, float theta, int norm,
-                     int dtype, void* stream);
+                     int dtype, long long x_bstride, long long y_bstride, void* stream);
 
 /*
  * csahca_kv_ring_rows / csahca_kv_append / csahca_kv_fork -- the cache lifecycle of one

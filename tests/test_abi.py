@@ -180,7 +180,8 @@ def test_kv_cache_validation():
 def test_norm_rope_validation():
     L = lib.load()
     nr = L.csahca_norm_rope
-    ok = [FAKE, FAKE, None, None, 2, 3, 4, 512, 1, 64, 1e-6, 10000.0, 1, 1, None]
+    ok = [FAKE, FAKE, None, None, 2, 3, 4, 512, 1, 64, 1e-6, 10000.0, 1, 1, 3 * 4 * 512, 3 * 4 * 512,
+          None]
 
     def with_(i, v, base=ok):
         a = list(base)
@@ -195,7 +196,10 @@ def test_norm_rope_validation():
     assert nr(*with_(12, 2)) == EINVAL       # norm flag
     assert nr(*with_(13, 2)) == ENOTSUP      # fp8 rows
     assert nr(*with_(1, FAKE + 8)) == EINVAL  # alignment
+    assert nr(*with_(2, FAKE + 4)) == EINVAL  # gain alignment
     assert nr(*with_(0, None)) == EINVAL
+    assert nr(*with_(14, 3 * 4 * 512 - 8)) == EINVAL  # stride below T*H*c
+    assert nr(*with_(15, 3 * 4 * 512 + 4)) == EINVAL  # stride not a multiple of 8
     assert nr(*with_(5, 0)) == 0             # no rows
     cp = L.csahca_compress_norm_rope
     cok = [FAKE, FAKE, None, None, FAKE, 1, 8, 512, 4, 0, 64, 1e-6, 10000.0, 1, 8 * 512, 2 * 512,
@@ -203,6 +207,7 @@ def test_norm_rope_validation():
     assert cp(*with_(7, 96, cok)) == EINVAL
     assert cp(*with_(10, 12, cok)) == EINVAL
     assert cp(*with_(9, -1, cok)) == EINVAL  # entry0
+    assert cp(*with_(3, FAKE + 4, cok)) == EINVAL  # gain alignment
     assert "csahca_compress_norm_rope" in lib.last_error()
     assert cp(*with_(13, 2, cok)) == ENOTSUP
     ov = L.csa_compress_overlap_norm_rope

@@ -207,9 +207,11 @@ def test_chain_attention_over_normalised_rotated_rows():
     lib.csahca_compress_norm_rope(dX, dZ, None, H.to_dev(gk), C, B, n, c, m, 0, d, EPS, THETA, BF16,
                                   n * c, N * c)
     wp = n - W
-    win = dX[:, wp:].contiguous()
+    win = H.empty((B, W, c), BF16)
     win_pos = torch.full((B,), wp, dtype=torch.int32, device=H.DEV)
-    lib.csahca_norm_rope(win, win, H.to_dev(gk), win_pos, B, W, 1, c, 1, d, EPS, THETA, 1, BF16)
+    # the window read straight out of the [B, n, c] raw array (batch stride n * c)
+    lib.csahca_norm_rope(dX[:, wp:], win, H.to_dev(gk), win_pos, B, W, 1, c, 1, d, EPS, THETA, 1, BF16,
+                         x_bstride=n * c, y_bstride=W * c)
     q_pos = torch.full((B,), n - 1, dtype=torch.int32, device=H.DEV)
     dQ = H.to_dev(Q)
     lib.csahca_norm_rope(dQ, dQ, H.to_dev(gq), q_pos, B, 1, n_h, c, 1, d, EPS, THETA, 1, BF16)

@@ -20,6 +20,7 @@ from .csahca import (  # noqa: F401
     decode_mxfp4,
     entry_counts,
     entry_positions,
+    grouped_out_proj,
     hca_rows,
     index_scores,
     norm_rope,

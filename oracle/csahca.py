@@ -357,6 +357,34 @@ def hca_rows(Ch, m_hca, win_src, win_pos, p, W):
 
 
 # ----------------------------------------------------------------------------------------
+# grouped output projection ([P2] V.3)
+# ----------------------------------------------------------------------------------------
+def grouped_out_proj(O, Wg):
+    """Grouped output projection of the concatenated head outputs.
+
+    [P2] V.3: the c * n_h concatenated head outputs are split into g groups of heads, each
+    group is projected by its own smaller matrix to d_g dimensions, and the g results are
+    concatenated (d = g * d_g).  Readings: group gi holds the contiguous heads
+    gi*n_h/g .. (gi+1)*n_h/g - 1, in head order; the outputs are concatenated in group
+    order; there is no bias.  Weights are laid out as a linear layer's, out x in:
+    Wg[gi] has shape [d_g, K_g] with K_g = n_h * c / g.
+
+    O: [T, n_h, c] (or [T, n_h * c]); Wg: [g, d_g, K_g].  Returns [T, g * d_g] fp64.
+    """
+    O = np.asarray(O, dtype=np.float64)
+    Wg = np.asarray(Wg, dtype=np.float64)
+    T = O.shape[0]
+    X = O.reshape(T, -1)                        # concatenated heads, head-major
+    g, d_g, K_g = Wg.shape
+    assert X.shape[1] == g * K_g
+    out = np.empty((T, g * d_g))
+    for gi in range(g):
+        Xg = X[:, gi * K_g:(gi + 1) * K_g]      # this group's heads
+        out[:, gi * d_g:(gi + 1) * d_g] = Xg @ Wg[gi].T
+    return out
+
+
+# ----------------------------------------------------------------------------------------
 # entry counts
 # ----------------------------------------------------------------------------------------
 def entry_counts(n, m, m_hca, k, W):

@@ -22,7 +22,8 @@ def _impl(**over):
                                attend=O.attend, visible=O.visible, csa_rows=O.csa_rows,
                                hca_rows=O.hca_rows, entry_counts=O.entry_counts,
                                window_positions=O.window_positions, rmsnorm=O.rmsnorm,
-                               rope_tail=O.rope_tail, norm_rope=O.norm_rope)
+                               rope_tail=O.rope_tail, norm_rope=O.norm_rope,
+                               grouped_out_proj=O.grouped_out_proj)
     for k, v in over.items():
         setattr(ns, k, v)
     return ns
@@ -395,11 +396,45 @@ def check_rope(o):
                                o.rmsnorm(o.rope_tail(x, np.arange(5), d), None, 1e-6), atol=1e-14)
 
 
+def check_grouped_out_proj(o):
+    """Grouped output projection: a dense projection whose weight is block diagonal over
+    the head groups; one group is a plain linear layer; one-hot inputs pick weights."""
+    rng = np.random.default_rng(23)
+    T, n_h, c, g, d_g = 3, 6, 4, 3, 5
+    K_g = n_h * c // g
+    O = rng.normal(size=(T, n_h, c))
+    Wg = rng.normal(size=(g, d_g, K_g))
+    Y = o.grouped_out_proj(O, Wg)
+    assert Y.shape == (T, g * d_g)
+    # the same map as one dense [g*d_g, n_h*c] weight with zero blocks off the diagonal,
+    # evaluated element by element
+    Wd = np.zeros((g * d_g, n_h * c))
+    for gi in range(g):
+        Wd[gi * d_g:(gi + 1) * d_g, gi * K_g:(gi + 1) * K_g] = Wg[gi]
+    X = O.reshape(T, -1)
+    dense = np.array([[sum(Wd[j, k] * X[t, k] for k in range(n_h * c)) for j in range(g * d_g)]
+                      for t in range(T)])
+    np.testing.assert_allclose(Y, dense, atol=1e-12)
+    # head h of a one-hot input lands in group h // (n_h / g) only, and picks the weight
+    # column of its position inside the group
+    for h, ch in ((0, 0), (2, 3), (5, 1)):
+        e = np.zeros((1, n_h, c))
+        e[0, h, ch] = 1.0
+        y = o.grouped_out_proj(e, Wg)[0]
+        gi, k = h // (n_h // g), (h % (n_h // g)) * c + ch
+        want = np.zeros(g * d_g)
+        want[gi * d_g:(gi + 1) * d_g] = Wg[gi][:, k]
+        np.testing.assert_array_equal(y, want)
+    # g = 1 is the plain linear layer of the concatenated heads
+    W1 = rng.normal(size=(1, 2, n_h * c))
+    np.testing.assert_allclose(o.grouped_out_proj(O, W1), X @ W1[0].T, atol=1e-12)
+
+
 ALL_CHECKS = [check_budget_counts, check_worked_example, check_pool_counts, check_budget_toy,
               check_pooling_recall, check_pool_closed_forms, check_pool_overlap_closed_forms,
               check_indexer_closed_forms,
               check_topk_brute, check_attend_textbook, check_attend_sink,
-              check_rows_and_visibility, check_rmsnorm, check_rope]
+              check_rows_and_visibility, check_rmsnorm, check_rope, check_grouped_out_proj]
 
 
 @pytest.mark.parametrize("check", ALL_CHECKS, ids=lambda f: f.__name__)
@@ -658,7 +693,33 @@ def _rope_variant(half_split=False, sign=1.0, fexp=2.0, head=False):
     return f
 
 
+def _gop_interleaved_groups(O, Wg):
+    O = np.asarray(O, dtype=np.float64)
+    T, n_h = O.shape[0], O.shape[1]
+    g = Wg.shape[0]
+    order = np.concatenate([np.arange(gi, n_h, g) for gi in range(g)])  # heads gi, gi+g, ...
+    return _gop_plain(O[:, order], Wg)
+
+
+def _gop_transposed_weight(O, Wg):
+    O = np.asarray(O, dtype=np.float64)
+    T = O.shape[0]
+    X = O.reshape(T, -1)
+    g, d_g, K_g = Wg.shape
+    Wt = np.asarray(Wg).reshape(g, K_g, d_g)   # reads the weight as in x out
+    return np.concatenate([X[:, gi * K_g:(gi + 1) * K_g] @ Wt[gi] for gi in range(g)], axis=1)
+
+
+def _gop_plain(O, Wg):
+    T = O.shape[0]
+    X = O.reshape(T, -1)
+    g, d_g, K_g = Wg.shape
+    return np.concatenate([X[:, gi * K_g:(gi + 1) * K_g] @ Wg[gi].T for gi in range(g)], axis=1)
+
+
 MUTANTS = {
+    "gop_interleaved_head_groups": dict(grouped_out_proj=_gop_interleaved_groups),
+    "gop_weight_read_in_by_out": dict(grouped_out_proj=_gop_transposed_weight),
     "rmsnorm_centred": dict(rmsnorm=_rmsnorm_centred),
     "rmsnorm_eps_outside_sqrt": dict(rmsnorm=_rmsnorm_eps_outside),
     "rope_half_split_pairs": dict(rope_tail=_rope_variant(half_split=True)),

@@ -56,6 +56,9 @@ def parse():
     ap.add_argument("--norm-rope", action="store_true",
                     help="run the step with RMSNorm + partial RoPE (64 dims): fused into the "
                          "pooling of new blocks, and on the queries and window rows")
+    ap.add_argument("--gop", action="store_true",
+                    help="time the grouped output projection at the config's shape (its "
+                         "tokens, n_h * c inputs in groups of 8 heads, 512 outputs per group)")
     ap.add_argument("--kv-append", action="store_true",
                     help="time the cache lifecycle at the config's shape (csahca_kv_append of a "
                          "chunk and of one decode token, CSA and HCA caches) instead of the step")
@@ -660,6 +663,86 @@ def kv_append(cfg, reps, cpu_seconds, no_cpu):
     print(json.dumps(line), flush=True)
 
 
+def gop_bench(cfg, reps, cpu_seconds, no_cpu):
+    """grouped_out_proj on the config's attention output: T = B * Tq tokens of n_h * c,
+    g = n_h / 8 groups (K_g = 8c), d_g = 512.  Decode shapes are bound by streaming the
+    weights (HBM roofline); the prefill chunk by MFMA (bf16 roofline)."""
+    import numpy as np
+    import torch
+
+    import compressed_attention_compress_amd as lib
+
+    T = cfg.B * cfg.Tq
+    g, d_g = cfg.n_h // 8, 512
+    K_g = cfg.n_h * cfg.c // g
+    gen = torch.Generator(device="cuda").manual_seed(2024)
+    o = torch.randn((T, g * K_g), generator=gen, device="cuda").to(torch.bfloat16)
+    reps_w = 1 if T > 64 else 8  # decode: rotate weight copies so every call streams HBM
+    ws = [(torch.randn((g, d_g, K_g), generator=gen, device="cuda") / math.sqrt(K_g)).to(torch.bfloat16)
+          for _ in range(reps_w)]
+    y = torch.empty((T, g * d_g), dtype=torch.bfloat16, device="cuda")
+    st = torch.cuda.Stream()
+
+    def call(i, stream):
+        lib.grouped_out_proj(o, ws[i % reps_w], y, T, g, K_g, d_g, g * K_g, g * d_g, 1, stream=stream)
+
+    call(0, st)
+    torch.cuda.synchronize()
+    n_in = 40 if T <= 64 else 4
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr, stream=st):
+        for i in range(n_in):
+            call(i, st)
+    gr.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(st):
+        e0.record(st)
+        for _ in range(reps):
+            gr.replay()
+        e1.record(st)
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) / 1e3 / (reps * n_in)
+    flops = 2.0 * T * g * K_g * d_g
+    nbytes = 2 * (g * d_g * K_g + T * g * K_g + T * g * d_g)
+    if T > 64:
+        bound, ach, peak, unit = "mfma", flops / sec / 1e12, 2500.0, "TFLOP/s"
+        kname = "gop_gemm"
+    else:
+        bound, ach, peak, unit = "hbm", nbytes / sec / 1e9, HBM_PEAK_GBS, "GB/s"
+        kname = "gop_skinny"
+    cpu = None
+    if not no_cpu:
+        import oracle
+        rng = np.random.default_rng(8)
+        tk = 4
+        Oc = rng.standard_normal((tk, g * K_g))
+        Wc = rng.standard_normal((g, d_g, K_g))
+        t0 = time.perf_counter()
+        done = 0
+        while time.perf_counter() - t0 < cpu_seconds:
+            oracle.grouped_out_proj(Oc, Wc)
+            done += tk
+        el = time.perf_counter() - t0
+        cpu = {"value": round(done / el, 2), "unit": "tokens/s", "cores": torch.get_num_threads(),
+               "kind": "oracle", "sample": f"{done} tokens in calls of {tk}, {el:.1f} s, NumPy fp64"}
+    line = {
+        "metric": "grouped output projection throughput (tokens/s)",
+        "value": round(T / sec, 1), "unit": "tokens/s", "n_gpus": 1, "steps": reps * n_in,
+        "warmup": 1, "us_per_call": round(sec * 1e6, 2), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"gop_{cfg.name}", "tokens": T, "groups": g, "K_g": K_g,
+                   "d_g": d_g, "timing": "HIP events around graph replays"},
+        "roofline": {"kernel": kname, "bound": bound, "achieved": round(ach, 1), "peak": peak,
+                     "unit": unit, "frac": round(ach / peak, 4), "traffic": None,
+                     "avg_launch_us": round(sec * 1e6, 2),
+                     "flops_per_launch" if bound == "mfma" else "bytes_per_launch":
+                         flops if bound == "mfma" else nbytes},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.traffic_from:
@@ -682,6 +765,9 @@ def main():
             print("--fp4-keys needs a config with an FP8 indexer", file=sys.stderr)
             sys.exit(2)
         cfg = cfg.scaled(idx_dtype=3)
+    if args.gop:
+        gop_bench(cfg, args.steps or 10, min(args.cpu_seconds, 10.0), args.no_cpu_baseline)
+        return
     if args.kv_append:
         kv_append(cfg, args.steps or 20, min(args.cpu_seconds, 10.0), args.no_cpu_baseline)
         return

@@ -30,6 +30,7 @@ _SIGNATURES = {
                                             _I, _F, _F, _I, _LL, _LL, _P]),
     "csahca_norm_rope": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _F, _I, _I, _LL, _LL,
                               _P]),
+    "grouped_out_proj": (_I, [_P, _P, _P, _I, _I, _I, _I, _LL, _LL, _I, _P]),
     "csahca_kv_ring_rows": (_I, [_I, _I]),
     "csahca_kv_append": (_I, [_P, _P, _P, _P, _P, _P, _I, _LL, _I, _I, _I, _I, _I, _LL, _LL, _LL,
                               _P]),
@@ -154,6 +155,11 @@ def csahca_norm_rope(x, y, gamma, pos, B, T, H, c, pstride, d_rope, eps, theta, 
         _ptr(x), _ptr(y), _ptr(gamma), _ptr(pos), B, T, H, c, pstride, d_rope, eps, theta, norm,
         dtype, seq if x_bstride is None else x_bstride, seq if y_bstride is None else y_bstride,
         _stream(stream)))
+
+
+def grouped_out_proj(o, w, y, T, g, K_g, d_g, ldo, ldy, dtype, stream=None):
+    return _check("grouped_out_proj", load().grouped_out_proj(
+        _ptr(o), _ptr(w), _ptr(y), T, g, K_g, d_g, ldo, ldy, dtype, _stream(stream)))
 
 
 def csahca_kv_ring_rows(W, m):

@@ -339,6 +339,28 @@ int csahca_kv_fork(void* dst_kv_ring, void* dst_gate_ring, void* dst_entries,
                    int B, long long n_entries, int c, int m, int W, int dtype,
                    long long ring_bstride, long long ent_bstride, void* stream);
 
+/*
+ * grouped_out_proj -- the grouped output projection shared by both branches.
+ * Source: "DeepSeek-V4 Hybrid Attention: CSA, HCA, mHC, MoE", section V.3 (the c * n_h
+ * concatenated head outputs are split into g groups of heads, each group projected by its
+ * own smaller matrix to d_g dimensions, the g results concatenated) and section IV.
+ *
+ *   y[t, gi*d_g + j] = sum_{k < K_g} o[t, gi*K_g + k] * w[gi, j, k]     (gi < g, j < d_g)
+ *
+ *   o   [T, g*K_g] bf16, row stride ldo >= g*K_g elements: each token's concatenated head
+ *       outputs in head order (an attention output [B, Tq, n_h, c] is T = B*Tq rows with
+ *       K_g = n_h*c/g, so group gi holds heads gi*n_h/g .. (gi+1)*n_h/g - 1).
+ *   w   [g, d_g, K_g] bf16: each group's matrix laid out as a linear layer's weight (out x
+ *       in).
+ *   y   [T, g*d_g] bf16, row stride ldy >= g*d_g; fp32 accumulation, rounded once.
+ * Readings: contiguous head groups, outputs concatenated in group order, no bias.
+ * Limits: dtype CSAHCA_BF16; K_g % 128 == 0; d_g % 16 == 0; strides multiples of 8;
+ * T == 0 does nothing.  Up to 64 tokens (or d_g % 128 != 0) a kernel streams w once per 64
+ * tokens; more tokens take 256 x 128 MFMA tiles.
+ */
+int grouped_out_proj(const void* o, const void* w, void* y, int T, int g, int K_g, int d_g,
+                     long long ldo, long long ldy, int dtype, void* stream);
+
 /* Message for the last non-OK status returned on the calling thread ("" if none). */
 const char* csahca_last_error(void);
 

@@ -216,3 +216,23 @@ def test_norm_rope_validation():
     assert ov(*with_(12, -3, ook)) == EINVAL
     assert ov(*with_(11, 2, ook)) == EINVAL  # prev
     assert ov(*with_(2, None, ook)) == EINVAL
+
+
+def test_grouped_out_proj_validation():
+    L = lib.load()
+    gp = L.grouped_out_proj
+    ok = [FAKE, FAKE, FAKE, 4, 16, 4096, 512, 16 * 4096, 16 * 512, 1, None]
+
+    def with_(i, v):
+        a = list(ok)
+        a[i] = v
+        return a
+    assert gp(*with_(9, 0)) == ENOTSUP            # fp32
+    assert gp(*with_(5, 4096 + 64)) == ENOTSUP    # K_g % 128
+    assert gp(*with_(6, 520)) == ENOTSUP          # d_g % 16
+    assert gp(*with_(7, 16 * 4096 - 8)) == EINVAL  # ldo
+    assert gp(*with_(8, 16 * 512 + 4)) == EINVAL  # ldy % 8
+    assert gp(*with_(0, None)) == EINVAL
+    assert gp(*with_(2, FAKE + 2)) == EINVAL      # alignment
+    assert gp(*with_(3, -1)) == EINVAL
+    assert gp(*with_(3, 0)) == 0                  # no tokens

@@ -9,13 +9,15 @@
 //   * gop_skinny (few tokens: decode): bound by streaming W once.  A workgroup owns 16
 //     output columns of one group for every token; its four waves split K and meet in
 //     LDS.  Each lane streams 16 B of one weight row per step, eight steps in flight.
-//   * gop_gemm (many tokens: prefill): bound by MFMA.  A workgroup computes a 256 x 128
-//     tile (tokens x columns) as 2 x 2 waves of 128 x 64, over K in stages of 64 that
-//     global_load_lds moves straight into LDS, three stages in flight.  LDS rows are 128 B
+//   * gop_gemm (many tokens: prefill): bound by MFMA.  A workgroup computes a 256 x 256
+//     tile (tokens x columns) as 2 x 4 waves of 128 x 64 (two waves per SIMD, so one's LDS
+//     reads overlap the other's MFMAs), over K in stages of 64 that global_load_lds moves
+//     straight into LDS, double-buffered.  A stage reads each row's slice as one 128-byte
+//     line (stages of 32 with twice the requests measured 20% slower).  LDS rows are 128 B
 //     with their 16-byte chunks XOR-swizzled by (row / 2) mod 8, so that the 16 rows a
-//     fragment read touches fall in 16 distinct bank groups.  Tiles are handed out so that
-//     each XCD gets a contiguous run; the four column tiles of a token tile run together
-//     there and share its rows in that XCD's L2.
+//     fragment read touches fall in 16 distinct bank groups.  Tiles are handed out so that each XCD
+//     gets a contiguous run; the column tiles of a token tile run together there and share
+//     its rows in that XCD's L2.
 #include "common.hpp"
 
 namespace {
@@ -101,25 +103,21 @@ __global__ __launch_bounds__(256) void gop_skinny(const uint16_t* __restrict__ X
 }
 
 // ---------------------------------------------------------------------------------------
-// gemm: 256 x 128 tiles, K stages of 64 through a ring of 3 in LDS
+// gemm: 256 x 256 tiles, 8 waves of 128 x 64, K stages of 64 double-buffered in LDS
 // ---------------------------------------------------------------------------------------
-constexpr int GM = 256, GN = 128, GK = 64, GNS = 3;
+constexpr int GM = 256, GN = 256, GK = 64, GNS = 2, GWAVES = 8;
 constexpr int ROWB = GK * 2;                               // 128 B per staged row
-constexpr int A_BYTES = GM * ROWB, B_BYTES = GN * ROWB;   // 32 KiB + 16 KiB
+constexpr int A_BYTES = GM * ROWB, B_BYTES = GN * ROWB;   // 32 KiB + 32 KiB
 constexpr int STAGE = A_BYTES + B_BYTES;
-constexpr int GEMM_LDS = GNS * STAGE;                      // 144 KiB
-constexpr int A_DMA = A_BYTES / 1024 / 4, B_DMA = B_BYTES / 1024 / 4;  // per wave per stage: 8, 4
-constexpr int DMA_PER_STAGE = A_DMA + B_DMA;                             // 12
+constexpr int GEMM_LDS = GNS * STAGE;                      // 128 KiB
+constexpr int LPR = ROWB / 16, RPI = 64 / LPR;            // lanes per row, rows per DMA
+constexpr int A_DMA = A_BYTES / 1024 / GWAVES, B_DMA = B_BYTES / 1024 / GWAVES;  // 4, 4
 
-template <int N>
-CSAHCA_DEV void wait_vm() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-// chunk position of 16-byte chunk kc in staged row r
+// position of 16-byte chunk kc (0..7) in staged row r: the 16 rows a fragment read
+// touches (2 per 256 bytes) land on 16 distinct 16-byte bank groups
 CSAHCA_DEV int swz(int r, int kc) { return kc ^ ((r >> 1) & 7); }
 
-__global__ __launch_bounds__(256, 1) void gop_gemm(const uint16_t* __restrict__ X,
+__global__ __launch_bounds__(512, 1) void gop_gemm(const uint16_t* __restrict__ X,
                                                    const uint16_t* __restrict__ Wt,
                                                    uint16_t* __restrict__ Y, int T, int K_g,
                                                    int d_g, long long ldx, long long ldy,
@@ -136,20 +134,21 @@ __global__ __launch_bounds__(256, 1) void gop_gemm(const uint16_t* __restrict__ 
   const int gi = tile / (ntiles * mtiles);
   const int m0 = mt * GM, n0 = nt * GN;
 
-  // DMA sources: instruction q of this wave moves rows 8q' .. 8q'+7 (q' = its global
-  // index), lane L row 8q' + L/8, LDS chunk L%8 holding data chunk swz(row, L%8)
+  // DMA: instruction q (of a stage's 32 A and 32 B ones) moves rows RPI*q .. RPI*q+7; lane
+  // L row RPI*q + L/LPR, LDS position L%LPR holding data chunk swz(row, L%LPR).  Each row
+  // slice is one 128-byte line.
   const uint16_t* asrc[A_DMA];
   const uint16_t* bsrc[B_DMA];
 #pragma unroll
   for (int i = 0; i < A_DMA; ++i) {
-    const int r = 8 * (wave * A_DMA + i) + (lane >> 3);
+    const int r = RPI * (wave * A_DMA + i) + lane / LPR;
     const int t = min(m0 + r, T - 1);  // rows past the end repeat the last (results dropped)
-    asrc[i] = X + (size_t)t * ldx + (size_t)gi * K_g + swz(r, lane & 7) * 8;
+    asrc[i] = X + (size_t)t * ldx + (size_t)gi * K_g + swz(r, lane % LPR) * 8;
   }
 #pragma unroll
   for (int i = 0; i < B_DMA; ++i) {
-    const int r = 8 * (wave * B_DMA + i) + (lane >> 3);
-    bsrc[i] = Wt + ((size_t)gi * d_g + n0 + r) * K_g + swz(r, lane & 7) * 8;
+    const int r = RPI * (wave * B_DMA + i) + lane / LPR;
+    bsrc[i] = Wt + ((size_t)gi * d_g + n0 + r) * K_g + swz(r, lane % LPR) * 8;
   }
   auto issue = [&](int s) {
     uint8_t* st = smem + (s % GNS) * STAGE;
@@ -163,7 +162,7 @@ __global__ __launch_bounds__(256, 1) void gop_gemm(const uint16_t* __restrict__ 
                                        0, 0);
   };
 
-  const int wm = wave >> 1, wn = wave & 1;  // 2 x 2 waves of 128 x 64
+  const int wm = wave >> 2, wn = wave & 3;  // 2 x 4 waves of 128 x 64
   f32x4 acc[8][4];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
@@ -172,15 +171,11 @@ __global__ __launch_bounds__(256, 1) void gop_gemm(const uint16_t* __restrict__ 
 
   const int nst = K_g / GK;
   issue(0);
-  if (nst > 1) issue(1);
   for (int s = 0; s < nst; ++s) {
-    // stage s landed (stage s + 1 may still be in flight), for every wave
-    if (s + 1 < nst)
-      wait_vm<DMA_PER_STAGE>();
-    else
-      wait_vm<0>();
+    // stage s landed for every wave; then stage s + 1 streams in while s is computed
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (s + 2 < nst) issue(s + 2);  // into the buffer every wave finished in iteration s - 1
+    if (s + 1 < nst) issue(s + 1);  // into the buffer every wave left at s - 1
     const uint8_t* st = smem + (s % GNS) * STAGE;
 #pragma unroll
     for (int ks = 0; ks < GK / 32; ++ks) {
@@ -242,7 +237,7 @@ extern "C" int grouped_out_proj(const void* o, const void* w, void* y, int T, in
   hipStream_t st = (hipStream_t)stream;
   const uint16_t *X = (const uint16_t*)o, *Wt = (const uint16_t*)w;
   uint16_t* Y = (uint16_t*)y;
-  if (T > 64 && d_g % GN == 0) {
+  if (T > 64 && d_g % GN == 0 && K_g % GK == 0) {
     const long long mtiles = cdiv<long long>(T, GM), ntiles = d_g / GN, tiles = mtiles * ntiles * g;
     if (tiles > 0x7FFFFFFFLL) return fail(CSAHCA_ENOTSUP, "grouped_out_proj: problem too large");
     if (!gemm_attr_set) {
@@ -251,7 +246,7 @@ extern "C" int grouped_out_proj(const void* o, const void* w, void* y, int T, in
         return fail(CSAHCA_ELAUNCH, "grouped_out_proj: cannot set the LDS size");
       gemm_attr_set = true;
     }
-    hipLaunchKernelGGL(gop_gemm, dim3((unsigned)tiles), dim3(256), GEMM_LDS, st, X, Wt, Y, T, K_g, d_g, ldo, ldy,
+    hipLaunchKernelGGL(gop_gemm, dim3((unsigned)tiles), dim3(64 * GWAVES), GEMM_LDS, st, X, Wt, Y, T, K_g, d_g, ldo, ldy,
                        (int)mtiles, (int)ntiles, (int)tiles);
     return launch_status(name);
   }

@@ -59,9 +59,10 @@ def run(o, w, T, g, K_g, d_g, pad_y=0):
     (17, 2, 128, 48, 8),       # ragged tokens, columns not a multiple of 128, padded rows
     (64, 1, 1024, 16, 0),      # four full 16-token tiles
     (150, 3, 256, 48, 0),      # many tokens with d_g % 128 != 0: 64-token groups
-    (65, 2, 512, 128, 0),      # the tile kernel with one token in the second row block
+    (65, 2, 512, 256, 0),      # the tile kernel, 65 tokens in one 256-token tile
     (300, 2, 256, 256, 16),    # ragged last tile, padded rows
-    (1000, 4, 384, 128, 0),    # several tiles; K_g not a multiple of 256
+    (1000, 2, 384, 512, 0),    # several tiles; K_g not a multiple of 256
+    (520, 1, 128, 128, 0),     # d_g % 256 != 0: the few-token kernel per 64 tokens
 ])
 def test_gop_parity(T, g, K_g, d_g, pad):
     print(f"[gop T={T} g={g} K_g={K_g} d_g={d_g} pad={pad}]", flush=True)
@@ -87,7 +88,7 @@ def test_gop_tokens_independent():
     """A token's output does not depend on which other tokens share the call (bitwise),
     across the few-token and the tile kernel."""
     rng = np.random.default_rng(9)
-    g, K_g, d_g = 4, 512, 128
+    g, K_g, d_g = 4, 512, 256
     o, w = make(rng, 300, g, K_g, d_g)
     big = run(o, w, 300, g, K_g, d_g)
     small = run(o[:5], w, 5, g, K_g, d_g)

@@ -53,6 +53,8 @@ def parse():
     ap.add_argument("--sink", action="store_true",
                     help="run both attention calls with a per-head attention sink "
                          "(csa_attend_sink / hca_attend_sink)")
+    ap.add_argument("--serial", action="store_true",
+                    help="run the CSA and HCA layers one after the other on one stream")
     ap.add_argument("--norm-rope", action="store_true",
                     help="run the step with RMSNorm + partial RoPE (64 dims): fused into the "
                          "pooling of new blocks, and on the queries and window rows")
@@ -73,7 +75,7 @@ class Workload:
 
     NR_D, NR_EPS, NR_THETA = 64, 1e-6, 10000.0
 
-    def __init__(self, cfg, replicas, sink=False, norm_rope=False):
+    def __init__(self, cfg, replicas, sink=False, norm_rope=False, serial=False):
         import torch
 
         import compressed_attention_compress_amd as lib
@@ -82,6 +84,7 @@ class Workload:
         self.lib = lib
         self.cfg = cfg
         self.R = replicas
+        self.s_hca = None if serial else torch.cuda.Stream()  # default priority
         dev = "cuda"
         prob = make_problem_device(cfg, dev)
         self.prob = prob
@@ -154,11 +157,11 @@ class Workload:
         torch.cuda.synchronize()
 
     # -- the step -------------------------------------------------------------------------
-    def pool_new_blocks(self, r):
+    def pool_new_blocks(self, r, layers=None):
         """Pool the blocks completed by the step's tokens into replica r's caches."""
         cfg, lib, prob = self.cfg, self.lib, self.prob
         B, c, n = cfg.B, cfg.c, self.n
-        for l in self.layers:
+        for l in (self.layers if layers is None else layers):
             m = cfg.m if l == "csa" else cfg.m_hca
             first_blk = self.n_old // m          # first block not yet in the cache
             n_new = n // m - first_blk
@@ -175,13 +178,17 @@ class Workload:
                 lib.csa_compress(X[:, tok0:], Z[:, tok0:], None, C[:, first_blk:], B, n_new * m, c,
                                  m, cfg.dtype, n * c, (n // m) * c)
 
+    def select(self, r):
+        cfg = self.cfg
+        self.lib.lightning_index_select(self.scores, self.q_pos, cfg.m, cfg.B, self.Tq, self.N_c,
+                                        cfg.k, self.idx, None, self.iws, self.iws_b)
+
     def index(self, r, split=True):
         cfg, lib, rp = self.cfg, self.lib, self.rep[r]
         B = cfg.B
         if split:
             self.index_score(r)
-            lib.lightning_index_select(self.scores, self.q_pos, cfg.m, B, self.Tq, self.N_c, cfg.k,
-                                       self.idx, None, self.iws, self.iws_b)
+            self.select(r)
         else:
             lib.lightning_index_topk(rp["qI"], rp["w"], rp["KI"], cfg.idx_dtype, self.q_pos, cfg.m,
                                      B, self.Tq, cfg.n_ih, cfg.c_I, self.N_c, cfg.k, self.idx, None,
@@ -207,11 +214,12 @@ class Workload:
                              self.NR_THETA, 1, cfg.dtype, x_bstride=n * c, y_bstride=self.nr_L * c)
         return self.nr_q[l], self.nr_win[l], self.nr_win_pos, self.nr_L
 
-    def attend(self, r):
+    def attend(self, r, layers=None):
         cfg, lib, rp, prob = self.cfg, self.lib, self.rep[r], self.prob
         B, c, n = cfg.B, cfg.c, self.n
         sk = self.sink
-        if "csa" in self.layers:
+        layers = self.layers if layers is None else layers
+        if "csa" in layers:
             q, win, wpos, L = self.norm_rope_rows(r, "csa")
             args = (q, rp["C_csa"], self.idx, win, wpos, self.q_pos, B,
                     self.Tq, cfg.n_h, c, self.N_c, cfg.k, L, cfg.W, self.scale)
@@ -220,7 +228,7 @@ class Workload:
                 lib.csa_attend(*args, *tail)
             else:
                 lib.csa_attend_sink(*args, sk, *tail)
-        if "hca" in self.layers:
+        if "hca" in layers:
             q, win, wpos, L = self.norm_rope_rows(r, "hca")
             args = (q, rp["C_hca"], win, wpos, self.q_pos, cfg.m_hca, B,
                     self.Tq, cfg.n_h, c, self.N_h, L, cfg.W, self.scale)
@@ -231,7 +239,25 @@ class Workload:
                 lib.hca_attend_sink(*args, sk, *tail)
 
     def step(self, r):
+        """One pass of the path.  With both layers present the HCA attention runs on a
+        second stream while the CSA top-k pass and attention run on the first: the HCA
+        layer needs nothing from the indexer, and the top-k pass occupies few compute
+        units.  The fork comes after the scoring kernel, which wants the whole chip.
+        (Forking before the pooling, so that the HCA pooling runs aside too, measured
+        slower: every edge between the graph's queues costs several microseconds.)"""
+        import torch
+
         self.pool_new_blocks(r)
+        if len(self.layers) == 2 and self.s_hca is not None:
+            self.index_score(r)
+            main = torch.cuda.current_stream()
+            self.s_hca.wait_stream(main)
+            with torch.cuda.stream(self.s_hca):
+                self.attend(r, ["hca"])
+            self.select(r)
+            self.attend(r, ["csa"])
+            main.wait_stream(self.s_hca)
+            return
         if "csa" in self.layers:
             self.index(r)
         self.attend(r)
@@ -779,7 +805,7 @@ def main():
     warmup = args.warmup if args.warmup is not None else (50 if decode else 3)
     R = args.replicas if args.replicas is not None else (6 if decode else 1)
     torch.cuda.set_device(0)
-    wl = Workload(cfg, R, sink=args.sink, norm_rope=args.norm_rope)
+    wl = Workload(cfg, R, sink=args.sink, norm_rope=args.norm_rope, serial=args.serial)
 
     # warm up eagerly (also sets the library's one-time kernel attributes)
     for i in range(warmup):
@@ -857,6 +883,8 @@ def main():
                    "c": cfg.c, "n_h": cfg.n_h, "m": cfg.m, "m_hca": cfg.m_hca, "k": cfg.k,
                    "n_ih": cfg.n_ih, "c_I": cfg.c_I, "window": cfg.W, "replicas": R,
                    "timing": "hip graph per step, rotating replicas",
+                   "streams": ("one" if args.serial or len(wl.layers) < 2 else
+                               "two: HCA attention concurrent with the CSA top-k and attention"),
                    **({"attention_sink": "per-head, N(0, 2^2)"} if args.sink else {}),
                    **({"indexer_keys": "MX FP4 (E2M1, E8M0 per 32), FP8 queries"} if args.fp4_keys else {}),
                    **({"norm_rope": "RMSNorm + RoPE on the last 64 dims: entries, queries, window"}

@@ -239,29 +239,29 @@ class Workload:
                 lib.hca_attend_sink(*args, sk, *tail)
 
     def step(self, r):
-        """One pass of the path.  With both layers present the pooling of both layers and
-        the HCA attention run on a second stream while the CSA top-k pass runs on the
-        first: the HCA layer needs nothing from the indexer, the indexer nothing from the
-        pooled KV entries, and the top-k pass occupies few compute units.  The CSA
-        attention waits for the top-k and for its pooled entry.  The fork comes after the
-        scoring kernel, which wants the whole chip.
-        (Forking before the pooling, so that the HCA pooling runs aside too, measured
-        slower: every edge between the graph's queues costs several microseconds.)"""
+        """One pass of the path.  With both layers present the HCA attention runs on a
+        second stream while the CSA top-k pass and attention run on the first: the HCA
+        layer needs nothing from the indexer, and the top-k pass occupies few compute
+        units.  The fork comes after the scoring kernel, which wants
+        the whole chip.  Edges between the graph's hardware queues resolve late (the
+        waiting queue resumes only when the other has drained), so the CSA chain keeps
+        no dependency on the second stream.  Both poolings stay in front of the scoring
+        kernel, so that the HCA attention starts with the top-k pass."""
         import torch
 
         if len(self.layers) == 2 and self.s_hca is not None:
-            self.index_score(r)
             main = torch.cuda.current_stream()
-            self.s_hca.wait_stream(main)
-            with torch.cuda.stream(self.s_hca):
-                self.pool_new_blocks(r, ["csa"])
-                pooled = torch.cuda.Event()
-                pooled.record(self.s_hca)
-                self.pool_new_blocks(r, ["hca"])
-                self.attend(r, ["hca"])
+            self.pool_new_blocks(r)
+            self.index_score(r)
+            scored = torch.cuda.Event()
+            scored.record(main)
+            # the CSA chain is issued first, so that it stays on the scoring kernel's
+            # hardware queue; the second stream forks from the scoring kernel
             self.select(r)
-            main.wait_event(pooled)  # the CSA entry of the step's own block
             self.attend(r, ["csa"])
+            self.s_hca.wait_event(scored)
+            with torch.cuda.stream(self.s_hca):
+                self.attend(r, ["hca"])
             main.wait_stream(self.s_hca)
             return
         self.pool_new_blocks(r)
@@ -891,7 +891,7 @@ def main():
                    "n_ih": cfg.n_ih, "c_I": cfg.c_I, "window": cfg.W, "replicas": R,
                    "timing": "hip graph per step, rotating replicas",
                    "streams": ("one" if args.serial or len(wl.layers) < 2 else
-                               "two: pooling and HCA attention concurrent with the CSA top-k pass"),
+                               "two: HCA attention concurrent with the CSA top-k pass and attention"),
                    **({"attention_sink": "per-head, N(0, 2^2)"} if args.sink else {}),
                    **({"indexer_keys": "MX FP4 (E2M1, E8M0 per 32), FP8 queries"} if args.fp4_keys else {}),
                    **({"norm_rope": "RMSNorm + RoPE on the last 64 dims: entries, queries, window"}

@@ -92,40 +92,19 @@ extern "C" int csahca_kv_append(void* kv_ring, void* gate_ring, void* entries, c
   const int e = elem_bytes(dtype), rb = c * e;
   const long long nbs = new_bstride * e, rbs = ring_bstride * e;
   const int t = (int)(n_old % m);
-  const long long a0 = t ? n_old + (m - t) : n_old;  // first block start at or after n_old
   const int keep = n_new < R ? n_new : R;  // the last tokens, kept for the window and tail
-  int rc;
-  // With room for the old tail and all new tokens (decode, short chunks), the new tokens
-  // enter the ring first and a block begun earlier is pooled from there; otherwise the
-  // block's missing tokens enter first, then the last tokens once it is pooled.
+  // With room for the old tail and all new tokens (decode, short chunks), the pooling
+  // launch also stores the new tokens of the blocks it completes (it overwrites no ring
+  // row it reads), and the new tail is stored beside it; otherwise the last tokens are
+  // stored after the pooling, which may have read the rows they replace.
   const bool early = n_new + t <= R;
-  if (early && (rc = store_rows(kv_new, gate_new, kv_ring, gate_ring, B, 0, n_new, n_old, R, rb, nbs, rbs, st)))
-    return rc;
-  // 1. a block begun by earlier appends (its tail is in the ring) and completed now
-  if (t && n_new >= m - t) {
-    if (!early &&
-        (rc = store_rows(kv_new, gate_new, kv_ring, gate_ring, B, 0, m - t, n_old, R, rb, nbs, rbs, st)))
-      return rc;
-    const long long blk = n_old / m;
-    const long long row = (blk * m) % R;
-    if ((rc = pool_entry(name, (const char*)kv_ring + row * rb, (const char*)gate_ring + row * rb, nullptr,
-                         nullptr, false, 0, pos_bias, (char*)entries + blk * rb, B, m, c, m, dtype,
-                         ring_bstride, ent_bstride, stream)))
-      return rc;
-  }
-  // 2. blocks that lie wholly in the new tokens: pooled from them directly
-  const long long a1 = last * m;
-  if (a1 > a0) {
-    const long long off = (a0 - n_old) * rb;
-    if ((rc = pool_entry(name, (const char*)kv_new + off, (const char*)gate_new + off, nullptr, nullptr,
-                         false, 0, pos_bias, (char*)entries + (a0 / m) * rb, B, (int)(a1 - a0), c, m,
-                         dtype, new_bstride, ent_bstride, stream)))
-      return rc;
-  }
-  // 3. the last tokens join the ring (after step 1 has read the rows they may replace)
-  if (early) {
-    clear_error();
-    return CSAHCA_OK;
+  int rc = pool_append(name, kv_new, gate_new, kv_ring, gate_ring, R, n_old, early, pos_bias, entries, B,
+                       first, last - first, c, m, dtype, new_bstride, ring_bstride, ent_bstride, stream);
+  if (rc) return rc;
+  if (early) {  // tokens past the last completed block (all of them when none completes)
+    const long long s0 = last * m > n_old ? last * m - n_old : 0;
+    return store_rows(kv_new, gate_new, kv_ring, gate_ring, B, (int)s0, n_new - (int)s0, n_old, R, rb, nbs,
+                      rbs, st);
   }
   return store_rows(kv_new, gate_new, kv_ring, gate_ring, B, n_new - keep, keep, n_old, R, rb, nbs, rbs, st);
 }

@@ -21,6 +21,7 @@ template <>
 struct Vec8<uint16_t> {
   u32x4 raw;
   CSAHCA_DEV void load(const uint16_t* p) { raw = *reinterpret_cast<const u32x4*>(p); }
+  CSAHCA_DEV void put(uint16_t* p) const { *reinterpret_cast<u32x4*>(p) = raw; }
   CSAHCA_DEV float get(int i) const {
     uint32_t w = raw[i >> 1];
     return (i & 1) ? __uint_as_float(w & 0xFFFF0000u) : __uint_as_float(w << 16);
@@ -39,6 +40,10 @@ struct Vec8<float> {
   CSAHCA_DEV void load(const float* p) {
     a = *reinterpret_cast<const f32x4*>(p);
     b = *reinterpret_cast<const f32x4*>(p + 4);
+  }
+  CSAHCA_DEV void put(float* p) const {
+    *reinterpret_cast<f32x4*>(p) = a;
+    *reinterpret_cast<f32x4*>(p + 4) = b;
   }
   CSAHCA_DEV float get(int i) const { return i < 4 ? a[i] : b[i - 4]; }
   static CSAHCA_DEV void store(float* p, const float* v) {

@@ -27,10 +27,13 @@ using csahca::VEC;
 // chunks of UB tokens issue all their loads first and reduce the chunk as balanced trees
 // (max, sum of weights, sum of weighted values), so the dependent chain per chunk is
 // log2(UB) deep instead of UB; a partial last chunk takes the guarded path.
-template <typename T, int UB, bool HAS_P>
+// With ST the tokens read are also written to a doubled ring (row j to sx + j*c and
+// sx + j*c + rs, likewise for the logits), so that an append stores what it pools.
+template <typename T, int UB, bool HAS_P, bool ST = false>
 CSAHCA_DEV void pool_run(const T* __restrict__ xp, const T* __restrict__ zp,
                          const float* __restrict__ pp, int c, int j_lo, int j_hi,
-                         float (&mx)[VEC], float (&sum)[VEC], float (&acc)[VEC]) {
+                         float (&mx)[VEC], float (&sum)[VEC], float (&acc)[VEC],
+                         T* sx = nullptr, T* sz = nullptr, long long rs = 0) {
   int j0 = j_lo;
   for (; j0 + UB <= j_hi; j0 += UB) {
     Vec8<T> xv[UB], zv[UB];
@@ -38,6 +41,16 @@ CSAHCA_DEV void pool_run(const T* __restrict__ xp, const T* __restrict__ zp,
     for (int u = 0; u < UB; ++u) {
       xv[u].load(xp + (long long)(j0 + u) * c);
       zv[u].load(zp + (long long)(j0 + u) * c);
+    }
+    if (ST) {
+#pragma unroll
+      for (int u = 0; u < UB; ++u) {
+        const long long o = (long long)(j0 + u) * c;
+        xv[u].put(sx + o);
+        xv[u].put(sx + o + rs);
+        zv[u].put(sz + o);
+        zv[u].put(sz + o + rs);
+      }
     }
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
@@ -76,6 +89,13 @@ CSAHCA_DEV void pool_run(const T* __restrict__ xp, const T* __restrict__ zp,
     Vec8<T> xv, zv;
     xv.load(xp + (long long)j0 * c);
     zv.load(zp + (long long)j0 * c);
+    if (ST) {
+      const long long o = (long long)j0 * c;
+      xv.put(sx + o);
+      xv.put(sx + o + rs);
+      zv.put(sz + o);
+      zv.put(sz + o + rs);
+    }
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
       float z = zv.get(e);
@@ -90,7 +110,48 @@ CSAHCA_DEV void pool_run(const T* __restrict__ xp, const T* __restrict__ zp,
   }
 }
 
-template <typename T, int UB, bool HAS_P, bool OV, bool NR>
+// Append mode: the entries are those an append of tokens n_old .. to a sequence
+// completes.  Row j of entry e (position e*m + j) comes from the new tokens (X, row
+// e*m + j - n_old) or, for the block begun by earlier appends, from the doubled ring
+// (row (e*m + j) mod R; a block never wraps, R being a multiple of m).  With `store`, the
+// new tokens read are also written to the ring (only when that overwrites none of the
+// ring rows read in the same launch).
+struct AppendRows {
+  const void* ring_x;
+  const void* ring_z;
+  int R;
+  int store;
+  long long n_old;
+  long long ring_bs;  // elements
+};
+
+constexpr int PLAIN = 0, TWO_STREAM = 1, APPEND = 2;
+
+// Pool tokens [j_lo, j_hi) of entry e (absolute index) in append mode.
+template <typename T, int UB, bool HAS_P>
+CSAHCA_DEV void pool_append_run(const T* X, const T* Z, const AppendRows& ap, const float* pp,
+                                int b, long long e, int m, int c, int cv, long long in_bs,
+                                int j_lo, int j_hi, float (&mx)[VEC], float (&sum)[VEC],
+                                float (&acc)[VEC]) {
+  const long long p0 = e * m;  // position of the block's first token
+  const int js = (int)max(0LL, min((long long)m, ap.n_old - p0));  // tokens from the ring
+  const long long ro = (long long)b * ap.ring_bs + (p0 % ap.R) * c + (long long)cv * VEC;
+  if (j_lo < js)
+    pool_run<T, UB, HAS_P>((const T*)ap.ring_x + ro, (const T*)ap.ring_z + ro, pp, c, j_lo,
+                           min(j_hi, js), mx, sum, acc);
+  if (j_hi > js) {
+    // rows j >= js of the new tokens: row j sits at new row p0 + j - n_old >= 0
+    const long long no = (long long)b * in_bs + (p0 - ap.n_old) * c + (long long)cv * VEC;
+    const int lo = max(j_lo, js);
+    if (ap.store)
+      pool_run<T, UB, HAS_P, true>(X + no, Z + no, pp, c, lo, j_hi, mx, sum, acc,
+                                   (T*)ap.ring_x + ro, (T*)ap.ring_z + ro, (long long)ap.R * c);
+    else
+      pool_run<T, UB, HAS_P>(X + no, Z + no, pp, c, lo, j_hi, mx, sum, acc);
+  }
+}
+
+template <typename T, int UB, bool HAS_P, int MODE, bool NR>
 __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ X,
                                                    const T* __restrict__ Z,
                                                    const T* __restrict__ Xb,
@@ -98,7 +159,9 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ X,
                                                    const float* __restrict__ P,
                                                    T* __restrict__ out, int N, int c, int m,
                                                    int prev, long long in_bs, long long out_bs,
-                                                   long long total, NormRope nr, long long entry0) {
+                                                   long long total, NormRope nr, long long entry0,
+                                                   AppendRows ap) {
+  constexpr bool OV = MODE == TWO_STREAM;
   const long long item = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (item >= total) return;
   const int CV = c / VEC;
@@ -125,7 +188,11 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ X,
     sum[e] = 0.f;
     acc[e] = 0.f;
   }
-  pool_run<T, UB, HAS_P>(X + base, Z + base, HAS_P ? P + cv * VEC : nullptr, c, 0, m, mx, sum, acc);
+  if (MODE == APPEND)
+    pool_append_run<T, UB, HAS_P>(X, Z, ap, HAS_P ? P + cv * VEC : nullptr, b, entry0 + i, m, c, cv,
+                                  in_bs, 0, m, mx, sum, acc);
+  else
+    pool_run<T, UB, HAS_P>(X + base, Z + base, HAS_P ? P + cv * VEC : nullptr, c, 0, m, mx, sum, acc);
   if (OV && blk >= 1)  // stream b over the previous block, bias rows m .. 2m-1
     pool_run<T, UB, HAS_P>(Xb + base - (long long)m * c, Zb + base - (long long)m * c,
                            HAS_P ? P + (long long)m * c + cv * VEC : nullptr, c, 0, m, mx, sum, acc);
@@ -149,7 +216,7 @@ CSAHCA_DEV void store_one<uint16_t>(uint16_t* p, float v) { *p = f32_to_bf16(v);
 template <>
 CSAHCA_DEV void store_one<float>(float* p, float v) { *p = v; }
 
-template <typename T, int UB, bool HAS_P, bool OV, bool NR>
+template <typename T, int UB, bool HAS_P, int MODE, bool NR>
 __global__ __launch_bounds__(NR ? 512 : 256) void pool_block_kernel(const T* __restrict__ X,
                                                         const T* __restrict__ Z,
                                                         const T* __restrict__ Xb,
@@ -158,7 +225,9 @@ __global__ __launch_bounds__(NR ? 512 : 256) void pool_block_kernel(const T* __r
                                                         T* __restrict__ out, int N, int c,
                                                         int m, int prev, int S, int CVG,
                                                         long long in_bs, long long out_bs,
-                                                        NormRope nr, long long entry0) {
+                                                        NormRope nr, long long entry0,
+                                                        AppendRows ap) {
+  constexpr bool OV = MODE == TWO_STREAM;
   extern __shared__ float part[];  // [S][CVG][3][VEC], then (NR) [c] results + [16] sums
   const int CG = c / VEC / CVG;
   const int cvl = threadIdx.x % CVG, s = threadIdx.x / CVG;
@@ -179,8 +248,12 @@ __global__ __launch_bounds__(NR ? 512 : 256) void pool_block_kernel(const T* __r
     sum[e] = 0.f;
     acc[e] = 0.f;
   }
-  pool_run<T, UB, HAS_P>(X + base, Z + base, HAS_P ? P + cv * VEC : nullptr, c, j_lo, min(j_hi, m),
-                         mx, sum, acc);
+  if (MODE == APPEND)
+    pool_append_run<T, UB, HAS_P>(X, Z, ap, HAS_P ? P + cv * VEC : nullptr, b, entry0 + i, m, c, cv,
+                                  in_bs, j_lo, min(j_hi, m), mx, sum, acc);
+  else
+    pool_run<T, UB, HAS_P>(X + base, Z + base, HAS_P ? P + cv * VEC : nullptr, c, j_lo, min(j_hi, m),
+                           mx, sum, acc);
   if (OV && j_hi > m)
     pool_run<T, UB, HAS_P>(Xb + base - (long long)m * c, Zb + base - (long long)m * c,
                            HAS_P ? P + (long long)m * c + cv * VEC : nullptr, c, max(j_lo, m) - m,
@@ -243,11 +316,12 @@ __global__ __launch_bounds__(NR ? 512 : 256) void pool_block_kernel(const T* __r
   }
 }
 
-template <typename T, bool HAS_P, bool OV, bool NR>
+template <typename T, bool HAS_P, int MODE, bool NR>
 void launch_pool(const void* kv, const void* gate, const void* kv_b, const void* gate_b,
                  const float* pos_bias, void* out, int B, long long N, int c, int m, int prev,
                  long long in_bs, long long out_bs, const NormRope& nr, long long entry0,
-                 hipStream_t st) {
+                 const AppendRows& ap, hipStream_t st) {
+  constexpr bool OV = MODE == TWO_STREAM;
   const long long total = (long long)B * N * (c / 8);
   const int CV = c / VEC;
   const int mt = OV ? 2 * m : m;  // tokens an entry reads
@@ -271,22 +345,24 @@ void launch_pool(const void* kv, const void* gate, const void* kv_b, const void*
     const size_t lds = ((size_t)S * CVG * 3 * VEC + (NR ? (size_t)c + 16 : 0)) * sizeof(float);
     const unsigned grid = (unsigned)(B * N * (CV / CVG)), threads = (unsigned)(S * CVG);
     if (span % 8 == 0 && m % 8 == 0)
-      hipLaunchKernelGGL((pool_block_kernel<T, 8, HAS_P, OV, NR>), dim3(grid), dim3(threads), lds, st,
+      hipLaunchKernelGGL((pool_block_kernel<T, 8, HAS_P, MODE, NR>), dim3(grid), dim3(threads), lds, st,
                          X, Z, Xb, Zb, pos_bias, (T*)out, (int)N, c, m, prev, S, CVG, in_bs, out_bs,
-                         nr, entry0);
+                         nr, entry0, ap);
     else
-      hipLaunchKernelGGL((pool_block_kernel<T, 4, HAS_P, OV, NR>), dim3(grid), dim3(threads), lds, st,
+      hipLaunchKernelGGL((pool_block_kernel<T, 4, HAS_P, MODE, NR>), dim3(grid), dim3(threads), lds, st,
                          X, Z, Xb, Zb, pos_bias, (T*)out, (int)N, c, m, prev, S, CVG, in_bs, out_bs,
-                         nr, entry0);
+                         nr, entry0, ap);
     return;
   }
   const unsigned blocks = (unsigned)cdiv<long long>(total, 256);
   if (m % 8 == 0)
-    hipLaunchKernelGGL((pool_kernel<T, 8, HAS_P, OV, NR>), dim3(blocks), dim3(256), 0, st, X, Z, Xb,
-                       Zb, pos_bias, (T*)out, (int)N, c, m, prev, in_bs, out_bs, total, nr, entry0);
+    hipLaunchKernelGGL((pool_kernel<T, 8, HAS_P, MODE, NR>), dim3(blocks), dim3(256), 0, st, X, Z, Xb,
+                       Zb, pos_bias, (T*)out, (int)N, c, m, prev, in_bs, out_bs, total, nr, entry0,
+                       ap);
   else
-    hipLaunchKernelGGL((pool_kernel<T, 4, HAS_P, OV, NR>), dim3(blocks), dim3(256), 0, st, X, Z, Xb,
-                       Zb, pos_bias, (T*)out, (int)N, c, m, prev, in_bs, out_bs, total, nr, entry0);
+    hipLaunchKernelGGL((pool_kernel<T, 4, HAS_P, MODE, NR>), dim3(blocks), dim3(256), 0, st, X, Z, Xb,
+                       Zb, pos_bias, (T*)out, (int)N, c, m, prev, in_bs, out_bs, total, nr, entry0,
+                       ap);
 }
 
 struct PoolArgs {
@@ -299,23 +375,27 @@ struct PoolArgs {
   long long in_bs, out_bs;
   NormRope nr;
   long long entry0;
+  AppendRows ap;
   hipStream_t st;
 };
 
-template <typename T, bool HP, bool OV, bool NR>
+template <typename T, bool HP, int MODE, bool NR>
 void run_pool(const PoolArgs& a) {
-  launch_pool<T, HP, OV, NR>(a.kv, a.gate, a.kv_b, a.gate_b, a.pos_bias, a.out, a.B, a.N, a.c, a.m,
-                             a.prev, a.in_bs, a.out_bs, a.nr, a.entry0, a.st);
+  launch_pool<T, HP, MODE, NR>(a.kv, a.gate, a.kv_b, a.gate_b, a.pos_bias, a.out, a.B, a.N, a.c,
+                               a.m, a.prev, a.in_bs, a.out_bs, a.nr, a.entry0, a.ap, a.st);
 }
 
 template <typename T>
-void pick_pool(const PoolArgs& a, bool hp, bool ov, bool nr) {
+void pick_pool(const PoolArgs& a, bool hp, int mode, bool nr) {
   using F = void (*)(const PoolArgs&);
-  static const F tab[8] = {run_pool<T, false, false, false>, run_pool<T, false, false, true>,
-                           run_pool<T, false, true, false>,  run_pool<T, false, true, true>,
-                           run_pool<T, true, false, false>,  run_pool<T, true, false, true>,
-                           run_pool<T, true, true, false>,   run_pool<T, true, true, true>};
-  tab[(hp ? 4 : 0) + (ov ? 2 : 0) + (nr ? 1 : 0)](a);
+  static const F tab[12] = {
+      run_pool<T, false, PLAIN, false>,      run_pool<T, false, PLAIN, true>,
+      run_pool<T, false, TWO_STREAM, false>, run_pool<T, false, TWO_STREAM, true>,
+      run_pool<T, false, APPEND, false>,     run_pool<T, false, APPEND, true>,
+      run_pool<T, true, PLAIN, false>,       run_pool<T, true, PLAIN, true>,
+      run_pool<T, true, TWO_STREAM, false>,  run_pool<T, true, TWO_STREAM, true>,
+      run_pool<T, true, APPEND, false>,      run_pool<T, true, APPEND, true>};
+  tab[(hp ? 6 : 0) + 2 * mode + (nr ? 1 : 0)](a);
 }
 
 }  // namespace
@@ -371,11 +451,34 @@ int pool_entry(const char* name, const void* kv, const void* gate, const void* k
     return CSAHCA_EINVAL;
   }
   PoolArgs a{kv, gate, kv_b, gate_b, pos_bias, out, B, N, c, m, prev, in_bs, out_bs,
-             nr ? *nr : NormRope{nullptr, 0.f, 1.f, 0, 0}, entry0, (hipStream_t)stream};
+             nr ? *nr : NormRope{nullptr, 0.f, 1.f, 0, 0}, entry0, AppendRows{nullptr, nullptr, 1, 0, 0, 0},
+             (hipStream_t)stream};
   if (dtype == CSAHCA_BF16)
-    pick_pool<uint16_t>(a, pos_bias != nullptr, ov, nr != nullptr);
+    pick_pool<uint16_t>(a, pos_bias != nullptr, ov ? TWO_STREAM : PLAIN, nr != nullptr);
   else
-    pick_pool<float>(a, pos_bias != nullptr, ov, nr != nullptr);
+    pick_pool<float>(a, pos_bias != nullptr, ov ? TWO_STREAM : PLAIN, nr != nullptr);
+  return launch_status(name);
+}
+
+int pool_append(const char* name, const void* kv_new, const void* gate_new, const void* ring_x,
+                const void* ring_z, int R, long long n_old, bool store, const float* pos_bias,
+                void* entries, int B, long long first, long long count, int c, int m, int dtype,
+                long long new_bs, long long ring_bs, long long ent_bs, void* stream) {
+  if (count <= 0) return CSAHCA_OK;
+  // N entries, the first being entry `first` of the cache; `out` addresses entry `first`
+  const long long total = (long long)B * count * (c / 8);
+  if (cdiv<long long>(total, 256) > 0x7FFFFFFFLL || count > 0x7FFFFFFFLL) {
+    set_error("%s: problem too large for one launch", name);
+    return CSAHCA_ENOTSUP;
+  }
+  const int e = dtype == CSAHCA_BF16 ? 2 : 4;
+  PoolArgs a{kv_new, gate_new, nullptr, nullptr, pos_bias, (char*)entries + first * c * e, B, count, c, m, 0,
+             new_bs, ent_bs, NormRope{nullptr, 0.f, 1.f, 0, 0}, first,
+             AppendRows{ring_x, ring_z, R, store ? 1 : 0, n_old, ring_bs}, (hipStream_t)stream};
+  if (dtype == CSAHCA_BF16)
+    pick_pool<uint16_t>(a, pos_bias != nullptr, APPEND, false);
+  else
+    pick_pool<float>(a, pos_bias != nullptr, APPEND, false);
   return launch_status(name);
 }
 

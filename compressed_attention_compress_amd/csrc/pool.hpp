@@ -16,4 +16,14 @@ int pool_entry(const char* name, const void* kv, const void* gate, const void* k
                int n, int c, int m, int dtype, long long in_bs, long long out_bs, void* stream,
                const NormRope* nr = nullptr, long long entry0 = 0);
 
+// Pools the `count` entries first .. first+count-1 that an append of tokens n_old .. to B
+// sequences completes, in one launch: rows before n_old come from the doubled rings
+// (R rows, batch stride ring_bs), the others from the new tokens (batch stride new_bs).
+// With `store` the new tokens read are also written to the rings (the caller guarantees
+// that this overwrites no ring row read here).  Arguments are validated by the caller.
+int pool_append(const char* name, const void* kv_new, const void* gate_new, const void* ring_x,
+                const void* ring_z, int R, long long n_old, bool store, const float* pos_bias,
+                void* entries, int B, long long first, long long count, int c, int m, int dtype,
+                long long new_bs, long long ring_bs, long long ent_bs, void* stream);
+
 }  // namespace csahca

@@ -130,7 +130,22 @@ CSAHCA_DEV void norm_rope8(float (&v)[VEC], const float (&g)[VEC], int ch0, int 
 #pragma unroll
     for (int e = 0; e < VEC; ++e) v[e] *= inv * g[e];
   }
-  if (ch0 >= c - nr.d) {
+  const int P = nr.d / 2;  // rotated pairs
+  if (P == 0) return;
+  if (P <= CV) {
+    // one angle per lane: lane li of the row's group forms the cos and sin of pair li,
+    // and the lanes holding the rotated channels fetch their four pairs
+    const int li = (int)(threadIdx.x & (CV - 1)), base = (int)(threadIdx.x & 63) & ~(CV - 1);
+    float cs = 1.f, sn = 0.f;
+    if (li < P) rope_cos_sin(pos, rope_freq(li, nr.d, nr.theta), cs, sn);
+    const int i0 = (ch0 - (c - nr.d)) / 2;  // negative outside the rotated channels
+#pragma unroll
+    for (int q = 0; q < VEC / 2; ++q) {
+      const int src = base + min(max(i0 + q, 0), P - 1);
+      const float cq = __shfl(cs, src, 64), sq = __shfl(sn, src, 64);
+      if (i0 >= 0) rope_apply(v[2 * q], v[2 * q + 1], cq, sq);
+    }
+  } else if (ch0 >= c - nr.d) {
     // the lane's four pairs: f_{i0+q} = f_{i0} * step^q, step = theta^(-2/d)
     const int i0 = (ch0 - (c - nr.d)) / 2;
     const double l2t = log2((double)nr.theta);

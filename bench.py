@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode query-tokens/s and achieved HBM GB/s, CSA+HCA at 128K/1M context"
 HBM_PEAK_GBS = 8000.0
+FP8_PEAK_TFLOPS = 5000.0  # dense fp8 matrix cores
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -94,6 +95,8 @@ class Workload:
         self.layers = [l for l in ("csa", "hca") if f"X_{l}" in prob]
         B, c, n, dt = cfg.B, cfg.c, self.n, cfg.dtype
         self.q_pos = prob["q_pos"]
+        # storage of KV rows, caches and outputs: float32, or bfloat16 bit patterns in int16
+        et = torch.float32 if dt == 0 else torch.int16
         self.win_pos = torch.zeros(B, dtype=torch.int32, device=dev)
         self.scale = 1.0 / math.sqrt(c)
         # the pooled caches as a prefill would leave them (untimed): every complete block
@@ -108,14 +111,14 @@ class Workload:
             self.nr_wpos0 = max(0, n - self.Tq - cfg.W + 1)
             self.nr_L = n - self.nr_wpos0
             self.nr_win_pos = torch.full((B,), self.nr_wpos0, dtype=torch.int32, device=dev)
-            self.nr_win = {l: torch.empty((B, self.nr_L, c), dtype=torch.int16, device=dev)
+            self.nr_win = {l: torch.empty((B, self.nr_L, c), dtype=et, device=dev)
                            for l in self.layers}
-            self.nr_q = {l: torch.empty((B, self.Tq, cfg.n_h, c), dtype=torch.int16, device=dev)
+            self.nr_q = {l: torch.empty((B, self.Tq, cfg.n_h, c), dtype=et, device=dev)
                          for l in self.layers}
         base = {}
         for l in self.layers:
             m = cfg.m if l == "csa" else cfg.m_hca
-            C = torch.zeros((B, n // m, c), dtype=torch.int16, device=dev)
+            C = torch.zeros((B, n // m, c), dtype=et, device=dev)
             if norm_rope:
                 lib.csahca_compress_norm_rope(prob[f"X_{l}"], prob[f"Z_{l}"], None, self.g_kv, C, B,
                                               self.n_old, c, m, 0, self.NR_D, self.NR_EPS,
@@ -138,7 +141,7 @@ class Workload:
         self.N_c = n // cfg.m
         self.N_h = n // cfg.m_hca
         nq = B * self.Tq
-        self.out = {l: torch.empty((B, self.Tq, cfg.n_h, c), dtype=torch.int16, device=dev)
+        self.out = {l: torch.empty((B, self.Tq, cfg.n_h, c), dtype=et, device=dev)
                     for l in self.layers}
         if "csa" in self.layers:
             self.idx = torch.empty((B, self.Tq, cfg.k), dtype=torch.int32, device=dev)
@@ -275,7 +278,7 @@ class Workload:
         once (compressed caches: only the rows the step reads)."""
         cfg = self.cfg
         B, c, W, Tq, n = cfg.B, cfg.c, cfg.W, self.Tq, self.n
-        e = 2  # bf16
+        e = 4 if cfg.dtype == 0 else 2  # bytes per KV / query / output element
         total = 0
         detail = {}
         for l in self.layers:
@@ -819,20 +822,30 @@ def main():
         wl.step(i % R)
     torch.cuda.synchronize()
 
-    graphs = []
+    # one graph holds R consecutive steps (one per replica), as a decode loop would hold
+    # many steps (and layers) in one graph; a second graph holds the K mod R left over
     side = torch.cuda.Stream()
-    for r in range(R):
+
+    def capture(n):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=side):
-            wl.step(r)
-        graphs.append(g)
-    for r in range(R):
-        graphs[r].replay()
+            for r in range(n):
+                wl.step(r)
+        return g
+
+    g_full = capture(R)
+    rem = steps % R
+    g_rem = capture(rem) if rem else None
+    g_full.replay()
+    if g_rem is not None:
+        g_rem.replay()
     torch.cuda.synchronize()
 
     t0 = time.perf_counter()
-    for i in range(steps):
-        graphs[i % R].replay()
+    for _ in range(steps // R):
+        g_full.replay()
+    if g_rem is not None:
+        g_rem.replay()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     sec = (t1 - t0) / steps
@@ -861,13 +874,22 @@ def main():
         dur = e0.elapsed_time(e1) / 1e3 / (rounds * reps)
         kb = wl.index_score_bytes()
         ach = kb / dur / 1e9
-        kname = "index_score_dec128" if decode and cfg.c_I == 128 else "index_score_fp8"
+        kname = ("index_score_f32" if cfg.idx_dtype == 0 else
+                 "index_score_dec128" if decode and cfg.c_I == 128 else
+                 "index_score_pre128" if cfg.c_I == 128 else "index_score_fp8")
         if cfg.idx_dtype == 3:
             kname += " (MX FP4 keys)"  # no counter record for this instance
-        roofline = {"kernel": kname, "bound": "hbm", "achieved": round(ach, 1),
-                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
-                    "traffic": read_traffic(kname) if decode else None,
-                    "avg_launch_us": round(dur * 1e6, 2), "bytes_per_launch": kb}
+        if decode or cfg.idx_dtype == 0:
+            roofline = {"kernel": kname, "bound": "hbm", "achieved": round(ach, 1),
+                        "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                        "traffic": read_traffic(kname) if decode else None,
+                        "avg_launch_us": round(dur * 1e6, 2), "bytes_per_launch": kb}
+        else:  # a prefill chunk's scoring is bound by the fp8 matrix cores
+            tf = f8 / dur / 1e12
+            roofline = {"kernel": kname, "bound": "mfma", "achieved": round(tf, 1),
+                        "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(tf / FP8_PEAK_TFLOPS, 4), "traffic": None,
+                        "avg_launch_us": round(dur * 1e6, 2), "flops_per_launch": f8}
 
     cpu = None
     if not args.no_cpu_baseline and decode:
@@ -884,12 +906,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16+fp8e4m3",
+        "dtype": ("f32" if cfg.dtype == 0 else "bf16") + "+" +
+                 {0: "f32", 2: "fp8e4m3", 3: "mxfp4"}.get(cfg.idx_dtype, "?"),
         "data": "synthetic",
         "config": {"workload": cfg.name, "batch": cfg.B, "context": wl.n, "query_tokens": wl.Tq,
                    "c": cfg.c, "n_h": cfg.n_h, "m": cfg.m, "m_hca": cfg.m_hca, "k": cfg.k,
                    "n_ih": cfg.n_ih, "c_I": cfg.c_I, "window": cfg.W, "replicas": R,
-                   "timing": "hip graph per step, rotating replicas",
+                   "timing": f"hip graphs of {R} steps (one per replica), rotating replicas",
                    "streams": ("one" if args.serial or len(wl.layers) < 2 else
                                "two: HCA attention concurrent with the CSA top-k pass and attention"),
                    **({"attention_sink": "per-head, N(0, 2^2)"} if args.sink else {}),

@@ -85,7 +85,9 @@ class Workload:
         self.lib = lib
         self.cfg = cfg
         self.R = replicas
-        self.s_hca = None if serial else torch.cuda.Stream()  # default priority
+        # a second stream for the HCA attention at decode (a prefill chunk keeps one: its
+        # two attention calls each fill the chip, and measured faster one after the other)
+        self.s_hca = None if serial or cfg.kind == "prefill" else torch.cuda.Stream()  # default priority
         dev = "cuda"
         prob = make_problem_device(cfg, dev)
         self.prob = prob
@@ -913,7 +915,7 @@ def main():
                    "c": cfg.c, "n_h": cfg.n_h, "m": cfg.m, "m_hca": cfg.m_hca, "k": cfg.k,
                    "n_ih": cfg.n_ih, "c_I": cfg.c_I, "window": cfg.W, "replicas": R,
                    "timing": f"hip graphs of {R} steps (one per replica), rotating replicas",
-                   "streams": ("one" if args.serial or len(wl.layers) < 2 else
+                   "streams": ("one" if wl.s_hca is None or len(wl.layers) < 2 else
                                "two: HCA attention concurrent with the CSA top-k pass and attention"),
                    **({"attention_sink": "per-head, N(0, 2^2)"} if args.sink else {}),
                    **({"indexer_keys": "MX FP4 (E2M1, E8M0 per 32), FP8 queries"} if args.fp4_keys else {}),

@@ -893,6 +893,32 @@ def main():
                         "frac": round(tf / FP8_PEAK_TFLOPS, 4), "traffic": None,
                         "avg_launch_us": round(dur * 1e6, 2), "flops_per_launch": f8}
 
+    if roofline is None and "hca" in wl.layers:
+        # no indexer: the HCA attention call (attention kernel and split merge) is the path
+        gh = torch.cuda.CUDAGraph()
+        reps = max(R, 8)
+        with torch.cuda.graph(gh, stream=side):
+            for i in range(reps):
+                wl.attend(i % R, ["hca"])
+        gh.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        rounds = 10 if decode else 1
+        with torch.cuda.stream(side):
+            e0.record(side)
+            for _ in range(rounds):
+                gh.replay()
+            e1.record(side)
+        torch.cuda.synchronize()
+        dur = e0.elapsed_time(e1) / 1e3 / (rounds * reps)
+        kb = detail["hca_attend"]
+        ach = kb / dur / 1e9
+        roofline = {"kernel": "hca_attend (attend_bf16 + attend_combine)", "bound": "hbm",
+                    "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                    "avg_launch_us": round(dur * 1e6, 2), "bytes_per_launch": kb}
+
     cpu = None
     if not args.no_cpu_baseline and decode:
         cpu = cpu_baseline(wl, args.cpu_seconds)

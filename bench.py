@@ -417,6 +417,27 @@ def calibrate_copy():
     print(json.dumps({"copy_bytes": COPY_BYTES}), flush=True)
 
 
+def measured_copy_gbs():
+    """Achievable HBM rate on this machine: one elementwise pass reading 1 GiB and writing 1 GiB
+    (torch.neg), bytes moved / time, best of five."""
+    import torch
+    a = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    torch.neg(a, out=b)
+    torch.cuda.synchronize()
+    best = 0.0
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        torch.neg(a, out=b)
+        e1.record()
+        torch.cuda.synchronize()
+        best = max(best, 2 * COPY_BYTES / (e0.elapsed_time(e1) / 1e3) / 1e9)
+    del a, b
+    torch.cuda.empty_cache()
+    return best
+
+
 def cpu_baseline(wl, seconds):
     """The oracle, as it stands, on a bounded sample of the same workload: complete steps
     for whole sequences, repeated until about `seconds` of CPU time is spent."""
@@ -918,6 +939,11 @@ def main():
                     "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
                     "avg_launch_us": round(dur * 1e6, 2), "bytes_per_launch": kb}
+
+    if roofline is not None and roofline["bound"] == "hbm":
+        cg = measured_copy_gbs()  # the same rate against what a plain copy reaches here
+        roofline["copy_ceiling_gbs"] = round(cg, 1)
+        roofline["frac_of_copy_ceiling"] = round(roofline["achieved"] / cg, 4)
 
     cpu = None
     if not args.no_cpu_baseline and decode:

@@ -235,3 +235,29 @@ def test_attend_reads_window_from_ring(m):
         torch.cuda.synchronize()
         assert torch.equal(o_r, o_d), f"n={n} Tq={Tq}"
         assert torch.equal(l_r, l_d), f"n={n} Tq={Tq}"
+
+
+def test_append_far_into_a_long_sequence():
+    """A sequence first given 2^20 + 3 tokens in one chunk (a prefill), then decode
+    appends: ring slots and entry indices at million-token positions."""
+    print("[kv append far positions]", flush=True)
+    rng = np.random.default_rng(12)
+    B, c, m, W = 1, 64, 4, 128
+    n0 = (1 << 20) + 3
+    chunks = [n0, 1, 1, 2, 5, 130]
+    total = sum(chunks)
+    cx = rng.standard_normal((B, total, c), dtype=np.float32) * 0.1
+    cz = rng.standard_normal((B, total, c), dtype=np.float32)
+    dX, dZ = H.to_dev(cx), H.to_dev(cz)
+    dev = DevCache(B, c, m, W, F32, total)
+    sim = K.KVSim(c, m, W)
+    X, Z = cx.astype(np.float64), cz.astype(np.float64)
+    lo = 0
+    for k in chunks:
+        dev.append(dX, dZ, lo, k)
+        torch.cuda.synchronize()
+        made = sim.append(X[0, lo:lo + k], Z[0, lo:lo + k])
+        check_ring(dev, sim, cx, cz, 0)
+        if made:  # the last few entries made (the first chunk makes 2^18 of them)
+            check_entries(dev, sim, X, Z, 0, max(made[0], made[-1] - 7), made[-1] + 1)
+        lo += k

@@ -61,6 +61,7 @@ def rows_tol(ref_norm, ref, d, dtype):
     (F32, 64, 16, 8, 9, 1, True, False),
     (F32, 64, 8, 1, 300, 1, True, True),
     (F32, 8, 8, 3, 4, 1, True, False),        # one lane per row
+    (F32, 64, 64, 1, 3, 1, False, False),     # more pairs than lanes per row (the per-lane path)
 ])
 def test_norm_rope_rows(dtype, c, d, H_, T, norm, gain, inplace):
     print(f"[norm_rope rows dtype={dtype} c={c} d={d} H={H_} T={T} norm={norm}]", flush=True)
@@ -68,7 +69,7 @@ def test_norm_rope_rows(dtype, c, d, H_, T, norm, gain, inplace):
     B = 3
     x = encode(rng.standard_normal((B, T, H_, c), dtype=np.float32) * 0.7, dtype)
     g = rng.uniform(0.5, 1.5, size=c).astype(np.float32) if gain else None
-    pos = np.array([0, 1 << 20, 123457], dtype=np.int32)
+    pos = np.array([0, 1 << 20, (1 << 30) + 123457], dtype=np.int32)  # up to 2^30
     pstride = 3
     dx = H.to_dev(x)
     dy = dx if inplace else torch.empty_like(dx)

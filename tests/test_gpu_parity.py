@@ -132,6 +132,8 @@ def small_cases():
         "csa_k_ge_visible": c3.scaled(B=2, n=4 * 100, seed=25, plants=4),
         "prefill_small": c4.scaled(n=4096, Tq=200, seed=26),
         "prefill_from_zero": c4.scaled(n=0, Tq=40, seed=27, k=8),
+        # an odd chunk: the last workgroup of two-query HCA prefill has one query only
+        "prefill_odd_tq": c4.scaled(n=4096 + 5, Tq=41, seed=32),
         "pair_h128": c5.scaled(B=2, n=4 * 3000, seed=28, plants=16),
         # MX FP4 indexer keys (FP8 queries)
         "csa_fp4_h64_k512": c3.scaled(B=2, n=4 * 900 + 2, seed=29, idx_dtype=MXFP4),
@@ -205,7 +207,8 @@ def test_chain_parity(name):
 
 
 @pytest.mark.parametrize("name", ["cfg1_tiny_fp32", "hca_h64_ragged", "csa_h128_k1024",
-                                  "prefill_small", "prefill_from_zero", "pair_h128"])
+                                  "prefill_small", "prefill_from_zero", "prefill_odd_tq",
+                                  "pair_h128"])
 def test_attention_sink(name):
     """csa_attend_sink / hca_attend_sink against the oracle's sink: per-head logits of
     both signs, one dominating the rows and one at -inf (no effect)."""

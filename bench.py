@@ -65,6 +65,8 @@ def parse():
     ap.add_argument("--kv-append", action="store_true",
                     help="time the cache lifecycle at the config's shape (csahca_kv_append of a "
                          "chunk and of one decode token, CSA and HCA caches) instead of the step")
+    ap.add_argument("--pool", action="store_true",
+                    help="time csa_compress / hca_compress over the config's whole context")
     ap.add_argument("--overlap-pool", action="store_true",
                     help="time the overlapped two-stream CSA pooling (full context pass and a "
                          "decode append) at the config's shape instead of the step")
@@ -610,6 +612,83 @@ def overlap_pool(cfg, reps, cpu_seconds, no_cpu):
     print(json.dumps(line), flush=True)
 
 
+def pool_bench(cfg, reps, cpu_seconds, no_cpu):
+    """csa_compress (m) and hca_compress (m') over the config's whole raw context (a prefill
+    config: the old context plus the chunk), one line per call and cache: a pass reads X
+    and Z [B, n, c] once and writes [B, n/m, c].  The caches a config keeps: config 2 the
+    HCA one, configs 1 and 3 the CSA one, configs 4 and 5 both."""
+    import numpy as np
+    import torch
+
+    import compressed_attention_compress_amd as lib
+
+    B, c, dt = cfg.B, cfg.c, cfg.dtype
+    n = cfg.n + (cfg.Tq if cfg.kind == "prefill" else 0)
+    layers = {"hca_decode": ["hca"], "csa_decode": ["csa"]}.get(cfg.kind, ["csa", "hca"])
+    tdt = torch.bfloat16 if dt == 1 else torch.float32
+    es = 2 if dt == 1 else 4
+    st = torch.cuda.current_stream()
+    g = torch.Generator(device="cuda").manual_seed(4321)
+    X = torch.empty((B, n, c), dtype=tdt, device="cuda")
+    Z = torch.empty((B, n, c), dtype=tdt, device="cuda")
+    for b in range(B):  # generated per sequence, to bound the float32 staging
+        X[b].copy_(torch.randn((n, c), generator=g, device="cuda").mul_(cfg.kv_std))
+        Z[b].copy_(torch.randn((n, c), generator=g, device="cuda"))
+    cpu = None
+    if not no_cpu:
+        import oracle
+        rng = np.random.default_rng(6)
+        ntok = 1 << 14  # tokens per oracle call (one sequence slice)
+        Xs, Zs = rng.standard_normal((ntok, c)), rng.standard_normal((ntok, c))
+        mm = cfg.m if layers[0] == "csa" else cfg.m_hca
+        t0 = time.perf_counter()
+        done = 0
+        while True:
+            oracle.pool(Xs, Zs, mm)
+            done += ntok
+            el = time.perf_counter() - t0
+            if el >= cpu_seconds:
+                break
+        cpu = {"value": round(done * (2 * c + c / mm) * es / el / 1e9, 3), "unit": "GB/s",
+               "cores": torch.get_num_threads(), "kind": "oracle",
+               "sample": f"{done} tokens in {ntok}-token slices of one sequence, m = {mm}, "
+                         f"{el:.1f} s, NumPy fp64 (bytes counted at the GPU's storage width)"}
+    for l in layers:
+        m = cfg.m if l == "csa" else cfg.m_hca
+        N = n // m
+        out = torch.empty((B, N, c), dtype=tdt, device="cuda")
+        call = lib.csa_compress if l == "csa" else lib.hca_compress
+
+        def run():
+            call(X, Z, None, out, B, n, c, m, dt, n * c, N * c, stream=st)
+
+        run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(reps):
+            run()
+        e1.record(st)
+        torch.cuda.synchronize()
+        sec = e0.elapsed_time(e1) / 1e3 / reps
+        nbytes = 2 * B * n * c * es + B * N * c * es
+        gbs = nbytes / sec / 1e9
+        line = {
+            "metric": f"{l.upper()} pooling ({l}_compress, m = {m}), achieved HBM GB/s over the full context",
+            "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": reps, "warmup": 1,
+            "ms_per_pass": round(sec * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16" if dt == 1 else "f32", "data": "synthetic",
+            "config": {"workload": f"{l}_pool_{cfg.name}", "batch": B, "context": n, "c": c,
+                       "m": m, "timing": "HIP events around back-to-back launches"},
+            "roofline": {"kernel": "pool_kernel", "bound": "hbm", "achieved": round(gbs, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "traffic": None, "avg_launch_us": round(sec * 1e6, 2), "bytes_per_launch": nbytes},
+            "cpu_baseline": cpu if l == layers[0] else None,
+        }
+        print(json.dumps(line), flush=True)
+        del out
+
+
 def kv_append(cfg, reps, cpu_seconds, no_cpu):
     """csahca_kv_append at the config's shape, for the CSA (m) and the HCA (m') cache of a
     layer pair.  Every sequence holds n - 1 tokens, so that both caches have a tail of
@@ -829,6 +908,9 @@ def main():
         return
     if args.kv_append:
         kv_append(cfg, args.steps or 20, min(args.cpu_seconds, 10.0), args.no_cpu_baseline)
+        return
+    if args.pool:
+        pool_bench(cfg, args.steps or 10, min(args.cpu_seconds, 10.0), args.no_cpu_baseline)
         return
     if args.overlap_pool:
         overlap_pool(cfg, args.steps or 10, min(args.cpu_seconds, 10.0), args.no_cpu_baseline)

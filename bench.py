@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 METRIC = "decode query-tokens/s and achieved HBM GB/s, CSA+HCA at 128K/1M context"
 HBM_PEAK_GBS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0  # dense fp8 matrix cores
+BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix cores
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -844,7 +845,7 @@ def gop_bench(cfg, reps, cpu_seconds, no_cpu):
     flops = 2.0 * T * g * K_g * d_g
     nbytes = 2 * (g * d_g * K_g + T * g * K_g + T * g * d_g)
     if T > 64:
-        bound, ach, peak, unit = "mfma", flops / sec / 1e12, 2500.0, "TFLOP/s"
+        bound, ach, peak, unit = "mfma", flops / sec / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s"
         kname = "gop_gemm"
     else:
         bound, ach, peak, unit = "hbm", nbytes / sec / 1e9, HBM_PEAK_GBS, "GB/s"
@@ -1059,6 +1060,12 @@ def main():
         "hbm_frac": round(abytes / sec / 1e9 / HBM_PEAK_GBS, 4),
         "algorithmic_bytes_per_step": abytes,
         "tflops": {"fp8": round(f8 / sec / 1e12, 2), "bf16": round(bf / sec / 1e12, 2)},
+        # matrix-core use of the whole step: all FLOPs against the bf16 peak, and each
+        # dtype's FLOPs against its own peak (the fraction of the step the matrix cores
+        # would need at peak)
+        "mfma_frac": {"all_vs_bf16_peak": round((f8 + bf) / sec / 1e12 / BF16_PEAK_TFLOPS, 4),
+                      "per_dtype_peak": round((f8 / FP8_PEAK_TFLOPS + bf / BF16_PEAK_TFLOPS)
+                                              / sec / 1e12, 4)},
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

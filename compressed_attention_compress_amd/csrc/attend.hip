@@ -179,9 +179,10 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && NS == 2) ? 2 : 1) void attend_
   uint8_t* tiles = smem;
   uint32_t* tmask = reinterpret_cast<uint32_t*>(smem + NS * TILE * ROWB);  // [NS][NW]
   int* sidx = reinterpret_cast<int*>(tmask + NS * NW);                     // [RS]
-  // exchange area (CS): after sidx, 16-byte aligned
-  uint8_t* xch = smem + NS * TILE * ROWB + NS * NW * 4 + (CSA ? a.RS * 4 : 0);
-  xch = reinterpret_cast<uint8_t*>((reinterpret_cast<uintptr_t>(xch) + 15) & ~(uintptr_t)15);
+  // exchange area (CS): after sidx, 16-byte aligned.  Aligned as an offset from smem, so
+  // that the pointer keeps its LDS address space (ds_read / ds_write, not flat accesses,
+  // whose waits would also drain the row DMA in flight).
+  uint8_t* xch = smem + ((NS * TILE * ROWB + NS * NW * 4 + (CSA ? a.RS * 4 : 0) + 15) & ~15);
 
   // XCD-aware order: consecutive work items (the head groups of one row range first) run
   // on the same XCD, so the rows they share are read from HBM once into that XCD's L2.

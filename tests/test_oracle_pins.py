@@ -23,7 +23,8 @@ def _impl(**over):
                                hca_rows=O.hca_rows, entry_counts=O.entry_counts,
                                window_positions=O.window_positions, rmsnorm=O.rmsnorm,
                                rope_tail=O.rope_tail, norm_rope=O.norm_rope,
-                               grouped_out_proj=O.grouped_out_proj)
+                               grouped_out_proj=O.grouped_out_proj,
+                               entry_positions=O.entry_positions)
     for k, v in over.items():
         setattr(ns, k, v)
     return ns
@@ -332,6 +333,16 @@ def check_rows_and_visibility(o):
     r2 = o.hca_rows(C, m, X[30:], 30, 50, W)
     np.testing.assert_array_equal(r1, r2)
     assert r1.shape[0] == o.visible(50, m, C.shape[0]) + W
+    # the position an entry carries for RoPE (reading: its block's first raw position).
+    # m = 1: an entry is its token, so it carries the token's position.
+    assert o.entry_positions(1, 5, 4).tolist() == [5, 6, 7, 8]
+    # against the visibility rule: entry s first becomes usable at the last position of
+    # its block, which starts m - 1 positions earlier
+    for mm in (4, 128):
+        for s_ in (0, 1, 7, 300):
+            p_first = next(p for p in range(mm * (s_ + 2)) if o.visible(p, mm, 10 ** 6) > s_)
+            assert o.entry_positions(mm, s_, 1)[0] == p_first - (mm - 1)
+    assert o.entry_positions(4, 3, 3).tolist() == [12, 16, 20]
 
 
 def check_rmsnorm(o):
@@ -710,6 +721,11 @@ def _gop_transposed_weight(O, Wg):
     return np.concatenate([X[:, gi * K_g:(gi + 1) * K_g] @ Wt[gi] for gi in range(g)], axis=1)
 
 
+def _entry_positions_block_end(m, entry0, N):
+    # the block's last raw position instead of its first
+    return m * (entry0 + np.arange(N)) + m - 1
+
+
 def _gop_plain(O, Wg):
     T = O.shape[0]
     X = O.reshape(T, -1)
@@ -740,6 +756,7 @@ MUTANTS = {
     "visibility_off_by_one": dict(visible=_visible_off_by_one),
     "window_excludes_query": dict(window_positions=_window_excl),
     "counts_round_up": dict(entry_counts=_counts_ceil),
+    "entry_position_block_end": dict(entry_positions=_entry_positions_block_end),
 }
 
 

@@ -169,7 +169,20 @@ class Workload:
         """Pool the blocks completed by the step's tokens into replica r's caches."""
         cfg, lib, prob = self.cfg, self.lib, self.prob
         B, c, n = cfg.B, cfg.c, self.n
-        for l in (self.layers if layers is None else layers):
+        layers = self.layers if layers is None else layers
+        if len(layers) == 2 and not self.nr:
+            # both caches in one call (one launch at decode)
+            sides = []
+            for l in ("csa", "hca"):
+                m = cfg.m if l == "csa" else cfg.m_hca
+                first_blk = self.n_old // m
+                tok0 = first_blk * m
+                C = self.rep[r][f"C_{l}"]
+                sides += [prob[f"X_{l}"][:, tok0:], prob[f"Z_{l}"][:, tok0:], C[:, first_blk:],
+                          n - tok0, m, n * c, (n // m) * c]
+            lib.csahca_compress_pair(*sides, B, c, cfg.dtype)
+            return
+        for l in layers:
             m = cfg.m if l == "csa" else cfg.m_hca
             first_blk = self.n_old // m          # first block not yet in the cache
             n_new = n // m - first_blk

@@ -23,6 +23,8 @@ _SZ = ctypes.c_size_t
 _SIGNATURES = {
     "csa_compress": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _LL, _LL, _P]),
     "hca_compress": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _LL, _LL, _P]),
+    "csahca_compress_pair": (_I, [_P, _P, _P, _I, _I, _LL, _LL, _P, _P, _P, _I, _I, _LL, _LL,
+                                  _I, _I, _I, _P]),
     "csa_compress_overlap": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _LL, _LL, _P]),
     "csahca_compress_norm_rope": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _LL, _I, _F, _F, _I,
                                        _LL, _LL, _P]),
@@ -129,6 +131,14 @@ def csa_compress_overlap(kv_a, gate_a, kv_b, gate_b, pos_bias, out, B, n, c, m, 
     return _check("csa_compress_overlap", load().csa_compress_overlap(
         _ptr(kv_a), _ptr(gate_a), _ptr(kv_b), _ptr(gate_b), _ptr(pos_bias), _ptr(out), B, n, c,
         m, prev, dtype, in_bstride, out_bstride, _stream(stream)))
+
+
+def csahca_compress_pair(kv_a, gate_a, out_a, n_a, m_a, in_bstride_a, out_bstride_a, kv_b, gate_b,
+                         out_b, n_b, m_b, in_bstride_b, out_bstride_b, B, c, dtype, stream=None):
+    return _check("csahca_compress_pair", load().csahca_compress_pair(
+        _ptr(kv_a), _ptr(gate_a), _ptr(out_a), n_a, m_a, in_bstride_a, out_bstride_a, _ptr(kv_b),
+        _ptr(gate_b), _ptr(out_b), n_b, m_b, in_bstride_b, out_bstride_b, B, c, dtype,
+        _stream(stream)))
 
 
 def csahca_compress_norm_rope(kv, gate, pos_bias, gamma, out, B, n, c, m, entry0, d_rope, eps,

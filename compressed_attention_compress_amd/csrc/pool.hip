@@ -151,18 +151,16 @@ CSAHCA_DEV void pool_append_run(const T* X, const T* Z, const AppendRows& ap, co
   }
 }
 
+// One thread per (sequence, entry, 8-channel slice); `bid` is the workgroup's index among
+// those of this pooling (a paired launch offsets it).
 template <typename T, int UB, bool HAS_P, int MODE, bool NR>
-__global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ X,
-                                                   const T* __restrict__ Z,
-                                                   const T* __restrict__ Xb,
-                                                   const T* __restrict__ Zb,
-                                                   const float* __restrict__ P,
-                                                   T* __restrict__ out, int N, int c, int m,
-                                                   int prev, long long in_bs, long long out_bs,
-                                                   long long total, NormRope nr, long long entry0,
-                                                   AppendRows ap) {
+CSAHCA_DEV void pool_items(const T* __restrict__ X, const T* __restrict__ Z,
+                           const T* __restrict__ Xb, const T* __restrict__ Zb,
+                           const float* __restrict__ P, T* __restrict__ out, int N, int c, int m,
+                           int prev, long long in_bs, long long out_bs, long long total,
+                           const NormRope& nr, long long entry0, const AppendRows& ap, int bid) {
   constexpr bool OV = MODE == TWO_STREAM;
-  const long long item = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long long item = (long long)bid * blockDim.x + threadIdx.x;
   if (item >= total) return;
   const int CV = c / VEC;
   int cv, i, b;
@@ -204,6 +202,20 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ X,
   Vec8<T>::store(out + (long long)b * out_bs + (long long)i * c + (long long)cv * VEC, res);
 }
 
+template <typename T, int UB, bool HAS_P, int MODE, bool NR>
+__global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ X,
+                                                   const T* __restrict__ Z,
+                                                   const T* __restrict__ Xb,
+                                                   const T* __restrict__ Zb,
+                                                   const float* __restrict__ P,
+                                                   T* __restrict__ out, int N, int c, int m,
+                                                   int prev, long long in_bs, long long out_bs,
+                                                   long long total, NormRope nr, long long entry0,
+                                                   AppendRows ap) {
+  pool_items<T, UB, HAS_P, MODE, NR>(X, Z, Xb, Zb, P, out, N, c, m, prev, in_bs, out_bs, total, nr,
+                                     entry0, ap, (int)blockIdx.x);
+}
+
 // Few blocks (a cache append at decode): the workgroups of one (sequence, block) split
 // its channels into groups of CVG 8-channel slices, and a workgroup's threads split the
 // block's tokens into S contiguous sub-ranges per slice, each with its own running
@@ -216,22 +228,19 @@ CSAHCA_DEV void store_one<uint16_t>(uint16_t* p, float v) { *p = f32_to_bf16(v);
 template <>
 CSAHCA_DEV void store_one<float>(float* p, float v) { *p = v; }
 
+// `bid` is the workgroup's index among those of this pooling (a paired launch offsets it);
+// the workgroup has exactly S * CVG threads.
 template <typename T, int UB, bool HAS_P, int MODE, bool NR>
-__global__ __launch_bounds__(NR ? 512 : 256) void pool_block_kernel(const T* __restrict__ X,
-                                                        const T* __restrict__ Z,
-                                                        const T* __restrict__ Xb,
-                                                        const T* __restrict__ Zb,
-                                                        const float* __restrict__ P,
-                                                        T* __restrict__ out, int N, int c,
-                                                        int m, int prev, int S, int CVG,
-                                                        long long in_bs, long long out_bs,
-                                                        NormRope nr, long long entry0,
-                                                        AppendRows ap) {
+CSAHCA_DEV void pool_block(const T* __restrict__ X, const T* __restrict__ Z,
+                           const T* __restrict__ Xb, const T* __restrict__ Zb,
+                           const float* __restrict__ P, T* __restrict__ out, int N, int c, int m,
+                           int prev, int S, int CVG, long long in_bs, long long out_bs,
+                           const NormRope& nr, long long entry0, const AppendRows& ap, int bid) {
   constexpr bool OV = MODE == TWO_STREAM;
   extern __shared__ float part[];  // [S][CVG][3][VEC], then (NR) [c] results + [16] sums
   const int CG = c / VEC / CVG;
   const int cvl = threadIdx.x % CVG, s = threadIdx.x / CVG;
-  const int cg = blockIdx.x % CG, bi = blockIdx.x / CG;
+  const int cg = bid % CG, bi = bid / CG;
   const int b = bi / N, i = bi - b * N;
   const int cv = cg * CVG + cvl;
   const int blk = OV ? i + prev : i;
@@ -314,6 +323,80 @@ __global__ __launch_bounds__(NR ? 512 : 256) void pool_block_kernel(const T* __r
       store_one<T>(orow + t, v);
     }
   }
+}
+
+template <typename T, int UB, bool HAS_P, int MODE, bool NR>
+__global__ __launch_bounds__(NR ? 512 : 256) void pool_block_kernel(const T* __restrict__ X,
+                                                        const T* __restrict__ Z,
+                                                        const T* __restrict__ Xb,
+                                                        const T* __restrict__ Zb,
+                                                        const float* __restrict__ P,
+                                                        T* __restrict__ out, int N, int c,
+                                                        int m, int prev, int S, int CVG,
+                                                        long long in_bs, long long out_bs,
+                                                        NormRope nr, long long entry0,
+                                                        AppendRows ap) {
+  pool_block<T, UB, HAS_P, MODE, NR>(X, Z, Xb, Zb, P, out, N, c, m, prev, S, CVG, in_bs, out_bs, nr,
+                                     entry0, ap, (int)blockIdx.x);
+}
+
+// Launch plan of a plain pooling (no bias, no norm) of N entries of m tokens: many entries
+// take pool_kernel (one thread per 8-channel slice of an entry); few entries of many tokens
+// take pool_block_kernel (the entry's tokens split over S sub-ranges per slice).
+struct PoolPlan {
+  bool block;   // pool_block_kernel
+  int ub;       // tokens per load round: 4 or 8
+  int S, CVG;   // block path: sub-ranges and slices per workgroup
+  unsigned grid, threads;
+  size_t lds;
+  long long total;
+};
+
+PoolPlan plan_plain(int B, long long N, int c, int m) {
+  PoolPlan p{};
+  p.total = (long long)B * N * (c / 8);
+  const int CV = c / VEC;
+  p.block = p.total < 32768 && m >= 8;
+  if (p.block) {
+    int CVG = 8;
+    while (CV % CVG != 0) CVG /= 2;
+    const int smax = 256 / CVG;
+    const int span = max(4, cdiv(m, smax));
+    p.S = cdiv(m, span);
+    p.CVG = CVG;
+    p.lds = (size_t)p.S * CVG * 3 * VEC * sizeof(float);
+    p.grid = (unsigned)(B * N * (CV / CVG));
+    p.threads = (unsigned)(p.S * CVG);
+    p.ub = (span % 8 == 0 && m % 8 == 0) ? 8 : 4;
+  } else {
+    p.grid = (unsigned)cdiv<long long>(p.total, 256);
+    p.threads = 256;
+    p.ub = m % 8 == 0 ? 8 : 4;
+  }
+  return p;
+}
+
+// One side of a paired pooling launch
+template <typename T>
+struct PoolSide {
+  const T *X, *Z;
+  T* out;
+  int N, c, m, S, CVG;
+  long long in_bs, out_bs, total;
+};
+
+// Two plain poolings in one launch: workgroups [0, gridA) run side A on pool_kernel's
+// layout, the rest run side B on pool_block_kernel's (256 threads each).
+template <typename T, int UBA, int UBB>
+__global__ __launch_bounds__(256) void pool_pair_kernel(PoolSide<T> A, PoolSide<T> Bs, int gridA,
+                                                        NormRope nr0, AppendRows ap0) {
+  if ((int)blockIdx.x < gridA)
+    pool_items<T, UBA, false, PLAIN, false>(A.X, A.Z, nullptr, nullptr, nullptr, A.out, A.N, A.c, A.m, 0,
+                                            A.in_bs, A.out_bs, A.total, nr0, 0, ap0, (int)blockIdx.x);
+  else
+    pool_block<T, UBB, false, PLAIN, false>(Bs.X, Bs.Z, nullptr, nullptr, nullptr, Bs.out, Bs.N, Bs.c,
+                                            Bs.m, 0, Bs.S, Bs.CVG, Bs.in_bs, Bs.out_bs, nr0, 0, ap0,
+                                            (int)blockIdx.x - gridA);
 }
 
 template <typename T, bool HAS_P, int MODE, bool NR>
@@ -402,11 +485,13 @@ void pick_pool(const PoolArgs& a, bool hp, int mode, bool nr) {
 
 namespace csahca {
 
-int pool_entry(const char* name, const void* kv, const void* gate, const void* kv_b,
-               const void* gate_b, bool ov, int prev, const float* pos_bias, void* out, int B,
-               int n, int c, int m, int dtype, long long in_bs, long long out_bs, void* stream,
-               const NormRope* nr, long long entry0) {
+// Argument checks of one pooling; *N_out receives the number of entries to emit (0: the
+// call has nothing to do and succeeds).
+int pool_check(const char* name, const void* kv, const void* gate, const void* kv_b,
+               const void* gate_b, bool ov, int prev, void* out, int B, int n, int c, int m,
+               int dtype, long long in_bs, long long out_bs, long long* N_out) {
   using namespace csahca;
+  *N_out = 0;
   if (B < 1 || n < 0 || c < 8 || (c % 8) != 0 || m < 1 || m > 4096) {
     set_error("%s: need B >= 1, n >= 0, c >= 8 with c %% 8 == 0, 1 <= m <= 4096", name);
     return CSAHCA_EINVAL;
@@ -420,10 +505,7 @@ int pool_entry(const char* name, const void* kv, const void* gate, const void* k
     return CSAHCA_ENOTSUP;
   }
   const long long N = n / m - prev;  // entries to emit
-  if (N <= 0) {  // no complete block to emit: nothing is read
-    clear_error();
-    return CSAHCA_OK;
-  }
+  if (N <= 0) return CSAHCA_OK;       // no complete block to emit: nothing is read
   if (!kv || !gate || !out || (ov && (!kv_b || !gate_b))) {
     set_error("%s: the KV, gate and out pointers must be non-NULL", name);
     return CSAHCA_EINVAL;
@@ -445,6 +527,22 @@ int pool_entry(const char* name, const void* kv, const void* gate, const void* k
     set_error("%s: problem too large for one launch", name);
     return CSAHCA_ENOTSUP;
   }
+  *N_out = N;
+  return CSAHCA_OK;
+}
+
+int pool_entry(const char* name, const void* kv, const void* gate, const void* kv_b,
+               const void* gate_b, bool ov, int prev, const float* pos_bias, void* out, int B,
+               int n, int c, int m, int dtype, long long in_bs, long long out_bs, void* stream,
+               const NormRope* nr, long long entry0) {
+  using namespace csahca;
+  long long N = 0;
+  int rc = pool_check(name, kv, gate, kv_b, gate_b, ov, prev, out, B, n, c, m, dtype, in_bs, out_bs, &N);
+  if (rc != CSAHCA_OK) return rc;
+  if (N == 0) {
+    clear_error();
+    return CSAHCA_OK;
+  }
   if (nr && (!norm_rope_args_ok(c, nr->d, nr->eps, nr->theta) || entry0 < 0 || !aligned16(nr->gamma))) {
     set_error("%s: the norm needs c / 8 a power of two <= 64, d_rope %% 8 == 0 and <= c, "
               "eps >= 0, theta > 0, entry0 >= 0 and gamma 16-byte aligned", name);
@@ -458,6 +556,65 @@ int pool_entry(const char* name, const void* kv, const void* gate, const void* k
   else
     pick_pool<float>(a, pos_bias != nullptr, ov ? TWO_STREAM : PLAIN, nr != nullptr);
   return launch_status(name);
+}
+
+// Two plain poolings of one layer pair (csa_compress and hca_compress arguments) in one
+// launch when one takes pool_kernel's layout and the other pool_block_kernel's at 256
+// threads; otherwise one launch each.  The entries are the same bits either way.
+int pool_pair(const void* kv_a, const void* gate_a, void* out_a, int n_a, int m_a, long long in_bs_a,
+              long long out_bs_a, const void* kv_b, const void* gate_b, void* out_b, int n_b, int m_b,
+              long long in_bs_b, long long out_bs_b, int B, int c, int dtype, void* stream) {
+  const char* name = "csahca_compress_pair";
+  long long NA = 0, NB = 0;
+  int rc = pool_check(name, kv_a, gate_a, nullptr, nullptr, false, 0, out_a, B, n_a, c, m_a, dtype,
+                      in_bs_a, out_bs_a, &NA);
+  if (rc != CSAHCA_OK) return rc;
+  rc = pool_check(name, kv_b, gate_b, nullptr, nullptr, false, 0, out_b, B, n_b, c, m_b, dtype, in_bs_b,
+                  out_bs_b, &NB);
+  if (rc != CSAHCA_OK) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  const PoolPlan pa = plan_plain(B, NA, c, m_a), pb = plan_plain(B, NB, c, m_b);
+  const bool swap = pa.block && !pb.block;  // side 1 takes pool_kernel's layout
+  const PoolPlan &p1 = swap ? pb : pa, &p2 = swap ? pa : pb;
+  if (NA > 0 && NB > 0 && !p1.block && p2.block && p2.threads == 256 &&
+      (long long)p1.grid + p2.grid <= 0x7FFFFFFFLL) {
+    const NormRope nr0{nullptr, 0.f, 1.f, 0, 0};
+    const AppendRows ap0{nullptr, nullptr, 1, 0, 0, 0};
+    auto go = [&](auto tag) {
+      using T = decltype(tag);
+      const PoolSide<T> sa{(const T*)kv_a, (const T*)gate_a, (T*)out_a, (int)NA, c, m_a,
+                           pa.S, pa.CVG, in_bs_a, out_bs_a, pa.total};
+      const PoolSide<T> sb{(const T*)kv_b, (const T*)gate_b, (T*)out_b, (int)NB, c, m_b,
+                           pb.S, pb.CVG, in_bs_b, out_bs_b, pb.total};
+      const PoolSide<T>& s1 = swap ? sb : sa;
+      const PoolSide<T>& s2 = swap ? sa : sb;
+      const dim3 grid(p1.grid + p2.grid);
+      const int g1 = (int)p1.grid;
+      if (p1.ub == 8 && p2.ub == 8)
+        hipLaunchKernelGGL((pool_pair_kernel<T, 8, 8>), grid, dim3(256), p2.lds, st, s1, s2, g1, nr0, ap0);
+      else if (p1.ub == 8)
+        hipLaunchKernelGGL((pool_pair_kernel<T, 8, 4>), grid, dim3(256), p2.lds, st, s1, s2, g1, nr0, ap0);
+      else if (p2.ub == 8)
+        hipLaunchKernelGGL((pool_pair_kernel<T, 4, 8>), grid, dim3(256), p2.lds, st, s1, s2, g1, nr0, ap0);
+      else
+        hipLaunchKernelGGL((pool_pair_kernel<T, 4, 4>), grid, dim3(256), p2.lds, st, s1, s2, g1, nr0, ap0);
+    };
+    if (dtype == CSAHCA_BF16)
+      go(uint16_t{});
+    else
+      go(float{});
+    return launch_status(name);
+  }
+  if (NA > 0) {
+    rc = pool_entry(name, kv_a, gate_a, nullptr, nullptr, false, 0, nullptr, out_a, B, n_a, c, m_a, dtype,
+                    in_bs_a, out_bs_a, stream);
+    if (rc != CSAHCA_OK) return rc;
+  }
+  if (NB > 0)
+    return pool_entry(name, kv_b, gate_b, nullptr, nullptr, false, 0, nullptr, out_b, B, n_b, c, m_b, dtype,
+                      in_bs_b, out_bs_b, stream);
+  clear_error();
+  return CSAHCA_OK;
 }
 
 int pool_append(const char* name, const void* kv_new, const void* gate_new, const void* ring_x,
@@ -491,6 +648,15 @@ extern "C" int csa_compress(const void* kv, const void* gate, const float* pos_b
                             long long out_bstride, void* stream) {
   return pool_entry("csa_compress", kv, gate, nullptr, nullptr, false, 0, pos_bias, out, B, n, c,
                     m, dtype, in_bstride, out_bstride, stream, nullptr, 0);
+}
+
+extern "C" int csahca_compress_pair(const void* kv_a, const void* gate_a, void* out_a, int n_a,
+                                    int m_a, long long in_bstride_a, long long out_bstride_a,
+                                    const void* kv_b, const void* gate_b, void* out_b, int n_b,
+                                    int m_b, long long in_bstride_b, long long out_bstride_b, int B,
+                                    int c, int dtype, void* stream) {
+  return csahca::pool_pair(kv_a, gate_a, out_a, n_a, m_a, in_bstride_a, out_bstride_a, kv_b, gate_b, out_b,
+                           n_b, m_b, in_bstride_b, out_bstride_b, B, c, dtype, stream);
 }
 
 extern "C" int hca_compress(const void* kv, const void* gate, const float* pos_bias, void* out,

@@ -97,6 +97,27 @@ int hca_compress(const void* kv, const void* gate, const float* pos_bias, void* 
                  void* stream);
 
 /*
+ * csahca_compress_pair -- the CSA and the HCA pooling of one layer pair (for instance the
+ * blocks a decode step completes in both caches) in one launch.
+ * Source: as csa_compress and hca_compress (the same per-block definition, run for two
+ * caches); "DeepSeek-V4 Architecture From Kernels ... C-Kernel-Engine", section 9 (an entry
+ * is made in each cache whenever a block of its size completes).
+ * Side a and side b each take the arguments of csa_compress / hca_compress without the
+ * bias: kv_x, gate_x [B, n_x, c] (batch stride in_bstride_x elements), out_x [B, n_x / m_x, c]
+ * (batch stride out_bstride_x), sharing B, c and dtype.  Every argument rule of those
+ * calls applies to both sides; a side with no complete block emits nothing.  The entries
+ * are bit-identical to the two separate calls.  When one side has few entries of many
+ * tokens and the other does not, both run in one kernel launch (the layout of a decode
+ * step); otherwise the two poolings are enqueued one after the other.  Errors are checked
+ * for both sides before anything is enqueued.
+ */
+int csahca_compress_pair(const void* kv_a, const void* gate_a, void* out_a, int n_a, int m_a,
+                         long long in_bstride_a, long long out_bstride_a, const void* kv_b,
+                         const void* gate_b, void* out_b, int n_b, int m_b,
+                         long long in_bstride_b, long long out_bstride_b, int B, int c,
+                         int dtype, void* stream);
+
+/*
  * csa_compress_overlap -- the overlapped two-stream CSA compressor.
  * Source: "DeepSeek-V4 Hybrid Attention: CSA, HCA, mHC, MoE", section V.1 (two KV
  * streams a and b with their own compression scores; entry i combines stream a's block i

@@ -52,6 +52,19 @@ def test_pool_validation():
     assert L.csa_compress(FAKE, FAKE, None, FAKE, 1, 8, 8, 0, 1, 64, 16, None) == EINVAL   # m
     # fewer tokens than one block: nothing to do, pointers may be NULL
     assert L.csa_compress(None, None, None, None, 1, 3, 8, 4, 1, 24, 0, None) == 0
+    # the pair: either side's error is reported (nothing enqueued); both sides empty is a no-op
+    pr = L.csahca_compress_pair
+    assert pr(FAKE, FAKE, FAKE, 8, 4, 64, 16, None, FAKE, FAKE, 256, 128, 2048, 16, 1, 8, 1,
+              None) == EINVAL
+    assert "non-NULL" in lib.last_error()
+    assert pr(FAKE, FAKE, FAKE, 8, 4, 32, 16, FAKE, FAKE, FAKE, 256, 128, 2048, 16, 1, 8, 1,
+              None) == EINVAL  # side a stride
+    assert pr(FAKE, FAKE, FAKE, 8, 4, 64, 16, FAKE, FAKE, FAKE, 256, 0, 2048, 16, 1, 8, 1,
+              None) == EINVAL  # side b m
+    assert pr(FAKE, FAKE, FAKE, 8, 4, 64, 16, FAKE, FAKE, FAKE, 256, 128, 2048, 16, 1, 8, 2,
+              None) == ENOTSUP  # dtype
+    assert pr(None, None, None, 3, 4, 24, 0, None, None, None, 100, 128, 800, 0, 1, 8, 1,
+              None) == 0
     # overlapped form: prev is 0 or 1, stream b pointers are required, an append of one
     # block with prev = 1 emits nothing
     ov = L.csa_compress_overlap

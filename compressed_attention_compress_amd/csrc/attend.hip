@@ -757,6 +757,79 @@ __global__ __launch_bounds__(256) void attend_combine(const uint16_t* __restrict
   if (lse && lane == 0) lse[qrow * n_h + h] = Lt > 0.f ? (M + __log2f(Lt)) * LN2 : -INFINITY;
 }
 
+constexpr int COMBINE_WAVE_SPLITS = 16;
+
+// Merge of up to COMBINE_WAVE_SPLITS splits (one load round; more take attend_combine):
+// every (query, head) by the log-sum-exp of its splits.  One wave per pair, four
+// pairs per workgroup.  Lane l loads the record (m, l, 2^e) of split l (of splits 64j + l
+// beyond 64); the partial rows are loaded 16 splits at a time, each lane holding 8
+// columns of every row, the first 16 issued together with the records.  The records
+// reach every lane by readlane, so no LDS and no barrier are needed, and the splits are
+// added in index order.  A split's partial row holds its output normalised by its own
+// sum l_s and scaled by 2^-e_s (float16); its weight in the merge is l_s * 2^(m_s - M) *
+// 2^e_s, M the largest running maximum.
+__global__ __launch_bounds__(256) void attend_combine_wave(const uint16_t* __restrict__ opart,
+                                                           const float* __restrict__ mlpart,
+                                                           uint16_t* __restrict__ out,
+                                                           float* __restrict__ lse,
+                                                           const float* __restrict__ sink, int n_h,
+                                                           int n_splits, long long n_pairs) {
+  constexpr int CH = COMBINE_WAVE_SPLITS;  // partial rows in flight per lane
+  const int lane = threadIdx.x & 63;
+  const long long pair = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (pair >= n_pairs) return;  // whole waves; no barrier follows
+  const long long qrow = pair / n_h;
+  const int h = (int)(pair - qrow * n_h);
+  const long long pr0 = qrow * n_splits * n_h + h;  // partial row of split s: pr0 + s*n_h
+  auto rec_of = [&](int s) {
+    return s < n_splits ? *reinterpret_cast<const f32x4*>(mlpart + (pr0 + (long long)s * n_h) * 4)
+                        : f32x4{-INFINITY, 0.f, 0.f, 0.f};
+  };
+  auto row_of = [&](int s) {
+    return s < n_splits ? *reinterpret_cast<const u32x4*>(opart + (pr0 + (long long)s * n_h) * C + lane * 8)
+                        : u32x4{0u, 0u, 0u, 0u};
+  };
+  f32x4 rec = rec_of(lane);
+  u32x4 x[CH];
+#pragma unroll
+  for (int u = 0; u < CH; ++u) x[u] = row_of(u);
+  float M = rec[0];
+  for (int s = lane + 64; s < n_splits; s += 64) M = fmaxf(M, rec_of(s)[0]);
+  for (int d = 1; d < 64; d <<= 1) M = fmaxf(M, shfl_xor_f(M, d));
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float Ls = 0.f;
+  for (int s0 = 0; s0 < n_splits; s0 += CH) {
+    if (s0 > 0) {
+      if ((s0 & 63) == 0) rec = rec_of(s0 + lane);
+#pragma unroll
+      for (int u = 0; u < CH; ++u) x[u] = row_of(s0 + u);
+    }
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      const int sl = (s0 + u) & 63;  // the lane holding split s0 + u's record
+      const float ms = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rec[0]), sl));
+      const float ls = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rec[1]), sl));
+      const float es = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rec[2]), sl));
+      const float w = ms == -INFINITY ? 0.f : ls * exp2f(ms - M);  // 0 past the last split
+      Ls += w;
+      const float wgt = w * es;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] = fmaf(wgt, f16_lo(x[u][i]), acc[2 * i]);
+        acc[2 * i + 1] = fmaf(wgt, f16_hi(x[u][i]), acc[2 * i + 1]);
+      }
+    }
+  }
+  float Lt = Ls;
+  const float rs = fold_sink(sink, h, M, Lt);
+  const float inv = Lt > 0.f ? rs / Lt : 0.f;
+  u32x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i] * inv, acc[2 * i + 1] * inv);
+  *reinterpret_cast<u32x4*>(out + (qrow * n_h + h) * C + lane * 8) = o;
+  if (lse && lane == 0) lse[qrow * n_h + h] = Lt > 0.f ? (M + __log2f(Lt)) * LN2 : -INFINITY;
+}
+
 // ---------------------------------------------------------------------------------------
 // float32 path (c <= 256): one workgroup per query, scores held in LDS
 // ---------------------------------------------------------------------------------------
@@ -1055,8 +1128,13 @@ int attend_impl(const char* name, bool csa, const void* q, const void* ckv, cons
   int rc = launch_status(name);
   if (rc != CSAHCA_OK || P.n_splits == 1) return rc;
   const long long nqh = (long long)B * Tq * n_h;
-  hipLaunchKernelGGL(attend_combine, dim3((unsigned)nqh), dim3(256), 0, st, A.opart, A.mlpart,
-                     A.out, lse, sink, n_h, P.n_splits);
+  // few splits: one wave per pair loads them all at once; many: four waves per pair
+  if (P.n_splits <= COMBINE_WAVE_SPLITS)
+    hipLaunchKernelGGL(attend_combine_wave, dim3((unsigned)cdiv<long long>(nqh, 4)), dim3(256), 0, st,
+                       A.opart, A.mlpart, A.out, lse, sink, n_h, P.n_splits, nqh);
+  else
+    hipLaunchKernelGGL(attend_combine, dim3((unsigned)nqh), dim3(256), 0, st, A.opart, A.mlpart, A.out,
+                       lse, sink, n_h, P.n_splits);
   return launch_status(name);
 }
 

@@ -1031,7 +1031,7 @@ def main():
         dur = e0.elapsed_time(e1) / 1e3 / (rounds * reps)
         kb = detail["hca_attend"]
         ach = kb / dur / 1e9
-        roofline = {"kernel": "hca_attend (attend_bf16 + attend_combine)", "bound": "hbm",
+        roofline = {"kernel": "hca_attend (attend_bf16 + split merge)", "bound": "hbm",
                     "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
                     "avg_launch_us": round(dur * 1e6, 2), "bytes_per_launch": kb}

@@ -51,6 +51,22 @@ CSAHCA_DEV float fold_sink(const float* sink, int h, float& m, float& l) {
   return r;
 }
 
+// The same for a head that keeps two sums over one maximum: l, the mass of its fp32
+// weights (for the log-sum-exp), and lq, the sum of the bf16-rounded weights the output
+// was accumulated with (for normalising the output).
+CSAHCA_DEV float fold_sink2(const float* sink, int h, float& m, float& l, float& lq) {
+  if (!sink) return 1.f;
+  const float s2 = sink[h] * LOG2E;
+  if (s2 == -INFINITY) return 1.f;
+  const float M = fmaxf(m, s2);
+  const float r = m == -INFINITY ? 0.f : exp2f(m - M);
+  const float e = exp2f(s2 - M);
+  l = l * r + e;
+  lq = lq * r + e;
+  m = M;
+  return r;
+}
+
 struct AttnArgs {
   const uint16_t* q;
   const uint16_t* ckv;
@@ -116,9 +132,10 @@ CSAHCA_DEV void wait_tiles(int inflight) {
 // workgroups (one workgroup per CU keeps three tiles in flight: decode).
 // Column-split workgroups (CS) add an exchange area: P^T operands [TPI][NW][64 lanes]
 // (16 bytes each), the per-head factors alpha [NW][16], one flag per wave, and at the end
-// the running maxima and sums [NW][16] and partial row maxima [NW][NW * 16].
+// the running maxima and sums [NW][16], partial row maxima [NW][NW * 16] and the sums of
+// the rounded weights [NW][16].
 constexpr size_t xch_bytes(int NW, int TPI) {
-  return (size_t)TPI * NW * 64 * 16 + (size_t)NW * 16 * 4 + 64 + 2 * (size_t)NW * 16 * 4 +
+  return (size_t)TPI * NW * 64 * 16 + (size_t)NW * 16 * 4 + 64 + 3 * (size_t)NW * 16 * 4 +
          (size_t)NW * NW * 16 * 4;
 }
 
@@ -347,7 +364,9 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && NS == 2) ? 2 : 1) void attend_
   for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(qf[ks]));
   for (int tt = TPI; tt < NS && tt < ntile; ++tt) issue(tt, false);
 
-  float m_run = -INFINITY, l_run = 0.f;
+  // l_run: mass of the fp32 weights (log-sum-exp, split records); lq_run: sum of the same
+  // weights rounded to bf16, as they enter the PV product (normalises the output)
+  float m_run = -INFINITY, l_run = 0.f, lq_run = 0.f;
   // O^T accumulators: without CS oacc[cb][i] is column 16*cb + 4*g + i of head
   // h0 + row16; with CS oacc[cbl*NW + hb][i] is column 16*(wave*32/NW + cbl) + 4*g + i of
   // head hg*HPW + 16*hb + row16
@@ -480,16 +499,28 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && NS == 2) ? 2 : 1) void attend_
         for (int e = 0; e < w; ++e) ps[e] += ps[e + w];
       const float psum = sum_over_row_groups(ps[0]);
       l_run = l_run * alpha + psum;
+      // the weights enter O^T += E^T P^T as bf16; their rounded sum normalises the output,
+      // which is then an exact convex combination of its rows (a query with a single
+      // usable row returns that row's bits)
+#pragma unroll
+      for (int e = 0; e < NSV; ++e) pe[e] = round_bf16(pe[e]);
+#pragma unroll
+      for (int e = 0; e < NSV / 2; ++e) ps[e] = pe[e] + pe[e + NSV / 2];
+#pragma unroll
+      for (int w = NSV / 4; w >= 1; w >>= 1)
+#pragma unroll
+        for (int e = 0; e < w; ++e) ps[e] += ps[e + w];
+      lq_run = lq_run * alpha + sum_over_row_groups(ps[0]);
       m_run = m_new;
       // P^T as B operands: k-slot e <-> slot (e < 4 ? 4g+e : 16+4g+e-4) of its tile
-      const bf16x8 pfA = __builtin_bit_cast(bf16x8, u32x4{pack_bf16x2(pe[0], pe[1]), pack_bf16x2(pe[2], pe[3]),
-                                                          pack_bf16x2(pe[4], pe[5]), pack_bf16x2(pe[6], pe[7])});
+      const bf16x8 pfA = __builtin_bit_cast(bf16x8, u32x4{pack_rounded_bf16x2(pe[0], pe[1]), pack_rounded_bf16x2(pe[2], pe[3]),
+                                                          pack_rounded_bf16x2(pe[4], pe[5]), pack_rounded_bf16x2(pe[6], pe[7])});
       bf16x8 pfB;
       if (TPI == 2)
-        pfB = __builtin_bit_cast(bf16x8, u32x4{pack_bf16x2(pe[8 % NSV], pe[9 % NSV]),
-                                               pack_bf16x2(pe[10 % NSV], pe[11 % NSV]),
-                                               pack_bf16x2(pe[12 % NSV], pe[13 % NSV]),
-                                               pack_bf16x2(pe[14 % NSV], pe[15 % NSV])});
+        pfB = __builtin_bit_cast(bf16x8, u32x4{pack_rounded_bf16x2(pe[8 % NSV], pe[9 % NSV]),
+                                               pack_rounded_bf16x2(pe[10 % NSV], pe[11 % NSV]),
+                                               pack_rounded_bf16x2(pe[12 % NSV], pe[13 % NSV]),
+                                               pack_rounded_bf16x2(pe[14 % NSV], pe[15 % NSV])});
       // ---- O^T += E^T P^T: E^T through LDS transpose reads, issued in asm ahead of use ----
       // ds_read_b64_tr_b16: in each 16-lane group, lane i receives column i%4 of the four
       // 4-element rows addressed by lanes i/4, i/4+4, i/4+8, i/4+12.  Lane j addresses row
@@ -563,9 +594,11 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && NS == 2) ? 2 : 1) void attend_
     float* xm = reinterpret_cast<float*>(xch + TPI * NW * 1024 + NW * 16 * 4 + 64);  // [NW][16]
     float* xl = xm + NW * 16;                                                       // [NW][16]
     float* xam = xl + NW * 16;  // [NW][NW*16]: |O| maxima over a wave's columns, per head
+    float* xlq = xam + NW * NW * 16;  // [NW][16]
     if (g == 0) {
       xm[wave * 16 + row16] = m_run;
       xl[wave * 16 + row16] = l_run;
+      xlq[wave * 16 + row16] = lq_run;
     }
 #pragma unroll
     for (int hb = 0; hb < NW; ++hb) {
@@ -582,11 +615,11 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && NS == 2) ? 2 : 1) void attend_
     // every head block's values of this wave's columns, as 16-bit rows [head][column]
 #pragma unroll
     for (int hb = 0; hb < NW; ++hb) {
-      float lh = xl[hb * 16 + row16], mh = xm[hb * 16 + row16];
+      float lh = xl[hb * 16 + row16], mh = xm[hb * 16 + row16], lqh = xlq[hb * 16 + row16];
       const bool as_f16 = a.n_splits > 1;
       // one split: the sink joins here (with splits, in the merge)
-      const float rs = as_f16 ? 1.f : fold_sink(a.sink, hg * a.HPW + 16 * hb + row16, mh, lh);
-      const float inv = lh > 0.f ? rs / lh : 0.f;
+      const float rs = as_f16 ? 1.f : fold_sink2(a.sink, hg * a.HPW + 16 * hb + row16, mh, lh, lqh);
+      const float inv = lqh > 0.f ? rs / lqh : 0.f;
       float f = inv;
       if (as_f16) {  // partial O / l scaled by 2^-e per row (see the merge)
         float amax = 0.f;
@@ -633,9 +666,9 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && NS == 2) ? 2 : 1) void attend_
   uint16_t* dst;        // the wave's first output row
   bool as_f16;
   if (a.n_splits == 1) {
-    float mm = m_run, ll = l_run;
-    const float rs = fold_sink(a.sink, h, mm, ll);
-    f = ll > 0.f ? rs / ll : 0.f;
+    float mm = m_run, ll = l_run, lq = lq_run;
+    const float rs = fold_sink2(a.sink, h, mm, ll, lq);
+    f = lq > 0.f ? rs / lq : 0.f;
     dst = a.out + (qrow * a.n_h + h0) * C;
     as_f16 = false;
     if (a.lse && g == 0) a.lse[qrow * a.n_h + h] = ll > 0.f ? (mm + __log2f(ll)) * LN2 : -INFINITY;
@@ -645,7 +678,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && NS == 2) ? 2 : 1) void attend_
     // keeps float16's 11-bit precision relative to the row's largest.  The record (m, l,
     // 2^e) lets the merge weigh the row by l * 2^(m - M) * 2^e.
     const long long pr0 = (qrow * a.n_splits + split) * a.n_h + h0;
-    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    const float inv = lq_run > 0.f ? 1.f / lq_run : 0.f;
     float amax = 0.f;
 #pragma unroll
     for (int cb = 0; cb < C / 16; ++cb)
@@ -688,8 +721,9 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && NS == 2) ? 2 : 1) void attend_
 // Merge the splits of every (query, head) by their log-sum-exp.  One workgroup per pair:
 // wave w takes the splits w, w+4, ..., eight partial rows in flight per lane (8 columns
 // each); the four wave sums are then added in a fixed order.  A split's partial row holds
-// its output normalised by its own sum l_s and scaled by 2^-e_s (float16); its weight in
-// the merge is l_s * 2^(m_s - M) * 2^e_s, M the largest running maximum.
+// its output normalised by the sum of its own (bf16-rounded) weights and scaled by 2^-e_s
+// (float16); its weight in the merge is l_s * 2^(m_s - M) * 2^e_s, with l_s the mass of
+// its fp32 weights and M the largest running maximum.
 __global__ __launch_bounds__(256) void attend_combine(const uint16_t* __restrict__ opart,
                                                       const float* __restrict__ mlpart,
                                                       uint16_t* __restrict__ out,
@@ -765,9 +799,10 @@ constexpr int COMBINE_WAVE_SPLITS = 16;
 // beyond 64); the partial rows are loaded 16 splits at a time, each lane holding 8
 // columns of every row, the first 16 issued together with the records.  The records
 // reach every lane by readlane, so no LDS and no barrier are needed, and the splits are
-// added in index order.  A split's partial row holds its output normalised by its own
-// sum l_s and scaled by 2^-e_s (float16); its weight in the merge is l_s * 2^(m_s - M) *
-// 2^e_s, M the largest running maximum.
+// added in index order.  A split's partial row holds its output normalised by the sum of
+// its own (bf16-rounded) weights and scaled by 2^-e_s (float16); its weight in the merge
+// is l_s * 2^(m_s - M) * 2^e_s, with l_s the mass of its fp32 weights and M the largest
+// running maximum.
 __global__ __launch_bounds__(256) void attend_combine_wave(const uint16_t* __restrict__ opart,
                                                            const float* __restrict__ mlpart,
                                                            uint16_t* __restrict__ out,

@@ -62,6 +62,18 @@ CSAHCA_DEV uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
 }
 
+// the float value of f rounded to bf16 (nearest even; f finite): low 16 bits cleared
+CSAHCA_DEV float round_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return __uint_as_float(u & 0xFFFF0000u);
+}
+
+// two values already rounded to bf16 (round_bf16), packed without another rounding
+CSAHCA_DEV uint32_t pack_rounded_bf16x2(float lo, float hi) {
+  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+}
+
 // float16, round to nearest even (the hardware conversion); two halves in one word
 CSAHCA_DEV uint32_t pack_f16x2(float lo, float hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |

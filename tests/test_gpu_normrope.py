@@ -190,10 +190,13 @@ def test_overlap_pool_norm_rope(m, B, n, prev):
 
 def test_chain_attention_over_normalised_rotated_rows():
     """Everything on the GPU (entries pooled with the norm and rotation fused, queries and
-    window rows through csahca_norm_rope, then hca_attend) against the oracle all the way.
-    The GPU stores the normalised queries, entries, window rows and the output in bf16
-    (2^-9 relative each), which the oracle does not, so the bound is the attention
-    tolerance 2e-2 RMS(O_ref) plus 2^-7 |O_ref| elementwise."""
+    window rows through csahca_norm_rope, then hca_attend), checked stage by stage as the
+    rest of the suite is: the normalised, rotated entries, window rows and queries the GPU
+    stored against the oracle at the row and pooling tolerances, then the attention over
+    exactly those stored bf16 rows at 2e-2 x RMS(O_ref) plus the output's own bf16
+    rounding (half an ulp of O_ref; see below).  The oracle-all-the-way error
+    (fp64 rows, no bf16 storage) is printed beside it: when a head's softmax is peaked its
+    output is close to one row, so it inherits that row's bf16 rounding (2^-9 |v|)."""
     rng = np.random.default_rng(31)
     B, c, m, W, n_h, d = 2, 512, 4, 32, 16, 64
     n = 4 * 96 + 2                                 # decode at position n - 1
@@ -219,14 +222,31 @@ def test_chain_attention_over_normalised_rotated_rows():
     out, _ = H.run_hca_attend(dQ, C, win, win_pos, q_pos, m, W, BF16, scale=1.0 / np.sqrt(c))
     torch.cuda.synchronize()
     got = oracle.decode(H.to_host_codes(out, BF16), BF16)
+    Cg = oracle.decode(H.to_host_codes(C, BF16), BF16)
+    Wg = oracle.decode(H.to_host_codes(win, BF16), BF16)
+    Qg = oracle.decode(H.to_host_codes(dQ, BF16), BF16)
     Xd, Zd, Qd = oracle.decode(X, BF16), oracle.decode(Z, BF16), oracle.decode(Q, BF16)
     for b in range(B):
-        Cr = oracle.norm_rope(oracle.pool(Xd[b], Zd[b], m), oracle.entry_positions(m, 0, N), gk, EPS,
-                              d, THETA)
-        Wr = oracle.norm_rope(Xd[b, wp:], np.arange(wp, n), gk, EPS, d, THETA)
-        qr = oracle.norm_rope(Qd[b, 0], np.full(n_h, n - 1), gq, EPS, d, THETA)
-        rows = oracle.hca_rows(Cr, m, Wr, wp, n - 1, W)
-        ref, _ = oracle.attend(qr, rows, 1.0 / np.sqrt(c))
+        # stage 1: the stored normalised, rotated rows against the oracle
+        Cr, xn, kc = pooled_reference(Xd[b], Zd[b], m, None, gk, d, 0)
+        check_pooled(Cg[b], Cr, xn, kc, d, BF16)
+        wn = oracle.rmsnorm(Xd[b, wp:], gk, EPS)
+        Wr = oracle.rope_tail(wn, np.arange(wp, n), d, THETA)
+        assert not (np.abs(Wg[b] - Wr) > rows_tol(wn, Wr, d, BF16)).any(), "window rows"
+        qn = oracle.rmsnorm(Qd[b, 0], gq, EPS)
+        qr = oracle.rope_tail(qn, np.full(n_h, n - 1), d, THETA)
+        assert not (np.abs(Qg[b, 0] - qr) > rows_tol(qn, qr, d, BF16)).any(), "queries"
+        # stage 2: attention over the rows the GPU consumed.  The bound is 2e-2 x RMS(O_ref)
+        # plus the half-ulp rounding of the stored bf16 output: here the output's largest
+        # value (1.58 in sequence 0) is 8.9x its RMS, so that rounding alone (2^-8 = 0.0039)
+        # is 1.10x of 2e-2 x RMS (0.0035) and no bf16 output could meet the bare bound.
+        ref, _ = oracle.attend(Qg[b, 0], oracle.hca_rows(Cg[b], m, Wg[b], wp, n - 1, W), 1.0 / np.sqrt(c))
         err = np.abs(got[b, 0] - ref)
-        tol = 2e-2 * np.sqrt((ref ** 2).mean()) + 2.0 ** -7 * np.abs(ref)
-        assert (err <= tol).all(), err.max()
+        rms_tol = 2e-2 * np.sqrt((ref ** 2).mean())
+        excess = err - 0.5 * bf16_ulp(ref)       # what is left after the output's own rounding
+        # oracle all the way, for the record
+        full, _ = oracle.attend(qr, oracle.hca_rows(Cr, m, Wr, wp, n - 1, W), 1.0 / np.sqrt(c))
+        print(f"chain seq {b}: max |d| = {err.max():.3g} ({err.max() / rms_tol:.3f} of 2e-2 x RMS), "
+              f"beyond the output's half-ulp {excess.max() / rms_tol:.3f} of 2e-2 x RMS; "
+              f"against fp64 rows throughout {np.abs(got[b, 0] - full).max():.3g}", flush=True)
+        assert excess.max() <= rms_tol, err.max()

@@ -5,10 +5,12 @@ the GPU-written compressed cache and the GPU's top-k list, the top-k check uses 
 GPU's own fp32 scores.  Tolerances:
   pooling    fp32: max |d| <= 1e-5; bf16: |d| <= one bf16 ulp of the fp64 value
              + 2^-16 * sum_j S_j |x_j| (fp32 rounding of the weighted sum)
-  indexer    |d| <= 1e-3 * max(|ref|, RMS of the query's scores)
+  indexer    |d| <= 1e-3 * |ref| + 1e-6 * RMS of the query's scores (the absolute floor
+             only matters for ReLU zeros and exact-zero weights)
   top-k      bit-exact index lists (ascending, -1 padded) given the GPU scores
-  attention  fp32: max |d| <= 1e-5; bf16: max |d| <= 2e-2 * RMS of the call's output, or
-             for a query with few rows the bf16 rounding bound 2^-7 (|O| + sum_r p_r |v_r|)
+  attention  fp32: max |d| <= 1e-5; bf16: max |d| <= 2e-2 * RMS of the call's output; a
+             query with at most 16 rows is held to 2e-2 * the larger of that and the RMS of
+             its own output (see check_attend)
 """
 import math
 
@@ -57,6 +59,12 @@ def decode_keys(prob):
     return oracle.decode(prob["qI"], cfg.idx_dtype), oracle.decode(prob["KI"], cfg.idx_dtype)
 
 
+def index_tol(ref):
+    """1e-3 relative, with an absolute floor of 1e-6 x the row's RMS for zero scores."""
+    rms = math.sqrt(float(np.mean(ref * ref))) if ref.size else 0.0
+    return 1e-3 * np.abs(ref) + 1e-6 * rms
+
+
 def check_index(prob, q_pos, k, idx, sc, alls):
     cfg = prob["cfg"]
     qI, KI = decode_keys(prob)
@@ -66,6 +74,7 @@ def check_index(prob, q_pos, k, idx, sc, alls):
     alls = alls.cpu().numpy()
     B, Tq = qI.shape[:2]
     N_c = KI.shape[1]
+    worst = 0.0
     for b in range(B):
         for t in range(Tq):
             p = int(q_pos[b]) + t
@@ -73,43 +82,60 @@ def check_index(prob, q_pos, k, idx, sc, alls):
             ref = oracle.index_scores(qI[b, t], w[b, t], KI[b], V)
             g = alls[b, t, :V].astype(np.float64)
             if V:
-                rms = math.sqrt(float(np.mean(ref * ref)))
-                tol = 1e-3 * np.maximum(np.abs(ref), rms)
-                assert np.all(np.abs(g - ref) <= tol), f"scores b={b} t={t}"
+                d = np.abs(g - ref)
+                tol = index_tol(ref)
+                worst = max(worst, float(np.max(d / np.maximum(tol, 1e-300))))
+                assert np.all(d <= tol), f"scores b={b} t={t}: worst {np.max(d / tol):.3g} of the tolerance"
             want = oracle.topk(g, k)
             assert np.array_equal(idx[b, t], want), f"top-k b={b} t={t}"
             keff = min(k, V)
             assert np.array_equal(sc[b, t, :keff], alls[b, t, want[:keff]])
             assert np.all(np.isneginf(sc[b, t, keff:]))
+    print(f"indexer scores: worst |d| = {worst:.3f} of the tolerance", flush=True)
 
 
-def check_attend(Qc, dtype, rows_fn, gpu_out, gpu_lse, scale, sink=None):
-    """rows_fn(b, t) -> fp64 row set for that query (from the GPU-consumed bytes)."""
+FEW_ROWS = 16  # queries attending to at most this many rows take their own output's RMS
+
+
+def check_attend(Qc, dtype, rows_fn, gpu_out, gpu_lse, scale, sink=None, label=""):
+    """rows_fn(b, t) -> fp64 row set for that query (from the GPU-consumed bytes).
+
+    bf16: max |d| <= 2e-2 x RMS of the call's whole output.  A query with at most
+    FEW_ROWS rows is instead held to 2e-2 x the larger of that RMS and the RMS of its own
+    output: its output is close to a single row, up to 10x the call's RMS when the call
+    also holds many-row queries, and the bf16 storage of such a value (half an ulp,
+    2^-9 relative) alone exceeds 2e-2 x the call's RMS."""
     Q = oracle.decode(Qc, dtype)
     B, Tq = Q.shape[:2]
     got = oracle.decode(H.to_host_codes(gpu_out, dtype), dtype)
     lse = gpu_lse.cpu().numpy().astype(np.float64)
     ref = np.zeros_like(got)
-    ref_abs = np.zeros_like(got)
     ref_lse = np.zeros(lse.shape)
+    nrows = np.zeros((B, Tq), dtype=np.int64)
     for b in range(B):
         for t in range(Tq):
             rows = rows_fn(b, t)
+            nrows[b, t] = rows.shape[0]
             ref[b, t], ref_lse[b, t] = oracle.attend(Q[b, t], rows, scale, sink)
-            if dtype != F32 and rows.shape[0]:
-                # the same softmax weights applied to |rows|: scale of the bf16 rounding of P
-                wts = np.exp(scale * Q[b, t] @ rows.T - ref_lse[b, t][:, None])
-                ref_abs[b, t] = wts @ np.abs(rows)
     err = np.abs(got - ref)
     if dtype == F32:
+        print(f"attention {label}: max |d| = {err.max():.3g} (tolerance 1e-5)", flush=True)
         assert err.max() <= 1e-5, f"attention max |d| = {err.max()}"
         assert np.max(np.abs(lse - ref_lse)) <= 1e-5
     else:
         rms = math.sqrt(float(np.mean(ref * ref)))
-        # 2e-2 x output RMS; for queries with only a few rows (the first tokens of a
-        # sequence) the bf16 rounding of P and O bounds the error by 2^-8 (|O| + sum p|v|)
-        tol = np.maximum(2e-2 * rms, 2.0 ** -7 * (np.abs(ref) + ref_abs))
-        assert np.all(err <= tol), f"attention max |d| = {err.max()}, RMS = {rms}"
+        tol = np.full((B, Tq), 2e-2 * rms)
+        few = nrows <= FEW_ROWS
+        own = 2e-2 * np.sqrt(np.mean(ref * ref, axis=(2, 3)))
+        tol[few] = np.maximum(tol[few], own[few])
+        qerr = err.max(axis=(2, 3))
+        ratio = qerr / tol
+        print(f"attention {label}: max |d| = {err.max():.3g}, {ratio.max():.3f} of the tolerance "
+              f"(2e-2 x RMS of the call; {int(few.sum())} of {few.size} queries with <= {FEW_ROWS} rows "
+              f"on their own RMS, worst of those {ratio[few].max() if few.any() else 0:.3f}, "
+              f"worst of the rest {ratio[~few].max() if (~few).any() else 0:.3f} of 2e-2 x the call's RMS)",
+              flush=True)
+        assert np.all(qerr <= tol), f"attention max |d| = {err.max()}, RMS = {rms}"
         assert np.max(np.abs(lse - ref_lse)) <= 1e-3
     return float(err.max())
 
@@ -191,7 +217,7 @@ def run_chain(cfg, split_index=False, W=None, sink=None):
             out, lse = H.run_hca_attend(Q, C, X, win_pos, q_pos, m, W, dt,
                                         sink=None if sink is None else H.to_dev(sink))
             rows = lambda b, t: oracle.hca_rows(Ch[b], m, Xd[b], 0, int(q_pos_h[b]) + t, W)
-        check_attend(prob[f"Q_{layer}"], dt, rows, out, lse, scale, sink)
+        check_attend(prob[f"Q_{layer}"], dt, rows, out, lse, scale, sink, label=layer)
         results[f"{layer}_out"] = out.cpu().numpy()
         results[f"{layer}_lse"] = lse.cpu().numpy()
         results[f"{layer}_C"] = C.cpu().numpy()

@@ -4,6 +4,8 @@ tokens) and in the fallback of two launches, and the separate calls are checked 
 the oracle.  Tolerance against the oracle as for pooling: fp32 max |d| <= 1e-5; bf16
 |d| <= one bf16 ulp of the fp64 value + 2^-16 * sum_j S_j |x_j|.
 """
+import zlib
+
 import numpy as np
 import pytest
 import torch
@@ -66,7 +68,7 @@ CASES = {
 def test_pair_equals_separate_calls(name):
     B, c, (n_a, m_a), (n_b, m_b), dt, pad = CASES[name]
     print(f"[pool pair {name}]", flush=True)
-    g = torch.Generator(device="cuda").manual_seed(hash(name) % 1000)
+    g = torch.Generator(device="cuda").manual_seed(zlib.crc32(name.encode()) % 1000)
     Xa, Za = _side(g, B, n_a, c, dt, pad)
     Xb, Zb = _side(g, B, n_b, c, dt, pad)
     ibs_a, ibs_b = (n_a + pad) * c, (n_b + pad) * c

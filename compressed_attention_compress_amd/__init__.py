@@ -40,6 +40,8 @@ _SIGNATURES = {
     "lightning_index_topk_workspace_size": (_SZ, [_I, _I, _I, _I, _I]),
     "lightning_index_topk": (_I, [_P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P,
                                   _P, _SZ, _P]),
+    "lightning_index_topk_noalloc": (_I, [_P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P,
+                                          _P, _P]),
     "lightning_index_score": (_I, [_P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _SZ,
                                    _P]),
     "lightning_index_select": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _SZ, _P]),
@@ -203,6 +205,13 @@ def lightning_index_topk(q_idx, w_idx, k_idx, idx_dtype, q_pos, m, B, Tq, n_ih, 
         _ptr(q_idx), _ptr(w_idx), _ptr(k_idx), idx_dtype, _ptr(q_pos), m, B, Tq, n_ih, c_I, N_c,
         k, _ptr(topk_idx), _ptr(topk_score), _ptr(all_scores), _ptr(workspace), ws_bytes,
         _stream(stream)))
+
+
+def lightning_index_topk_noalloc(q_idx, w_idx, k_idx, idx_dtype, q_pos, m, B, Tq, n_ih, c_I, N_c,
+                                 k, topk_idx, topk_score, all_scores, stream=None):
+    return _check("lightning_index_topk_noalloc", load().lightning_index_topk_noalloc(
+        _ptr(q_idx), _ptr(w_idx), _ptr(k_idx), idx_dtype, _ptr(q_pos), m, B, Tq, n_ih, c_I, N_c,
+        k, _ptr(topk_idx), _ptr(topk_score), _ptr(all_scores), _stream(stream)))
 
 
 def lightning_index_score(q_idx, w_idx, k_idx, idx_dtype, q_pos, m, B, Tq, n_ih, c_I, N_c, k,

@@ -16,6 +16,8 @@
 // LDS histogram per 11-bit digit) that skip the bits all remaining candidates share and
 // rank the last few candidates directly.  The candidates are kept in index order, so the
 // output comes out ascending without a sort.
+#include <mutex>
+
 #include "indexer.hpp"
 
 namespace {
@@ -334,25 +336,118 @@ extern "C" int lightning_index_select(const float* scores, const int* q_pos, int
                      N_c, k, topk_idx, topk_score, (hipStream_t)stream);
 }
 
-extern "C" int lightning_index_topk(const void* q_idx, const float* w_idx, const void* k_idx,
-                                    int idx_dtype, const int* q_pos, int m, int B, int Tq,
-                                    int n_ih, int c_I, int N_c, int k, int* topk_idx,
-                                    float* topk_score, float* all_scores, void* workspace,
-                                    size_t ws_bytes, void* stream) {
+namespace {
+
+// lightning_index_topk on a given workspace (the caller's, or the allocation-free variant's
+// file-scope scratch); argument checks included
+int index_topk_impl(const char* name, const void* q_idx, const float* w_idx, const void* k_idx,
+                    int idx_dtype, const int* q_pos, int m, int B, int Tq, int n_ih, int c_I,
+                    int N_c, int k, int* topk_idx, float* topk_score, float* all_scores,
+                    void* workspace, size_t ws_bytes, hipStream_t s) {
   using namespace csahca;
   int st = index_check_common(q_idx, w_idx, k_idx, idx_dtype, q_pos, m, B, Tq, n_ih, c_I, N_c, k);
   if (st != CSAHCA_OK) return st;
-  if (!topk_idx) return fail(CSAHCA_EINVAL, "lightning_index_topk: topk_idx must be non-NULL");
+  if (!topk_idx) {
+    set_error("%s: topk_idx must be non-NULL", name);
+    return CSAHCA_EINVAL;
+  }
   const WsLayout L = ws_layout((long long)B * Tq, N_c);
-  if (!workspace || ws_bytes < L.total)
-    return fail(CSAHCA_EWORKSPACE, "lightning_index_topk: workspace missing or too small");
-  if (all_scores && !aligned16(all_scores))
-    return fail(CSAHCA_EINVAL, "lightning_index_topk: all_scores must be 16-byte aligned");
+  if (!workspace || ws_bytes < L.total) {
+    set_error("%s: workspace missing or too small (%zu bytes needed)", name, L.total);
+    return CSAHCA_EWORKSPACE;
+  }
+  if (all_scores && !aligned16(all_scores)) {
+    set_error("%s: all_scores must be 16-byte aligned", name);
+    return CSAHCA_EINVAL;
+  }
   float* scores = all_scores ? all_scores : (float*)((char*)workspace + L.scores_off);
   uint32_t* gkeys = (uint32_t*)((char*)workspace + L.gkeys_off);
-  hipStream_t s = (hipStream_t)stream;
   st = index_score_impl(q_idx, w_idx, k_idx, idx_dtype, q_pos, m, B, Tq, n_ih, c_I, N_c, scores, gkeys, s);
   if (st != CSAHCA_OK) return st;
   return index_select_impl(scores, gkeys, q_pos, m, B, Tq, N_c, k, topk_idx, topk_score, s);
 }
 
+}  // namespace
+
+extern "C" int lightning_index_topk(const void* q_idx, const float* w_idx, const void* k_idx,
+                                    int idx_dtype, const int* q_pos, int m, int B, int Tq,
+                                    int n_ih, int c_I, int N_c, int k, int* topk_idx,
+                                    float* topk_score, float* all_scores, void* workspace,
+                                    size_t ws_bytes, void* stream) {
+  return index_topk_impl("lightning_index_topk", q_idx, w_idx, k_idx, idx_dtype, q_pos, m, B, Tq,
+                         n_ih, c_I, N_c, k, topk_idx, topk_score, all_scores, workspace, ws_bytes,
+                         (hipStream_t)stream);
+}
+
+// ---------------------------------------------------------------------------------------
+// allocation-free variant: the workspace is a file-scope device array
+// ---------------------------------------------------------------------------------------
+// Every GPU the library runs on holds its own copy of `scratch` (placed by the code-object
+// loader, zero-filled) until the process ends.  In host code the array's name only stands
+// for the symbol: its device address is taken once per device with hipGetSymbolAddress,
+// and only that address is ever handed to a kernel.
+static __device__ __align__(256) uint8_t scratch[CSAHCA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int MAX_DEVICES = 64;
+std::mutex scratch_mu;
+void* scratch_dev[MAX_DEVICES];  // device address of `scratch` per device, null until set up
+
+// The device address of this device's scratch array; set up on the first call per device
+// (that device current).  Fails when the stream belongs to another device than the
+// current one, whose copy of the array the kernels would then not be able to reach.
+int scratch_for(const char* name, hipStream_t stream, void** out) {
+  using namespace csahca;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) {
+    set_error("%s: no current device (or device ordinal >= %d)", name, MAX_DEVICES);
+    return CSAHCA_ELAUNCH;
+  }
+  if (stream) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess || (int)sdev != dev) {
+      set_error("%s: the stream must belong to the current device", name);
+      return CSAHCA_EINVAL;
+    }
+  }
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_dev[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      set_error("%s: cannot locate the scratch array on device %d: %s", name, dev, hipGetErrorString(e));
+      return CSAHCA_ELAUNCH;
+    }
+    scratch_dev[dev] = p;
+  }
+  *out = scratch_dev[dev];
+  return CSAHCA_OK;
+}
+
+}  // namespace
+
+extern "C" int lightning_index_topk_noalloc(const void* q_idx, const float* w_idx,
+                                            const void* k_idx, int idx_dtype, const int* q_pos,
+                                            int m, int B, int Tq, int n_ih, int c_I, int N_c,
+                                            int k, int* topk_idx, float* topk_score,
+                                            float* all_scores, void* stream) {
+  using namespace csahca;
+  const char* name = "lightning_index_topk_noalloc";
+  // shape checks first: the size test below needs sane B, Tq and N_c
+  int st = index_check_common(q_idx, w_idx, k_idx, idx_dtype, q_pos, m, B, Tq, n_ih, c_I, N_c, k);
+  if (st != CSAHCA_OK) return st;
+  const size_t need = ws_layout((long long)B * Tq, N_c).total;
+  if (need > CSAHCA_NOALLOC_SCRATCH_BYTES) {
+    set_error("%s: the call needs %zu bytes of scratch, above the built maximum of %zu "
+              "(use lightning_index_topk with a workspace)", name, need,
+              (size_t)CSAHCA_NOALLOC_SCRATCH_BYTES);
+    return CSAHCA_EWORKSPACE;
+  }
+  void* ws = nullptr;
+  st = scratch_for(name, (hipStream_t)stream, &ws);
+  if (st != CSAHCA_OK) return st;
+  return index_topk_impl(name, q_idx, w_idx, k_idx, idx_dtype, q_pos, m, B, Tq, n_ih, c_I, N_c, k,
+                         topk_idx, topk_score, all_scores, ws, CSAHCA_NOALLOC_SCRATCH_BYTES,
+                         (hipStream_t)stream);
+}

@@ -180,6 +180,26 @@ int lightning_index_topk(const void* q_idx, const float* w_idx, const void* k_id
                          float* all_scores, void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * lightning_index_topk_noalloc -- lightning_index_topk for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): same arguments and results, minus the workspace.
+ *
+ * The workspace is instead a file-scope device array of CSAHCA_NOALLOC_SCRATCH_BYTES that
+ * every GPU the library runs on holds until the process ends.  Its device address is
+ * looked up once per device, on the first call with that device current; the stream must
+ * belong to the current device (else CSAHCA_EINVAL).  The call allocates and frees
+ * nothing.  A call whose lightning_index_topk_workspace_size() exceeds the maximum returns
+ * CSAHCA_EWORKSPACE and enqueues nothing.  All calls on one GPU share that GPU's array:
+ * calls that overlap on one GPU (different streams, or host threads without ordering)
+ * race on it and their results are undefined; calls ordered on one stream are fine.
+ */
+#define CSAHCA_NOALLOC_SCRATCH_BYTES (32u << 20)
+int lightning_index_topk_noalloc(const void* q_idx, const float* w_idx, const void* k_idx,
+                                 int idx_dtype, const int* q_pos, int m, int B, int Tq,
+                                 int n_ih, int c_I, int N_c, int k, int* topk_idx,
+                                 float* topk_score, float* all_scores, void* stream);
+
+/*
  * The two halves of lightning_index_topk, for callers that time or check them apart.
  * lightning_index_score writes every usable score to `scores` [B, Tq, N_c] and the
  * per-16-entry group maxima to the workspace; lightning_index_select must then be given

@@ -38,7 +38,9 @@ def _rngs(seed):
 
 def layers_of(cfg):
     return {"csa_decode": ("csa",), "hca_decode": ("hca",),
-            "prefill": ("csa", "hca"), "pair_decode": ("csa", "hca")}[cfg.kind]
+            "prefill": ("csa", "hca"), "pair_decode": ("csa", "hca"),
+            # the indexer's inputs only (no raw KV, queries or gates)
+            "index_decode": ("index",), "index_prefill": ("index",)}[cfg.kind]
 
 
 def make_problem(cfg):
@@ -51,7 +53,7 @@ def make_problem(cfg):
     r = _rngs(cfg.seed)
     B, c = cfg.B, cfg.c
     Tq = cfg.Tq
-    n_total = cfg.n + (Tq if cfg.kind == "prefill" else 0)
+    n_total = cfg.n + (Tq if cfg.kind in ("prefill", "index_prefill") else 0)
     lay = layers_of(cfg)
     out = {"cfg": cfg, "n_total": n_total, "Tq": Tq}
     out["q_pos"] = np.full((B,), n_total - Tq, dtype=np.int32)
@@ -59,7 +61,8 @@ def make_problem(cfg):
     def normal(name, shape, std=1.0):
         return (r[name].standard_normal(shape, dtype=np.float32) * np.float32(std)).astype(np.float32)
 
-    X = normal("X_csa", (B, n_total, c), cfg.kv_std)
+    if "csa" in lay or "hca" in lay:
+        X = normal("X_csa", (B, n_total, c), cfg.kv_std)
     if "csa" in lay:
         out["X_csa"] = encode(X, cfg.dtype)
         out["Z_csa"] = encode(normal("Z_csa", (B, n_total, c)), cfg.dtype)
@@ -74,7 +77,7 @@ def make_problem(cfg):
             out["Q_hca"] = out["Q_csa"]
         else:
             out["Q_hca"] = encode(normal("Q_hca", (B, Tq, cfg.n_h, c)), cfg.dtype)
-    if "csa" in lay:
+    if "csa" in lay or "index" in lay:
         N_c = n_total // cfg.m
         qI = normal("qI", (B, Tq, cfg.n_ih, cfg.c_I))
         w = r["w"].random((B, Tq, cfg.n_ih), dtype=np.float32)

@@ -75,6 +75,24 @@ def test_pool_validation():
     assert ov(None, None, None, None, None, None, 1, 4, 8, 4, 1, 1, 32, 0, None) == 0
 
 
+def test_indexer_noalloc_validation():
+    """The allocation-free variant checks shapes, then its scratch bound, before any HIP
+    call (no GPU needed for these)."""
+    L = lib.load()
+    fn = L.lightning_index_topk_noalloc
+    # a call whose workspace would exceed the built scratch array is refused
+    big = [FAKE, FAKE, FAKE, 2, FAKE, 4, 64, 1, 64, 128, 262144, 1024, FAKE, None, None, None]
+    assert L.lightning_index_topk_workspace_size(64, 1, 64, 262144, 1024) > (32 << 20)
+    assert fn(*big) == EWORKSPACE
+    assert "scratch" in lib.last_error()
+    bad = list(big)
+    bad[0] = None
+    assert fn(*bad) == EINVAL
+    bad = list(big)
+    bad[9] = 96  # c_I
+    assert fn(*bad) == ENOTSUP
+
+
 def test_indexer_validation():
     L = lib.load()
     B, Tq, n_ih, c_I, N_c, k = 2, 1, 64, 128, 1000, 64

@@ -204,7 +204,7 @@ class Workload:
         self.lib.lightning_index_select(self.scores, self.q_pos, cfg.m, cfg.B, self.Tq, self.N_c,
                                         cfg.k, self.idx, None, self.iws, self.iws_b)
 
-    def index(self, r, split=True):
+    def index(self, r, split=False):
         cfg, lib, rp = self.cfg, self.lib, self.rep[r]
         B = cfg.B
         if split:
@@ -261,9 +261,9 @@ class Workload:
 
     def step(self, r):
         """One pass of the path.  At decode, with both layers present, the HCA attention
-        runs on a second stream while the scoring kernel, the CSA top-k pass and the CSA
-        attention run on the first: the HCA layer needs nothing from the indexer, and the
-        top-k pass occupies few compute units.  The second stream forks after the pooling.
+        runs on a second stream while the indexer (scoring with its fused top-k selection)
+        and the CSA attention run on the first: the HCA layer needs nothing from the
+        indexer.  The second stream forks after the pooling.
         Edges between the graph's hardware queues resolve late (the waiting node started
         15 to 40 microseconds after its producer in kernel traces), so the CSA chain is
         issued first, stays on the pooling's queue, and keeps no edge from the second
@@ -277,8 +277,7 @@ class Workload:
             pooled.record(main)
             # the CSA chain is issued first, so that it stays on the pooling's hardware
             # queue; the second stream forks from the pooling
-            self.index_score(r)
-            self.select(r)
+            self.index(r)
             self.attend(r, ["csa"])
             self.s_hca.wait_event(pooled)
             with torch.cuda.stream(self.s_hca):
@@ -976,9 +975,11 @@ def main():
     if "csa" in wl.layers:
         gs = torch.cuda.CUDAGraph()
         reps = max(R, 8)
+        # the indexer call as the step makes it: at decode the scoring kernel with the
+        # top-k selection fused into the same launch
         with torch.cuda.graph(gs, stream=side):
             for i in range(reps):
-                wl.index_score(i % R)
+                wl.index(i % R)
         gs.replay()
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
@@ -998,8 +999,11 @@ def main():
                  "index_score_pre128" if cfg.c_I == 128 else "index_score_fp8")
         if cfg.idx_dtype == 3:
             kname += " (MX FP4 keys)"  # no counter record for this instance
+        fused = decode and cfg.c_I == 128 and cfg.idx_dtype in (2, 3)
         if decode or cfg.idx_dtype == 0:
-            roofline = {"kernel": kname, "bound": "hbm", "achieved": round(ach, 1),
+            roofline = {"kernel": (("lightning_index_topk: " + kname + " writing chunk lists, then select_topk")
+                                   if fused else kname), "bound": "hbm",
+                        "achieved": round(ach, 1),
                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
                         "traffic": read_traffic(kname) if decode else None,
                         "avg_launch_us": round(dur * 1e6, 2), "bytes_per_launch": kb}
@@ -1064,7 +1068,7 @@ def main():
                    "n_ih": cfg.n_ih, "c_I": cfg.c_I, "window": cfg.W, "replicas": R,
                    "timing": f"hip graphs of {R} steps (one per replica), rotating replicas",
                    "streams": ("one" if wl.s_hca is None or len(wl.layers) < 2 else
-                               "two: HCA attention concurrent with the CSA top-k pass and attention"),
+                               "two: HCA attention concurrent with the CSA indexer and attention"),
                    **({"attention_sink": "per-head, N(0, 2^2)"} if args.sink else {}),
                    **({"indexer_keys": "MX FP4 (E2M1, E8M0 per 32), FP8 queries"} if args.fp4_keys else {}),
                    **({"norm_rope": "RMSNorm + RoPE on the last 64 dims: entries, queries, window"}

@@ -14,16 +14,12 @@
 // head weights and the cross-head sum are applied to the MFMA accumulators in registers.
 // Every score is written once (fp32) and every group of 16 consecutive keys also writes
 // the order-preserving 32-bit key of its maximum score.
-#include "indexer.hpp"
+#include "fused_topk.hpp"
 
 namespace {
 
 using namespace csahca;
 
-#ifndef CSAHCA_SCORE_WGS
-#define CSAHCA_SCORE_WGS 512  // scoring workgroups to aim for (about two per CU)
-#endif
-constexpr int SCORE_STAGE = 4096;  // keys per decode workgroup (LDS-staged scores)
 
 // ---------------------------------------------------------------------------------------
 // scoring, FP8 E4M3FN keys on MFMA
@@ -237,12 +233,15 @@ CSAHCA_DEV void wait_vm_le(int n) {
   }
 }
 
-template <int HB, bool F4>
+// LISTS: the per-chunk half of the top-k selection runs in the same launch
+// (fused_topk.hpp): every workgroup also lists the best entries of its chunk.
+template <int HB, bool F4, bool LISTS>
 __global__ __launch_bounds__(256, 2) void index_score_dec128(
     const uint8_t* __restrict__ qI, const float* __restrict__ w, const uint8_t* __restrict__ KI,
     const uint8_t* __restrict__ KS,
     const int* __restrict__ q_pos, int m, int N_c, int CH, int NG, float* __restrict__ scores,
-    uint32_t* __restrict__ gkeys) {
+    uint32_t* __restrict__ gkeys, ChunkLists cl) {
+  static_assert(!LISTS || FT_NT == 256, "the chunk cut runs on the scoring workgroup");
   constexpr int C_I = 128, NIH = HB * 16;
   // a block of 16 keys: FP8 rows of 128 bytes, or FP4 rows of 64 bytes followed by a
   // 256-byte slot whose first 64 bytes are the 16 keys' four E8M0 scales each
@@ -391,6 +390,36 @@ __global__ __launch_bounds__(256, 2) void index_score_dec128(
   uint32_t* grow = gkeys + (size_t)q * NG;
   for (int i = (int)threadIdx.x; i < n; i += 256) srow[e_begin + i] = s_sc[i];
   for (int i = (int)threadIdx.x; i < cdiv(n, GROUP); i += 256) grow[e_begin / GROUP + i] = s_gk[i];
+  if constexpr (LISTS) {
+    const int keff = min(cl.k, V);
+    if (keff < V) {  // (with keff == V the selection takes every usable entry)
+      // the key ring is free (every DMA has landed and the workgroup passed the barrier)
+      FtScratch& sc = *reinterpret_cast<FtScratch*>(&ring[0][0][0]);
+      static_assert(sizeof(FtScratch) <= sizeof(ring), "the cut's scratch fits the key ring");
+      uint32_t u[FT_LKPT];
+      uint64_t kr[FT_LKPT];
+#pragma unroll
+      for (int j = 0; j < FT_LKPT; ++j) {
+        const int i = (int)threadIdx.x + 256 * j;
+        u[j] = i < n ? score_key(s_sc[i]) : 0u;
+        kr[j] = i < n ? ((uint64_t)u[j] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)(e_begin + i)) : 0ull;
+      }
+      // list about this query's share of the top k per chunk plus four standard
+      // deviations (the host sized the lists for the whole cache; a shorter sequence has
+      // fewer chunks, each holding more of its top k)
+      const int P_eff = cdiv(V, CH);
+      const float per = (float)keff / (float)P_eff;
+      const int JT = min(cl.JMAX, (int)(per + 4.f * sqrtf(per) + 8.f) + 1);
+      const FtCut cut = ft_local_cut(u, n, JT, cl.JMAX, sc);
+      const int chunk = blockIdx.x;
+      uint64_t* list = cl.cand + ((size_t)q * cl.P + chunk) * cl.JMAX;
+      ft_compact(
+          kr, [&](uint64_t key) { return key != 0ull && (key >> 32) >= cut.cut; },
+          [&](uint32_t pos, uint64_t key) { list[pos] = key; }, sc);
+      for (int i = (int)cut.count + (int)threadIdx.x; i < cl.JMAX; i += 256) list[i] = 0ull;  // padding
+      if (threadIdx.x == 0) cl.edge[(size_t)q * FT_MAX_P + chunk] = cut.cut == 0ull ? 0ull : cut.cut << 32;
+    }
+  }
   CSAHCA_TRACE(4);
   CSAHCA_TRACE_RT(15);
 }
@@ -612,24 +641,29 @@ __global__ __launch_bounds__(256) void index_score_f32(
 template <int C_I, int HB, bool F4>
 void launch_fp8(const void* q_idx, const float* w_idx, const void* k_idx, const int* q_pos,
                 int m, int Tq, int N_c, int nq, int NG, float* scores, uint32_t* gkeys,
-                hipStream_t st) {
+                hipStream_t st, const ChunkLists* cl) {
   const bool decode = Tq == 1;
   const int QPW = decode ? 1 : 4;
   const int qgroups = cdiv(nq, QPW);
   // about two workgroups per CU, each streaming a long chunk of keys (decode: at most
-  // SCORE_STAGE keys, the LDS staging of its scores)
-  int chunks = cdiv(CSAHCA_SCORE_WGS, qgroups);
+  // SCORE_STAGE keys, the LDS staging of its scores; the chunks of the decode kernel
+  // follow the plan its fused selection is sized by)
+  int chunks = cdiv(SCORE_WGS, qgroups);
   chunks = max(1, min(chunks, cdiv(N_c, 256)));
   if (decode) chunks = max(chunks, cdiv(N_c, SCORE_STAGE));
-  const int CH = cdiv(cdiv(N_c, chunks), 64) * 64;
+  int CH = cdiv(cdiv(N_c, chunks), 64) * 64;
+  if (decode && C_I == 128) CH = topk_plan_decode(nq, N_c, cl ? cl->k : 1).CH;
   chunks = cdiv(N_c, CH);
   dim3 grid((unsigned)chunks, (unsigned)qgroups);
   const uint8_t* KI = (const uint8_t*)k_idx;
   // MX FP4 keys: [B, N_c, 64] E2M1 rows, then [B, N_c, 4] E8M0 scales
   const uint8_t* KS = F4 ? KI + (size_t)(nq / Tq) * N_c * (C_I / 2) : nullptr;
-  if (decode && C_I == 128)
-    hipLaunchKernelGGL((index_score_dec128<HB, F4>), grid, dim3(256), 0, st, (const uint8_t*)q_idx,
-                       w_idx, KI, KS, q_pos, m, N_c, CH, NG, scores, gkeys);
+  if (decode && C_I == 128 && cl)
+    hipLaunchKernelGGL((index_score_dec128<HB, F4, true>), grid, dim3(256), 0, st, (const uint8_t*)q_idx,
+                       w_idx, KI, KS, q_pos, m, N_c, CH, NG, scores, gkeys, *cl);
+  else if (decode && C_I == 128)
+    hipLaunchKernelGGL((index_score_dec128<HB, F4, false>), grid, dim3(256), 0, st, (const uint8_t*)q_idx,
+                       w_idx, KI, KS, q_pos, m, N_c, CH, NG, scores, gkeys, ChunkLists{});
   else if (C_I == 128)
     hipLaunchKernelGGL((index_score_pre128<HB, F4>),
                        dim3((unsigned)(nq / Tq * cdiv(Tq, 4)), (unsigned)cdiv(N_c, PRE_KEYS)), dim3(256), 0, st,
@@ -645,12 +679,12 @@ void launch_fp8(const void* q_idx, const float* w_idx, const void* k_idx, const 
 template <int C_I, bool F4>
 bool launch_fp8_heads(int n_ih, const void* q_idx, const float* w_idx, const void* k_idx,
                       const int* q_pos, int m, int Tq, int N_c, int nq, int NG, float* scores,
-                      uint32_t* gkeys, hipStream_t st) {
+                      uint32_t* gkeys, hipStream_t st, const ChunkLists* cl) {
   switch (n_ih / 16) {
-    case 1: launch_fp8<C_I, 1, F4>(q_idx, w_idx, k_idx, q_pos, m, Tq, N_c, nq, NG, scores, gkeys, st); return true;
-    case 2: launch_fp8<C_I, 2, F4>(q_idx, w_idx, k_idx, q_pos, m, Tq, N_c, nq, NG, scores, gkeys, st); return true;
-    case 4: launch_fp8<C_I, 4, F4>(q_idx, w_idx, k_idx, q_pos, m, Tq, N_c, nq, NG, scores, gkeys, st); return true;
-    case 8: launch_fp8<C_I, 8, F4>(q_idx, w_idx, k_idx, q_pos, m, Tq, N_c, nq, NG, scores, gkeys, st); return true;
+    case 1: launch_fp8<C_I, 1, F4>(q_idx, w_idx, k_idx, q_pos, m, Tq, N_c, nq, NG, scores, gkeys, st, cl); return true;
+    case 2: launch_fp8<C_I, 2, F4>(q_idx, w_idx, k_idx, q_pos, m, Tq, N_c, nq, NG, scores, gkeys, st, cl); return true;
+    case 4: launch_fp8<C_I, 4, F4>(q_idx, w_idx, k_idx, q_pos, m, Tq, N_c, nq, NG, scores, gkeys, st, cl); return true;
+    case 8: launch_fp8<C_I, 8, F4>(q_idx, w_idx, k_idx, q_pos, m, Tq, N_c, nq, NG, scores, gkeys, st, cl); return true;
     default: return false;
   }
 }
@@ -689,20 +723,25 @@ int index_check_common(const void* q_idx, const float* w_idx, const void* k_idx,
 }
 
 
+bool index_can_list(int idx_dtype, int Tq, int c_I, int n_ih, const TopkPlan& plan) {
+  return plan.lists && Tq == 1 && c_I == 128 && (n_ih == 16 || n_ih == 32 || n_ih == 64 || n_ih == 128) &&
+         (idx_dtype == CSAHCA_FP8_E4M3FN || idx_dtype == CSAHCA_MXFP4);
+}
+
 int index_score_impl(const void* q_idx, const float* w_idx, const void* k_idx, int idx_dtype,
                      const int* q_pos, int m, int B, int Tq, int n_ih, int c_I, int N_c,
-                     float* scores, uint32_t* gkeys, hipStream_t st) {
+                     float* scores, uint32_t* gkeys, hipStream_t st, const ChunkLists* cl) {
   using namespace csahca;
   const int nq = B * Tq;
   const int NG = cdiv(N_c, GROUP);
   if (idx_dtype == CSAHCA_FP8_E4M3FN) {
     bool ok = false;
-    if (c_I == 128) ok = launch_fp8_heads<128, false>(n_ih, q_idx, w_idx, k_idx, q_pos, m, Tq, N_c, nq, NG, scores, gkeys, st);
-    else if (c_I == 64) ok = launch_fp8_heads<64, false>(n_ih, q_idx, w_idx, k_idx, q_pos, m, Tq, N_c, nq, NG, scores, gkeys, st);
-    else ok = launch_fp8_heads<32, false>(n_ih, q_idx, w_idx, k_idx, q_pos, m, Tq, N_c, nq, NG, scores, gkeys, st);
+    if (c_I == 128) ok = launch_fp8_heads<128, false>(n_ih, q_idx, w_idx, k_idx, q_pos, m, Tq, N_c, nq, NG, scores, gkeys, st, cl);
+    else if (c_I == 64) ok = launch_fp8_heads<64, false>(n_ih, q_idx, w_idx, k_idx, q_pos, m, Tq, N_c, nq, NG, scores, gkeys, st, nullptr);
+    else ok = launch_fp8_heads<32, false>(n_ih, q_idx, w_idx, k_idx, q_pos, m, Tq, N_c, nq, NG, scores, gkeys, st, nullptr);
     if (!ok) return fail(CSAHCA_ENOTSUP, "indexer: FP8 keys need n_ih in {16, 32, 64, 128}");
   } else if (idx_dtype == CSAHCA_MXFP4) {
-    if (!launch_fp8_heads<128, true>(n_ih, q_idx, w_idx, k_idx, q_pos, m, Tq, N_c, nq, NG, scores, gkeys, st))
+    if (!launch_fp8_heads<128, true>(n_ih, q_idx, w_idx, k_idx, q_pos, m, Tq, N_c, nq, NG, scores, gkeys, st, cl))
       return fail(CSAHCA_ENOTSUP, "indexer: MX FP4 keys need n_ih in {16, 32, 64, 128}");
   } else {
     const size_t lds = (size_t)(n_ih * c_I + n_ih) * sizeof(float);
@@ -723,7 +762,7 @@ extern "C" int lightning_index_score(const void* q_idx, const float* w_idx, cons
   int st = index_check_common(q_idx, w_idx, k_idx, idx_dtype, q_pos, m, B, Tq, n_ih, c_I, N_c, k);
   if (st != CSAHCA_OK) return st;
   if (!scores) return fail(CSAHCA_EINVAL, "lightning_index_score: scores must be non-NULL");
-  const WsLayout L = ws_layout((long long)B * Tq, N_c);
+  const WsLayout L = ws_layout((long long)B * Tq, N_c, k, Tq == 1);
   if (!workspace || ws_bytes < L.total)
     return fail(CSAHCA_EWORKSPACE, "lightning_index_score: workspace missing or too small");
   return index_score_impl(q_idx, w_idx, k_idx, idx_dtype, q_pos, m, B, Tq, n_ih, c_I, N_c, scores,

@@ -25,12 +25,17 @@ namespace {
 using namespace csahca;
 
 // ---------------------------------------------------------------------------------------
-// selection
+// selection (one workgroup of SEL_THREADS threads per query)
 // ---------------------------------------------------------------------------------------
 constexpr int DBITS = 11;                // radix digit
 constexpr int NBIN = 1 << DBITS;
 constexpr int BPT = NBIN / SEL_THREADS;  // digits each thread scans
 constexpr int NWAVE = SEL_THREADS / 64;
+constexpr int SEL_COMPACT = 4096;        // list keys compacted into LDS for the k-th search
+constexpr int CPT = SEL_COMPACT / SEL_THREADS;
+constexpr int GPW = KPT * 64 / GROUP;    // listed groups per wave in the candidate gather
+static_assert(NWAVE * GPW == MAX_K, "the candidate gather holds k groups");
+static_assert(FT_MAX_P <= 128 && SEL_THREADS >= 128, "the bounds are read by the first two waves");
 
 struct SelScratch {
   uint32_t hist[2][NBIN];
@@ -46,43 +51,52 @@ struct SelScratch {
 };
 
 // K-th largest (1-based) of the distinct nonzero keys the workgroup holds in registers
-// (KPT per thread; 0 = empty).  One AND/OR reduction finds the highest bit on which the
+// (KP per thread; 0 = empty).  One AND/OR reduction finds the highest bit on which the
 // keys differ; from there MSB-first radix passes of 11 bits narrow the candidates.  A
-// pass builds an LDS histogram of the digit, then every wave scans 128 digits (two per
-// lane, in descending order) and the lane whose range holds the K-th key reports the
-// digit.  The search stops as soon as that digit holds a single candidate.  (All 1024
-// threads run on one CU, so every phase costs its instruction count times 16 cycles:
-// a second pass is cheaper than gathering and ranking even a hundred keys.)
-CSAHCA_DEV uint64_t radix_select_kth(const uint64_t (&kr)[KPT], int kth, SelScratch& sc) {
+// pass builds an LDS histogram of the digit, then every thread scans BPT digits (in
+// descending order) and the thread whose range holds the K-th key reports the digit.  The
+// search stops as soon as that digit holds a single candidate.
+//
+// With RANGE the caller passes bounds lo <= every key <= hi instead (and has zeroed both
+// histograms, sc.hist): the keys share the bits above the highest bit where lo and hi
+// differ, so the AND/OR reduction is skipped.
+template <int KP, bool RANGE = false>
+CSAHCA_DEV uint64_t radix_select_kth(const uint64_t (&kr)[KP], int kth, SelScratch& sc,
+                                     uint64_t lo = 0ull, uint64_t hi = 0ull) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t alo = ~0u, ahi = ~0u, olo = 0u, ohi = 0u;
+  uint64_t a = lo, o = hi;
+  if constexpr (!RANGE) {
+    uint32_t alo = ~0u, ahi = ~0u, olo = 0u, ohi = 0u;
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) {
-    if (kr[j] != 0ull) {
-      alo &= (uint32_t)kr[j];
-      ahi &= (uint32_t)(kr[j] >> 32);
-      olo |= (uint32_t)kr[j];
-      ohi |= (uint32_t)(kr[j] >> 32);
+    for (int j = 0; j < KP; ++j) {
+      if (kr[j] != 0ull) {
+        alo &= (uint32_t)kr[j];
+        ahi &= (uint32_t)(kr[j] >> 32);
+        olo |= (uint32_t)kr[j];
+        ohi |= (uint32_t)(kr[j] >> 32);
+      }
     }
-  }
-  alo = wave_and(alo);
-  ahi = wave_and(ahi);
-  olo = wave_or(olo);
-  ohi = wave_or(ohi);
-  if (lane == 0) {
-    sc.red_and[wave] = ((uint64_t)ahi << 32) | alo;
-    sc.red_or[wave] = ((uint64_t)ohi << 32) | olo;
-  }
-  for (int i = threadIdx.x; i < 2 * NBIN; i += SEL_THREADS) (&sc.hist[0][0])[i] = 0u;
-  __syncthreads();
-  uint64_t a = ~0ull, o = 0ull;
+    alo = wave_and(alo);
+    ahi = wave_and(ahi);
+    olo = wave_or(olo);
+    ohi = wave_or(ohi);
+    if (lane == 0) {
+      sc.red_and[wave] = ((uint64_t)ahi << 32) | alo;
+      sc.red_or[wave] = ((uint64_t)ohi << 32) | olo;
+    }
+    for (int i = threadIdx.x; i < 2 * NBIN; i += SEL_THREADS) (&sc.hist[0][0])[i] = 0u;
+    __syncthreads();
+    a = ~0ull;
+    o = 0ull;
 #pragma unroll
-  for (int i = 0; i < NWAVE; ++i) {
-    a &= sc.red_and[i];
-    o |= sc.red_or[i];
+    for (int i = 0; i < NWAVE; ++i) {
+      a &= sc.red_and[i];
+      o |= sc.red_or[i];
+    }
+    __syncthreads();
   }
   const uint64_t diff = a ^ o;
-  if (diff == 0ull) return a;  // a single key
+  if (diff == 0ull) return a;  // a single key (with RANGE: lo == hi)
   const int hb = 63 - __builtin_clzll(diff);
   // bits above hb are common to every key
   uint64_t mask = hb == 63 ? 0ull : (~0ull << (hb + 1));
@@ -97,7 +111,7 @@ CSAHCA_DEV uint64_t radix_select_kth(const uint64_t (&kr)[KPT], int kth, SelScra
   for (int sh = hb >= DBITS - 1 ? hb - (DBITS - 1) : 0;; sh = sh >= DBITS ? sh - DBITS : 0) {
     uint32_t* h = sc.hist[buf];
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) {
+    for (int j = 0; j < KP; ++j) {
       const uint64_t k = kr[j];
       if (k != 0ull && (k & mask) == prefix) atomicAdd(&h[(uint32_t)(k >> sh) & (NBIN - 1)], 1u);
     }
@@ -107,7 +121,7 @@ CSAHCA_DEV uint64_t radix_select_kth(const uint64_t (&kr)[KPT], int kth, SelScra
     if (threadIdx.x == 0 && blockIdx.x < 8192 && tfirst)
       csahca_trace[blockIdx.x * 16 + tslot + 1] = __builtin_amdgcn_s_memtime();
 #endif
-    // this lane's BPT digits, descending with the thread index
+    // this thread's BPT digits, descending with the thread index
     const int d_hi = NBIN - 1 - BPT * (int)threadIdx.x;
     uint32_t c[BPT], csum = 0;
 #pragma unroll
@@ -144,10 +158,13 @@ CSAHCA_DEV uint64_t radix_select_kth(const uint64_t (&kr)[KPT], int kth, SelScra
     const uint32_t count = sc.found_count;
     prefix = (prefix & ~((uint64_t)(NBIN - 1) << sh)) | (dsel << sh);
     mask |= (uint64_t)(NBIN - 1) << sh;
-    if (sh == 0) return prefix;  // every bit decided
-    if (count == 1) {            // the K-th key is the only candidate left
+    if (sh == 0) {  // every bit decided
+      __syncthreads();
+      return prefix;
+    }
+    if (count == 1) {  // the K-th key is the only candidate left
 #pragma unroll
-      for (int j = 0; j < KPT; ++j)
+      for (int j = 0; j < KP; ++j)
         if (kr[j] != 0ull && (kr[j] & mask) == prefix) sc.result = kr[j];
       __syncthreads();
       const uint64_t r = sc.result;
@@ -158,29 +175,86 @@ CSAHCA_DEV uint64_t radix_select_kth(const uint64_t (&kr)[KPT], int kth, SelScra
   }
 }
 
+// Hands every key of kr for which pred holds to sink(position, key, j), positions counted
+// in the order (j, wave, lane) when JMAJOR, else (wave, j, lane); returns their number.
+// Two ballot rounds (counts, then positions), so no ballot is held in registers.
+template <int KP, bool JMAJOR, typename Pred, typename Sink>
+CSAHCA_DEV uint32_t compact_in_order(const uint64_t (&kr)[KP], Pred pred, Sink sink, SelScratch& sc) {
+  static_assert(KP * NWAVE <= 4 * 64, "one wave scans the (j, wave) counts, four per lane");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int j = 0; j < KP; ++j) {
+    const uint64_t bal = __ballot(pred(kr[j]));
+    if (lane == 0) sc.jw[JMAJOR ? j * NWAVE + wave : wave * KP + j] = (uint32_t)__popcll(bal);
+  }
+  __syncthreads();
+  if (wave == 0) {
+    constexpr int N = KP * NWAVE, PER = (N + 63) / 64;
+    uint32_t c[PER], sum = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int x = lane * PER + i;
+      c[i] = x < N ? sc.jw[x] : 0u;
+      sum += c[i];
+    }
+    const uint32_t incl = wave_incl_scan(sum);
+    uint32_t run = incl - sum;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int x = lane * PER + i;
+      if (x < N) sc.jw[x] = run;
+      run += c[i];
+    }
+    if (lane == 63) sc.total = incl;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < KP; ++j) {
+    const bool p = pred(kr[j]);
+    const uint64_t bal = __ballot(p);
+    if (p)
+      sink(sc.jw[JMAJOR ? j * NWAVE + wave : wave * KP + j] +
+               __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u)),
+           kr[j], j);
+  }
+  const uint32_t total = sc.total;
+  __syncthreads();
+  return total;
+}
+
+// Every key of kr that is >= T, written out in the order (j, wave, lane) when JMAJOR, else
+// (wave, j, lane) (the callers make that the index order); then the padding up to k.
+template <int KP, bool JMAJOR>
+CSAHCA_DEV void write_selected(const uint64_t (&kr)[KP], uint64_t T, int keff, int k, int* orow,
+                               float* osc, SelScratch& sc) {
+  compact_in_order<KP, JMAJOR>(
+      kr, [&](uint64_t key) { return key != 0ull && key >= T; },
+      [&](uint32_t pos, uint64_t key, int) {
+        orow[pos] = (int)key_index(key);
+        if (osc) osc[pos] = key_score((uint32_t)(key >> 32));
+      },
+      sc);
+  for (int i = keff + threadIdx.x; i < k; i += SEL_THREADS) {
+    orow[i] = -1;
+    if (osc) osc[i] = -INFINITY;
+  }
+}
+
+// With chunk lists (decode; fused_topk.hpp) the selection first takes the k-th largest key
+// K of the union of the query's lists: if no chunk left out an entry at or above K, the
+// union's keys >= K are the top k.  Otherwise, and without lists, it selects through the
+// group maxima as described at the top of this file.
 __global__ __launch_bounds__(SEL_THREADS) void select_topk(
     const float* __restrict__ scores, const uint32_t* __restrict__ gmax,
     const int* __restrict__ q_pos, int m, int Tq, int N_c, int NG, int k,
-    int* __restrict__ topk_idx, float* __restrict__ topk_score) {
+    int* __restrict__ topk_idx, float* __restrict__ topk_score, ChunkLists cl) {
   __shared__ SelScratch sc;
   __shared__ int glist[MAX_K];
-  static_assert(KPT * NWAVE == 4 * 64, "one wave scans the per-(j, wave) counts");
-  static_assert(NWAVE * 64 == MAX_K, "one listed group per 16 lanes per key slot");
+  __shared__ uint64_t s_keys[SEL_COMPACT];
   CSAHCA_TRACE(0);
   CSAHCA_TRACE_RT(14);
   const int q = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  // group maxima, coalesced: thread t holds groups j*SEL_THREADS + t (j < KPT); issued
-  // before the visible count is known, masked afterwards.  A group's key is its maximum
-  // score key, then the lower group index: as groups are index ranges, that orders equal
-  // maxima as their best entries are ordered.
-  const uint32_t* grow = gmax + (size_t)q * NG;
-  uint64_t kr[KPT];
-#pragma unroll
-  for (int j = 0; j < KPT; ++j) {
-    const int gi = j * SEL_THREADS + (int)threadIdx.x;
-    kr[j] = gi < NG ? ((uint64_t)grow[gi] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)gi) : 0ull;
-  }
   const int b = q / Tq, t = q - b * Tq;
   const int V = visible_entries(q_pos, b, t, m, N_c);
   const int keff = min(k, V);
@@ -193,66 +267,110 @@ __global__ __launch_bounds__(SEL_THREADS) void select_topk(
       orow[i] = i < V ? i : -1;
       if (osc) osc[i] = i < V ? srow[i] : -INFINITY;
     }
+    if (cl.path && threadIdx.x == 0) cl.path[q] = FT_PATH_ALL;
     return;
   }
+  uint64_t kr[KPT];
+  if (cl.cand) {
+    // The union: slot s = chunk * JMAX + position (lists are padded with zero keys);
+    // thread (wave, lane) holds slots wave * 64 KPT + 64 j + lane, so that (wave, j, lane)
+    // order is slot order, which is index order (chunks are index ranges, each list is in
+    // index order).  The lists give the top k exactly when K, their k-th largest key, is
+    // at least every chunk's bound E; so only keys >= max E matter, and if fewer than k
+    // remain, the lists cannot decide.
+    CSAHCA_TRACE(1);
+    const int P_eff = cdiv(V, cl.CH);
+    const int nslots = P_eff * cl.JMAX;
+    const uint64_t* cq = cl.cand + (size_t)q * cl.P * cl.JMAX;
+    uint64_t e = (int)threadIdx.x < P_eff ? cl.edge[(size_t)q * FT_MAX_P + threadIdx.x] : 0ull;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const int s = wave * 64 * KPT + 64 * j + lane;
+      kr[j] = s < nslots ? cq[s] : 0ull;
+    }
+    // the histograms of the k-th search are cleared while the loads are in flight
+    for (int i = threadIdx.x; i < 2 * NBIN; i += SEL_THREADS) (&sc.hist[0][0])[i] = 0u;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) e = umax64(e, shfl_xor_u64(e, d));
+    if (lane == 0) sc.red_or[wave] = e;
+    __syncthreads();
+    const uint64_t emax = umax64(sc.red_or[0], sc.red_or[1]);
+    uint64_t kmax = 0ull;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      kr[j] = kr[j] >= emax ? kr[j] : 0ull;
+      kmax = umax64(kmax, kr[j]);
+    }
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) kmax = umax64(kmax, shfl_xor_u64(kmax, d));
+    if (lane == 0) sc.red_and[wave] = kmax;  // (the barriers inside the compaction order it)
+    // the kept keys, compacted in slot order into LDS when few enough
+    const uint32_t total = compact_in_order<KPT, false>(
+        kr, [](uint64_t key) { return key != 0ull; },
+        [&](uint32_t pos, uint64_t key, int) {
+          if (pos < (uint32_t)SEL_COMPACT) s_keys[pos] = key;
+        },
+        sc);
+    CSAHCA_TRACE(2);
+    if (total >= (uint32_t)keff) {
+#pragma unroll
+      for (int i = 0; i < NWAVE; ++i) kmax = umax64(kmax, sc.red_and[i]);
+      // every kept key lies in [lowest kept, kmax]; emax <= the lowest, and all of them
+      // share the bits above the highest bit where emax (or 1, when every chunk listed
+      // everything) and kmax differ
+      const uint64_t lo = emax ? emax : 1ull;
+      if (total <= (uint32_t)SEL_COMPACT) {
+        uint64_t f[CPT];  // (j, thread) order is the compacted order
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) {
+          const uint32_t i = (uint32_t)(j * SEL_THREADS) + threadIdx.x;
+          f[j] = i < total ? s_keys[i] : 0ull;
+        }
+        const uint64_t K = radix_select_kth<CPT, true>(f, keff, sc, lo, kmax);  // >= emax, so >= every bound
+        CSAHCA_TRACE(3);
+        write_selected<CPT, true>(f, K, keff, k, orow, osc, sc);
+      } else {
+        const uint64_t K = radix_select_kth<KPT, true>(kr, keff, sc, lo, kmax);
+        CSAHCA_TRACE(3);
+        write_selected<KPT, false>(kr, K, keff, k, orow, osc, sc);
+      }
+      if (threadIdx.x == 0) cl.path[q] = FT_PATH_LISTS;
+      CSAHCA_TRACE(4);
+      CSAHCA_TRACE_RT(15);
+      return;
+    }
+    if (threadIdx.x == 0) cl.path[q] = FT_PATH_GROUPS;
+  }
+  // group maxima, coalesced: thread t holds groups j*SEL_THREADS + t (j < KPT).  A group's
+  // key is its maximum score key, then the lower group index: as groups are index ranges,
+  // that orders equal maxima as their best entries are ordered.
+  const uint32_t* grow = gmax + (size_t)q * NG;
   const int ng = cdiv(V, GROUP);
 #pragma unroll
-  for (int j = 0; j < KPT; ++j)
-    if (j * SEL_THREADS + (int)threadIdx.x >= ng) kr[j] = 0ull;  // not (yet) complete groups
+  for (int j = 0; j < KPT; ++j) {
+    const int gi = j * SEL_THREADS + (int)threadIdx.x;
+    kr[j] = gi < ng ? ((uint64_t)grow[gi] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)gi) : 0ull;
+  }
   // With fewer groups than K every group is a candidate (T1 = 0 keeps every usable key).
   const uint64_t T1 = keff < ng ? radix_select_kth(kr, keff, sc) : 0ull;
   // entries scoring below the T1 group's maximum cannot be among the top K
   const uint64_t T1s = T1 & 0xFFFFFFFF00000000ull;
   CSAHCA_TRACE(1);
-
   // exactly min(K, ng) groups have a maximum >= T1; list them in index order, which is
-  // (j, wave, lane) order: per-(j, wave) counts by ballot, one scan over them
-  uint32_t ngl;
-  {
-    uint64_t bal[KPT];
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      bal[j] = __ballot(kr[j] != 0ull && kr[j] >= T1);
-      if (lane == 0) sc.jw[j * NWAVE + wave] = (uint32_t)__popcll(bal[j]);
-    }
-    __syncthreads();
-    if (wave == 0) {  // exclusive scan of the KPT*NWAVE counts, four per lane
-      uint32_t c4[4], sum = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        c4[i] = sc.jw[4 * lane + i];
-        sum += c4[i];
-      }
-      const uint32_t incl = wave_incl_scan(sum);
-      uint32_t run = incl - sum;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sc.jw[4 * lane + i] = run;
-        run += c4[i];
-      }
-      if (lane == 63) sc.total = incl;
-    }
-    __syncthreads();
-    ngl = sc.total;
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      if ((bal[j] >> lane) & 1ull) {
-        const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal[j] >> 32),
-                                                         __builtin_amdgcn_mbcnt_lo((uint32_t)bal[j], 0u));
-        glist[sc.jw[j * NWAVE + wave] + below] = j * SEL_THREADS + (int)threadIdx.x;
-      }
-    }
-    __syncthreads();
-  }
+  // (j, wave, lane) order
+  const uint32_t ngl = compact_in_order<KPT, true>(
+      kr, [&](uint64_t key) { return key != 0ull && key >= T1; },
+      [&](uint32_t pos, uint64_t, int j) { glist[pos] = j * SEL_THREADS + (int)threadIdx.x; }, sc);
   CSAHCA_TRACE(2);
   // candidates, coalesced: 16 lanes read the 16 scores of one listed group; key j of lane
-  // (wave, lane) is element lane%16 of listed group wave*64 + j*4 + lane/16.  Every load
-  // is issued (clamped to valid memory) before any is used, so they overlap.
+  // (wave, lane) is element lane%16 of listed group wave*GPW + j*4 + lane/16, so that
+  // (wave, j, lane) order is index order.  Every load is issued (clamped to valid memory)
+  // before any is used, so they overlap.
   int ce[KPT];
   float cv[KPT];
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
-    const int gp = wave * 64 + j * 4 + (lane >> 4);
+    const int gp = wave * GPW + j * 4 + (lane >> 4);
     ce[j] = gp < (int)ngl ? glist[gp] * GROUP + (lane & 15) : V;
     cv[j] = srow[min(ce[j], N_c - 1)];
   }
@@ -263,35 +381,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_topk(
   }
   const uint64_t T2 = radix_select_kth(kr, keff, sc);
   CSAHCA_TRACE(3);
-  {
-    // candidate rank (index order) is wave*1024 + j*64 + lane: running count per wave
-    uint32_t off[KPT];
-    uint32_t run = 0;
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const uint64_t bl = __ballot(kr[j] != 0ull && kr[j] >= T2);
-      off[j] = run + __builtin_amdgcn_mbcnt_hi((uint32_t)(bl >> 32),
-                                               __builtin_amdgcn_mbcnt_lo((uint32_t)bl, 0u));
-      run += (uint32_t)__popcll(bl);
-    }
-    if (lane == 0) sc.scan[wave] = run;
-    __syncthreads();
-    uint32_t before = 0;
-#pragma unroll
-    for (int i = 0; i < NWAVE; ++i) before += i < wave ? sc.scan[i] : 0u;
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const uint64_t key = kr[j];
-      if (key != 0ull && key >= T2) {
-        orow[before + off[j]] = (int)key_index(key);
-        if (osc) osc[before + off[j]] = key_score((uint32_t)(key >> 32));
-      }
-    }
-  }
-  for (int i = keff + threadIdx.x; i < k; i += SEL_THREADS) {
-    orow[i] = -1;
-    if (osc) osc[i] = -INFINITY;
-  }
+  write_selected<KPT, false>(kr, T2, keff, k, orow, osc, sc);
   CSAHCA_TRACE(4);
   CSAHCA_TRACE_RT(15);
 }
@@ -301,12 +391,14 @@ __global__ __launch_bounds__(SEL_THREADS) void select_topk(
 namespace csahca {
 
 int index_select_impl(const float* scores, const uint32_t* gmax, const int* q_pos, int m, int B,
-                      int Tq, int N_c, int k, int* topk_idx, float* topk_score, hipStream_t st) {
+                      int Tq, int N_c, int k, int* topk_idx, float* topk_score, hipStream_t st,
+                      const ChunkLists* lists) {
   using namespace csahca;
   const int nq = B * Tq;
   const int NG = cdiv(N_c, GROUP);
   hipLaunchKernelGGL(select_topk, dim3((unsigned)nq), dim3(SEL_THREADS), 0, st, scores,
-                     gmax, q_pos, m, Tq, N_c, NG, k, topk_idx, topk_score);
+                     gmax, q_pos, m, Tq, N_c, NG, k, topk_idx, topk_score,
+                     lists ? *lists : ChunkLists{});
   return launch_status("lightning_index_select");
 }
 
@@ -314,9 +406,8 @@ int index_select_impl(const float* scores, const uint32_t* gmax, const int* q_po
 
 extern "C" size_t lightning_index_topk_workspace_size(int B, int Tq, int n_ih, int N_c, int k) {
   (void)n_ih;
-  (void)k;
-  if (B < 1 || Tq < 1 || N_c < 1) return 0;
-  return ws_layout((long long)B * Tq, N_c).total;
+  if (B < 1 || Tq < 1 || N_c < 1 || k < 1) return 0;
+  return ws_layout((long long)B * Tq, N_c, k, Tq == 1).total;
 }
 
 extern "C" int lightning_index_select(const float* scores, const int* q_pos, int m, int B,
@@ -329,7 +420,7 @@ extern "C" int lightning_index_select(const float* scores, const int* q_pos, int
     return fail(CSAHCA_EINVAL, "lightning_index_select: B, Tq, N_c, m and k must be >= 1");
   if (N_c > MAX_NC || k > MAX_K)
     return fail(CSAHCA_ENOTSUP, "lightning_index_select: N_c <= 262144 and k <= 1024 are built");
-  const WsLayout L = ws_layout((long long)B * Tq, N_c);
+  const WsLayout L = ws_layout((long long)B * Tq, N_c, k, Tq == 1);
   if (!workspace || ws_bytes < L.total)
     return fail(CSAHCA_EWORKSPACE, "lightning_index_select: workspace missing or too small");
   return index_select_impl(scores, (const uint32_t*)((char*)workspace + L.gkeys_off), q_pos, m, B, Tq,
@@ -351,7 +442,7 @@ int index_topk_impl(const char* name, const void* q_idx, const float* w_idx, con
     set_error("%s: topk_idx must be non-NULL", name);
     return CSAHCA_EINVAL;
   }
-  const WsLayout L = ws_layout((long long)B * Tq, N_c);
+  const WsLayout L = ws_layout((long long)B * Tq, N_c, k, Tq == 1);
   if (!workspace || ws_bytes < L.total) {
     set_error("%s: workspace missing or too small (%zu bytes needed)", name, L.total);
     return CSAHCA_EWORKSPACE;
@@ -360,8 +451,25 @@ int index_topk_impl(const char* name, const void* q_idx, const float* w_idx, con
     set_error("%s: all_scores must be 16-byte aligned", name);
     return CSAHCA_EINVAL;
   }
-  float* scores = all_scores ? all_scores : (float*)((char*)workspace + L.scores_off);
-  uint32_t* gkeys = (uint32_t*)((char*)workspace + L.gkeys_off);
+  char* ws = (char*)workspace;
+  float* scores = all_scores ? all_scores : (float*)(ws + L.scores_off);
+  uint32_t* gkeys = (uint32_t*)(ws + L.gkeys_off);
+  if (index_can_list(idx_dtype, Tq, c_I, n_ih, L.plan)) {
+    // decode: the scoring launch also writes every chunk's list; the selection launch
+    // selects from their union first
+    ChunkLists cl;
+    cl.edge = (uint64_t*)(ws + L.edge_off);
+    cl.cand = (uint64_t*)(ws + L.cand_off);
+    cl.path = (uint32_t*)(ws + L.path_off);
+    cl.k = k;
+    cl.P = L.plan.P;
+    cl.JMAX = L.plan.JMAX;
+    cl.CH = L.plan.CH;
+    st = index_score_impl(q_idx, w_idx, k_idx, idx_dtype, q_pos, m, B, Tq, n_ih, c_I, N_c, scores, gkeys,
+                          s, &cl);
+    if (st != CSAHCA_OK) return st;
+    return index_select_impl(scores, gkeys, q_pos, m, B, Tq, N_c, k, topk_idx, topk_score, s, &cl);
+  }
   st = index_score_impl(q_idx, w_idx, k_idx, idx_dtype, q_pos, m, B, Tq, n_ih, c_I, N_c, scores, gkeys, s);
   if (st != CSAHCA_OK) return st;
   return index_select_impl(scores, gkeys, q_pos, m, B, Tq, N_c, k, topk_idx, topk_score, s);
@@ -437,7 +545,7 @@ extern "C" int lightning_index_topk_noalloc(const void* q_idx, const float* w_id
   // shape checks first: the size test below needs sane B, Tq and N_c
   int st = index_check_common(q_idx, w_idx, k_idx, idx_dtype, q_pos, m, B, Tq, n_ih, c_I, N_c, k);
   if (st != CSAHCA_OK) return st;
-  const size_t need = ws_layout((long long)B * Tq, N_c).total;
+  const size_t need = ws_layout((long long)B * Tq, N_c, k, Tq == 1).total;
   if (need > CSAHCA_NOALLOC_SCRATCH_BYTES) {
     set_error("%s: the call needs %zu bytes of scratch, above the built maximum of %zu "
               "(use lightning_index_topk with a workspace)", name, need,

@@ -172,6 +172,13 @@ int csa_compress_overlap(const void* kv_a, const void* gate_a, const void* kv_b,
  *   keys n_ih in {16, 32, 64, 128} and c_I = 128 (source: "DeepSeek-V4: Anatomy of an
  *   Open-Source Frontier Model", the indexer's query-key path trained down to FP4); F32 keys
  *   need n_ih * c_I <= 4096.  1 <= k <= 1024, N_c <= 262144.
+ *
+ * Workspace: lightning_index_topk_workspace_size() bytes, caller-owned, no initial
+ * contents needed.  After a decode call that selected from chunk lists (Tq == 1,
+ * c_I == 128) the workspace's last B*Tq 32-bit words (rounded up to 256 bytes) say how
+ * each query's selection went: 1 the chunks' lists held the top k, 2 it went through the
+ * group maxima (the best entries clustered in a few chunks), 3 every usable entry was
+ * selected.
  */
 size_t lightning_index_topk_workspace_size(int B, int Tq, int n_ih, int N_c, int k);
 int lightning_index_topk(const void* q_idx, const float* w_idx, const void* k_idx,

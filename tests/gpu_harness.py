@@ -74,7 +74,7 @@ def run_index(qI, w, KI, q_pos, m, k, idx_dtype, split=False, N_c=None):
     B, Tq, n_ih, c_I = qI.shape
     N_c = KI.shape[1] if N_c is None else N_c
     ws_bytes = lib.lightning_index_topk_workspace_size(B, Tq, n_ih, N_c, k)
-    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=DEV)
     idx = torch.empty((B, Tq, k), dtype=torch.int32, device=DEV)
     sc = torch.empty((B, Tq, k), dtype=torch.float32, device=DEV)
     alls = torch.full((B, Tq, N_c), float("nan"), dtype=torch.float32, device=DEV)

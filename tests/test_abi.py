@@ -98,8 +98,14 @@ def test_indexer_validation():
     B, Tq, n_ih, c_I, N_c, k = 2, 1, 64, 128, 1000, 64
     ws = L.lightning_index_topk_workspace_size(B, Tq, n_ih, N_c, k)
     NG = -(-N_c // 16)
-    # one 32-bit maximum key per group of 16 entries, then the fp32 scores
-    assert ws == (-(-(B * NG * 4) // 256) * 256) + (-(-(B * N_c * 4) // 256) * 256)
+    up = lambda x: -(-x // 256) * 256
+    # one 32-bit maximum key per group of 16 entries, the fp32 scores; a decode call adds
+    # each chunk's bound and zero-padded list (the plan for 1000 entries and k = 64 over
+    # two queries: 4 chunks of 256, lists of up to 64 keys) and one path word per query
+    base = up(B * NG * 4) + up(B * N_c * 4)
+    assert ws == base + up(B * 128 * 8) + up(B * 4 * 64 * 8) + up(B * 4)
+    # a prefill shape has no chunk lists
+    assert L.lightning_index_topk_workspace_size(B, 3, n_ih, N_c, k) == up(3 * B * NG * 4) + up(3 * B * N_c * 4)
     args = [FAKE, FAKE, FAKE, 2, FAKE, 4, B, Tq, n_ih, c_I, N_c, k, FAKE, None, None]
     assert L.lightning_index_topk(*args, FAKE, ws - 1, None) == EWORKSPACE
     assert L.lightning_index_topk(*args, None, ws, None) == EWORKSPACE

@@ -38,7 +38,7 @@ def run_both(cfg):
         alls = torch.full((B, Tq, N_c), float("nan"), dtype=torch.float32, device=H.DEV)
         if name == "workspace":
             ws_bytes = lib.lightning_index_topk_workspace_size(B, Tq, n_ih, N_c, k)
-            ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=H.DEV)
+            ws = torch.empty(ws_bytes, dtype=torch.uint8, device=H.DEV)
             lib.lightning_index_topk(qI, w, KI, cfg.idx_dtype, q_pos, cfg.m, B, Tq, n_ih, c_I, N_c, k,
                                      idx, sc, alls, ws, ws_bytes)
         else:

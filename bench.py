@@ -453,30 +453,50 @@ def measured_copy_gbs():
     return best
 
 
+def host_cpu():
+    """The host the oracle runs on: cores this process may use, BLAS threads, CPU model."""
+    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        blas = None
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return cores, blas, model
+
+
 def cpu_baseline(wl, seconds):
-    """The oracle, as it stands, on a bounded sample of the same workload: complete steps
-    for whole sequences, repeated until about `seconds` of CPU time is spent."""
+    """The oracle, as it stands, on a bounded sample of the same workload, repeated until
+    about `seconds` of CPU time is spent.  Decode: complete steps of whole sequences.  A
+    prefill chunk: the pooling of the chunk's new blocks (timed once, its share added per
+    query) and complete index / top-k / CSA / HCA passes for queries spread over the chunk."""
     import numpy as np
-    import torch
 
     import oracle
     from synthgen.configs import BF16
 
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
-    except Exception:  # noqa: BLE001
-        threads = len(os.sched_getaffinity(0))
+    cores, blas, model = host_cpu()
     cfg, prob = wl.cfg, wl.prob
-    if wl.Tq != 1:
-        return None
-    n, c, W = wl.n, cfg.c, cfg.W
-    p = n - 1
+    n, c, W, Tq = wl.n, cfg.c, cfg.W, wl.Tq
 
     def codes(t):
         a = t.detach().cpu().numpy()
         return a.view(np.uint16) if a.dtype == np.int16 else a
 
+    def host(**extra):
+        return {"cores": cores, "blas_threads": blas, "cpu_model": model, "kind": "oracle", **extra}
+
+    if Tq != 1:
+        return prefill_cpu_baseline(wl, seconds, codes, host)
+    p = n - 1
     # inputs of each sequence, decoded once (input preparation, not timed)
     seqs = []
     for b in range(cfg.B):
@@ -521,9 +541,63 @@ def cpu_baseline(wl, seconds):
         el = time.perf_counter() - t0
         if el >= seconds:
             break
-    return {"value": done / el, "unit": "query-tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} complete decode steps of single sequences of this workload "
-                      f"({cfg.B} distinct sequences cycled), {el:.1f} s, NumPy fp64"}
+    return {"value": done / el, "unit": "query-tokens/s", **host(
+        sample=f"{done} complete decode steps of single sequences of this workload "
+               f"({cfg.B} distinct sequences cycled), {el:.1f} s, NumPy fp64")}
+
+
+def prefill_cpu_baseline(wl, seconds, codes, host):
+    """Oracle timing on a prefill chunk: the chunk's pooling once, then whole query passes
+    (scores over every visible entry, top-k, CSA and HCA attention) for queries spread
+    evenly over the chunk until the time is spent; query-tokens/s counts the pooling at
+    its share per query."""
+    import numpy as np
+
+    import oracle
+    from synthgen.configs import BF16
+
+    cfg, prob = wl.cfg, wl.prob
+    n, W, Tq = wl.n, cfg.W, wl.Tq
+    n0 = n - Tq
+    b = 0
+    X = oracle.decode(codes(prob["X_csa"][b]), BF16)     # old context and chunk (shared raw rows)
+    Cs = oracle.decode(codes(wl.rep[0]["C_csa"][b]), BF16)
+    Ch = oracle.decode(codes(wl.rep[0]["C_hca"][b]), BF16)
+    Zc = oracle.decode(codes(prob["Z_csa"][b]), BF16)
+    Zh = oracle.decode(codes(prob["Z_hca"][b]), BF16)
+    qI = oracle.decode(codes(prob["qI"][b]), cfg.idx_dtype)
+    w = prob["w"][b].cpu().numpy()
+    KI = oracle.decode(codes(prob["KI"][b]), cfg.idx_dtype)
+    Q = oracle.decode(codes(prob["Q_csa"][b]), BF16)
+    # the chunk's new blocks, pooled once
+    t0 = time.perf_counter()
+    for m, Z, C in ((cfg.m, Zc, Cs), (cfg.m_hca, Zh, Ch)):
+        f = n0 // m
+        C[f:n // m] = oracle.pool(X[f * m:(n // m) * m], Z[f * m:(n // m) * m], m)
+    t_pool = time.perf_counter() - t0
+    order = np.linspace(0, Tq - 1, 64).astype(int)
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        for t in order:
+            p = n0 + int(t)
+            V = oracle.visible(p, cfg.m, Cs.shape[0])
+            s = oracle.index_scores(qI[t], w[t], KI, V)
+            sel = oracle.topk(s, cfg.k)
+            oracle.attend(Q[t], oracle.csa_rows(Cs, sel, X, 0, p, W), wl.scale)
+            oracle.attend(Q[t], oracle.hca_rows(Ch, cfg.m_hca, X, 0, p, W), wl.scale)
+            done += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    per_query = el / done + t_pool / Tq
+    return {"value": 1.0 / per_query, "unit": "query-tokens/s", **host(
+        sample=f"{done} complete query passes (index over up to {Cs.shape[0]} entries, top-{cfg.k}, "
+               f"CSA and HCA attention) of the {Tq}-token chunk, queries spread evenly over it, "
+               f"{el:.1f} s; plus the chunk's pooling ({t_pool:.1f} s) at its share per query; "
+               f"NumPy fp64")}
 
 
 def overlap_pool(cfg, reps, cpu_seconds, no_cpu):
@@ -605,7 +679,7 @@ def overlap_pool(cfg, reps, cpu_seconds, no_cpu):
             if el >= cpu_seconds:
                 break
         cpu = {"value": round(done * (4 * c + c / m) * es / el / 1e9, 3), "unit": "GB/s",
-               "cores": torch.get_num_threads(), "kind": "oracle",
+               **dict(zip(("cores", "blas_threads", "cpu_model"), host_cpu())), "kind": "oracle",
                "sample": f"{done} tokens in {ntok}-token slices of one sequence, {el:.1f} s, "
                          f"NumPy fp64 (bytes counted at the GPU's storage width)"}
     gbs = nbytes / sec / 1e9
@@ -663,7 +737,7 @@ def pool_bench(cfg, reps, cpu_seconds, no_cpu):
             if el >= cpu_seconds:
                 break
         cpu = {"value": round(done * (2 * c + c / mm) * es / el / 1e9, 3), "unit": "GB/s",
-               "cores": torch.get_num_threads(), "kind": "oracle",
+               **dict(zip(("cores", "blas_threads", "cpu_model"), host_cpu())), "kind": "oracle",
                "sample": f"{done} tokens in {ntok}-token slices of one sequence, m = {mm}, "
                          f"{el:.1f} s, NumPy fp64 (bytes counted at the GPU's storage width)"}
     for l in layers:
@@ -792,7 +866,7 @@ def kv_append(cfg, reps, cpu_seconds, no_cpu):
             done += 1
         per = sum(c * es * (2 * ntok + ntok // cc["m"] + 2 * min(ntok, cc["R"])) for cc in caches)
         cpu = {"value": round(done * per / el / 1e9, 4), "unit": "GB/s",
-               "cores": torch.get_num_threads(), "kind": "oracle",
+               **dict(zip(("cores", "blas_threads", "cpu_model"), host_cpu())), "kind": "oracle",
                "sample": f"{done} appends of {ntok} tokens to the CSA and HCA simulators of one "
                          f"sequence, {el:.1f} s, NumPy fp64 (bytes counted at the GPU's storage "
                          f"width)"}
@@ -875,7 +949,7 @@ def gop_bench(cfg, reps, cpu_seconds, no_cpu):
             oracle.grouped_out_proj(Oc, Wc)
             done += tk
         el = time.perf_counter() - t0
-        cpu = {"value": round(done / el, 2), "unit": "tokens/s", "cores": torch.get_num_threads(),
+        cpu = {"value": round(done / el, 2), "unit": "tokens/s", **dict(zip(("cores", "blas_threads", "cpu_model"), host_cpu())),
                "kind": "oracle", "sample": f"{done} tokens in calls of {tk}, {el:.1f} s, NumPy fp64"}
     line = {
         "metric": "grouped output projection throughput (tokens/s)",
@@ -1046,7 +1120,7 @@ def main():
         roofline["frac_of_copy_ceiling"] = round(roofline["achieved"] / cg, 4)
 
     cpu = None
-    if not args.no_cpu_baseline and decode:
+    if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, args.cpu_seconds)
 
     line = {

@@ -12,7 +12,10 @@ import os
 F32, BF16, FP8_E4M3FN = 0, 1, 2
 OK, EINVAL, ENOTSUP, EWORKSPACE, ELAUNCH = 0, -1, -2, -3, -4
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsahca.so")
+# CSAHCA_LIB selects another build of the same library (the host-sanitizer build in its
+# tests); by default the library next to this file
+LIB_PATH = os.environ.get("CSAHCA_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                        "libcsahca.so")
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int

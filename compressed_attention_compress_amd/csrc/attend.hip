@@ -25,6 +25,8 @@
 //     accumulator produced it; E^T comes from the same LDS tile through the gfx950
 //     transpose read (ds_read_b64_tr_b16), two reads per MFMA.
 // float32 path: plain FMA over LDS-resident scores (small heads only).
+#include <mutex>
+
 #include "common.hpp"
 
 namespace {
@@ -1017,13 +1019,15 @@ Plan make_plan(int B, int Tq, int n_h, int n_slots_c, int W, bool csa) {
 
 template <int NW, int NS, bool CSA, bool CS>
 int launch_attend(const Plan& P, const AttnArgs& A, hipStream_t st) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    if (hipFuncSetAttribute((const void*)attend_bf16<NW, NS, CSA, CS>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 1024) != hipSuccess)
-      return csahca::fail(CSAHCA_ELAUNCH, "attend: cannot raise the LDS limit");
-    attr_set = true;
-  }
+  // raise the kernel's dynamic LDS limit once per process, whichever thread calls first
+  // (the attribute belongs to the kernel, for every device)
+  static std::once_flag once;
+  static hipError_t attr = hipSuccess;
+  std::call_once(once, [] {
+    attr = hipFuncSetAttribute((const void*)attend_bf16<NW, NS, CSA, CS>,
+                               hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 1024);
+  });
+  if (attr != hipSuccess) return csahca::fail(CSAHCA_ELAUNCH, "attend: cannot raise the LDS limit");
   hipLaunchKernelGGL((attend_bf16<NW, NS, CSA, CS>), dim3((unsigned)(P.per_xcd * 8)),
                      dim3(NW * 64), P.lds, st, A);
   return CSAHCA_OK;

@@ -112,14 +112,20 @@ class Workload:
             gn = torch.Generator(device=dev).manual_seed(77)
             self.g_kv = torch.rand((c,), generator=gn, device=dev) + 0.5
             self.g_q = torch.rand((c,), generator=gn, device=dev) + 0.5
-            # normalised, rotated window rows (positions n - Tq - W + 1 .. n - 1) and queries
+            # normalised, rotated window rows (positions n - Tq - W + 1 .. n - 1): a row is
+            # normalised once, when its token arrives; the rows of earlier tokens are made
+            # here (untimed), the step's own Tq rows inside the step.  The queries are
+            # normalised by the attention kernel as it loads them.
             self.nr_wpos0 = max(0, n - self.Tq - cfg.W + 1)
             self.nr_L = n - self.nr_wpos0
             self.nr_win_pos = torch.full((B,), self.nr_wpos0, dtype=torch.int32, device=dev)
+            self.nr_new_pos = torch.full((B,), n - self.Tq, dtype=torch.int32, device=dev)
             self.nr_win = {l: torch.empty((B, self.nr_L, c), dtype=et, device=dev)
                            for l in self.layers}
-            self.nr_q = {l: torch.empty((B, self.Tq, cfg.n_h, c), dtype=et, device=dev)
-                         for l in self.layers}
+            for l in self.layers:
+                lib.csahca_norm_rope(prob[f"X_{l}"][:, self.nr_wpos0:], self.nr_win[l], self.g_kv,
+                                     self.nr_win_pos, B, self.nr_L, 1, c, 1, self.NR_D, self.NR_EPS,
+                                     self.NR_THETA, 1, dt, x_bstride=n * c, y_bstride=self.nr_L * c)
         base = {}
         for l in self.layers:
             m = cfg.m if l == "csa" else cfg.m_hca
@@ -170,7 +176,7 @@ class Workload:
         cfg, lib, prob = self.cfg, self.lib, self.prob
         B, c, n = cfg.B, cfg.c, self.n
         layers = self.layers if layers is None else layers
-        if len(layers) == 2 and not self.nr:
+        if len(layers) == 2:
             # both caches in one call (one launch at decode)
             sides = []
             for l in ("csa", "hca"):
@@ -178,9 +184,17 @@ class Workload:
                 first_blk = self.n_old // m
                 tok0 = first_blk * m
                 C = self.rep[r][f"C_{l}"]
-                sides += [prob[f"X_{l}"][:, tok0:], prob[f"Z_{l}"][:, tok0:], C[:, first_blk:],
-                          n - tok0, m, n * c, (n // m) * c]
-            lib.csahca_compress_pair(*sides, B, c, cfg.dtype)
+                X, Z = prob[f"X_{l}"][:, tok0:], prob[f"Z_{l}"][:, tok0:]
+                if self.nr:
+                    sides += [X, Z, self.g_kv, C[:, first_blk:], n - tok0, m, first_blk, n * c,
+                              (n // m) * c]
+                else:
+                    sides += [X, Z, C[:, first_blk:], n - tok0, m, n * c, (n // m) * c]
+            if self.nr:
+                lib.csahca_compress_pair_norm_rope(*sides, B, c, self.NR_D, self.NR_EPS, self.NR_THETA,
+                                                   cfg.dtype)
+            else:
+                lib.csahca_compress_pair(*sides, B, c, cfg.dtype)
             return
         for l in layers:
             m = cfg.m if l == "csa" else cfg.m_hca
@@ -221,40 +235,45 @@ class Workload:
                                        cfg.B, self.Tq, cfg.n_ih, cfg.c_I, self.N_c, cfg.k,
                                        self.scores, self.iws, self.iws_b)
 
-    def norm_rope_rows(self, r, l):
-        """Queries and window rows of layer l through RMSNorm + partial RoPE; returns the
-        (queries, window source, win_pos, L) the attention call reads."""
-        cfg, lib, rp, prob = self.cfg, self.lib, self.rep[r], self.prob
+    def window_rows(self, r, l):
+        """The window source of layer l the attention call reads: (rows, win_pos, L).  With
+        norm_rope, the step's own Tq tokens enter the normalised window rows first."""
+        cfg, lib, prob = self.cfg, self.lib, self.prob
         B, c, n = cfg.B, cfg.c, self.n
         if not self.nr:
-            return rp[f"Q_{l}"], prob[f"X_{l}"], self.win_pos, n
-        lib.csahca_norm_rope(rp[f"Q_{l}"], self.nr_q[l], self.g_q, self.q_pos, B, self.Tq, cfg.n_h, c,
-                             1, self.NR_D, self.NR_EPS, self.NR_THETA, 1, cfg.dtype)
-        lib.csahca_norm_rope(prob[f"X_{l}"][:, self.nr_wpos0:], self.nr_win[l], self.g_kv,
-                             self.nr_win_pos, B, self.nr_L, 1, c, 1, self.NR_D, self.NR_EPS,
-                             self.NR_THETA, 1, cfg.dtype, x_bstride=n * c, y_bstride=self.nr_L * c)
-        return self.nr_q[l], self.nr_win[l], self.nr_win_pos, self.nr_L
+            return prob[f"X_{l}"], self.win_pos, n
+        Tq, L = self.Tq, self.nr_L
+        lib.csahca_norm_rope(prob[f"X_{l}"][:, n - Tq:], self.nr_win[l][:, L - Tq:], self.g_kv,
+                             self.nr_new_pos, B, Tq, 1, c, 1, self.NR_D, self.NR_EPS, self.NR_THETA,
+                             1, cfg.dtype, x_bstride=n * c, y_bstride=L * c)
+        return self.nr_win[l], self.nr_win_pos, L
 
     def attend(self, r, layers=None):
         cfg, lib, rp, prob = self.cfg, self.lib, self.rep[r], self.prob
         B, c, n = cfg.B, cfg.c, self.n
         sk = self.sink
         layers = self.layers if layers is None else layers
+        # with norm_rope the queries' RMSNorm + RoPE runs inside the attention kernel
+        nrq = (self.g_q, 1, self.NR_D, self.NR_EPS, self.NR_THETA) if self.nr else None
         if "csa" in layers:
-            q, win, wpos, L = self.norm_rope_rows(r, "csa")
-            args = (q, rp["C_csa"], self.idx, win, wpos, self.q_pos, B,
+            win, wpos, L = self.window_rows(r, "csa")
+            args = (rp["Q_csa"], rp["C_csa"], self.idx, win, wpos, self.q_pos, B,
                     self.Tq, cfg.n_h, c, self.N_c, cfg.k, L, cfg.W, self.scale)
             tail = (cfg.dtype, self.out["csa"], None, self.cws, self.cws_b)
-            if sk is None:
+            if nrq is not None:
+                lib.csa_attend_ex(*args, sk, *nrq, *tail)
+            elif sk is None:
                 lib.csa_attend(*args, *tail)
             else:
                 lib.csa_attend_sink(*args, sk, *tail)
         if "hca" in layers:
-            q, win, wpos, L = self.norm_rope_rows(r, "hca")
-            args = (q, rp["C_hca"], win, wpos, self.q_pos, cfg.m_hca, B,
+            win, wpos, L = self.window_rows(r, "hca")
+            args = (rp["Q_hca"], rp["C_hca"], win, wpos, self.q_pos, cfg.m_hca, B,
                     self.Tq, cfg.n_h, c, self.N_h, L, cfg.W, self.scale)
             tail = (cfg.dtype, self.out["hca"], None, self.hws, self.hws_b)
-            if sk is None:
+            if nrq is not None:
+                lib.hca_attend_ex(*args, sk, *nrq, *tail)
+            elif sk is None:
                 lib.hca_attend(*args, *tail)
             else:
                 lib.hca_attend_sink(*args, sk, *tail)
@@ -326,8 +345,8 @@ class Workload:
             att = rows * c * e + 2 * B * Tq * cfg.n_h * c * e
             detail["hca_attend"] = att
             total += att
-        if self.nr:  # queries and window rows read and written once more
-            nrb = len(self.layers) * 2 * B * (Tq * cfg.n_h + self.nr_L) * c * e
+        if self.nr:  # the step's new window rows read and written once (queries: in attention)
+            nrb = len(self.layers) * 2 * B * Tq * c * e
             detail["norm_rope_rows"] = nrb
             total += nrb
         return total, detail
@@ -1145,7 +1164,7 @@ def main():
                                "two: HCA attention concurrent with the CSA indexer and attention"),
                    **({"attention_sink": "per-head, N(0, 2^2)"} if args.sink else {}),
                    **({"indexer_keys": "MX FP4 (E2M1, E8M0 per 32), FP8 queries"} if args.fp4_keys else {}),
-                   **({"norm_rope": "RMSNorm + RoPE on the last 64 dims: entries, queries, window"}
+                   **({"norm_rope": "RMSNorm + RoPE on the last 64 dims: entries when pooled, new window rows, queries inside attention"}
                       if args.norm_rope else {})},
         "hbm_gbs": round(abytes / sec / 1e9, 1),
         "hbm_frac": round(abytes / sec / 1e9 / HBM_PEAK_GBS, 4),

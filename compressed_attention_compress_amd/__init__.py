@@ -28,6 +28,8 @@ _SIGNATURES = {
     "hca_compress": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _LL, _LL, _P]),
     "csahca_compress_pair": (_I, [_P, _P, _P, _I, _I, _LL, _LL, _P, _P, _P, _I, _I, _LL, _LL,
                                   _I, _I, _I, _P]),
+    "csahca_compress_pair_norm_rope": (_I, [_P, _P, _P, _P, _I, _I, _LL, _LL, _LL, _P, _P, _P, _P,
+                                            _I, _I, _LL, _LL, _LL, _I, _I, _I, _F, _F, _I, _P]),
     "csa_compress_overlap": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _LL, _LL, _P]),
     "csahca_compress_norm_rope": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _LL, _I, _F, _F, _I,
                                        _LL, _LL, _P]),
@@ -58,6 +60,10 @@ _SIGNATURES = {
                              _P, _P, _P, _SZ, _P]),
     "hca_attend_sink": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _I, _P,
                              _P, _P, _SZ, _P]),
+    "csa_attend_ex": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _I,
+                           _I, _F, _F, _I, _P, _P, _P, _SZ, _P]),
+    "hca_attend_ex": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _I, _I,
+                           _F, _F, _I, _P, _P, _P, _SZ, _P]),
     "csahca_last_error": (ctypes.c_char_p, []),
     "csahca_version": (_I, []),
 }
@@ -144,6 +150,16 @@ def csahca_compress_pair(kv_a, gate_a, out_a, n_a, m_a, in_bstride_a, out_bstrid
         _ptr(kv_a), _ptr(gate_a), _ptr(out_a), n_a, m_a, in_bstride_a, out_bstride_a, _ptr(kv_b),
         _ptr(gate_b), _ptr(out_b), n_b, m_b, in_bstride_b, out_bstride_b, B, c, dtype,
         _stream(stream)))
+
+
+def csahca_compress_pair_norm_rope(kv_a, gate_a, gamma_a, out_a, n_a, m_a, entry0_a, in_bstride_a,
+                                   out_bstride_a, kv_b, gate_b, gamma_b, out_b, n_b, m_b, entry0_b,
+                                   in_bstride_b, out_bstride_b, B, c, d_rope, eps, theta, dtype,
+                                   stream=None):
+    return _check("csahca_compress_pair_norm_rope", load().csahca_compress_pair_norm_rope(
+        _ptr(kv_a), _ptr(gate_a), _ptr(gamma_a), _ptr(out_a), n_a, m_a, entry0_a, in_bstride_a,
+        out_bstride_a, _ptr(kv_b), _ptr(gate_b), _ptr(gamma_b), _ptr(out_b), n_b, m_b, entry0_b,
+        in_bstride_b, out_bstride_b, B, c, d_rope, float(eps), float(theta), dtype, _stream(stream)))
 
 
 def csahca_compress_norm_rope(kv, gate, pos_bias, gamma, out, B, n, c, m, entry0, d_rope, eps,
@@ -268,3 +284,21 @@ def hca_attend_sink(q, ckv, win_kv, win_pos, q_pos, m, B, Tq, n_h, c, N_h, L, W,
         _ptr(q), _ptr(ckv), _ptr(win_kv), _ptr(win_pos), _ptr(q_pos), m, B, Tq, n_h, c, N_h, L, W,
         float(scale), _ptr(sink), dtype, _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
         _stream(stream)))
+
+
+def csa_attend_ex(q, ckv, topk_idx, win_kv, win_pos, q_pos, B, Tq, n_h, c, N_c, k, L, W, scale,
+                  sink, q_gamma, q_norm, d_rope, eps, theta, dtype, out, lse, workspace, ws_bytes,
+                  stream=None):
+    return _check("csa_attend_ex", load().csa_attend_ex(
+        _ptr(q), _ptr(ckv), _ptr(topk_idx), _ptr(win_kv), _ptr(win_pos), _ptr(q_pos), B, Tq,
+        n_h, c, N_c, k, L, W, float(scale), _ptr(sink), _ptr(q_gamma), q_norm, d_rope, float(eps),
+        float(theta), dtype, _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def hca_attend_ex(q, ckv, win_kv, win_pos, q_pos, m, B, Tq, n_h, c, N_h, L, W, scale, sink,
+                  q_gamma, q_norm, d_rope, eps, theta, dtype, out, lse, workspace, ws_bytes,
+                  stream=None):
+    return _check("hca_attend_ex", load().hca_attend_ex(
+        _ptr(q), _ptr(ckv), _ptr(win_kv), _ptr(win_pos), _ptr(q_pos), m, B, Tq, n_h, c, N_h, L, W,
+        float(scale), _ptr(sink), _ptr(q_gamma), q_norm, d_rope, float(eps), float(theta), dtype,
+        _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)))

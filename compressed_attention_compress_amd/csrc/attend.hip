@@ -27,7 +27,7 @@
 // float32 path: plain FMA over LDS-resident scores (small heads only).
 #include <mutex>
 
-#include "common.hpp"
+#include "normrope.hpp"
 
 namespace {
 
@@ -81,6 +81,11 @@ struct AttnArgs {
   uint16_t* opart;  // [nq, n_splits, n_h, C] partial outputs O/l, scaled float16
   float* mlpart;    // [nq, n_splits, n_h, 4] running max (log2 units), sum, scale, pad
   const float* sink;  // [n_h] attention sink logits (natural-log units) or null
+  // RMSNorm + partial RoPE of the queries as they are loaded (qnr; normrope.hpp), gain
+  // nullable
+  const float* q_gamma;
+  int qnr, d_rope;
+  float nr_eps, nr_theta;
   int B, Tq, n_h, Nc, k, L, W, m;
   int is_csa;
   int n_slots_c;  // compressed slots: k (CSA) or Nc (HCA)
@@ -136,15 +141,17 @@ CSAHCA_DEV void wait_tiles(int inflight) {
 // (16 bytes each), the per-head factors alpha [NW][16], one flag per wave, and at the end
 // the running maxima and sums [NW][16], partial row maxima [NW][NW * 16] and the sums of
 // the rounded weights [NW][16].
-constexpr size_t xch_bytes(int NW, int TPI) {
+__host__ __device__ constexpr size_t xch_bytes(int NW, int TPI) {
   return (size_t)TPI * NW * 64 * 16 + (size_t)NW * 16 * 4 + 64 + 3 * (size_t)NW * 16 * 4 +
          (size_t)NW * NW * 16 * 4;
 }
 
-size_t attend_lds_bytes(int NS, int NW, int RS, bool csa, bool cs) {
+// ... and with the query RMSNorm + RoPE, its gains [C]
+size_t attend_lds_bytes(int NS, int NW, int RS, bool csa, bool cs, bool nr) {
   const int TPI = NS >= 4 ? 2 : 1;
-  return (size_t)NS * TILE * ROWB + (size_t)NS * NW * sizeof(uint32_t) +
-         (csa ? (size_t)RS * sizeof(int) : 0) + (cs ? xch_bytes(NW, TPI) : 0);
+  const size_t x = csahca::align_up((size_t)NS * TILE * ROWB + (size_t)NS * NW * sizeof(uint32_t) +
+                                        (csa ? (size_t)RS * sizeof(int) : 0), 16);
+  return x + (cs ? xch_bytes(NW, TPI) : 0) + (nr ? (size_t)C * sizeof(float) : 0);
 }
 
 // bits [lo, hi) of a 32-bit mask, the bounds relative to `base` and clipped to [0, 32)
@@ -202,6 +209,8 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && NS == 2) ? 2 : 1) void attend_
   // that the pointer keeps its LDS address space (ds_read / ds_write, not flat accesses,
   // whose waits would also drain the row DMA in flight).
   uint8_t* xch = smem + ((NS * TILE * ROWB + NS * NW * 4 + (CSA ? a.RS * 4 : 0) + 15) & ~15);
+  // the query norm gains after the exchange area
+  float* s_gain = reinterpret_cast<float*>(xch + (CS ? xch_bytes(NW, NS >= 4 ? 2 : 1) : 0));
 
   // XCD-aware order: consecutive work items (the head groups of one row range first) run
   // on the same XCD, so the rows they share are read from HBM once into that XCD's L2.
@@ -318,6 +327,13 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && NS == 2) ? 2 : 1) void attend_
   // Start-up, ordered so that independent latencies overlap: the Q fragments, then (CSA)
   // this split's entry indices or (HCA, when the first tiles hold only compressed rows)
   // the first tiles themselves, while the positions arrive.
+  // query norm gains, this thread's share of the C channels (to LDS once Q has arrived)
+  constexpr int GPT = C / (NW * 64);
+  float gq[GPT];
+  if (a.qnr) {
+#pragma unroll
+    for (int i = 0; i < GPT; ++i) gq[i] = a.q_gamma ? a.q_gamma[(int)threadIdx.x + i * NW * 64] : 1.f;
+  }
   bf16x8 qf[KS];
   {
     const uint16_t* qp = a.q + (qrow * a.n_h + h0 + row16) * C + g * (C / 4);
@@ -364,6 +380,54 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && NS == 2) ? 2 : 1) void attend_
     for (int tt = 0; tt < TPI && tt < ntile; ++tt) issue(tt, false);
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(qf[ks]));
+  if (a.qnr) {
+#pragma unroll
+    for (int i = 0; i < GPT; ++i) s_gain[(int)threadIdx.x + i * NW * 64] = gq[i];
+    lds_reads_done_barrier();
+    // RMSNorm of the query row (this lane holds channels g*C/4 .. +C/4 of head h0+row16,
+    // its three partners the rest), then RoPE on the last d_rope channels.  The angles
+    // depend only on the wave's query position: lane i < d_rope/2 forms pair i's, the lanes
+    // holding rotated channels fetch theirs.
+    float ss = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const u32x4 w4 = __builtin_bit_cast(u32x4, qf[ks]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float lo = __uint_as_float(w4[e] << 16), hi = __uint_as_float(w4[e] & 0xFFFF0000u);
+        ss = fmaf(lo, lo, ss);
+        ss = fmaf(hi, hi, ss);
+      }
+    }
+    ss = sum_over_row_groups(ss);
+    const float inv = 1.0f / sqrtf(ss / (float)C + a.nr_eps);
+    const int P = a.d_rope / 2;   // <= 64 rotated pairs (the host checks)
+    const int r0 = C - a.d_rope;  // first rotated channel
+    float cs = 1.f, sn = 0.f;
+    if (lane < P) csahca::rope_cos_sin(p, csahca::rope_freq(lane, a.d_rope, a.nr_theta), cs, sn);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int d0 = g * (C / 4) + 8 * ks;
+      const u32x4 w4 = __builtin_bit_cast(u32x4, qf[ks]);
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[2 * e] = __uint_as_float(w4[e] << 16) * inv * s_gain[d0 + 2 * e];
+        v[2 * e + 1] = __uint_as_float(w4[e] & 0xFFFF0000u) * inv * s_gain[d0 + 2 * e + 1];
+      }
+      if (3 * (C / 4) + 8 * ks + 8 > r0) {  // some lane group holds rotated channels here
+        const int i0 = (d0 - r0) / 2;        // negative outside the rotated channels
+#pragma unroll
+        for (int q2 = 0; q2 < 4; ++q2) {
+          const int src = min(max(i0 + q2, 0), max(P - 1, 0));
+          const float cq = __shfl(cs, src, 64), sq = __shfl(sn, src, 64);
+          if (d0 >= r0) csahca::rope_apply(v[2 * q2], v[2 * q2 + 1], cq, sq);
+        }
+      }
+      qf[ks] = __builtin_bit_cast(bf16x8, u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                                pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])});
+    }
+  }
   for (int tt = TPI; tt < NS && tt < ntile; ++tt) issue(tt, false);
 
   // l_run: mass of the fp32 weights (log-sum-exp, split records); lq_run: sum of the same
@@ -1013,7 +1077,7 @@ Plan make_plan(int B, int Tq, int n_h, int n_slots_c, int W, bool csa) {
   // column split only with the 2-tile ring (many workgroups, one tile per iteration):
   // with two tiles per iteration the exchange costs what the fewer transpose reads save
   P.CS = P.Tg == 1 && (P.NW == 2 || P.NW == 4) && P.NS == 2;
-  P.lds = attend_lds_bytes(P.NS, P.NW, P.RS, csa, P.CS);
+  P.lds = attend_lds_bytes(P.NS, P.NW, P.RS, csa, P.CS, true);  // room for the query norm gains
   return P;
 }
 
@@ -1084,10 +1148,40 @@ int check_attend(const char* name, const void* q, const void* ckv, const void* w
   return CSAHCA_OK;
 }
 
+// RMSNorm + partial RoPE of the queries inside the attention kernel
+struct NrArgs {
+  const float* q_gamma = nullptr;
+  int q_norm = 0, d_rope = 0;
+  float eps = 0.f, theta = 1.f;
+};
+
+int check_nr(const char* name, const NrArgs& nr, int dtype) {
+  using namespace csahca;
+  if (nr.q_norm == 0) return CSAHCA_OK;
+  if (nr.q_norm != 1) {
+    set_error("%s: q_norm must be 0 or 1", name);
+    return CSAHCA_EINVAL;
+  }
+  if (dtype != CSAHCA_BF16) {
+    set_error("%s: RMSNorm + RoPE inside attention needs bfloat16", name);
+    return CSAHCA_ENOTSUP;
+  }
+  if (nr.d_rope < 0 || nr.d_rope % 8 != 0 || nr.d_rope > 128) {
+    set_error("%s: d_rope must be a multiple of 8 in [0, 128]", name);
+    return CSAHCA_EINVAL;
+  }
+  if (!(nr.eps >= 0.f) || !(nr.theta > 0.f) || nr.theta == INFINITY || nr.eps == INFINITY) {
+    set_error("%s: need eps >= 0 and theta > 0, both finite", name);
+    return CSAHCA_EINVAL;
+  }
+  return CSAHCA_OK;
+}
+
 int attend_impl(const char* name, bool csa, const void* q, const void* ckv, const int* topk,
                 const void* win_kv, const int* win_pos, const int* q_pos, int m, int B, int Tq,
                 int n_h, int c, int N, int k, int L, int W, float scale, const float* sink,
-                int dtype, void* out, float* lse, void* workspace, size_t ws_bytes, hipStream_t st) {
+                const NrArgs& nr, int dtype, void* out, float* lse, void* workspace, size_t ws_bytes,
+                hipStream_t st) {
   using namespace csahca;
   const int n_slots_c = csa ? k : N;
   if (dtype == CSAHCA_F32) {
@@ -1136,6 +1230,11 @@ int attend_impl(const char* name, bool csa, const void* q, const void* ckv, cons
   A.out = (uint16_t*)out;
   A.lse = lse;
   A.sink = sink;
+  A.q_gamma = nr.q_gamma;
+  A.qnr = nr.q_norm;
+  A.d_rope = nr.d_rope;
+  A.nr_eps = nr.eps;
+  A.nr_theta = nr.theta;
   A.opart = P.n_splits > 1 ? (uint16_t*)workspace : nullptr;
   A.mlpart = P.n_splits > 1 ? (float*)((char*)workspace + P.opart_bytes) : nullptr;
   A.B = B;
@@ -1195,11 +1294,12 @@ namespace {
 
 int csa_entry(const char* name, const void* q, const void* ckv, const int* topk_idx,
               const void* win_kv, const int* win_pos, const int* q_pos, int B, int Tq, int n_h,
-              int c, int N_c, int k, int L, int W, float scale, const float* sink, int dtype,
-              void* out, float* lse, void* workspace, size_t ws_bytes, void* stream) {
+              int c, int N_c, int k, int L, int W, float scale, const float* sink, const NrArgs& nr,
+              int dtype, void* out, float* lse, void* workspace, size_t ws_bytes, void* stream) {
   using namespace csahca;
   int rc = check_attend(name, q, ckv, win_kv, win_pos, q_pos, B, Tq, n_h, c, N_c, L, W, dtype, out, k);
   if (rc != CSAHCA_OK) return rc;
+  if ((rc = check_nr(name, nr, dtype)) != CSAHCA_OK) return rc;
   if (!topk_idx || k < 1) {
     set_error("%s: topk_idx must be non-NULL and k >= 1", name);
     return CSAHCA_EINVAL;
@@ -1209,16 +1309,17 @@ int csa_entry(const char* name, const void* q, const void* ckv, const int* topk_
     return CSAHCA_EINVAL;
   }
   return attend_impl(name, true, q, ckv, topk_idx, win_kv, win_pos, q_pos, 1, B, Tq, n_h, c, N_c, k,
-                     L, W, scale, sink, dtype, out, lse, workspace, ws_bytes, (hipStream_t)stream);
+                     L, W, scale, sink, nr, dtype, out, lse, workspace, ws_bytes, (hipStream_t)stream);
 }
 
 int hca_entry(const char* name, const void* q, const void* ckv, const void* win_kv,
               const int* win_pos, const int* q_pos, int m, int B, int Tq, int n_h, int c, int N_h,
-              int L, int W, float scale, const float* sink, int dtype, void* out, float* lse,
-              void* workspace, size_t ws_bytes, void* stream) {
+              int L, int W, float scale, const float* sink, const NrArgs& nr, int dtype, void* out,
+              float* lse, void* workspace, size_t ws_bytes, void* stream) {
   using namespace csahca;
   int rc = check_attend(name, q, ckv, win_kv, win_pos, q_pos, B, Tq, n_h, c, N_h, L, W, dtype, out, N_h);
   if (rc != CSAHCA_OK) return rc;
+  if ((rc = check_nr(name, nr, dtype)) != CSAHCA_OK) return rc;
   if (m < 1) {
     set_error("%s: m must be >= 1", name);
     return CSAHCA_EINVAL;
@@ -1228,7 +1329,7 @@ int hca_entry(const char* name, const void* q, const void* ckv, const void* win_
     return CSAHCA_EINVAL;
   }
   return attend_impl(name, false, q, ckv, nullptr, win_kv, win_pos, q_pos, m, B, Tq, n_h, c, N_h, N_h,
-                     L, W, scale, sink, dtype, out, lse, workspace, ws_bytes, (hipStream_t)stream);
+                     L, W, scale, sink, nr, dtype, out, lse, workspace, ws_bytes, (hipStream_t)stream);
 }
 
 }  // namespace
@@ -1239,7 +1340,7 @@ extern "C" int csa_attend(const void* q, const void* ckv, const int* topk_idx,
                           int dtype, void* out, float* lse, void* workspace, size_t ws_bytes,
                           void* stream) {
   return csa_entry("csa_attend", q, ckv, topk_idx, win_kv, win_pos, q_pos, B, Tq, n_h, c, N_c, k, L,
-                   W, scale, nullptr, dtype, out, lse, workspace, ws_bytes, stream);
+                   W, scale, nullptr, NrArgs{}, dtype, out, lse, workspace, ws_bytes, stream);
 }
 
 extern "C" int hca_attend(const void* q, const void* ckv, const void* win_kv, const int* win_pos,
@@ -1247,7 +1348,7 @@ extern "C" int hca_attend(const void* q, const void* ckv, const void* win_kv, co
                           int L, int W, float scale, int dtype, void* out, float* lse,
                           void* workspace, size_t ws_bytes, void* stream) {
   return hca_entry("hca_attend", q, ckv, win_kv, win_pos, q_pos, m, B, Tq, n_h, c, N_h, L, W, scale,
-                   nullptr, dtype, out, lse, workspace, ws_bytes, stream);
+                   nullptr, NrArgs{}, dtype, out, lse, workspace, ws_bytes, stream);
 }
 
 extern "C" int csa_attend_sink(const void* q, const void* ckv, const int* topk_idx,
@@ -1256,7 +1357,7 @@ extern "C" int csa_attend_sink(const void* q, const void* ckv, const int* topk_i
                                const float* sink, int dtype, void* out, float* lse,
                                void* workspace, size_t ws_bytes, void* stream) {
   return csa_entry("csa_attend_sink", q, ckv, topk_idx, win_kv, win_pos, q_pos, B, Tq, n_h, c, N_c,
-                   k, L, W, scale, sink, dtype, out, lse, workspace, ws_bytes, stream);
+                   k, L, W, scale, sink, NrArgs{}, dtype, out, lse, workspace, ws_bytes, stream);
 }
 
 extern "C" int hca_attend_sink(const void* q, const void* ckv, const void* win_kv,
@@ -1265,5 +1366,27 @@ extern "C" int hca_attend_sink(const void* q, const void* ckv, const void* win_k
                                const float* sink, int dtype, void* out, float* lse,
                                void* workspace, size_t ws_bytes, void* stream) {
   return hca_entry("hca_attend_sink", q, ckv, win_kv, win_pos, q_pos, m, B, Tq, n_h, c, N_h, L, W,
-                   scale, sink, dtype, out, lse, workspace, ws_bytes, stream);
+                   scale, sink, NrArgs{}, dtype, out, lse, workspace, ws_bytes, stream);
+}
+
+extern "C" int csa_attend_ex(const void* q, const void* ckv, const int* topk_idx,
+                             const void* win_kv, const int* win_pos, const int* q_pos, int B,
+                             int Tq, int n_h, int c, int N_c, int k, int L, int W, float scale,
+                             const float* sink, const float* q_gamma, int q_norm, int d_rope,
+                             float eps, float theta, int dtype, void* out, float* lse,
+                             void* workspace, size_t ws_bytes, void* stream) {
+  return csa_entry("csa_attend_ex", q, ckv, topk_idx, win_kv, win_pos, q_pos, B, Tq, n_h, c, N_c, k,
+                   L, W, scale, sink, NrArgs{q_gamma, q_norm, d_rope, eps, theta},
+                   dtype, out, lse, workspace, ws_bytes, stream);
+}
+
+extern "C" int hca_attend_ex(const void* q, const void* ckv, const void* win_kv,
+                             const int* win_pos, const int* q_pos, int m, int B, int Tq,
+                             int n_h, int c, int N_h, int L, int W, float scale,
+                             const float* sink, const float* q_gamma, int q_norm, int d_rope,
+                             float eps, float theta, int dtype, void* out, float* lse,
+                             void* workspace, size_t ws_bytes, void* stream) {
+  return hca_entry("hca_attend_ex", q, ckv, win_kv, win_pos, q_pos, m, B, Tq, n_h, c, N_h, L, W,
+                   scale, sink, NrArgs{q_gamma, q_norm, d_rope, eps, theta}, dtype,
+                   out, lse, workspace, ws_bytes, stream);
 }

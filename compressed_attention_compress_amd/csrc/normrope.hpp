@@ -70,15 +70,31 @@ CSAHCA_DEV float row_sum(float v, int CV) {
 }
 
 // cos and sin of pos * f for a rotation frequency f given in double.  The angle is formed
-// and reduced modulo 2 pi in double (positions reach 2^20 and more, where a float angle
-// would be off by a sizeable fraction of a radian); the reduced angle, in [-pi, pi], goes
-// to the float sincos.
+// in double (positions reach 2^20 and more, where a float angle would be off by a sizeable
+// fraction of a radian) and reduced by multiples of pi/2 in double (Cody-Waite, pi/2 split
+// into two doubles), leaving |x| <= pi/4 and the quadrant.  On that interval the Taylor
+// series of sin to x^9 and of cos to x^10 are within 2e-9 of the functions, below half a
+// float ulp, so they are evaluated in float by Horner's rule; the quadrant then swaps and
+// negates.  (A short, branch-free sequence: the attention kernel runs it with most of its
+// registers holding accumulators.)
 CSAHCA_DEV void rope_cos_sin(long long pos, double f, float& cs, float& sn) {
   const double a = (double)pos * f;
-  const double k = rint(a * 0.15915494309189535);        // 1 / (2 pi)
-  double r = fma(-k, 6.283185307179586, a);               // 2 pi, high part
-  r = fma(-k, 2.4492935982947064e-16, r);                 // 2 pi, low part
-  sincosf((float)r, &sn, &cs);
+  const double k = rint(a * 0.6366197723675814);       // 2 / pi
+  double r = fma(-k, 1.5707963267948966, a);            // pi/2, high part
+  r = fma(-k, 6.123233995736766e-17, r);                // pi/2, low part
+  const float x = (float)r, x2 = x * x;
+  const float s = x * fmaf(x2, fmaf(x2, fmaf(x2, fmaf(x2, 1.f / 362880.f, -1.f / 5040.f), 1.f / 120.f),
+                                    -1.f / 6.f),
+                           1.f);
+  const float c = fmaf(x2,
+                       fmaf(x2, fmaf(x2, fmaf(x2, fmaf(x2, -1.f / 3628800.f, 1.f / 40320.f), -1.f / 720.f),
+                                     1.f / 24.f),
+                            -0.5f),
+                       1.f);
+  const int q = (int)((long long)k & 3);
+  const float s1 = (q & 1) ? c : s, c1 = (q & 1) ? s : c;
+  sn = (q & 2) ? -s1 : s1;
+  cs = ((q + 1) & 2) ? -c1 : c1;
 }
 
 // Frequency of rotated pair i: theta^(-2i/d) = 2^(-2i log2(theta) / d), in double.

@@ -14,6 +14,9 @@
 // Overlapped two-stream form (csa_compress_overlap, section V.1's equation with two KV
 // streams): entry i walks stream a over block i and then stream b over block i-1 with
 // the same running softmax, which is one joint softmax over the 2m logits.
+#include <mutex>
+#include <type_traits>
+
 #include "normrope.hpp"
 #include "pool.hpp"
 
@@ -325,8 +328,17 @@ CSAHCA_DEV void pool_block(const T* __restrict__ X, const T* __restrict__ Z,
   }
 }
 
+// Workgroup size cap of the norm's block path: 1024 threads (128 registers each) hold the
+// plain bf16 pooling's loads in flight; the other forms (float, bias, two streams,
+// append) need more registers per thread than 512-thread workgroups leave them (128), so
+// they take 256
+template <typename T, bool HAS_P, int MODE>
+constexpr int nr_block_threads() {
+  return (sizeof(T) == 2 && !HAS_P && MODE == PLAIN) ? 1024 : 256;
+}
+
 template <typename T, int UB, bool HAS_P, int MODE, bool NR>
-__global__ __launch_bounds__(NR ? 512 : 256) void pool_block_kernel(const T* __restrict__ X,
+__global__ __launch_bounds__((NR ? nr_block_threads<T, HAS_P, MODE>() : 256)) void pool_block_kernel(const T* __restrict__ X,
                                                         const T* __restrict__ Z,
                                                         const T* __restrict__ Xb,
                                                         const T* __restrict__ Zb,
@@ -376,6 +388,30 @@ PoolPlan plan_plain(int B, long long N, int c, int m) {
   return p;
 }
 
+// ... and with the norm: the block path holds the whole entry (CVG = all slices) in at
+// most 1024 threads, the per-slice path runs 1024-thread workgroups
+PoolPlan plan_norm(int B, long long N, int c, int m) {
+  PoolPlan p{};
+  p.total = (long long)B * N * (c / 8);
+  const int CV = c / VEC;
+  p.block = p.total < 32768 && m >= 8;
+  if (p.block) {
+    const int unit = CV >= 64 ? 1 : 64 / CV;
+    const int span = max(4, cdiv(m, 1024 / CV));
+    p.S = cdiv(cdiv(m, span), unit) * unit;
+    p.CVG = CV;
+    p.lds = ((size_t)p.S * CV * 3 * VEC + (size_t)c + 16) * sizeof(float);
+    p.grid = (unsigned)(B * N);
+    p.threads = (unsigned)(p.S * CV);
+    p.ub = (span % 8 == 0 && m % 8 == 0) ? 8 : 4;
+  } else {
+    p.grid = (unsigned)cdiv<long long>(p.total, 1024);
+    p.threads = 1024;
+    p.ub = m % 8 == 0 ? 8 : 4;
+  }
+  return p;
+}
+
 // One side of a paired pooling launch
 template <typename T>
 struct PoolSide {
@@ -383,24 +419,61 @@ struct PoolSide {
   T* out;
   int N, c, m, S, CVG;
   long long in_bs, out_bs, total;
+  const float* gamma;  // NR: this side's gain
+  long long entry0;    // NR: cache index of the first entry (its position is m * entry0)
 };
 
-// Two plain poolings in one launch: workgroups [0, gridA) run side A on pool_kernel's
-// layout, the rest run side B on pool_block_kernel's (256 threads each).
-template <typename T, int UBA, int UBB>
-__global__ __launch_bounds__(256) void pool_pair_kernel(PoolSide<T> A, PoolSide<T> Bs, int gridA,
-                                                        NormRope nr0, AppendRows ap0) {
-  if ((int)blockIdx.x < gridA)
-    pool_items<T, UBA, false, PLAIN, false>(A.X, A.Z, nullptr, nullptr, nullptr, A.out, A.N, A.c, A.m, 0,
-                                            A.in_bs, A.out_bs, A.total, nr0, 0, ap0, (int)blockIdx.x);
-  else
-    pool_block<T, UBB, false, PLAIN, false>(Bs.X, Bs.Z, nullptr, nullptr, nullptr, Bs.out, Bs.N, Bs.c,
-                                            Bs.m, 0, Bs.S, Bs.CVG, Bs.in_bs, Bs.out_bs, nr0, 0, ap0,
-                                            (int)blockIdx.x - gridA);
+// Two poolings in one launch: workgroups [0, gridA) run side A on pool_kernel's layout,
+// the rest run side B on pool_block_kernel's (256 threads each; 1024 with the norm).
+template <typename T, int UBA, int UBB, bool NR>
+__global__ __launch_bounds__(NR ? 1024 : 256) void pool_pair_kernel(PoolSide<T> A, PoolSide<T> Bs,
+                                                                    int gridA, NormRope nr,
+                                                                    AppendRows ap0) {
+  if ((int)blockIdx.x < gridA) {
+    const NormRope na{A.gamma, nr.eps, nr.theta, nr.d, nr.norm};
+    pool_items<T, UBA, false, PLAIN, NR>(A.X, A.Z, nullptr, nullptr, nullptr, A.out, A.N, A.c, A.m, 0,
+                                         A.in_bs, A.out_bs, A.total, na, A.entry0, ap0, (int)blockIdx.x);
+  } else {
+    const NormRope nb{Bs.gamma, nr.eps, nr.theta, nr.d, nr.norm};
+    pool_block<T, UBB, false, PLAIN, NR>(Bs.X, Bs.Z, nullptr, nullptr, nullptr, Bs.out, Bs.N, Bs.c,
+                                         Bs.m, 0, Bs.S, Bs.CVG, Bs.in_bs, Bs.out_bs, nb, Bs.entry0, ap0,
+                                         (int)blockIdx.x - gridA);
+  }
+}
+
+// The norm's block path holds up to 1024 x 24 floats of partial states (96 KiB): raise
+// the dynamic LDS limit of its kernels once per process (the attribute belongs to the
+// kernel, for every device)
+template <typename T, bool HAS_P, int MODE>
+hipError_t raise_lds_limit() {
+  static std::once_flag once;
+  static hipError_t rc = hipSuccess;
+  std::call_once(once, [] {
+    rc = hipFuncSetAttribute((const void*)pool_block_kernel<T, 8, HAS_P, MODE, true>,
+                             hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);
+    if (rc == hipSuccess)
+      rc = hipFuncSetAttribute((const void*)pool_block_kernel<T, 4, HAS_P, MODE, true>,
+                               hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);
+  });
+  return rc;
+}
+
+// the same for the paired launch with the norm (bf16)
+hipError_t raise_pair_lds_limit() {
+  using T = uint16_t;
+  static std::once_flag once;
+  static hipError_t rc = hipSuccess;
+  std::call_once(once, [] {
+    const void* k[4] = {(const void*)pool_pair_kernel<T, 8, 8, true>, (const void*)pool_pair_kernel<T, 8, 4, true>,
+                        (const void*)pool_pair_kernel<T, 4, 8, true>, (const void*)pool_pair_kernel<T, 4, 4, true>};
+    for (int i = 0; i < 4 && rc == hipSuccess; ++i)
+      rc = hipFuncSetAttribute(k[i], hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);
+  });
+  return rc;
 }
 
 template <typename T, bool HAS_P, int MODE, bool NR>
-void launch_pool(const void* kv, const void* gate, const void* kv_b, const void* gate_b,
+int launch_pool(const void* kv, const void* gate, const void* kv_b, const void* gate_b,
                  const float* pos_bias, void* out, int B, long long N, int c, int m, int prev,
                  long long in_bs, long long out_bs, const NormRope& nr, long long entry0,
                  const AppendRows& ap, hipStream_t st) {
@@ -412,12 +485,13 @@ void launch_pool(const void* kv, const void* gate, const void* kv_b, const void*
   if (total < 32768 && mt >= 8) {
     // few blocks of many tokens: 8-channel slices in groups of up to 8 per workgroup,
     // tokens in sub-ranges of at least 4, at most 256 threads per workgroup.  With the
-    // norm the workgroup holds the whole entry (all CV slices, at most 512 threads, a
-    // whole number of waves).
+    // norm the workgroup holds the whole entry (all CV slices, a whole number of waves, as
+    // many threads as the form allows: a decode step pools one entry per sequence, so the
+    // workgroups are few and each takes as many loads in flight as it can)
     int CVG = 8, smax, unit = 1;
     if (NR) {
       CVG = CV;
-      smax = 512 / CV;
+      smax = nr_block_threads<T, HAS_P, MODE>() / CV;
       unit = CV >= 64 ? 1 : 64 / CV;
     } else {
       while (CV % CVG != 0) CVG /= 2;
@@ -427,6 +501,8 @@ void launch_pool(const void* kv, const void* gate, const void* kv_b, const void*
     const int S = cdiv(cdiv(mt, span), unit) * unit;
     const size_t lds = ((size_t)S * CVG * 3 * VEC + (NR ? (size_t)c + 16 : 0)) * sizeof(float);
     const unsigned grid = (unsigned)(B * N * (CV / CVG)), threads = (unsigned)(S * CVG);
+    if (NR && raise_lds_limit<T, HAS_P, MODE>() != hipSuccess)
+      return csahca::fail(CSAHCA_ELAUNCH, "pooling: cannot raise the LDS limit");
     if (span % 8 == 0 && m % 8 == 0)
       hipLaunchKernelGGL((pool_block_kernel<T, 8, HAS_P, MODE, NR>), dim3(grid), dim3(threads), lds, st,
                          X, Z, Xb, Zb, pos_bias, (T*)out, (int)N, c, m, prev, S, CVG, in_bs, out_bs,
@@ -435,7 +511,7 @@ void launch_pool(const void* kv, const void* gate, const void* kv_b, const void*
       hipLaunchKernelGGL((pool_block_kernel<T, 4, HAS_P, MODE, NR>), dim3(grid), dim3(threads), lds, st,
                          X, Z, Xb, Zb, pos_bias, (T*)out, (int)N, c, m, prev, S, CVG, in_bs, out_bs,
                          nr, entry0, ap);
-    return;
+    return CSAHCA_OK;
   }
   const unsigned blocks = (unsigned)cdiv<long long>(total, 256);
   if (m % 8 == 0)
@@ -446,6 +522,7 @@ void launch_pool(const void* kv, const void* gate, const void* kv_b, const void*
     hipLaunchKernelGGL((pool_kernel<T, 4, HAS_P, MODE, NR>), dim3(blocks), dim3(256), 0, st, X, Z, Xb,
                        Zb, pos_bias, (T*)out, (int)N, c, m, prev, in_bs, out_bs, total, nr, entry0,
                        ap);
+  return CSAHCA_OK;
 }
 
 struct PoolArgs {
@@ -463,14 +540,14 @@ struct PoolArgs {
 };
 
 template <typename T, bool HP, int MODE, bool NR>
-void run_pool(const PoolArgs& a) {
-  launch_pool<T, HP, MODE, NR>(a.kv, a.gate, a.kv_b, a.gate_b, a.pos_bias, a.out, a.B, a.N, a.c,
+int run_pool(const PoolArgs& a) {
+  return launch_pool<T, HP, MODE, NR>(a.kv, a.gate, a.kv_b, a.gate_b, a.pos_bias, a.out, a.B, a.N, a.c,
                                a.m, a.prev, a.in_bs, a.out_bs, a.nr, a.entry0, a.ap, a.st);
 }
 
 template <typename T>
-void pick_pool(const PoolArgs& a, bool hp, int mode, bool nr) {
-  using F = void (*)(const PoolArgs&);
+int pick_pool(const PoolArgs& a, bool hp, int mode, bool nr) {
+  using F = int (*)(const PoolArgs&);
   static const F tab[12] = {
       run_pool<T, false, PLAIN, false>,      run_pool<T, false, PLAIN, true>,
       run_pool<T, false, TWO_STREAM, false>, run_pool<T, false, TWO_STREAM, true>,
@@ -478,7 +555,7 @@ void pick_pool(const PoolArgs& a, bool hp, int mode, bool nr) {
       run_pool<T, true, PLAIN, false>,       run_pool<T, true, PLAIN, true>,
       run_pool<T, true, TWO_STREAM, false>,  run_pool<T, true, TWO_STREAM, true>,
       run_pool<T, true, APPEND, false>,      run_pool<T, true, APPEND, true>};
-  tab[(hp ? 6 : 0) + 2 * mode + (nr ? 1 : 0)](a);
+  return tab[(hp ? 6 : 0) + 2 * mode + (nr ? 1 : 0)](a);
 }
 
 }  // namespace
@@ -551,20 +628,22 @@ int pool_entry(const char* name, const void* kv, const void* gate, const void* k
   PoolArgs a{kv, gate, kv_b, gate_b, pos_bias, out, B, N, c, m, prev, in_bs, out_bs,
              nr ? *nr : NormRope{nullptr, 0.f, 1.f, 0, 0}, entry0, AppendRows{nullptr, nullptr, 1, 0, 0, 0},
              (hipStream_t)stream};
-  if (dtype == CSAHCA_BF16)
-    pick_pool<uint16_t>(a, pos_bias != nullptr, ov ? TWO_STREAM : PLAIN, nr != nullptr);
-  else
-    pick_pool<float>(a, pos_bias != nullptr, ov ? TWO_STREAM : PLAIN, nr != nullptr);
-  return launch_status(name);
+  const int lrc = dtype == CSAHCA_BF16
+                      ? pick_pool<uint16_t>(a, pos_bias != nullptr, ov ? TWO_STREAM : PLAIN, nr != nullptr)
+                      : pick_pool<float>(a, pos_bias != nullptr, ov ? TWO_STREAM : PLAIN, nr != nullptr);
+  return lrc != CSAHCA_OK ? lrc : launch_status(name);
 }
 
-// Two plain poolings of one layer pair (csa_compress and hca_compress arguments) in one
-// launch when one takes pool_kernel's layout and the other pool_block_kernel's at 256
-// threads; otherwise one launch each.  The entries are the same bits either way.
-int pool_pair(const void* kv_a, const void* gate_a, void* out_a, int n_a, int m_a, long long in_bs_a,
-              long long out_bs_a, const void* kv_b, const void* gate_b, void* out_b, int n_b, int m_b,
-              long long in_bs_b, long long out_bs_b, int B, int c, int dtype, void* stream) {
-  const char* name = "csahca_compress_pair";
+// Two poolings of one layer pair (csa_compress and hca_compress arguments; with nr, those
+// of csahca_compress_norm_rope, each side with its own gain and first entry) in one
+// launch when one takes pool_kernel's layout and the other pool_block_kernel's at the
+// same workgroup size; otherwise one launch each.  The entries are the same bits either
+// way.
+int pool_pair(const char* name, const void* kv_a, const void* gate_a, void* out_a, int n_a, int m_a,
+              long long in_bs_a, long long out_bs_a, const void* kv_b, const void* gate_b, void* out_b,
+              int n_b, int m_b, long long in_bs_b, long long out_bs_b, int B, int c, int dtype,
+              const NormRope* nr, const float* gamma_a, long long entry0_a, const float* gamma_b,
+              long long entry0_b, void* stream) {
   long long NA = 0, NB = 0;
   int rc = pool_check(name, kv_a, gate_a, nullptr, nullptr, false, 0, out_a, B, n_a, c, m_a, dtype,
                       in_bs_a, out_bs_a, &NA);
@@ -572,47 +651,66 @@ int pool_pair(const void* kv_a, const void* gate_a, void* out_a, int n_a, int m_
   rc = pool_check(name, kv_b, gate_b, nullptr, nullptr, false, 0, out_b, B, n_b, c, m_b, dtype, in_bs_b,
                   out_bs_b, &NB);
   if (rc != CSAHCA_OK) return rc;
+  if (nr && (!norm_rope_args_ok(c, nr->d, nr->eps, nr->theta) || entry0_a < 0 || entry0_b < 0 ||
+             !aligned16(gamma_a) || !aligned16(gamma_b))) {
+    set_error("%s: the norm needs c / 8 a power of two <= 64, d_rope %% 8 == 0 and <= c, "
+              "eps >= 0, theta > 0, entry0 >= 0 and gamma 16-byte aligned", name);
+    return CSAHCA_EINVAL;
+  }
   hipStream_t st = (hipStream_t)stream;
-  const PoolPlan pa = plan_plain(B, NA, c, m_a), pb = plan_plain(B, NB, c, m_b);
+  const PoolPlan pa = nr ? plan_norm(B, NA, c, m_a) : plan_plain(B, NA, c, m_a);
+  const PoolPlan pb = nr ? plan_norm(B, NB, c, m_b) : plan_plain(B, NB, c, m_b);
+  const unsigned wg = nr ? 1024u : 256u;
   const bool swap = pa.block && !pb.block;  // side 1 takes pool_kernel's layout
   const PoolPlan &p1 = swap ? pb : pa, &p2 = swap ? pa : pb;
-  if (NA > 0 && NB > 0 && !p1.block && p2.block && p2.threads == 256 &&
+  // (with the norm, bf16 only: the float form does not fit 1024-thread workgroups)
+  if (NA > 0 && NB > 0 && !p1.block && p2.block && p2.threads == wg && (!nr || dtype == CSAHCA_BF16) &&
       (long long)p1.grid + p2.grid <= 0x7FFFFFFFLL) {
-    const NormRope nr0{nullptr, 0.f, 1.f, 0, 0};
+    if (nr && raise_pair_lds_limit() != hipSuccess)
+      return fail(CSAHCA_ELAUNCH, "csahca_compress_pair: cannot raise the LDS limit");
+    const NormRope n0 = nr ? *nr : NormRope{nullptr, 0.f, 1.f, 0, 0};
     const AppendRows ap0{nullptr, nullptr, 1, 0, 0, 0};
-    auto go = [&](auto tag) {
+    auto go = [&](auto tag, auto nrtag) {
       using T = decltype(tag);
+      constexpr bool NR = decltype(nrtag)::value;
       const PoolSide<T> sa{(const T*)kv_a, (const T*)gate_a, (T*)out_a, (int)NA, c, m_a,
-                           pa.S, pa.CVG, in_bs_a, out_bs_a, pa.total};
+                           pa.S, pa.CVG, in_bs_a, out_bs_a, pa.total, gamma_a, entry0_a};
       const PoolSide<T> sb{(const T*)kv_b, (const T*)gate_b, (T*)out_b, (int)NB, c, m_b,
-                           pb.S, pb.CVG, in_bs_b, out_bs_b, pb.total};
+                           pb.S, pb.CVG, in_bs_b, out_bs_b, pb.total, gamma_b, entry0_b};
       const PoolSide<T>& s1 = swap ? sb : sa;
       const PoolSide<T>& s2 = swap ? sa : sb;
-      const dim3 grid(p1.grid + p2.grid);
+      const dim3 grid(p1.grid + p2.grid), blk(wg);
       const int g1 = (int)p1.grid;
       if (p1.ub == 8 && p2.ub == 8)
-        hipLaunchKernelGGL((pool_pair_kernel<T, 8, 8>), grid, dim3(256), p2.lds, st, s1, s2, g1, nr0, ap0);
+        hipLaunchKernelGGL((pool_pair_kernel<T, 8, 8, NR>), grid, blk, p2.lds, st, s1, s2, g1, n0, ap0);
       else if (p1.ub == 8)
-        hipLaunchKernelGGL((pool_pair_kernel<T, 8, 4>), grid, dim3(256), p2.lds, st, s1, s2, g1, nr0, ap0);
+        hipLaunchKernelGGL((pool_pair_kernel<T, 8, 4, NR>), grid, blk, p2.lds, st, s1, s2, g1, n0, ap0);
       else if (p2.ub == 8)
-        hipLaunchKernelGGL((pool_pair_kernel<T, 4, 8>), grid, dim3(256), p2.lds, st, s1, s2, g1, nr0, ap0);
+        hipLaunchKernelGGL((pool_pair_kernel<T, 4, 8, NR>), grid, blk, p2.lds, st, s1, s2, g1, n0, ap0);
       else
-        hipLaunchKernelGGL((pool_pair_kernel<T, 4, 4>), grid, dim3(256), p2.lds, st, s1, s2, g1, nr0, ap0);
+        hipLaunchKernelGGL((pool_pair_kernel<T, 4, 4, NR>), grid, blk, p2.lds, st, s1, s2, g1, n0, ap0);
     };
-    if (dtype == CSAHCA_BF16)
-      go(uint16_t{});
+    if (nr)
+      go(uint16_t{}, std::true_type{});
+    else if (dtype == CSAHCA_BF16)
+      go(uint16_t{}, std::false_type{});
     else
-      go(float{});
+      go(float{}, std::false_type{});
     return launch_status(name);
+  }
+  NormRope na{}, nb{};
+  if (nr) {
+    na = NormRope{gamma_a, nr->eps, nr->theta, nr->d, nr->norm};
+    nb = NormRope{gamma_b, nr->eps, nr->theta, nr->d, nr->norm};
   }
   if (NA > 0) {
     rc = pool_entry(name, kv_a, gate_a, nullptr, nullptr, false, 0, nullptr, out_a, B, n_a, c, m_a, dtype,
-                    in_bs_a, out_bs_a, stream);
+                    in_bs_a, out_bs_a, stream, nr ? &na : nullptr, entry0_a);
     if (rc != CSAHCA_OK) return rc;
   }
   if (NB > 0)
     return pool_entry(name, kv_b, gate_b, nullptr, nullptr, false, 0, nullptr, out_b, B, n_b, c, m_b, dtype,
-                      in_bs_b, out_bs_b, stream);
+                      in_bs_b, out_bs_b, stream, nr ? &nb : nullptr, entry0_b);
   clear_error();
   return CSAHCA_OK;
 }
@@ -632,11 +730,9 @@ int pool_append(const char* name, const void* kv_new, const void* gate_new, cons
   PoolArgs a{kv_new, gate_new, nullptr, nullptr, pos_bias, (char*)entries + first * c * e, B, count, c, m, 0,
              new_bs, ent_bs, NormRope{nullptr, 0.f, 1.f, 0, 0}, first,
              AppendRows{ring_x, ring_z, R, store ? 1 : 0, n_old, ring_bs}, (hipStream_t)stream};
-  if (dtype == CSAHCA_BF16)
-    pick_pool<uint16_t>(a, pos_bias != nullptr, APPEND, false);
-  else
-    pick_pool<float>(a, pos_bias != nullptr, APPEND, false);
-  return launch_status(name);
+  const int lrc = dtype == CSAHCA_BF16 ? pick_pool<uint16_t>(a, pos_bias != nullptr, APPEND, false)
+                                      : pick_pool<float>(a, pos_bias != nullptr, APPEND, false);
+  return lrc != CSAHCA_OK ? lrc : launch_status(name);
 }
 
 }  // namespace csahca
@@ -655,8 +751,23 @@ extern "C" int csahca_compress_pair(const void* kv_a, const void* gate_a, void* 
                                     const void* kv_b, const void* gate_b, void* out_b, int n_b,
                                     int m_b, long long in_bstride_b, long long out_bstride_b, int B,
                                     int c, int dtype, void* stream) {
-  return csahca::pool_pair(kv_a, gate_a, out_a, n_a, m_a, in_bstride_a, out_bstride_a, kv_b, gate_b, out_b,
-                           n_b, m_b, in_bstride_b, out_bstride_b, B, c, dtype, stream);
+  return csahca::pool_pair("csahca_compress_pair", kv_a, gate_a, out_a, n_a, m_a, in_bstride_a, out_bstride_a,
+                           kv_b, gate_b, out_b, n_b, m_b, in_bstride_b, out_bstride_b, B, c, dtype, nullptr,
+                           nullptr, 0, nullptr, 0, stream);
+}
+
+extern "C" int csahca_compress_pair_norm_rope(const void* kv_a, const void* gate_a, const float* gamma_a,
+                                              void* out_a, int n_a, int m_a, long long entry0_a,
+                                              long long in_bstride_a, long long out_bstride_a,
+                                              const void* kv_b, const void* gate_b, const float* gamma_b,
+                                              void* out_b, int n_b, int m_b, long long entry0_b,
+                                              long long in_bstride_b, long long out_bstride_b, int B,
+                                              int c, int d_rope, float eps, float theta, int dtype,
+                                              void* stream) {
+  const NormRope nr{nullptr, eps, theta, d_rope, 1};
+  return csahca::pool_pair("csahca_compress_pair_norm_rope", kv_a, gate_a, out_a, n_a, m_a, in_bstride_a,
+                           out_bstride_a, kv_b, gate_b, out_b, n_b, m_b, in_bstride_b, out_bstride_b, B, c,
+                           dtype, &nr, gamma_a, entry0_a, gamma_b, entry0_b, stream);
 }
 
 extern "C" int hca_compress(const void* kv, const void* gate, const float* pos_bias, void* out,

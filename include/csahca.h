@@ -337,6 +337,58 @@ int csahca_norm_rope(const void* x, void* y, const float* gamma, const int* pos,
                      int dtype, long long x_bstride, long long y_bstride, void* stream);
 
 /*
+ * csahca_compress_pair_norm_rope -- csahca_compress_pair with every emitted entry
+ * normalised and rotated as csahca_compress_norm_rope does: the two poolings of one layer
+ * pair (the blocks a decode step completes in both caches) in one launch.
+ * Source: as csahca_compress_pair and csahca_compress_norm_rope.
+ * Side x takes csahca_compress_norm_rope's arguments without the bias: its own gain
+ * gamma_x ([c] float32 device, 16-byte aligned, or NULL) and first entry index entry0_x
+ * (entry e carries position m_x * (entry0_x + e)); d_rope, eps and theta are shared.
+ * Every argument rule of both calls applies; the entries are bit-identical to two
+ * csahca_compress_norm_rope calls.  One launch when one side has few entries of many
+ * tokens and the other does not; otherwise the two are enqueued one after the other.
+ */
+int csahca_compress_pair_norm_rope(const void* kv_a, const void* gate_a, const float* gamma_a,
+                                   void* out_a, int n_a, int m_a, long long entry0_a,
+                                   long long in_bstride_a, long long out_bstride_a,
+                                   const void* kv_b, const void* gate_b, const float* gamma_b,
+                                   void* out_b, int n_b, int m_b, long long entry0_b,
+                                   long long in_bstride_b, long long out_bstride_b, int B, int c,
+                                   int d_rope, float eps, float theta, int dtype, void* stream);
+
+/*
+ * csa_attend_ex / hca_attend_ex -- csa_attend_sink / hca_attend_sink with the RMSNorm and
+ * partial RoPE of the queries done inside the attention kernel, as it loads them.
+ * Source: "DeepSeek-V4 Hybrid Attention: CSA, HCA, mHC, MoE", section IV (queries and KV
+ * entries normalised, the last 64 dimensions rotated, in both branches), with the
+ * norm_rope definition above.
+ *
+ * With q_norm = 1 the result equals csahca_norm_rope (norm = 1, pos = q_pos, pstride 1)
+ * applied to q first, the normalised query rounded once to bfloat16 as there, and then
+ * the _sink call; q itself is not written.  Keys are used as stored: compressed entries
+ * are normalised when pooled (csahca_compress_norm_rope), and a window row is normalised
+ * once, when its token arrives (csahca_norm_rope on the new rows), not at every step.
+ *
+ *   q_norm   1: RMSNorm + RoPE of the queries; 0: the _sink call.
+ *   q_gamma  [c] float32 device, or NULL for unit gain.
+ *   d_rope   rotated channels at the end of the row, a multiple of 8 in [0, 128].
+ *   eps >= 0, theta > 0 (finite).
+ *   sink     as in the _sink calls (NULL for none).
+ * Every other argument, the limits and the errors are those of csa_attend / hca_attend
+ * (same workspace size); with q_norm = 1 dtype must be CSAHCA_BF16 (else CSAHCA_ENOTSUP).
+ */
+int csa_attend_ex(const void* q, const void* ckv, const int* topk_idx, const void* win_kv,
+                  const int* win_pos, const int* q_pos, int B, int Tq, int n_h, int c, int N_c,
+                  int k, int L, int W, float scale, const float* sink, const float* q_gamma,
+                  int q_norm, int d_rope, float eps, float theta, int dtype, void* out,
+                  float* lse, void* workspace, size_t ws_bytes, void* stream);
+int hca_attend_ex(const void* q, const void* ckv, const void* win_kv, const int* win_pos,
+                  const int* q_pos, int m, int B, int Tq, int n_h, int c, int N_h, int L, int W,
+                  float scale, const float* sink, const float* q_gamma, int q_norm, int d_rope,
+                  float eps, float theta, int dtype, void* out, float* lse, void* workspace,
+                  size_t ws_bytes, void* stream);
+
+/*
  * csahca_kv_ring_rows / csahca_kv_append / csahca_kv_fork -- the cache lifecycle of one
  * layer: raw tokens arrive, completed blocks become compressed entries, the recent window
  * stays exact, a request can start from another's prefix.

@@ -88,7 +88,10 @@ def run_index(qI, w, KI, q_pos, m, k, idx_dtype, split=False, N_c=None):
     return idx, sc, alls
 
 
-def run_csa_attend(Q, C, topk, win, win_pos, q_pos, W, dtype, scale=None, lse=True, sink=None):
+def run_csa_attend(Q, C, topk, win, win_pos, q_pos, W, dtype, scale=None, lse=True, sink=None,
+                   nrq=None):
+    """nrq: (q_gamma device or None, d_rope, eps, theta) to normalise and rotate the queries
+    inside the call (csa_attend_ex), else None."""
     B, Tq, n_h, c = Q.shape
     N_c = C.shape[1]
     k = topk.shape[2]
@@ -98,7 +101,10 @@ def run_csa_attend(Q, C, topk, win, win_pos, q_pos, W, dtype, scale=None, lse=Tr
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=DEV)
     out = empty((B, Tq, n_h, c), dtype)
     l = torch.empty((B, Tq, n_h), dtype=torch.float32, device=DEV) if lse else None
-    if sink is None:
+    if nrq is not None:
+        lib.csa_attend_ex(Q, C, topk, win, win_pos, q_pos, B, Tq, n_h, c, N_c, k, L, W, scale, sink,
+                          nrq[0], 1, *nrq[1:], dtype, out, l, ws, ws_bytes)
+    elif sink is None:
         lib.csa_attend(Q, C, topk, win, win_pos, q_pos, B, Tq, n_h, c, N_c, k, L, W, scale, dtype,
                        out, l, ws, ws_bytes)
     else:
@@ -107,7 +113,8 @@ def run_csa_attend(Q, C, topk, win, win_pos, q_pos, W, dtype, scale=None, lse=Tr
     return out, l
 
 
-def run_hca_attend(Q, C, win, win_pos, q_pos, m, W, dtype, scale=None, lse=True, sink=None):
+def run_hca_attend(Q, C, win, win_pos, q_pos, m, W, dtype, scale=None, lse=True, sink=None,
+                   nrq=None):
     B, Tq, n_h, c = Q.shape
     N_h = C.shape[1]
     L = win.shape[1]
@@ -116,7 +123,10 @@ def run_hca_attend(Q, C, win, win_pos, q_pos, m, W, dtype, scale=None, lse=True,
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=DEV)
     out = empty((B, Tq, n_h, c), dtype)
     l = torch.empty((B, Tq, n_h), dtype=torch.float32, device=DEV) if lse else None
-    if sink is None:
+    if nrq is not None:
+        lib.hca_attend_ex(Q, C, win, win_pos, q_pos, m, B, Tq, n_h, c, N_h, L, W, scale, sink, nrq[0],
+                          1, *nrq[1:], dtype, out, l, ws, ws_bytes)
+    elif sink is None:
         lib.hca_attend(Q, C, win, win_pos, q_pos, m, B, Tq, n_h, c, N_h, L, W, scale, dtype, out, l,
                        ws, ws_bytes)
     else:

@@ -164,6 +164,21 @@ def test_attend_validation():
     assert "csa_attend_sink" in lib.last_error()
     assert L.hca_attend_sink(*hbad, 0.04, FAKE, 1, FAKE, None, FAKE, wh, None) == EINVAL
     assert L.hca_attend_sink(*hb, 0.04, FAKE, 2, FAKE, None, FAKE, wh, None) == ENOTSUP
+    # the _ex variants: the same checks, then the query norm arguments
+    nr = [FAKE, None, 1, 64, 1e-6, 1e4]        # sink, q_gamma, q_norm, d_rope, eps, theta
+    assert L.csa_attend_ex(*base, 0.04, *nr, 1, FAKE, None, FAKE, ws - 1, None) == EWORKSPACE
+    for i, v in [(2, 2), (3, 136), (3, 60), (3, -8), (4, -1.0), (5, 0.0), (5, float("inf"))]:
+        bad = list(nr)
+        bad[i] = v
+        assert L.csa_attend_ex(*base, 0.04, *bad, 1, FAKE, None, FAKE, ws, None) == EINVAL, (i, v)
+        assert "csa_attend_ex" in lib.last_error()
+        assert L.hca_attend_ex(*hb, 0.04, *bad, 1, FAKE, None, FAKE, wh, None) == EINVAL, (i, v)
+    # the query norm is a bfloat16 path; q_norm = 0 leaves float32 to its own limits
+    f32 = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, B, Tq, 8, 64, 4096, 64, 4096, 16]
+    assert L.csa_attend_ex(*f32, 0.04, *nr, 0, FAKE, None, FAKE, ws, None) == ENOTSUP
+    assert "bfloat16" in lib.last_error()
+    assert L.hca_attend_ex(*hbad, 0.04, None, None, 0, 64, 1e-6, 1e4, 1, FAKE, None, FAKE, wh,
+                           None) == EINVAL  # m, checked before the norm arguments
 
 
 def test_binding_raises_with_message():

@@ -20,7 +20,7 @@ import torch
 
 import oracle
 from synthgen.configs import BF16, CONFIGS, F32, FP8, MXFP4
-from synthgen.host import make_problem
+from synthgen.host import encode, make_problem
 from tests import gpu_harness as H
 
 pytestmark = pytest.mark.gpu
@@ -97,15 +97,17 @@ def check_index(prob, q_pos, k, idx, sc, alls):
 FEW_ROWS = 16  # queries attending to at most this many rows take their own output's RMS
 
 
-def check_attend(Qc, dtype, rows_fn, gpu_out, gpu_lse, scale, sink=None, label=""):
+def check_attend(Qc, dtype, rows_fn, gpu_out, gpu_lse, scale, sink=None, label="", Q_ref=None):
     """rows_fn(b, t) -> fp64 row set for that query (from the GPU-consumed bytes).
+    Q_ref: the fp64 queries the oracle attends with, when not the decoded Qc (queries
+    normalised inside the call).
 
     bf16: max |d| <= 2e-2 x RMS of the call's whole output.  A query with at most
     FEW_ROWS rows is instead held to 2e-2 x the larger of that RMS and the RMS of its own
     output: its output is close to a single row, up to 10x the call's RMS when the call
     also holds many-row queries, and the bf16 storage of such a value (half an ulp,
     2^-9 relative) alone exceeds 2e-2 x the call's RMS."""
-    Q = oracle.decode(Qc, dtype)
+    Q = oracle.decode(Qc, dtype) if Q_ref is None else Q_ref
     B, Tq = Q.shape[:2]
     got = oracle.decode(H.to_host_codes(gpu_out, dtype), dtype)
     lse = gpu_lse.cpu().numpy().astype(np.float64)
@@ -171,9 +173,15 @@ def small_cases():
 CASES = small_cases()
 
 
-def run_chain(cfg, split_index=False, W=None, sink=None):
+def run_chain(cfg, split_index=False, W=None, sink=None, nrq=None):
     """Run every stage on the GPU and check each against the oracle; return outputs.
-    sink: optional [n_h] float32 attention sink for both attention calls."""
+    sink: optional [n_h] float32 attention sink for both attention calls.
+    nrq: optional (gamma [c] float32 or None, d_rope, eps, theta): the attention calls
+    normalise and rotate the queries themselves (csa_attend_ex / hca_attend_ex).  The
+    kernel multiplies the normalised query as a bf16 MFMA operand, as the separate path
+    would store it; the oracle attends with oracle.rope_tail(oracle.rmsnorm(q)) computed
+    in fp64 and rounded to bf16 (nearest even) at that same point, and the error against
+    the unrounded fp64 query is printed beside it."""
     prob = make_problem(cfg)
     W = cfg.W if W is None else W
     B, c, dt = cfg.B, cfg.c, cfg.dtype
@@ -183,6 +191,10 @@ def run_chain(cfg, split_index=False, W=None, sink=None):
     q_pos = H.to_dev(q_pos_h)
     scale = 1.0 / math.sqrt(c)
     results = {}
+    nrq_dev = None
+    if nrq is not None:
+        g, d, eps, theta = nrq
+        nrq_dev = (None if g is None else H.to_dev(g), d, eps, theta)
     for layer in ("csa", "hca"):
         if f"X_{layer}" not in prob:
             continue
@@ -205,7 +217,7 @@ def run_chain(cfg, split_index=False, W=None, sink=None):
             check_index(prob, q_pos_h, cfg.k, idx, sc, alls)
             idx_h = idx.cpu().numpy()
             out, lse = H.run_csa_attend(Q, C, idx, X, win_pos, q_pos, W, dt,
-                                        sink=None if sink is None else H.to_dev(sink))
+                                        sink=None if sink is None else H.to_dev(sink), nrq=nrq_dev)
             rows = lambda b, t: oracle.csa_rows(Ch[b], idx_h[b, t], Xd[b], 0, int(q_pos_h[b]) + t, W)
             results["csa_idx"] = idx_h
             if "plant_positions" in prob:
@@ -215,9 +227,22 @@ def run_chain(cfg, split_index=False, W=None, sink=None):
             if C.shape[1] == 0:
                 continue
             out, lse = H.run_hca_attend(Q, C, X, win_pos, q_pos, m, W, dt,
-                                        sink=None if sink is None else H.to_dev(sink))
+                                        sink=None if sink is None else H.to_dev(sink), nrq=nrq_dev)
             rows = lambda b, t: oracle.hca_rows(Ch[b], m, Xd[b], 0, int(q_pos_h[b]) + t, W)
-        check_attend(prob[f"Q_{layer}"], dt, rows, out, lse, scale, sink, label=layer)
+        Q_ref = None
+        if nrq is not None:
+            g, d, eps, theta = nrq
+            pos = q_pos_h[:, None, None] + np.arange(Tq)[None, :, None]       # [B, Tq, 1]
+            q64 = oracle.rope_tail(oracle.rmsnorm(oracle.decode(prob[f"Q_{layer}"], dt), g, eps),
+                                   np.broadcast_to(pos, (B, Tq, cfg.n_h)), d, theta)
+            Q_ref = oracle.decode(encode(q64, dt), dt)
+            got = oracle.decode(H.to_host_codes(out, dt), dt)
+            full = np.stack([np.stack([oracle.attend(q64[b, t], rows(b, t), scale, sink)[0]
+                                       for t in range(Tq)]) for b in range(B)])
+            print(f"{layer}: against the fp64 (unrounded) normalised query max |d| = "
+                  f"{np.abs(got - full).max():.3g}, {np.abs(got - full).max() / (2e-2 * np.sqrt(np.mean(full ** 2))):.3f} "
+                  f"of 2e-2 x RMS", flush=True)
+        check_attend(prob[f"Q_{layer}"], dt, rows, out, lse, scale, sink, label=layer, Q_ref=Q_ref)
         results[f"{layer}_out"] = out.cpu().numpy()
         results[f"{layer}_lse"] = lse.cpu().numpy()
         results[f"{layer}_C"] = C.cpu().numpy()
@@ -245,6 +270,62 @@ def test_attention_sink(name):
     sink[0] = 30.0
     sink[-1] = -np.inf
     run_chain(cfg, sink=sink)
+
+
+NR_EPS, NR_THETA = 1e-6, 10000.0
+
+
+@pytest.mark.parametrize("name,d,gain,sink", [
+    ("hca_h64_ragged", 64, True, False),
+    ("csa_h128_k1024", 64, True, True),
+    ("csa_h64_k512", 128, False, False),
+    ("pair_h128", 64, True, False),
+    ("prefill_small", 64, True, False),
+    ("prefill_odd_tq", 0, True, True),      # norm only
+    ("few_heads_h32", 64, True, False),     # two waves, column-split workgroups
+])
+def test_queries_normalised_inside_attention(name, d, gain, sink):
+    """csa_attend_ex / hca_attend_ex with q_norm = 1: RMSNorm + RoPE of the queries in the
+    attention kernel, against the oracle attending with rope_tail(rmsnorm(q)) formed in
+    fp64 and rounded to bf16 where the kernel rounds it (the MFMA operand, the precision
+    the separate row kernel stores)."""
+    print(f"[query norm {name} d={d} gain={gain} sink={sink}]", flush=True)
+    cfg = CASES[name] if name in CASES else CONFIGS[3].scaled(B=2, n=4 * 700 + 3, n_h=32, seed=72)
+    rng = np.random.default_rng(73)
+    g = rng.uniform(0.5, 1.5, size=cfg.c).astype(np.float32) if gain else None
+    sk = (rng.standard_normal(cfg.n_h) * 3).astype(np.float32) if sink else None
+    run_chain(cfg, sink=sk, nrq=(g, d, NR_EPS, NR_THETA))
+
+
+def test_query_norm_inside_equals_the_row_kernel_first():
+    """The fused query norm against csahca_norm_rope on the queries followed by the plain
+    call: the same arithmetic up to the order of the sum of squares, so outputs agree to a
+    bf16 ulp or two (a normalised query element can round the other way)."""
+    cfg = CASES["pair_h128"]
+    prob = make_problem(cfg)
+    B, c, Tq, n_h, W = cfg.B, cfg.c, prob["Tq"], cfg.n_h, cfg.W
+    m = cfg.m_hca
+    rng = np.random.default_rng(74)
+    g = H.to_dev(rng.uniform(0.5, 1.5, size=c).astype(np.float32))
+    q_pos = H.to_dev(prob["q_pos"])
+    X, Z = H.to_dev(prob["X_hca"]), H.to_dev(prob["Z_hca"])
+    C = H.run_pool(X, Z, m, BF16, fn=H.lib.hca_compress)
+    win_pos = H.to_dev(np.zeros(B, np.int32))
+    Q = H.to_dev(prob["Q_hca"])
+    fused, lf = H.run_hca_attend(Q, C, X, win_pos, q_pos, m, W, BF16, nrq=(g, 64, NR_EPS, NR_THETA))
+    Qn = torch.empty_like(Q)
+    H.lib.csahca_norm_rope(Q, Qn, g, q_pos, B, Tq, n_h, c, 1, 64, NR_EPS, NR_THETA, 1, BF16)
+    two, lt = H.run_hca_attend(Qn, C, X, win_pos, q_pos, m, W, BF16)
+    torch.cuda.synchronize()
+    a = oracle.decode(H.to_host_codes(fused, BF16), BF16)
+    b = oracle.decode(H.to_host_codes(two, BF16), BF16)
+    same = float(np.mean(a == b))
+    d = np.abs(a - b).max()
+    rms = math.sqrt(float(np.mean(b * b)))
+    print(f"fused vs two calls: {same:.4f} of outputs bit-identical, max |d| = {d:.3g} "
+          f"({d / rms:.3g} x RMS), lse max |d| = {(lf - lt).abs().max().item():.3g}", flush=True)
+    assert d <= 2e-3 * rms and same >= 0.9
+    assert (lf - lt).abs().max().item() <= 1e-3
 
 
 def test_sink_of_minus_inf_changes_no_bit():

@@ -123,3 +123,51 @@ def test_pair_in_a_graph_replays():
         torch.cuda.synchronize()
         assert torch.equal(oa.view(torch.int16), ra.view(torch.int16)), rep
         assert torch.equal(ob.view(torch.int16), rb.view(torch.int16)), rep
+
+
+NR_CASES = ["decode_pair", "decode_pair_swapped", "chunk_pair", "ragged_strides", "hca_side_empty",
+            "fp32_small_c"]
+
+
+@pytest.mark.parametrize("name", NR_CASES)
+def test_pair_norm_rope_equals_separate_calls(name):
+    """csahca_compress_pair_norm_rope against two csahca_compress_norm_rope calls (same
+    bits), each side with its own gain and first entry; the decode pair also against the
+    oracle (pooling, RMSNorm, RoPE at position m * entry)."""
+    from tests.test_gpu_normrope import check_pooled, pooled_reference
+
+    B, c, (n_a, m_a), (n_b, m_b), dt, pad = CASES[name]
+    print(f"[pool pair norm_rope {name}]", flush=True)
+    g = torch.Generator(device="cuda").manual_seed(zlib.crc32(name.encode()) % 1000 + 1)
+    Xa, Za = _side(g, B, n_a, c, dt, pad)
+    Xb, Zb = _side(g, B, n_b, c, dt, pad)
+    ga = torch.rand((c,), generator=g, device="cuda") + 0.5
+    gb = torch.rand((c,), generator=g, device="cuda") + 0.5
+    e0a, e0b = 1000, 7
+    d, eps, theta = min(64, c), 1e-6, 10000.0
+    ibs_a, ibs_b = (n_a + pad) * c, (n_b + pad) * c
+    Na, Nb = n_a // m_a, n_b // m_b
+    tdt = Xa.dtype
+    sep_a = torch.full((B, max(Na, 1) + 1, c), 7, dtype=tdt, device="cuda")
+    sep_b = torch.full((B, max(Nb, 1) + 1, c), 7, dtype=tdt, device="cuda")
+    pair_a, pair_b = sep_a.clone(), sep_b.clone()
+    obs_a, obs_b = sep_a.shape[1] * c, sep_b.shape[1] * c
+    lib.csahca_compress_norm_rope(Xa, Za, None, ga, sep_a, B, n_a, c, m_a, e0a, d, eps, theta, dt, ibs_a,
+                                  obs_a)
+    lib.csahca_compress_norm_rope(Xb, Zb, None, gb, sep_b, B, n_b, c, m_b, e0b, d, eps, theta, dt, ibs_b,
+                                  obs_b)
+    lib.csahca_compress_pair_norm_rope(Xa, Za, ga, pair_a, n_a, m_a, e0a, ibs_a, obs_a, Xb, Zb, gb, pair_b,
+                                       n_b, m_b, e0b, ibs_b, obs_b, B, c, d, eps, theta, dt)
+    torch.cuda.synchronize()
+    iv = torch.int16 if dt == BF16 else torch.int32
+    assert torch.equal(pair_a.view(iv), sep_a.view(iv))
+    assert torch.equal(pair_b.view(iv), sep_b.view(iv))
+    assert bool((pair_a[:, Na:] == 7).all()) and bool((pair_b[:, Nb:] == 7).all())
+    if name == "decode_pair":
+        for X, Z, out, m, gg, e0, N in ((Xa, Za, pair_a, m_a, ga, e0a, Na), (Xb, Zb, pair_b, m_b, gb, e0b, Nb)):
+            x = oracle.decode(_codes(X, dt), dt)
+            z = oracle.decode(_codes(Z, dt), dt)
+            got = oracle.decode(_codes(out, dt), dt)
+            for b in range(B):
+                ref, xn, kc = pooled_reference(x[b, :N * m], z[b, :N * m], m, None, gg.cpu().numpy(), d, e0)
+                check_pooled(got[b, :N], ref, xn, kc, d, dt)

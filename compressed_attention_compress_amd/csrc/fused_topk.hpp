@@ -41,6 +41,11 @@ struct FtScratch {
 // ---------------------------------------------------------------------------------------
 // block-wide helpers (FT_NT threads; every thread calls them)
 // ---------------------------------------------------------------------------------------
+// Workgroup barrier for LDS traffic only: this wave's LDS operations have completed, then
+// s_barrier.  __syncthreads would also wait for the wave's outstanding global stores (the
+// chunk's scores, just issued), which nothing here reads back.
+CSAHCA_DEV void ft_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 CSAHCA_DEV int ft_lane() { return threadIdx.x & 63; }
 CSAHCA_DEV int ft_wave() { return threadIdx.x >> 6; }
 
@@ -48,14 +53,14 @@ CSAHCA_DEV int ft_wave() { return threadIdx.x >> 6; }
 CSAHCA_DEV uint32_t ft_block_scan(uint32_t c, uint32_t& total, FtScratch& sc) {
   const uint32_t incl = wave_incl_scan(c);
   if (ft_lane() == 63) sc.scan[ft_wave()] = incl;
-  __syncthreads();
+  ft_barrier();
   uint32_t before = 0, all = 0;
 #pragma unroll
   for (int w = 0; w < FT_NW; ++w) {
     before += w < ft_wave() ? sc.scan[w] : 0u;
     all += sc.scan[w];
   }
-  __syncthreads();
+  ft_barrier();
   total = all;
   return before + incl - c;
 }
@@ -72,7 +77,7 @@ CSAHCA_DEV uint32_t ft_compact(const uint64_t (&kr)[KP], Pred pred, Sink sink, F
     bal[j] = __ballot(pred(kr[j]));
     if (ft_lane() == 0) sc.jw[j * FT_NW + ft_wave()] = (uint32_t)__popcll(bal[j]);
   }
-  __syncthreads();
+  ft_barrier();
   if (ft_wave() == 0) {
     constexpr int PER = (KP * FT_NW + 63) / 64;
     uint32_t c[PER], sum = 0;
@@ -92,7 +97,7 @@ CSAHCA_DEV uint32_t ft_compact(const uint64_t (&kr)[KP], Pred pred, Sink sink, F
     }
     if (ft_lane() == 63) sc.total = incl;
   }
-  __syncthreads();
+  ft_barrier();
 #pragma unroll
   for (int j = 0; j < KP; ++j) {
     if ((bal[j] >> ft_lane()) & 1ull) {
@@ -102,7 +107,7 @@ CSAHCA_DEV uint32_t ft_compact(const uint64_t (&kr)[KP], Pred pred, Sink sink, F
     }
   }
   const uint32_t total = sc.total;
-  __syncthreads();
+  ft_barrier();
   return total;
 }
 
@@ -132,7 +137,7 @@ CSAHCA_DEV FtCut ft_local_cut(const uint32_t (&u)[FT_LKPT], int n, int JT, int J
     sc.red_and[ft_wave()] = a;
     sc.red_or[ft_wave()] = o;
   }
-  __syncthreads();
+  ft_barrier();
   a = ~0u;
   o = 0u;
 #pragma unroll
@@ -140,7 +145,7 @@ CSAHCA_DEV FtCut ft_local_cut(const uint32_t (&u)[FT_LKPT], int n, int JT, int J
     a &= sc.red_and[w];
     o |= sc.red_or[w];
   }
-  __syncthreads();
+  ft_barrier();
   if (a == o) return {(uint64_t)a + 1, 0u};  // all equal: no cut separates them
   int hb = 31 - __builtin_clz(a ^ o);          // highest bit on which the keys differ
   uint32_t prefix = a & (hb == 31 ? 0u : ~0u << (hb + 1));
@@ -150,11 +155,11 @@ CSAHCA_DEV FtCut ft_local_cut(const uint32_t (&u)[FT_LKPT], int n, int JT, int J
     const uint32_t dmask = (2u << (hb - lo)) - 1u;  // digit: bits lo .. hb
     const uint32_t hmask = hb == 31 ? 0u : ~0u << (hb + 1);
     sc.hist[threadIdx.x] = 0u;  // FT_NT == 256 bins
-    __syncthreads();
+    ft_barrier();
 #pragma unroll
     for (int j = 0; j < FT_LKPT; ++j)
       if (u[j] && (u[j] & hmask) == prefix) atomicAdd(&sc.hist[(u[j] >> lo) & dmask], 1u);
-    __syncthreads();
+    ft_barrier();
     // thread t owns digit 255 - t: cum = keys whose digit is >= it, plus those above
     const uint32_t c = sc.hist[255 - threadIdx.x];
     uint32_t tot;
@@ -162,7 +167,7 @@ CSAHCA_DEV FtCut ft_local_cut(const uint32_t (&u)[FT_LKPT], int n, int JT, int J
     // the largest digit D with cum(D) >= JT: the first thread whose cum reaches JT
     const uint64_t hit = __ballot(cum >= (uint32_t)JT);
     if (ft_lane() == 0) sc.first[ft_wave()] = hit ? (uint32_t)(ft_wave() * 64 + __builtin_ctzll(hit)) : 0xFFFFu;
-    __syncthreads();
+    ft_barrier();
     uint32_t tf = 0xFFFFu;
 #pragma unroll
     for (int w = 0; w < FT_NW; ++w) tf = min(tf, sc.first[w]);
@@ -170,9 +175,9 @@ CSAHCA_DEV FtCut ft_local_cut(const uint32_t (&u)[FT_LKPT], int n, int JT, int J
       sc.found_count = cum;
       sc.found_bin = c;
     }
-    __syncthreads();
+    ft_barrier();
     const uint32_t D = 255u - tf, cD = sc.found_count, hD = sc.found_bin;
-    __syncthreads();
+    ft_barrier();
     if (cD <= (uint32_t)JMAX) return {(uint64_t)(prefix | (D << lo)), cD};
     if (lo == 0) return {(uint64_t)(prefix | D) + 1, cD - hD};  // one key value: list those above
     above = cD - hD;

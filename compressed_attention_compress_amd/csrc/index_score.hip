@@ -388,7 +388,20 @@ __global__ __launch_bounds__(256, 2) void index_score_dec128(
   const int n = e_end - e_begin;
   float* srow = scores + (size_t)q * N_c;
   uint32_t* grow = gkeys + (size_t)q * NG;
-  for (int i = (int)threadIdx.x; i < n; i += 256) srow[e_begin + i] = s_sc[i];
+  // the chunk's scores, entry threadIdx.x + 256 j: all LDS reads issued before the first
+  // store (one wait, not one per store), kept for the list below
+  constexpr int SPT = SCORE_STAGE / 256;
+  float sv[SPT];
+#pragma unroll
+  for (int j = 0; j < SPT; ++j) {
+    const int i = (int)threadIdx.x + 256 * j;
+    sv[j] = i < n ? s_sc[i] : 0.f;
+  }
+#pragma unroll
+  for (int j = 0; j < SPT; ++j) {
+    const int i = (int)threadIdx.x + 256 * j;
+    if (i < n) srow[e_begin + i] = sv[j];
+  }
   for (int i = (int)threadIdx.x; i < cdiv(n, GROUP); i += 256) grow[e_begin / GROUP + i] = s_gk[i];
   if constexpr (LISTS) {
     const int keff = min(cl.k, V);
@@ -398,10 +411,11 @@ __global__ __launch_bounds__(256, 2) void index_score_dec128(
       static_assert(sizeof(FtScratch) <= sizeof(ring), "the cut's scratch fits the key ring");
       uint32_t u[FT_LKPT];
       uint64_t kr[FT_LKPT];
+      static_assert(FT_LKPT == SPT, "the list takes the scores read above");
 #pragma unroll
       for (int j = 0; j < FT_LKPT; ++j) {
         const int i = (int)threadIdx.x + 256 * j;
-        u[j] = i < n ? score_key(s_sc[i]) : 0u;
+        u[j] = i < n ? score_key(sv[j]) : 0u;
         kr[j] = i < n ? ((uint64_t)u[j] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)(e_begin + i)) : 0ull;
       }
       // list about this query's share of the top k per chunk plus four standard
@@ -419,6 +433,7 @@ __global__ __launch_bounds__(256, 2) void index_score_dec128(
       for (int i = (int)cut.count + (int)threadIdx.x; i < cl.JMAX; i += 256) list[i] = 0ull;  // padding
       if (threadIdx.x == 0) cl.edge[(size_t)q * FT_MAX_P + chunk] = cut.cut == 0ull ? 0ull : cut.cut << 32;
     }
+    if (threadIdx.x == 0 && blockIdx.x == 0) cl.path[q] = FT_LISTS_READY;
   }
   CSAHCA_TRACE(4);
   CSAHCA_TRACE_RT(15);
@@ -754,6 +769,35 @@ int index_score_impl(const void* q_idx, const float* w_idx, const void* k_idx, i
 
 }  // namespace csahca
 
+namespace {
+
+// one word per thread set to zero (a fill kernel rather than hipMemsetAsync, so that a
+// captured graph holds only kernels)
+__global__ __launch_bounds__(256) void clear_words(uint32_t* p, int n) {
+  const int i = (int)(blockIdx.x * 256 + threadIdx.x);
+  if (i < n) p[i] = 0u;
+}
+
+}  // namespace
+
+namespace csahca {
+
+// The chunk lists of a decode workspace (null fields when the layout has none)
+ChunkLists chunk_lists_of(char* ws, const WsLayout& L, int k) {
+  ChunkLists cl{};
+  if (!L.plan.lists) return cl;
+  cl.edge = (uint64_t*)(ws + L.edge_off);
+  cl.cand = (uint64_t*)(ws + L.cand_off);
+  cl.path = (uint32_t*)(ws + L.path_off);
+  cl.k = k;
+  cl.P = L.plan.P;
+  cl.JMAX = L.plan.JMAX;
+  cl.CH = L.plan.CH;
+  return cl;
+}
+
+}  // namespace csahca
+
 extern "C" int lightning_index_score(const void* q_idx, const float* w_idx, const void* k_idx,
                                      int idx_dtype, const int* q_pos, int m, int B, int Tq,
                                      int n_ih, int c_I, int N_c, int k, float* scores,
@@ -765,6 +809,18 @@ extern "C" int lightning_index_score(const void* q_idx, const float* w_idx, cons
   const WsLayout L = ws_layout((long long)B * Tq, N_c, k, Tq == 1);
   if (!workspace || ws_bytes < L.total)
     return fail(CSAHCA_EWORKSPACE, "lightning_index_score: workspace missing or too small");
-  return index_score_impl(q_idx, w_idx, k_idx, idx_dtype, q_pos, m, B, Tq, n_ih, c_I, N_c, scores,
-                          (uint32_t*)((char*)workspace + L.gkeys_off), (hipStream_t)stream);
+  // as in lightning_index_topk, the decode launch also writes the chunk lists (and marks
+  // each query's lists ready); a decode layout without them clears the marks
+  char* ws = (char*)workspace;
+  uint32_t* gkeys = (uint32_t*)(ws + L.gkeys_off);
+  const hipStream_t s = (hipStream_t)stream;
+  const ChunkLists cl = chunk_lists_of(ws, L, k);
+  if (cl.cand && index_can_list(idx_dtype, Tq, c_I, n_ih, L.plan))
+    return index_score_impl(q_idx, w_idx, k_idx, idx_dtype, q_pos, m, B, Tq, n_ih, c_I, N_c, scores, gkeys, s,
+                            &cl);
+  st = index_score_impl(q_idx, w_idx, k_idx, idx_dtype, q_pos, m, B, Tq, n_ih, c_I, N_c, scores, gkeys, s);
+  if (st != CSAHCA_OK || !cl.path) return st;
+  const int nq = B * Tq;
+  hipLaunchKernelGGL(clear_words, dim3((unsigned)cdiv(nq, 256)), dim3(256), 0, s, cl.path, nq);
+  return launch_status("lightning_index_score");
 }

@@ -27,6 +27,9 @@ constexpr int FT_MAX_SLOTS = SEL_THREADS * KPT;      // chunks x list capacity p
 constexpr uint32_t FT_PATH_LISTS = 1;   // the union of the chunk lists held the top k
 constexpr uint32_t FT_PATH_GROUPS = 2;  // selected through the group maxima and scores
 constexpr uint32_t FT_PATH_ALL = 3;     // k >= the usable entries: every one selected
+// written to a query's word by the scoring launch that wrote its chunk lists, so that the
+// selection launch (also through lightning_index_select) takes the lists only after them
+constexpr uint32_t FT_LISTS_READY = 0x4C157EADu;
 
 // number of usable entries for query t of sequence b: block s is usable iff
 // m*(s+1) - 1 <= p, i.e. s < (p+1)/m
@@ -113,13 +116,16 @@ inline WsLayout ws_layout(long long nq, int N_c, int k, bool decode) {
 struct ChunkLists {
   uint64_t* edge;  // [nq][FT_MAX_P] every unlisted entry of the chunk has a smaller key
   uint64_t* cand;  // [nq][P][JMAX] listed keys in index order, then zeros
-  uint32_t* path;  // [nq] FT_PATH_* of each query's selection
+  uint32_t* path;  // [nq] FT_LISTS_READY once the lists are written, then FT_PATH_*
   int k, P, JMAX, CH;  // top-k size; the plan's list layout and chunk length
 };
 
 // argument checks shared by lightning_index_score and lightning_index_topk
 int index_check_common(const void* q_idx, const float* w_idx, const void* k_idx, int idx_dtype,
                        const int* q_pos, int m, int B, int Tq, int n_ih, int c_I, int N_c, int k);
+
+// the chunk lists of a workspace laid out by ws_layout (all fields null without them)
+ChunkLists chunk_lists_of(char* ws, const WsLayout& L, int k);
 
 // whether index_score_impl can write chunk lists for these arguments
 bool index_can_list(int idx_dtype, int Tq, int c_I, int n_ih, const TopkPlan& plan);

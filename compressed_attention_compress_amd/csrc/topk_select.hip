@@ -271,7 +271,9 @@ __global__ __launch_bounds__(SEL_THREADS) void select_topk(
     return;
   }
   uint64_t kr[KPT];
-  if (cl.cand) {
+  // (a thread may see its own workgroup's FT_PATH_GROUPS below instead of the old word:
+  // either way not FT_LISTS_READY, so every thread takes the same branch)
+  if (cl.cand && cl.path[q] == FT_LISTS_READY) {
     // The union: slot s = chunk * JMAX + position (lists are padded with zero keys);
     // thread (wave, lane) holds slots wave * 64 KPT + 64 j + lane, so that (wave, j, lane)
     // order is slot order, which is index order (chunks are index ranges, each list is in
@@ -339,8 +341,8 @@ __global__ __launch_bounds__(SEL_THREADS) void select_topk(
       CSAHCA_TRACE_RT(15);
       return;
     }
-    if (threadIdx.x == 0) cl.path[q] = FT_PATH_GROUPS;
   }
+  if (cl.path && threadIdx.x == 0) cl.path[q] = FT_PATH_GROUPS;
   // group maxima, coalesced: thread t holds groups j*SEL_THREADS + t (j < KPT).  A group's
   // key is its maximum score key, then the lower group index: as groups are index ranges,
   // that orders equal maxima as their best entries are ordered.
@@ -423,8 +425,10 @@ extern "C" int lightning_index_select(const float* scores, const int* q_pos, int
   const WsLayout L = ws_layout((long long)B * Tq, N_c, k, Tq == 1);
   if (!workspace || ws_bytes < L.total)
     return fail(CSAHCA_EWORKSPACE, "lightning_index_select: workspace missing or too small");
+  // the chunk lists are taken for the queries whose lists the scoring launch marked ready
+  const ChunkLists cl = chunk_lists_of((char*)workspace, L, k);
   return index_select_impl(scores, (const uint32_t*)((char*)workspace + L.gkeys_off), q_pos, m, B, Tq,
-                     N_c, k, topk_idx, topk_score, (hipStream_t)stream);
+                           N_c, k, topk_idx, topk_score, (hipStream_t)stream, cl.cand ? &cl : nullptr);
 }
 
 namespace {
@@ -457,14 +461,7 @@ int index_topk_impl(const char* name, const void* q_idx, const float* w_idx, con
   if (index_can_list(idx_dtype, Tq, c_I, n_ih, L.plan)) {
     // decode: the scoring launch also writes every chunk's list; the selection launch
     // selects from their union first
-    ChunkLists cl;
-    cl.edge = (uint64_t*)(ws + L.edge_off);
-    cl.cand = (uint64_t*)(ws + L.cand_off);
-    cl.path = (uint32_t*)(ws + L.path_off);
-    cl.k = k;
-    cl.P = L.plan.P;
-    cl.JMAX = L.plan.JMAX;
-    cl.CH = L.plan.CH;
+    const ChunkLists cl = chunk_lists_of(ws, L, k);
     st = index_score_impl(q_idx, w_idx, k_idx, idx_dtype, q_pos, m, B, Tq, n_ih, c_I, N_c, scores, gkeys,
                           s, &cl);
     if (st != CSAHCA_OK) return st;

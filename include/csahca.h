@@ -209,9 +209,10 @@ int lightning_index_topk_noalloc(const void* q_idx, const float* w_idx, const vo
 /*
  * The two halves of lightning_index_topk, for callers that time or check them apart.
  * lightning_index_score writes every usable score to `scores` [B, Tq, N_c] and the
- * per-16-entry group maxima to the workspace; lightning_index_select must then be given
- * the same scores, workspace and shape arguments.  Running both equals one
- * lightning_index_topk call.  Same limits and workspace size.
+ * per-16-entry group maxima to the workspace (at decode, where lightning_index_topk
+ * fuses the chunk lists into scoring, the lists too); lightning_index_select must then be
+ * given the same scores, workspace and shape arguments.  Running both equals one
+ * lightning_index_topk call, launch for launch.  Same limits and workspace size.
  */
 int lightning_index_score(const void* q_idx, const float* w_idx, const void* k_idx,
                           int idx_dtype, const int* q_pos, int m, int B, int Tq, int n_ih,

@@ -177,3 +177,32 @@ def test_one_workspace_across_shapes():
         qc, kc = encode(qI, FP8), encode(KI, FP8)
         q_pos = decode_pos(B, N_c)
         check(qc, w, kc, q_pos, 4, k, run(qc, w, kc, q_pos, 4, k, ws=ws), f"shape {i}", path=LISTS)
+
+
+def test_split_calls_use_the_lists_too():
+    """lightning_index_score + lightning_index_select at decode: the scoring launch writes
+    and marks the chunk lists, the selection takes them (path LISTS) and the result is the
+    fused call's, bit for bit.  A second selection over the same scoring output finds the
+    mark consumed and selects through the group maxima: same result again."""
+    B, N_c, k = 4, 30000, 1024
+    _, qI, w, KI = draw(300, B, N_c)
+    qc, kc = encode(qI, FP8), encode(KI, FP8)
+    q_pos = decode_pos(B, N_c)
+    fused = run(qc, w, kc, q_pos, 4, k)
+    ws_bytes = lib.lightning_index_topk_workspace_size(B, 1, 64, N_c, k)
+    ws = torch.full((ws_bytes,), 0xA5, dtype=torch.uint8, device=H.DEV)
+    scores = torch.empty((B, 1, N_c), dtype=torch.float32, device=H.DEV)
+    dq, dw, dk, dp = H.to_dev(qc), H.to_dev(w), H.to_dev(kc), H.to_dev(q_pos)
+    lib.lightning_index_score(dq, dw, dk, FP8, dp, 4, B, 1, 64, 128, N_c, k, scores, ws, ws_bytes)
+    path_off = ws_bytes - (-(-B * 4 // 256) * 256)
+    for want_path in (LISTS, GROUPS):
+        idx = torch.full((B, 1, k), -7, dtype=torch.int32, device=H.DEV)
+        sc = torch.full((B, 1, k), float("nan"), dtype=torch.float32, device=H.DEV)
+        lib.lightning_index_select(scores, dp, 4, B, 1, N_c, k, idx, sc, ws, ws_bytes)
+        torch.cuda.synchronize()
+        paths = ws[path_off:path_off + 4 * B].view(torch.int32).cpu().numpy()
+        print(f"split selection paths {paths.tolist()}", flush=True)
+        assert np.all(paths == want_path)
+        assert np.array_equal(idx.cpu().numpy(), fused[0])
+        assert np.array_equal(sc.cpu().numpy(), fused[1])
+        assert np.array_equal(scores.cpu().numpy(), fused[2])

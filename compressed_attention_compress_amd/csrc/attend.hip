@@ -373,6 +373,12 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && NS == 2) ? 2 : 1) void attend_
   if (CSA) __syncthreads();  // sidx complete
   CSAHCA_TRACE(1);
 
+  // Query RMSNorm + RoPE: the rotation angles depend only on the wave's query position,
+  // so they are formed while Q is in flight (lane i < d_rope/2 forms pair i's)
+  const int nr_P = a.d_rope / 2;  // <= 64 rotated pairs (the host checks)
+  float nr_cs = 1.f, nr_sn = 0.f;
+  if (a.qnr && lane < nr_P) csahca::rope_cos_sin(p, csahca::rope_freq(lane, a.d_rope, a.nr_theta), nr_cs, nr_sn);
+
   // The compiler does not assume that row DMAs and register loads complete in order, so
   // its wait for Q (forced here by the empty asm, once, rather than before the first MFMA
   // of every iteration) drains every load issued so far: only the tiles needed first.
@@ -380,55 +386,76 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && NS == 2) ? 2 : 1) void attend_
     for (int tt = 0; tt < TPI && tt < ntile; ++tt) issue(tt, false);
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(qf[ks]));
-  if (a.qnr) {
+  if (a.qnr) {  // the gains arrived with Q
 #pragma unroll
     for (int i = 0; i < GPT; ++i) s_gain[(int)threadIdx.x + i * NW * 64] = gq[i];
-    lds_reads_done_barrier();
+  }
+  for (int tt = TPI; tt < NS && tt < ntile; ++tt) issue(tt, false);
+  if (a.qnr) {
     // RMSNorm of the query row (this lane holds channels g*C/4 .. +C/4 of head h0+row16,
-    // its three partners the rest), then RoPE on the last d_rope channels.  The angles
-    // depend only on the wave's query position: lane i < d_rope/2 forms pair i's, the lanes
-    // holding rotated channels fetch theirs.
-    float ss = 0.f;
+    // its three partners the rest), then RoPE on the last d_rope channels; the arithmetic
+    // of the row kernel (norm_rope8), with the sum of squares in another order.  The
+    // ring's DMA is in flight meanwhile (the barrier waits for LDS only).
+    lds_reads_done_barrier();
+    float ssp[4] = {0.f, 0.f, 0.f, 0.f};  // four chains (the sum's order is fixed)
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const u32x4 w4 = __builtin_bit_cast(u32x4, qf[ks]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float lo = __uint_as_float(w4[e] << 16), hi = __uint_as_float(w4[e] & 0xFFFF0000u);
-        ss = fmaf(lo, lo, ss);
-        ss = fmaf(hi, hi, ss);
+        ssp[e] = fmaf(lo, lo, ssp[e]);
+        ssp[e] = fmaf(hi, hi, ssp[e]);
       }
     }
-    ss = sum_over_row_groups(ss);
+    const float ss = sum_over_row_groups((ssp[0] + ssp[1]) + (ssp[2] + ssp[3]));
     const float inv = 1.0f / sqrtf(ss / (float)C + a.nr_eps);
-    const int P = a.d_rope / 2;   // <= 64 rotated pairs (the host checks)
+    // d_rope <= 128, so only lane group 3 (channels 384..511) holds rotated channels, and
+    // in step ks it holds pairs i0 .. i0+3, i0 = (384 + 8 ks - (C - d_rope)) / 2, the same
+    // for all its lanes: their angles come by readlane
     const int r0 = C - a.d_rope;  // first rotated channel
-    float cs = 1.f, sn = 0.f;
-    if (lane < P) csahca::rope_cos_sin(p, csahca::rope_freq(lane, a.d_rope, a.nr_theta), cs, sn);
+    constexpr int KB = 4;         // steps per batch of gain reads (one LDS wait per batch)
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int d0 = g * (C / 4) + 8 * ks;
-      const u32x4 w4 = __builtin_bit_cast(u32x4, qf[ks]);
-      float v[8];
+    for (int kb = 0; kb < KS; kb += KB) {
+      f32x4 gv[KB][2];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        v[2 * e] = __uint_as_float(w4[e] << 16) * inv * s_gain[d0 + 2 * e];
-        v[2 * e + 1] = __uint_as_float(w4[e] & 0xFFFF0000u) * inv * s_gain[d0 + 2 * e + 1];
+      for (int u = 0; u < KB; ++u) {
+        const int d0 = g * (C / 4) + 8 * (kb + u);
+        gv[u][0] = *reinterpret_cast<const f32x4*>(s_gain + d0);
+        gv[u][1] = *reinterpret_cast<const f32x4*>(s_gain + d0 + 4);
       }
-      if (3 * (C / 4) + 8 * ks + 8 > r0) {  // some lane group holds rotated channels here
-        const int i0 = (d0 - r0) / 2;        // negative outside the rotated channels
 #pragma unroll
-        for (int q2 = 0; q2 < 4; ++q2) {
-          const int src = min(max(i0 + q2, 0), max(P - 1, 0));
-          const float cq = __shfl(cs, src, 64), sq = __shfl(sn, src, 64);
-          if (d0 >= r0) csahca::rope_apply(v[2 * q2], v[2 * q2 + 1], cq, sq);
+      for (int u = 0; u < KB; ++u) {
+        const int ks = kb + u;
+        const u32x4 w4 = __builtin_bit_cast(u32x4, qf[ks]);
+        const float gg[8] = {gv[u][0][0], gv[u][0][1], gv[u][0][2], gv[u][0][3],
+                             gv[u][1][0], gv[u][1][1], gv[u][1][2], gv[u][1][3]};
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[2 * e] = __uint_as_float(w4[e] << 16) * (inv * gg[2 * e]);
+          v[2 * e + 1] = __uint_as_float(w4[e] & 0xFFFF0000u) * (inv * gg[2 * e + 1]);
         }
+        const int c3 = 3 * (C / 4) + 8 * ks;  // group 3's first channel in this step
+        if (c3 >= r0) {                      // uniform
+          const int i0 = (c3 - r0) / 2;
+#pragma unroll
+          for (int q2 = 0; q2 < 4; ++q2) {
+            const float cq = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, nr_cs), i0 + q2));
+            const float sq = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, nr_sn), i0 + q2));
+            float a0 = v[2 * q2], a1 = v[2 * q2 + 1];
+            csahca::rope_apply(a0, a1, cq, sq);
+            if (g == 3) {
+              v[2 * q2] = a0;
+              v[2 * q2 + 1] = a1;
+            }
+          }
+        }
+        qf[ks] = __builtin_bit_cast(bf16x8, u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                                  pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])});
       }
-      qf[ks] = __builtin_bit_cast(bf16x8, u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
-                                                pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])});
     }
   }
-  for (int tt = TPI; tt < NS && tt < ntile; ++tt) issue(tt, false);
 
   // l_run: mass of the fp32 weights (log-sum-exp, split records); lq_run: sum of the same
   // weights rounded to bf16, as they enter the PV product (normalises the output)
@@ -568,8 +595,13 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && NS == 2) ? 2 : 1) void attend_
       // the weights enter O^T += E^T P^T as bf16; their rounded sum normalises the output,
       // which is then an exact convex combination of its rows (a query with a single
       // usable row returns that row's bits)
+      uint32_t pk[NSV / 2];  // consecutive weights as packed bf16 pairs, and their values
 #pragma unroll
-      for (int e = 0; e < NSV; ++e) pe[e] = round_bf16(pe[e]);
+      for (int e = 0; e < NSV / 2; ++e) {
+        pk[e] = pack_bf16x2(pe[2 * e], pe[2 * e + 1]);
+        pe[2 * e] = __uint_as_float(pk[e] << 16);
+        pe[2 * e + 1] = __uint_as_float(pk[e] & 0xFFFF0000u);
+      }
 #pragma unroll
       for (int e = 0; e < NSV / 2; ++e) ps[e] = pe[e] + pe[e + NSV / 2];
 #pragma unroll
@@ -579,14 +611,11 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && NS == 2) ? 2 : 1) void attend_
       lq_run = lq_run * alpha + sum_over_row_groups(ps[0]);
       m_run = m_new;
       // P^T as B operands: k-slot e <-> slot (e < 4 ? 4g+e : 16+4g+e-4) of its tile
-      const bf16x8 pfA = __builtin_bit_cast(bf16x8, u32x4{pack_rounded_bf16x2(pe[0], pe[1]), pack_rounded_bf16x2(pe[2], pe[3]),
-                                                          pack_rounded_bf16x2(pe[4], pe[5]), pack_rounded_bf16x2(pe[6], pe[7])});
+      const bf16x8 pfA = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
       bf16x8 pfB;
       if (TPI == 2)
-        pfB = __builtin_bit_cast(bf16x8, u32x4{pack_rounded_bf16x2(pe[8 % NSV], pe[9 % NSV]),
-                                               pack_rounded_bf16x2(pe[10 % NSV], pe[11 % NSV]),
-                                               pack_rounded_bf16x2(pe[12 % NSV], pe[13 % NSV]),
-                                               pack_rounded_bf16x2(pe[14 % NSV], pe[15 % NSV])});
+        pfB = __builtin_bit_cast(bf16x8, u32x4{pk[4 % (NSV / 2)], pk[5 % (NSV / 2)], pk[6 % (NSV / 2)],
+                                               pk[7 % (NSV / 2)]});
       // ---- O^T += E^T P^T: E^T through LDS transpose reads, issued in asm ahead of use ----
       // ds_read_b64_tr_b16: in each 16-lane group, lane i receives column i%4 of the four
       // 4-element rows addressed by lanes i/4, i/4+4, i/4+8, i/4+12.  Lane j addresses row

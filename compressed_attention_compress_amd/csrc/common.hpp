@@ -52,27 +52,20 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 CSAHCA_DEV float bf16_to_f32(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
 
 // round to nearest even; inputs are finite
-CSAHCA_DEV uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
+// float -> bfloat16, round to nearest even: gfx950's v_cvt_pk_bf16_f32 (two values per
+// instruction)
+typedef __bf16 bf16x2_hw __attribute__((ext_vector_type(2)));
+
+CSAHCA_DEV uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 CSAHCA_DEV uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+  const bf16x2_hw v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
-// the float value of f rounded to bf16 (nearest even; f finite): low 16 bits cleared
-CSAHCA_DEV float round_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return __uint_as_float(u & 0xFFFF0000u);
-}
+// the float value of f rounded to bf16 (nearest even): low 16 bits cleared
+CSAHCA_DEV float round_bf16(float f) { return __uint_as_float((uint32_t)f32_to_bf16(f) << 16); }
 
-// two values already rounded to bf16 (round_bf16), packed without another rounding
-CSAHCA_DEV uint32_t pack_rounded_bf16x2(float lo, float hi) {
-  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
-}
 
 // float16, round to nearest even (the hardware conversion); two halves in one word
 CSAHCA_DEV uint32_t pack_f16x2(float lo, float hi) {

@@ -98,12 +98,17 @@ CSAHCA_DEV uint32_t ft_compact(const uint64_t (&kr)[KP], Pred pred, Sink sink, F
     if (ft_lane() == 63) sc.total = incl;
   }
   ft_barrier();
+  // this wave's offsets, read before any sink writes (which may alias them for the
+  // compiler: each read would wait for the writes before it)
+  uint32_t off[KP];
+#pragma unroll
+  for (int j = 0; j < KP; ++j) off[j] = sc.jw[j * FT_NW + ft_wave()];
 #pragma unroll
   for (int j = 0; j < KP; ++j) {
     if ((bal[j] >> ft_lane()) & 1ull) {
       const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal[j] >> 32),
                                                        __builtin_amdgcn_mbcnt_lo((uint32_t)bal[j], 0u));
-      sink(sc.jw[j * FT_NW + ft_wave()] + below, kr[j]);
+      sink(off[j] + below, kr[j]);
     }
   }
   const uint32_t total = sc.total;

@@ -208,13 +208,17 @@ CSAHCA_DEV uint32_t compact_in_order(const uint64_t (&kr)[KP], Pred pred, Sink s
     if (lane == 63) sc.total = incl;
   }
   __syncthreads();
+  // this wave's KP offsets, read before any sink writes (which the compiler cannot tell
+  // apart from the offsets: each read would wait for the writes before it)
+  uint32_t off[KP];
+#pragma unroll
+  for (int j = 0; j < KP; ++j) off[j] = sc.jw[JMAJOR ? j * NWAVE + wave : wave * KP + j];
 #pragma unroll
   for (int j = 0; j < KP; ++j) {
     const bool p = pred(kr[j]);
     const uint64_t bal = __ballot(p);
     if (p)
-      sink(sc.jw[JMAJOR ? j * NWAVE + wave : wave * KP + j] +
-               __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u)),
+      sink(off[j] + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u)),
            kr[j], j);
   }
   const uint32_t total = sc.total;

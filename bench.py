@@ -377,15 +377,26 @@ class Workload:
         return cfg.B * f8, cfg.B * bf
 
 
+# the sources the decode scoring kernel is built from (its file and the headers it includes)
+SCORE_SOURCES = ("index_score.hip", "fused_topk.hpp", "indexer.hpp", "common.hpp")
+
+
+def score_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for name in SCORE_SOURCES:
+        with open(os.path.join(ROOT, "compressed_attention_compress_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
 def read_traffic(kernel_name):
-    """HBM traffic of the dominant kernel from committed counter runs, if the kernel source
-    is unchanged since they were taken (else None)."""
+    """HBM traffic of the dominant kernel from committed counter runs, if the kernel's
+    sources are unchanged since they were taken (else None)."""
     try:
-        import hashlib
         with open(PROFILE_TRAFFIC) as f:
             rec = json.load(f)
-        src = os.path.join(ROOT, "compressed_attention_compress_amd", "csrc", "index_score.hip")
-        h = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        h = score_source_hash()
         ent = rec.get(kernel_name)
         if ent and ent.get("source_sha256") == h:
             return ent["bytes_per_launch"]
@@ -418,12 +429,10 @@ def _counter_means(folder, counter, name_part):
 def write_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, out_path):
     """HBM bytes per launch of the dominant kernel: FETCH_SIZE + WRITE_SIZE (KiB per
     dispatch), each scaled by what the same counter reads for a plain 1 GiB device copy."""
-    import hashlib
     cf, _ = _counter_means(copy_fetch_dir, "FETCH_SIZE", COPY_KERNEL)
     cw, _ = _counter_means(copy_write_dir, "WRITE_SIZE", COPY_KERNEL)
     f_scale = COPY_BYTES / (cf * 1024.0)   # true bytes per counted byte
     w_scale = COPY_BYTES / (cw * 1024.0)
-    src = os.path.join(ROOT, "compressed_attention_compress_amd", "csrc", "index_score.hip")
     rec = {"copy_calibration": {"bytes": COPY_BYTES, "fetch_kib": cf, "write_kib": cw,
                                 "fetch_scale": f_scale, "write_scale": w_scale}}
     for key, name in TRAFFIC_KERNELS.items():
@@ -432,7 +441,7 @@ def write_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, out_path
         rec[key] = {"fetch_kib_per_dispatch": fk, "write_kib_per_dispatch": wk,
                     "dispatches": [nf, nw],
                     "bytes_per_launch": round(fk * 1024.0 * f_scale + wk * 1024.0 * w_scale),
-                    "source_sha256": hashlib.sha256(open(src, "rb").read()).hexdigest()}
+                    "source_sha256": score_source_hash()}
     with open(out_path, "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec))

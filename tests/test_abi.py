@@ -65,6 +65,26 @@ def test_pool_validation():
               None) == ENOTSUP  # dtype
     assert pr(None, None, None, 3, 4, 24, 0, None, None, None, 100, 128, 800, 0, 1, 8, 1,
               None) == 0
+    # the pair with the norm: the pair's checks, then the norm's (each side its own gain and
+    # first entry)
+    pn = L.csahca_compress_pair_norm_rope
+    ok = [FAKE, FAKE, None, FAKE, 8, 4, 0, 64, 16, FAKE, FAKE, None, FAKE, 256, 128, 0, 2048, 16, 1, 8,
+          8, 1e-6, 1e4, 1, None]
+    bad_cases = [(7, 32, EINVAL),          # side a stride
+                 (14, 0, EINVAL),          # side b m
+                 (20, 12, EINVAL),         # d_rope % 8
+                 (20, 16, EINVAL),         # d_rope > c
+                 (21, -1.0, EINVAL),       # eps
+                 (22, 0.0, EINVAL),        # theta
+                 (6, -1, EINVAL),          # entry0_a
+                 (15, -3, EINVAL),         # entry0_b
+                 (2, FAKE + 4, EINVAL),    # gamma_a alignment
+                 (23, 2, ENOTSUP)]         # dtype
+    for i, v, want in bad_cases:
+        args = list(ok)
+        args[i] = v
+        assert pn(*args) == want, (i, v)
+        assert "csahca_compress_pair_norm_rope" in lib.last_error()
     # overlapped form: prev is 0 or 1, stream b pointers are required, an append of one
     # block with prev = 1 emits nothing
     ov = L.csa_compress_overlap

@@ -206,3 +206,37 @@ def test_split_calls_use_the_lists_too():
         assert np.array_equal(idx.cpu().numpy(), fused[0])
         assert np.array_equal(sc.cpu().numpy(), fused[1])
         assert np.array_equal(scores.cpu().numpy(), fused[2])
+
+
+def test_fused_call_in_a_graph_replays():
+    """lightning_index_topk captured in a HIP graph (the scoring launch marks each query's
+    lists ready, the selection takes them): replayed three times with new keys copied in
+    between, each replay equal to the eager call on the same inputs, bit for bit."""
+    B, N_c, k = 4, 30000, 1024
+    rng, qI, w, KI = draw(400, B, N_c)
+    qc, kc = encode(qI, FP8), encode(KI, FP8)
+    q_pos = decode_pos(B, N_c)
+    dq, dw, dk, dp = H.to_dev(qc), H.to_dev(w), H.to_dev(kc), H.to_dev(q_pos)
+    ws_bytes = lib.lightning_index_topk_workspace_size(B, 1, 64, N_c, k)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=H.DEV)
+    idx = torch.empty((B, 1, k), dtype=torch.int32, device=H.DEV)
+    sc = torch.empty((B, 1, k), dtype=torch.float32, device=H.DEV)
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        lib.lightning_index_topk(dq, dw, dk, FP8, dp, 4, B, 1, 64, 128, N_c, k, idx, sc, None, ws, ws_bytes,
+                                 stream=s)
+    path_off = ws_bytes - (-(-B * 4 // 256) * 256)
+    for rep in range(3):
+        KI2 = rng.standard_normal((B, N_c, 128), dtype=np.float32)
+        dk.copy_(H.to_dev(encode(KI2, FP8)))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got_i, got_s = idx.clone(), sc.clone()
+        paths = ws[path_off:path_off + 4 * B].view(torch.int32).cpu().numpy()
+        assert np.all(paths == LISTS), (rep, paths)
+        lib.lightning_index_topk(dq, dw, dk, FP8, dp, 4, B, 1, 64, 128, N_c, k, idx, sc, None, ws, ws_bytes)
+        torch.cuda.synchronize()
+        assert torch.equal(got_i, idx) and torch.equal(got_s, sc), rep

@@ -364,9 +364,10 @@ int csahca_compress_pair_norm_rope(const void* kv_a, const void* gate_a, const f
  * entries normalised, the last 64 dimensions rotated, in both branches), with the
  * norm_rope definition above.
  *
- * With q_norm = 1 the result equals csahca_norm_rope (norm = 1, pos = q_pos, pstride 1)
- * applied to q first, the normalised query rounded once to bfloat16 as there, and then
- * the _sink call; q itself is not written.  Keys are used as stored: compressed entries
+ * With q_norm = 1 the result is that of csahca_norm_rope (norm = 1, pos = q_pos,
+ * pstride 1) applied to q first, the normalised query rounded once to bfloat16 as there,
+ * and then the _sink call, up to the order in which the row's sum of squares is taken (a
+ * normalised element can round the other way); q itself is not written.  Keys are used as stored: compressed entries
  * are normalised when pooled (csahca_compress_norm_rope), and a window row is normalised
  * once, when its token arrives (csahca_norm_rope on the new rows), not at every step.
  *

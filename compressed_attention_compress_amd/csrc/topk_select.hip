@@ -4,7 +4,9 @@
 // keeps the k best blocks by index score); "DeepSeek-V4: Anatomy of an Open-Source
 // Frontier Model" (lesson 6.7): no more entries than exist can be picked.
 //
-// Selection: one workgroup per query.  Selection keys are
+// Selection: one workgroup per query, or, without chunk lists when k <= 512 and there are
+// at most 5120 groups (a prefill chunk), one wave per query (the second kernel below: the
+// same two thresholds found by bisection).  Selection keys are
 // (order-preserving score bits << 32) | (~index), so all keys are distinct and "larger
 // key" means "better, lower index on ties".  A group of 16 entries is keyed by its maximum
 // score, then by the lower group index (groups are index ranges, so this orders equal
@@ -33,8 +35,7 @@ constexpr int BPT = NBIN / SEL_THREADS;  // digits each thread scans
 constexpr int NWAVE = SEL_THREADS / 64;
 constexpr int SEL_COMPACT = 4096;        // list keys compacted into LDS for the k-th search
 constexpr int CPT = SEL_COMPACT / SEL_THREADS;
-constexpr int GPW = KPT * 64 / GROUP;    // listed groups per wave in the candidate gather
-static_assert(NWAVE * GPW == MAX_K, "the candidate gather holds k groups");
+static_assert(NWAVE * KPT * 64 / GROUP == MAX_K, "the candidate gather holds k groups");
 static_assert(FT_MAX_P <= 128 && SEL_THREADS >= 128, "the bounds are read by the first two waves");
 
 struct SelScratch {
@@ -248,13 +249,16 @@ CSAHCA_DEV void write_selected(const uint64_t (&kr)[KP], uint64_t T, int keff, i
 // K of the union of the query's lists: if no chunk left out an entry at or above K, the
 // union's keys >= K are the top k.  Otherwise, and without lists, it selects through the
 // group maxima as described at the top of this file.
-__global__ __launch_bounds__(SEL_THREADS) void select_topk(
+// KP is the number of keys a thread holds: KPT in general; 8 for a selection without lists
+// with k <= 512 and at most 8192 groups (a prefill chunk), which holds a thread to 64
+// registers, so that two workgroups share a compute unit.
+template <int KP>
+__global__ __launch_bounds__(SEL_THREADS, KP == KPT ? 1 : 8) void select_topk(
     const float* __restrict__ scores, const uint32_t* __restrict__ gmax,
     const int* __restrict__ q_pos, int m, int Tq, int N_c, int NG, int k,
     int* __restrict__ topk_idx, float* __restrict__ topk_score, ChunkLists cl) {
   __shared__ SelScratch sc;
   __shared__ int glist[MAX_K];
-  __shared__ uint64_t s_keys[SEL_COMPACT];
   CSAHCA_TRACE(0);
   CSAHCA_TRACE_RT(14);
   const int q = blockIdx.x;
@@ -274,10 +278,12 @@ __global__ __launch_bounds__(SEL_THREADS) void select_topk(
     if (cl.path && threadIdx.x == 0) cl.path[q] = FT_PATH_ALL;
     return;
   }
-  uint64_t kr[KPT];
+  constexpr int GPWk = KP * 64 / GROUP;  // listed groups per wave in the candidate gather
+  uint64_t kr[KP];
   // (a thread may see its own workgroup's FT_PATH_GROUPS below instead of the old word:
   // either way not FT_LISTS_READY, so every thread takes the same branch)
-  if (cl.cand && cl.path[q] == FT_LISTS_READY) {
+  if constexpr (KP == KPT) if (cl.cand && cl.path[q] == FT_LISTS_READY) {
+    __shared__ uint64_t s_keys[SEL_COMPACT];
     // The union: slot s = chunk * JMAX + position (lists are padded with zero keys);
     // thread (wave, lane) holds slots wave * 64 KPT + 64 j + lane, so that (wave, j, lane)
     // order is slot order, which is index order (chunks are index ranges, each list is in
@@ -347,13 +353,13 @@ __global__ __launch_bounds__(SEL_THREADS) void select_topk(
     }
   }
   if (cl.path && threadIdx.x == 0) cl.path[q] = FT_PATH_GROUPS;
-  // group maxima, coalesced: thread t holds groups j*SEL_THREADS + t (j < KPT).  A group's
+  // group maxima, coalesced: thread t holds groups j*SEL_THREADS + t (j < KP).  A group's
   // key is its maximum score key, then the lower group index: as groups are index ranges,
   // that orders equal maxima as their best entries are ordered.
   const uint32_t* grow = gmax + (size_t)q * NG;
   const int ng = cdiv(V, GROUP);
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) {
+  for (int j = 0; j < KP; ++j) {
     const int gi = j * SEL_THREADS + (int)threadIdx.x;
     kr[j] = gi < ng ? ((uint64_t)grow[gi] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)gi) : 0ull;
   }
@@ -364,32 +370,365 @@ __global__ __launch_bounds__(SEL_THREADS) void select_topk(
   CSAHCA_TRACE(1);
   // exactly min(K, ng) groups have a maximum >= T1; list them in index order, which is
   // (j, wave, lane) order
-  const uint32_t ngl = compact_in_order<KPT, true>(
+  const uint32_t ngl = compact_in_order<KP, true>(
       kr, [&](uint64_t key) { return key != 0ull && key >= T1; },
       [&](uint32_t pos, uint64_t, int j) { glist[pos] = j * SEL_THREADS + (int)threadIdx.x; }, sc);
   CSAHCA_TRACE(2);
   // candidates, coalesced: 16 lanes read the 16 scores of one listed group; key j of lane
-  // (wave, lane) is element lane%16 of listed group wave*GPW + j*4 + lane/16, so that
+  // (wave, lane) is element lane%16 of listed group wave*GPWk + j*4 + lane/16, so that
   // (wave, j, lane) order is index order.  Every load is issued (clamped to valid memory)
   // before any is used, so they overlap.
-  int ce[KPT];
-  float cv[KPT];
+  int ce[KP];
+  float cv[KP];
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) {
-    const int gp = wave * GPW + j * 4 + (lane >> 4);
+  for (int j = 0; j < KP; ++j) {
+    const int gp = wave * GPWk + j * 4 + (lane >> 4);
     ce[j] = gp < (int)ngl ? glist[gp] * GROUP + (lane & 15) : V;
     cv[j] = srow[min(ce[j], N_c - 1)];
   }
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) {
+  for (int j = 0; j < KP; ++j) {
     const uint64_t key = ce[j] < V ? entry_key(cv[j], (uint32_t)ce[j]) : 0ull;
     kr[j] = key >= T1s ? key : 0ull;
   }
   const uint64_t T2 = radix_select_kth(kr, keff, sc);
   CSAHCA_TRACE(3);
-  write_selected<KPT, false>(kr, T2, keff, k, orow, osc, sc);
+  write_selected<KP, false>(kr, T2, keff, k, orow, osc, sc);
   CSAHCA_TRACE(4);
   CSAHCA_TRACE_RT(15);
+}
+
+// ---------------------------------------------------------------------------------------
+// selection by one wave per query (no lists, k <= WS_MAX_K, at most 64 WS_MAX_NGPL groups)
+// ---------------------------------------------------------------------------------------
+// The same two thresholds as above, found by bisection instead of histograms: the K-th
+// largest of a set of 32-bit keys is the largest x for which at least K keys are >= x,
+// decided one bit at a time from the highest bit on which the keys differ, each count a
+// sum of ballot popcounts.  Once few keys are left undecided (inside the interval the
+// decided bits leave), they are compacted into LDS and the search goes on over those
+// alone.  No step needs more than the wave, so the four queries of a workgroup run
+// independently, with no workgroup barrier.
+//   T1: s1, the K-th largest group maximum (score key).  The groups above s1, and the
+//       groups at s1 of lowest index up to K in all, are the K groups of the group-key
+//       order above.
+//   Candidates: the entries of those groups scoring >= s1, in index order (held in LDS up
+//       to WS_CAP; beyond that every count re-reads the groups' scores).
+//   T2: s2, the K-th largest candidate score key; the selected are the candidates above
+//       s2 and, of those at s2, the lowest indices up to K.
+// Score keys are nonzero for every non-NaN score, so 0 marks "no key".
+constexpr int WS_WAVES = 4;      // queries per workgroup
+constexpr int WS_MAX_K = 512;
+constexpr int WS_CAP = 1024;     // candidates held in LDS per query
+constexpr int WS_UNROLL = 16;    // candidate batches (4 groups each) per load round
+constexpr int WS_MAX_NGPL = 80;  // group maxima per lane (5120 groups; four waves per SIMD)
+constexpr int WS_SHRINK = 4;     // undecided keys per lane once compacted (256 per wave)
+
+CSAHCA_DEV uint32_t lane_below(uint64_t bal) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+}
+
+// LDS written by lanes of this wave is read back by other lanes of it: one wave's LDS
+// operations complete in order, so only the compiler must not move them across this
+CSAHCA_DEV void wave_lds_order() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// the lowest n set bits of m
+CSAHCA_DEV uint64_t lowest_bits(uint64_t m, uint32_t n) {
+  if (n >= (uint32_t)__popcll(m)) return m;
+  uint64_t out = 0ull;
+  for (uint32_t i = 0; i < n; ++i) {
+    const uint64_t lowest = m & (~m + 1ull);
+    out |= lowest;
+    m ^= lowest;
+  }
+  return out;
+}
+
+// The lanes of one row (64 keys in index order) that are selected by the rule "above the
+// threshold, or equal to it among the first `take` equal keys in index order"; eq_seen
+// counts the equal keys of the rows before.
+CSAHCA_DEV uint64_t row_selection(bool above, bool equal, uint32_t take, uint32_t& eq_seen) {
+  uint64_t sel = __ballot(above);
+  const uint64_t beq = __ballot(equal);
+  if (beq) {
+    sel |= lowest_bits(beq, take > eq_seen ? take - eq_seen : 0u);
+    eq_seen += (uint32_t)__popcll(beq);
+  }
+  return sel;
+}
+
+template <int N>
+CSAHCA_DEV uint32_t count_ge(const uint32_t (&v)[N], uint32_t x) {
+  uint32_t c = 0;
+#pragma unroll
+  for (int j = 0; j < N; ++j) c += (uint32_t)__popcll(__ballot(v[j] >= x));
+  return c;
+}
+
+// K-th largest of the nonzero keys v (n of them, n >= K; a and o the AND and OR of them).
+// lds: 64 (WS_SHRINK + 1) words of this wave's LDS to compact the undecided keys into.
+template <int N>
+CSAHCA_DEV uint32_t wave_kth_largest(const uint32_t (&v)[N], uint32_t n, uint32_t K, uint32_t a, uint32_t o,
+                                     uint32_t* lds) {
+  a = __builtin_amdgcn_readfirstlane(a);  // (the same in every lane: scalar from here)
+  o = __builtin_amdgcn_readfirstlane(o);
+  const uint32_t diff = a ^ o;
+  if (diff == 0u) return a;
+  int bit = 31 - __builtin_clz(diff);
+  uint32_t t = bit == 31 ? 0u : a & ~((2u << bit) - 1u);  // the bits every key shares
+  uint32_t clo = n, chi = 0u;  // keys >= t; keys >= t + 2^(bit+1) (all below K)
+  for (; bit >= 0; --bit) {
+    if (N > WS_SHRINK && clo - chi <= (uint32_t)(64 * WS_SHRINK)) break;
+    const uint32_t c = t | (1u << bit);
+    const uint32_t cnt = count_ge(v, c);
+    if (cnt >= K) {
+      t = c;
+      clo = cnt;
+    } else {
+      chi = cnt;
+    }
+  }
+  if constexpr (N > WS_SHRINK) {
+    if (bit < 0) return t;
+    // the undecided keys lie in [t, t + 2^(bit+1)); compact them (in any order), each lane
+    // writing its own in a row from its offset (the others to a slot of its own past them)
+    const int lane = threadIdx.x & 63;
+    uint32_t hmask = bit == 31 ? 0u : ~((2u << bit) - 1u);  // (t has none of the other bits)
+    uint32_t mine = 0;
+#pragma unroll
+    for (int j = 0; j < N; ++j) mine += (v[j] != 0u && (v[j] & hmask) == t) ? 1u : 0u;
+    const uint32_t incl = wave_incl_scan(mine);
+    uint32_t pos = incl - mine;
+    asm volatile("" : "+s"(hmask));  // (the tests are made again below, not kept)
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const bool in = v[j] != 0u && (v[j] & hmask) == t;
+      lds[in ? pos : (uint32_t)(64 * WS_SHRINK + lane)] = v[j];
+      pos += in ? 1u : 0u;
+    }
+    wave_lds_order();
+    const uint32_t nu = clo - chi;
+    uint32_t u[WS_SHRINK];
+#pragma unroll
+    for (int j = 0; j < WS_SHRINK; ++j) {
+      const uint32_t i = (uint32_t)(64 * j + lane);
+      u[j] = i < nu ? lds[i] : 0u;
+    }
+    wave_lds_order();  // (the caller may reuse the LDS)
+    const uint32_t K2 = K - chi;
+    for (; bit >= 0; --bit) {
+      const uint32_t c = t | (1u << bit);
+      if (count_ge(u, c) >= K2) t = c;
+    }
+  }
+  return t;
+}
+
+// Calls f(i, e, key) for the candidate batches i = 0, 1, ... of a query: lane l of batch
+// i holds entry e = 16 glist[4i + l/16] + l%16 and its score key (0 past V or the list),
+// so that (i, lane) order is index order.  The loads of the next WS_UNROLL batches are
+// issued before the current ones are used.
+template <typename F>
+CSAHCA_DEV void ws_for_candidates(const int* gl, int ngl, const float* srow, int V, int N_c, F f) {
+  const int lane = threadIdx.x & 63;
+  const int nb = cdiv(ngl, 4);
+  auto issue = [&](int i0, int (&e)[WS_UNROLL], float (&v)[WS_UNROLL]) {
+#pragma unroll
+    for (int u = 0; u < WS_UNROLL; ++u) {
+      const int gp = 4 * (i0 + u) + (lane >> 4);
+      e[u] = gp < ngl ? gl[gp] * GROUP + (lane & 15) : V;
+      v[u] = srow[min(e[u], N_c - 1)];
+    }
+  };
+  int e[WS_UNROLL], e2[WS_UNROLL];
+  float v[WS_UNROLL], v2[WS_UNROLL];
+  issue(0, e, v);
+  for (int i0 = 0; i0 < nb; i0 += WS_UNROLL) {
+    const bool more = i0 + WS_UNROLL < nb;
+    if (more) issue(i0 + WS_UNROLL, e2, v2);
+#pragma unroll
+    for (int u = 0; u < WS_UNROLL; ++u)
+      if (i0 + u < nb) f(i0 + u, e[u], e[u] < V ? score_key(v[u]) : 0u);
+    if (more) {
+#pragma unroll
+      for (int u = 0; u < WS_UNROLL; ++u) {
+        e[u] = e2[u];
+        v[u] = v2[u];
+      }
+    }
+  }
+}
+
+template <int NGPL>
+__global__ __launch_bounds__(64 * WS_WAVES, 4) void select_topk_wave(
+    const float* __restrict__ scores, const uint32_t* __restrict__ gmax,
+    const int* __restrict__ q_pos, int m, int Tq, int N_c, int NG, int nq, int k,
+    int* __restrict__ topk_idx, float* __restrict__ topk_score) {
+  __shared__ int s_glist[WS_WAVES][WS_MAX_K];
+  __shared__ uint32_t s_ckey[WS_WAVES][WS_CAP];
+  __shared__ int s_cidx[WS_WAVES][WS_CAP];
+  static_assert(WS_CAP >= 64 * (WS_SHRINK + 1), "the key compaction reuses the candidate keys' LDS");
+  // (the wave index is uniform in the wave: everything per query is scalar)
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int q = blockIdx.x * WS_WAVES + wave;
+  if (q >= nq) return;
+  CSAHCA_TRACE(0);
+  CSAHCA_TRACE_RT(14);
+  const int b = q / Tq, t = q - b * Tq;
+  const int V = visible_entries(q_pos, b, t, m, N_c);
+  const int keff = min(k, V);
+  const float* srow = scores + (size_t)q * N_c;
+  int* orow = topk_idx + (size_t)q * k;
+  float* osc = topk_score ? topk_score + (size_t)q * k : nullptr;
+  for (int i = keff + lane; i < k; i += 64) {
+    orow[i] = -1;
+    if (osc) osc[i] = -INFINITY;
+  }
+  if (keff == V) {  // everything usable is selected
+    for (int i = lane; i < V; i += 64) {
+      orow[i] = i;
+      if (osc) osc[i] = srow[i];
+    }
+    return;
+  }
+  int* gl = s_glist[wave];
+  uint32_t* ckey = s_ckey[wave];
+  int* cidx = s_cidx[wave];
+
+  // T1 over the group maxima: lane l holds groups 64 j + l
+  const int ng = cdiv(V, GROUP);
+  const uint32_t* grow = gmax + (size_t)q * NG;
+  // (loads clamped to the row; one per-lane limit decides which are past it, so that no
+  // per-group index stays live)
+  const int lim = ng - 1 - lane;
+  const uint32_t* gp = grow + lane;
+  uint32_t mx[NGPL];
+#pragma unroll
+  for (int j = 0; j < NGPL; ++j) mx[j] = gp[min(64 * j, lim)];
+  uint32_t a = ~0u, o = 0u;
+#pragma unroll
+  for (int j = 0; j < NGPL; ++j) {
+    if (64 * j > lim) mx[j] = 0u;
+    a &= mx[j] ? mx[j] : ~0u;
+    o |= mx[j];
+  }
+  a = wave_and(a);
+  o = wave_or(o);
+  CSAHCA_TRACE(1);
+  // with no more groups than K every group is taken (threshold 0: every nonzero key is
+  // above it) and every usable entry is a candidate
+  const bool all_groups = keff >= ng;
+  const uint32_t s1 = all_groups ? 0u : wave_kth_largest(mx, (uint32_t)ng, (uint32_t)keff, a, o, ckey);
+  CSAHCA_TRACE(2);
+  // the K groups, listed in index order
+  {
+    uint32_t above = 0;
+#pragma unroll
+    for (int j = 0; j < NGPL; ++j) above += (uint32_t)__popcll(__ballot(mx[j] > s1));
+    const uint32_t take = all_groups ? 0u : (uint32_t)keff - above;  // groups at s1 to take
+    uint32_t base = 0, eq_seen = 0;
+    int gid = lane;
+    asm volatile("" : "+v"(gid));  // (formed afresh here, not kept from the loads)
+#pragma unroll
+    for (int j = 0; j < NGPL; ++j) {
+      const uint64_t sel = row_selection(mx[j] > s1, !all_groups && mx[j] == s1, take, eq_seen);
+      if ((sel >> lane) & 1ull) gl[base + lane_below(sel)] = 64 * j + gid;
+      base += (uint32_t)__popcll(sel);
+    }
+  }
+  const int ngl = all_groups ? ng : keff;
+  // every candidate key lies in [s1, the largest group maximum] (o bounds them above)
+  wave_lds_order();
+  CSAHCA_TRACE(3);
+
+  // candidates: the listed groups' entries scoring >= s1, compacted in index order
+  const uint32_t cmin = s1 ? s1 : 1u;
+  uint32_t nc = 0;
+  ws_for_candidates(gl, ngl, srow, V, N_c, [&](int, int e, uint32_t key) {
+    const bool c = key >= cmin;
+    const uint64_t bal = __ballot(c);
+    const uint32_t pos = nc + lane_below(bal);
+    if (c && pos < (uint32_t)WS_CAP) {
+      ckey[pos] = key;
+      cidx[pos] = e;
+    }
+    nc += (uint32_t)__popcll(bal);
+  });
+  CSAHCA_TRACE(4);
+  constexpr int CPL = WS_CAP / 64;
+  if (nc <= (uint32_t)WS_CAP) {
+    wave_lds_order();
+    uint32_t ck[CPL];
+    uint32_t ca = ~0u, co = 0u;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      const uint32_t i = 64 * j + lane;
+      ck[j] = i < nc ? ckey[i] : 0u;
+      ca &= ck[j] ? ck[j] : ~0u;
+      co |= ck[j];
+    }
+    ca = wave_and(ca);
+    co = wave_or(co);
+    int cid[CPL];
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) cid[j] = cidx[64 * j + lane];
+    wave_lds_order();  // (the compaction below reuses the candidate keys' LDS)
+    const uint32_t s2 = wave_kth_largest(ck, nc, (uint32_t)keff, ca, co, ckey);
+    uint32_t above = 0;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) above += (uint32_t)__popcll(__ballot(ck[j] > s2));
+    const uint32_t take = (uint32_t)keff - above;
+    uint32_t base = 0, eq_seen = 0;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      const uint64_t sel = row_selection(ck[j] > s2, ck[j] == s2, take, eq_seen);
+      if ((sel >> lane) & 1ull) {
+        const uint32_t pos = base + lane_below(sel);
+        orow[pos] = cid[j];
+        if (osc) osc[pos] = key_score(ck[j]);
+      }
+      base += (uint32_t)__popcll(sel);
+    }
+    CSAHCA_TRACE(5);
+    CSAHCA_TRACE_RT(15);
+    return;
+  }
+  // more candidates than LDS holds: every count re-reads the listed groups' scores
+  const uint32_t hi = o;
+  auto count_at_least = [&](uint32_t x) {
+    uint32_t c = 0;
+    ws_for_candidates(gl, ngl, srow, V, N_c, [&](int, int, uint32_t key) {
+      c += (uint32_t)__popcll(__ballot(key >= x));
+    });
+    return c;
+  };
+  // largest x in [cmin, hi] with at least keff candidates >= x
+  uint32_t s2 = cmin;
+  {
+    const uint32_t diff = cmin ^ hi;
+    if (diff) {
+      const int hb = 31 - __builtin_clz(diff);
+      s2 = hb == 31 ? 0u : cmin & ~((2u << hb) - 1u);
+      for (int bit = hb; bit >= 0; --bit) {
+        const uint32_t c = s2 | (1u << bit);
+        if (count_at_least(c) >= (uint32_t)keff) s2 = c;
+      }
+    }
+  }
+  const uint32_t take = (uint32_t)keff - count_at_least(s2 + 1u);
+  uint32_t base = 0, eq_seen = 0;
+  ws_for_candidates(gl, ngl, srow, V, N_c, [&](int, int e, uint32_t key) {
+    const uint64_t sel = row_selection(key > s2, key == s2, take, eq_seen);
+    if ((sel >> lane) & 1ull) {
+      const uint32_t pos = base + lane_below(sel);
+      orow[pos] = e;
+      if (osc) osc[pos] = key_score(key);
+    }
+    base += (uint32_t)__popcll(sel);
+  });
 }
 
 }  // namespace
@@ -402,9 +741,21 @@ int index_select_impl(const float* scores, const uint32_t* gmax, const int* q_po
   using namespace csahca;
   const int nq = B * Tq;
   const int NG = cdiv(N_c, GROUP);
-  hipLaunchKernelGGL(select_topk, dim3((unsigned)nq), dim3(SEL_THREADS), 0, st, scores,
-                     gmax, q_pos, m, Tq, N_c, NG, k, topk_idx, topk_score,
-                     lists ? *lists : ChunkLists{});
+  if (!lists && k <= WS_MAX_K && NG <= 64 * WS_MAX_NGPL) {
+    const unsigned grid = (unsigned)cdiv(nq, WS_WAVES);
+    auto kern = NG <= 64 * 16 ? select_topk_wave<16> : NG <= 64 * 48 ? select_topk_wave<48>
+                                                                       : select_topk_wave<WS_MAX_NGPL>;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * WS_WAVES), 0, st, scores, gmax, q_pos, m, Tq, N_c, NG, nq,
+                       k, topk_idx, topk_score);
+    return launch_status("lightning_index_select");
+  }
+  // (the 8-key kernel gathers k <= 512 candidate groups and holds at most 8192 maxima)
+  if (!lists && k <= NWAVE * 8 * 64 / GROUP && NG <= SEL_THREADS * 8)
+    hipLaunchKernelGGL(select_topk<8>, dim3((unsigned)nq), dim3(SEL_THREADS), 0, st, scores, gmax,
+                       q_pos, m, Tq, N_c, NG, k, topk_idx, topk_score, ChunkLists{});
+  else
+    hipLaunchKernelGGL(select_topk<KPT>, dim3((unsigned)nq), dim3(SEL_THREADS), 0, st, scores, gmax,
+                       q_pos, m, Tq, N_c, NG, k, topk_idx, topk_score, lists ? *lists : ChunkLists{});
   return launch_status("lightning_index_select");
 }
 

@@ -33,8 +33,18 @@ namespace {
 
 constexpr int C = 512;            // head dim of the bf16 path
 constexpr int TILE = 32;          // slots per LDS tile
-constexpr int ROWB = C * 2 + 16;  // LDS row stride in bytes
+constexpr int ROWB = C * 2 + 32;  // LDS row stride in bytes (rows are placed by row_base)
 constexpr int KS = C / 32;        // MFMA K-steps of S (16 x 32 dims)
+
+// LDS byte offset of row r of a tile.  Modulo the 256 bytes the 64 banks cover per cycle,
+// row r starts at 32 (r % 8) + 16 ((r / 8) % 2): the S reads (16 bytes of 16 rows at one
+// column per 16 lanes) hit the sixteen distinct 16-byte slots, and the transpose reads
+// (32 bytes of 8 consecutive rows per 32 lanes) eight disjoint 32-byte windows.  With a
+// plain 16-byte pad per row, neighbouring rows' 32-byte windows overlapped (a two-way
+// bank conflict on every transpose read).  Rows stay 16-byte aligned for the row DMA,
+// and row r + 16 lies exactly 16 strides after row r.
+CSAHCA_DEV constexpr int row_base(int r) { return r * ROWB + 16 * ((r >> 3) & 1); }
+static_assert(row_base(TILE - 1) + C * 2 <= TILE * ROWB, "a tile's rows fit its stage");
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
@@ -266,7 +276,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && NS == 2) ? 2 : 1) void attend_
   for (int i = 0; i < LPW; ++i) mybits |= 1u << (wave + i * NW);
   auto dma_row = [&](const uint16_t* src, uint8_t* st, int r) {
     __builtin_amdgcn_global_load_lds(src + lane * 8,
-                                     (__attribute__((address_space(3))) void*)(st + r * ROWB),
+                                     (__attribute__((address_space(3))) void*)(st + row_base(r)),
                                      16, 0, 0);
   };
   auto issue = [&](int tt, bool spec) {
@@ -468,8 +478,10 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && NS == 2) ? 2 : 1) void attend_
   for (int cb = 0; cb < C / 16; ++cb) oacc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // LDS byte offsets of this lane's operands inside a tile
-  const int s_off = row16 * ROWB + g * (C / 4) * 2;                  // S: A = row, 8 dims
-  const int t_off = (4 * g + (row16 >> 2)) * ROWB + (row16 & 3) * 8;  // PV: transpose reads
+  int s_off = row_base(row16) + g * (C / 4) * 2;                  // S: A = row, 8 dims
+  int t_off = row_base(4 * g + (row16 >> 2)) + (row16 & 3) * 8;  // PV: transpose reads
+  // (one register each: left to itself the compiler keeps their parts apart, and spills)
+  asm volatile("" : "+v"(s_off), "+v"(t_off));
 
   auto tile_mask = [&](int stage, int base) -> uint32_t {
     uint32_t loaded = 0;

@@ -1100,7 +1100,9 @@ Plan make_plan(int B, int Tq, int n_h, int n_slots_c, int W, bool csa) {
   P.n_slots = n_slots_c + W + P.Tg - 1;
   P.nqg = cdiv(Tq, P.Tg);
   const long long base = (long long)P.n_hg * B * P.nqg;
-  P.NS = (P.NW == 4 && base < 256) ? 4 : 2;
+  // the 4-tile ring (two tiles per iteration) where it costs no occupancy: 4-wave
+  // workgroups when there are few, and 8-wave ones (a whole CU's registers anyway)
+  P.NS = ((P.NW == 4 && base < 256) || P.NW == 8) ? 4 : 2;
   // splits hold whole iterations (TPI tiles), at least one each
   const int tpi = P.NS >= 4 ? 2 : 1;
   const int niter = cdiv(cdiv(P.n_slots, TILE), tpi);
@@ -1147,7 +1149,7 @@ int launch_attend_nw(const Plan& P, const AttnArgs& A, hipStream_t st) {
     case 4:
       if (P.CS) return launch_attend<4, 2, CSA, true>(P, A, st);
       return P.NS == 4 ? launch_attend<4, 4, CSA, false>(P, A, st) : launch_attend<4, 2, CSA, false>(P, A, st);
-    case 8: return launch_attend<8, 2, CSA, false>(P, A, st);
+    case 8: return launch_attend<8, 4, CSA, false>(P, A, st);
     default: return csahca::fail(CSAHCA_ENOTSUP, "attend: unsupported wave count");
   }
 }

@@ -120,18 +120,21 @@ CSAHCA_DEV uint32_t ft_compact(const uint64_t (&kr)[KP], Pred pred, Sink sink, F
 // 1. the chunk's cut
 // ---------------------------------------------------------------------------------------
 // u[j]: 32-bit score key of the chunk's entry threadIdx.x + FT_NT*j, 0 if none (a finite
-// score never maps to 0).  Returns the cut as a 33-bit bound: the listed keys are those
-// with u >= cut; 0 lists every entry.  count: how many are listed.
+// score never maps to 0); LKPT keys per thread cover the chunk.  Returns the cut as a
+// 33-bit bound: the listed keys are those with u >= cut; 0 lists every entry.  count: how
+// many are listed.
 struct FtCut {
   uint64_t cut;
   uint32_t count;
 };
 
-CSAHCA_DEV FtCut ft_local_cut(const uint32_t (&u)[FT_LKPT], int n, int JT, int JMAX, FtScratch& sc) {
+template <int LKPT>
+CSAHCA_DEV FtCut ft_local_cut(const uint32_t (&u)[LKPT], int n, int JT, int JMAX, FtScratch& sc) {
+  static_assert(LKPT <= FT_LKPT, "a chunk holds at most SCORE_STAGE keys");
   if (n <= JMAX) return {0ull, (uint32_t)n};
   uint32_t a = ~0u, o = 0u;
 #pragma unroll
-  for (int j = 0; j < FT_LKPT; ++j)
+  for (int j = 0; j < LKPT; ++j)
     if (u[j]) {
       a &= u[j];
       o |= u[j];
@@ -162,7 +165,7 @@ CSAHCA_DEV FtCut ft_local_cut(const uint32_t (&u)[FT_LKPT], int n, int JT, int J
     sc.hist[threadIdx.x] = 0u;  // FT_NT == 256 bins
     ft_barrier();
 #pragma unroll
-    for (int j = 0; j < FT_LKPT; ++j)
+    for (int j = 0; j < LKPT; ++j)
       if (u[j] && (u[j] & hmask) == prefix) atomicAdd(&sc.hist[(u[j] >> lo) & dmask], 1u);
     ft_barrier();
     // thread t owns digit 255 - t: cum = keys whose digit is >= it, plus those above

@@ -235,7 +235,9 @@ CSAHCA_DEV void wait_vm_le(int n) {
 
 // LISTS: the per-chunk half of the top-k selection runs in the same launch
 // (fused_topk.hpp): every workgroup also lists the best entries of its chunk.
-template <int HB, bool F4, bool LISTS>
+// SPT: the chunk's scores per thread in the write-out and the list (CH <= 256 * SPT), so
+// that those loops run over no slot past the chunk.
+template <int HB, bool F4, bool LISTS, int SPT>
 __global__ __launch_bounds__(256, 2) void index_score_dec128(
     const uint8_t* __restrict__ qI, const float* __restrict__ w, const uint8_t* __restrict__ KI,
     const uint8_t* __restrict__ KS,
@@ -249,8 +251,9 @@ __global__ __launch_bounds__(256, 2) void index_score_dec128(
   __shared__ __attribute__((aligned(16))) uint8_t ring[4][RING][BLKB];
   __shared__ __attribute__((aligned(16))) uint8_t s_q[NIH * C_I];
   __shared__ float s_w[cdiv(NIH, 64) * 64];
-  __shared__ float s_sc[SCORE_STAGE];
-  __shared__ uint32_t s_gk[SCORE_STAGE / GROUP];
+  static_assert(SPT * 256 <= SCORE_STAGE, "a chunk's scores fit the LDS stage");
+  __shared__ float s_sc[SPT * 256];
+  __shared__ uint32_t s_gk[SPT * 256 / GROUP];
   CSAHCA_TRACE(0);
   CSAHCA_TRACE_RT(14);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -390,7 +393,6 @@ __global__ __launch_bounds__(256, 2) void index_score_dec128(
   uint32_t* grow = gkeys + (size_t)q * NG;
   // the chunk's scores, entry threadIdx.x + 256 j: all LDS reads issued before the first
   // store (one wait, not one per store), kept for the list below
-  constexpr int SPT = SCORE_STAGE / 256;
   float sv[SPT];
 #pragma unroll
   for (int j = 0; j < SPT; ++j) {
@@ -409,11 +411,10 @@ __global__ __launch_bounds__(256, 2) void index_score_dec128(
       // the key ring is free (every DMA has landed and the workgroup passed the barrier)
       FtScratch& sc = *reinterpret_cast<FtScratch*>(&ring[0][0][0]);
       static_assert(sizeof(FtScratch) <= sizeof(ring), "the cut's scratch fits the key ring");
-      uint32_t u[FT_LKPT];
-      uint64_t kr[FT_LKPT];
-      static_assert(FT_LKPT == SPT, "the list takes the scores read above");
+      uint32_t u[SPT];
+      uint64_t kr[SPT];
 #pragma unroll
-      for (int j = 0; j < FT_LKPT; ++j) {
+      for (int j = 0; j < SPT; ++j) {
         const int i = (int)threadIdx.x + 256 * j;
         u[j] = i < n ? score_key(sv[j]) : 0u;
         kr[j] = i < n ? ((uint64_t)u[j] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)(e_begin + i)) : 0ull;
@@ -673,12 +674,15 @@ void launch_fp8(const void* q_idx, const float* w_idx, const void* k_idx, const 
   const uint8_t* KI = (const uint8_t*)k_idx;
   // MX FP4 keys: [B, N_c, 64] E2M1 rows, then [B, N_c, 4] E8M0 scales
   const uint8_t* KS = F4 ? KI + (size_t)(nq / Tq) * N_c * (C_I / 2) : nullptr;
-  if (decode && C_I == 128 && cl)
-    hipLaunchKernelGGL((index_score_dec128<HB, F4, true>), grid, dim3(256), 0, st, (const uint8_t*)q_idx,
-                       w_idx, KI, KS, q_pos, m, N_c, CH, NG, scores, gkeys, *cl);
-  else if (decode && C_I == 128)
-    hipLaunchKernelGGL((index_score_dec128<HB, F4, false>), grid, dim3(256), 0, st, (const uint8_t*)q_idx,
-                       w_idx, KI, KS, q_pos, m, N_c, CH, NG, scores, gkeys, ChunkLists{});
+  if (decode && C_I == 128) {
+    // the chunk's scores per thread in the write-out and the list: 8 for chunks of up to
+    // 2048 keys (the plans of the 128K and 1M decode shapes), else 16
+    const ChunkLists cla = cl ? *cl : ChunkLists{};
+    auto kern = cl ? (CH <= 2048 ? index_score_dec128<HB, F4, true, 8> : index_score_dec128<HB, F4, true, 16>)
+                   : (CH <= 2048 ? index_score_dec128<HB, F4, false, 8> : index_score_dec128<HB, F4, false, 16>);
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, (const uint8_t*)q_idx, w_idx, KI, KS, q_pos, m, N_c, CH,
+                       NG, scores, gkeys, cla);
+  }
   else if (C_I == 128)
     hipLaunchKernelGGL((index_score_pre128<HB, F4>),
                        dim3((unsigned)(nq / Tq * cdiv(Tq, 4)), (unsigned)cdiv(N_c, PRE_KEYS)), dim3(256), 0, st,

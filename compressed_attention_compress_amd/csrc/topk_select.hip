@@ -251,8 +251,10 @@ CSAHCA_DEV void write_selected(const uint64_t (&kr)[KP], uint64_t T, int keff, i
 // group maxima as described at the top of this file.
 // KP is the number of keys a thread holds: KPT in general; 8 for a selection without lists
 // with k <= 512 and at most 8192 groups (a prefill chunk), which holds a thread to 64
-// registers, so that two workgroups share a compute unit.
-template <int KP>
+// registers, so that two workgroups share a compute unit.  LKP (0: no lists) is the number
+// of list slots a thread holds, the smallest power of two with P * JMAX <= SEL_THREADS * LKP,
+// so that no loop of the list path runs over slots that no chunk can fill.
+template <int KP, int LKP>
 __global__ __launch_bounds__(SEL_THREADS, KP == KPT ? 1 : 8) void select_topk(
     const float* __restrict__ scores, const uint32_t* __restrict__ gmax,
     const int* __restrict__ q_pos, int m, int Tq, int N_c, int NG, int k,
@@ -269,6 +271,25 @@ __global__ __launch_bounds__(SEL_THREADS, KP == KPT ? 1 : 8) void select_topk(
   const float* srow = scores + (size_t)q * N_c;
   int* orow = topk_idx + (size_t)q * k;
   float* osc = topk_score ? topk_score + (size_t)q * k : nullptr;
+  // With lists: every slot and bound of the query's lists is loaded together with its
+  // ready word and the position (all of it is workspace memory), and masked to the usable
+  // chunks once the position has arrived: chunks past the usable entries wrote nothing in
+  // this call.  Thread (wave, lane) holds slots wave * 64 LKP + 64 j + lane.
+  constexpr int LK = LKP > 0 ? LKP : 1;
+  uint64_t lk[LK];
+  uint64_t e = 0ull;
+  uint32_t ready = 0u;
+  if (LKP > 0 && cl.cand) {
+    const uint64_t* cq = cl.cand + (size_t)q * cl.P * cl.JMAX;
+    const int nall = cl.P * cl.JMAX;
+    ready = cl.path[q];
+    e = (int)threadIdx.x < cl.P ? cl.edge[(size_t)q * FT_MAX_P + threadIdx.x] : 0ull;
+#pragma unroll
+    for (int j = 0; j < LK; ++j) {
+      const int s = wave * 64 * LK + 64 * j + lane;
+      lk[j] = s < nall ? cq[s] : 0ull;
+    }
+  }
 
   if (keff == V) {  // everything usable is selected
     for (int i = threadIdx.x; i < k; i += SEL_THREADS) {
@@ -280,76 +301,75 @@ __global__ __launch_bounds__(SEL_THREADS, KP == KPT ? 1 : 8) void select_topk(
   }
   constexpr int GPWk = KP * 64 / GROUP;  // listed groups per wave in the candidate gather
   uint64_t kr[KP];
-  // (a thread may see its own workgroup's FT_PATH_GROUPS below instead of the old word:
-  // either way not FT_LISTS_READY, so every thread takes the same branch)
-  if constexpr (KP == KPT) if (cl.cand && cl.path[q] == FT_LISTS_READY) {
+  if constexpr (LKP > 0) if (cl.cand) {
+    static_assert(LKP <= KPT, "the list slots fit the selection's registers");
     __shared__ uint64_t s_keys[SEL_COMPACT];
-    // The union: slot s = chunk * JMAX + position (lists are padded with zero keys);
-    // thread (wave, lane) holds slots wave * 64 KPT + 64 j + lane, so that (wave, j, lane)
-    // order is slot order, which is index order (chunks are index ranges, each list is in
-    // index order).  The lists give the top k exactly when K, their k-th largest key, is
-    // at least every chunk's bound E; so only keys >= max E matter, and if fewer than k
-    // remain, the lists cannot decide.
+    // The union: slot s = chunk * JMAX + position (lists are padded with zero keys), held
+    // so that (wave, j, lane) order is slot order, which is index order (chunks are index
+    // ranges, each list is in index order).  The lists give the top k exactly when K, their
+    // k-th largest key, is at least every chunk's bound E; so only keys >= max E matter,
+    // and if fewer than k remain, the lists cannot decide.
+    // (a thread may see its own workgroup's FT_PATH_GROUPS below instead of the old word:
+    // either way not FT_LISTS_READY, so every thread takes the same branch)
     CSAHCA_TRACE(1);
-    const int P_eff = cdiv(V, cl.CH);
-    const int nslots = P_eff * cl.JMAX;
-    const uint64_t* cq = cl.cand + (size_t)q * cl.P * cl.JMAX;
-    uint64_t e = (int)threadIdx.x < P_eff ? cl.edge[(size_t)q * FT_MAX_P + threadIdx.x] : 0ull;
+    if (ready == FT_LISTS_READY) {
+      const int P_eff = cdiv(V, cl.CH);
+      const int nslots = P_eff * cl.JMAX;
+      if ((int)threadIdx.x >= P_eff) e = 0ull;
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const int s = wave * 64 * KPT + 64 * j + lane;
-      kr[j] = s < nslots ? cq[s] : 0ull;
-    }
-    // the histograms of the k-th search are cleared while the loads are in flight
-    for (int i = threadIdx.x; i < 2 * NBIN; i += SEL_THREADS) (&sc.hist[0][0])[i] = 0u;
+      for (int j = 0; j < LKP; ++j)
+        if (wave * 64 * LKP + 64 * j + lane >= nslots) lk[j] = 0ull;
+      // the histograms of the k-th search are cleared while the loads are in flight
+      for (int i = threadIdx.x; i < 2 * NBIN; i += SEL_THREADS) (&sc.hist[0][0])[i] = 0u;
 #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) e = umax64(e, shfl_xor_u64(e, d));
-    if (lane == 0) sc.red_or[wave] = e;
-    __syncthreads();
-    const uint64_t emax = umax64(sc.red_or[0], sc.red_or[1]);
-    uint64_t kmax = 0ull;
+      for (int d = 1; d < 64; d <<= 1) e = umax64(e, shfl_xor_u64(e, d));
+      if (lane == 0) sc.red_or[wave] = e;
+      __syncthreads();
+      const uint64_t emax = umax64(sc.red_or[0], sc.red_or[1]);
+      uint64_t kmax = 0ull;
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      kr[j] = kr[j] >= emax ? kr[j] : 0ull;
-      kmax = umax64(kmax, kr[j]);
-    }
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) kmax = umax64(kmax, shfl_xor_u64(kmax, d));
-    if (lane == 0) sc.red_and[wave] = kmax;  // (the barriers inside the compaction order it)
-    // the kept keys, compacted in slot order into LDS when few enough
-    const uint32_t total = compact_in_order<KPT, false>(
-        kr, [](uint64_t key) { return key != 0ull; },
-        [&](uint32_t pos, uint64_t key, int) {
-          if (pos < (uint32_t)SEL_COMPACT) s_keys[pos] = key;
-        },
-        sc);
-    CSAHCA_TRACE(2);
-    if (total >= (uint32_t)keff) {
-#pragma unroll
-      for (int i = 0; i < NWAVE; ++i) kmax = umax64(kmax, sc.red_and[i]);
-      // every kept key lies in [lowest kept, kmax]; emax <= the lowest, and all of them
-      // share the bits above the highest bit where emax (or 1, when every chunk listed
-      // everything) and kmax differ
-      const uint64_t lo = emax ? emax : 1ull;
-      if (total <= (uint32_t)SEL_COMPACT) {
-        uint64_t f[CPT];  // (j, thread) order is the compacted order
-#pragma unroll
-        for (int j = 0; j < CPT; ++j) {
-          const uint32_t i = (uint32_t)(j * SEL_THREADS) + threadIdx.x;
-          f[j] = i < total ? s_keys[i] : 0ull;
-        }
-        const uint64_t K = radix_select_kth<CPT, true>(f, keff, sc, lo, kmax);  // >= emax, so >= every bound
-        CSAHCA_TRACE(3);
-        write_selected<CPT, true>(f, K, keff, k, orow, osc, sc);
-      } else {
-        const uint64_t K = radix_select_kth<KPT, true>(kr, keff, sc, lo, kmax);
-        CSAHCA_TRACE(3);
-        write_selected<KPT, false>(kr, K, keff, k, orow, osc, sc);
+      for (int j = 0; j < LKP; ++j) {
+        lk[j] = lk[j] >= emax ? lk[j] : 0ull;
+        kmax = umax64(kmax, lk[j]);
       }
-      if (threadIdx.x == 0) cl.path[q] = FT_PATH_LISTS;
-      CSAHCA_TRACE(4);
-      CSAHCA_TRACE_RT(15);
-      return;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) kmax = umax64(kmax, shfl_xor_u64(kmax, d));
+      if (lane == 0) sc.red_and[wave] = kmax;  // (the barriers inside the compaction order it)
+      // the kept keys, compacted in slot order into LDS when few enough
+      const uint32_t total = compact_in_order<LKP, false>(
+          lk, [](uint64_t key) { return key != 0ull; },
+          [&](uint32_t pos, uint64_t key, int) {
+            if (pos < (uint32_t)SEL_COMPACT) s_keys[pos] = key;
+          },
+          sc);
+      CSAHCA_TRACE(2);
+      if (total >= (uint32_t)keff) {
+#pragma unroll
+        for (int i = 0; i < NWAVE; ++i) kmax = umax64(kmax, sc.red_and[i]);
+        // every kept key lies in [lowest kept, kmax]; emax <= the lowest, and all of them
+        // share the bits above the highest bit where emax (or 1, when every chunk listed
+        // everything) and kmax differ
+        const uint64_t lo = emax ? emax : 1ull;
+        if (total <= (uint32_t)SEL_COMPACT) {
+          uint64_t f[CPT];  // (j, thread) order is the compacted order
+#pragma unroll
+          for (int j = 0; j < CPT; ++j) {
+            const uint32_t i = (uint32_t)(j * SEL_THREADS) + threadIdx.x;
+            f[j] = i < total ? s_keys[i] : 0ull;
+          }
+          const uint64_t K = radix_select_kth<CPT, true>(f, keff, sc, lo, kmax);  // >= emax, so >= every bound
+          CSAHCA_TRACE(3);
+          write_selected<CPT, true>(f, K, keff, k, orow, osc, sc);
+        } else {
+          const uint64_t K = radix_select_kth<LKP, true>(lk, keff, sc, lo, kmax);
+          CSAHCA_TRACE(3);
+          write_selected<LKP, false>(lk, K, keff, k, orow, osc, sc);
+        }
+        if (threadIdx.x == 0) cl.path[q] = FT_PATH_LISTS;
+        CSAHCA_TRACE(4);
+        CSAHCA_TRACE_RT(15);
+        return;
+      }
     }
   }
   if (cl.path && threadIdx.x == 0) cl.path[q] = FT_PATH_GROUPS;
@@ -751,11 +771,21 @@ int index_select_impl(const float* scores, const uint32_t* gmax, const int* q_po
   }
   // (the 8-key kernel gathers k <= 512 candidate groups and holds at most 8192 maxima)
   if (!lists && k <= NWAVE * 8 * 64 / GROUP && NG <= SEL_THREADS * 8)
-    hipLaunchKernelGGL(select_topk<8>, dim3((unsigned)nq), dim3(SEL_THREADS), 0, st, scores, gmax,
+    hipLaunchKernelGGL((select_topk<8, 0>), dim3((unsigned)nq), dim3(SEL_THREADS), 0, st, scores, gmax,
                        q_pos, m, Tq, N_c, NG, k, topk_idx, topk_score, ChunkLists{});
-  else
-    hipLaunchKernelGGL(select_topk<KPT>, dim3((unsigned)nq), dim3(SEL_THREADS), 0, st, scores, gmax,
-                       q_pos, m, Tq, N_c, NG, k, topk_idx, topk_score, lists ? *lists : ChunkLists{});
+  else if (!lists)
+    hipLaunchKernelGGL((select_topk<KPT, 0>), dim3((unsigned)nq), dim3(SEL_THREADS), 0, st, scores, gmax,
+                       q_pos, m, Tq, N_c, NG, k, topk_idx, topk_score, ChunkLists{});
+  else {
+    // list slots per thread: the smallest power of two that holds every chunk's list
+    const long long slots = (long long)lists->P * lists->JMAX;
+    auto kern = slots <= SEL_THREADS * 2 ? select_topk<KPT, 2>
+              : slots <= SEL_THREADS * 4 ? select_topk<KPT, 4>
+              : slots <= SEL_THREADS * 8 ? select_topk<KPT, 8>
+                                          : select_topk<KPT, KPT>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)nq), dim3(SEL_THREADS), 0, st, scores, gmax, q_pos, m, Tq, N_c,
+                       NG, k, topk_idx, topk_score, *lists);
+  }
   return launch_status("lightning_index_select");
 }
 

@@ -334,6 +334,37 @@ __global__ __launch_bounds__(SEL_THREADS, KP == KPT ? 1 : 8) void select_topk(
       }
 #pragma unroll
       for (int d = 1; d < 64; d <<= 1) kmax = umax64(kmax, shfl_xor_u64(kmax, d));
+      if constexpr (LKP <= 8) {
+        // Few slots per thread: the k-th search and the write run on the registers
+        // themselves, with one barrier for the count of kept keys and their maximum.
+        // (The counts sit in sc.scan, which the k-th search writes only after its first
+        // barrier, and the write-out's compaction does not touch.)
+        uint32_t cnt = 0;
+#pragma unroll
+        for (int j = 0; j < LKP; ++j) cnt += (uint32_t)__popcll(__ballot(lk[j] != 0ull));
+        if (lane == 0) {
+          sc.red_and[wave] = kmax;
+          sc.scan[wave] = cnt;
+        }
+        __syncthreads();
+        uint32_t total = 0;
+#pragma unroll
+        for (int i = 0; i < NWAVE; ++i) {
+          kmax = umax64(kmax, sc.red_and[i]);
+          total += sc.scan[i];
+        }
+        CSAHCA_TRACE(2);
+        if (total >= (uint32_t)keff) {
+          // every kept key lies in [emax (or 1 when every chunk listed everything), kmax]
+          const uint64_t K = radix_select_kth<LKP, true>(lk, keff, sc, emax ? emax : 1ull, kmax);
+          CSAHCA_TRACE(3);
+          write_selected<LKP, false>(lk, K, keff, k, orow, osc, sc);
+          if (threadIdx.x == 0) cl.path[q] = FT_PATH_LISTS;
+          CSAHCA_TRACE(4);
+          CSAHCA_TRACE_RT(15);
+          return;
+        }
+      } else {
       if (lane == 0) sc.red_and[wave] = kmax;  // (the barriers inside the compaction order it)
       // the kept keys, compacted in slot order into LDS when few enough
       const uint32_t total = compact_in_order<LKP, false>(
@@ -369,6 +400,7 @@ __global__ __launch_bounds__(SEL_THREADS, KP == KPT ? 1 : 8) void select_topk(
         CSAHCA_TRACE(4);
         CSAHCA_TRACE_RT(15);
         return;
+      }
       }
     }
   }

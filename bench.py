@@ -108,6 +108,7 @@ class Workload:
         # before the step's own new blocks
         self.n_old = n - (self.Tq if self.kind == "prefill" else 1)
         self.nr = norm_rope
+        self.rows_pooled = False  # the step's window rows were normalised with the pooling
         if norm_rope:  # seeded gains U(0.5, 1.5) for the KV rows and for the queries
             gn = torch.Generator(device=dev).manual_seed(77)
             self.g_kv = torch.rand((c,), generator=gn, device=dev) + 0.5
@@ -191,8 +192,16 @@ class Workload:
                 else:
                     sides += [X, Z, C[:, first_blk:], n - tok0, m, n * c, (n // m) * c]
             if self.nr:
-                lib.csahca_compress_pair_norm_rope(*sides, B, c, self.NR_D, self.NR_EPS, self.NR_THETA,
-                                                   cfg.dtype)
+                # the step's new tokens enter both layers' normalised window rows in the same
+                # launch (window_rows then has nothing left to do)
+                Tq, L = self.Tq, self.nr_L
+                rows = []
+                for l in ("csa", "hca"):
+                    rows += [prob[f"X_{l}"][:, n - Tq:], self.nr_win[l][:, L - Tq:], self.nr_new_pos,
+                             n * c, L * c]
+                lib.csahca_compress_pair_norm_rope_rows(*sides, B, c, self.NR_D, self.NR_EPS,
+                                                        self.NR_THETA, cfg.dtype, Tq, *rows)
+                self.rows_pooled = True
             else:
                 lib.csahca_compress_pair(*sides, B, c, cfg.dtype)
             return
@@ -243,6 +252,8 @@ class Workload:
         if not self.nr:
             return prob[f"X_{l}"], self.win_pos, n
         Tq, L = self.Tq, self.nr_L
+        if self.rows_pooled:  # normalised by the paired pooling launch of this step
+            return self.nr_win[l], self.nr_win_pos, L
         lib.csahca_norm_rope(prob[f"X_{l}"][:, n - Tq:], self.nr_win[l][:, L - Tq:], self.g_kv,
                              self.nr_new_pos, B, Tq, 1, c, 1, self.NR_D, self.NR_EPS, self.NR_THETA,
                              1, cfg.dtype, x_bstride=n * c, y_bstride=L * c)

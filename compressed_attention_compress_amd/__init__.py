@@ -30,6 +30,10 @@ _SIGNATURES = {
                                   _I, _I, _I, _P]),
     "csahca_compress_pair_norm_rope": (_I, [_P, _P, _P, _P, _I, _I, _LL, _LL, _LL, _P, _P, _P, _P,
                                             _I, _I, _LL, _LL, _LL, _I, _I, _I, _F, _F, _I, _P]),
+    "csahca_compress_pair_norm_rope_rows": (_I, [_P, _P, _P, _P, _I, _I, _LL, _LL, _LL, _P, _P, _P,
+                                                 _P, _I, _I, _LL, _LL, _LL, _I, _I, _I, _F, _F, _I,
+                                                 _I, _P, _P, _P, _LL, _LL, _P, _P, _P, _LL, _LL,
+                                                 _P]),
     "csa_compress_overlap": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _LL, _LL, _P]),
     "csahca_compress_norm_rope": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _LL, _I, _F, _F, _I,
                                        _LL, _LL, _P]),
@@ -160,6 +164,21 @@ def csahca_compress_pair_norm_rope(kv_a, gate_a, gamma_a, out_a, n_a, m_a, entry
         _ptr(kv_a), _ptr(gate_a), _ptr(gamma_a), _ptr(out_a), n_a, m_a, entry0_a, in_bstride_a,
         out_bstride_a, _ptr(kv_b), _ptr(gate_b), _ptr(gamma_b), _ptr(out_b), n_b, m_b, entry0_b,
         in_bstride_b, out_bstride_b, B, c, d_rope, float(eps), float(theta), dtype, _stream(stream)))
+
+
+def csahca_compress_pair_norm_rope_rows(kv_a, gate_a, gamma_a, out_a, n_a, m_a, entry0_a,
+                                        in_bstride_a, out_bstride_a, kv_b, gate_b, gamma_b, out_b,
+                                        n_b, m_b, entry0_b, in_bstride_b, out_bstride_b, B, c,
+                                        d_rope, eps, theta, dtype, T, row_x_a, row_y_a, row_pos_a,
+                                        row_x_bstride_a, row_y_bstride_a, row_x_b, row_y_b,
+                                        row_pos_b, row_x_bstride_b, row_y_bstride_b, stream=None):
+    return _check("csahca_compress_pair_norm_rope_rows", load().csahca_compress_pair_norm_rope_rows(
+        _ptr(kv_a), _ptr(gate_a), _ptr(gamma_a), _ptr(out_a), n_a, m_a, entry0_a, in_bstride_a,
+        out_bstride_a, _ptr(kv_b), _ptr(gate_b), _ptr(gamma_b), _ptr(out_b), n_b, m_b, entry0_b,
+        in_bstride_b, out_bstride_b, B, c, d_rope, float(eps), float(theta), dtype, T,
+        _ptr(row_x_a), _ptr(row_y_a), _ptr(row_pos_a), row_x_bstride_a, row_y_bstride_a,
+        _ptr(row_x_b), _ptr(row_y_b), _ptr(row_pos_b), row_x_bstride_b, row_y_bstride_b,
+        _stream(stream)))
 
 
 def csahca_compress_norm_rope(kv, gate, pos_bias, gamma, out, B, n, c, m, entry0, d_rope, eps,

@@ -39,17 +39,9 @@ __global__ __launch_bounds__(256) void norm_rope_rows(const T* __restrict__ x, T
     b = (int)(bt / T_);
   }
   if (row >= rows) return;  // whole rows leave together (CV divides 64)
-  const long long in_seq = (row - (long long)b * T_ * H) * c + cv * VEC;  // (t, h) offset
-  Vec8<T> v;
-  v.load(x + b * x_bs + in_seq);  // the row, its gains and its position load together
-  float g[VEC];
-  csahca::load_gain8(nr, cv * VEC, g);
+  const long long in_seq = (row - (long long)b * T_ * H) * c;  // (t, h) offset
   const long long p = (pos ? (long long)pos[b] : 0LL) + (long long)t * pstride;
-  float f[VEC];
-#pragma unroll
-  for (int e = 0; e < VEC; ++e) f[e] = v.get(e);
-  csahca::norm_rope8(f, g, cv * VEC, CV, c, nr, p);
-  Vec8<T>::store(y + b * y_bs + in_seq, f);
+  csahca::norm_rope_row8<T>(x + b * x_bs + in_seq, y + b * y_bs + in_seq, nr, p, cv, CV, c);
 }
 
 }  // namespace

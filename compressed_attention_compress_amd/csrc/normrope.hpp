@@ -177,6 +177,23 @@ CSAHCA_DEV void norm_rope8(float (&v)[VEC], const float (&g)[VEC], int ch0, int 
   }
 }
 
+// One row's channels cv*8 .. cv*8+7 (the row's c channels held by CV consecutive lanes):
+// loaded from x_row, normalised and rotated at position `pos`, rounded once and stored to
+// y_row.  Every lane of the row's group calls it (the mean square is a lane sum).
+template <typename T>
+CSAHCA_DEV void norm_rope_row8(const T* x_row, T* y_row, const NormRope& nr, long long pos, int cv,
+                               int CV, int c) {
+  Vec8<T> v;
+  v.load(x_row + cv * VEC);  // the row and its gains load together
+  float g[VEC];
+  load_gain8(nr, cv * VEC, g);
+  float f[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) f[e] = v.get(e);
+  norm_rope8(f, g, cv * VEC, CV, c, nr, pos);
+  Vec8<T>::store(y_row + cv * VEC, f);
+}
+
 // Host-side check shared by the entry points that take a NormRope.
 inline bool norm_rope_args_ok(int c, int d, float eps, float theta) {
   const int CV = c / VEC;

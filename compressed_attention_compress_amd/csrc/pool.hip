@@ -423,12 +423,46 @@ struct PoolSide {
   long long entry0;    // NR: cache index of the first entry (its position is m * entry0)
 };
 
+// Rows normalised and rotated beside a paired pooling with the norm (a decode step's new
+// window rows): T rows per sequence, row (b, t) at x + b * x_bs + t * c, position
+// pos[b] + t (0 + t without pos), written to y likewise; the gain is the side's.
+template <typename T>
+struct RowSide {
+  const T* x;
+  T* y;
+  const int* pos;
+  long long x_bs, y_bs;
+  const float* gamma;
+  int T_;
+};
+
 // Two poolings in one launch: workgroups [0, gridA) run side A on pool_kernel's layout,
-// the rest run side B on pool_block_kernel's (256 threads each; 1024 with the norm).
+// workgroups [gridA, gridAB) side B on pool_block_kernel's (256 threads each; 1024 with
+// the norm).  With the norm, the workgroups from gridAB on normalise the rows of RA then
+// RB (B sequences each), one row per c/8 consecutive lanes.
 template <typename T, int UBA, int UBB, bool NR>
 __global__ __launch_bounds__(NR ? 1024 : 256) void pool_pair_kernel(PoolSide<T> A, PoolSide<T> Bs,
                                                                     int gridA, NormRope nr,
-                                                                    AppendRows ap0) {
+                                                                    AppendRows ap0, RowSide<T> RA,
+                                                                    RowSide<T> RB, int gridAB, int B) {
+  if constexpr (NR) {
+    if ((int)blockIdx.x >= gridAB) {
+      const int c = A.c, CV = c / VEC;
+      const long long item = (long long)((int)blockIdx.x - gridAB) * blockDim.x + threadIdx.x;
+      const long long row = item / CV, nra = (long long)B * RA.T_, nrows = nra + (long long)B * RB.T_;
+      if (row >= nrows) return;  // whole rows leave together (CV divides 64)
+      const int cv = (int)(item - row * CV);
+      const bool sa = row < nra;
+      const RowSide<T>& R = sa ? RA : RB;
+      const long long r = sa ? row : row - nra;
+      const int b = (int)(r / R.T_), t = (int)(r - (long long)b * R.T_);
+      const long long p = (R.pos ? (long long)R.pos[b] : 0LL) + t;
+      const NormRope nx{R.gamma, nr.eps, nr.theta, nr.d, 1};
+      csahca::norm_rope_row8<T>(R.x + b * R.x_bs + (long long)t * c, R.y + b * R.y_bs + (long long)t * c, nx,
+                                p, cv, CV, c);
+      return;
+    }
+  }
   if ((int)blockIdx.x < gridA) {
     const NormRope na{A.gamma, nr.eps, nr.theta, nr.d, nr.norm};
     pool_items<T, UBA, false, PLAIN, NR>(A.X, A.Z, nullptr, nullptr, nullptr, A.out, A.N, A.c, A.m, 0,
@@ -639,11 +673,36 @@ int pool_entry(const char* name, const void* kv, const void* gate, const void* k
 // launch when one takes pool_kernel's layout and the other pool_block_kernel's at the
 // same workgroup size; otherwise one launch each.  The entries are the same bits either
 // way.
+// Window rows normalised beside a paired pooling with the norm (csahca_norm_rope's
+// arguments for one side, H = 1, pstride 1): none when T == 0.
+struct PairRows {
+  int T;
+  const void *x_a, *x_b;
+  void *y_a, *y_b;
+  const int *pos_a, *pos_b;
+  long long x_bs_a, y_bs_a, x_bs_b, y_bs_b;
+};
+
+int pair_rows_check(const char* name, const PairRows& r, int c) {
+  const char* why = nullptr;
+  if (r.T < 0) why = "T must be >= 0";
+  else if (r.T > 0 && (!r.x_a || !r.y_a || !r.x_b || !r.y_b))
+    why = "the row sources and destinations must be non-NULL";
+  else if (r.T > 0 && (!aligned16(r.x_a) || !aligned16(r.y_a) || !aligned16(r.x_b) || !aligned16(r.y_b)))
+    why = "the row sources and destinations must be 16-byte aligned";
+  else if (r.T > 0)
+    for (long long bs : {r.x_bs_a, r.y_bs_a, r.x_bs_b, r.y_bs_b})
+      if (bs < (long long)r.T * c || bs % 8) why = "row batch strides must be >= T*c and multiples of 8";
+  if (!why) return CSAHCA_OK;
+  set_error("%s: %s", name, why);
+  return CSAHCA_EINVAL;
+}
+
 int pool_pair(const char* name, const void* kv_a, const void* gate_a, void* out_a, int n_a, int m_a,
               long long in_bs_a, long long out_bs_a, const void* kv_b, const void* gate_b, void* out_b,
               int n_b, int m_b, long long in_bs_b, long long out_bs_b, int B, int c, int dtype,
               const NormRope* nr, const float* gamma_a, long long entry0_a, const float* gamma_b,
-              long long entry0_b, void* stream) {
+              long long entry0_b, void* stream, const PairRows* rows = nullptr) {
   long long NA = 0, NB = 0;
   int rc = pool_check(name, kv_a, gate_a, nullptr, nullptr, false, 0, out_a, B, n_a, c, m_a, dtype,
                       in_bs_a, out_bs_a, &NA);
@@ -657,6 +716,11 @@ int pool_pair(const char* name, const void* kv_a, const void* gate_a, void* out_
               "eps >= 0, theta > 0, entry0 >= 0 and gamma 16-byte aligned", name);
     return CSAHCA_EINVAL;
   }
+  if (rows) {
+    rc = pair_rows_check(name, *rows, c);
+    if (rc != CSAHCA_OK) return rc;
+  }
+  const int nrow_t = rows ? rows->T : 0;  // rows per sequence and side
   hipStream_t st = (hipStream_t)stream;
   const PoolPlan pa = nr ? plan_norm(B, NA, c, m_a) : plan_plain(B, NA, c, m_a);
   const PoolPlan pb = nr ? plan_norm(B, NB, c, m_b) : plan_plain(B, NB, c, m_b);
@@ -665,7 +729,7 @@ int pool_pair(const char* name, const void* kv_a, const void* gate_a, void* out_
   const PoolPlan &p1 = swap ? pb : pa, &p2 = swap ? pa : pb;
   // (with the norm, bf16 only: the float form does not fit 1024-thread workgroups)
   if (NA > 0 && NB > 0 && !p1.block && p2.block && p2.threads == wg && (!nr || dtype == CSAHCA_BF16) &&
-      (long long)p1.grid + p2.grid <= 0x7FFFFFFFLL) {
+      (long long)p1.grid + p2.grid + cdiv<long long>(2LL * B * nrow_t * (c / 8), wg) <= 0x7FFFFFFFLL) {
     if (nr && raise_pair_lds_limit() != hipSuccess)
       return fail(CSAHCA_ELAUNCH, "csahca_compress_pair: cannot raise the LDS limit");
     const NormRope n0 = nr ? *nr : NormRope{nullptr, 0.f, 1.f, 0, 0};
@@ -679,16 +743,25 @@ int pool_pair(const char* name, const void* kv_a, const void* gate_a, void* out_
                            pb.S, pb.CVG, in_bs_b, out_bs_b, pb.total, gamma_b, entry0_b};
       const PoolSide<T>& s1 = swap ? sb : sa;
       const PoolSide<T>& s2 = swap ? sa : sb;
-      const dim3 grid(p1.grid + p2.grid), blk(wg);
-      const int g1 = (int)p1.grid;
+      RowSide<T> ra{}, rb{};
+      long long grid_rows = 0;
+      if (NR && nrow_t > 0) {
+        ra = RowSide<T>{(const T*)rows->x_a, (T*)rows->y_a, rows->pos_a, rows->x_bs_a, rows->y_bs_a, gamma_a,
+                        nrow_t};
+        rb = RowSide<T>{(const T*)rows->x_b, (T*)rows->y_b, rows->pos_b, rows->x_bs_b, rows->y_bs_b, gamma_b,
+                        nrow_t};
+        grid_rows = cdiv<long long>(2LL * B * nrow_t * (c / 8), wg);
+      }
+      const int g1 = (int)p1.grid, g12 = (int)(p1.grid + p2.grid);
+      const dim3 grid((unsigned)(g12 + grid_rows)), blk(wg);
       if (p1.ub == 8 && p2.ub == 8)
-        hipLaunchKernelGGL((pool_pair_kernel<T, 8, 8, NR>), grid, blk, p2.lds, st, s1, s2, g1, n0, ap0);
+        hipLaunchKernelGGL((pool_pair_kernel<T, 8, 8, NR>), grid, blk, p2.lds, st, s1, s2, g1, n0, ap0, ra, rb, g12, B);
       else if (p1.ub == 8)
-        hipLaunchKernelGGL((pool_pair_kernel<T, 8, 4, NR>), grid, blk, p2.lds, st, s1, s2, g1, n0, ap0);
+        hipLaunchKernelGGL((pool_pair_kernel<T, 8, 4, NR>), grid, blk, p2.lds, st, s1, s2, g1, n0, ap0, ra, rb, g12, B);
       else if (p2.ub == 8)
-        hipLaunchKernelGGL((pool_pair_kernel<T, 4, 8, NR>), grid, blk, p2.lds, st, s1, s2, g1, n0, ap0);
+        hipLaunchKernelGGL((pool_pair_kernel<T, 4, 8, NR>), grid, blk, p2.lds, st, s1, s2, g1, n0, ap0, ra, rb, g12, B);
       else
-        hipLaunchKernelGGL((pool_pair_kernel<T, 4, 4, NR>), grid, blk, p2.lds, st, s1, s2, g1, n0, ap0);
+        hipLaunchKernelGGL((pool_pair_kernel<T, 4, 4, NR>), grid, blk, p2.lds, st, s1, s2, g1, n0, ap0, ra, rb, g12, B);
     };
     if (nr)
       go(uint16_t{}, std::true_type{});
@@ -708,9 +781,18 @@ int pool_pair(const char* name, const void* kv_a, const void* gate_a, void* out_
                     in_bs_a, out_bs_a, stream, nr ? &na : nullptr, entry0_a);
     if (rc != CSAHCA_OK) return rc;
   }
-  if (NB > 0)
-    return pool_entry(name, kv_b, gate_b, nullptr, nullptr, false, 0, nullptr, out_b, B, n_b, c, m_b, dtype,
-                      in_bs_b, out_bs_b, stream, nr ? &nb : nullptr, entry0_b);
+  if (NB > 0) {
+    rc = pool_entry(name, kv_b, gate_b, nullptr, nullptr, false, 0, nullptr, out_b, B, n_b, c, m_b, dtype,
+                    in_bs_b, out_bs_b, stream, nr ? &nb : nullptr, entry0_b);
+    if (rc != CSAHCA_OK) return rc;
+  }
+  if (nr && nrow_t > 0) {  // the rows in launches of their own
+    rc = csahca_norm_rope(rows->x_a, rows->y_a, gamma_a, rows->pos_a, B, nrow_t, 1, c, 1, nr->d, nr->eps,
+                          nr->theta, 1, dtype, rows->x_bs_a, rows->y_bs_a, stream);
+    if (rc != CSAHCA_OK) return rc;
+    return csahca_norm_rope(rows->x_b, rows->y_b, gamma_b, rows->pos_b, B, nrow_t, 1, c, 1, nr->d, nr->eps,
+                            nr->theta, 1, dtype, rows->x_bs_b, rows->y_bs_b, stream);
+  }
   clear_error();
   return CSAHCA_OK;
 }
@@ -768,6 +850,21 @@ extern "C" int csahca_compress_pair_norm_rope(const void* kv_a, const void* gate
   return csahca::pool_pair("csahca_compress_pair_norm_rope", kv_a, gate_a, out_a, n_a, m_a, in_bstride_a,
                            out_bstride_a, kv_b, gate_b, out_b, n_b, m_b, in_bstride_b, out_bstride_b, B, c,
                            dtype, &nr, gamma_a, entry0_a, gamma_b, entry0_b, stream);
+}
+
+extern "C" int csahca_compress_pair_norm_rope_rows(
+    const void* kv_a, const void* gate_a, const float* gamma_a, void* out_a, int n_a, int m_a, long long entry0_a,
+    long long in_bstride_a, long long out_bstride_a, const void* kv_b, const void* gate_b, const float* gamma_b,
+    void* out_b, int n_b, int m_b, long long entry0_b, long long in_bstride_b, long long out_bstride_b, int B,
+    int c, int d_rope, float eps, float theta, int dtype, int T, const void* row_x_a, void* row_y_a,
+    const int* row_pos_a, long long row_x_bstride_a, long long row_y_bstride_a, const void* row_x_b,
+    void* row_y_b, const int* row_pos_b, long long row_x_bstride_b, long long row_y_bstride_b, void* stream) {
+  const NormRope nr{nullptr, eps, theta, d_rope, 1};
+  const csahca::PairRows rows{T, row_x_a, row_x_b, row_y_a, row_y_b, row_pos_a, row_pos_b,
+                              row_x_bstride_a, row_y_bstride_a, row_x_bstride_b, row_y_bstride_b};
+  return csahca::pool_pair("csahca_compress_pair_norm_rope_rows", kv_a, gate_a, out_a, n_a, m_a, in_bstride_a,
+                           out_bstride_a, kv_b, gate_b, out_b, n_b, m_b, in_bstride_b, out_bstride_b, B, c,
+                           dtype, &nr, gamma_a, entry0_a, gamma_b, entry0_b, stream, &rows);
 }
 
 extern "C" int hca_compress(const void* kv, const void* gate, const float* pos_bias, void* out,

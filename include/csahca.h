@@ -358,6 +358,32 @@ int csahca_compress_pair_norm_rope(const void* kv_a, const void* gate_a, const f
                                    int d_rope, float eps, float theta, int dtype, void* stream);
 
 /*
+ * csahca_compress_pair_norm_rope_rows -- csahca_compress_pair_norm_rope, and in the same
+ * launch the T newest raw rows of each side normalised and rotated as window rows: a decode
+ * step's new tokens enter both layers' windows while the blocks they complete are pooled.
+ * Source: as csahca_compress_pair_norm_rope; "DeepSeek-V4 Hybrid Attention: CSA, HCA, mHC,
+ * MoE", section IV (the window branch sees normalised, partially rotated keys too).
+ * The pooling arguments and results are those of csahca_compress_pair_norm_rope.  The rows
+ * of side x are those of
+ *   csahca_norm_rope(row_x_x, row_y_x, gamma_x, row_pos_x, B, T, 1, c, 1, d_rope, eps,
+ *                    theta, 1, dtype, row_x_bstride_x, row_y_bstride_x)
+ * (the side's gain; row (b, t) at position row_pos_x[b] + t, or t when row_pos_x is NULL),
+ * with the same bits.  T >= 0 (0: no rows, the call is csahca_compress_pair_norm_rope);
+ * with T > 0 every row pointer is non-NULL and 16-byte aligned, the row strides are
+ * >= T*c and multiples of 8, and no row range overlaps a pooling input or output.
+ * One launch when the pooling pair is one launch; otherwise the rows follow in two
+ * csahca_norm_rope launches.  Errors as in the two calls; nothing is enqueued on error.
+ */
+int csahca_compress_pair_norm_rope_rows(
+    const void* kv_a, const void* gate_a, const float* gamma_a, void* out_a, int n_a, int m_a,
+    long long entry0_a, long long in_bstride_a, long long out_bstride_a, const void* kv_b,
+    const void* gate_b, const float* gamma_b, void* out_b, int n_b, int m_b, long long entry0_b,
+    long long in_bstride_b, long long out_bstride_b, int B, int c, int d_rope, float eps,
+    float theta, int dtype, int T, const void* row_x_a, void* row_y_a, const int* row_pos_a,
+    long long row_x_bstride_a, long long row_y_bstride_a, const void* row_x_b, void* row_y_b,
+    const int* row_pos_b, long long row_x_bstride_b, long long row_y_bstride_b, void* stream);
+
+/*
  * csa_attend_ex / hca_attend_ex -- csa_attend_sink / hca_attend_sink with the RMSNorm and
  * partial RoPE of the queries done inside the attention kernel, as it loads them.
  * Source: "DeepSeek-V4 Hybrid Attention: CSA, HCA, mHC, MoE", section IV (queries and KV

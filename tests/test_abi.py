@@ -85,6 +85,26 @@ def test_pool_validation():
         args[i] = v
         assert pn(*args) == want, (i, v)
         assert "csahca_compress_pair_norm_rope" in lib.last_error()
+    # ... and with the window rows: the pair's checks, then the rows' (T >= 0; with T > 0
+    # every row pointer set and aligned, strides >= T*c and multiples of 8)
+    pr_rows = L.csahca_compress_pair_norm_rope_rows
+    rows_ok = [1, FAKE, FAKE, None, 8, 8, FAKE, FAKE, None, 8, 8]
+    ok_r = ok[:-1] + rows_ok + [None]
+    for i, v, want in bad_cases[:3]:
+        args = list(ok_r)
+        args[i] = v
+        assert pr_rows(*args) == want, (i, v)
+    R0 = len(ok) - 1  # index of T
+    for off, v, want in [(0, -1, EINVAL),         # T
+                         (1, None, EINVAL),        # row_x_a
+                         (7, None, EINVAL),        # row_y_b
+                         (2, FAKE + 4, EINVAL),    # row_y_a alignment
+                         (4, 7, EINVAL),           # row_x_bstride_a below T*c
+                         (10, 12, EINVAL)]:        # row_y_bstride_b not a multiple of 8
+        args = list(ok_r)
+        args[R0 + off] = v
+        assert pr_rows(*args) == want, (off, v)
+        assert "csahca_compress_pair_norm_rope_rows" in lib.last_error()
     # overlapped form: prev is 0 or 1, stream b pointers are required, an append of one
     # block with prev = 1 emits nothing
     ov = L.csa_compress_overlap

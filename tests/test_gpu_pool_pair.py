@@ -171,3 +171,54 @@ def test_pair_norm_rope_equals_separate_calls(name):
             for b in range(B):
                 ref, xn, kc = pooled_reference(x[b, :N * m], z[b, :N * m], m, None, gg.cpu().numpy(), d, e0)
                 check_pooled(got[b, :N], ref, xn, kc, d, dt)
+
+
+@pytest.mark.parametrize("name,T", [("decode_pair", 1), ("decode_pair_swapped", 3), ("ragged_strides", 2),
+                                    ("hca_side_empty", 1)])
+def test_pair_norm_rope_rows_equals_separate_calls(name, T):
+    """csahca_compress_pair_norm_rope_rows against csahca_compress_pair_norm_rope and two
+    csahca_norm_rope calls on the rows (same bits): the window rows of both sides, each
+    with its side's gain and its own positions, in the paired launch (decode shapes) and
+    after the fallback launches (one side empty); rows past T are left alone."""
+    B, c, (n_a, m_a), (n_b, m_b), dt, pad = CASES[name]
+    print(f"[pool pair norm_rope rows {name} T={T}]", flush=True)
+    g = torch.Generator(device="cuda").manual_seed(zlib.crc32(name.encode()) % 1000 + 2)
+    Xa, Za = _side(g, B, n_a, c, dt, pad)
+    Xb, Zb = _side(g, B, n_b, c, dt, pad)
+    ga = torch.rand((c,), generator=g, device="cuda") + 0.5
+    gb = torch.rand((c,), generator=g, device="cuda") + 0.5
+    e0a, e0b = 1000, 7
+    d, eps, theta = min(64, c), 1e-6, 10000.0
+    ibs_a, ibs_b = (n_a + pad) * c, (n_b + pad) * c
+    Na, Nb = n_a // m_a, n_b // m_b
+    tdt = Xa.dtype
+    sep_a = torch.full((B, max(Na, 1) + 1, c), 7, dtype=tdt, device="cuda")
+    sep_b = torch.full((B, max(Nb, 1) + 1, c), 7, dtype=tdt, device="cuda")
+    pair_a, pair_b = sep_a.clone(), sep_b.clone()
+    obs_a, obs_b = sep_a.shape[1] * c, sep_b.shape[1] * c
+    # rows: the last T raw tokens of each side into a window buffer of T + 5 rows per
+    # sequence (strided), at positions from a device array
+    LW = T + 5
+    xa_rows, xb_rows = Xa[:, n_a + pad - T:], Xb[:, n_b + pad - T:]
+    ya_sep = torch.full((B, LW, c), 3, dtype=tdt, device="cuda")
+    yb_sep = ya_sep.clone()
+    ya_pair, yb_pair = ya_sep.clone(), yb_sep.clone()
+    pos_a = torch.arange(B, dtype=torch.int32, device="cuda") * 1000003 + n_a - T
+    pos_b = torch.arange(B, dtype=torch.int32, device="cuda") * 7919 + n_b - T
+    lib.csahca_compress_pair_norm_rope(Xa, Za, ga, sep_a, n_a, m_a, e0a, ibs_a, obs_a, Xb, Zb, gb, sep_b,
+                                       n_b, m_b, e0b, ibs_b, obs_b, B, c, d, eps, theta, dt)
+    lib.csahca_norm_rope(xa_rows, ya_sep[:, 2:], ga, pos_a, B, T, 1, c, 1, d, eps, theta, 1, dt,
+                         x_bstride=ibs_a, y_bstride=LW * c)
+    lib.csahca_norm_rope(xb_rows, yb_sep[:, 2:], gb, pos_b, B, T, 1, c, 1, d, eps, theta, 1, dt,
+                         x_bstride=ibs_b, y_bstride=LW * c)
+    lib.csahca_compress_pair_norm_rope_rows(Xa, Za, ga, pair_a, n_a, m_a, e0a, ibs_a, obs_a, Xb, Zb, gb,
+                                            pair_b, n_b, m_b, e0b, ibs_b, obs_b, B, c, d, eps, theta, dt,
+                                            T, xa_rows, ya_pair[:, 2:], pos_a, ibs_a, LW * c, xb_rows,
+                                            yb_pair[:, 2:], pos_b, ibs_b, LW * c)
+    torch.cuda.synchronize()
+    iv = torch.int16 if dt == BF16 else torch.int32
+    assert torch.equal(pair_a.view(iv), sep_a.view(iv))
+    assert torch.equal(pair_b.view(iv), sep_b.view(iv))
+    assert torch.equal(ya_pair.view(iv), ya_sep.view(iv))
+    assert torch.equal(yb_pair.view(iv), yb_sep.view(iv))
+    assert bool((ya_pair[:, :2] == 3).all()) and bool((ya_pair[:, 2 + T:] == 3).all())

@@ -247,6 +247,13 @@ CSAHCA_DEV void pool_block(const T* __restrict__ X, const T* __restrict__ Z,
   const int b = bi / N, i = bi - b * N;
   const int cv = cg * CVG + cvl;
   const int blk = OV ? i + prev : i;
+  // NR: the gains of this thread's first channel of the epilogue (and its pair partner),
+  // loaded now so that their latency hides under the pooling
+  float g_t = 1.f, g_u = 1.f;
+  if (NR && nr.gamma && (int)threadIdx.x < c) {
+    g_t = nr.gamma[threadIdx.x];
+    g_u = nr.gamma[threadIdx.x ^ 1];
+  }
   // the entry's tokens: stream a's m, then (overlapped, after the first block) stream b's
   // m of the previous block; thread s takes the s-th sub-range of them
   const int mt = (OV && blk >= 1) ? 2 * m : m;
@@ -315,7 +322,9 @@ CSAHCA_DEV void pool_block(const T* __restrict__ X, const T* __restrict__ Z,
     const long long pos = (long long)m * (entry0 + i);
     for (int t = threadIdx.x; t < c; t += blockDim.x) {
       const int u = t ^ 1;  // the pair's other channel
-      const float gt = nr.gamma ? nr.gamma[t] : 1.f, gu = nr.gamma ? nr.gamma[u] : 1.f;
+      const bool first = t == (int)threadIdx.x;  // gains loaded at the start
+      const float gt = !nr.gamma ? 1.f : first ? g_t : nr.gamma[t];
+      const float gu = !nr.gamma ? 1.f : first ? g_u : nr.gamma[u];
       float v = fin[t] * (inv * gt);
       if (t >= c - nr.d) {
         const float w = fin[u] * (inv * gu);

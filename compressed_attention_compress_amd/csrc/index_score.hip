@@ -212,8 +212,12 @@ __global__ __launch_bounds__(256) void index_score_fp8(
 // private to a wave, so there is no barrier until the final write-out.  Inside a block,
 // row r holds its 16-byte chunks in the order c ^ (r & 7): a lane reading 32 bytes of its
 // key row then hits eight distinct bank groups per eight lanes.
+// Four blocks per wave ring (three in flight, 12 KiB of DMA per workgroup): with the
+// workgroup's LDS at 49 KiB, three workgroups fit a CU.  Measured at the 1M and 128K
+// decode shapes: rings of 3 and 4 blocks 28.7 us per launch, 5 blocks 29.6, 6 blocks 30.1,
+// 7 blocks 30.8.
 #ifndef CSAHCA_SCORE_RING
-#define CSAHCA_SCORE_RING 6  // key blocks per wave ring (RING - 1 in flight)
+#define CSAHCA_SCORE_RING 4  // key blocks per wave ring (RING - 1 in flight)
 #endif
 constexpr int RING = CSAHCA_SCORE_RING;
 

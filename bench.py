@@ -401,15 +401,15 @@ def score_source_hash():
     return h.hexdigest()
 
 
-def read_traffic(kernel_name):
-    """HBM traffic of the dominant kernel from committed counter runs, if the kernel's
-    sources are unchanged since they were taken (else None)."""
+def read_traffic(kernel_name, workload):
+    """HBM traffic of the dominant kernel from committed counter runs, if they were taken
+    on this workload and the kernel's sources are unchanged since (else None)."""
     try:
         with open(PROFILE_TRAFFIC) as f:
             rec = json.load(f)
         h = score_source_hash()
         ent = rec.get(kernel_name)
-        if ent and ent.get("source_sha256") == h:
+        if ent and ent.get("source_sha256") == h and ent.get("workload") == workload:
             return ent["bytes_per_launch"]
     except (OSError, ValueError, KeyError):
         pass
@@ -437,9 +437,10 @@ def _counter_means(folder, counter, name_part):
     return sum(vals) / len(vals), len(vals)
 
 
-def write_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, out_path):
+def write_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, out_path, workload):
     """HBM bytes per launch of the dominant kernel: FETCH_SIZE + WRITE_SIZE (KiB per
-    dispatch), each scaled by what the same counter reads for a plain 1 GiB device copy."""
+    dispatch), each scaled by what the same counter reads for a plain 1 GiB device copy.
+    `workload`: the config the counter runs used (the record applies to it alone)."""
     cf, _ = _counter_means(copy_fetch_dir, "FETCH_SIZE", COPY_KERNEL)
     cw, _ = _counter_means(copy_write_dir, "WRITE_SIZE", COPY_KERNEL)
     f_scale = COPY_BYTES / (cf * 1024.0)   # true bytes per counted byte
@@ -452,7 +453,7 @@ def write_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, out_path
         rec[key] = {"fetch_kib_per_dispatch": fk, "write_kib_per_dispatch": wk,
                     "dispatches": [nf, nw],
                     "bytes_per_launch": round(fk * 1024.0 * f_scale + wk * 1024.0 * w_scale),
-                    "source_sha256": score_source_hash()}
+                    "workload": workload, "source_sha256": score_source_hash()}
     with open(out_path, "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec))
@@ -1010,7 +1011,8 @@ def gop_bench(cfg, reps, cpu_seconds, no_cpu):
 def main():
     args = parse()
     if args.traffic_from:
-        write_traffic(*args.traffic_from, args.traffic_out)
+        from synthgen.configs import CONFIGS as CFGS  # --config: the one the counter runs used
+        write_traffic(*args.traffic_from, args.traffic_out, CFGS[args.config].name)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -1119,7 +1121,7 @@ def main():
                         "bound": "hbm",
                         "achieved": round(ach, 1),
                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
-                        "traffic": read_traffic(kname) if decode else None,
+                        "traffic": read_traffic(kname, cfg.name) if decode else None,
                         "avg_launch_us": round(dur * 1e6, 2), "bytes_per_launch": kb}
         else:  # a prefill chunk's scoring is bound by the fp8 matrix cores
             tf = f8 / dur / 1e12

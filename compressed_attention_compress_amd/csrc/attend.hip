@@ -1086,8 +1086,8 @@ struct Plan {
 
 // Launch shape.  A workgroup holds up to 64 heads (4 waves; 8 waves when two prefill
 // queries share the rows).  When the queries alone give fewer than 256 workgroups their
-// rows are split over more (one per CU, each keeping three tiles in flight), each split
-// holding whole iterations (64 rows with the 4-tile ring).
+// rows are split over more, each split holding whole iterations (32 rows with the 2-tile
+// ring, 64 with the 4-tile one).
 Plan make_plan(int B, int Tq, int n_h, int n_slots_c, int W, bool csa) {
   Plan P;
   P.Tg = 1;
@@ -1100,9 +1100,12 @@ Plan make_plan(int B, int Tq, int n_h, int n_slots_c, int W, bool csa) {
   P.n_slots = n_slots_c + W + P.Tg - 1;
   P.nqg = cdiv(Tq, P.Tg);
   const long long base = (long long)P.n_hg * B * P.nqg;
-  // the 4-tile ring (two tiles per iteration) where it costs no occupancy: 4-wave
-  // workgroups when there are few, and 8-wave ones (a whole CU's registers anyway)
-  P.NS = ((P.NW == 4 && base < 256) || P.NW == 8) ? 4 : 2;
+  // The 4-tile ring (two tiles per iteration) where it costs no occupancy: 4-wave
+  // prefill workgroups when there are few, and 8-wave ones (a whole CU's registers
+  // anyway).  Decode keeps the 2-tile ring: two workgroups fit a CU, so the CSA and HCA
+  // calls of one step, run side by side on two streams, share CUs instead of waiting for
+  // whole ones (Pro 1M decode 81.2 -> 78.3 us per step; the 128K shapes unchanged).
+  P.NS = ((P.NW == 4 && base < 256 && Tq > 1) || P.NW == 8) ? 4 : 2;
   // splits hold whole iterations (TPI tiles), at least one each
   const int tpi = P.NS >= 4 ? 2 : 1;
   const int niter = cdiv(cdiv(P.n_slots, TILE), tpi);
@@ -1118,8 +1121,10 @@ Plan make_plan(int B, int Tq, int n_h, int n_slots_c, int W, bool csa) {
   P.ml_bytes = P.n_splits > 1 ? csahca::align_up((size_t)(nqh * P.n_splits * 4 * 4), 256) : 0;
   P.ws = P.opart_bytes + P.ml_bytes;
   // column split only with the 2-tile ring (many workgroups, one tile per iteration):
-  // with two tiles per iteration the exchange costs what the fewer transpose reads save
-  P.CS = P.Tg == 1 && (P.NW == 2 || P.NW == 4) && P.NS == 2;
+  // with two tiles per iteration the exchange costs what the fewer transpose reads save;
+  // and not at decode, where each workgroup runs few iterations and the exchange costs
+  // what it saves
+  P.CS = P.Tg == 1 && (P.NW == 2 || P.NW == 4) && P.NS == 2 && Tq > 1;
   P.lds = attend_lds_bytes(P.NS, P.NW, P.RS, csa, P.CS, true);  // room for the query norm gains
   return P;
 }

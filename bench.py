@@ -290,27 +290,40 @@ class Workload:
                 lib.hca_attend_sink(*args, sk, *tail)
 
     def step(self, r):
-        """One pass of the path.  At decode, with both layers present, the HCA attention
-        runs on a second stream while the indexer (scoring with its fused top-k selection)
-        and the CSA attention run on the first: the HCA layer needs nothing from the
-        indexer.  The second stream forks after the pooling.
-        Edges between the graph's hardware queues resolve late (the waiting node started
-        15 to 40 microseconds after its producer in kernel traces), so the CSA chain is
-        issued first, stays on the pooling's queue, and keeps no edge from the second
-        stream."""
+        """One pass of the path.  At decode, with both layers present, the HCA layer runs on
+        a second stream beside the CSA chain: each stream pools its own cache's new block,
+        then the CSA stream scores, selects and attends, and the HCA stream attends.  The
+        second stream forks at the start of the step and joins at its end.
+        Edges between the graph's hardware queues resolve late (a waiting node started up
+        to tens of microseconds after its producer in kernel traces), so the CSA chain is
+        issued first and keeps no edge from the second stream; a fork after the pooling of
+        both caches started the HCA attention only while the CSA attention ran."""
         import torch
 
-        if len(self.layers) == 2 and self.s_hca is not None:
+        if len(self.layers) == 2 and self.s_hca is not None and self.nr:
+            # with norm and rotation: both caches and both layers' new window rows in one
+            # launch (csahca_compress_pair_norm_rope_rows), then the fork
             main = torch.cuda.current_stream()
             self.pool_new_blocks(r)
             pooled = torch.cuda.Event()
             pooled.record(main)
-            # the CSA chain is issued first, so that it stays on the pooling's hardware
-            # queue; the second stream forks from the pooling
             self.index(r)
             self.attend(r, ["csa"])
             self.s_hca.wait_event(pooled)
             with torch.cuda.stream(self.s_hca):
+                self.attend(r, ["hca"])
+            main.wait_stream(self.s_hca)
+            return
+        if len(self.layers) == 2 and self.s_hca is not None:
+            main = torch.cuda.current_stream()
+            start = torch.cuda.Event()
+            start.record(main)
+            self.pool_new_blocks(r, ["csa"])
+            self.index(r)
+            self.attend(r, ["csa"])
+            self.s_hca.wait_event(start)
+            with torch.cuda.stream(self.s_hca):
+                self.pool_new_blocks(r, ["hca"])
                 self.attend(r, ["hca"])
             main.wait_stream(self.s_hca)
             return

@@ -68,6 +68,14 @@ _SIGNATURES = {
                            _I, _F, _F, _I, _P, _P, _P, _SZ, _P]),
     "hca_attend_ex": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _I, _I,
                            _F, _F, _I, _P, _P, _P, _SZ, _P]),
+    "csa_attend_begin": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _I,
+                              _I, _F, _F, _I, _P, _P, _P, _SZ, _P]),
+    "hca_attend_begin": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _I, _I,
+                              _F, _F, _I, _P, _P, _P, _SZ, _P]),
+    "csa_attend_end": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _I,
+                            _I, _F, _F, _I, _P, _P, _P, _SZ, _P]),
+    "hca_attend_end": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _I, _I,
+                            _F, _F, _I, _P, _P, _P, _SZ, _P]),
     "csahca_last_error": (ctypes.c_char_p, []),
     "csahca_version": (_I, []),
 }
@@ -318,6 +326,42 @@ def hca_attend_ex(q, ckv, win_kv, win_pos, q_pos, m, B, Tq, n_h, c, N_h, L, W, s
                   q_gamma, q_norm, d_rope, eps, theta, dtype, out, lse, workspace, ws_bytes,
                   stream=None):
     return _check("hca_attend_ex", load().hca_attend_ex(
+        _ptr(q), _ptr(ckv), _ptr(win_kv), _ptr(win_pos), _ptr(q_pos), m, B, Tq, n_h, c, N_h, L, W,
+        float(scale), _ptr(sink), _ptr(q_gamma), q_norm, d_rope, float(eps), float(theta), dtype,
+        _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def csa_attend_begin(q, ckv, topk_idx, win_kv, win_pos, q_pos, B, Tq, n_h, c, N_c, k, L, W, scale,
+                     sink, q_gamma, q_norm, d_rope, eps, theta, dtype, out, lse, workspace, ws_bytes,
+                     stream=None):
+    return _check("csa_attend_begin", load().csa_attend_begin(
+        _ptr(q), _ptr(ckv), _ptr(topk_idx), _ptr(win_kv), _ptr(win_pos), _ptr(q_pos), B, Tq,
+        n_h, c, N_c, k, L, W, float(scale), _ptr(sink), _ptr(q_gamma), q_norm, d_rope, float(eps),
+        float(theta), dtype, _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def hca_attend_begin(q, ckv, win_kv, win_pos, q_pos, m, B, Tq, n_h, c, N_h, L, W, scale, sink,
+                     q_gamma, q_norm, d_rope, eps, theta, dtype, out, lse, workspace, ws_bytes,
+                     stream=None):
+    return _check("hca_attend_begin", load().hca_attend_begin(
+        _ptr(q), _ptr(ckv), _ptr(win_kv), _ptr(win_pos), _ptr(q_pos), m, B, Tq, n_h, c, N_h, L, W,
+        float(scale), _ptr(sink), _ptr(q_gamma), q_norm, d_rope, float(eps), float(theta), dtype,
+        _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def csa_attend_end(q, ckv, topk_idx, win_kv, win_pos, q_pos, B, Tq, n_h, c, N_c, k, L, W, scale,
+                   sink, q_gamma, q_norm, d_rope, eps, theta, dtype, out, lse, workspace, ws_bytes,
+                   stream=None):
+    return _check("csa_attend_end", load().csa_attend_end(
+        _ptr(q), _ptr(ckv), _ptr(topk_idx), _ptr(win_kv), _ptr(win_pos), _ptr(q_pos), B, Tq,
+        n_h, c, N_c, k, L, W, float(scale), _ptr(sink), _ptr(q_gamma), q_norm, d_rope, float(eps),
+        float(theta), dtype, _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def hca_attend_end(q, ckv, win_kv, win_pos, q_pos, m, B, Tq, n_h, c, N_h, L, W, scale, sink,
+                   q_gamma, q_norm, d_rope, eps, theta, dtype, out, lse, workspace, ws_bytes,
+                   stream=None):
+    return _check("hca_attend_end", load().hca_attend_end(
         _ptr(q), _ptr(ckv), _ptr(win_kv), _ptr(win_pos), _ptr(q_pos), m, B, Tq, n_h, c, N_h, L, W,
         float(scale), _ptr(sink), _ptr(q_gamma), q_norm, d_rope, float(eps), float(theta), dtype,
         _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)))

@@ -1225,13 +1225,22 @@ int check_nr(const char* name, const NrArgs& nr, int dtype) {
   return CSAHCA_OK;
 }
 
+// phase: PHASE_ALL the attention launch and, with several splits, the split merge;
+// PHASE_BEGIN the attention launch only; PHASE_END the split merge only (nothing when the
+// plan has one split, or on the float32 path, whose one launch is the begin phase).
+constexpr int PHASE_ALL = 0, PHASE_BEGIN = 1, PHASE_END = 2;
+
 int attend_impl(const char* name, bool csa, const void* q, const void* ckv, const int* topk,
                 const void* win_kv, const int* win_pos, const int* q_pos, int m, int B, int Tq,
                 int n_h, int c, int N, int k, int L, int W, float scale, const float* sink,
                 const NrArgs& nr, int dtype, void* out, float* lse, void* workspace, size_t ws_bytes,
-                hipStream_t st) {
+                hipStream_t st, int phase = PHASE_ALL) {
   using namespace csahca;
   const int n_slots_c = csa ? k : N;
+  if (dtype == CSAHCA_F32 && phase == PHASE_END) {
+    clear_error();
+    return CSAHCA_OK;
+  }
   if (dtype == CSAHCA_F32) {
     AttnF32Args A;
     A.q = (const float*)q;
@@ -1309,10 +1318,15 @@ int attend_impl(const char* name, bool csa, const void* q, const void* ckv, cons
     set_error("%s: a split needs too much LDS", name);
     return CSAHCA_ENOTSUP;
   }
-  const int lrc = csa ? launch_attend_nw<true>(P, A, st) : launch_attend_nw<false>(P, A, st);
-  if (lrc != CSAHCA_OK) return lrc;
-  int rc = launch_status(name);
-  if (rc != CSAHCA_OK || P.n_splits == 1) return rc;
+  if (phase != PHASE_END) {
+    const int lrc = csa ? launch_attend_nw<true>(P, A, st) : launch_attend_nw<false>(P, A, st);
+    if (lrc != CSAHCA_OK) return lrc;
+    const int rc = launch_status(name);
+    if (rc != CSAHCA_OK || P.n_splits == 1 || phase == PHASE_BEGIN) return rc;
+  } else if (P.n_splits == 1) {
+    clear_error();
+    return CSAHCA_OK;
+  }
   const long long nqh = (long long)B * Tq * n_h;
   // few splits: one wave per pair loads them all at once; many: four waves per pair
   if (P.n_splits <= COMBINE_WAVE_SPLITS)
@@ -1343,7 +1357,8 @@ namespace {
 int csa_entry(const char* name, const void* q, const void* ckv, const int* topk_idx,
               const void* win_kv, const int* win_pos, const int* q_pos, int B, int Tq, int n_h,
               int c, int N_c, int k, int L, int W, float scale, const float* sink, const NrArgs& nr,
-              int dtype, void* out, float* lse, void* workspace, size_t ws_bytes, void* stream) {
+              int dtype, void* out, float* lse, void* workspace, size_t ws_bytes, void* stream,
+              int phase = PHASE_ALL) {
   using namespace csahca;
   int rc = check_attend(name, q, ckv, win_kv, win_pos, q_pos, B, Tq, n_h, c, N_c, L, W, dtype, out, k);
   if (rc != CSAHCA_OK) return rc;
@@ -1357,13 +1372,13 @@ int csa_entry(const char* name, const void* q, const void* ckv, const int* topk_
     return CSAHCA_EINVAL;
   }
   return attend_impl(name, true, q, ckv, topk_idx, win_kv, win_pos, q_pos, 1, B, Tq, n_h, c, N_c, k,
-                     L, W, scale, sink, nr, dtype, out, lse, workspace, ws_bytes, (hipStream_t)stream);
+                     L, W, scale, sink, nr, dtype, out, lse, workspace, ws_bytes, (hipStream_t)stream, phase);
 }
 
 int hca_entry(const char* name, const void* q, const void* ckv, const void* win_kv,
               const int* win_pos, const int* q_pos, int m, int B, int Tq, int n_h, int c, int N_h,
               int L, int W, float scale, const float* sink, const NrArgs& nr, int dtype, void* out,
-              float* lse, void* workspace, size_t ws_bytes, void* stream) {
+              float* lse, void* workspace, size_t ws_bytes, void* stream, int phase = PHASE_ALL) {
   using namespace csahca;
   int rc = check_attend(name, q, ckv, win_kv, win_pos, q_pos, B, Tq, n_h, c, N_h, L, W, dtype, out, N_h);
   if (rc != CSAHCA_OK) return rc;
@@ -1377,7 +1392,7 @@ int hca_entry(const char* name, const void* q, const void* ckv, const void* win_
     return CSAHCA_EINVAL;
   }
   return attend_impl(name, false, q, ckv, nullptr, win_kv, win_pos, q_pos, m, B, Tq, n_h, c, N_h, N_h,
-                     L, W, scale, sink, nr, dtype, out, lse, workspace, ws_bytes, (hipStream_t)stream);
+                     L, W, scale, sink, nr, dtype, out, lse, workspace, ws_bytes, (hipStream_t)stream, phase);
 }
 
 }  // namespace
@@ -1437,4 +1452,50 @@ extern "C" int hca_attend_ex(const void* q, const void* ckv, const void* win_kv,
   return hca_entry("hca_attend_ex", q, ckv, win_kv, win_pos, q_pos, m, B, Tq, n_h, c, N_h, L, W,
                    scale, sink, NrArgs{q_gamma, q_norm, d_rope, eps, theta}, dtype,
                    out, lse, workspace, ws_bytes, stream);
+}
+
+// The two halves of csa_attend_ex / hca_attend_ex: the attention launch, and the split
+// merge, so that a caller can run the merge on another stream than the attention.
+extern "C" int csa_attend_begin(const void* q, const void* ckv, const int* topk_idx,
+                                const void* win_kv, const int* win_pos, const int* q_pos, int B,
+                                int Tq, int n_h, int c, int N_c, int k, int L, int W, float scale,
+                                const float* sink, const float* q_gamma, int q_norm, int d_rope,
+                                float eps, float theta, int dtype, void* out, float* lse,
+                                void* workspace, size_t ws_bytes, void* stream) {
+  return csa_entry("csa_attend_begin", q, ckv, topk_idx, win_kv, win_pos, q_pos, B, Tq, n_h, c, N_c, k,
+                   L, W, scale, sink, NrArgs{q_gamma, q_norm, d_rope, eps, theta}, dtype, out, lse,
+                   workspace, ws_bytes, stream, PHASE_BEGIN);
+}
+
+extern "C" int csa_attend_end(const void* q, const void* ckv, const int* topk_idx,
+                              const void* win_kv, const int* win_pos, const int* q_pos, int B,
+                              int Tq, int n_h, int c, int N_c, int k, int L, int W, float scale,
+                              const float* sink, const float* q_gamma, int q_norm, int d_rope,
+                              float eps, float theta, int dtype, void* out, float* lse,
+                              void* workspace, size_t ws_bytes, void* stream) {
+  return csa_entry("csa_attend_end", q, ckv, topk_idx, win_kv, win_pos, q_pos, B, Tq, n_h, c, N_c, k,
+                   L, W, scale, sink, NrArgs{q_gamma, q_norm, d_rope, eps, theta}, dtype, out, lse,
+                   workspace, ws_bytes, stream, PHASE_END);
+}
+
+extern "C" int hca_attend_begin(const void* q, const void* ckv, const void* win_kv,
+                                const int* win_pos, const int* q_pos, int m, int B, int Tq,
+                                int n_h, int c, int N_h, int L, int W, float scale,
+                                const float* sink, const float* q_gamma, int q_norm, int d_rope,
+                                float eps, float theta, int dtype, void* out, float* lse,
+                                void* workspace, size_t ws_bytes, void* stream) {
+  return hca_entry("hca_attend_begin", q, ckv, win_kv, win_pos, q_pos, m, B, Tq, n_h, c, N_h, L, W,
+                   scale, sink, NrArgs{q_gamma, q_norm, d_rope, eps, theta}, dtype, out, lse, workspace,
+                   ws_bytes, stream, PHASE_BEGIN);
+}
+
+extern "C" int hca_attend_end(const void* q, const void* ckv, const void* win_kv,
+                              const int* win_pos, const int* q_pos, int m, int B, int Tq,
+                              int n_h, int c, int N_h, int L, int W, float scale,
+                              const float* sink, const float* q_gamma, int q_norm, int d_rope,
+                              float eps, float theta, int dtype, void* out, float* lse,
+                              void* workspace, size_t ws_bytes, void* stream) {
+  return hca_entry("hca_attend_end", q, ckv, win_kv, win_pos, q_pos, m, B, Tq, n_h, c, N_h, L, W,
+                   scale, sink, NrArgs{q_gamma, q_norm, d_rope, eps, theta}, dtype, out, lse, workspace,
+                   ws_bytes, stream, PHASE_END);
 }

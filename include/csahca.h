@@ -417,6 +417,41 @@ int hca_attend_ex(const void* q, const void* ckv, const void* win_kv, const int*
                   size_t ws_bytes, void* stream);
 
 /*
+ * csa_attend_begin / csa_attend_end, hca_attend_begin / hca_attend_end -- the two halves
+ * of csa_attend_ex / hca_attend_ex, for a caller that runs the split merge on another
+ * stream than the attention (a decode step that joins its two attention layers on one
+ * stream: the merge there waits only for the attention, already finished).
+ * Source: as csa_attend / hca_attend (the split merge combines partial softmax results by
+ * their log-sum-exp, which is exact for the joint softmax).
+ * Arguments, limits, workspace and errors are those of csa_attend_ex / hca_attend_ex; both
+ * halves take the same arguments.  _begin enqueues the attention: when the launch plan
+ * has a single split (or dtype is CSAHCA_F32) it writes out and lse itself and _end does
+ * nothing; otherwise it leaves per-split partial results in the workspace, and _end
+ * (enqueued after _begin has completed, with the workspace untouched in between) merges
+ * them into out and lse.  _begin then _end give the same bits as the _ex call.
+ */
+int csa_attend_begin(const void* q, const void* ckv, const int* topk_idx, const void* win_kv,
+                     const int* win_pos, const int* q_pos, int B, int Tq, int n_h, int c, int N_c,
+                     int k, int L, int W, float scale, const float* sink, const float* q_gamma,
+                     int q_norm, int d_rope, float eps, float theta, int dtype, void* out,
+                     float* lse, void* workspace, size_t ws_bytes, void* stream);
+int csa_attend_end(const void* q, const void* ckv, const int* topk_idx, const void* win_kv,
+                   const int* win_pos, const int* q_pos, int B, int Tq, int n_h, int c, int N_c,
+                   int k, int L, int W, float scale, const float* sink, const float* q_gamma,
+                   int q_norm, int d_rope, float eps, float theta, int dtype, void* out,
+                   float* lse, void* workspace, size_t ws_bytes, void* stream);
+int hca_attend_begin(const void* q, const void* ckv, const void* win_kv, const int* win_pos,
+                     const int* q_pos, int m, int B, int Tq, int n_h, int c, int N_h, int L, int W,
+                     float scale, const float* sink, const float* q_gamma, int q_norm,
+                     int d_rope, float eps, float theta, int dtype, void* out, float* lse,
+                     void* workspace, size_t ws_bytes, void* stream);
+int hca_attend_end(const void* q, const void* ckv, const void* win_kv, const int* win_pos,
+                   const int* q_pos, int m, int B, int Tq, int n_h, int c, int N_h, int L, int W,
+                   float scale, const float* sink, const float* q_gamma, int q_norm, int d_rope,
+                   float eps, float theta, int dtype, void* out, float* lse, void* workspace,
+                   size_t ws_bytes, void* stream);
+
+/*
  * csahca_kv_ring_rows / csahca_kv_append / csahca_kv_fork -- the cache lifecycle of one
  * layer: raw tokens arrive, completed blocks become compressed entries, the recent window
  * stays exact, a request can start from another's prefix.

@@ -219,6 +219,19 @@ def test_attend_validation():
     assert "bfloat16" in lib.last_error()
     assert L.hca_attend_ex(*hbad, 0.04, None, None, 0, 64, 1e-6, 1e4, 1, FAKE, None, FAKE, wh,
                            None) == EINVAL  # m, checked before the norm arguments
+    # the two halves (_begin / _end) check exactly what the _ex call checks
+    for half in ("begin", "end"):
+        cfn, hfn = getattr(L, f"csa_attend_{half}"), getattr(L, f"hca_attend_{half}")
+        assert cfn(*base, 0.04, *nr, 1, FAKE, None, FAKE, ws - 1, None) == EWORKSPACE
+        assert f"csa_attend_{half}" in lib.last_error()
+        assert hfn(*hb, 0.04, *nr, 1, FAKE, None, FAKE, wh - 1, None) == EWORKSPACE
+        assert cfn(*base, -1.0, *nr, 1, FAKE, None, FAKE, ws, None) == EINVAL
+        assert hfn(*hbad, 0.04, *nr, 1, FAKE, None, FAKE, wh, None) == EINVAL
+        for i, v in [(2, 2), (3, 60), (4, -1.0)]:
+            bad = list(nr)
+            bad[i] = v
+            assert cfn(*base, 0.04, *bad, 1, FAKE, None, FAKE, ws, None) == EINVAL, (half, i, v)
+            assert hfn(*hb, 0.04, *bad, 1, FAKE, None, FAKE, wh, None) == EINVAL, (half, i, v)
 
 
 def test_binding_raises_with_message():

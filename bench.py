@@ -177,6 +177,26 @@ class Workload:
         cfg, lib, prob = self.cfg, self.lib, self.prob
         B, c, n = cfg.B, cfg.c, self.n
         layers = self.layers if layers is None else layers
+        if self.nr and self.kind != "prefill" and len(self.layers) == 2 and len(layers) == 1:
+            # one layer of the pair on its own stream: its pooling with the norm and its new
+            # window rows in one launch (the pair call with the other side empty)
+            l = layers[0]
+            m = cfg.m if l == "csa" else cfg.m_hca
+            first_blk = self.n_old // m
+            tok0 = first_blk * m
+            C = self.rep[r][f"C_{l}"]
+            Tq, L = self.Tq, self.nr_L
+            side = [prob[f"X_{l}"][:, tok0:], prob[f"Z_{l}"][:, tok0:], self.g_kv, C[:, first_blk:], n - tok0,
+                    m, first_blk, n * c, (n // m) * c]
+            empty = [None, None, None, None, 0, cfg.m_hca if l == "csa" else cfg.m, 0, c, c]
+            rows = [prob[f"X_{l}"][:, n - Tq:], self.nr_win[l][:, L - Tq:], self.nr_new_pos, n * c, L * c]
+            no_rows = [None, None, None, c, c]
+            a, b = (side, empty) if l == "csa" else (empty, side)
+            ra, rb = (rows, no_rows) if l == "csa" else (no_rows, rows)
+            lib.csahca_compress_pair_norm_rope_rows(*a, *b, B, c, self.NR_D, self.NR_EPS, self.NR_THETA,
+                                                    cfg.dtype, Tq, *ra, *rb)
+            self.rows_pooled = True
+            return
         if len(layers) == 2:
             # both caches in one call (one launch at decode)
             sides = []
@@ -291,29 +311,16 @@ class Workload:
 
     def step(self, r):
         """One pass of the path.  At decode, with both layers present, the HCA layer runs on
-        a second stream beside the CSA chain: each stream pools its own cache's new block,
-        then the CSA stream scores, selects and attends, and the HCA stream attends.  The
-        second stream forks at the start of the step and joins at its end.
+        a second stream beside the CSA chain: each stream pools its own cache's new block
+        (with norm and rotation, together with its layer's new window row), then the CSA
+        stream scores, selects and attends, and the HCA stream attends.  The second stream
+        forks at the start of the step and joins at its end.
         Edges between the graph's hardware queues resolve late (a waiting node started up
         to tens of microseconds after its producer in kernel traces), so the CSA chain is
         issued first and keeps no edge from the second stream; a fork after the pooling of
         both caches started the HCA attention only while the CSA attention ran."""
         import torch
 
-        if len(self.layers) == 2 and self.s_hca is not None and self.nr:
-            # with norm and rotation: both caches and both layers' new window rows in one
-            # launch (csahca_compress_pair_norm_rope_rows), then the fork
-            main = torch.cuda.current_stream()
-            self.pool_new_blocks(r)
-            pooled = torch.cuda.Event()
-            pooled.record(main)
-            self.index(r)
-            self.attend(r, ["csa"])
-            self.s_hca.wait_event(pooled)
-            with torch.cuda.stream(self.s_hca):
-                self.attend(r, ["hca"])
-            main.wait_stream(self.s_hca)
-            return
         if len(self.layers) == 2 and self.s_hca is not None:
             main = torch.cuda.current_stream()
             start = torch.cuda.Event()

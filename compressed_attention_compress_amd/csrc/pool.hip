@@ -692,16 +692,20 @@ struct PairRows {
   long long x_bs_a, y_bs_a, x_bs_b, y_bs_b;
 };
 
+// A side's rows are skipped when both its pointers are NULL.
 int pair_rows_check(const char* name, const PairRows& r, int c) {
   const char* why = nullptr;
+  const bool has_a = r.x_a || r.y_a, has_b = r.x_b || r.y_b;
   if (r.T < 0) why = "T must be >= 0";
-  else if (r.T > 0 && (!r.x_a || !r.y_a || !r.x_b || !r.y_b))
-    why = "the row sources and destinations must be non-NULL";
+  else if (r.T > 0 && ((has_a && (!r.x_a || !r.y_a)) || (has_b && (!r.x_b || !r.y_b))))
+    why = "a side's row source and destination must both be set or both be NULL";
   else if (r.T > 0 && (!aligned16(r.x_a) || !aligned16(r.y_a) || !aligned16(r.x_b) || !aligned16(r.y_b)))
     why = "the row sources and destinations must be 16-byte aligned";
   else if (r.T > 0)
-    for (long long bs : {r.x_bs_a, r.y_bs_a, r.x_bs_b, r.y_bs_b})
-      if (bs < (long long)r.T * c || bs % 8) why = "row batch strides must be >= T*c and multiples of 8";
+    for (int sd = 0; sd < 2; ++sd)
+      if (sd == 0 ? has_a : has_b)
+        for (long long bs : {sd == 0 ? r.x_bs_a : r.x_bs_b, sd == 0 ? r.y_bs_a : r.y_bs_b})
+          if (bs < (long long)r.T * c || bs % 8) why = "row batch strides must be >= T*c and multiples of 8";
   if (!why) return CSAHCA_OK;
   set_error("%s: %s", name, why);
   return CSAHCA_EINVAL;
@@ -737,7 +741,7 @@ int pool_pair(const char* name, const void* kv_a, const void* gate_a, void* out_
   const bool swap = pa.block && !pb.block;  // side 1 takes pool_kernel's layout
   const PoolPlan &p1 = swap ? pb : pa, &p2 = swap ? pa : pb;
   // (with the norm, bf16 only: the float form does not fit 1024-thread workgroups)
-  if (NA > 0 && NB > 0 && !p1.block && p2.block && p2.threads == wg && (!nr || dtype == CSAHCA_BF16) &&
+  if ((NA > 0 || NB > 0) && !p1.block && p2.block && p2.threads == wg && (!nr || dtype == CSAHCA_BF16) &&
       (long long)p1.grid + p2.grid + cdiv<long long>(2LL * B * nrow_t * (c / 8), wg) <= 0x7FFFFFFFLL) {
     if (nr && raise_pair_lds_limit() != hipSuccess)
       return fail(CSAHCA_ELAUNCH, "csahca_compress_pair: cannot raise the LDS limit");
@@ -754,12 +758,13 @@ int pool_pair(const char* name, const void* kv_a, const void* gate_a, void* out_
       const PoolSide<T>& s2 = swap ? sa : sb;
       RowSide<T> ra{}, rb{};
       long long grid_rows = 0;
-      if (NR && nrow_t > 0) {
+      if (NR && nrow_t > 0) {  // a side without rows gets T = 0
+        const int ta = rows->x_a ? nrow_t : 0, tb = rows->x_b ? nrow_t : 0;
         ra = RowSide<T>{(const T*)rows->x_a, (T*)rows->y_a, rows->pos_a, rows->x_bs_a, rows->y_bs_a, gamma_a,
-                        nrow_t};
+                        ta};
         rb = RowSide<T>{(const T*)rows->x_b, (T*)rows->y_b, rows->pos_b, rows->x_bs_b, rows->y_bs_b, gamma_b,
-                        nrow_t};
-        grid_rows = cdiv<long long>(2LL * B * nrow_t * (c / 8), wg);
+                        tb};
+        grid_rows = cdiv<long long>((long long)B * (ta + tb) * (c / 8), wg);
       }
       const int g1 = (int)p1.grid, g12 = (int)(p1.grid + p2.grid);
       const dim3 grid((unsigned)(g12 + grid_rows)), blk(wg);
@@ -796,11 +801,14 @@ int pool_pair(const char* name, const void* kv_a, const void* gate_a, void* out_
     if (rc != CSAHCA_OK) return rc;
   }
   if (nr && nrow_t > 0) {  // the rows in launches of their own
-    rc = csahca_norm_rope(rows->x_a, rows->y_a, gamma_a, rows->pos_a, B, nrow_t, 1, c, 1, nr->d, nr->eps,
-                          nr->theta, 1, dtype, rows->x_bs_a, rows->y_bs_a, stream);
-    if (rc != CSAHCA_OK) return rc;
-    return csahca_norm_rope(rows->x_b, rows->y_b, gamma_b, rows->pos_b, B, nrow_t, 1, c, 1, nr->d, nr->eps,
-                            nr->theta, 1, dtype, rows->x_bs_b, rows->y_bs_b, stream);
+    if (rows->x_a) {
+      rc = csahca_norm_rope(rows->x_a, rows->y_a, gamma_a, rows->pos_a, B, nrow_t, 1, c, 1, nr->d, nr->eps,
+                            nr->theta, 1, dtype, rows->x_bs_a, rows->y_bs_a, stream);
+      if (rc != CSAHCA_OK) return rc;
+    }
+    if (rows->x_b)
+      return csahca_norm_rope(rows->x_b, rows->y_b, gamma_b, rows->pos_b, B, nrow_t, 1, c, 1, nr->d, nr->eps,
+                              nr->theta, 1, dtype, rows->x_bs_b, rows->y_bs_b, stream);
   }
   clear_error();
   return CSAHCA_OK;

@@ -369,10 +369,13 @@ int csahca_compress_pair_norm_rope(const void* kv_a, const void* gate_a, const f
  *                    theta, 1, dtype, row_x_bstride_x, row_y_bstride_x)
  * (the side's gain; row (b, t) at position row_pos_x[b] + t, or t when row_pos_x is NULL),
  * with the same bits.  T >= 0 (0: no rows, the call is csahca_compress_pair_norm_rope);
- * with T > 0 every row pointer is non-NULL and 16-byte aligned, the row strides are
- * >= T*c and multiples of 8, and no row range overlaps a pooling input or output.
- * One launch when the pooling pair is one launch; otherwise the rows follow in two
- * csahca_norm_rope launches.  Errors as in the two calls; nothing is enqueued on error.
+ * with T > 0 a side's row_x and row_y are both NULL (no rows for that side) or both
+ * non-NULL and 16-byte aligned, its row strides then >= T*c and multiples of 8, and no
+ * row range overlaps a pooling input or output.  A side may also pool nothing (n_x < m_x,
+ * its pointers NULL): one layer's pooling and window rows in one launch.
+ * One launch when the pooling is one launch (one side with few entries of many tokens,
+ * bfloat16); otherwise the rows follow in csahca_norm_rope launches.  Errors as in the
+ * two calls; nothing is enqueued on error.
  */
 int csahca_compress_pair_norm_rope_rows(
     const void* kv_a, const void* gate_a, const float* gamma_a, void* out_a, int n_a, int m_a,

@@ -173,13 +173,16 @@ def test_pair_norm_rope_equals_separate_calls(name):
                 check_pooled(got[b, :N], ref, xn, kc, d, dt)
 
 
-@pytest.mark.parametrize("name,T", [("decode_pair", 1), ("decode_pair_swapped", 3), ("ragged_strides", 2),
-                                    ("hca_side_empty", 1)])
-def test_pair_norm_rope_rows_equals_separate_calls(name, T):
-    """csahca_compress_pair_norm_rope_rows against csahca_compress_pair_norm_rope and two
-    csahca_norm_rope calls on the rows (same bits): the window rows of both sides, each
-    with its side's gain and its own positions, in the paired launch (decode shapes) and
-    after the fallback launches (one side empty); rows past T are left alone."""
+@pytest.mark.parametrize("name,T,sides", [("decode_pair", 1, "ab"), ("decode_pair_swapped", 3, "ab"),
+                                          ("ragged_strides", 2, "ab"), ("hca_side_empty", 1, "ab"),
+                                          ("decode_pair", 1, "a"), ("hca_side_empty", 2, "b"),
+                                          ("fp32_small_c", 2, "ab")])
+def test_pair_norm_rope_rows_equals_separate_calls(name, T, sides):
+    """csahca_compress_pair_norm_rope_rows against csahca_compress_pair_norm_rope and
+    csahca_norm_rope calls on the rows (same bits): the window rows of the sides named in
+    `sides` (the other side's row pointers NULL), each with its side's gain and its own
+    positions, in one launch (decode shapes, one side without entries) and after the
+    fallback launches (float32); rows past T, and a side without rows, are left alone."""
     B, c, (n_a, m_a), (n_b, m_b), dt, pad = CASES[name]
     print(f"[pool pair norm_rope rows {name} T={T}]", flush=True)
     g = torch.Generator(device="cuda").manual_seed(zlib.crc32(name.encode()) % 1000 + 2)
@@ -207,14 +210,17 @@ def test_pair_norm_rope_rows_equals_separate_calls(name, T):
     pos_b = torch.arange(B, dtype=torch.int32, device="cuda") * 7919 + n_b - T
     lib.csahca_compress_pair_norm_rope(Xa, Za, ga, sep_a, n_a, m_a, e0a, ibs_a, obs_a, Xb, Zb, gb, sep_b,
                                        n_b, m_b, e0b, ibs_b, obs_b, B, c, d, eps, theta, dt)
-    lib.csahca_norm_rope(xa_rows, ya_sep[:, 2:], ga, pos_a, B, T, 1, c, 1, d, eps, theta, 1, dt,
-                         x_bstride=ibs_a, y_bstride=LW * c)
-    lib.csahca_norm_rope(xb_rows, yb_sep[:, 2:], gb, pos_b, B, T, 1, c, 1, d, eps, theta, 1, dt,
-                         x_bstride=ibs_b, y_bstride=LW * c)
+    if "a" in sides:
+        lib.csahca_norm_rope(xa_rows, ya_sep[:, 2:], ga, pos_a, B, T, 1, c, 1, d, eps, theta, 1, dt,
+                             x_bstride=ibs_a, y_bstride=LW * c)
+    if "b" in sides:
+        lib.csahca_norm_rope(xb_rows, yb_sep[:, 2:], gb, pos_b, B, T, 1, c, 1, d, eps, theta, 1, dt,
+                             x_bstride=ibs_b, y_bstride=LW * c)
+    ra = (xa_rows, ya_pair[:, 2:]) if "a" in sides else (None, None)
+    rb = (xb_rows, yb_pair[:, 2:]) if "b" in sides else (None, None)
     lib.csahca_compress_pair_norm_rope_rows(Xa, Za, ga, pair_a, n_a, m_a, e0a, ibs_a, obs_a, Xb, Zb, gb,
                                             pair_b, n_b, m_b, e0b, ibs_b, obs_b, B, c, d, eps, theta, dt,
-                                            T, xa_rows, ya_pair[:, 2:], pos_a, ibs_a, LW * c, xb_rows,
-                                            yb_pair[:, 2:], pos_b, ibs_b, LW * c)
+                                            T, *ra, pos_a, ibs_a, LW * c, *rb, pos_b, ibs_b, LW * c)
     torch.cuda.synchronize()
     iv = torch.int16 if dt == BF16 else torch.int32
     assert torch.equal(pair_a.view(iv), sep_a.view(iv))

@@ -51,6 +51,9 @@ _SIGNATURES = {
                                   _P, _SZ, _P]),
     "lightning_index_topk_noalloc": (_I, [_P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P,
                                           _P, _P]),
+    "lightning_index_topk_csa_compress": (_I, [_P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I, _P,
+                                               _P, _P, _P, _SZ, _P, _P, _P, _I, _I, _I, _LL, _LL,
+                                               _P]),
     "lightning_index_score": (_I, [_P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _SZ,
                                    _P]),
     "lightning_index_select": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _SZ, _P]),
@@ -251,6 +254,16 @@ def lightning_index_topk(q_idx, w_idx, k_idx, idx_dtype, q_pos, m, B, Tq, n_ih, 
         _ptr(q_idx), _ptr(w_idx), _ptr(k_idx), idx_dtype, _ptr(q_pos), m, B, Tq, n_ih, c_I, N_c,
         k, _ptr(topk_idx), _ptr(topk_score), _ptr(all_scores), _ptr(workspace), ws_bytes,
         _stream(stream)))
+
+
+def lightning_index_topk_csa_compress(q_idx, w_idx, k_idx, idx_dtype, q_pos, m, B, Tq, n_ih, c_I,
+                                      N_c, k, topk_idx, topk_score, all_scores, workspace,
+                                      ws_bytes, kv, gate, out, n, c, dtype, in_bstride,
+                                      out_bstride, stream=None):
+    return _check("lightning_index_topk_csa_compress", load().lightning_index_topk_csa_compress(
+        _ptr(q_idx), _ptr(w_idx), _ptr(k_idx), idx_dtype, _ptr(q_pos), m, B, Tq, n_ih, c_I, N_c,
+        k, _ptr(topk_idx), _ptr(topk_score), _ptr(all_scores), _ptr(workspace), ws_bytes,
+        _ptr(kv), _ptr(gate), _ptr(out), n, c, dtype, in_bstride, out_bstride, _stream(stream)))
 
 
 def lightning_index_topk_noalloc(q_idx, w_idx, k_idx, idx_dtype, q_pos, m, B, Tq, n_ih, c_I, N_c,

@@ -138,10 +138,24 @@ int index_score_impl(const void* q_idx, const float* w_idx, const void* k_idx, i
                      float* scores, uint32_t* gkeys, hipStream_t st,
                      const ChunkLists* lists = nullptr);
 
+// A decode step's new CSA block(s) to pool in the selection launch (bfloat16, no bias,
+// m < 8: the one-thread-per-(sequence, entry, 8-channel slice) layout of csa_compress);
+// total = B * N * (c / 8) items, N entries per sequence.
+struct PoolBeside {
+  const uint16_t* X;
+  const uint16_t* Z;
+  uint16_t* out;
+  int N, c, m;
+  long long in_bs, out_bs, total;
+};
+
 // enqueue the selection kernel over scores and group maxima written by index_score_impl
-// (and, with lists, the chunk lists, which it tries first)
+// (and, with lists, the chunk lists, which it tries first).  With `pool` the selection
+// launch also pools those blocks when it is the list selection (*pooled set to true);
+// otherwise *pooled is false and the caller pools them itself.
 int index_select_impl(const float* scores, const uint32_t* gkeys, const int* q_pos, int m,
                       int B, int Tq, int N_c, int k, int* topk_idx, float* topk_score,
-                      hipStream_t st, const ChunkLists* lists = nullptr);
+                      hipStream_t st, const ChunkLists* lists = nullptr,
+                      const PoolBeside* pool = nullptr, bool* pooled = nullptr);
 
 }  // namespace csahca

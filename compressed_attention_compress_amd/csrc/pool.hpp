@@ -16,6 +16,12 @@ int pool_entry(const char* name, const void* kv, const void* gate, const void* k
                int n, int c, int m, int dtype, long long in_bs, long long out_bs, void* stream,
                const NormRope* nr = nullptr, long long entry0 = 0);
 
+// Host-side validation of a pooling call (csa_compress's rules; `ov`/`prev` the two-stream
+// form): *N_out receives the number of entries per sequence the call emits.
+int pool_check(const char* name, const void* kv, const void* gate, const void* kv_b,
+               const void* gate_b, bool ov, int prev, void* out, int B, int n, int c, int m,
+               int dtype, long long in_bs, long long out_bs, long long* N_out);
+
 // Pools the `count` entries first .. first+count-1 that an append of tokens n_old .. to B
 // sequences completes, in one launch: rows before n_old come from the doubled rings
 // (R rows, batch stride ring_bs), the others from the new tokens (batch stride new_bs).

@@ -21,6 +21,8 @@
 #include <mutex>
 
 #include "indexer.hpp"
+#include "pool.hpp"
+#include "pool_device.hpp"
 
 namespace {
 
@@ -254,11 +256,23 @@ CSAHCA_DEV void write_selected(const uint64_t (&kr)[KP], uint64_t T, int keff, i
 // registers, so that two workgroups share a compute unit.  LKP (0: no lists) is the number
 // of list slots a thread holds, the smallest power of two with P * JMAX <= SEL_THREADS * LKP,
 // so that no loop of the list path runs over slots that no chunk can fill.
+// Workgroups past the queries (pb.total > 0; the list selection only) pool a decode step's
+// new CSA blocks instead, with csa_compress's arithmetic (one thread per 8-channel slice of
+// an entry).
 template <int KP, int LKP>
 __global__ __launch_bounds__(SEL_THREADS, KP == KPT ? 1 : 8) void select_topk(
     const float* __restrict__ scores, const uint32_t* __restrict__ gmax,
     const int* __restrict__ q_pos, int m, int Tq, int N_c, int NG, int k,
-    int* __restrict__ topk_idx, float* __restrict__ topk_score, ChunkLists cl) {
+    int* __restrict__ topk_idx, float* __restrict__ topk_score, ChunkLists cl, int nq,
+    PoolBeside pb) {
+  if constexpr (LKP > 0) if (pb.total > 0 && (int)blockIdx.x >= nq) {
+    pool_items<uint16_t, 4, false, PLAIN, false>(pb.X, pb.Z, nullptr, nullptr, nullptr, pb.out, pb.N, pb.c,
+                                                 pb.m, 0, pb.in_bs, pb.out_bs, pb.total,
+                                                 NormRope{nullptr, 0.f, 1.f, 0, 0}, 0,
+                                                 AppendRows{nullptr, nullptr, 1, 0, 0, 0},
+                                                 (int)blockIdx.x - nq);
+    return;
+  }
   __shared__ SelScratch sc;
   __shared__ int glist[MAX_K];
   CSAHCA_TRACE(0);
@@ -789,9 +803,11 @@ namespace csahca {
 
 int index_select_impl(const float* scores, const uint32_t* gmax, const int* q_pos, int m, int B,
                       int Tq, int N_c, int k, int* topk_idx, float* topk_score, hipStream_t st,
-                      const ChunkLists* lists) {
+                      const ChunkLists* lists, const PoolBeside* pool, bool* pooled) {
   using namespace csahca;
   const int nq = B * Tq;
+  if (pooled) *pooled = false;
+  const PoolBeside no_pool{nullptr, nullptr, nullptr, 0, 8, 4, 0, 0, 0};
   const int NG = cdiv(N_c, GROUP);
   if (!lists && k <= WS_MAX_K && NG <= 64 * WS_MAX_NGPL) {
     const unsigned grid = (unsigned)cdiv(nq, WS_WAVES);
@@ -804,10 +820,10 @@ int index_select_impl(const float* scores, const uint32_t* gmax, const int* q_po
   // (the 8-key kernel gathers k <= 512 candidate groups and holds at most 8192 maxima)
   if (!lists && k <= NWAVE * 8 * 64 / GROUP && NG <= SEL_THREADS * 8)
     hipLaunchKernelGGL((select_topk<8, 0>), dim3((unsigned)nq), dim3(SEL_THREADS), 0, st, scores, gmax,
-                       q_pos, m, Tq, N_c, NG, k, topk_idx, topk_score, ChunkLists{});
+                       q_pos, m, Tq, N_c, NG, k, topk_idx, topk_score, ChunkLists{}, nq, no_pool);
   else if (!lists)
     hipLaunchKernelGGL((select_topk<KPT, 0>), dim3((unsigned)nq), dim3(SEL_THREADS), 0, st, scores, gmax,
-                       q_pos, m, Tq, N_c, NG, k, topk_idx, topk_score, ChunkLists{});
+                       q_pos, m, Tq, N_c, NG, k, topk_idx, topk_score, ChunkLists{}, nq, no_pool);
   else {
     // list slots per thread: the smallest power of two that holds every chunk's list
     const long long slots = (long long)lists->P * lists->JMAX;
@@ -815,8 +831,11 @@ int index_select_impl(const float* scores, const uint32_t* gmax, const int* q_po
               : slots <= SEL_THREADS * 4 ? select_topk<KPT, 4>
               : slots <= SEL_THREADS * 8 ? select_topk<KPT, 8>
                                           : select_topk<KPT, KPT>;
-    hipLaunchKernelGGL(kern, dim3((unsigned)nq), dim3(SEL_THREADS), 0, st, scores, gmax, q_pos, m, Tq, N_c,
-                       NG, k, topk_idx, topk_score, *lists);
+    const bool with_pool = pool && pool->total > 0;
+    const long long gpool = with_pool ? cdiv<long long>(pool->total, SEL_THREADS) : 0;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(nq + gpool)), dim3(SEL_THREADS), 0, st, scores, gmax, q_pos, m, Tq,
+                       N_c, NG, k, topk_idx, topk_score, *lists, nq, with_pool ? *pool : no_pool);
+    if (pooled) *pooled = with_pool;
   }
   return launch_status("lightning_index_select");
 }
@@ -852,10 +871,19 @@ namespace {
 
 // lightning_index_topk on a given workspace (the caller's, or the allocation-free variant's
 // file-scope scratch); argument checks included
+// The pooling of a decode step's new CSA block(s) enqueued with the indexer call
+// (lightning_index_topk_csa_compress): csa_compress's arguments without the bias.
+struct PoolReq {
+  const void *kv, *gate;
+  void* out;
+  int n, c, dtype;
+  long long in_bs, out_bs;
+};
+
 int index_topk_impl(const char* name, const void* q_idx, const float* w_idx, const void* k_idx,
                     int idx_dtype, const int* q_pos, int m, int B, int Tq, int n_ih, int c_I,
                     int N_c, int k, int* topk_idx, float* topk_score, float* all_scores,
-                    void* workspace, size_t ws_bytes, hipStream_t s) {
+                    void* workspace, size_t ws_bytes, hipStream_t s, const PoolReq* pr = nullptr) {
   using namespace csahca;
   int st = index_check_common(q_idx, w_idx, k_idx, idx_dtype, q_pos, m, B, Tq, n_ih, c_I, N_c, k);
   if (st != CSAHCA_OK) return st;
@@ -872,6 +900,21 @@ int index_topk_impl(const char* name, const void* q_idx, const float* w_idx, con
     set_error("%s: all_scores must be 16-byte aligned", name);
     return CSAHCA_EINVAL;
   }
+  // the pooling's arguments, all checked before anything is enqueued
+  long long NP = 0;
+  if (pr) {
+    st = pool_check(name, pr->kv, pr->gate, nullptr, nullptr, false, 0, pr->out, B, pr->n, pr->c, m,
+                    pr->dtype, pr->in_bs, pr->out_bs, &NP);
+    if (st != CSAHCA_OK) return st;
+  }
+  // in the selection launch when it is the list selection (bfloat16, m < 8: csa_compress's
+  // one-thread-per-slice layout with 4 tokens per load round), else its own launch after
+  const bool beside = pr && NP > 0 && pr->dtype == CSAHCA_BF16 && m < 8 && pr->c % 8 == 0 &&
+                      (long long)B * NP * (pr->c / 8) <= 0x7FFFFFFFLL;
+  const PoolBeside pb{(const uint16_t*)(pr ? pr->kv : nullptr), (const uint16_t*)(pr ? pr->gate : nullptr),
+                      (uint16_t*)(pr ? pr->out : nullptr), (int)NP, pr ? pr->c : 8, m, pr ? pr->in_bs : 0,
+                      pr ? pr->out_bs : 0, beside ? (long long)B * NP * (pr->c / 8) : 0};
+  bool pooled = false;
   char* ws = (char*)workspace;
   float* scores = all_scores ? all_scores : (float*)(ws + L.scores_off);
   uint32_t* gkeys = (uint32_t*)(ws + L.gkeys_off);
@@ -882,11 +925,16 @@ int index_topk_impl(const char* name, const void* q_idx, const float* w_idx, con
     st = index_score_impl(q_idx, w_idx, k_idx, idx_dtype, q_pos, m, B, Tq, n_ih, c_I, N_c, scores, gkeys,
                           s, &cl);
     if (st != CSAHCA_OK) return st;
-    return index_select_impl(scores, gkeys, q_pos, m, B, Tq, N_c, k, topk_idx, topk_score, s, &cl);
+    st = index_select_impl(scores, gkeys, q_pos, m, B, Tq, N_c, k, topk_idx, topk_score, s, &cl,
+                           beside ? &pb : nullptr, &pooled);
+  } else {
+    st = index_score_impl(q_idx, w_idx, k_idx, idx_dtype, q_pos, m, B, Tq, n_ih, c_I, N_c, scores, gkeys, s);
+    if (st != CSAHCA_OK) return st;
+    st = index_select_impl(scores, gkeys, q_pos, m, B, Tq, N_c, k, topk_idx, topk_score, s);
   }
-  st = index_score_impl(q_idx, w_idx, k_idx, idx_dtype, q_pos, m, B, Tq, n_ih, c_I, N_c, scores, gkeys, s);
-  if (st != CSAHCA_OK) return st;
-  return index_select_impl(scores, gkeys, q_pos, m, B, Tq, N_c, k, topk_idx, topk_score, s);
+  if (st != CSAHCA_OK || !pr || pooled || NP == 0) return st;
+  return pool_entry(name, pr->kv, pr->gate, nullptr, nullptr, false, 0, nullptr, pr->out, B, pr->n, pr->c, m,
+                    pr->dtype, pr->in_bs, pr->out_bs, s);
 }
 
 }  // namespace
@@ -899,6 +947,17 @@ extern "C" int lightning_index_topk(const void* q_idx, const float* w_idx, const
   return index_topk_impl("lightning_index_topk", q_idx, w_idx, k_idx, idx_dtype, q_pos, m, B, Tq,
                          n_ih, c_I, N_c, k, topk_idx, topk_score, all_scores, workspace, ws_bytes,
                          (hipStream_t)stream);
+}
+
+extern "C" int lightning_index_topk_csa_compress(
+    const void* q_idx, const float* w_idx, const void* k_idx, int idx_dtype, const int* q_pos, int m, int B,
+    int Tq, int n_ih, int c_I, int N_c, int k, int* topk_idx, float* topk_score, float* all_scores,
+    void* workspace, size_t ws_bytes, const void* kv, const void* gate, void* out, int n, int c, int dtype,
+    long long in_bstride, long long out_bstride, void* stream) {
+  const PoolReq pr{kv, gate, out, n, c, dtype, in_bstride, out_bstride};
+  return index_topk_impl("lightning_index_topk_csa_compress", q_idx, w_idx, k_idx, idx_dtype, q_pos, m, B,
+                         Tq, n_ih, c_I, N_c, k, topk_idx, topk_score, all_scores, workspace, ws_bytes,
+                         (hipStream_t)stream, &pr);
 }
 
 // ---------------------------------------------------------------------------------------

@@ -420,6 +420,27 @@ int hca_attend_ex(const void* q, const void* ckv, const void* win_kv, const int*
                   size_t ws_bytes, void* stream);
 
 /*
+ * lightning_index_topk_csa_compress -- lightning_index_topk, and with it
+ *   csa_compress(kv, gate, NULL, out, B, n, c, m, dtype, in_bstride, out_bstride)
+ * on the same stream: a decode step's new CSA block pooled while the indexer selects (the
+ * indexer reads no pooled entry, so the two are independent).
+ * Source: as lightning_index_topk and csa_compress.
+ * Arguments: those of lightning_index_topk, then csa_compress's pooling arguments without
+ * the bias (the block size is the indexer's m).  Every argument rule of both calls
+ * applies, and all are checked before anything is enqueued; the results are those of the
+ * two calls, bit for bit.  With bfloat16 entries, m < 8 and a decode selection from chunk
+ * lists, the pooling runs in extra workgroups of the selection launch; otherwise its own
+ * launch follows the indexer's.
+ */
+int lightning_index_topk_csa_compress(const void* q_idx, const float* w_idx, const void* k_idx,
+                                      int idx_dtype, const int* q_pos, int m, int B, int Tq,
+                                      int n_ih, int c_I, int N_c, int k, int* topk_idx,
+                                      float* topk_score, float* all_scores, void* workspace,
+                                      size_t ws_bytes, const void* kv, const void* gate, void* out,
+                                      int n, int c, int dtype, long long in_bstride,
+                                      long long out_bstride, void* stream);
+
+/*
  * csa_attend_begin / csa_attend_end, hca_attend_begin / hca_attend_end -- the two halves
  * of csa_attend_ex / hca_attend_ex, for a caller that runs the split merge on another
  * stream than the attention (a decode step that joins its two attention layers on one

@@ -169,6 +169,22 @@ def test_indexer_validation():
     assert L.lightning_index_topk(*bad, FAKE, ws, None) == ENOTSUP
     assert L.lightning_index_select(None, FAKE, 4, B, Tq, N_c, k, FAKE, None, FAKE, ws, None) == EINVAL
     assert L.lightning_index_score(*args[:12], None, FAKE, ws, None) == EINVAL
+    # the indexer with the CSA block pooled beside it: both calls' rules, checked up front
+    pool = [FAKE, FAKE, FAKE, 4 * N_c, 512, 1, 0, 0]
+    fused = L.lightning_index_topk_csa_compress
+    assert fused(*args, FAKE, ws - 1, *pool, None) == EWORKSPACE
+    bad = list(pool)
+    bad[0] = None  # kv
+    assert fused(*args, FAKE, ws, *bad, None) == EINVAL
+    bad = list(pool)
+    bad[4] = 7  # c not a multiple of 8
+    assert fused(*args, FAKE, ws, *bad, None) == EINVAL
+    bad = list(pool)
+    bad[3] = -1  # n
+    assert fused(*args, FAKE, ws, *bad, None) == EINVAL
+    bad = list(pool)
+    bad[5] = 9  # dtype
+    assert fused(*args, FAKE, ws, *bad, None) == ENOTSUP
 
 
 def test_attend_validation():

@@ -247,12 +247,26 @@ class Workload:
         self.lib.lightning_index_select(self.scores, self.q_pos, cfg.m, cfg.B, self.Tq, self.N_c,
                                         cfg.k, self.idx, None, self.iws, self.iws_b)
 
-    def index(self, r, split=False):
+    def index(self, r, split=False, pool_csa=False):
+        """The indexer; with pool_csa (norm and rotation) the CSA cache's new blocks and the
+        layer's new window rows are pooled and normalised in the same call (in the
+        selection launch's spare workgroups at decode)."""
         cfg, lib, rp = self.cfg, self.lib, self.rep[r]
         B = cfg.B
         if split:
             self.index_score(r)
             self.select(r)
+        elif pool_csa:
+            m, n, c, Tq, L = cfg.m, self.n, cfg.c, self.Tq, self.nr_L
+            first_blk = self.n_old // m
+            tok0 = first_blk * m
+            X, Z, C = self.prob["X_csa"], self.prob["Z_csa"], rp["C_csa"]
+            lib.lightning_index_topk_csa_compress_norm_rope_rows(
+                rp["qI"], rp["w"], rp["KI"], cfg.idx_dtype, self.q_pos, m, B, Tq, cfg.n_ih, cfg.c_I, self.N_c,
+                cfg.k, self.idx, None, self.scores, self.iws, self.iws_b, X[:, tok0:], Z[:, tok0:], self.g_kv,
+                C[:, first_blk:], n - tok0, c, first_blk, self.NR_D, self.NR_EPS, self.NR_THETA, cfg.dtype, n * c,
+                (n // m) * c, Tq, X[:, n - Tq:], self.nr_win["csa"][:, L - Tq:], self.nr_new_pos, n * c, L * c)
+            self.rows_pooled = True
         else:
             lib.lightning_index_topk(rp["qI"], rp["w"], rp["KI"], cfg.idx_dtype, self.q_pos, cfg.m,
                                      B, self.Tq, cfg.n_ih, cfg.c_I, self.N_c, cfg.k, self.idx, None,
@@ -314,7 +328,7 @@ class Workload:
         carries the pooling of both caches and the HCA attention, while the first stream
         scores and selects; the CSA attention then waits for the CSA pooling, which
         finished long before.  (With norm and rotation each layer's pooling comes with its
-        new window row, and the CSA one stays on the first stream, before the scoring.)
+        new window row, and the CSA one runs in the selection launch's spare workgroups.)
         The second stream forks at the start of the step and joins at its end.
         Edges between the graph's hardware queues resolve late when the producer is still
         running as the waiting queue reaches them (the waiting node started up to tens of
@@ -327,10 +341,6 @@ class Workload:
             start = torch.cuda.Event()
             start.record(main)
             csa_pooled = torch.cuda.Event()
-            if self.nr:
-                # with norm and rotation the CSA pooling (with its window row) stays on the
-                # first stream, before the scoring (measured 84.5 against 85.3-86.0 us)
-                self.pool_new_blocks(r, ["csa"])
             self.s_hca.wait_event(start)
             with torch.cuda.stream(self.s_hca):
                 if not self.nr:
@@ -338,7 +348,8 @@ class Workload:
                     csa_pooled.record(self.s_hca)
                 self.pool_new_blocks(r, ["hca"])
                 self.attend(r, ["hca"])
-            self.index(r)
+            # with norm and rotation the indexer call pools the CSA block and its window row
+            self.index(r, pool_csa=self.nr)
             if not self.nr:
                 main.wait_event(csa_pooled)
             self.attend(r, ["csa"])

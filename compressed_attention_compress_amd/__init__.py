@@ -54,6 +54,10 @@ _SIGNATURES = {
     "lightning_index_topk_csa_compress": (_I, [_P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I, _P,
                                                _P, _P, _P, _SZ, _P, _P, _P, _I, _I, _I, _LL, _LL,
                                                _P]),
+    "lightning_index_topk_csa_compress_norm_rope_rows": (_I, [_P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I,
+                                                           _P, _P, _P, _P, _SZ, _P, _P, _P, _P, _I, _I,
+                                                           _LL, _I, _F, _F, _I, _LL, _LL, _I, _P, _P, _P,
+                                                           _LL, _LL, _P]),
     "lightning_index_score": (_I, [_P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _SZ,
                                    _P]),
     "lightning_index_select": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _SZ, _P]),
@@ -264,6 +268,19 @@ def lightning_index_topk_csa_compress(q_idx, w_idx, k_idx, idx_dtype, q_pos, m, 
         _ptr(q_idx), _ptr(w_idx), _ptr(k_idx), idx_dtype, _ptr(q_pos), m, B, Tq, n_ih, c_I, N_c,
         k, _ptr(topk_idx), _ptr(topk_score), _ptr(all_scores), _ptr(workspace), ws_bytes,
         _ptr(kv), _ptr(gate), _ptr(out), n, c, dtype, in_bstride, out_bstride, _stream(stream)))
+
+
+def lightning_index_topk_csa_compress_norm_rope_rows(
+        q_idx, w_idx, k_idx, idx_dtype, q_pos, m, B, Tq, n_ih, c_I, N_c, k, topk_idx, topk_score,
+        all_scores, workspace, ws_bytes, kv, gate, gamma, out, n, c, entry0, d_rope, eps, theta, dtype,
+        in_bstride, out_bstride, T, row_x, row_y, row_pos, row_x_bstride, row_y_bstride, stream=None):
+    return _check("lightning_index_topk_csa_compress_norm_rope_rows",
+                  load().lightning_index_topk_csa_compress_norm_rope_rows(
+                      _ptr(q_idx), _ptr(w_idx), _ptr(k_idx), idx_dtype, _ptr(q_pos), m, B, Tq, n_ih, c_I,
+                      N_c, k, _ptr(topk_idx), _ptr(topk_score), _ptr(all_scores), _ptr(workspace),
+                      ws_bytes, _ptr(kv), _ptr(gate), _ptr(gamma), _ptr(out), n, c, entry0, d_rope,
+                      float(eps), float(theta), dtype, in_bstride, out_bstride, T, _ptr(row_x),
+                      _ptr(row_y), _ptr(row_pos), row_x_bstride, row_y_bstride, _stream(stream)))
 
 
 def lightning_index_topk_noalloc(q_idx, w_idx, k_idx, idx_dtype, q_pos, m, B, Tq, n_ih, c_I, N_c,

@@ -5,6 +5,7 @@
 #pragma once
 
 #include "common.hpp"
+#include "normrope.hpp"
 
 namespace csahca {
 
@@ -140,13 +141,27 @@ int index_score_impl(const void* q_idx, const float* w_idx, const void* k_idx, i
 
 // A decode step's new CSA block(s) to pool in the selection launch (bfloat16, no bias,
 // m < 8: the one-thread-per-(sequence, entry, 8-channel slice) layout of csa_compress);
-// total = B * N * (c / 8) items, N entries per sequence.
+// total = B * N * (c / 8) items, N entries per sequence, in the first pool_wgs extra
+// workgroups.  With norm, every entry is then normalised and rotated (nr, the first one
+// being entry entry0 of the cache), and the workgroups after those normalise rT window
+// rows per sequence (row (b, t) at rx + b * rx_bs + t * c, position rpos[b] + t, written
+// to ry likewise; nr's gain), one row per c / 8 consecutive lanes: rows = B * rT.
 struct PoolBeside {
   const uint16_t* X;
   const uint16_t* Z;
   uint16_t* out;
   int N, c, m;
   long long in_bs, out_bs, total;
+  int norm;
+  NormRope nr;
+  long long entry0;
+  int pool_wgs;
+  const uint16_t* rx;
+  uint16_t* ry;
+  const int* rpos;
+  long long rx_bs, ry_bs;
+  int rT;
+  long long rows;
 };
 
 // enqueue the selection kernel over scores and group maxima written by index_score_impl

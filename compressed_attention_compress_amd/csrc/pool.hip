@@ -500,17 +500,6 @@ int pool_entry(const char* name, const void* kv, const void* gate, const void* k
 // launch when one takes pool_kernel's layout and the other pool_block_kernel's at the
 // same workgroup size; otherwise one launch each.  The entries are the same bits either
 // way.
-// Window rows normalised beside a paired pooling with the norm (csahca_norm_rope's
-// arguments for one side, H = 1, pstride 1): none when T == 0.
-struct PairRows {
-  int T;
-  const void *x_a, *x_b;
-  void *y_a, *y_b;
-  const int *pos_a, *pos_b;
-  long long x_bs_a, y_bs_a, x_bs_b, y_bs_b;
-};
-
-// A side's rows are skipped when both its pointers are NULL.
 int pair_rows_check(const char* name, const PairRows& r, int c) {
   const char* why = nullptr;
   const bool has_a = r.x_a || r.y_a, has_b = r.x_b || r.y_b;
@@ -533,7 +522,7 @@ int pool_pair(const char* name, const void* kv_a, const void* gate_a, void* out_
               long long in_bs_a, long long out_bs_a, const void* kv_b, const void* gate_b, void* out_b,
               int n_b, int m_b, long long in_bs_b, long long out_bs_b, int B, int c, int dtype,
               const NormRope* nr, const float* gamma_a, long long entry0_a, const float* gamma_b,
-              long long entry0_b, void* stream, const PairRows* rows = nullptr) {
+              long long entry0_b, void* stream, const PairRows* rows) {
   long long NA = 0, NB = 0;
   int rc = pool_check(name, kv_a, gate_a, nullptr, nullptr, false, 0, out_a, B, n_a, c, m_a, dtype,
                       in_bs_a, out_bs_a, &NA);

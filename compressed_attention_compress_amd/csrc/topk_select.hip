@@ -256,21 +256,40 @@ CSAHCA_DEV void write_selected(const uint64_t (&kr)[KP], uint64_t T, int keff, i
 // registers, so that two workgroups share a compute unit.  LKP (0: no lists) is the number
 // of list slots a thread holds, the smallest power of two with P * JMAX <= SEL_THREADS * LKP,
 // so that no loop of the list path runs over slots that no chunk can fill.
-// Workgroups past the queries (pb.total > 0; the list selection only) pool a decode step's
-// new CSA blocks instead, with csa_compress's arithmetic (one thread per 8-channel slice of
-// an entry).
+// Workgroups past the queries (the list selection only) pool a decode step's new CSA
+// blocks instead, with csa_compress's arithmetic (one thread per 8-channel slice of an
+// entry; with pb.norm, csahca_compress_norm_rope's), then normalise the step's window rows
+// as csahca_norm_rope does.
 template <int KP, int LKP>
 __global__ __launch_bounds__(SEL_THREADS, KP == KPT ? 1 : 8) void select_topk(
     const float* __restrict__ scores, const uint32_t* __restrict__ gmax,
     const int* __restrict__ q_pos, int m, int Tq, int N_c, int NG, int k,
     int* __restrict__ topk_idx, float* __restrict__ topk_score, ChunkLists cl, int nq,
     PoolBeside pb) {
-  if constexpr (LKP > 0) if (pb.total > 0 && (int)blockIdx.x >= nq) {
-    pool_items<uint16_t, 4, false, PLAIN, false>(pb.X, pb.Z, nullptr, nullptr, nullptr, pb.out, pb.N, pb.c,
-                                                 pb.m, 0, pb.in_bs, pb.out_bs, pb.total,
-                                                 NormRope{nullptr, 0.f, 1.f, 0, 0}, 0,
-                                                 AppendRows{nullptr, nullptr, 1, 0, 0, 0},
-                                                 (int)blockIdx.x - nq);
+  if constexpr (LKP > 0) if ((int)blockIdx.x >= nq) {
+    const int w = (int)blockIdx.x - nq;
+    const AppendRows ap0{nullptr, nullptr, 1, 0, 0, 0};
+    if (w < pb.pool_wgs) {
+      if (pb.norm)
+        pool_items<uint16_t, 4, false, PLAIN, true>(pb.X, pb.Z, nullptr, nullptr, nullptr, pb.out, pb.N, pb.c,
+                                                    pb.m, 0, pb.in_bs, pb.out_bs, pb.total, pb.nr, pb.entry0,
+                                                    ap0, w);
+      else
+        pool_items<uint16_t, 4, false, PLAIN, false>(pb.X, pb.Z, nullptr, nullptr, nullptr, pb.out, pb.N,
+                                                     pb.c, pb.m, 0, pb.in_bs, pb.out_bs, pb.total,
+                                                     NormRope{nullptr, 0.f, 1.f, 0, 0}, 0, ap0, w);
+      return;
+    }
+    const int CV = pb.c / VEC;
+    const long long item = (long long)(w - pb.pool_wgs) * blockDim.x + threadIdx.x;
+    const long long row = item / CV;
+    if (row >= pb.rows) return;  // whole rows leave together (CV divides 64)
+    const int cv = (int)(item - row * CV);
+    const int b = (int)(row / pb.rT), t = (int)(row - (long long)b * pb.rT);
+    const long long p = (pb.rpos ? (long long)pb.rpos[b] : 0LL) + t;
+    const NormRope nx{pb.nr.gamma, pb.nr.eps, pb.nr.theta, pb.nr.d, 1};
+    norm_rope_row8<uint16_t>(pb.rx + b * pb.rx_bs + (long long)t * pb.c, pb.ry + b * pb.ry_bs + (long long)t * pb.c,
+                             nx, p, cv, CV, pb.c);
     return;
   }
   __shared__ SelScratch sc;
@@ -807,7 +826,8 @@ int index_select_impl(const float* scores, const uint32_t* gmax, const int* q_po
   using namespace csahca;
   const int nq = B * Tq;
   if (pooled) *pooled = false;
-  const PoolBeside no_pool{nullptr, nullptr, nullptr, 0, 8, 4, 0, 0, 0};
+  const PoolBeside no_pool{nullptr, nullptr, nullptr, 0, 8, 4, 0, 0, 0, 0, NormRope{nullptr, 0.f, 1.f, 0, 0},
+                           0, 0, nullptr, nullptr, nullptr, 0, 0, 1, 0};
   const int NG = cdiv(N_c, GROUP);
   if (!lists && k <= WS_MAX_K && NG <= 64 * WS_MAX_NGPL) {
     const unsigned grid = (unsigned)cdiv(nq, WS_WAVES);
@@ -831,8 +851,9 @@ int index_select_impl(const float* scores, const uint32_t* gmax, const int* q_po
               : slots <= SEL_THREADS * 4 ? select_topk<KPT, 4>
               : slots <= SEL_THREADS * 8 ? select_topk<KPT, 8>
                                           : select_topk<KPT, KPT>;
-    const bool with_pool = pool && pool->total > 0;
-    const long long gpool = with_pool ? cdiv<long long>(pool->total, SEL_THREADS) : 0;
+    const bool with_pool = pool && (pool->total > 0 || pool->rows > 0);
+    const long long gpool = with_pool ? pool->pool_wgs + cdiv<long long>(pool->rows * (pool->c / VEC), SEL_THREADS)
+                                      : 0;
     hipLaunchKernelGGL(kern, dim3((unsigned)(nq + gpool)), dim3(SEL_THREADS), 0, st, scores, gmax, q_pos, m, Tq,
                        N_c, NG, k, topk_idx, topk_score, *lists, nq, with_pool ? *pool : no_pool);
     if (pooled) *pooled = with_pool;
@@ -872,12 +893,17 @@ namespace {
 // lightning_index_topk on a given workspace (the caller's, or the allocation-free variant's
 // file-scope scratch); argument checks included
 // The pooling of a decode step's new CSA block(s) enqueued with the indexer call
-// (lightning_index_topk_csa_compress): csa_compress's arguments without the bias.
+// (lightning_index_topk_csa_compress): csa_compress's arguments without the bias; with nr
+// (lightning_index_topk_csa_compress_norm_rope_rows) csahca_compress_norm_rope's, and the
+// step's window rows of csahca_compress_pair_norm_rope_rows's side a.
 struct PoolReq {
   const void *kv, *gate;
   void* out;
   int n, c, dtype;
   long long in_bs, out_bs;
+  const NormRope* nr;
+  long long entry0;
+  const PairRows* rows;
 };
 
 int index_topk_impl(const char* name, const void* q_idx, const float* w_idx, const void* k_idx,
@@ -902,18 +928,40 @@ int index_topk_impl(const char* name, const void* q_idx, const float* w_idx, con
   }
   // the pooling's arguments, all checked before anything is enqueued
   long long NP = 0;
+  const bool norm = pr && pr->nr;
+  const int row_t = norm && pr->rows && pr->rows->x_a ? pr->rows->T : 0;  // window rows per sequence
   if (pr) {
     st = pool_check(name, pr->kv, pr->gate, nullptr, nullptr, false, 0, pr->out, B, pr->n, pr->c, m,
                     pr->dtype, pr->in_bs, pr->out_bs, &NP);
     if (st != CSAHCA_OK) return st;
+    if (norm && (!norm_rope_args_ok(pr->c, pr->nr->d, pr->nr->eps, pr->nr->theta) || pr->entry0 < 0 ||
+                 !aligned16(pr->nr->gamma))) {
+      set_error("%s: the norm needs c / 8 a power of two <= 64, d_rope %% 8 == 0 and <= c, "
+                "eps >= 0, theta > 0, entry0 >= 0 and gamma 16-byte aligned", name);
+      return CSAHCA_EINVAL;
+    }
+    if (norm && pr->rows) {
+      st = pair_rows_check(name, *pr->rows, pr->c);
+      if (st != CSAHCA_OK) return st;
+    }
   }
   // in the selection launch when it is the list selection (bfloat16, m < 8: csa_compress's
   // one-thread-per-slice layout with 4 tokens per load round), else its own launch after
-  const bool beside = pr && NP > 0 && pr->dtype == CSAHCA_BF16 && m < 8 && pr->c % 8 == 0 &&
-                      (long long)B * NP * (pr->c / 8) <= 0x7FFFFFFFLL;
-  const PoolBeside pb{(const uint16_t*)(pr ? pr->kv : nullptr), (const uint16_t*)(pr ? pr->gate : nullptr),
-                      (uint16_t*)(pr ? pr->out : nullptr), (int)NP, pr ? pr->c : 8, m, pr ? pr->in_bs : 0,
-                      pr ? pr->out_bs : 0, beside ? (long long)B * NP * (pr->c / 8) : 0};
+  const bool beside = pr && (NP > 0 || row_t > 0) && pr->dtype == CSAHCA_BF16 && m < 8 && pr->c % 8 == 0 &&
+                      (long long)B * NP * (pr->c / 8) <= 0x7FFFFFFFLL &&
+                      (long long)B * row_t * (pr->c / 8) <= 0x7FFFFFFFLL;
+  PoolBeside pb{};
+  if (beside) {
+    const PairRows* r = pr->rows;
+    pb = PoolBeside{(const uint16_t*)pr->kv, (const uint16_t*)pr->gate, (uint16_t*)pr->out, (int)NP, pr->c, m,
+                    pr->in_bs, pr->out_bs, (long long)B * NP * (pr->c / 8), norm ? 1 : 0,
+                    norm ? *pr->nr : NormRope{nullptr, 0.f, 1.f, 0, 0}, pr->entry0,
+                    (int)cdiv<long long>((long long)B * NP * (pr->c / 8), SEL_THREADS),
+                    row_t ? (const uint16_t*)r->x_a : nullptr, row_t ? (uint16_t*)r->y_a : nullptr,
+                    row_t ? r->pos_a : nullptr, row_t ? r->x_bs_a : 0, row_t ? r->y_bs_a : 0, row_t ? row_t : 1,
+                    (long long)B * row_t};
+    if (norm) pb.nr.norm = 1;
+  }
   bool pooled = false;
   char* ws = (char*)workspace;
   float* scores = all_scores ? all_scores : (float*)(ws + L.scores_off);
@@ -932,7 +980,12 @@ int index_topk_impl(const char* name, const void* q_idx, const float* w_idx, con
     if (st != CSAHCA_OK) return st;
     st = index_select_impl(scores, gkeys, q_pos, m, B, Tq, N_c, k, topk_idx, topk_score, s);
   }
-  if (st != CSAHCA_OK || !pr || pooled || NP == 0) return st;
+  if (st != CSAHCA_OK || !pr || pooled) return st;
+  if (norm)  // the one-layer form of the paired pooling (side b empty)
+    return pool_pair(name, pr->kv, pr->gate, pr->out, pr->n, m, pr->in_bs, pr->out_bs, nullptr, nullptr, nullptr,
+                     0, m, pr->c, pr->c, B, pr->c, pr->dtype, pr->nr, pr->nr->gamma, pr->entry0, nullptr, 0, s,
+                     pr->rows);
+  if (NP == 0) return st;
   return pool_entry(name, pr->kv, pr->gate, nullptr, nullptr, false, 0, nullptr, pr->out, B, pr->n, pr->c, m,
                     pr->dtype, pr->in_bs, pr->out_bs, s);
 }
@@ -954,10 +1007,25 @@ extern "C" int lightning_index_topk_csa_compress(
     int Tq, int n_ih, int c_I, int N_c, int k, int* topk_idx, float* topk_score, float* all_scores,
     void* workspace, size_t ws_bytes, const void* kv, const void* gate, void* out, int n, int c, int dtype,
     long long in_bstride, long long out_bstride, void* stream) {
-  const PoolReq pr{kv, gate, out, n, c, dtype, in_bstride, out_bstride};
+  const PoolReq pr{kv, gate, out, n, c, dtype, in_bstride, out_bstride, nullptr, 0, nullptr};
   return index_topk_impl("lightning_index_topk_csa_compress", q_idx, w_idx, k_idx, idx_dtype, q_pos, m, B,
                          Tq, n_ih, c_I, N_c, k, topk_idx, topk_score, all_scores, workspace, ws_bytes,
                          (hipStream_t)stream, &pr);
+}
+
+extern "C" int lightning_index_topk_csa_compress_norm_rope_rows(
+    const void* q_idx, const float* w_idx, const void* k_idx, int idx_dtype, const int* q_pos, int m, int B,
+    int Tq, int n_ih, int c_I, int N_c, int k, int* topk_idx, float* topk_score, float* all_scores,
+    void* workspace, size_t ws_bytes, const void* kv, const void* gate, const float* gamma, void* out, int n,
+    int c, long long entry0, int d_rope, float eps, float theta, int dtype, long long in_bstride,
+    long long out_bstride, int T, const void* row_x, void* row_y, const int* row_pos, long long row_x_bstride,
+    long long row_y_bstride, void* stream) {
+  const NormRope nr{gamma, eps, theta, d_rope, 1};
+  const PairRows rows{T, row_x, nullptr, row_y, nullptr, row_pos, nullptr, row_x_bstride, row_y_bstride, c, c};
+  const PoolReq pr{kv, gate, out, n, c, dtype, in_bstride, out_bstride, &nr, entry0, &rows};
+  return index_topk_impl("lightning_index_topk_csa_compress_norm_rope_rows", q_idx, w_idx, k_idx, idx_dtype,
+                         q_pos, m, B, Tq, n_ih, c_I, N_c, k, topk_idx, topk_score, all_scores, workspace,
+                         ws_bytes, (hipStream_t)stream, &pr);
 }
 
 // ---------------------------------------------------------------------------------------

@@ -441,6 +441,31 @@ int lightning_index_topk_csa_compress(const void* q_idx, const float* w_idx, con
                                       long long out_bstride, void* stream);
 
 /*
+ * lightning_index_topk_csa_compress_norm_rope_rows -- lightning_index_topk, and with it
+ *   csahca_compress_pair_norm_rope_rows with side a only: the CSA cache's new entries pooled,
+ *   normalised and rotated (csahca_compress_norm_rope(kv, gate, NULL, gamma, out, B, n, c, m,
+ *   entry0, d_rope, eps, theta, dtype, in_bstride, out_bstride)), and the step's T new window
+ *   rows normalised and rotated (csahca_norm_rope(row_x, row_y, gamma, row_pos, B, T, 1, c, 1,
+ *   d_rope, eps, theta, 1, dtype, row_x_bstride, row_y_bstride)); none of the three reads
+ *   another's output.
+ * Source: as lightning_index_topk, csa_compress and csahca_compress_norm_rope.
+ * Arguments: those of lightning_index_topk, then those of the pooling and the rows (the
+ * block size is the indexer's m; row_x and row_y both NULL, or T == 0, for no rows).
+ * Every argument rule of the calls applies, all checked before anything is enqueued; the
+ * results are those of the calls, bit for bit.  With bfloat16 entries, m < 8 and a
+ * decode selection from chunk lists, the pooling and the rows run in extra workgroups of
+ * the selection launch; otherwise in launches of their own after the indexer's.
+ */
+int lightning_index_topk_csa_compress_norm_rope_rows(
+    const void* q_idx, const float* w_idx, const void* k_idx, int idx_dtype, const int* q_pos, int m,
+    int B, int Tq, int n_ih, int c_I, int N_c, int k, int* topk_idx, float* topk_score,
+    float* all_scores, void* workspace, size_t ws_bytes, const void* kv, const void* gate,
+    const float* gamma, void* out, int n, int c, long long entry0, int d_rope, float eps,
+    float theta, int dtype, long long in_bstride, long long out_bstride, int T,
+    const void* row_x, void* row_y, const int* row_pos, long long row_x_bstride,
+    long long row_y_bstride, void* stream);
+
+/*
  * csa_attend_begin / csa_attend_end, hca_attend_begin / hca_attend_end -- the two halves
  * of csa_attend_ex / hca_attend_ex, for a caller that runs the split merge on another
  * stream than the attention (a decode step that joins its two attention layers on one

@@ -185,6 +185,32 @@ def test_indexer_validation():
     bad = list(pool)
     bad[5] = 9  # dtype
     assert fused(*args, FAKE, ws, *bad, None) == ENOTSUP
+    # ... and with the norm and the window rows
+    nrp = [FAKE, FAKE, FAKE, FAKE, 4 * N_c, 512, 0, 64, 1e-6, 10000.0, 1, 0, 0]
+    rows = [1, FAKE, FAKE, FAKE, 512, 512]
+    fnr = L.lightning_index_topk_csa_compress_norm_rope_rows
+    assert fnr(*args, FAKE, ws - 1, *nrp, *rows, None) == EWORKSPACE
+    bad = list(nrp)
+    bad[7] = 60  # d_rope not a multiple of 8
+    assert fnr(*args, FAKE, ws, *bad, *rows, None) == EINVAL
+    bad = list(nrp)
+    bad[6] = -1  # entry0
+    assert fnr(*args, FAKE, ws, *bad, *rows, None) == EINVAL
+    bad = list(nrp)
+    bad[9] = 0.0  # theta
+    assert fnr(*args, FAKE, ws, *bad, *rows, None) == EINVAL
+    bad = list(nrp)
+    bad[2] = FAKE + 4  # gamma not 16-byte aligned
+    assert fnr(*args, FAKE, ws, *bad, *rows, None) == EINVAL
+    badr = list(rows)
+    badr[2] = None  # a row source without its destination
+    assert fnr(*args, FAKE, ws, *nrp, *badr, None) == EINVAL
+    badr = list(rows)
+    badr[4] = 256  # row stride below T * c
+    assert fnr(*args, FAKE, ws, *nrp, *badr, None) == EINVAL
+    badr = list(rows)
+    badr[0] = -1  # T
+    assert fnr(*args, FAKE, ws, *nrp, *badr, None) == EINVAL
 
 
 def test_attend_validation():

@@ -1090,11 +1090,17 @@ struct Plan {
 // ring, 64 with the 4-tile one).
 Plan make_plan(int B, int Tq, int n_h, int n_slots_c, int W, bool csa) {
   Plan P;
+  // heads per workgroup: the largest of 64, 32, 16 that divides n_h (n_h % 16 == 0), so
+  // that the head groups tile the heads exactly; queries per workgroup (HCA prefill with
+  // at most 64 heads): a power of two up to 128 / HPW, so that the wave count
+  // Tg * HPW / 16 is 1, 2, 4 or 8.  Other head counts (float32 calls, which take only
+  // the workspace size from this plan) keep one group of n_h heads.
+  P.HPW = n_h % 64 == 0 ? 64 : n_h % 32 == 0 ? 32 : n_h % 16 == 0 ? 16 : n_h;
   P.Tg = 1;
-  if (!csa && Tq > 1 && n_h <= 64) P.Tg = 128 / n_h < Tq ? 128 / n_h : Tq;
-  if (P.Tg > 8) P.Tg = 8;
-  P.HPW = n_h < 64 ? n_h : 64;
-  if (P.HPW * P.Tg > 128) P.HPW = 128 / P.Tg;
+  if (!csa && Tq > 1 && n_h <= 64) {
+    const int lim = Tq < 128 / P.HPW ? Tq : 128 / P.HPW;
+    while (P.Tg * 2 <= lim) P.Tg *= 2;
+  }
   P.NW = P.Tg * P.HPW / 16;
   P.n_hg = n_h / P.HPW;
   P.n_slots = n_slots_c + W + P.Tg - 1;

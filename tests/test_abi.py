@@ -213,6 +213,21 @@ def test_indexer_validation():
     assert fnr(*args, FAKE, ws, *nrp, *badr, None) == EINVAL
 
 
+def test_attend_workspace_sizes_every_head_count():
+    """The workspace queries run the launch plan on the host for any head count (float32
+    calls take any n_h; bfloat16 calls any multiple of 16 up to 128), with no division by
+    an empty head group.  A decode call with one query splits its rows over workgroups,
+    so it needs a partial-output workspace."""
+    L = lib.load()
+    for n_h in list(range(1, 40)) + [48, 64, 72, 80, 96, 112, 128, 200]:
+        for Tq in (1, 3, 7, 8192):
+            assert L.csa_attend_workspace_size(1, Tq, n_h, 512, 512, 128) >= 0
+            assert L.hca_attend_workspace_size(1, Tq, n_h, 512, 1024, 128) >= 0
+    for n_h in range(16, 129, 16):
+        assert L.csa_attend_workspace_size(1, 1, n_h, 512, 512, 128) > 0
+        assert L.hca_attend_workspace_size(1, 1, n_h, 512, 1024, 128) > 0
+
+
 def test_attend_validation():
     L = lib.load()
     B, Tq, n_h, c, k, W = 2, 1, 64, 512, 512, 128

@@ -727,13 +727,13 @@ int index_check_common(const void* q_idx, const float* w_idx, const void* k_idx,
   if (k > MAX_K) return fail(CSAHCA_ENOTSUP, "indexer: k above 1024 is not built");
   if ((long long)B * Tq > 0x7FFFFFFFLL / 2) return fail(CSAHCA_ENOTSUP, "indexer: too many queries");
   if (idx_dtype == CSAHCA_FP8_E4M3FN) {
-    if (n_ih % 16 != 0 || n_ih > 128)
-      return fail(CSAHCA_ENOTSUP, "indexer: FP8 keys need n_ih % 16 == 0 and n_ih <= 128");
+    if (n_ih != 16 && n_ih != 32 && n_ih != 64 && n_ih != 128)
+      return fail(CSAHCA_ENOTSUP, "indexer: FP8 keys need n_ih in {16, 32, 64, 128}");
     if (c_I != 32 && c_I != 64 && c_I != 128)
       return fail(CSAHCA_ENOTSUP, "indexer: FP8 keys need c_I in {32, 64, 128}");
   } else if (idx_dtype == CSAHCA_MXFP4) {
-    if (n_ih % 16 != 0 || n_ih > 128 || c_I != 128)
-      return fail(CSAHCA_ENOTSUP, "indexer: MX FP4 keys need n_ih % 16 == 0, n_ih <= 128, c_I == 128");
+    if ((n_ih != 16 && n_ih != 32 && n_ih != 64 && n_ih != 128) || c_I != 128)
+      return fail(CSAHCA_ENOTSUP, "indexer: MX FP4 keys need n_ih in {16, 32, 64, 128} and c_I == 128");
   } else if (idx_dtype == CSAHCA_F32) {
     if (n_ih * c_I > 4096)
       return fail(CSAHCA_ENOTSUP, "indexer: float32 keys need n_ih * c_I <= 4096");

@@ -152,6 +152,9 @@ def test_indexer_validation():
     bad = list(args)
     bad[8] = 48 + 8  # n_ih not a multiple of 16
     assert L.lightning_index_topk(*bad, FAKE, ws, None) == ENOTSUP
+    for n_ih_bad in (48, 80, 96, 112, 256):  # FP8 / MX FP4 scoring is built for 16, 32, 64, 128 heads
+        bad[8] = n_ih_bad
+        assert L.lightning_index_topk(*bad, FAKE, ws, None) == ENOTSUP
     bad = list(args)
     bad[9] = 96  # c_I
     assert L.lightning_index_topk(*bad, FAKE, ws, None) == ENOTSUP

@@ -18,6 +18,8 @@
 //     fragment read touches fall in 16 distinct bank groups.  Tiles are handed out so that each XCD
 //     gets a contiguous run; the column tiles of a token tile run together there and share
 //     its rows in that XCD's L2.
+#include <mutex>
+
 #include "common.hpp"
 
 namespace {
@@ -213,7 +215,6 @@ __global__ __launch_bounds__(512, 1) void gop_gemm(const uint16_t* __restrict__ 
     }
 }
 
-bool gemm_attr_set = false;
 
 }  // namespace
 
@@ -240,12 +241,13 @@ extern "C" int grouped_out_proj(const void* o, const void* w, void* y, int T, in
   if (T > 64 && d_g % GN == 0 && K_g % GK == 0) {
     const long long mtiles = cdiv<long long>(T, GM), ntiles = d_g / GN, tiles = mtiles * ntiles * g;
     if (tiles > 0x7FFFFFFFLL) return fail(CSAHCA_ENOTSUP, "grouped_out_proj: problem too large");
-    if (!gemm_attr_set) {
-      if (hipFuncSetAttribute((const void*)gop_gemm, hipFuncAttributeMaxDynamicSharedMemorySize, GEMM_LDS) !=
-          hipSuccess)
-        return fail(CSAHCA_ELAUNCH, "grouped_out_proj: cannot set the LDS size");
-      gemm_attr_set = true;
-    }
+    // raise the kernel's dynamic LDS limit once per process, whichever thread calls first
+    static std::once_flag once;
+    static hipError_t attr = hipSuccess;
+    std::call_once(once, [] {
+      attr = hipFuncSetAttribute((const void*)gop_gemm, hipFuncAttributeMaxDynamicSharedMemorySize, GEMM_LDS);
+    });
+    if (attr != hipSuccess) return fail(CSAHCA_ELAUNCH, "grouped_out_proj: cannot set the LDS size");
     hipLaunchKernelGGL(gop_gemm, dim3((unsigned)tiles), dim3(64 * GWAVES), GEMM_LDS, st, X, Wt, Y, T, K_g, d_g, ldo, ldy,
                        (int)mtiles, (int)ntiles, (int)tiles);
     return launch_status(name);

@@ -402,6 +402,15 @@ def test_window_source_offset():
         assert torch.equal(a, b) and torch.equal(la, lb), layer
 
 
+@pytest.mark.parametrize("k,W", [(1, 1), (100, 37), (777, 64), (1000, 5)])
+def test_window_and_k_sizes(k, W):
+    """Windows of any length up to the ring and top-k sizes that are no power of two (the
+    attention splits hold whole 32-row tiles, so the compressed/window boundary and the
+    list end fall inside tiles); k = 1000 is more than the 900 usable entries."""
+    run_chain(CONFIGS[3].scaled(B=2, n=4 * 900 + 2, k=k, W=W, seed=80 + W))
+    run_chain(CONFIGS[2].scaled(B=2, n=128 * 9 + 5, W=W, seed=90 + W))
+
+
 @pytest.mark.parametrize("n_h", [16, 32, 48, 80, 96, 112])
 def test_fewer_heads(n_h):
     """Every head count the bfloat16 calls accept (n_h % 16 == 0, n_h <= 128): the head

@@ -402,6 +402,15 @@ def test_window_source_offset():
         assert torch.equal(a, b) and torch.equal(la, lb), layer
 
 
+@pytest.mark.parametrize("n_ih,c_I", [(16, 128), (128, 128), (32, 64), (64, 64), (128, 32), (16, 32)])
+def test_indexer_heads_and_widths(n_ih, c_I):
+    """Every indexer shape the FP8 path is built for: 16 to 128 heads, key widths 32, 64
+    and 128 (widths below 128 take the general scoring kernel and the selection through
+    the group maxima), at decode and in a prefill chunk."""
+    run_chain(CONFIGS[3].scaled(B=2, n=4 * 900 + 2, n_ih=n_ih, c_I=c_I, seed=100 + n_ih + c_I))
+    run_chain(CONFIGS[4].scaled(n=2048 + 7, Tq=33, n_ih=n_ih, c_I=c_I, seed=200 + n_ih + c_I))
+
+
 @pytest.mark.parametrize("k,W", [(1, 1), (100, 37), (777, 64), (1000, 5)])
 def test_window_and_k_sizes(k, W):
     """Windows of any length up to the ring and top-k sizes that are no power of two (the
